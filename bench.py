@@ -1,0 +1,261 @@
+"""Benchmark of the block-scaled MoE layer on one MI355X.
+
+One step = the whole hot path over one batch: moe_route (router logits, top-8, gate
+weights, hidden-state amax) + moe_forward (permutation, hidden-state quantisation,
+gate_up GEMM with SwiGLU and intermediate quantisation, down GEMM, weighted
+combine), with all inputs and packed weights resident in HBM. The default workload
+is the NVFP4 decode step (64 tokens, d_model 4096, d_ff 2560, 384 experts, top-8);
+--workload i selects one of the five seeded synthetic workloads.
+
+Printed: one JSON line (rank 0). `roofline` covers the dominant kernel (the gate_up
+GEMM) timed live with HIP events recorded around its launch on the library's stream;
+`cpu_baseline` is the CPU oracle timed on this host's cores over a bounded sample of
+the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"f16": 2516.6, "fp8": 5033.2}  # dense, MI355X
+METRIC = "MoE layer tokens/s; % peak HBM BW (decode), % scaled-MFMA peak (prefill)"
+
+
+class HipEvents:
+    """Raw hipEvent_t handles (libamdhip64), recorded by the library on its stream."""
+
+    def __init__(self, n: int):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(ev)) == 0
+            self.arr[i] = ev
+
+    def ms(self, i: int, j: int) -> float:
+        out = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(out), self.arr[i], self.arr[j])
+        assert rc == 0, f"hipEventElapsedTime failed ({rc})"
+        return float(out.value)
+
+    def close(self):
+        for i in range(len(self.arr)):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def packed_bytes_per_expert(fmt: str, N: int, K: int) -> int:
+    if fmt == "nvfp4":
+        return N * K // 2 + N * K // 16 + 4
+    return N * K + N * K // 32
+
+
+def make_weights(moe, torch, wl, dev):
+    """Packed gate_up and down of all experts, masters drawn on the GPU in expert chunks."""
+    E, D, F = wl.E, wl.D, wl.F
+    gu = moe.PackedWeights.empty(wl.fmt, E, 2 * F, D, device=dev)
+    dn = moe.PackedWeights.empty(wl.fmt, E, D, F, device=dev)
+    chunk = max(1, min(E, (1 << 30) // (2 * F * D * 2)))
+    buf = torch.empty(chunk * 2 * F * D, dtype=torch.int16, device=dev)
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        n = e1 - e0
+        g = buf[: n * 2 * F * D]
+        wl.gate_up_master_device(e0, e1, g)
+        moe.quantize_weights(wl.fmt, g.view(n, 2 * F, D), out=gu.experts(e0, e1))
+        d = buf[: n * D * F]
+        wl.down_master_device(e0, e1, d)
+        moe.quantize_weights(wl.fmt, d.view(n, D, F), out=dn.experts(e0, e1))
+    torch.cuda.synchronize()
+    del buf
+    return gu, dn
+
+
+def cpu_baseline(wl, h, wr, bias, target_s: float = 10.0):
+    """The oracle (route + forward, fp64 experts) on the first tokens of the workload,
+    timed on this host; the sample grows until it takes about target_s seconds.
+    Experts are compacted to those the sample touches (weights quantised by the
+    oracle itself, untimed)."""
+    import oracle
+
+    cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    n = 2
+    while True:
+        hs = np.ascontiguousarray(h[:n])
+        t0 = time.perf_counter()
+        idx, w = oracle.route(hs, wr, k=wl.k, bias=bias)
+        t_route = time.perf_counter() - t0
+        local = (idx >= wl.e_begin) & (idx < wl.local_end)
+        used = np.unique(idx[local])
+        remap = np.full(wl.E, -1, np.int32)
+        remap[used] = np.arange(len(used), dtype=np.int32)
+        cidx = np.where(local, remap[idx], len(used)).astype(np.int32)  # non-local -> outside [0, m)
+        m = len(used)
+        gu = {"codes": [], "scales": [], "tensor_scale": []}
+        dn = {"codes": [], "scales": [], "tensor_scale": []}
+        for e in used:
+            for d, master in ((gu, wl.gate_up_master(int(e))), (dn, wl.down_master(int(e)))):
+                q = oracle.quantize_weights(wl.fmt, master)
+                for key in d:
+                    d[key].append(q[key])
+        cat = lambda d: {k_: (None if v[0] is None else np.concatenate(v)) for k_, v in d.items()}
+        gu, dn = cat(gu), cat(dn)
+        t1 = time.perf_counter()
+        oracle.moe_forward(wl.fmt, hs, cidx, w, D=wl.D, F=wl.F, E=m + 1, e_begin=0, e_end=m,
+                           gate_up=_pad_expert(gu, wl.fmt), down=_pad_expert(dn, wl.fmt))
+        t_fwd = time.perf_counter() - t1
+        total = t_route + t_fwd
+        if total >= target_s or n >= wl.T:
+            return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                    "sample": f"first {n} of {wl.T} tokens of the workload, route + forward, "
+                              f"{m} touched experts, {total:.1f} s"}
+        n = min(wl.T, max(n * 2, int(n * target_s / max(total, 1e-3)) + 1))
+
+
+def _pad_expert(d, fmt):
+    """Append one all-zero expert (the non-local slot target of the compacted table)."""
+    out = {}
+    for k_, v in d.items():
+        if v is None:
+            out[k_] = None
+            continue
+        pad = np.zeros((1,) + v.shape[1:], v.dtype)
+        if k_ == "tensor_scale":
+            pad = np.ones(1, v.dtype)
+        out[k_] = np.concatenate([v, pad])
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=1, help="index into the five synthetic workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-target-s", type=float, default=10.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer is built for one "
+              "GPU's expert share; see DESIGN.md for how it shards.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_moe_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    T, D, F, E, k = wl.T, wl.D, wl.F, wl.E, wl.k
+    print(f"[bench] workload {wl.index} {wl.name}: T={T} D={D} F={F} E={E} local=[{wl.e_begin},{wl.local_end})",
+          file=sys.stderr, flush=True)
+
+    h = wl.hidden()
+    wr = wl.router_weight()
+    bias = wl.router_bias()
+    d_h = torch.from_numpy(h.view(np.int16)).to(dev)
+    d_wr = torch.from_numpy(wr.view(np.int16)).to(dev)
+    d_bias = None if bias is None else torch.from_numpy(bias).to(dev)
+    t0 = time.perf_counter()
+    gu, dn = make_weights(moe, torch, wl, dev)
+    print(f"[bench] packed weights ready in {time.perf_counter() - t0:.1f} s "
+          f"({(gu.nbytes() + dn.nbytes()) / 1e9:.2f} GB)", file=sys.stderr, flush=True)
+
+    layer = moe.Layer(wl.fmt, T, D, F, E, gu, dn, top_k=k, e_begin=wl.e_begin, e_end=wl.local_end)
+    out = torch.empty((T, D), dtype=torch.float32, device=dev)
+    nv = wl.fmt == "nvfp4"
+
+    def step(events=None):
+        idx, w, _, amax = moe.route(d_h, d_wr, k, d_bias, want_amax=nv)
+        layer.forward(d_h, idx, w, out=out, h_amax=amax, events=events)
+        return idx
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = HipEvents(K * moe.N_EVENTS)
+    per_step = [ctypes.cast(ctypes.addressof(ev.arr) + i * moe.N_EVENTS * ctypes.sizeof(ctypes.c_void_p),
+                            ctypes.c_void_p) for i in range(K)]
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(K):
+        idx = step(per_step[i])
+    stop.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_step = total_ms / K
+    base = lambda i: i * moe.N_EVENTS
+    gate_up_ms = float(np.mean([ev.ms(base(i) + 1, base(i) + 2) for i in range(K)]))
+    down_ms = float(np.mean([ev.ms(base(i) + 3, base(i) + 4) for i in range(K)]))
+    fwd_ms = float(np.mean([ev.ms(base(i) + 0, base(i) + 5) for i in range(K)]))
+    ev.close()
+
+    # algorithmic bytes and flops of the dominant kernel (the gate_up GEMM)
+    idx_h = idx.cpu().numpy()
+    local = (idx_h >= wl.e_begin) & (idx_h < wl.local_end)
+    S = int(local.sum())
+    touched = int(len(np.unique(idx_h[local])))
+    gu_b = packed_bytes_per_expert(wl.fmt, 2 * F, D)
+    dn_b = packed_bytes_per_expert(wl.fmt, D, F)
+    act_b = lambda rows, cols: rows * (cols // 2 + cols // 16) if nv else rows * (cols + cols // 32)
+    gate_up_bytes = touched * gu_b + act_b(T, D) + act_b(S, F)
+    gate_up_flops = 4.0 * S * F * D
+    layer_bytes = touched * (gu_b + dn_b) + E * D * 2 + T * D * 2 + T * D * 4
+    mfma_peak = MFMA_PEAK_TFLOPS["f16" if nv else "fp8"]
+    decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge
+    if decode:
+        achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(achieved / mfma_peak, 4), "traffic": None}
+    roof["kernel"] = "gemm_" + wl.fmt + "_kernel (gate_up)"
+    roof["per_launch"] = {"bytes": gate_up_bytes, "flops": gate_up_flops, "ms": round(gate_up_ms, 4)}
+
+    print(f"[bench] {ms_step:.3f} ms/step (forward {fwd_ms:.3f} ms: gate_up {gate_up_ms:.3f} ms, down "
+          f"{down_ms:.3f} ms); S={S}, {touched} experts touched, layer {layer_bytes / 1e9:.3f} GB "
+          f"-> {layer_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s whole-step", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, h, wr, bias, args.cpu_target_s)
+        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+
+    value = T * K / (total_ms * 1e-3)
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16 (exact NVFP4 values), fp32 accumulate" if nv else "e4m3 (MXFP8), fp32 accumulate",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "tokens": T, "d_model": D, "d_ff": F, "experts": E, "top_k": k,
+                   "format": wl.fmt, "local_experts": [wl.e_begin, wl.local_end], "experts_touched": touched,
+                   "slots": S, "layer_bytes": layer_bytes,
+                   "layer_GBps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,94 @@
+// internal.h - launchers shared between the kernel files and the host API.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Device control block at the head of the forward workspace.
+struct Ctrl {
+    int32_t S;           // local token-slots
+    int32_t n_tiles;     // M-tiles of the grouped GEMMs
+    uint32_t amax_a;     // max |h| (fp32 bits) when computed by the forward itself
+    uint32_t amax_i;     // max |SwiGLU output| over the S rows (fp32 bits), NVFP4
+    int32_t pad[60];
+};
+
+// ---- weight / activation quantisers (quant.hip)
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
+hipError_t launch_amax_bf16_rows(const uint16_t *x, int64_t rows, int64_t K, int64_t groups,
+                                 uint32_t *amax_bits, hipStream_t s);
+hipError_t launch_quant_weights_nvfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K,
+                                      const uint32_t *amax_bits, uint8_t *codes, uint8_t *scales,
+                                      hipStream_t s);
+hipError_t launch_finish_tensor_scale(float *ts_inout, int32_t n, hipStream_t s);
+hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, int32_t K,
+                                      uint8_t *codes, uint8_t *scales, hipStream_t s);
+// hidden states [T][D] -> NVFP4 codes/scales and the exact fp16 value codes*scale
+hipError_t launch_quant_act_nvfp4(const uint16_t *h, int32_t T, int32_t D, const uint32_t *amax_bits,
+                                  uint8_t *codes, uint8_t *scales, _Float16 *deq, float *tscale_out,
+                                  hipStream_t s);
+// hidden states [T][D] -> MXFP8 codes/scales and the exact bf16 value code*2^scale
+hipError_t launch_quant_act_mxfp8(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes,
+                                  uint8_t *scales, uint16_t *deq_bf16, hipStream_t s);
+// intermediate [rows <= ctrl->S][F] fp32 -> NVFP4 (tensor scale from ctrl->amax_i)
+hipError_t launch_quant_inter_nvfp4(const float *x, int32_t max_rows, int32_t F, const Ctrl *ctrl,
+                                    uint8_t *codes, uint8_t *scales, _Float16 *deq, float *tscale_out,
+                                    hipStream_t s);
+
+// ---- router (route.hip)
+hipError_t launch_router_logits(int32_t T, int32_t D, int32_t E, const uint16_t *h, const uint16_t *wr,
+                                const float *bias, float *logits, uint32_t *amax_bits, hipStream_t s);
+hipError_t launch_router_topk(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *idx,
+                              float *w, hipStream_t s);
+
+// ---- permutation (permute.hip)
+struct PermuteArgs {
+    int32_t T, k, e_begin, n_loc;
+    int32_t chunk_tokens, n_chunks;
+    int32_t bm;          // M-tile rows of the grouped GEMMs
+    int32_t max_tiles;
+    const int32_t *idx;  // [T][k]
+    int32_t *chunk_counts;  // [n_chunks][n_loc]
+    int32_t *counts;        // [n_loc]
+    int32_t *offsets;       // [n_loc + 1]
+    int32_t *tile_expert;   // [max_tiles]  local expert of each M-tile
+    int32_t *tile_row0;     // [max_tiles]  first sorted position of each M-tile
+    int32_t *sorted_slot;   // [T*k]
+    int32_t *slot_pos;      // [T*k]  sorted position of each slot or -1
+    Ctrl *ctrl;
+};
+hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
+
+// ---- grouped GEMMs (gemm.hip)
+struct GemmArgs {
+    const Ctrl *ctrl;
+    const int32_t *tile_expert, *tile_row0, *offsets, *sorted_slot;
+    int32_t top_k;
+    int32_t gather_by_token;  // A row of sorted position p: token sorted_slot[p]/top_k (1) or p (0)
+    int32_t N, K;             // weight matrix [N][K] per expert; gate_up: N = 2F
+    int32_t e_begin;          // global index of local expert 0
+    // A operand: exact 16-bit values of the quantised activations, [rows][K]
+    const void *a_vals;       // NVFP4: fp16; MXFP8: bf16
+    const float *a_tscale;    // NVFP4: [1] activation tensor scale
+    // weights (canonical packed layout, global expert index)
+    const uint8_t *w_codes, *w_scales;
+    const float *w_tscale;    // NVFP4: [E]
+    // outputs
+    float *out_f32;           // gate_up NVFP4: SwiGLU [S][F]; down: y [S][N]
+    uint32_t *amax_bits;      // gate_up NVFP4: max |SwiGLU|
+    uint8_t *o_codes, *o_scales;  // gate_up MXFP8: quantised SwiGLU [S][F], [S][F/32]
+    void *o_vals;             // gate_up MXFP8: exact bf16 values of those codes [S][F]
+    float *o_tap;             // gate_up MXFP8: optional fp32 SwiGLU [S][F]
+};
+enum class GemmShape { Decode, Prefill };
+hipError_t launch_grouped_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, GemmShape shape,
+                               int32_t max_tiles, hipStream_t s);
+int32_t gemm_bm(GemmShape shape);
+
+// ---- combine (combine.hip)
+hipError_t launch_combine(int32_t T, int32_t D, int32_t k, const int32_t *slot_pos, const float *w,
+                          const float *y, float *out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,320 @@
+// moe_api.hip - host side of the C ABI declared in include/moe.h: argument
+// validation (pure host code, no HIP call), the forward workspace plan, and the
+// launch sequence on the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int32_t to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                                \
+    do {                                             \
+        const hipError_t err_ = (expr);              \
+        if (err_ != hipSuccess) return MOE_ERR_HIP;  \
+    } while (0)
+
+// Rows per expert above which the grouped GEMMs use the 128-row tile.
+constexpr int32_t kPrefillRowsPerExpert = 48;
+
+struct Plan {
+    GemmShape shape;
+    int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
+    size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
+    size_t a_codes, a_scales, a_tscale, a16;
+    size_t inter32, i_codes, i_scales, i_tscale, i16, y;
+    size_t total;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+Plan make_plan(const moe_forward_args *a) {
+    Plan p{};
+    const int64_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
+    const bool nv = a->fmt == MOE_FMT_NVFP4;
+    p.n_loc = a->e_end - a->e_begin;
+    p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
+    p.bm = gemm_bm(p.shape);
+    int32_t ct = (int32_t)(T / 256);
+    p.chunk_tokens = ct < 1 ? 1 : (ct > 64 ? 64 : ct);
+    p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
+    p.max_tiles = (int32_t)(p.n_loc + TK / p.bm + 1);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += up256(bytes);
+        return at;
+    };
+    p.ctrl = take(sizeof(Ctrl));
+    p.chunk_counts = take(sizeof(int32_t) * (size_t)p.n_chunks * p.n_loc);
+    p.counts = take(sizeof(int32_t) * p.n_loc);
+    p.offsets = take(sizeof(int32_t) * (p.n_loc + 1));
+    p.tile_expert = take(sizeof(int32_t) * p.max_tiles);
+    p.tile_row0 = take(sizeof(int32_t) * p.max_tiles);
+    p.sorted_slot = take(sizeof(int32_t) * TK);
+    p.slot_pos = take(sizeof(int32_t) * TK);
+    p.a_codes = take(nv ? T * D / 2 : T * D);
+    p.a_scales = take(nv ? T * D / 16 : T * D / 32);
+    p.a_tscale = take(sizeof(float));
+    p.a16 = take(2 * T * D);  // exact 16-bit values of the hidden-state codes
+    p.inter32 = nv ? take(sizeof(float) * TK * F) : 0;
+    p.i_codes = take(nv ? TK * F / 2 : TK * F);
+    p.i_scales = take(nv ? TK * F / 16 : TK * F / 32);
+    p.i_tscale = take(sizeof(float));
+    p.i16 = take(2 * TK * F);  // exact 16-bit values of the intermediate codes
+    p.y = take(sizeof(float) * TK * D);
+    p.total = off;
+    return p;
+}
+
+int32_t check_packed(const moe_packed &w, int32_t fmt, int32_t E, int32_t N, int32_t K) {
+    if (w.fmt != fmt || w.E != E || w.N != N || w.K != K) return MOE_ERR_INVALID_ARG;
+    if (!w.codes || !w.scales || (fmt == MOE_FMT_NVFP4 && !w.tensor_scale)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w.codes) || !aligned16(w.scales) || (w.tensor_scale && ((uintptr_t)w.tensor_scale & 3u)))
+        return MOE_ERR_ALIGNMENT;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char *moe_status_string(int32_t s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+        case MOE_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+        case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+        case MOE_ERR_HIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
+    if (!out || !w) return MOE_ERR_INVALID_ARG;
+    const int32_t fmt = out->fmt, E = out->E, N = out->N, K = out->K;
+    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
+    if (K % (fmt == MOE_FMT_NVFP4 ? 16 : 32)) return MOE_ERR_INVALID_ARG;
+    if (!out->codes || !out->scales || (fmt == MOE_FMT_NVFP4 && !out->tensor_scale)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w) || !aligned16(out->codes) || ((uintptr_t)out->tensor_scale & 3u)) return MOE_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (fmt == MOE_FMT_MXFP8)
+        return to_status(launch_quant_weights_mxfp8(w, E, N, K, out->codes, out->scales, s));
+    uint32_t *amax = reinterpret_cast<uint32_t *>(out->tensor_scale);  // amax bits, then the scale
+    MOE_TRY(launch_fill_u32(amax, 0u, E, s));
+    MOE_TRY(launch_amax_bf16_rows(w, (int64_t)E * N, K, E, amax, s));
+    MOE_TRY(launch_quant_weights_nvfp4(w, E, N, K, amax, out->codes, out->scales, s));
+    return to_status(launch_finish_tensor_scale(out->tensor_scale, E, s));
+}
+
+int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t *h, const uint16_t *wr,
+                  const float *bias, float *logits, int32_t *topk_idx, float *topk_w, float *h_amax,
+                  void *stream) {
+    if (T < 0 || D <= 0 || E <= 0 || E > 4096 || top_k < 1 || top_k > 8 || top_k > E) return MOE_ERR_INVALID_ARG;
+    if (T == 0) return MOE_OK;
+    if (!h || !wr || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(h) || !aligned16(wr) || !aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+        (bias && !aligned16(bias)) || (h_amax && !aligned16(h_amax)))
+        return MOE_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    uint32_t *amax = reinterpret_cast<uint32_t *>(h_amax);
+    if (amax) MOE_TRY(launch_fill_u32(amax, 0u, 1, s));
+    MOE_TRY(launch_router_logits(T, D, E, h, wr, bias, logits, amax, s));
+    return to_status(launch_router_topk(T, E, top_k, logits, topk_idx, topk_w, s));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The size fields alone (what the workspace plan depends on).
+int32_t validate_shape(const moe_forward_args *a) {
+    if (!a) return MOE_ERR_INVALID_ARG;
+    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->E > 4096) return MOE_ERR_INVALID_ARG;
+    if (a->top_k < 1 || a->top_k > 8 || a->top_k > a->E) return MOE_ERR_INVALID_ARG;
+    if (a->e_begin < 0 || a->e_end <= a->e_begin || a->e_end > a->E) return MOE_ERR_INVALID_ARG;
+    if ((int64_t)a->T * a->top_k > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
+    if (a->D % 128 || a->F % 128) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_forward_validate(const moe_forward_args *a) {
+    const int32_t shape = validate_shape(a);
+    if (shape != MOE_OK) return shape;
+    if (a->T == 0) return MOE_OK;
+    if (!a->h || !a->topk_idx || !a->topk_w || !a->out) return MOE_ERR_INVALID_ARG;
+    int32_t rc = check_packed(a->gate_up, a->fmt, a->E, 2 * a->F, a->D);
+    if (rc != MOE_OK) return rc;
+    rc = check_packed(a->down, a->fmt, a->E, a->D, a->F);
+    if (rc != MOE_OK) return rc;
+    if (!aligned16(a->h) || !aligned16(a->topk_idx) || !aligned16(a->topk_w) || !aligned16(a->out) ||
+        (a->h_amax && !aligned16(a->h_amax)))
+        return MOE_ERR_ALIGNMENT;
+    if (a->taps && a->taps->inter && !aligned16(a->taps->inter)) return MOE_ERR_ALIGNMENT;
+    return MOE_OK;
+}
+
+size_t moe_forward_workspace_bytes(const moe_forward_args *a) {
+    if (validate_shape(a) != MOE_OK) return 0;
+    if (a->T == 0) return 0;
+    return make_plan(a).total;
+}
+
+int32_t moe_forward(const moe_forward_args *a, void *stream) {
+    int32_t rc = moe_forward_validate(a);
+    if (rc != MOE_OK) return rc;
+    if (a->T == 0) return MOE_OK;
+    const Plan P = make_plan(a);
+    if (!a->workspace || a->workspace_bytes < P.total) return MOE_ERR_WORKSPACE;
+    if (((uintptr_t)a->workspace & 255u) != 0) return MOE_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    uint8_t *ws = static_cast<uint8_t *>(a->workspace);
+    const bool nv = a->fmt == MOE_FMT_NVFP4;
+    const int32_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
+    Ctrl *ctrl = reinterpret_cast<Ctrl *>(ws + P.ctrl);
+    auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
+    auto U8 = [&](size_t off) { return ws + off; };
+    auto F32 = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+    auto F16 = [&](size_t off) { return reinterpret_cast<_Float16 *>(ws + off); };
+
+    auto mark = [&](int i) -> hipError_t {
+        return a->events ? hipEventRecord((hipEvent_t)a->events[i], s) : hipSuccess;
+    };
+    MOE_TRY(mark(MOE_EV_BEGIN));
+    MOE_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(ctrl), 0u, sizeof(Ctrl) / 4, s));
+
+    // 1. stable grouping of the local slots and the GEMM tile list
+    PermuteArgs pa{};
+    pa.T = T;
+    pa.k = k;
+    pa.e_begin = a->e_begin;
+    pa.n_loc = P.n_loc;
+    pa.chunk_tokens = P.chunk_tokens;
+    pa.n_chunks = P.n_chunks;
+    pa.bm = P.bm;
+    pa.max_tiles = P.max_tiles;
+    pa.idx = a->topk_idx;
+    pa.chunk_counts = I32(P.chunk_counts);
+    pa.counts = I32(P.counts);
+    pa.offsets = I32(P.offsets);
+    pa.tile_expert = I32(P.tile_expert);
+    pa.tile_row0 = I32(P.tile_row0);
+    pa.sorted_slot = I32(P.sorted_slot);
+    pa.slot_pos = I32(P.slot_pos);
+    pa.ctrl = ctrl;
+    MOE_TRY(launch_permute(pa, s));
+
+    // 2. hidden states quantised once per token
+    if (nv) {
+        const uint32_t *amax = reinterpret_cast<const uint32_t *>(a->h_amax);
+        if (!amax) {
+            MOE_TRY(launch_amax_bf16_rows(a->h, T, D, 1, &ctrl->amax_a, s));
+            amax = &ctrl->amax_a;
+        }
+        MOE_TRY(launch_quant_act_nvfp4(a->h, T, D, amax, U8(P.a_codes), U8(P.a_scales), F16(P.a16),
+                                       F32(P.a_tscale), s));
+    } else {
+        MOE_TRY(launch_quant_act_mxfp8(a->h, T, D, U8(P.a_codes), U8(P.a_scales),
+                                       reinterpret_cast<uint16_t *>(ws + P.a16), s));
+    }
+
+    // 3. gate_up GEMM + SwiGLU (+ MXFP8 intermediate quantisation)
+    GemmArgs g{};
+    g.ctrl = ctrl;
+    g.tile_expert = I32(P.tile_expert);
+    g.tile_row0 = I32(P.tile_row0);
+    g.offsets = I32(P.offsets);
+    g.sorted_slot = I32(P.sorted_slot);
+    g.top_k = k;
+    g.gather_by_token = 1;
+    g.N = 2 * F;
+    g.K = D;
+    g.e_begin = a->e_begin;
+    g.w_codes = a->gate_up.codes;
+    g.w_scales = a->gate_up.scales;
+    g.w_tscale = a->gate_up.tensor_scale;
+    g.a_vals = ws + P.a16;
+    if (nv) {
+        g.a_tscale = F32(P.a_tscale);
+        g.out_f32 = F32(P.inter32);
+        g.amax_bits = &ctrl->amax_i;
+        MOE_TRY(mark(MOE_EV_GATE_UP));
+        MOE_TRY(launch_grouped_gemm(g, true, true, P.shape, P.max_tiles, s));
+        MOE_TRY(mark(MOE_EV_GATE_UP_END));
+        // 4. NVFP4 intermediate: one tensor scale over all S rows
+        MOE_TRY(launch_quant_inter_nvfp4(F32(P.inter32), TK, F, ctrl, U8(P.i_codes), U8(P.i_scales), F16(P.i16),
+                                         F32(P.i_tscale), s));
+    } else {
+        g.o_codes = U8(P.i_codes);
+        g.o_vals = ws + P.i16;
+        g.o_scales = U8(P.i_scales);
+        g.o_tap = a->taps ? a->taps->inter : nullptr;
+        MOE_TRY(mark(MOE_EV_GATE_UP));
+        MOE_TRY(launch_grouped_gemm(g, false, true, P.shape, P.max_tiles, s));
+        MOE_TRY(mark(MOE_EV_GATE_UP_END));
+    }
+
+    // 5. down GEMM -> y [S][D]
+    GemmArgs d = g;
+    d.gather_by_token = 0;
+    d.N = D;
+    d.K = F;
+    d.w_codes = a->down.codes;
+    d.w_scales = a->down.scales;
+    d.w_tscale = a->down.tensor_scale;
+    d.out_f32 = F32(P.y);
+    d.amax_bits = nullptr;
+    d.o_codes = nullptr;
+    d.o_scales = nullptr;
+    d.o_tap = nullptr;
+    d.o_vals = nullptr;
+    d.a_vals = ws + P.i16;
+    d.a_tscale = nv ? F32(P.i_tscale) : nullptr;
+    MOE_TRY(mark(MOE_EV_DOWN));
+    MOE_TRY(launch_grouped_gemm(d, nv, false, P.shape, P.max_tiles, s));
+    MOE_TRY(mark(MOE_EV_DOWN_END));
+
+    // 6. weighted combine
+    MOE_TRY(launch_combine(T, D, k, I32(P.slot_pos), a->topk_w, F32(P.y), a->out, s));
+    MOE_TRY(mark(MOE_EV_END));
+
+    // debug taps
+    if (a->taps) {
+        const moe_taps *t = a->taps;
+        auto cp = [&](void *dst, const void *src, size_t n) -> hipError_t {
+            return dst ? hipMemcpyAsync(dst, src, n, hipMemcpyDeviceToDevice, s) : hipSuccess;
+        };
+        MOE_TRY(cp(t->counts, ws + P.counts, sizeof(int32_t) * P.n_loc));
+        MOE_TRY(cp(t->offsets, ws + P.offsets, sizeof(int32_t) * (P.n_loc + 1)));
+        MOE_TRY(cp(t->sorted_slot, ws + P.sorted_slot, sizeof(int32_t) * (size_t)TK));
+        MOE_TRY(cp(t->a_codes, ws + P.a_codes, nv ? (size_t)T * D / 2 : (size_t)T * D));
+        MOE_TRY(cp(t->a_scales, ws + P.a_scales, nv ? (size_t)T * D / 16 : (size_t)T * D / 32));
+        if (nv) {
+            MOE_TRY(cp(t->a_tscale, ws + P.a_tscale, sizeof(float)));
+            MOE_TRY(cp(t->inter, ws + P.inter32, sizeof(float) * (size_t)TK * F));
+            MOE_TRY(cp(t->inter_tscale, ws + P.i_tscale, sizeof(float)));
+        }
+        MOE_TRY(cp(t->inter_codes, ws + P.i_codes, nv ? (size_t)TK * F / 2 : (size_t)TK * F));
+        MOE_TRY(cp(t->inter_scales, ws + P.i_scales, nv ? (size_t)TK * F / 16 : (size_t)TK * F / 32));
+        MOE_TRY(cp(t->y, ws + P.y, sizeof(float) * (size_t)TK * D));
+    }
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,275 @@
+// quant.hip - block quantisers of weights, hidden states and the SwiGLU intermediate.
+//
+// NVFP4 with the 4-vs-6 block rule (AI Primer, "Thinking Machines releases Inkling 2
+// Small weights under Apache 2.0", section "TL;DR") and MXFP8 (vLLM recipe
+// "thinkingmachines/Inkling-2-Small", section "Overview"); activations are quantised
+// to the layer's weight format (AI Primer, section "NVFP4 and MXFP8 experts").
+// One thread owns one 16-block (NVFP4) or 32-block (MXFP8): the block is read with
+// 16-byte loads, quantised in registers and written as packed bytes. Each NVFP4
+// tensor scale needs the tensor's max |x| first, so NVFP4 runs as amax pass, block
+// pass, then a tiny pass turning the amax into the fp32 tensor scale.
+#include "formats.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ void __launch_bounds__(kThreads) fill_u32_kernel(uint32_t *p, uint32_t v, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// amax_bits[g] = max |x| over group g (x is `groups` consecutive groups of `per`
+// bf16 values, `per` a multiple of 8). Max of non-negative floats equals the max
+// of their bit patterns, so the cross-block step is an integer atomic max.
+__global__ void __launch_bounds__(kThreads) amax_bf16_kernel(const uint16_t *__restrict__ x, int64_t per,
+                                                             uint32_t *__restrict__ amax_bits) {
+    const int g = blockIdx.y;
+    const uint4 *src = reinterpret_cast<const uint4 *>(x + (int64_t)g * per);
+    const int64_t n8 = per / 8;
+    uint32_t m = 0;  // max of |bf16| bit patterns (sign cleared); order-preserving
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 v = src[i];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            m = max(m, w[j] & 0x7fffu);
+            m = max(m, (w[j] >> 16) & 0x7fffu);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+    __shared__ uint32_t red[kThreads / 64];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
+        if (m) atomicMax(amax_bits + g, m << 16);  // bf16 bits -> fp32 bits
+    }
+}
+
+__device__ __forceinline__ void load16_bf16(const uint16_t *p, float (&x)[16]) {
+    const uint4 *q = reinterpret_cast<const uint4 *>(p);
+    const uint4 a = q[0], b = q[1];
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        x[2 * j] = __uint_as_float(w[j] << 16);
+        x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+    }
+}
+
+// exact fp16 of e2m1(code) * e4m3(scale) for the 16 codes of a block
+__device__ __forceinline__ void store_dequant16(_Float16 *dst, uint32_t lo, uint32_t hi, int scale) {
+    const float s = e4m3_value_pos(scale);
+    uint32_t o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const uint32_t word = j < 4 ? lo : hi;
+        const int sh = 8 * (j & 3);
+        const _Float16 v0 = (_Float16)(e2m1_value((word >> sh) & 15) * s);
+        const _Float16 v1 = (_Float16)(e2m1_value((word >> (sh + 4)) & 15) * s);
+        o[j] = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
+    }
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
+    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+}
+
+// NVFP4 weights: block b of expert e = b / blocks_per_expert; the tensor scale comes
+// from the expert's amax (fp32 bits, filled by amax_bf16_kernel).
+__global__ void __launch_bounds__(kThreads) quant_w_nvfp4_kernel(const uint16_t *__restrict__ w, int64_t n_blocks,
+                                                                 int64_t blocks_per_expert,
+                                                                 const uint32_t *__restrict__ amax_bits,
+                                                                 uint8_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = b / blocks_per_expert;
+        const float sg = nvfp4_tensor_scale(__uint_as_float(amax_bits[e]));
+        float x[16];
+        load16_bf16(w + b * 16, x);
+        uint32_t lo, hi;
+        int sc;
+        nvfp4_quant_block(x, sg, lo, hi, sc);
+        reinterpret_cast<uint2 *>(codes)[b] = make_uint2(lo, hi);
+        scales[b] = (uint8_t)sc;
+    }
+}
+
+__global__ void finish_tensor_scale_kernel(float *ts, int32_t n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) ts[i] = nvfp4_tensor_scale(ts[i]);
+}
+
+// MXFP8 (weights or hidden states): one thread per 32-block of a [rows][K] bf16 tensor;
+// deq (optional) receives the exact bf16 values code * 2^(scale - 127).
+__global__ void __launch_bounds__(kThreads) quant_mxfp8_bf16_kernel(const uint16_t *__restrict__ x, int64_t n_blocks,
+                                                                    uint8_t *__restrict__ codes,
+                                                                    uint8_t *__restrict__ scales,
+                                                                    uint16_t *__restrict__ deq) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + b * 32);
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 u = src[q];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * q + 2 * j] = __uint_as_float(w[j] << 16);
+                v[8 * q + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+        uint32_t c[8];
+        const int sc = mxfp8_quant_block(v, c);
+        uint4 *d = reinterpret_cast<uint4 *>(codes + b * 32);
+        d[0] = make_uint4(c[0], c[1], c[2], c[3]);
+        d[1] = make_uint4(c[4], c[5], c[6], c[7]);
+        scales[b] = (uint8_t)sc;
+        if (deq) {
+            const float s2 = ldexpf(1.0f, sc - 127);
+            uint4 *o = reinterpret_cast<uint4 *>(deq + b * 32);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                uint32_t ow[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int i = 8 * q + 2 * j;
+                    const int c0 = (c[i / 4] >> (8 * (i & 3))) & 0xff, c1 = (c[i / 4] >> (8 * (i & 3) + 8)) & 0xff;
+                    const uint32_t b0 = (__float_as_uint(e4m3_value_pos(c0 & 0x7f) * s2) >> 16) | ((uint32_t)(c0 & 0x80) << 8);
+                    const uint32_t b1 = (__float_as_uint(e4m3_value_pos(c1 & 0x7f) * s2) >> 16) | ((uint32_t)(c1 & 0x80) << 8);
+                    ow[j] = b0 | (b1 << 16);
+                }
+                o[q] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
+            }
+        }
+    }
+}
+
+// NVFP4 hidden states: one tensor scale over all T*D values.
+__global__ void __launch_bounds__(kThreads) quant_act_nvfp4_kernel(const uint16_t *__restrict__ h, int64_t n_blocks,
+                                                                   const uint32_t *__restrict__ amax_bits,
+                                                                   uint8_t *__restrict__ codes,
+                                                                   uint8_t *__restrict__ scales,
+                                                                   _Float16 *__restrict__ deq,
+                                                                   float *__restrict__ tscale_out) {
+    const float sg = nvfp4_tensor_scale(__uint_as_float(amax_bits[0]));
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b == 0 && tscale_out) tscale_out[0] = sg;
+    if (b >= n_blocks) return;
+    float x[16];
+    load16_bf16(h + b * 16, x);
+    uint32_t lo, hi;
+    int sc;
+    nvfp4_quant_block(x, sg, lo, hi, sc);
+    reinterpret_cast<uint2 *>(codes)[b] = make_uint2(lo, hi);
+    scales[b] = (uint8_t)sc;
+    store_dequant16(deq + b * 16, lo, hi, sc);
+}
+
+// NVFP4 SwiGLU intermediate: rows [0, S) of x [*][F] fp32, one tensor scale over
+// all S rows (max |x| gathered by the gate_up epilogue into ctrl->amax_i).
+__global__ void __launch_bounds__(kThreads) quant_inter_nvfp4_kernel(const float *__restrict__ x, int32_t F,
+                                                                     const Ctrl *__restrict__ ctrl,
+                                                                     uint8_t *__restrict__ codes,
+                                                                     uint8_t *__restrict__ scales,
+                                                                     _Float16 *__restrict__ deq,
+                                                                     float *__restrict__ tscale_out) {
+    const float sg = nvfp4_tensor_scale(__uint_as_float(ctrl->amax_i));
+    const int64_t n_blocks = (int64_t)ctrl->S * (F / 16);
+    const int64_t b0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b0 == 0 && tscale_out) tscale_out[0] = sg;
+    for (int64_t b = b0; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
+        const float4 *src = reinterpret_cast<const float4 *>(x + b * 16);
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 f = src[q];
+            v[4 * q] = f.x;
+            v[4 * q + 1] = f.y;
+            v[4 * q + 2] = f.z;
+            v[4 * q + 3] = f.w;
+        }
+        uint32_t lo, hi;
+        int sc;
+        nvfp4_quant_block(v, sg, lo, hi, sc);
+        reinterpret_cast<uint2 *>(codes)[b] = make_uint2(lo, hi);
+        scales[b] = (uint8_t)sc;
+        store_dequant16(deq + b * 16, lo, hi, sc);
+    }
+}
+
+inline unsigned grid_for(int64_t n, int64_t cap = 1 << 20) {
+    int64_t g = (n + kThreads - 1) / kThreads;
+    if (g < 1) g = 1;
+    if (g > cap) g = cap;
+    return (unsigned)g;
+}
+
+}  // namespace
+
+hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3(grid_for(n, 4096)), dim3(kThreads), 0, s, p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_amax_bf16_rows(const uint16_t *x, int64_t rows, int64_t K, int64_t groups, uint32_t *amax_bits,
+                                 hipStream_t s) {
+    const int64_t per = rows * K / groups;
+    int64_t bx = (per / 8 + kThreads * 8 - 1) / (kThreads * 8);  // about 8 loads per thread
+    if (bx < 1) bx = 1;
+    if (bx > 2048) bx = 2048;
+    hipLaunchKernelGGL(amax_bf16_kernel, dim3((unsigned)bx, (unsigned)groups), dim3(kThreads), 0, s, x, per,
+                       amax_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weights_nvfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K, const uint32_t *amax_bits,
+                                      uint8_t *codes, uint8_t *scales, hipStream_t s) {
+    const int64_t per = (int64_t)N * (K / 16);
+    const int64_t nb = per * E;
+    hipLaunchKernelGGL(quant_w_nvfp4_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, per, amax_bits, codes,
+                       scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_finish_tensor_scale(float *ts, int32_t n, hipStream_t s) {
+    hipLaunchKernelGGL(finish_tensor_scale_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ts, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
+                                      uint8_t *scales, hipStream_t s) {
+    const int64_t nb = (int64_t)E * N * (K / 32);
+    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, codes, scales,
+                       (uint16_t *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_nvfp4(const uint16_t *h, int32_t T, int32_t D, const uint32_t *amax_bits, uint8_t *codes,
+                                  uint8_t *scales, _Float16 *deq, float *tscale_out, hipStream_t s) {
+    const int64_t nb = (int64_t)T * (D / 16);
+    hipLaunchKernelGGL(quant_act_nvfp4_kernel, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
+                       h, nb, amax_bits, codes, scales, deq, tscale_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_mxfp8(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
+                                  uint16_t *deq_bf16, hipStream_t s) {
+    const int64_t nb = (int64_t)T * (D / 32);
+    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, h, nb, codes, scales,
+                       deq_bf16);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_inter_nvfp4(const float *x, int32_t max_rows, int32_t F, const Ctrl *ctrl, uint8_t *codes,
+                                    uint8_t *scales, _Float16 *deq, float *tscale_out, hipStream_t s) {
+    const int64_t nb = (int64_t)max_rows * (F / 16);
+    hipLaunchKernelGGL(quant_inter_nvfp4_kernel, dim3(grid_for(nb, 8192)), dim3(kThreads), 0, s, x, F, ctrl, codes,
+                       scales, deq, tscale_out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,176 @@
+/*
+ * moe.h - C ABI of the block-scaled routed-expert MoE layer for AMD MI355X (gfx950).
+ *
+ * The layer (vLLM recipe "thinkingmachines/Inkling-2-Small", section "Overview";
+ * AI Primer "Thinking Machines releases Inkling 2 Small weights under Apache 2.0",
+ * section "NVFP4 and MXFP8 experts"): every token is sent to 8 of 384 routed experts,
+ * there is no shared expert, expert weights are NVFP4 (layers 0-39) or MXFP8 (layers
+ * 40-47), and the expert activations are quantised to the layer's weight format.
+ * The pages fix neither the gate, the expert MLP nor the bit layouts; the readings
+ * used here are: softmax-then-top-8 gate, SwiGLU experts (gate_up [2F, D] with rows
+ * [0, F) = gate and [F, 2F) = up, down [D, F]), NVFP4 = E2M1 codes + one E4M3 scale
+ * per 16 values + an fp32 tensor scale amax / (6 * 448), with each 16-block scaled
+ * so that its maximum maps to 6 or to 4, whichever gives the lower squared error
+ * (AI Primer, section "TL;DR"), and MXFP8 = E4M3 codes + one E8M0 scale
+ * 2^(floor(log2 amax) - 8) per 32 values.
+ *
+ * Conventions for every call:
+ *  - All pointers are DEVICE pointers unless stated otherwise. The caller allocates
+ *    and frees every buffer; the library allocates no device memory, holds no
+ *    per-call global state and may be called concurrently on different streams
+ *    with different buffers.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream). Every
+ *    call only enqueues work on it and returns; nothing synchronises the host.
+ *  - Arguments are validated on the host before anything is enqueued; an invalid
+ *    call returns a negative status and enqueues nothing. Faults inside kernels
+ *    (for example from a bad pointer) surface at the caller's next synchronisation.
+ *  - NaN or infinite inputs are outside the contract (results unspecified).
+ *  - Device pointers must be 16-byte aligned (MOE_ERR_ALIGNMENT otherwise).
+ */
+#ifndef BLOCK_SCALED_MOE_H
+#define BLOCK_SCALED_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* Status codes (0 = success). */
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, bad size, bad range            */
+#define MOE_ERR_UNSUPPORTED (-2) /* valid layer, but a shape this build rejects  */
+#define MOE_ERR_ALIGNMENT (-3)   /* a device pointer is not 16-byte aligned      */
+#define MOE_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required   */
+#define MOE_ERR_HIP (-5)         /* a HIP launch failed                          */
+
+/* Expert formats (recipe "Overview": NVFP4 in layers 0-39, MXFP8 in 40-47). */
+#define MOE_FMT_NVFP4 1
+#define MOE_FMT_MXFP8 2
+
+/*
+ * Packed expert weights of one matrix kind for E experts, each [N][K] row-major
+ * (K is the reduction dimension), in the canonical byte layout:
+ *   NVFP4: codes  u8 [E][N][K/2]  E2M1, element 2i in the low nibble of byte i
+ *          scales u8 [E][N][K/16] E4M3 (OCP "FN": bias 7, max 448, no inf)
+ *          tensor_scale fp32 [E]  one per expert and matrix (amax / 2688, or 1)
+ *   MXFP8: codes  u8 [E][N][K]    E4M3
+ *          scales u8 [E][N][K/32] E8M0 (2^(c - 127))
+ *          tensor_scale unused (may be NULL)
+ */
+typedef struct moe_packed {
+    int32_t fmt;
+    int32_t E, N, K;
+    uint8_t *codes;
+    uint8_t *scales;
+    float *tensor_scale;
+} moe_packed;
+
+/* Optional debug outputs of moe_forward (each pointer NULL = not written).
+ * S = number of local token-slots (known on the device only; read offsets[n_loc]).
+ * Slot-indexed arrays are in sorted (expert-grouped) order, sized for S <= T*top_k. */
+typedef struct moe_taps {
+    int32_t *counts;       /* [n_loc] slots per local expert                        */
+    int32_t *offsets;      /* [n_loc + 1] exclusive prefix sum of counts            */
+    int32_t *sorted_slot;  /* [T*top_k] slot id t*top_k + j at each sorted position  */
+    uint8_t *a_codes;      /* hidden-state codes [T][D/2] (NVFP4) or [T][D] (MXFP8) */
+    uint8_t *a_scales;     /* [T][D/16] E4M3 (NVFP4) or [T][D/32] E8M0 (MXFP8)      */
+    float *a_tscale;       /* [1] NVFP4 hidden-state tensor scale                   */
+    float *inter;          /* [T*top_k][F] fp32 SwiGLU output before quantisation   */
+    uint8_t *inter_codes;  /* [T*top_k][F/2] or [T*top_k][F]                        */
+    uint8_t *inter_scales; /* [T*top_k][F/16] or [T*top_k][F/32]                    */
+    float *inter_tscale;   /* [1] NVFP4 intermediate tensor scale                   */
+    float *y;              /* [T*top_k][D] fp32 down projection per slot (unweighted) */
+} moe_taps;
+
+/* Stage boundaries at which moe_forward records caller-created events (timing). */
+#define MOE_EV_BEGIN 0        /* before the first kernel of the call          */
+#define MOE_EV_GATE_UP 1      /* just before the gate_up GEMM                 */
+#define MOE_EV_GATE_UP_END 2  /* just after the gate_up GEMM                  */
+#define MOE_EV_DOWN 3         /* just before the down GEMM                    */
+#define MOE_EV_DOWN_END 4     /* just after the down GEMM                     */
+#define MOE_EV_END 5          /* after the last kernel (the combine)          */
+#define MOE_N_EVENTS 6
+
+/* Arguments of moe_forward. */
+typedef struct moe_forward_args {
+    int32_t fmt;              /* MOE_FMT_NVFP4 or MOE_FMT_MXFP8                         */
+    int32_t T, D, F, E;       /* tokens, d_model, d_ff, routed experts                  */
+    int32_t top_k;            /* experts per token (8)                                  */
+    int32_t e_begin, e_end;   /* local expert range [e_begin, e_end) computed here      */
+    const uint16_t *h;        /* bf16 hidden states [T][D]                              */
+    const float *h_amax;      /* NVFP4: max |h| as written by moe_route, or NULL        */
+    const int32_t *topk_idx;  /* [T][top_k] experts per token, distinct within a row    */
+    const float *topk_w;      /* [T][top_k] gate weights                                */
+    moe_packed gate_up;       /* N = 2F, K = D                                          */
+    moe_packed down;          /* N = D,  K = F                                          */
+    float *out;               /* fp32 [T][D]; tokens without a local slot get zeros     */
+    void *workspace;          /* device scratch of moe_forward_workspace_bytes() bytes  */
+    size_t workspace_bytes;
+    const moe_taps *taps;     /* host pointer to a moe_taps, or NULL                    */
+    void *const *events;      /* NULL, or a host array of MOE_N_EVENTS hipEvent_t that are
+                                 recorded on the stream at the MOE_EV_* boundaries      */
+} moe_forward_args;
+
+/* ABI version (MOE_ABI_VERSION) and a static description of a status code. */
+int32_t moe_abi_version(void);
+const char *moe_status_string(int32_t status);
+
+/*
+ * Quantise bf16 expert weights w [E][N][K] into `out` (fmt, E, N, K and the three
+ * buffers set by the caller). NVFP4 (AI Primer, "TL;DR"): per expert, tensor scale
+ * s = amax/2688 (1 if the expert is all zero); per 16-block, r = amax_b / s, scale
+ * candidates E4M3(r/6) and E4M3(r/4), codes E2M1(x / (E4M3 * s)), keep the candidate
+ * with the smaller fp32 squared error (ties keep r/6). MXFP8: per 32-block, E8M0
+ * exponent floor(log2 amax_b) - 8, codes E4M3(x * 2^-exponent). All roundings are
+ * IEEE round-to-nearest-even with saturation to the format's largest finite value.
+ * K must be a multiple of 16 (NVFP4) or 32 (MXFP8).
+ */
+int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
+
+/*
+ * Router (softmax-then-top-k gate, recipe "Overview": 8 of 384 experts per token):
+ *   logits[t][e] = sum over d ascending of h[t][d] * wr[e][d], accumulated in fp32
+ *                  from +0 (each bf16 product is exact in fp32), plus bias[e] if given;
+ *   topk_idx[t]  = the top_k largest logits, ties to the lower expert index, in rank
+ *                  order;
+ *   topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected (fp64,
+ *                  rounded to fp32): the softmax over all E renormalised over the top_k.
+ * h: bf16 [T][D]; wr: bf16 [E][D]; bias: fp32 [E] or NULL; logits: fp32 [T][E]
+ * (written; caller-owned scratch that doubles as an output); h_amax: fp32 [1] or NULL
+ * (if given, receives max |h| over all of h, for moe_forward's NVFP4 tensor scale).
+ * Requires 1 <= top_k <= 8, top_k <= E <= 4096. T = 0 is a no-op.
+ */
+int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t *h,
+                  const uint16_t *wr, const float *bias, float *logits, int32_t *topk_idx,
+                  float *topk_w, float *h_amax, void *stream);
+
+/* Host-only check of moe_forward's arguments (everything but the workspace size). */
+int32_t moe_forward_validate(const moe_forward_args *a);
+
+/* Bytes of device workspace moe_forward needs; depends on the size fields only (fmt, T, D,
+ * F, E, top_k, e_begin, e_end) and is 0 if those are invalid or T = 0. */
+size_t moe_forward_workspace_bytes(const moe_forward_args *a);
+
+/*
+ * MoE layer forward over the local experts [e_begin, e_end):
+ *  1. slots (t, j) with topk_idx[t][j] local are grouped by expert, stable in t*top_k+j;
+ *  2. hidden states are quantised once per token to the layer's format (NVFP4 with
+ *     one tensor scale over all of h, MXFP8 per 32-block);
+ *  3. gate_up GEMM per expert (fp32 accumulation; NVFP4 sums are multiplied by
+ *     fl32(s_h * s_gate_up[e])), then h = SwiGLU = g * u / (1 + exp(-g));
+ *  4. h is quantised to the layer's format (NVFP4: one tensor scale over all S rows);
+ *  5. down GEMM per expert (NVFP4: times fl32(s_inter * s_down[e])) -> y fp32;
+ *  6. out[t] = sum over the token's local slots, j ascending, of topk_w[t][j] * y.
+ * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), 1 <= top_k <= 8,
+ * 0 <= e_begin < e_end <= E. gate_up/down must match fmt and shapes. T = 0 is a no-op.
+ */
+int32_t moe_forward(const moe_forward_args *a, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BLOCK_SCALED_MOE_H */

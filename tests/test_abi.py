@@ -1,0 +1,115 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every function
+include/moe.h declares, and its host-side validation returns the documented status
+codes before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_scaled_moe_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+OK, EINVAL, EUNSUP, EALIGN, EWS = 0, -1, -2, -3, -4
+A16 = 0x10000  # a fake, 16-byte aligned "device" address: never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_header_functions_are_exported_and_bound():
+    lib = moe.lib()
+    names = declared_functions()
+    assert len(names) == 7, names
+    for n in names:
+        assert hasattr(lib, n), f"{n} not exported by libmoe.so"
+        assert n in moe.SIGNATURES, f"{n} has no binding"
+    assert lib.moe_abi_version() == 1
+    assert lib.moe_status_string(EWS) == b"workspace missing or too small"
+
+
+def _args(**over):
+    a = moe.MoeForwardArgs()
+    a.fmt, a.T, a.D, a.F, a.E, a.top_k, a.e_begin, a.e_end = 1, 64, 4096, 2560, 384, 8, 0, 384
+    a.h = a.topk_idx = a.topk_w = a.out = A16
+    a.gate_up = moe.MoePacked(1, 384, 5120, 4096, A16, A16, A16)
+    a.down = moe.MoePacked(1, 384, 4096, 2560, A16, A16, A16)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+def _validate(a):
+    return moe.lib().moe_forward_validate(ctypes.byref(a))
+
+
+def test_forward_validation_accepts_the_workloads():
+    assert _validate(_args()) == OK
+    mx = _args(fmt=2)
+    mx.gate_up = moe.MoePacked(2, 384, 5120, 4096, A16, A16, 0)
+    mx.down = moe.MoePacked(2, 384, 4096, 2560, A16, A16, 0)
+    assert _validate(mx) == OK
+    assert _validate(_args(T=0, h=0, topk_idx=0, topk_w=0, out=0)) == OK  # empty batch
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(fmt=3), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
+    (dict(e_begin=10, e_end=10), EINVAL), (dict(e_end=385), EINVAL), (dict(e_begin=-1), EINVAL),
+    (dict(E=5000), EINVAL), (dict(h=0), EINVAL), (dict(out=0), EINVAL),
+    (dict(D=4000), EUNSUP), (dict(F=2500), EUNSUP),
+    (dict(h=A16 + 2), EALIGN), (dict(out=A16 + 4), EALIGN), (dict(topk_w=A16 + 8), EALIGN),
+])
+def test_forward_validation_rejects(over, status):
+    assert _validate(_args(**over)) == status
+
+
+def test_packed_weights_must_match_the_layer():
+    a = _args()
+    a.gate_up = moe.MoePacked(1, 384, 5120, 2048, A16, A16, A16)  # K != D
+    assert _validate(a) == EINVAL
+    a = _args()
+    a.down = moe.MoePacked(2, 384, 4096, 2560, A16, A16, A16)  # format mismatch
+    assert _validate(a) == EINVAL
+    a = _args()
+    a.gate_up = moe.MoePacked(1, 384, 5120, 4096, A16, A16, 0)  # NVFP4 needs tensor scales
+    assert _validate(a) == EINVAL
+    a = _args()
+    a.down = moe.MoePacked(1, 384, 4096, 2560, A16 + 1, A16, A16)
+    assert _validate(a) == EALIGN
+
+
+def test_forward_rejects_missing_workspace_before_any_launch():
+    a = _args()
+    assert moe.lib().moe_forward(ctypes.byref(a), None) == EWS
+    a.workspace, a.workspace_bytes = A16, 1024
+    assert moe.lib().moe_forward(ctypes.byref(a), None) == EWS
+    assert moe.lib().moe_forward(ctypes.byref(_args(top_k=9)), None) == EINVAL
+
+
+def test_workspace_plan_sizes():
+    ws = moe.lib().moe_forward_workspace_bytes
+    small = ws(ctypes.byref(_args()))
+    big = ws(ctypes.byref(_args(T=8192, e_end=96)))
+    assert 0 < small < big
+    # dominated by the fp32 per-slot down projection y [T*k][D]
+    assert big >= 8192 * 8 * 4096 * 4
+    assert ws(ctypes.byref(_args(top_k=0))) == 0
+
+
+def test_route_and_quantize_validate_on_the_host():
+    lib = moe.lib()
+    p = ctypes.c_void_p
+    assert lib.moe_route(4, 64, 16, 9, p(A16), p(A16), None, p(A16), p(A16), p(A16), None, None) == EINVAL
+    assert lib.moe_route(4, 64, 16, 8, p(A16 + 2), p(A16), None, p(A16), p(A16), p(A16), None, None) == EALIGN
+    assert lib.moe_route(0, 64, 16, 8, None, None, None, None, None, None, None, None) == OK
+    bad = moe.MoePacked(1, 2, 16, 24, A16, A16, A16)  # NVFP4 K must be a multiple of 16
+    assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
+    bad = moe.MoePacked(2, 2, 16, 48, A16, A16, 0)     # MXFP8 K must be a multiple of 32
+    assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
+    bad = moe.MoePacked(1, 2, 16, 32, A16, A16, 0)     # NVFP4 needs tensor scales
+    assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL

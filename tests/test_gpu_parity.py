@@ -1,0 +1,181 @@
+"""GPU path against the CPU oracle, through the C ABI (needs an MI355X).
+
+Bit-exact: quantised weight codes, scales and tensor scales; router logits and top-k
+indices; counts, offsets and the sorted slot order; hidden-state codes and scales;
+the intermediate codes and scales given the GPU's own pre-quantisation values.
+Within tolerance: gate weights (1e-6 relative), the SwiGLU intermediate, and the
+layer output (max |error| <= 2e-3 x RMS of the oracle's output).
+Sizes span several tiles in M, N and K with ragged tails; the layer cases cover both
+formats, both tile shapes (decode and prefill), an expert-parallel share and skewed
+routing.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_scaled_moe_amd as moe
+import oracle
+import synth
+from gpu_util import case_inputs, check_intermediate_codes, host, report, rms, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    moe.lib()
+
+
+# ------------------------------------------------------------------ weights
+def _adversarial_masters(E, N, K, seed):
+    """bf16 masters with an all-zero expert, zero blocks, saturating and tiny values."""
+    wl = synth.custom("nvfp4", T=1, D=K, F=N // 2, E=E, seed=seed)
+    w = wl.gate_up_master(0, E).copy()
+    w[0] = 0                                   # all-zero expert: tensor scale 1, all codes 0
+    w[1, :, :32] = 0                           # zero blocks in a live expert
+    w[1, 3, 5] = 0x8000                        # a negative zero
+    big = synth.normal_bf16(seed, 9, 0, N * K, 300.0).reshape(N, K)
+    w[E - 1] = big                             # large values (tensor scale >> 1)
+    if E > 3:
+        tiny = synth.normal_bf16(seed, 10, 0, N * K, 1e-6).reshape(N, K)
+        w[2] = tiny                            # tiny values next to the live experts
+    return w
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("shape", [(5, 256, 512), (2, 96, 2048)])
+def test_quantize_weights_bitexact(fmt, shape):
+    E, N, K = shape
+    w = _adversarial_masters(E, N, K, seed=7)
+    report("quantize_weights", fmt=fmt, E=E, N=N, K=K)
+    got = moe.quantize_weights(fmt, to_dev(w))
+    torch.cuda.synchronize()
+    ref = oracle.quantize_weights(fmt, w)
+    assert np.array_equal(host(got.codes), ref["codes"]), "codes differ"
+    assert np.array_equal(host(got.scales), ref["scales"]), "scales differ"
+    if fmt == "nvfp4":
+        assert np.array_equal(host(got.tensor_scale).view(np.uint32), ref["tensor_scale"].view(np.uint32))
+
+
+# ------------------------------------------------------------------ router
+ROUTER_CASES = [
+    dict(T=37, D=256, E=64, skew=False),      # small-T kernel, ragged token tile
+    dict(T=64, D=4096, E=384, skew=False),    # decode shape
+    dict(T=1030, D=512, E=384, skew=True),    # mid-T kernel, biased logits
+    dict(T=8200, D=256, E=384, skew=False),   # large-T kernel, ragged tail
+]
+
+
+@pytest.mark.parametrize("c", ROUTER_CASES, ids=lambda c: f"T{c['T']}_D{c['D']}_E{c['E']}")
+def test_route_bitexact(c):
+    wl = synth.custom("nvfp4", T=c["T"], D=c["D"], F=128, E=c["E"], skew=c["skew"], seed=11)
+    h, wr, bias = wl.hidden(), wl.router_weight(), wl.router_bias()
+    report("route", **c)
+    idx, w, logits, amax = moe.route(to_dev(h), to_dev(wr), 8, None if bias is None else to_dev(bias), True)
+    torch.cuda.synchronize()
+    o_idx, o_w, o_lg = oracle.route(h, wr, k=8, bias=bias, want_logits=True)
+    assert np.array_equal(host(logits).view(np.uint32), o_lg.view(np.uint32)), "logits differ"
+    assert np.array_equal(host(idx), o_idx), "top-k indices differ"
+    np.testing.assert_allclose(host(w), o_w, rtol=1e-6, atol=0)
+    ref_amax = np.abs(synth.bf16_to_f32(h)).max()
+    assert host(amax)[0] == ref_amax
+
+
+# ------------------------------------------------------------------ layer
+LAYER_CASES = [
+    dict(name="tiny-nvfp4", wl=synth.WORKLOADS[0]),
+    dict(name="decode-nvfp4", wl=synth.custom("nvfp4", T=40, D=256, F=256, E=16, seed=21)),
+    dict(name="decode-mxfp8", wl=synth.custom("mxfp8", T=40, D=256, F=256, E=16, seed=22)),
+    dict(name="decode-nvfp4-k384", wl=synth.custom("nvfp4", T=24, D=512, F=384, E=12, seed=23)),
+    dict(name="decode-mxfp8-k384", wl=synth.custom("mxfp8", T=24, D=512, F=384, E=12, seed=24)),
+    dict(name="prefill-nvfp4", wl=synth.custom("nvfp4", T=300, D=256, F=256, E=16, seed=25)),
+    dict(name="prefill-mxfp8", wl=synth.custom("mxfp8", T=300, D=256, F=256, E=16, seed=26)),
+    dict(name="ep-share-nvfp4", wl=synth.custom("nvfp4", T=64, D=256, F=128, E=32, e_begin=8, e_end=20, seed=27)),
+    dict(name="ep-share-prefill-mxfp8",
+         wl=synth.custom("mxfp8", T=400, D=256, F=128, E=24, e_begin=0, e_end=6, seed=28)),
+    dict(name="skew-mxfp8", wl=synth.custom("mxfp8", T=256, D=256, F=256, E=64, skew=True, seed=29)),
+    dict(name="skew-prefill-nvfp4", wl=synth.custom("nvfp4", T=600, D=256, F=128, E=16, skew=True, seed=30)),
+]
+
+
+@pytest.mark.parametrize("c", LAYER_CASES, ids=lambda c: c["name"])
+def test_forward_parity(c):
+    wl = c["wl"]
+    fmt, T, D, F, E, k = wl.fmt, wl.T, wl.D, wl.F, wl.E, wl.k
+    eb, ee = wl.e_begin, wl.local_end
+    h, wr, bias, gu_m, dn_m = case_inputs(wl)
+    report("forward", case=c["name"], fmt=fmt, T=T, D=D, F=F, E=E, local=(eb, ee))
+
+    # GPU: quantise, route, forward with every tap
+    gu = moe.quantize_weights(fmt, to_dev(gu_m))
+    dn = moe.quantize_weights(fmt, to_dev(dn_m))
+    d_h = to_dev(h)
+    idx, w, _, amax = moe.route(d_h, to_dev(wr), k, None if bias is None else to_dev(bias), True)
+    layer = moe.Layer(fmt, T, D, F, E, gu, dn, top_k=k, e_begin=eb, e_end=ee)
+    taps = layer.enable_taps()
+    out = host(layer.forward(d_h, idx, w, h_amax=amax if fmt == "nvfp4" else None))
+    torch.cuda.synchronize()
+    tp = {k_: host(v) for k_, v in taps.items()}
+
+    # oracle: its own quantised weights, routing and layer
+    o_gu, o_dn = oracle.quantize_weights(fmt, gu_m), oracle.quantize_weights(fmt, dn_m)
+    o_idx, o_w = oracle.route(h, wr, k=k, bias=bias)
+    assert np.array_equal(host(idx), o_idx)
+    ref, otp = oracle.moe_forward(fmt, h, o_idx, o_w, D=D, F=F, E=E, e_begin=eb, e_end=ee, gate_up=o_gu,
+                                  down=o_dn, taps=True)
+    counts, offs, ss = oracle.permute(o_idx, eb, ee)
+    S = int(offs[-1])
+
+    # bit-exact: permutation and hidden-state quantisation
+    assert np.array_equal(tp["counts"], counts)
+    assert np.array_equal(tp["offsets"], offs)
+    assert np.array_equal(tp["sorted_slot"][:S], ss)
+    assert np.array_equal(tp["a_codes"], otp["a_codes"]), "hidden-state codes differ"
+    assert np.array_equal(tp["a_scales"], otp["a_scales"]), "hidden-state scales differ"
+    if fmt == "nvfp4":
+        assert tp["a_tscale"][0] == otp["a_tscale"][0]
+
+    # intermediate: values close to the oracle's, codes exact given the GPU's own values
+    g_inter = tp["inter"][:S]
+    scale_i = np.abs(otp["inter"]).max()
+    inter_err = float(np.abs(g_inter - otp["inter"]).max()) / scale_i
+    check_intermediate_codes(fmt, g_inter, tp["inter_codes"][:S], tp["inter_scales"][:S],
+                             tp["inter_tscale"][0] if fmt == "nvfp4" else None)
+    flips = int(np.count_nonzero(tp["inter_codes"][:S] != otp["inter_codes"]))
+    assert inter_err < 1e-4, f"SwiGLU intermediate differs by {inter_err:.2e} of its max"
+
+    # output
+    r = rms(ref)
+    err = float(np.abs(out - ref).max())
+    report("  result", S=S, inter_rel=f"{inter_err:.2e}", independent_code_flips=flips,
+           out_err_over_rms=f"{err / r:.2e}")
+    assert err <= 2e-3 * r, f"max |out - oracle| = {err:.3e} > 2e-3 x RMS ({r:.3e})"
+    has_local = ((o_idx >= eb) & (o_idx < ee)).any(1)
+    assert not out[~has_local].any(), "tokens without a local slot must be zero"
+
+
+def test_empty_batch_is_a_no_op():
+    wl = synth.WORKLOADS[0]
+    gu = moe.quantize_weights("nvfp4", to_dev(wl.gate_up_master(0, wl.E)))
+    dn = moe.quantize_weights("nvfp4", to_dev(wl.down_master(0, wl.E)))
+    layer = moe.Layer("nvfp4", 0, wl.D, wl.F, wl.E, gu, dn)
+    out = torch.empty((0, wl.D), dtype=torch.float32, device="cuda")
+    empty_i = torch.empty((0, 8), dtype=torch.int32, device="cuda")
+    empty_w = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    empty_h = torch.empty((0, wl.D), dtype=torch.int16, device="cuda")
+    layer.forward(empty_h, empty_i, empty_w, out=out)
+    torch.cuda.synchronize()
+
+
+def test_repeat_calls_are_deterministic():
+    """Same inputs, same bytes: the forward reuses its workspace without stale state."""
+    wl = synth.custom("nvfp4", T=40, D=256, F=256, E=16, seed=41)
+    h, wr, _, gu_m, dn_m = case_inputs(wl)
+    gu, dn = moe.quantize_weights("nvfp4", to_dev(gu_m)), moe.quantize_weights("nvfp4", to_dev(dn_m))
+    d_h = to_dev(h)
+    idx, w, _, _ = moe.route(d_h, to_dev(wr), 8)
+    layer = moe.Layer("nvfp4", wl.T, wl.D, wl.F, wl.E, gu, dn)
+    a = host(layer.forward(d_h, idx, w)).copy()
+    b = host(layer.forward(d_h, idx, w))
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
