@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--workload", type=int, default=1, help="index into the five synthetic workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-target-s", type=float, default=10.0)
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer is built for one "
@@ -235,6 +237,17 @@ def main():
     print(f"[bench] {ms_step:.3f} ms/step (forward {fwd_ms:.3f} ms: gate_up {gate_up_ms:.3f} ms, down "
           f"{down_ms:.3f} ms); S={S}, {touched} experts touched, layer {layer_bytes / 1e9:.3f} GB "
           f"-> {layer_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s whole-step", file=sys.stderr, flush=True)
+
+    if args.calib_copy_mb:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters
+        n = args.calib_copy_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:
