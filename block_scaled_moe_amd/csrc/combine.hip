@@ -20,16 +20,26 @@ __global__ void __launch_bounds__(256) combine_kernel(int32_t T, int32_t D, int3
     if (q >= (int64_t)T * per_row) return;
     const int64_t t = q / per_row;
     const int64_t c = (q % per_row) * 4;
+    // all slot positions and weights first (independent loads), then the rows
+    int32_t pos[8];
+    double wj[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        pos[j] = j < k ? slot_pos[t * k + j] : -1;
+        wj[j] = j < k ? (double)w[t * k + j] : 0.0;
+    }
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        v[j] = pos[j] >= 0 ? *reinterpret_cast<const float4 *>(y + (int64_t)pos[j] * D + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-    for (int j = 0; j < k; ++j) {
-        const int32_t pos = slot_pos[t * k + j];
-        if (pos < 0) continue;
-        const double wj = (double)w[t * k + j];
-        const float4 v = *reinterpret_cast<const float4 *>(y + (int64_t)pos * D + c);
-        a0 += wj * (double)v.x;
-        a1 += wj * (double)v.y;
-        a2 += wj * (double)v.z;
-        a3 += wj * (double)v.w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        if (pos[j] < 0) continue;
+        a0 += wj[j] * (double)v[j].x;
+        a1 += wj[j] * (double)v[j].y;
+        a2 += wj[j] * (double)v[j].z;
+        a3 += wj[j] * (double)v[j].w;
     }
     *reinterpret_cast<float4 *>(out + t * D + c) = make_float4((float)a0, (float)a1, (float)a2, (float)a3);
 }

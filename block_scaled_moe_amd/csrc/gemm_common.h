@@ -1,0 +1,64 @@
+// gemm_common.h - exact 16-bit expansion of NVFP4 / MXFP8 codes for the gfx950 MFMAs,
+// shared by the grouped GEMM kernels (tiled and streaming).
+//
+// NVFP4 (E2M1 codes, E4M3 scale per 16; vLLM recipe "thinkingmachines/Inkling-2-Small",
+// section "Overview"): c * s has at most 6 significant bits and lies in [2^-10, 2688],
+// inside fp16's normal range, so v_cvt_scalef32_pk_f16_fp4 (whose scale operand only
+// contributes an exponent, so it is given 1.0) followed by v_pk_mul_f16 by the E4M3
+// scale forms each value exactly. MXFP8 (E4M3 codes, E8M0 scale per 32): E4M3 * 2^e has
+// 4 significant bits; v_cvt_scalef32_pk_bf16_fp8 applies the E8M0 exponent exactly.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+namespace gemm_detail {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// exact fp16 of a non-negative E4M3 scale byte (normal: rebias 7 -> 15; subnormal m*2^-9)
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t c) {
+    const uint32_t e = (c >> 3) & 15, m = c & 7;
+    if (e == 0) return (_Float16)((float)m * 0x1p-9f);
+    return __builtin_bit_cast(_Float16, (uint16_t)(((e + 8) << 10) | (m << 7)));
+}
+
+// 8 E2M1 codes (element i in nibble i) times the E4M3 scale s -> 8 exact fp16
+__device__ __forceinline__ half8 dequant_nvfp4(uint32_t codes, _Float16 s) {
+    const half2_t ss = {s, s};
+    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * ss;
+    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * ss;
+    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * ss;
+    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * ss;
+    half8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// 8 E4M3 codes (element i in byte i) times 2^(e - 127) -> 8 exact bf16; `scale` is the
+// float whose exponent field is the E8M0 byte e (the convert uses only the exponent).
+__device__ __forceinline__ bf16x8 dequant_mxfp8(u32x2 codes, float scale) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, false);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.x, scale, true);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, false);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes.y, scale, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// SwiGLU g * u / (1 + exp(-g)) in fp64, rounded once to fp32
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return (float)((double)g * (double)u / (1.0 + exp(-(double)g)));
+}
+
+}  // namespace gemm_detail
+}  // namespace moe

@@ -1,0 +1,279 @@
+// gemm_stream.hip - grouped expert GEMMs for decode-sized batches: few rows per expert,
+// so the layer is bound by streaming the packed expert weights from HBM once.
+//
+// Same arithmetic as the tiled kernels (exact 16-bit expansion of NVFP4 / MXFP8 codes,
+// 16x16x32 MFMA, fp32 accumulation; see gemm_common.h), organised for bandwidth:
+//  - a workgroup owns one M-tile (<= 16 sorted rows of one expert) and 64 weight rows
+//    (gate_up: 32 gate rows and the 32 matching up rows; down: 64 output columns);
+//  - its 4 waves split K into quarters, and each lane streams its weight bytes straight
+//    from HBM into registers in the MFMA operand layout (16-byte loads; the 4 lanes of a
+//    row cover 64 contiguous bytes per NVFP4 group, 128 per MXFP8 group), keeping a
+//    window of W groups of loads in flight; nothing goes through LDS and the K loop has
+//    no barriers;
+//  - the wave's block scales are staged once in LDS with full-line loads;
+//  - the four partial sums are added in a fixed order through LDS before the epilogue,
+//    so results are deterministic.
+// K-slot mapping inside a 128-wide group of a wave's K quarter: lane group g = lane/16
+// holds k = 32g + 8j .. 32g + 8j + 7 for MFMA step j; the activation fragment of lane
+// (row r, g) is read at the same k from the exact 16-bit activation row.
+#include "formats.h"
+#include "gemm_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+using namespace gemm_detail;
+
+constexpr int kSub = 4;    // 16-row weight subtiles per workgroup
+constexpr int kRows = 64;  // weight rows per workgroup
+
+// Tuning: K groups of weight loads in flight per wave, and an optional occupancy
+// target (waves per SIMD) that caps the registers the compiler may use.
+#ifndef MOE_STREAM_W_NV
+#define MOE_STREAM_W_NV 4
+#endif
+#ifndef MOE_STREAM_W_MX
+#define MOE_STREAM_W_MX 2
+#endif
+#ifndef MOE_STREAM_WAVES_PER_EU
+#define MOE_STREAM_WAVES_PER_EU 0
+#endif
+#if MOE_STREAM_WAVES_PER_EU > 0
+#define MOE_STREAM_OCCUPANCY __attribute__((amdgpu_waves_per_eu(MOE_STREAM_WAVES_PER_EU)))
+#else
+#define MOE_STREAM_OCCUPANCY
+#endif
+
+template <bool NV, bool GATE_UP, int G>  // G = 128-wide K groups per wave (K = 512 G)
+__global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(const GemmArgs p) {
+    using Frag = typename std::conditional<NV, half8, bf16x8>::type;
+    constexpr int NQ = NV ? 1 : 2;                 // 16-byte code loads per lane, group and subtile
+    constexpr int W = NV ? MOE_STREAM_W_NV : MOE_STREAM_W_MX;  // groups of loads in flight
+    constexpr int BLK = NV ? 16 : 32;
+    constexpr int SBW = G * 128 / BLK;             // scale bytes per weight row in a wave's K quarter
+    __shared__ __attribute__((aligned(16))) uint8_t s_scale[4][kRows * SBW];
+    __shared__ __attribute__((aligned(16))) float s_red[4][kSub][64][4];
+    __shared__ float s_epi[16][33];                // MXFP8 gate_up: SwiGLU tile, 16 rows x 32 f
+
+    const int tile = blockIdx.x;
+    if (tile >= p.ctrl->n_tiles) return;
+    const int el = p.tile_expert[tile];
+    const int p0 = p.tile_row0[tile];
+    const int rows = min(16, p.offsets[el + 1] - p0);
+    const int e = p.e_begin + el;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int K = p.K;
+    const int F = p.N / 2;
+    const int n0 = GATE_UP ? blockIdx.y * (kRows / 2) : blockIdx.y * kRows;
+    const int kw = wave * G * 128;  // first k of this wave's quarter
+    const int64_t row_bytes = NV ? K / 2 : K;
+
+    auto wrow_of = [&](int r) -> int {  // weight row of tile row r (0..63)
+        return GATE_UP ? (r < kRows / 2 ? n0 + r : F + n0 + (r - kRows / 2)) : n0 + r;
+    };
+
+    // ---- block scales of this wave's quarter: global -> registers now, -> LDS after the
+    //      first weight loads are in flight (full-line loads, consecutive lanes = consecutive dwords)
+    constexpr int SREG = kRows * SBW / 4 / 64;
+    static_assert(kRows * SBW / 4 % 64 == 0, "scale dwords tile the wave");
+    uint32_t sreg[SREG];
+    {
+        const uint8_t *sbase = p.w_scales + (int64_t)e * p.N * (K / BLK) + kw / BLK;
+#pragma unroll
+        for (int i = 0; i < SREG; ++i) {
+            const int d = lane + 64 * i;
+            const int r = d / (SBW / 4), q = d % (SBW / 4);
+            sreg[i] = *reinterpret_cast<const uint32_t *>(sbase + (int64_t)wrow_of(r) * (K / BLK) + 4 * q);
+        }
+    }
+
+    // ---- weight code pointers of this lane (one per subtile) and activation row
+    const uint8_t *bsrc[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s)
+        bsrc[s] = p.w_codes + ((int64_t)e * p.N + wrow_of(16 * s + r16)) * row_bytes + (NV ? kw / 2 : kw) +
+                  (NV ? 16 : 32) * g;
+    const uint8_t *asrc = nullptr;
+    if (r16 < rows) {
+        const int pos = p0 + r16;
+        const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
+        asrc = static_cast<const uint8_t *>(p.a_vals) + (arow * K + kw + 32 * g) * 2;
+    }
+
+    u32x4 bq[G][kSub][NQ];
+    u32x4 aq[G][4];
+    auto load_group = [&](int jj) {
+#pragma unroll
+        for (int s = 0; s < kSub; ++s)
+#pragma unroll
+            for (int q = 0; q < NQ; ++q)
+                bq[jj][s][q] = *reinterpret_cast<const u32x4 *>(bsrc[s] + (NV ? 64 : 128) * jj + 16 * q);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            aq[jj][j] = asrc ? *reinterpret_cast<const u32x4 *>(asrc + 256 * jj + 16 * j) : (u32x4){0u, 0u, 0u, 0u};
+    };
+
+    float4_t acc[kSub];
+#pragma unroll
+    for (int s = 0; s < kSub; ++s) acc[s] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int jj = 0; jj < W && jj < G; ++jj) load_group(jj);
+#pragma unroll
+    for (int i = 0; i < SREG; ++i) {
+        const int d = lane + 64 * i;
+        *reinterpret_cast<uint32_t *>(&s_scale[wave][(d / (SBW / 4)) * SBW + 4 * (d % (SBW / 4))]) = sreg[i];
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's scale stores are done
+    __builtin_amdgcn_wave_barrier();     // and no LDS read is hoisted above them
+
+#pragma unroll
+    for (int jj = 0; jj < G; ++jj) {
+        if (jj + W < G) load_group(jj + W);
+        _Float16 sh[kSub][2];
+        float sm[kSub];
+#pragma unroll
+        for (int s = 0; s < kSub; ++s) {
+            const uint8_t *srow = &s_scale[wave][(16 * s + r16) * SBW];
+            if (NV) {
+                const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
+                sh[s][0] = e4m3_to_f16(two & 0xff);
+                sh[s][1] = e4m3_to_f16(two >> 8);
+            } else {
+                sm[s] = __uint_as_float((uint32_t)srow[4 * jj + g] << 23);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const Frag af = __builtin_bit_cast(Frag, aq[jj][j]);
+#pragma unroll
+            for (int s = 0; s < kSub; ++s) {
+                if constexpr (NV) {
+                    const half8 bf = dequant_nvfp4(bq[jj][s][0][j], sh[s][j >> 1]);
+                    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[s], 0, 0, 0);
+                } else {
+                    const u32x4 w4 = bq[jj][s][j >> 1];
+                    const u32x2 w2 = (j & 1) ? (u32x2){w4.z, w4.w} : (u32x2){w4.x, w4.y};
+                    const bf16x8 bf = dequant_mxfp8(w2, sm[s]);
+                    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[s], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // ---- cross-wave reduction in a fixed order, then the epilogue
+#pragma unroll
+    for (int s = 0; s < kSub; ++s)
+        *reinterpret_cast<float4_t *>(&s_red[wave][s][lane][0]) = acc[s];
+    __syncthreads();
+    auto reduced = [&](int s) -> float4_t {
+        float4_t v = *reinterpret_cast<const float4_t *>(&s_red[0][s][lane][0]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const float4_t *>(&s_red[w][s][lane][0]);
+        return v;
+    };
+    const float sc = NV ? p.a_tscale[0] * p.w_tscale[e] : 1.0f;
+    if (GATE_UP) {
+        // waves 0 and 1: gate subtile w with up subtile w + 2 (16 f columns each)
+        if (wave < 2) {
+            const float4_t gv = reduced(wave), uv = reduced(wave + 2);
+            const int fl = 16 * wave + r16;  // f inside the tile
+            uint32_t amax = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 4 * g + i;
+                const float hv = swiglu(gv[i] * sc, uv[i] * sc);
+                if (NV) {
+                    if (m < rows) {
+                        p.out_f32[(int64_t)(p0 + m) * F + n0 + fl] = hv;
+                        amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
+                    }
+                } else {
+                    s_epi[m][fl] = hv;
+                }
+            }
+            if (NV) {
+                for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+                if (lane == 0 && amax) atomicMax(p.amax_bits, amax);
+            }
+        }
+        if (!NV) {
+            __syncthreads();
+            // one 32-block of the MXFP8 intermediate per tile row
+            const int m = threadIdx.x;
+            if (m < rows) {
+                float x[32];
+#pragma unroll
+                for (int i = 0; i < 32; ++i) x[i] = s_epi[m][i];
+                uint32_t cw[8];
+                const int sc8 = mxfp8_quant_block(x, cw);
+                const int64_t row = p0 + m;
+                u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + n0);
+                dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
+                p.o_scales[row * (F / 32) + n0 / 32] = (uint8_t)sc8;
+                const float s2 = ldexpf(1.0f, sc8 - 127);
+                uint32_t *dq = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.o_vals) + (row * F + n0) * 2);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int c0 = (cw[i / 2] >> (16 * (i & 1))) & 0xff, c1 = (cw[i / 2] >> (16 * (i & 1) + 8)) & 0xff;
+                    const uint32_t b0 = (__float_as_uint(e4m3_value_pos(c0 & 0x7f) * s2) >> 16) | ((uint32_t)(c0 & 0x80) << 8);
+                    const uint32_t b1 = (__float_as_uint(e4m3_value_pos(c1 & 0x7f) * s2) >> 16) | ((uint32_t)(c1 & 0x80) << 8);
+                    dq[i] = b0 | (b1 << 16);
+                }
+                if (p.o_tap) {
+                    float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + n0);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                }
+            }
+        }
+    } else {
+        // wave w writes output subtile w (16 columns)
+        const float4_t v = reduced(wave);
+        const int n = n0 + 16 * wave + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * g + i;
+            if (m < rows) p.out_f32[(int64_t)(p0 + m) * p.N + n] = NV ? v[i] * sc : v[i];
+        }
+    }
+}
+
+template <bool NV, bool GATE_UP, int G>
+hipError_t launch_g(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
+    const int n_tiles_n = GATE_UP ? (a.N / 2) / (kRows / 2) : a.N / kRows;
+    hipLaunchKernelGGL((stream_gemm_kernel<NV, GATE_UP, G>), dim3((unsigned)max_tiles, (unsigned)n_tiles_n),
+                       dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+template <bool NV, bool GATE_UP>
+hipError_t launch_k(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
+    switch (a.K / 512) {
+        case 1: return launch_g<NV, GATE_UP, 1>(a, max_tiles, s);
+        case 2: return launch_g<NV, GATE_UP, 2>(a, max_tiles, s);
+        case 3: return launch_g<NV, GATE_UP, 3>(a, max_tiles, s);
+        case 4: return launch_g<NV, GATE_UP, 4>(a, max_tiles, s);
+        case 5: return launch_g<NV, GATE_UP, 5>(a, max_tiles, s);
+        case 6: return launch_g<NV, GATE_UP, 6>(a, max_tiles, s);
+        case 7: return launch_g<NV, GATE_UP, 7>(a, max_tiles, s);
+        case 8: return launch_g<NV, GATE_UP, 8>(a, max_tiles, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up) {
+    return K % 512 == 0 && K / 512 >= 1 && K / 512 <= 8 && (gate_up ? (N / 2) % 32 == 0 : N % 64 == 0);
+}
+
+hipError_t launch_stream_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s) {
+    if (nvfp4) return gate_up ? launch_k<true, true>(a, max_tiles, s) : launch_k<true, false>(a, max_tiles, s);
+    return gate_up ? launch_k<false, true>(a, max_tiles, s) : launch_k<false, false>(a, max_tiles, s);
+}
+
+}  // namespace moe

@@ -60,6 +60,10 @@ struct PermuteArgs {
     Ctrl *ctrl;
 };
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
+// one-workgroup variant for T*k <= 8192 and <= 1024 local experts; also clears the
+// control block's accumulators (no separate fill needed)
+bool permute_small_ok(int32_t T, int32_t k, int32_t n_loc);
+hipError_t launch_permute_small(const PermuteArgs &a, hipStream_t s);
 
 // ---- grouped GEMMs (gemm.hip)
 struct GemmArgs {
@@ -86,6 +90,9 @@ enum class GemmShape { Decode, Prefill };
 hipError_t launch_grouped_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, GemmShape shape,
                                int32_t max_tiles, hipStream_t s);
 int32_t gemm_bm(GemmShape shape);
+// decode-shaped streaming variant (gemm_stream.hip): 16-row M-tiles, K a multiple of 512
+bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
+hipError_t launch_stream_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int32_t T, int32_t D, int32_t k, const int32_t *slot_pos, const float *w,

@@ -43,7 +43,7 @@ Plan make_plan(const moe_forward_args *a) {
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
     p.bm = gemm_bm(p.shape);
     int32_t ct = (int32_t)(T / 256);
-    p.chunk_tokens = ct < 1 ? 1 : (ct > 64 ? 64 : ct);
+    p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
     p.max_tiles = (int32_t)(p.n_loc + TK / p.bm + 1);
     size_t off = 0;
@@ -72,6 +72,12 @@ Plan make_plan(const moe_forward_args *a) {
     p.y = take(sizeof(float) * TK * D);
     p.total = off;
     return p;
+}
+
+hipError_t run_gemm(const GemmArgs &g, bool nv, bool gate_up, const Plan &P, hipStream_t s) {
+    if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
+        return launch_stream_gemm(g, nv, gate_up, P.max_tiles, s);
+    return launch_grouped_gemm(g, nv, gate_up, P.shape, P.max_tiles, s);
 }
 
 int32_t check_packed(const moe_packed &w, int32_t fmt, int32_t E, int32_t N, int32_t K) {
@@ -121,7 +127,7 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
 int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t *h, const uint16_t *wr,
                   const float *bias, float *logits, int32_t *topk_idx, float *topk_w, float *h_amax,
                   void *stream) {
-    if (T < 0 || D <= 0 || E <= 0 || E > 4096 || top_k < 1 || top_k > 8 || top_k > E) return MOE_ERR_INVALID_ARG;
+    if (T < 0 || D <= 0 || E <= 0 || E > 1024 || top_k < 1 || top_k > 8 || top_k > E) return MOE_ERR_INVALID_ARG;
     if (T == 0) return MOE_OK;
     if (!h || !wr || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
     if (!aligned16(h) || !aligned16(wr) || !aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
@@ -197,7 +203,8 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         return a->events ? hipEventRecord((hipEvent_t)a->events[i], s) : hipSuccess;
     };
     MOE_TRY(mark(MOE_EV_BEGIN));
-    MOE_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(ctrl), 0u, sizeof(Ctrl) / 4, s));
+    const bool small = permute_small_ok(T, k, P.n_loc);
+    if (!small) MOE_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(ctrl), 0u, sizeof(Ctrl) / 4, s));
 
     // 1. stable grouping of the local slots and the GEMM tile list
     PermuteArgs pa{};
@@ -218,7 +225,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     pa.sorted_slot = I32(P.sorted_slot);
     pa.slot_pos = I32(P.slot_pos);
     pa.ctrl = ctrl;
-    MOE_TRY(launch_permute(pa, s));
+    MOE_TRY(small ? launch_permute_small(pa, s) : launch_permute(pa, s));
 
     // 2. hidden states quantised once per token
     if (nv) {
@@ -255,7 +262,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         g.out_f32 = F32(P.inter32);
         g.amax_bits = &ctrl->amax_i;
         MOE_TRY(mark(MOE_EV_GATE_UP));
-        MOE_TRY(launch_grouped_gemm(g, true, true, P.shape, P.max_tiles, s));
+        MOE_TRY(run_gemm(g, true, true, P, s));
         MOE_TRY(mark(MOE_EV_GATE_UP_END));
         // 4. NVFP4 intermediate: one tensor scale over all S rows
         MOE_TRY(launch_quant_inter_nvfp4(F32(P.inter32), TK, F, ctrl, U8(P.i_codes), U8(P.i_scales), F16(P.i16),
@@ -266,7 +273,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         g.o_scales = U8(P.i_scales);
         g.o_tap = a->taps ? a->taps->inter : nullptr;
         MOE_TRY(mark(MOE_EV_GATE_UP));
-        MOE_TRY(launch_grouped_gemm(g, false, true, P.shape, P.max_tiles, s));
+        MOE_TRY(run_gemm(g, false, true, P, s));
         MOE_TRY(mark(MOE_EV_GATE_UP_END));
     }
 
@@ -287,7 +294,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     d.a_vals = ws + P.i16;
     d.a_tscale = nv ? F32(P.i_tscale) : nullptr;
     MOE_TRY(mark(MOE_EV_DOWN));
-    MOE_TRY(launch_grouped_gemm(d, nv, false, P.shape, P.max_tiles, s));
+    MOE_TRY(run_gemm(d, nv, false, P, s));
     MOE_TRY(mark(MOE_EV_DOWN_END));
 
     // 6. weighted combine

@@ -63,6 +63,37 @@ __device__ int32_t block_exclusive_scan(int32_t *v, int n, int32_t *part) {
     return total;
 }
 
+// In-place exclusive prefix sum of v[0..n) by one workgroup of kSmall threads
+// (n <= 4 * kSmall); returns the total. part must hold kScanThreads entries.
+template <int kSmall>
+__device__ int32_t small_scan_impl(int32_t *v, int n, int32_t *part) {
+    const int tid = threadIdx.x;
+    const int per = (n + kSmall - 1) / kSmall;
+    const int b = tid * per, e = min(b + per, n);
+    int32_t sum = 0;
+    for (int i = b; i < e; ++i) sum += v[i];
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < kSmall; off <<= 1) {
+        const int32_t add = tid >= off ? part[tid - off] : 0;
+        __syncthreads();
+        part[tid] += add;
+        __syncthreads();
+    }
+    int32_t run = part[tid] - sum;
+    for (int i = b; i < e; ++i) {
+        const int32_t x = v[i];
+        v[i] = run;
+        run += x;
+    }
+    const int32_t total = part[kSmall - 1];
+    __syncthreads();
+    return total;
+}
+__device__ __forceinline__ int32_t small_exclusive_scan(int32_t *v, int n, int32_t *part) {
+    return small_scan_impl<256>(v, n, part);
+}
+
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(PermuteArgs a) {
     __shared__ int32_t cnt[4096];
     __shared__ int32_t tiles[4096];
@@ -133,7 +164,103 @@ __global__ void __launch_bounds__(64) scatter_kernel(PermuteArgs a, int32_t n_sl
     }
 }
 
+// Whole permutation in one workgroup for small batches (T*k <= 8192 slots, <= 1024
+// local experts): per-wave histograms of four contiguous quarters of the slots, the
+// exclusive scans and the tile list, then each wave scatters its quarter with the
+// ballot ranking, starting from its own per-expert bases. Also clears the control
+// block's accumulators, so no separate fill is needed.
+constexpr int kSmallThreads = 256;
+constexpr int kSmallMaxLocal = 1024;
+
+__global__ void __launch_bounds__(kSmallThreads) permute_small_kernel(PermuteArgs a) {
+    __shared__ int32_t cnt[4][kSmallMaxLocal];  // per-wave counts, then per-wave bases
+    __shared__ int32_t tot[kSmallMaxLocal];
+    __shared__ int32_t tiles[kSmallMaxLocal];
+    __shared__ int32_t part[kScanThreads];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int n = a.n_loc;
+    const int32_t n_slots = a.T * a.k;
+    const int32_t q = (n_slots + 3) / 4;  // slots per wave quarter
+    const int32_t s0 = wave * q, s1 = min(n_slots, s0 + q);
+    for (int i = tid; i < 4 * kSmallMaxLocal; i += kSmallThreads) (&cnt[0][0])[i] = 0;
+    if (tid == 0) {
+        a.ctrl->amax_a = 0;
+        a.ctrl->amax_i = 0;
+    }
+    __syncthreads();
+    for (int32_t s = s0 + lane; s < s1; s += 64) {
+        const int el = a.idx[s] - a.e_begin;
+        if (el >= 0 && el < n) atomicAdd(&cnt[wave][el], 1);
+    }
+    __syncthreads();
+    for (int el = tid; el < n; el += kSmallThreads) {
+        int32_t run = 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const int32_t c = cnt[w][el];
+            cnt[w][el] = run;  // base of wave w within the expert
+            run += c;
+        }
+        tot[el] = run;
+        a.counts[el] = run;
+        tiles[el] = (run + a.bm - 1) / a.bm;
+    }
+    __syncthreads();
+    const int32_t S = small_exclusive_scan(tot, n, part);
+    const int32_t n_tiles = small_exclusive_scan(tiles, n, part);
+    for (int el = tid; el < n; el += kSmallThreads) {
+        a.offsets[el] = tot[el];
+        const int32_t t0 = tiles[el];
+        const int32_t t1 = el + 1 < n ? tiles[el + 1] : n_tiles;
+        for (int32_t t = t0; t < t1; ++t) {
+            a.tile_expert[t] = el;
+            a.tile_row0[t] = tot[el] + (t - t0) * a.bm;
+        }
+#pragma unroll
+        for (int w = 0; w < 4; ++w) cnt[w][el] += tot[el];  // absolute cursors
+    }
+    if (tid == 0) {
+        a.offsets[n] = S;
+        a.ctrl->S = S;
+        a.ctrl->n_tiles = n_tiles;
+    }
+    __syncthreads();
+    const uint64_t lt = (1ull << lane) - 1;
+    int32_t *cursor = cnt[wave];
+    for (int32_t gbase = s0; gbase < s1; gbase += 64) {
+        const int32_t s = gbase + lane;
+        const bool valid = s < s1;
+        const int el = valid ? a.idx[s] - a.e_begin : -1;
+        const bool local = valid && el >= 0 && el < n;
+        if (valid && !local) a.slot_pos[s] = -1;
+        uint64_t rem = __ballot(local);
+        while (rem) {
+            const int leader = __ffsll((unsigned long long)rem) - 1;
+            const int e = __shfl(el, leader);
+            const bool mine = local && el == e;
+            const uint64_t m = __ballot(mine);
+            const int32_t start = __builtin_amdgcn_readfirstlane(cursor[e]);
+            if (mine) {
+                const int32_t pos = start + __popcll(m & lt);
+                a.sorted_slot[pos] = s;
+                a.slot_pos[s] = pos;
+            }
+            if (lane == leader) cursor[e] = start + __popcll(m);
+            rem &= ~m;
+        }
+    }
+}
+
 }  // namespace
+
+bool permute_small_ok(int32_t T, int32_t k, int32_t n_loc) {
+    return (int64_t)T * k <= 8192 && n_loc <= kSmallMaxLocal;
+}
+
+hipError_t launch_permute_small(const PermuteArgs &a, hipStream_t s) {
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, a);
+    return hipGetLastError();
+}
 
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s) {
     const int32_t n_slots = a.T * a.k;

@@ -142,7 +142,7 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
  * h: bf16 [T][D]; wr: bf16 [E][D]; bias: fp32 [E] or NULL; logits: fp32 [T][E]
  * (written; caller-owned scratch that doubles as an output); h_amax: fp32 [1] or NULL
  * (if given, receives max |h| over all of h, for moe_forward's NVFP4 tensor scale).
- * Requires 1 <= top_k <= 8, top_k <= E <= 4096. T = 0 is a no-op.
+ * Requires 1 <= top_k <= 8, top_k <= E <= 1024. T = 0 is a no-op.
  */
 int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t *h,
                   const uint16_t *wr, const float *bias, float *logits, int32_t *topk_idx,

@@ -96,6 +96,14 @@ LAYER_CASES = [
          wl=synth.custom("mxfp8", T=400, D=256, F=128, E=24, e_begin=0, e_end=6, seed=28)),
     dict(name="skew-mxfp8", wl=synth.custom("mxfp8", T=256, D=256, F=256, E=64, skew=True, seed=29)),
     dict(name="skew-prefill-nvfp4", wl=synth.custom("nvfp4", T=600, D=256, F=128, E=16, skew=True, seed=30)),
+    # decode shapes with K a multiple of 512 run the streaming kernels
+    dict(name="stream-nvfp4-k2048", wl=synth.custom("nvfp4", T=48, D=2048, F=1536, E=16, seed=31)),
+    dict(name="stream-mxfp8-k2048", wl=synth.custom("mxfp8", T=48, D=2048, F=1536, E=16, seed=32)),
+    dict(name="stream-mxfp8-k4096-k512", wl=synth.custom("mxfp8", T=24, D=4096, F=512, E=8, seed=33)),
+    dict(name="stream-nvfp4-full-dims", wl=synth.custom("nvfp4", T=64, D=4096, F=2560, E=16, seed=34)),
+    dict(name="stream-mxfp8-full-dims", wl=synth.custom("mxfp8", T=64, D=4096, F=2560, E=16, seed=35)),
+    dict(name="stream-nvfp4-ep-share", wl=synth.custom("nvfp4", T=64, D=2048, F=1024, E=32, e_begin=4, e_end=12,
+                                                       seed=36)),
 ]
 
 
