@@ -90,6 +90,9 @@ enum class GemmShape { Decode, Prefill };
 hipError_t launch_grouped_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, GemmShape shape,
                                int32_t max_tiles, hipStream_t s);
 int32_t gemm_bm(GemmShape shape);
+// prefill-shaped MFMA tiles (gemm_tile.hip): 64-row M-tiles, 256 weight rows per workgroup
+bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up);
+hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);
 // decode-shaped streaming variant (gemm_stream.hip): 16-row M-tiles, K a multiple of 512
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
 hipError_t launch_stream_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);

@@ -26,6 +26,7 @@ constexpr int32_t kPrefillRowsPerExpert = 48;
 
 struct Plan {
     GemmShape shape;
+    bool tile64;  // prefill on the 64-row MFMA tile kernels
     int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
     size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
     size_t a_codes, a_scales, a_tscale, a16;
@@ -41,7 +42,9 @@ Plan make_plan(const moe_forward_args *a) {
     const bool nv = a->fmt == MOE_FMT_NVFP4;
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
-    p.bm = gemm_bm(p.shape);
+    p.tile64 = p.shape == GemmShape::Prefill && tile_gemm_supported(a->D, 2 * a->F, true) &&
+               tile_gemm_supported(a->F, a->D, false);
+    p.bm = p.tile64 ? 64 : gemm_bm(p.shape);
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
@@ -75,6 +78,7 @@ Plan make_plan(const moe_forward_args *a) {
 }
 
 hipError_t run_gemm(const GemmArgs &g, bool nv, bool gate_up, const Plan &P, hipStream_t s) {
+    if (P.tile64) return launch_tile_gemm(g, nv, gate_up, P.max_tiles, s);
     if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
         return launch_stream_gemm(g, nv, gate_up, P.max_tiles, s);
     return launch_grouped_gemm(g, nv, gate_up, P.shape, P.max_tiles, s);

@@ -89,6 +89,8 @@ def _load():
     lib.orc_permute.restype = i64
     lib.orc_moe_forward.argtypes = [ctypes.POINTER(_Args)]
     lib.orc_moe_forward.restype = ctypes.c_int
+    lib.orc_down_combine.argtypes = [i32] * 8 + [p, p, p, p, flt, p, p, p, p]
+    lib.orc_down_combine.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -286,3 +288,24 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
         a.tok_list, a.n_tok = _ptr(tl), len(tl)
     _check(lib.orc_moe_forward(ctypes.byref(a)), "moe_forward")
     return (out, tp) if taps else out
+
+
+def down_combine(fmt: str, idx, w, inter_codes, inter_scales, inter_tscale, down, *, D: int, F: int, E: int,
+                 e_begin: int = 0, e_end: int | None = None):
+    """Down projection and combine alone (the forward's last two steps) from given
+    intermediate codes of the S local slots in sorted order -> out float32 [T, D]."""
+    f = _FMT[fmt]
+    idx = np.ascontiguousarray(idx, np.int32)
+    w = np.ascontiguousarray(w, np.float32)
+    T, k = idx.shape
+    e_end = E if e_end is None else e_end
+    ic = np.ascontiguousarray(inter_codes, np.uint8)
+    is_ = np.ascontiguousarray(inter_scales, np.uint8)
+    c = np.ascontiguousarray(down["codes"], np.uint8)
+    sc = np.ascontiguousarray(down["scales"], np.uint8)
+    ts = None if down.get("tensor_scale") is None else np.ascontiguousarray(down["tensor_scale"], np.float32)
+    out = np.empty((T, D), np.float32)
+    _check(_load().orc_down_combine(f, T, D, F, E, k, e_begin, e_end, _ptr(idx), _ptr(w), _ptr(ic), _ptr(is_),
+                                    float(inter_tscale if inter_tscale is not None else 1.0), _ptr(c), _ptr(sc),
+                                    _ptr(ts), _ptr(out)), "down_combine")
+    return out

@@ -713,3 +713,84 @@ done:
     free(cidx); free(cdn); free(gu_raw); free(ihat); free(y64); free(inter64); free(inter);
     return rc;
 }
+
+/*
+ * Steps 5 and 6 of the forward alone, from given intermediate codes: for each local
+ * slot p (sorted order as orc_permute gives it), y = dequant(intermediate row p) . W_d[e]^T
+ * summed in fp64 and rounded and scaled exactly as in orc_moe_forward, then
+ * out[t] = sum over the token's local slots, j ascending, of w[t][j] * y (fp64, rounded
+ * to fp32). Used to check a down projection and combine on another implementation's
+ * intermediate codes. i_codes / i_scales: [S][F/2] and [S][F/16] (NVFP4, tensor scale
+ * i_ts) or [S][F] and [S][F/32] (MXFP8).
+ */
+int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, int32_t k, int32_t e_begin,
+                     int32_t e_end, const int32_t *idx, const float *w, const uint8_t *i_codes,
+                     const uint8_t *i_scales, float i_ts, const uint8_t *dn_codes, const uint8_t *dn_scales,
+                     const float *dn_tscale, float *out) {
+    if (fmt != 1 && fmt != 2) return ORC_EINVAL;
+    if (T < 0 || D <= 0 || F <= 0 || E <= 0 || k <= 0 || e_begin < 0 || e_end > E || e_end <= e_begin) return ORC_EINVAL;
+    if (T == 0) return ORC_OK;
+    if (!idx || !w || !i_codes || !i_scales || !dn_codes || !dn_scales || !out || (fmt == 1 && !dn_tscale))
+        return ORC_EINVAL;
+    init_tables();
+    const int32_t n_loc = e_end - e_begin;
+    int32_t *counts = (int32_t *)malloc(sizeof(int32_t) * n_loc);
+    int32_t *offs = (int32_t *)malloc(sizeof(int32_t) * (n_loc + 1));
+    int32_t *sorted = (int32_t *)malloc(sizeof(int32_t) * ((int64_t)T * k + 1));
+    int64_t *pos = (int64_t *)malloc(sizeof(int64_t) * (int64_t)T * k);
+    double *ihat = NULL, *y64 = NULL;
+    int rc = ORC_OK;
+    if (!counts || !offs || !sorted || !pos) { rc = ORC_ENOMEM; goto done; }
+    const int64_t S = orc_permute(T, k, idx, e_begin, e_end, counts, offs, sorted);
+    ihat = (double *)malloc(sizeof(double) * (S > 0 ? S : 1) * F);
+    y64 = (double *)malloc(sizeof(double) * (S > 0 ? S : 1) * D);
+    if (!ihat || !y64) { rc = ORC_ENOMEM; goto done; }
+    if (fmt == 1) orc_dequant_nvfp4(i_codes, i_scales, i_ts, S, F, 0, ihat);
+    else orc_dequant_mxfp8(i_codes, i_scales, S, F, ihat);
+    {
+        int fail = 0;
+#pragma omp parallel
+        {
+            double *wrow = (double *)malloc(sizeof(double) * F);
+            if (!wrow) {
+#pragma omp atomic write
+                fail = 1;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t it = 0; it < (int64_t)n_loc * D; ++it) {
+                    int32_t el = (int32_t)(it / D);
+                    int64_t n = it % D;
+                    if (offs[el] == offs[el + 1]) continue;
+                    int32_t e = e_begin + el;
+                    weight_row(fmt, NULL, dn_codes, dn_scales, (int64_t)e * D + n, F, wrow);
+                    float sc = fmt == 1 ? i_ts * dn_tscale[e] : 1.0f;
+                    for (int64_t p = offs[el]; p < offs[el + 1]; ++p) {
+                        const double *irow = ihat + p * F;
+                        double s = 0.0;
+                        for (int64_t f = 0; f < F; ++f) s += irow[f] * wrow[f];
+                        y64[p * D + n] = fmt == 1 ? (double)(float)((float)s * sc) : (double)(float)s;
+                    }
+                }
+            }
+            free(wrow);
+        }
+        if (fail) { rc = ORC_ENOMEM; goto done; }
+    }
+    for (int64_t s = 0; s < (int64_t)T * k; ++s) pos[s] = -1;
+    for (int64_t p = 0; p < S; ++p) pos[sorted[p]] = p;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int64_t n = 0; n < D; ++n) {
+            double acc = 0.0;
+            for (int64_t j = 0; j < k; ++j) {
+                int64_t p = pos[t * k + j];
+                if (p < 0) continue;
+                acc += (double)w[t * k + j] * y64[p * D + n];
+            }
+            out[t * D + n] = (float)acc;
+        }
+    }
+done:
+    free(counts); free(offs); free(sorted); free(pos); free(ihat); free(y64);
+    return rc;
+}

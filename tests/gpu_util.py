@@ -47,3 +47,39 @@ def check_intermediate_codes(fmt: str, inter: np.ndarray, codes: np.ndarray, sca
     bad_c = int(np.count_nonzero(oc != codes))
     bad_s = int(np.count_nonzero(os_ != scales))
     assert bad_c == 0 and bad_s == 0, f"intermediate codes differ: {bad_c} code bytes, {bad_s} scale bytes"
+
+
+def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w: np.ndarray, gpu_inter_codes,
+                  gpu_inter_scales, gpu_inter_tscale, oracle_inter_codes, oracle_inter_scales, sorted_slot,
+                  down: dict, *, D: int, F: int, E: int, e_begin: int, e_end: int, rows=None):
+    """Output parity with intermediate-code flips accounted for.
+
+    The intermediate codes are a rounding of fp32 sums; the GPU sums in a different order
+    than the oracle's fp64, so a value on a rounding boundary can land on the neighbouring
+    code ("flip"), and one flip moves the affected outputs by up to ~1e-2 x RMS.
+     1. stage-wise: the oracle's down projection and combine fed the GPU's intermediate
+        codes match the GPU output on every token, to 2e-3 x RMS;
+     2. independent: tokens none of whose slots holds a flipped intermediate row match
+        the fully independent oracle output, to 2e-3 x RMS;
+     3. flips stay rare (< 1e-3 of the intermediate elements).
+    rows: optional token subset to compare (the others are not computed by the oracle).
+    Returns (stage error / RMS, independent error / RMS, flips, tokens excluded)."""
+    k = idx.shape[1]
+    S = len(sorted_slot)
+    stage = oracle.down_combine(fmt, idx, w, gpu_inter_codes, gpu_inter_scales, gpu_inter_tscale, down, D=D, F=F,
+                                E=E, e_begin=e_begin, e_end=e_end)
+    sel = np.arange(out.shape[0]) if rows is None else np.asarray(rows)
+    r_stage = rms(stage[sel])
+    e_stage = float(np.abs(out[sel] - stage[sel]).max()) / r_stage
+    assert e_stage <= 2e-3, f"stage-wise output error {e_stage:.2e} x RMS"
+    cb = gpu_inter_codes.reshape(S, -1) != oracle_inter_codes.reshape(S, -1)
+    sb = gpu_inter_scales.reshape(S, -1) != oracle_inter_scales.reshape(S, -1)
+    flipped_rows = np.nonzero(cb.any(1) | sb.any(1))[0]
+    flips = int(cb.sum())
+    assert flips <= 1e-3 * S * F, f"{flips} intermediate code flips in {S * F} elements"
+    bad_tokens = set((sorted_slot[flipped_rows] // k).tolist())
+    keep = np.array([t for t in sel if t not in bad_tokens], dtype=np.int64)
+    r_ref = rms(ref[sel])
+    e_ind = float(np.abs(out[keep] - ref[keep]).max()) / r_ref if len(keep) else 0.0
+    assert e_ind <= 2e-3, f"independent output error {e_ind:.2e} x RMS on tokens without flips"
+    return e_stage, e_ind, flips, len(sel) - len(keep)

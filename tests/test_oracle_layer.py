@@ -228,3 +228,21 @@ def test_empty_batch_is_a_no_op():
     out = oracle.moe_forward("nvfp4", h[:0], np.zeros((0, 8), np.int32), np.zeros((0, 8), f32),
                              D=64, F=32, E=16, gate_up=gu, down=dn)
     assert out.shape == (0, 64)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+def test_down_combine_reproduces_the_forward(fmt):
+    """The stage-wise entry point (down projection + combine from given intermediate codes),
+    fed the forward's own intermediate codes, gives the forward's output bit for bit, also
+    on an expert-parallel share."""
+    T, D, F, E = 24, 64, 96, 12
+    wl, h, wr, _ = _small(fmt, T=T, D=D, F=F, E=E, seed=44)
+    gu, dn = _quantised(fmt, wl)
+    idx, w = oracle.route(h, wr, k=8)
+    for eb, ee in ((0, E), (3, 8)):
+        out, tp = oracle.moe_forward(fmt, h, idx, w, D=D, F=F, E=E, e_begin=eb, e_end=ee, gate_up=gu, down=dn,
+                                     taps=True)
+        ts = tp["inter_tscale"][0] if fmt == "nvfp4" else None
+        got = oracle.down_combine(fmt, idx, w, tp["inter_codes"], tp["inter_scales"], ts, dn, D=D, F=F, E=E,
+                                  e_begin=eb, e_end=ee)
+        assert np.array_equal(got.view(np.uint32), out.view(np.uint32))
