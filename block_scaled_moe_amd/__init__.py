@@ -101,7 +101,9 @@ def _check(rc: int, what: str):
 
 @dataclasses.dataclass
 class PackedWeights:
-    """Device tensors of one packed matrix kind for E experts ([E][N][K] each)."""
+    """Device tensors of one packed matrix kind for E experts (logically [E][N][K]) in the
+    tiled layout of include/moe.h: codes [E][N/32][K/64][32][32 | 64] and scales
+    [E][N/32][K/64][32][4 | 2] (NVFP4 | MXFP8)."""
     fmt: str
     E: int
     N: int
@@ -113,8 +115,10 @@ class PackedWeights:
     @staticmethod
     def empty(fmt: str, E: int, N: int, K: int, device="cuda") -> "PackedWeights":
         nv = fmt == "nvfp4"
-        codes = torch.empty((E, N, K // 2 if nv else K), dtype=torch.uint8, device=device)
-        scales = torch.empty((E, N, K // 16 if nv else K // 32), dtype=torch.uint8, device=device)
+        if N % 32 or K % 64:
+            raise ValueError(f"packed weights need N % 32 == 0 and K % 64 == 0 (got N={N}, K={K})")
+        codes = torch.empty((E, N // 32, K // 64, 32, 32 if nv else 64), dtype=torch.uint8, device=device)
+        scales = torch.empty((E, N // 32, K // 64, 32, 4 if nv else 2), dtype=torch.uint8, device=device)
         ts = torch.empty(E, dtype=torch.float32, device=device) if nv else None
         return PackedWeights(fmt, E, N, K, codes, scales, ts)
 

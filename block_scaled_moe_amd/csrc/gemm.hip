@@ -34,6 +34,7 @@
 #include "formats.h"
 #include "gemm_common.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace moe {
 namespace {
@@ -111,13 +112,14 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
         const int r = item / (C::B_ROW / 16), q = item % (C::B_ROW / 16);
         const int wrow = GATE_UP ? (r < BN / 2 ? n0 + r : F + n0 + (r - BN / 2)) : n0 + r;
         b_dst[i] = C::B_OFF + r * C::B_STRIDE + 16 * q;
-        b_src[i] = p.w_codes + ((int64_t)e * p.N + wrow) * w_row_bytes + 16 * q;
+        // packed tile layout (layout.h): a 16-byte piece stays inside one row's 64-wide slot
+        b_src[i] = p.w_codes + (int64_t)e * p.N * w_row_bytes + layout::code_offset(NV, K, wrow, (NV ? 32 : 16) * q);
     }
     const uint8_t *s_src = nullptr;
     int s_dst = 0;
     if (tid < BN) {
         const int wrow = GATE_UP ? (tid < BN / 2 ? n0 + tid : F + n0 + (tid - BN / 2)) : n0 + tid;
-        s_src = p.w_scales + ((int64_t)e * p.N + wrow) * (K / C::BLK);
+        s_src = p.w_scales + (int64_t)e * p.N * (K / C::BLK) + layout::scale_offset(NV, K, wrow, 0);
         s_dst = C::S_OFF + tid * C::SB;
     }
 
@@ -144,17 +146,20 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                 a_reg[i] = a_src[i] ? *reinterpret_cast<const u32x4 *>(a_src[i] + 2 * kn) : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < C::B_ITEMS; ++i)
-                b_reg[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (NV ? kn / 2 : kn));
+                b_reg[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (int64_t)(kn / 64) * layout::code_block_bytes(NV));
             if (s_src) {
-                const uint8_t *sp = s_src + kn / C::BLK;
-                if (C::SB == 16) {
-                    s_reg = *reinterpret_cast<const u32x4 *>(sp);
-                } else if (C::SB == 8) {
-                    const u32x2 v = *reinterpret_cast<const u32x2 *>(sp);
-                    s_reg = (u32x4){v.x, v.y, 0u, 0u};
-                } else {
-                    s_reg = (u32x4){*reinterpret_cast<const uint32_t *>(sp), 0u, 0u, 0u};
+                // the chunk's KC/64 block slots of this row, gathered in column order
+                constexpr int NBLK = KC / 64, SBW = layout::scale_bytes_per_row(NV);
+                const uint8_t *sp = s_src + (int64_t)(kn / 64) * layout::scale_block_bytes(NV);
+                uint32_t wv[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int b = 0; b < NBLK; ++b) {
+                    const uint32_t v = SBW == 4 ? *reinterpret_cast<const uint32_t *>(sp + b * layout::scale_block_bytes(NV))
+                                                : (uint32_t)*reinterpret_cast<const uint16_t *>(sp + b * layout::scale_block_bytes(NV));
+                    if (SBW == 4) wv[b] = v;
+                    else wv[b / 2] |= v << (16 * (b & 1));
                 }
+                s_reg = (u32x4){wv[0], wv[1], wv[2], wv[3]};
             }
         }
         if (c > 0) {  // multiply chunk c-1 out of LDS

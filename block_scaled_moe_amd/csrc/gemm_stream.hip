@@ -10,7 +10,9 @@
 //    row cover 64 contiguous bytes per NVFP4 group, 128 per MXFP8 group), keeping a
 //    window of W groups of loads in flight; nothing goes through LDS and the K loop has
 //    no barriers;
-//  - the wave's block scales are staged once in LDS with full-line loads;
+//  - weights are in the packed tile layout (layout.h), so the 16 rows x 4 lanes of one
+//    load instruction read two contiguous 512-byte (NVFP4) runs;
+//  - the wave's block scales are staged once in LDS with contiguous loads;
 //  - the four partial sums are added in a fixed order through LDS before the epilogue,
 //    so results are deterministic.
 // K-slot mapping inside a 128-wide group of a wave's K quarter: lane group g = lane/16
@@ -19,6 +21,7 @@
 #include "formats.h"
 #include "gemm_common.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace moe {
 namespace {
@@ -74,27 +77,41 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
         return GATE_UP ? (r < kRows / 2 ? n0 + r : F + n0 + (r - kRows / 2)) : n0 + r;
     };
 
-    // ---- block scales of this wave's quarter: global -> registers now, -> LDS after the
-    //      first weight loads are in flight (full-line loads, consecutive lanes = consecutive dwords)
+    // packed tile layout (layout.h): rows in groups of 32, K in blocks of 64
+    constexpr int CB = layout::code_bytes_per_row(NV);
+    constexpr int CBLK = layout::code_block_bytes(NV), SBLK = layout::scale_block_bytes(NV);
+    const int64_t kb = K / 64;
+    const uint8_t *w_codes_e = p.w_codes + (int64_t)e * p.N * row_bytes;
+    const uint8_t *w_scales_e = p.w_scales + (int64_t)e * p.N * (K / BLK);
+
+    // ---- block scales of this wave's quarter: global -> registers now, -> LDS (row-major,
+    //      SBW bytes per row) after the first weight loads are in flight. Register i of
+    //      lane l: NVFP4 row l's 4 scales of chunk i; MXFP8 rows 2(l%32), 2(l%32)+1 of chunk
+    //      2i + l/32 (consecutive lanes read consecutive bytes of one block).
     constexpr int SREG = kRows * SBW / 4 / 64;
     static_assert(kRows * SBW / 4 % 64 == 0, "scale dwords tile the wave");
     uint32_t sreg[SREG];
-    {
-        const uint8_t *sbase = p.w_scales + (int64_t)e * p.N * (K / BLK) + kw / BLK;
 #pragma unroll
-        for (int i = 0; i < SREG; ++i) {
-            const int d = lane + 64 * i;
-            const int r = d / (SBW / 4), q = d % (SBW / 4);
-            sreg[i] = *reinterpret_cast<const uint32_t *>(sbase + (int64_t)wrow_of(r) * (K / BLK) + 4 * q);
+    for (int i = 0; i < SREG; ++i) {
+        if (NV) {
+            const int r = lane, row = wrow_of(r);
+            sreg[i] = *reinterpret_cast<const uint32_t *>(w_scales_e + ((row >> 5) * kb + kw / 64 + i) * SBLK +
+                                                          4 * (row & 31));
+        } else {
+            const int r = 2 * (lane & 31), row = wrow_of(r), cl = 2 * i + (lane >> 5);
+            sreg[i] = *reinterpret_cast<const uint32_t *>(w_scales_e + ((row >> 5) * kb + kw / 64 + cl) * SBLK +
+                                                          2 * (row & 31));
         }
     }
 
-    // ---- weight code pointers of this lane (one per subtile) and activation row
+    // ---- weight code pointers of this lane (one per subtile; lane group g reads half g%2
+    //      of the row's slot in 64-wide chunk g/2 of each 128-wide group) and activation row
     const uint8_t *bsrc[kSub];
 #pragma unroll
-    for (int s = 0; s < kSub; ++s)
-        bsrc[s] = p.w_codes + ((int64_t)e * p.N + wrow_of(16 * s + r16)) * row_bytes + (NV ? kw / 2 : kw) +
-                  (NV ? 16 : 32) * g;
+    for (int s = 0; s < kSub; ++s) {
+        const int row = wrow_of(16 * s + r16);
+        bsrc[s] = w_codes_e + ((row >> 5) * kb + kw / 64 + (g >> 1)) * CBLK + (row & 31) * CB + (CB / 2) * (g & 1);
+    }
     const uint8_t *asrc = nullptr;
     if (r16 < rows) {
         const int pos = p0 + r16;
@@ -109,7 +126,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
         for (int s = 0; s < kSub; ++s)
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                bq[jj][s][q] = *reinterpret_cast<const u32x4 *>(bsrc[s] + (NV ? 64 : 128) * jj + 16 * q);
+                bq[jj][s][q] = *reinterpret_cast<const u32x4 *>(bsrc[s] + 2 * CBLK * jj + 16 * q);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             aq[jj][j] = asrc ? *reinterpret_cast<const u32x4 *>(asrc + 256 * jj + 16 * j) : (u32x4){0u, 0u, 0u, 0u};
@@ -123,8 +140,13 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     for (int jj = 0; jj < W && jj < G; ++jj) load_group(jj);
 #pragma unroll
     for (int i = 0; i < SREG; ++i) {
-        const int d = lane + 64 * i;
-        *reinterpret_cast<uint32_t *>(&s_scale[wave][(d / (SBW / 4)) * SBW + 4 * (d % (SBW / 4))]) = sreg[i];
+        if (NV) {
+            *reinterpret_cast<uint32_t *>(&s_scale[wave][lane * SBW + 4 * i]) = sreg[i];
+        } else {
+            const int r = 2 * (lane & 31), cl = 2 * i + (lane >> 5);
+            *reinterpret_cast<uint16_t *>(&s_scale[wave][r * SBW + 2 * cl]) = (uint16_t)sreg[i];
+            *reinterpret_cast<uint16_t *>(&s_scale[wave][(r + 1) * SBW + 2 * cl]) = (uint16_t)(sreg[i] >> 16);
+        }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's scale stores are done
     __builtin_amdgcn_wave_barrier();     // and no LDS read is hoisted above them

@@ -3,22 +3,32 @@
 //
 // Same arithmetic as the other grouped GEMMs (exact 16-bit expansion of NVFP4 / MXFP8
 // codes, fp32 accumulation; see gemm_common.h), tiled for MFMA throughput:
-//  - workgroup tile 64 sorted rows x 256 weight rows, 4 waves side by side in N, each
-//    wave 64 x 64 as 2 x 2 tiles of v_mfma_f32_32x32x16_{f16,bf16}; the waves share the
-//    activation tile and own disjoint weight rows, so every weight value is expanded
-//    once per workgroup;
-//  - gate_up tiles hold 128 gate rows and the 128 matching up rows; wave w owns gate
-//    rows 32w..32w+31 and the same up rows, so SwiGLU pairs two accumulators of a lane;
-//  - K chunks of 64 go global -> registers (16-byte loads, next chunk prefetched while
-//    the current one is multiplied) -> double-buffered LDS, one barrier per chunk;
-//  - 64-row tiles keep the padding of ~170-row experts near 10%.
+//  - workgroup tile 64 sorted rows x (128 NS) weight rows, 4 waves side by side in N,
+//    each wave 64 x 32NS as 2 x NS tiles of v_mfma_f32_32x32x16_{f16,bf16};
+//  - the waves own disjoint weight rows, so weights never pass through LDS: each lane
+//    loads its weight row's codes straight into registers and expands them into the
+//    MFMA B operand; only the shared activation tile is staged in LDS;
+//  - K order inside a 64-wide chunk is permuted identically for both operands: lane half
+//    g (lanes 32g..32g+31) supplies k = 32g..32g+31 over the chunk's four MFMA steps
+//    (step s: k = 32g + 8s .. +7). With the packed tile layout (layout.h) a wave's codes
+//    for one chunk and 32-row subtile are then one contiguous 1 KiB (NVFP4) / 2 KiB
+//    (MXFP8) run and its scales one 128 / 64-byte run; the fp32 sums are unchanged up
+//    to rounding order;
+//  - software pipeline without branches: activations two chunks ahead (two register
+//    sets, LDS double buffer), weights four chunks ahead (four-slot register ring), so
+//    every wait count in the loop is partial;
+//  - gate_up tiles pair gate row f with up row F + f in the same lane and accumulator
+//    slot, so SwiGLU needs no data exchange;
+//  - work items (M-tile, N-block) are ordered in groups of 4 consecutive M-tiles, N-block
+//    next, and dealt to the 8 XCDs in contiguous ranges, so one XCD's L2 holds the
+//    activation rows of a few M-tiles while it sweeps their weight rows once.
 // 32x32x16 operand layout (measured on gfx950): A lane l holds row l%32, k 8(l/32)..+7;
 // B lane l holds k 8(l/32)..+7 of column l%32; accumulator v of lane l is row
-// 8(v/4) + 4(l/32) + v%4, column l%32. One 16-wide k step is one NVFP4 scale block and
-// half an MXFP8 block.
+// 8(v/4) + 4(l/32) + v%4, column l%32.
 #include "formats.h"
 #include "gemm_common.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace moe {
 namespace {
@@ -27,176 +37,221 @@ using namespace gemm_detail;
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
+constexpr int kBM = 64, kKC = 64, kThreads = 256, kGroup = 4;
+constexpr int kAStride = kKC * 2 + 16;                  // LDS bytes per activation row
+constexpr int kAStage = kBM * kAStride;                 // one LDS buffer
+constexpr int kAItems = kBM * kKC * 2 / 16 / kThreads;  // 16-byte activation loads per thread
+static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the threads");
+
+#ifndef MOE_TILE_NS_NV
+#define MOE_TILE_NS_NV 2
+#endif
+#ifndef MOE_TILE_NS_MX
+#define MOE_TILE_NS_MX 2
+#endif
+
 template <bool NV>
-struct TileCfg {
-    static constexpr int BM = 64, BN = 256, KC = 64, NT = 256;
-    static constexpr int BLK = NV ? 16 : 32;
-    static constexpr int B_ROW = NV ? KC / 2 : KC;     // code bytes per weight row per chunk
-    static constexpr int SB = KC / BLK;                // scale bytes per weight row per chunk
-    static constexpr int A_STRIDE = KC * 2 + 16;       // LDS bytes per activation row
-    static constexpr int B_STRIDE = B_ROW + 16;        // LDS bytes per weight row
-    static constexpr int A_OFF = 0;
-    static constexpr int B_OFF = BM * A_STRIDE;
-    static constexpr int S_OFF = B_OFF + BN * B_STRIDE;
-    static constexpr int STAGE = S_OFF + BN * SB;
-    static constexpr int A_ITEMS = BM * KC * 2 / 16 / NT;  // 16-byte loads per thread
-    static constexpr int B_ITEMS = BN * B_ROW / 16 / NT;
-    static_assert(BM * KC * 2 / 16 % NT == 0 && BN * B_ROW / 16 % NT == 0, "loads tile the threads");
-    static_assert(SB == 2 || SB == 4, "one scale load per weight row");
-};
+constexpr int tile_ns() { return NV ? MOE_TILE_NS_NV : MOE_TILE_NS_MX; }
 
-template <bool NV, bool GATE_UP>
-__global__ void __launch_bounds__(256, 2) tile_gemm_kernel(const GemmArgs p) {
-    using C = TileCfg<NV>;
+template <bool NV, bool GATE_UP, int NS>
+__global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(const GemmArgs p) {
     using Frag = typename std::conditional<NV, half8, bf16x8>::type;
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * C::STAGE];
+    constexpr int BN = 128 * NS;        // weight rows per workgroup
+    constexpr int CV = NV ? 1 : 2;      // 16-byte code loads per weight row per lane per chunk
+    static_assert(NS % 2 == 0, "gate_up pairs subtiles");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kAStage];
 
-    const int tile = blockIdx.x;
-    if (tile >= p.ctrl->n_tiles) return;
+    const int K = p.K, N = p.N, F = N / 2;
+    const int NB = GATE_UP ? F / (BN / 2) : N / BN;
+
+    // ---- work item of this workgroup (XCD-contiguous ranges; see the header)
+    const int n_tiles = p.ctrl->n_tiles;
+    const int total = (n_tiles + kGroup - 1) / kGroup * kGroup * NB;
+    const int per_xcd = (total + 7) / 8;
+    const int b = blockIdx.x;
+    if ((b >> 3) >= per_xcd) return;
+    const int w = (b & 7) * per_xcd + (b >> 3);
+    if (w >= total) return;
+    const int grp = w / (kGroup * NB), rem = w % (kGroup * NB);
+    const int nb = rem / kGroup;
+    const int tile = grp * kGroup + rem % kGroup;
+    if (tile >= n_tiles) return;
+
     const int el = p.tile_expert[tile];
     const int p0 = p.tile_row0[tile];
-    const int rows = min(C::BM, p.offsets[el + 1] - p0);
+    const int rows = min(kBM, p.offsets[el + 1] - p0);
     const int e = p.e_begin + el;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g2 = lane >> 5;
-    const int K = p.K, N = p.N, F = N / 2;
-    const int n0 = GATE_UP ? blockIdx.y * (C::BN / 2) : blockIdx.y * C::BN;
-    const int64_t w_row_bytes = NV ? K / 2 : K;
+    // packed tile layout (layout.h): per chunk, a lane's 32 codes sit at byte
+    // (row % 32) * CB + CB/2 * g of the chunk's block of its row group, and its scales in
+    // the block's 4-byte (NVFP4) or 2-byte (MXFP8) row slot
+    constexpr int CB = layout::code_bytes_per_row(NV);
+    constexpr int CBLK = layout::code_block_bytes(NV), SBLK = layout::scale_block_bytes(NV);
+    const int64_t kb = K / 64;  // blocks per row group
+    const uint8_t *w_codes_e = p.w_codes + (int64_t)e * N * (NV ? K / 2 : K);
+    const uint8_t *w_scales_e = p.w_scales + (int64_t)e * N * (NV ? K / 16 : K / 32);
 
-    // weight row of LDS tile row r
-    auto wrow_of = [&](int r) -> int {
-        return GATE_UP ? (r < C::BN / 2 ? n0 + r : F + n0 + (r - C::BN / 2)) : n0 + r;
-    };
-
-    // ---- per-thread global sources (fixed over K) and LDS destinations
-    const uint8_t *a_src[C::A_ITEMS];
-    int a_dst[C::A_ITEMS];
+    // ---- this lane's weight rows, one per N subtile (each subtile is one row group)
+    const uint8_t *wc[NS];
+    const uint8_t *ws[NS];
 #pragma unroll
-    for (int i = 0; i < C::A_ITEMS; ++i) {
-        const int item = tid + i * C::NT;
-        const int r = item / (C::KC * 2 / 16), q = item % (C::KC * 2 / 16);
-        a_dst[i] = C::A_OFF + r * C::A_STRIDE + 16 * q;
-        a_src[i] = nullptr;
-        if (r < rows) {
-            const int pos = p0 + r;
-            const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
-            a_src[i] = static_cast<const uint8_t *>(p.a_vals) + arow * K * 2 + 16 * q;
+    for (int ns = 0; ns < NS; ++ns) {
+        int row;
+        if (GATE_UP) {
+            const int col = nb * (BN / 2) + wave * 16 * NS + 32 * (ns % (NS / 2)) + l32;
+            row = ns < NS / 2 ? col : F + col;
+        } else {
+            row = nb * BN + wave * 32 * NS + 32 * ns + l32;
         }
+        const int64_t blk0 = (int64_t)(row >> 5) * kb;
+        wc[ns] = w_codes_e + blk0 * CBLK + l32 * CB + (CB / 2) * g2;
+        ws[ns] = w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
     }
-    const uint8_t *b_src[C::B_ITEMS];
-    int b_dst[C::B_ITEMS];
+
+    // ---- activation staging: global -> registers -> LDS. Rows past the tile's end load
+    // the tile's first row instead of zeros: their accumulators are never stored, and
+    // unconditional loads from one global base keep the wait counts per chunk.
+    const uint8_t *a_base = static_cast<const uint8_t *>(p.a_vals);
+    int64_t a_off[kAItems];
+    int a_dst[kAItems];
 #pragma unroll
-    for (int i = 0; i < C::B_ITEMS; ++i) {
-        const int item = tid + i * C::NT;
-        const int r = item / (C::B_ROW / 16), q = item % (C::B_ROW / 16);
-        b_dst[i] = C::B_OFF + r * C::B_STRIDE + 16 * q;
-        b_src[i] = p.w_codes + ((int64_t)e * N + wrow_of(r)) * w_row_bytes + 16 * q;
+    for (int i = 0; i < kAItems; ++i) {
+        const int item = tid + i * kThreads;
+        const int r = item >> 3, q = item & 7;
+        a_dst[i] = r * kAStride + 16 * q;
+        const int pos = p0 + (r < rows ? r : 0);
+        const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
+        a_off[i] = arow * K * 2 + 16 * q;
     }
-    const uint8_t *s_src = p.w_scales + ((int64_t)e * N + wrow_of(tid)) * (K / C::BLK);
-    const int s_dst = C::S_OFF + tid * C::SB;
-
-    // LDS weight row of this lane in its wave's subtile ns (0, 1)
-    const int brow0 = GATE_UP ? 32 * wave + l32 : 64 * wave + l32;
-    const int brow1 = GATE_UP ? C::BN / 2 + 32 * wave + l32 : 64 * wave + 32 + l32;
-
-    float16_t acc[2][2];
+    float16_t acc[2][NS];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = (float16_t){};
+        for (int j = 0; j < NS; ++j) acc[i][j] = (float16_t){};
 
-    u32x4 a_reg[C::A_ITEMS], b_reg[C::B_ITEMS];
-    uint32_t s_reg = 0;
-    const int n_chunks = K / C::KC;
-    auto load = [&](int c) {
-        const int kn = c * C::KC;
-#pragma unroll
-        for (int i = 0; i < C::A_ITEMS; ++i)
-            a_reg[i] = a_src[i] ? *reinterpret_cast<const u32x4 *>(a_src[i] + 2 * kn) : (u32x4){0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < C::B_ITEMS; ++i)
-            b_reg[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (NV ? kn / 2 : kn));
-        s_reg = C::SB == 4 ? *reinterpret_cast<const uint32_t *>(s_src + kn / C::BLK)
-                           : (uint32_t)*reinterpret_cast<const uint16_t *>(s_src + kn / C::BLK);
-    };
-    auto store = [&](int buf) {
-        uint8_t *base = smem + buf * C::STAGE;
-#pragma unroll
-        for (int i = 0; i < C::A_ITEMS; ++i) *reinterpret_cast<u32x4 *>(base + a_dst[i]) = a_reg[i];
-#pragma unroll
-        for (int i = 0; i < C::B_ITEMS; ++i) *reinterpret_cast<u32x4 *>(base + b_dst[i]) = b_reg[i];
-        if (C::SB == 4) *reinterpret_cast<uint32_t *>(base + s_dst) = s_reg;
-        else *reinterpret_cast<uint16_t *>(base + s_dst) = (uint16_t)s_reg;
-    };
+    // software pipeline: activations two chunks ahead in two register sets (chunk c + 2
+    // is loaded while chunk c is multiplied, and stored to LDS at the end of chunk c + 1),
+    // weights four chunks ahead in a four-slot register ring
+    constexpr int WR = 4;
+    u32x4 a_reg[2][kAItems];
+    u32x4 wcode[WR][NS][CV];
+    uint32_t wsc[WR][NS];
+    const int n_chunks = K / kKC;  // a multiple of WR (K % 256 == 0)
 
-    load(0);
-    store(0);
-    __syncthreads();
-    for (int c = 0; c < n_chunks; ++c) {
-        if (c + 1 < n_chunks) load(c + 1);
-        const uint8_t *base = smem + (c & 1) * C::STAGE;
-#pragma unroll
-        for (int st = 0; st < C::KC / 16; ++st) {
-            const int kk = 16 * st + 8 * g2;  // this lane's k inside the chunk
-            Frag af[2];
-#pragma unroll
-            for (int ms = 0; ms < 2; ++ms)
-                af[ms] = *reinterpret_cast<const Frag *>(base + C::A_OFF + (32 * ms + l32) * C::A_STRIDE + 2 * kk);
-#pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-                const int row = ns ? brow1 : brow0;
-                const uint8_t *brow = base + C::B_OFF + row * C::B_STRIDE;
-                const uint8_t sc = base[C::S_OFF + row * C::SB + (NV ? st : st / 2)];
-                if constexpr (NV) {
-                    const half8 bf = dequant_nvfp4(*reinterpret_cast<const uint32_t *>(brow + kk / 2), e4m3_to_f16(sc));
-#pragma unroll
-                    for (int ms = 0; ms < 2; ++ms)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
-                } else {
-                    const bf16x8 bf = dequant_mxfp8(*reinterpret_cast<const u32x2 *>(brow + kk),
-                                                    __uint_as_float((uint32_t)sc << 23));
-#pragma unroll
-                    for (int ms = 0; ms < 2; ++ms)
-                        acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
-                }
-            }
-        }
-        if (c + 1 < n_chunks) store((c + 1) & 1);
-        __syncthreads();
+#define MOE_LOAD_A(set, c)                                                                                 \
+    _Pragma("unroll") for (int i = 0; i < kAItems; ++i) a_reg[set][i] =                                    \
+        *reinterpret_cast<const u32x4 *>(a_base + a_off[i] + 2 * kKC * (c));
+#define MOE_STORE_A(buf, set)                                                                              \
+    _Pragma("unroll") for (int i = 0; i < kAItems; ++i)                                                    \
+        *reinterpret_cast<u32x4 *>(smem + (buf) * kAStage + a_dst[i]) = a_reg[set][i];
+#define MOE_LOAD_W(slot, c)                                                                                \
+    _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                    \
+        _Pragma("unroll") for (int v = 0; v < CV; ++v) wcode[slot][ns][v] =                                \
+            *reinterpret_cast<const u32x4 *>(wc[ns] + (int64_t)CBLK * (c) + 16 * v);                       \
+        wsc[slot][ns] = *reinterpret_cast<const uint32_t *>(ws[ns] + (int64_t)SBLK * (c));                \
     }
 
-    // ---- epilogue: accumulator v of lane l = row 8(v/4) + 4 g2 + v%4 (+32 ms), column l32
+    MOE_LOAD_A(0, 0);
+    MOE_STORE_A(0, 0);
+    MOE_LOAD_A(1, 1);
+#pragma unroll
+    for (int r = 0; r < WR; ++r) { MOE_LOAD_W(r, r); }
+    __syncthreads();
+
+    for (int c0 = 0; c0 < n_chunks; c0 += WR) {
+#pragma unroll
+        for (int j = 0; j < WR; ++j) {
+            const int c = c0 + j;
+            // LDS buffer c%2 holds chunk c, register set (c+1)%2 chunk c + 1, weight slot j
+            // chunk c. Prefetches past the end reload chunk n - 1 (in bounds, unused), so
+            // the body has no branches and every wait count is exact.
+            MOE_LOAD_A(j & 1, min(c + 2, n_chunks - 1));
+            __builtin_amdgcn_sched_barrier(0);
+            const uint8_t *abuf = smem + (j & 1) * kAStage;
+            // scale words: NVFP4 holds the row's 4 block scales of the chunk (this lane's
+            // pair is bytes 2g, 2g+1); MXFP8 holds two rows' 2 block scales (this lane's
+            // is byte 2 (row % 2) + g)
+            half2_t sc_nv[NS];
+            float sc_mx[NS];
+#pragma unroll
+            for (int ns = 0; ns < NS; ++ns) {
+                if constexpr (NV) {
+                    sc_nv[ns] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsc[j][ns] >> (16 * g2), 1.0f, false);
+                } else {
+                    sc_mx[ns] = __uint_as_float(((wsc[j][ns] >> (8 * (2 * (l32 & 1) + g2))) & 0xffu) << 23);
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < kKC / 16; ++s) {
+                Frag af[2];
+#pragma unroll
+                for (int ms = 0; ms < 2; ++ms)
+                    af[ms] = *reinterpret_cast<const Frag *>(abuf + (32 * ms + l32) * kAStride + 64 * g2 + 16 * s);
+#pragma unroll
+                for (int ns = 0; ns < NS; ++ns) {
+                    if constexpr (NV) {
+                        const _Float16 sc = sc_nv[ns][s >> 1];
+                        const half8 bf = dequant_nvfp4(wcode[j][ns][0][s], sc);
+#pragma unroll
+                        for (int ms = 0; ms < 2; ++ms)
+                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                    } else {
+                        const u32x4 q = wcode[j][ns][s >> 1];
+                        const u32x2 cw = (s & 1) ? (u32x2){q.z, q.w} : (u32x2){q.x, q.y};
+                        const bf16x8 bf = dequant_mxfp8(cw, sc_mx[ns]);
+#pragma unroll
+                        for (int ms = 0; ms < 2; ++ms)
+                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                    }
+                }
+            }
+            MOE_LOAD_W(j, min(c + WR, n_chunks - 1));
+            // buffer (c+1)%2 was last read in chunk c - 1, before the previous barrier
+            MOE_STORE_A((j + 1) & 1, (j + 1) & 1);
+            __syncthreads();
+        }
+    }
+#undef MOE_LOAD_A
+#undef MOE_STORE_A
+#undef MOE_LOAD_W
+
+    // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
     const float scl = NV ? p.a_tscale[0] * p.w_tscale[e] : 1.0f;
     if (GATE_UP) {
-        const int f = n0 + 32 * wave + l32;
         uint32_t amax = 0;
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms) {
+        for (int q = 0; q < NS / 2; ++q) {
+            const int fb = nb * (BN / 2) + wave * 16 * NS + 32 * q;  // first column of this pair
+            const int f = fb + l32;
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                const float hv = swiglu(acc[ms][0][v] * scl, acc[ms][1][v] * scl);
-                if (NV) {
-                    if (m < rows) {
-                        p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
-                        amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
-                    }
-                } else {
-                    // MXFP8: the 32 columns of row m (one block) are the 32 lanes of this half-wave
-                    float a = fabsf(hv);
+            for (int ms = 0; ms < 2; ++ms) {
 #pragma unroll
-                    for (int off = 16; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-                    const int sc8 = e8m0_code_for_amax(a);
-                    const int code = e4m3_encode(ldexpf(hv, -(sc8 - 127)));
-                    if (m < rows) {
-                        const int64_t row = p0 + m;
-                        p.o_codes[row * F + f] = (uint8_t)code;
-                        const float s2 = ldexpf(1.0f, sc8 - 127);
-                        static_cast<uint16_t *>(p.o_vals)[row * F + f] =
-                            (uint16_t)((__float_as_uint(e4m3_value_pos(code & 0x7f) * s2) >> 16) |
-                                       ((uint32_t)(code & 0x80) << 8));
-                        if (l32 == 0) p.o_scales[row * (F / 32) + (n0 + 32 * wave) / 32] = (uint8_t)sc8;
-                        if (p.o_tap) p.o_tap[row * F + f] = hv;
+                for (int v = 0; v < 16; ++v) {
+                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                    const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
+                    if (NV) {
+                        if (m < rows) {
+                            p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
+                            amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
+                        }
+                    } else {
+                        // MXFP8: the 32 columns of row m (one block) are the 32 lanes of this half-wave
+                        float a = fabsf(hv);
+#pragma unroll
+                        for (int off = 16; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
+                        const int sc8 = e8m0_code_for_amax(a);
+                        const int code = e4m3_encode(ldexpf(hv, -(sc8 - 127)));
+                        if (m < rows) {
+                            const int64_t row = p0 + m;
+                            p.o_codes[row * F + f] = (uint8_t)code;
+                            const float s2 = ldexpf(1.0f, sc8 - 127);
+                            static_cast<uint16_t *>(p.o_vals)[row * F + f] =
+                                (uint16_t)((__float_as_uint(e4m3_value_pos(code & 0x7f) * s2) >> 16) |
+                                           ((uint32_t)(code & 0x80) << 8));
+                            if (l32 == 0) p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc8;
+                            if (p.o_tap) p.o_tap[row * F + f] = hv;
+                        }
                     }
                 }
             }
@@ -209,8 +264,8 @@ __global__ void __launch_bounds__(256, 2) tile_gemm_kernel(const GemmArgs p) {
 #pragma unroll
         for (int ms = 0; ms < 2; ++ms)
 #pragma unroll
-            for (int ns = 0; ns < 2; ++ns) {
-                const int n = n0 + 64 * wave + 32 * ns + l32;
+            for (int ns = 0; ns < NS; ++ns) {
+                const int n = nb * BN + wave * 32 * NS + 32 * ns + l32;
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
@@ -222,17 +277,21 @@ __global__ void __launch_bounds__(256, 2) tile_gemm_kernel(const GemmArgs p) {
 
 template <bool NV, bool GATE_UP>
 hipError_t launch_t(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
-    using C = TileCfg<NV>;
-    const int n_tiles_n = GATE_UP ? (a.N / 2) / (C::BN / 2) : a.N / C::BN;
-    hipLaunchKernelGGL((tile_gemm_kernel<NV, GATE_UP>), dim3((unsigned)max_tiles, (unsigned)n_tiles_n), dim3(256), 0,
-                       s, a);
+    constexpr int NS = tile_ns<NV>();
+    constexpr int BN = 128 * NS;
+    const int64_t nb = GATE_UP ? (a.N / 2) / (BN / 2) : a.N / BN;
+    const int64_t items = (int64_t)(max_tiles + kGroup - 1) / kGroup * kGroup * nb;
+    const int64_t grid = (items + 7) / 8 * 8;
+    hipLaunchKernelGGL((tile_gemm_kernel<NV, GATE_UP, NS>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up) {
-    return K % 64 == 0 && (gate_up ? (N / 2) % 128 == 0 : N % 256 == 0);
+    // both formats must fit, since the plan picks one kernel family per layer shape
+    const int bn = 128 * (MOE_TILE_NS_NV > MOE_TILE_NS_MX ? MOE_TILE_NS_NV : MOE_TILE_NS_MX);
+    return K % (4 * kKC) == 0 && (gate_up ? (N / 2) % (bn / 2) == 0 : N % bn == 0);
 }
 
 hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s) {

@@ -1,0 +1,57 @@
+// layout.h - byte layout of packed expert weights (codes and block scales), shared by
+// the weight quantiser and the grouped GEMM kernels.
+//
+// Per expert, a weight matrix [N][K] (N % 32 == 0, K % 64 == 0) is cut into blocks of
+// 32 rows x 64 columns, stored block-row-major ([N/32][K/64]). Inside a block the 32
+// rows follow each other, each holding its 64 columns' codes: 32 bytes for NVFP4 (E2M1,
+// element 2i in the low nibble of byte i) or 64 bytes for MXFP8 (E4M3), so one block is
+// 1 KiB or 2 KiB of contiguous memory. The block scales follow the same block order,
+// 4 bytes (four E4M3 scales of 16) or 2 bytes (two E8M0 scales of 32) per row.
+//
+// The GEMM kernels give each lane one weight row of a 32-row MFMA subtile, so a wave's
+// codes for one 64-column chunk are a single contiguous run instead of 32 strided
+// pieces, and its scales for the chunk one 128- or 64-byte run.
+//
+// In storage order, quantisation block r of an expert (16 values NVFP4, 32 MXFP8) has
+// its codes at byte 8r / 32r and its scale at byte r; its source row and column follow
+// from r below.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+namespace layout {
+
+__host__ __device__ constexpr int code_bytes_per_row(bool nv) { return nv ? 32 : 64; }
+__host__ __device__ constexpr int scale_bytes_per_row(bool nv) { return nv ? 4 : 2; }
+__host__ __device__ constexpr int code_block_bytes(bool nv) { return 32 * code_bytes_per_row(nv); }
+__host__ __device__ constexpr int scale_block_bytes(bool nv) { return 32 * scale_bytes_per_row(nv); }
+
+// index of the 32 x 64 block holding (n, k)
+__host__ __device__ inline int64_t block_index(int64_t K, int64_t n, int64_t k) {
+    return (n >> 5) * (K >> 6) + (k >> 6);
+}
+
+// byte offset inside one expert's codes of element (n, k); k even for NVFP4
+__host__ __device__ inline int64_t code_offset(bool nv, int64_t K, int64_t n, int64_t k) {
+    const int cb = code_bytes_per_row(nv);
+    return block_index(K, n, k) * (32 * cb) + (n & 31) * cb + (nv ? (k & 63) >> 1 : (k & 63));
+}
+
+// byte offset inside one expert's scales of the block scale covering (n, k)
+__host__ __device__ inline int64_t scale_offset(bool nv, int64_t K, int64_t n, int64_t k) {
+    const int sb = scale_bytes_per_row(nv);
+    return block_index(K, n, k) * (32 * sb) + (n & 31) * sb + ((k & 63) >> (nv ? 4 : 5));
+}
+
+// source row and first column of quantisation block r (storage order) of one expert
+__host__ __device__ inline void block_source(bool nv, int64_t K, int64_t r, int64_t &n, int64_t &k) {
+    const int per_row = nv ? 4 : 2;  // quantisation blocks per row of a 32 x 64 block
+    const int64_t piece = r % per_row, row = (r / per_row) & 31, blk = r / (32 * per_row);
+    const int64_t kb = K >> 6;
+    n = 32 * (blk / kb) + row;
+    k = 64 * (blk % kb) + (nv ? 16 : 32) * piece;
+}
+
+}  // namespace layout
+}  // namespace moe

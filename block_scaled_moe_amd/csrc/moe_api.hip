@@ -115,7 +115,7 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     const int32_t fmt = out->fmt, E = out->E, N = out->N, K = out->K;
     if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
     if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
-    if (K % (fmt == MOE_FMT_NVFP4 ? 16 : 32)) return MOE_ERR_INVALID_ARG;
+    if (N % 32 || K % 64) return MOE_ERR_INVALID_ARG;  // tiled layout of include/moe.h
     if (!out->codes || !out->scales || (fmt == MOE_FMT_NVFP4 && !out->tensor_scale)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(out->codes) || ((uintptr_t)out->tensor_scale & 3u)) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;

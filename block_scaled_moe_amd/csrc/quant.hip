@@ -10,6 +10,7 @@
 // pass, then a tiny pass turning the amax into the fp32 tensor scale.
 #include "formats.h"
 #include "internal.h"
+#include "layout.h"
 
 namespace moe {
 namespace {
@@ -77,18 +78,21 @@ __device__ __forceinline__ void store_dequant16(_Float16 *dst, uint32_t lo, uint
     d[1] = make_uint4(o[4], o[5], o[6], o[7]);
 }
 
-// NVFP4 weights: block b of expert e = b / blocks_per_expert; the tensor scale comes
-// from the expert's amax (fp32 bits, filled by amax_bf16_kernel).
+// NVFP4 weights, in the packed tile layout (layout.h): thread b writes storage block
+// b (codes at 8b, scale at b) from its source row and columns in the bf16 masters; the
+// tensor scale comes from the expert's amax (fp32 bits, filled by amax_bf16_kernel).
 __global__ void __launch_bounds__(kThreads) quant_w_nvfp4_kernel(const uint16_t *__restrict__ w, int64_t n_blocks,
-                                                                 int64_t blocks_per_expert,
+                                                                 int64_t blocks_per_expert, int32_t K,
                                                                  const uint32_t *__restrict__ amax_bits,
                                                                  uint8_t *__restrict__ codes,
                                                                  uint8_t *__restrict__ scales) {
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e = b / blocks_per_expert;
+        int64_t n, k;
+        layout::block_source(true, K, b - e * blocks_per_expert, n, k);
         const float sg = nvfp4_tensor_scale(__uint_as_float(amax_bits[e]));
         float x[16];
-        load16_bf16(w + b * 16, x);
+        load16_bf16(w + (e * (blocks_per_expert / (K / 16)) + n) * K + k, x);
         uint32_t lo, hi;
         int sc;
         nvfp4_quant_block(x, sg, lo, hi, sc);
@@ -102,14 +106,24 @@ __global__ void finish_tensor_scale_kernel(float *ts, int32_t n) {
     if (i < n) ts[i] = nvfp4_tensor_scale(ts[i]);
 }
 
-// MXFP8 (weights or hidden states): one thread per 32-block of a [rows][K] bf16 tensor;
-// deq (optional) receives the exact bf16 values code * 2^(scale - 127).
+// MXFP8: one thread per 32-block. Hidden states (tile_K == 0): block b of a row-major
+// [rows][K] bf16 tensor, codes row-major too; deq (optional) receives the exact bf16
+// values code * 2^(scale - 127). Weights (tile_K == K): storage block b of the packed
+// tile layout (layout.h), read from its source row and columns of [E][N][K] masters.
 __global__ void __launch_bounds__(kThreads) quant_mxfp8_bf16_kernel(const uint16_t *__restrict__ x, int64_t n_blocks,
+                                                                    int32_t tile_K, int64_t blocks_per_expert,
                                                                     uint8_t *__restrict__ codes,
                                                                     uint8_t *__restrict__ scales,
                                                                     uint16_t *__restrict__ deq) {
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(x + b * 32);
+        int64_t src_off = b * 32;
+        if (tile_K) {
+            const int64_t e = b / blocks_per_expert;
+            int64_t n, k;
+            layout::block_source(false, tile_K, b - e * blocks_per_expert, n, k);
+            src_off = (e * (blocks_per_expert / (tile_K / 32)) + n) * tile_K + k;
+        }
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + src_off);
         float v[32];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -230,7 +244,7 @@ hipError_t launch_quant_weights_nvfp4(const uint16_t *w, int32_t E, int32_t N, i
                                       uint8_t *codes, uint8_t *scales, hipStream_t s) {
     const int64_t per = (int64_t)N * (K / 16);
     const int64_t nb = per * E;
-    hipLaunchKernelGGL(quant_w_nvfp4_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, per, amax_bits, codes,
+    hipLaunchKernelGGL(quant_w_nvfp4_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, per, K, amax_bits, codes,
                        scales);
     return hipGetLastError();
 }
@@ -242,8 +256,9 @@ hipError_t launch_finish_tensor_scale(float *ts, int32_t n, hipStream_t s) {
 
 hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
                                       uint8_t *scales, hipStream_t s) {
-    const int64_t nb = (int64_t)E * N * (K / 32);
-    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, codes, scales,
+    const int64_t per = (int64_t)N * (K / 32);
+    const int64_t nb = per * E;
+    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, K, per, codes, scales,
                        (uint16_t *)nullptr);
     return hipGetLastError();
 }
@@ -259,8 +274,8 @@ hipError_t launch_quant_act_nvfp4(const uint16_t *h, int32_t T, int32_t D, const
 hipError_t launch_quant_act_mxfp8(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
                                   uint16_t *deq_bf16, hipStream_t s) {
     const int64_t nb = (int64_t)T * (D / 32);
-    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, h, nb, codes, scales,
-                       deq_bf16);
+    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, h, nb, 0, (int64_t)0, codes,
+                       scales, deq_bf16);
     return hipGetLastError();
 }
 

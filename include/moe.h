@@ -52,14 +52,22 @@ extern "C" {
 #define MOE_FMT_MXFP8 2
 
 /*
- * Packed expert weights of one matrix kind for E experts, each [N][K] row-major
- * (K is the reduction dimension), in the canonical byte layout:
- *   NVFP4: codes  u8 [E][N][K/2]  E2M1, element 2i in the low nibble of byte i
- *          scales u8 [E][N][K/16] E4M3 (OCP "FN": bias 7, max 448, no inf)
+ * Packed expert weights of one matrix kind for E experts, each logically [N][K]
+ * (K is the reduction dimension; N % 32 == 0, K % 64 == 0), stored per expert in a
+ * tiled byte layout: the matrix is cut into 32-row x 64-column blocks kept in
+ * block-row-major order ([N/32][K/64]); a block holds its 32 rows one after another,
+ * each row with the codes of its 64 columns; the scales use the same block order.
+ *   NVFP4: codes  u8 [E][N/32][K/64][32][32] E2M1, element 2i in the low nibble of byte i
+ *          scales u8 [E][N/32][K/64][32][4]  E4M3 (OCP "FN": bias 7, max 448, no inf),
+ *                                            one per 16 columns
  *          tensor_scale fp32 [E]  one per expert and matrix (amax / 2688, or 1)
- *   MXFP8: codes  u8 [E][N][K]    E4M3
- *          scales u8 [E][N][K/32] E8M0 (2^(c - 127))
+ *   MXFP8: codes  u8 [E][N/32][K/64][32][64] E4M3
+ *          scales u8 [E][N/32][K/64][32][2]  E8M0 (2^(c - 127)), one per 32 columns
  *          tensor_scale unused (may be NULL)
+ * Sizes are those of the row-major arrays ([E][N][K/2] / [E][N][K] codes, [E][N][K/16]
+ * / [E][N][K/32] scales); only the order differs. The tiling lets one wave of the
+ * expert GEMMs load a 32-row weight subtile's codes for 64 columns as a single
+ * contiguous 1 KiB (NVFP4) or 2 KiB (MXFP8) run.
  */
 typedef struct moe_packed {
     int32_t fmt;
@@ -127,7 +135,7 @@ const char *moe_status_string(int32_t status);
  * with the smaller fp32 squared error (ties keep r/6). MXFP8: per 32-block, E8M0
  * exponent floor(log2 amax_b) - 8, codes E4M3(x * 2^-exponent). All roundings are
  * IEEE round-to-nearest-even with saturation to the format's largest finite value.
- * K must be a multiple of 16 (NVFP4) or 32 (MXFP8).
+ * N must be a multiple of 32 and K of 64 (the tiled layout above).
  */
 int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
 

@@ -21,6 +21,13 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def untile(a: np.ndarray) -> np.ndarray:
+    """Packed weight bytes [E][N/32][K/64][32][b] (tiled layout of include/moe.h) ->
+    the row-major [E][N][K/64 * b] arrays the oracle produces (a pure reordering)."""
+    E, nb, kb, r, b = a.shape
+    return np.ascontiguousarray(a.transpose(0, 1, 3, 2, 4)).reshape(E, nb * r, kb * b)
+
+
 def rms(x: np.ndarray) -> float:
     return float(np.sqrt(np.mean(np.asarray(x, np.float64) ** 2)))
 

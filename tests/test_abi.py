@@ -107,9 +107,13 @@ def test_route_and_quantize_validate_on_the_host():
     assert lib.moe_route(4, 64, 16, 9, p(A16), p(A16), None, p(A16), p(A16), p(A16), None, None) == EINVAL
     assert lib.moe_route(4, 64, 16, 8, p(A16 + 2), p(A16), None, p(A16), p(A16), p(A16), None, None) == EALIGN
     assert lib.moe_route(0, 64, 16, 8, None, None, None, None, None, None, None, None) == OK
-    bad = moe.MoePacked(1, 2, 16, 24, A16, A16, A16)  # NVFP4 K must be a multiple of 16
+    bad = moe.MoePacked(1, 2, 32, 96, A16, A16, A16)   # K must be a multiple of 64 (tiled layout)
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
-    bad = moe.MoePacked(2, 2, 16, 48, A16, A16, 0)     # MXFP8 K must be a multiple of 32
+    bad = moe.MoePacked(2, 2, 48, 64, A16, A16, 0)     # N must be a multiple of 32 (tiled layout)
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
-    bad = moe.MoePacked(1, 2, 16, 32, A16, A16, 0)     # NVFP4 needs tensor scales
+    bad = moe.MoePacked(1, 2, 32, 64, A16, A16, 0)     # NVFP4 needs the tensor-scale buffer
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
+    bad = moe.MoePacked(3, 2, 32, 64, A16, A16, A16)   # unknown format
+    assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
+    bad = moe.MoePacked(2, 2, 32, 64, A16 + 8, A16, 0)  # misaligned codes
+    assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EALIGN
