@@ -182,8 +182,10 @@ def main():
     out = torch.empty((T, D), dtype=torch.float32, device=dev)
     nv = wl.fmt == "nvfp4"
 
+    route_ws = moe.route_workspace(T, D, E, dev)
+
     def step(events=None):
-        idx, w, _, amax = moe.route(d_h, d_wr, k, d_bias, want_amax=nv)
+        idx, w, _, amax = moe.route(d_h, d_wr, k, d_bias, want_amax=nv, workspace=route_ws)
         layer.forward(d_h, idx, w, out=out, h_amax=amax, events=events)
         return idx
 

@@ -64,7 +64,8 @@ SIGNATURES = {
     "moe_abi_version": ([], ctypes.c_int32),
     "moe_status_string": ([ctypes.c_int32], ctypes.c_char_p),
     "moe_quantize_weights": ([ctypes.c_void_p, ctypes.POINTER(MoePacked), ctypes.c_void_p], ctypes.c_int32),
-    "moe_route": ([ctypes.c_int32] * 4 + [ctypes.c_void_p] * 8, ctypes.c_int32),
+    "moe_route_workspace_bytes": ([ctypes.c_int32] * 3, ctypes.c_size_t),
+    "moe_route": ([ctypes.c_int32] * 4 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int32),
     "moe_forward_validate": ([ctypes.POINTER(MoeForwardArgs)], ctypes.c_int32),
     "moe_forward_workspace_bytes": ([ctypes.POINTER(MoeForwardArgs)], ctypes.c_size_t),
     "moe_forward": ([ctypes.POINTER(MoeForwardArgs), ctypes.c_void_p], ctypes.c_int32),
@@ -153,19 +154,28 @@ def quantize_weights(fmt: str, w: torch.Tensor, out: PackedWeights | None = None
     return out
 
 
+def route_workspace(T: int, D: int, E: int, device="cuda") -> torch.Tensor:
+    """Device scratch for moe_route over T tokens (reusable across calls of that size)."""
+    n = int(lib().moe_route_workspace_bytes(T, D, E))
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
 def route(h: torch.Tensor, wr: torch.Tensor, top_k: int = 8, bias: torch.Tensor | None = None,
-          want_amax: bool = False):
-    """Router (moe_route) -> (topk_idx int32 [T,k], topk_w fp32 [T,k], logits fp32 [T,E], h_amax | None)."""
+          want_amax: bool = False, want_logits: bool = False, workspace: torch.Tensor | None = None):
+    """Router (moe_route) -> (topk_idx int32 [T,k], topk_w fp32 [T,k], logits fp32 [T,E] | None,
+    h_amax | None). Logits are computed in full only when want_logits is set."""
     h, wr = _bf16_view(h), _bf16_view(wr)
     T, D = h.shape
     E = wr.shape[0]
     dev = h.device
     idx = torch.empty((T, top_k), dtype=torch.int32, device=dev)
     w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
-    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev) if want_logits else None
     amax = torch.empty(4, dtype=torch.float32, device=dev) if want_amax else None
+    if workspace is None:
+        workspace = route_workspace(T, D, E, dev)
     _check(lib().moe_route(T, D, E, top_k, _ptr(h), _ptr(wr), _ptr(bias), _ptr(logits), _ptr(idx), _ptr(w),
-                           _ptr(amax), _stream(dev)), "moe_route")
+                           _ptr(amax), _ptr(workspace), workspace.numel(), _stream(dev)), "moe_route")
     return idx, w, logits, amax
 
 

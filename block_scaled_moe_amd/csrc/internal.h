@@ -38,10 +38,18 @@ hipError_t launch_quant_inter_nvfp4(const float *x, int32_t max_rows, int32_t F,
                                     hipStream_t s);
 
 // ---- router (route.hip)
-hipError_t launch_router_logits(int32_t T, int32_t D, int32_t E, const uint16_t *h, const uint16_t *wr,
-                                const float *bias, float *logits, uint32_t *amax_bits, hipStream_t s);
-hipError_t launch_router_topk(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *idx,
-                              float *w, hipStream_t s);
+// Workspace plan of one moe_route call (byte offsets into the caller's workspace).
+struct RoutePlan {
+    bool screen;          // MFMA screening + exact candidates (large T), else all exact
+    int32_t Ep, n_parts;  // padded expert count; 64-wide K blocks of the weight norms
+    size_t off_wk4, off_logits, off_wk8, off_wpart, off_hn, off_wn, bytes;
+};
+RoutePlan route_plan(int32_t T, int32_t D, int32_t E);
+// logits_out: fp32 [T][E] exact logits, or NULL; amax_bits: max |h| (fp32 bits, the
+// caller zeroes it first) or NULL
+hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int32_t k, const uint16_t *h,
+                        const uint16_t *wr, const float *bias, float *logits_out, int32_t *idx, float *w,
+                        uint32_t *amax_bits, void *workspace, hipStream_t s);
 
 // ---- permutation (permute.hip)
 struct PermuteArgs {

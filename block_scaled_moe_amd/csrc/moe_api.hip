@@ -128,20 +128,28 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     return to_status(launch_finish_tensor_scale(out->tensor_scale, E, s));
 }
 
+size_t moe_route_workspace_bytes(int32_t T, int32_t D, int32_t E) {
+    if (T <= 0 || D <= 0 || D % 64 || E <= 0 || E > 1024) return 0;
+    return route_plan(T, D, E).bytes;
+}
+
 int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t *h, const uint16_t *wr,
                   const float *bias, float *logits, int32_t *topk_idx, float *topk_w, float *h_amax,
-                  void *stream) {
+                  void *workspace, size_t workspace_bytes, void *stream) {
     if (T < 0 || D <= 0 || E <= 0 || E > 1024 || top_k < 1 || top_k > 8 || top_k > E) return MOE_ERR_INVALID_ARG;
+    if (D % 64) return MOE_ERR_UNSUPPORTED;
     if (T == 0) return MOE_OK;
-    if (!h || !wr || !logits || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(h) || !aligned16(wr) || !aligned16(logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
-        (bias && !aligned16(bias)) || (h_amax && !aligned16(h_amax)))
+    if (!h || !wr || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(h) || !aligned16(wr) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+        (logits && !aligned16(logits)) || (bias && !aligned16(bias)) || (h_amax && !aligned16(h_amax)))
         return MOE_ERR_ALIGNMENT;
+    const RoutePlan plan = route_plan(T, D, E);
+    if (!workspace || workspace_bytes < plan.bytes) return MOE_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
     uint32_t *amax = reinterpret_cast<uint32_t *>(h_amax);
     if (amax) MOE_TRY(launch_fill_u32(amax, 0u, 1, s));
-    MOE_TRY(launch_router_logits(T, D, E, h, wr, bias, logits, amax, s));
-    return to_status(launch_router_topk(T, E, top_k, logits, topk_idx, topk_w, s));
+    return to_status(launch_route(plan, T, D, E, top_k, h, wr, bias, logits, topk_idx, topk_w, amax, workspace, s));
 }
 
 }  // extern "C"

@@ -1,187 +1,543 @@
 // route.hip - softmax-then-top-k router (vLLM recipe "thinkingmachines/Inkling-2-Small",
 // section "Overview": each token is routed to 8 of 384 experts, no shared expert).
 //
-// Logits: logits[t][e] = sum over d ascending of h[t][d] * wr[e][d] in fp32 from +0.
-// Each bf16 product is exact in fp32, so fmaf(h, w, acc) rounds exactly like
-// acc + h*w; the fixed order makes the top-k selection a deterministic function of
-// the inputs. Each logit is one dependent chain of D FMAs, so the kernel is a
-// register-blocked SIMT product: a wave owns TPW tokens and 64*EPL experts (lane =
-// expert column), h values are LDS broadcasts, and the K chunks are prefetched two
-// ahead into registers and double-buffered in LDS so the chains never wait on memory.
+// The specified logit is logits[t][e] = sum over d ascending of h[t][d] * wr[e][d] in
+// fp32 from +0 (each bf16 product is exact in fp32, so fmaf(h, w, acc) rounds exactly
+// like acc + h*w), plus bias[e]. Top-k is by (logit desc, index asc) and the weights
+// are the fp64 softmax of the selected logits renormalised over the k. Each logit is a
+// dependent chain of D FMAs, so computing all T*E of them is VALU-bound; two paths:
+//
+//  exact (small T, or when the caller asks for all logits): one expert per lane and a
+//    few tokens per wave, h broadcast from wave-uniform loads, the router weight read
+//    from an expert-fastest fp32 copy (coalesced 16-byte loads); then the top-k kernel.
+//
+//  screened (large T): all logits approximated by a bf16 MFMA GEMM (exact products,
+//    fp32 sums in the hardware's order), then per token a rigorous bound on the gap to
+//    the sequential sum keeps only experts that can still reach the top k; their logits
+//    are recomputed by the exact chain and the top k chosen among them. The bound: both
+//    sums approximate S = sum_d p_d with |fl(S) - S| <= gamma_D sum_d |p_d| for any
+//    summation order (unit 2^-24 for the sequential RNE chain, 2^-23 allowed for the
+//    MFMA's internal rounding), plus D * 2^-124 for denormal flushes, and
+//    sum_d |p_d| <= ||h_t|| ||w_e|| (Cauchy-Schwarz). If lo_e <= logit_e <= hi_e and
+//    theta is the k-th largest lo, at least k experts have logit >= theta, so the k-th
+//    largest logit is >= theta and every expert with hi_e < theta lies strictly below
+//    it; the top k (ties included) are therefore among {e : hi_e >= theta}, and the
+//    selection there is the same as over all experts. Indices and weights are
+//    bit-identical to the exact path.
 #include "formats.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-// LDS tiles are row-major with one padding float per row, so a lane per expert reads
-// ws[e][k] from distinct banks and the 8-byte stores of 4 consecutive k stay simple.
-template <int TPW, int EPL, int KC>
-struct RouterCfg {
-    static constexpr int BT = 4 * TPW;          // tokens per workgroup
-    static constexpr int BE = 64 * EPL;         // experts per workgroup
-    static constexpr int HS = KC + 4;           // floats per LDS h row
-    static constexpr int WS = KC + 1;           // floats per LDS router-weight row
-    static constexpr int H_TOTAL = BT * KC / 4; // 8-byte (4 x bf16) loads per chunk
-    static constexpr int W_TOTAL = BE * KC / 4;
-    static constexpr int H_ITEMS = (H_TOTAL + 255) / 256;
-    static constexpr int W_ITEMS = (W_TOTAL + 255) / 256;
-    static constexpr int BUF = BT * HS + BE * WS;  // floats per LDS buffer
-};
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int TPW, int EPL, int KC>
-__global__ void __launch_bounds__(256) router_logits_kernel(int32_t T, int32_t D, int32_t E,
-                                                            const uint16_t *__restrict__ h,
-                                                            const uint16_t *__restrict__ wr,
-                                                            const float *__restrict__ bias,
-                                                            float *__restrict__ logits,
-                                                            uint32_t *__restrict__ amax_bits) {
-    using C = RouterCfg<TPW, EPL, KC>;
-    __shared__ float lds[2][C::BUF];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int t0 = blockIdx.x * C::BT, e0 = blockIdx.y * C::BE;
-    const bool do_amax = amax_bits != nullptr && blockIdx.y == 0;
-    uint32_t amax = 0;
+constexpr int kMaxE = 1024;       // experts supported by the selection kernels
+constexpr int kScreenMinT = 512;  // tokens from which the screened path is used
+constexpr int kScreenMaxE = 512;  // experts up to which it is (LDS of the selection)
 
-    float acc[TPW][EPL];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i)
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) acc[i][j] = 0.0f;
-
-    // two register sets of prefetched 8-byte loads (4 bf16 each); zero past T, E or D
-    uint2 rh[2][C::H_ITEMS], rw[2][C::W_ITEMS];
-    const int n_chunks = (D + KC - 1) / KC;
-    auto load = [&](uint2 (&dh)[C::H_ITEMS], uint2 (&dw)[C::W_ITEMS], int c) {
-        const int k0 = c * KC;
-#pragma unroll
-        for (int i = 0; i < C::H_ITEMS; ++i) {
-            const int item = tid + 256 * i;
-            const int r = item / (KC / 4), k = k0 + 4 * (item % (KC / 4));
-            const int t = t0 + r;
-            dh[i] = make_uint2(0, 0);
-            if (item < C::H_TOTAL && t < T && k < D) {
-                const uint16_t *src = h + (int64_t)t * D + k;
-                if (k + 4 <= D && ((reinterpret_cast<uintptr_t>(src) & 7) == 0)) {
-                    dh[i] = *reinterpret_cast<const uint2 *>(src);
-                } else {
-                    uint32_t v[4] = {0, 0, 0, 0};
-                    for (int q = 0; q < 4 && k + q < D; ++q) v[q] = src[q];
-                    dh[i] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::W_ITEMS; ++i) {
-            const int item = tid + 256 * i;
-            const int r = item / (KC / 4), k = k0 + 4 * (item % (KC / 4));
-            const int e = e0 + r;
-            dw[i] = make_uint2(0, 0);
-            if (item < C::W_TOTAL && e < E && k < D) {
-                const uint16_t *src = wr + (int64_t)e * D + k;
-                if (k + 4 <= D && ((reinterpret_cast<uintptr_t>(src) & 7) == 0)) {
-                    dw[i] = *reinterpret_cast<const uint2 *>(src);
-                } else {
-                    uint32_t v[4] = {0, 0, 0, 0};
-                    for (int q = 0; q < 4 && k + q < D; ++q) v[q] = src[q];
-                    dw[i] = make_uint2(v[0] | (v[1] << 16), v[2] | (v[3] << 16));
-                }
-            }
-        }
-    };
-    auto store = [&](const uint2 (&dh)[C::H_ITEMS], const uint2 (&dw)[C::W_ITEMS], float *buf) {
-#pragma unroll
-        for (int i = 0; i < C::H_ITEMS; ++i) {
-            const int item = tid + 256 * i;
-            if (item >= C::H_TOTAL) continue;
-            const int r = item / (KC / 4), kq = 4 * (item % (KC / 4));
-            float *d = buf + r * C::HS + kq;
-            d[0] = __uint_as_float(dh[i].x << 16);
-            d[1] = __uint_as_float(dh[i].x & 0xffff0000u);
-            d[2] = __uint_as_float(dh[i].y << 16);
-            d[3] = __uint_as_float(dh[i].y & 0xffff0000u);
-            if (do_amax) {
-                amax = max(amax, max(max(dh[i].x & 0x7fffu, (dh[i].x >> 16) & 0x7fffu),
-                                     max(dh[i].y & 0x7fffu, (dh[i].y >> 16) & 0x7fffu)));
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < C::W_ITEMS; ++i) {
-            const int item = tid + 256 * i;
-            if (item >= C::W_TOTAL) continue;
-            const int r = item / (KC / 4), kq = 4 * (item % (KC / 4));
-            float *d = buf + C::BT * C::HS + r * C::WS + kq;
-            d[0] = __uint_as_float(dw[i].x << 16);
-            d[1] = __uint_as_float(dw[i].x & 0xffff0000u);
-            d[2] = __uint_as_float(dw[i].y << 16);
-            d[3] = __uint_as_float(dw[i].y & 0xffff0000u);
-        }
-    };
-
-    load(rh[0], rw[0], 0);
-    if (n_chunks > 1) load(rh[1], rw[1], 1);
-    for (int c = 0; c < n_chunks; c += 2) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {  // register set s holds chunk c + s
-            const int cc = c + s;
-            if (cc >= n_chunks) break;
-            float *buf = lds[s];
-            store(rh[s], rw[s], buf);
-            __syncthreads();
-            if (cc + 2 < n_chunks) load(rh[s], rw[s], cc + 2);
-            const int kc = min(KC, D - cc * KC);
-            const float *hb = buf + (wave * TPW) * C::HS;
-            const float *wb = buf + C::BT * C::HS + lane * C::WS;
-            // k strictly ascending for every accumulator; full chunks are unrolled so the
-            // LDS reads run ahead of the dependent FMA chain
-            auto step = [&](int kk) {
-                float hv[TPW], wv[EPL];
-#pragma unroll
-                for (int i = 0; i < TPW; ++i) hv[i] = hb[i * C::HS + kk];
-#pragma unroll
-                for (int j = 0; j < EPL; ++j) wv[j] = wb[64 * j * C::WS + kk];
-#pragma unroll
-                for (int i = 0; i < TPW; ++i)
-#pragma unroll
-                    for (int j = 0; j < EPL; ++j) acc[i][j] = __builtin_fmaf(hv[i], wv[j], acc[i][j]);
-            };
-            if (kc == KC) {
-#pragma unroll 16
-                for (int kk = 0; kk < KC; ++kk) step(kk);
-            } else {
-                for (int kk = 0; kk < kc; ++kk) step(kk);
-            }
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-        const int t = t0 + wave * TPW + i;
-        if (t >= T) continue;
-#pragma unroll
-        for (int j = 0; j < EPL; ++j) {
-            const int e = e0 + lane + 64 * j;
-            if (e >= E) continue;
-            float v = acc[i][j];
-            if (bias) v = v + bias[e];
-            logits[(int64_t)t * E + e] = v;
-        }
-    }
-    if (do_amax) {
-        for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-        if (lane == 0 && amax) atomicMax(amax_bits, amax << 16);
-    }
-}
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // (value, index) a ranks before (value, index) b: larger logit, ties to the lower index
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
     return va > vb || (va == vb && ia < ib);
 }
 
-// One wave per token: the token's logits are read once into registers (expert
-// e = lane + 64 i), then k rounds of a wave-wide arg-max over the not-yet-taken experts,
-// then the renormalised softmax weights of the selected logits in fp64.
-constexpr int kTopkMaxE = 1024;  // experts held in registers (16 per lane)
+// ---- router weight copies with the expert index fastest: wk4 fp32 [D/4][Ep][4],
+// wk8 bf16 [D/8][Ep][8] (optional), zero past E; wpart fp64 [D/64][Ep] partial sums
+// of w^2 (optional). One thread per (expert, 64-wide K block): it reads one full line
+// of its row, and consecutive threads write consecutive experts.
+__global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, int32_t Ep,
+                                                          const uint16_t *__restrict__ wr, float *__restrict__ wk4,
+                                                          uint16_t *__restrict__ wk8, double *__restrict__ wpart) {
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= Ep) return;
+    const int k0 = 64 * blockIdx.y;
+    u32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = e < E ? *reinterpret_cast<const u32x4 *>(wr + (int64_t)e * D + k0 + 8 * i) : (u32x4){0u, 0u, 0u, 0u};
+    double ss = 0.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int k = k0 + 8 * i;
+        if (wk8) *reinterpret_cast<u32x4 *>(wk8 + ((int64_t)(k / 8) * Ep + e) * 8) = v[i];
+        const float f[8] = {bf_lo(v[i].x), bf_hi(v[i].x), bf_lo(v[i].y), bf_hi(v[i].y),
+                            bf_lo(v[i].z), bf_hi(v[i].z), bf_lo(v[i].w), bf_hi(v[i].w)};
+        *reinterpret_cast<float4 *>(wk4 + ((int64_t)(k / 4) * Ep + e) * 4) = make_float4(f[0], f[1], f[2], f[3]);
+        *reinterpret_cast<float4 *>(wk4 + ((int64_t)(k / 4 + 1) * Ep + e) * 4) = make_float4(f[4], f[5], f[6], f[7]);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) ss += (double)f[q] * (double)f[q];
+    }
+    if (wpart) wpart[(int64_t)blockIdx.y * Ep + e] = ss;
+}
 
+// ---- exact logits: wave = TPW tokens x 64 experts (one per lane); the chains of a
+// lane run k ascending. h is read with wave-uniform addresses (broadcast).
+template <int TPW>
+__global__ void __launch_bounds__(256) router_exact_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep,
+                                                           const uint16_t *__restrict__ h,
+                                                           const float *__restrict__ wk4,
+                                                           const float *__restrict__ bias, float *__restrict__ logits,
+                                                           uint32_t *__restrict__ amax_bits) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int eg = blockIdx.y * 4 + wave;  // 64-expert group of this wave
+    if (eg * 64 >= Ep) return;
+    const int e = eg * 64 + lane;
+    const int t0 = blockIdx.x * TPW;
+    const uint16_t *hp[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) hp[i] = h + (int64_t)min(t0 + i, T - 1) * D;
+    const float *wp = wk4 + (int64_t)e * 4;
+    const int64_t wstep = (int64_t)Ep * 4;
+    const bool do_amax = amax_bits != nullptr && eg == 0;
+    uint32_t amax = 0;
+    float acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = 0.0f;
+    // 32-k blocks, the next one loaded while the current one is multiplied
+    constexpr int KB = 32;
+    const int nb = D / KB;  // even (D % 64 == 0)
+    float4 wv[2][KB / 4];
+    u32x4 hv[2][TPW][KB / 8];
+    auto load = [&](int buf, int blk) {
+#pragma unroll
+        for (int q = 0; q < KB / 4; ++q)
+            wv[buf][q] = *reinterpret_cast<const float4 *>(wp + (int64_t)(blk * (KB / 4) + q) * wstep);
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+#pragma unroll
+            for (int q = 0; q < KB / 8; ++q)
+                hv[buf][i][q] = *reinterpret_cast<const u32x4 *>(hp[i] + blk * KB + 8 * q);
+    };
+    auto compute = [&](int buf) {
+#pragma unroll
+        for (int q = 0; q < KB / 8; ++q) {
+            const float4 w0 = wv[buf][2 * q], w1 = wv[buf][2 * q + 1];
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const u32x4 x = hv[buf][i][q];
+                float a = acc[i];
+                a = __builtin_fmaf(bf_lo(x.x), w0.x, a);
+                a = __builtin_fmaf(bf_hi(x.x), w0.y, a);
+                a = __builtin_fmaf(bf_lo(x.y), w0.z, a);
+                a = __builtin_fmaf(bf_hi(x.y), w0.w, a);
+                a = __builtin_fmaf(bf_lo(x.z), w1.x, a);
+                a = __builtin_fmaf(bf_hi(x.z), w1.y, a);
+                a = __builtin_fmaf(bf_lo(x.w), w1.z, a);
+                a = __builtin_fmaf(bf_hi(x.w), w1.w, a);
+                acc[i] = a;
+                if (do_amax && t0 + i < T) {
+                    amax = max(amax, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu),
+                                         max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
+                    amax = max(amax, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu),
+                                         max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
+                }
+            }
+        }
+    };
+    load(0, 0);
+    for (int blk = 0; blk < nb; blk += 2) {
+        load(1, blk + 1);
+        compute(0);
+        load(0, min(blk + 2, nb - 1));  // past the end: reload the last block (unused)
+        compute(1);
+    }
+    if (e < E) {
+        const float b = bias ? bias[e] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < TPW; ++i)
+            if (t0 + i < T) logits[(int64_t)(t0 + i) * E + e] = bias ? acc[i] + b : acc[i];
+    }
+    if (do_amax && lane == 0 && amax) atomicMax(amax_bits, amax << 16);
+}
+
+// ---- approximate logits by bf16 MFMA: workgroup = 32 tokens x 128 experts, wave =
+// 32 x 32 (one v_mfma_f32_32x32x16_bf16 tile); K in 64-wide chunks with the same k
+// permutation for both operands (lane half g supplies k = 32g + 8s for step s). The h
+// tile goes through a double-buffered LDS tile; the weight fragments are 16-byte
+// coalesced loads from wk8. Workgroups of the first expert tile also write
+// hn[t] = sum h^2 (fp64) and max |h|; those of the first token tile write
+// wn[e] = ||w_e|| rounded up, from the partial sums.
+constexpr int kHStride = 64 * 2 + 16;  // LDS bytes per h row
+
+__global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, int32_t Ep, int32_t n_parts,
+                                                          const uint16_t *__restrict__ h,
+                                                          const uint16_t *__restrict__ wk8,
+                                                          const double *__restrict__ wpart, float *__restrict__ lt,
+                                                          double *__restrict__ hn, float *__restrict__ wn,
+                                                          uint32_t *__restrict__ amax_bits) {
+    __shared__ __attribute__((aligned(16))) uint8_t hs[2][32 * kHStride];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, g2 = lane >> 5;
+    const int t0 = blockIdx.x * 32;
+    const int e = blockIdx.y * 128 + wave * 32 + l32;  // this lane's expert (B column)
+    const bool stats = blockIdx.y == 0;
+
+    if (blockIdx.x == 0 && tid < 128) {
+        const int ee = blockIdx.y * 128 + tid;
+        double ss = 0.0;
+        for (int p = 0; p < n_parts; ++p) ss += wpart[(int64_t)p * Ep + ee];
+        // sqrt and the fp32 rounding each lose < 1 ulp; the factor keeps it an upper bound
+        wn[ee] = (float)(sqrt(ss) * (1.0 + 0x1p-20));
+    }
+
+    // h staging: thread (row r, 16-byte piece q) of the 32 x 64 chunk
+    const int r = tid >> 3, q = tid & 7;
+    const uint16_t *hsrc = h + (int64_t)min(t0 + r, T - 1) * D + 8 * q;
+    const int hdst = r * kHStride + 16 * q;
+    const bool hlive = t0 + r < T;
+    const uint16_t *bsrc = wk8 + (int64_t)e * 8 + (int64_t)(4 * g2) * Ep * 8;  // k = 32 g2 within the chunk
+    const int64_t bstep = (int64_t)Ep * 8;  // one k-octet
+
+    double ss = 0.0;
+    uint32_t amax = 0;
+    float16_t acc = {};
+    const int n_chunks = D / 64;
+    u32x4 hreg = *reinterpret_cast<const u32x4 *>(hsrc);
+    u32x4 breg[2][4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) breg[0][s] = *reinterpret_cast<const u32x4 *>(bsrc + s * bstep);
+    *reinterpret_cast<u32x4 *>(hs[0] + hdst) = hreg;
+    __syncthreads();
+    for (int c0 = 0; c0 < n_chunks; c0 += 2) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int c = c0 + j;
+            if (c >= n_chunks) break;
+            if (stats && hlive) {
+                const uint32_t w4[4] = {hreg.x, hreg.y, hreg.z, hreg.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float a = bf_lo(w4[i]), b = bf_hi(w4[i]);
+                    ss += (double)a * a + (double)b * b;
+                    amax = max(amax, max(w4[i] & 0x7fffu, (w4[i] >> 16) & 0x7fffu));
+                }
+            }
+            const int cn = min(c + 1, n_chunks - 1);
+            hreg = *reinterpret_cast<const u32x4 *>(hsrc + 64 * cn);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                breg[1 - j][s] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)(8 * cn + s) * bstep);
+            const uint8_t *abuf = hs[j];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(abuf + l32 * kHStride + 64 * g2 + 16 * s);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, breg[j][s]), acc, 0, 0,
+                                                              0);
+            }
+            *reinterpret_cast<u32x4 *>(hs[1 - j] + hdst) = hreg;
+            __syncthreads();
+        }
+    }
+    // accumulator v of lane l: token row 8(v/4) + 4 g2 + v%4, expert column l32
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+        const int t = t0 + 8 * (v / 4) + 4 * g2 + (v % 4);
+        if (t < T) lt[(int64_t)t * Ep + e] = acc[v];
+    }
+    if (stats) {
+        // the 8 threads of a row hold its partial sums (lanes 8r'..8r'+7 of the wave)
+        for (int off = 1; off < 8; off <<= 1) ss += __shfl_xor(ss, off);
+        if (q == 0 && hlive) hn[t0 + r] = ss;
+        for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+        if (lane == 0 && amax && amax_bits) atomicMax(amax_bits, amax << 16);
+    }
+}
+
+// ---- screened selection: 16 lanes per token, 4 tokens per wave, 16 per workgroup.
+//  1. bounds lo/hi of every logit from the MFMA value (see the header), theta = k-th
+//     largest lo; candidates {e : hi_e >= theta} compacted into LDS;
+//  2. exact sequential chains for the candidates: the union of the workgroup's
+//     candidate experts is staged chunk by chunk (32 k) from the row-major router
+//     weight into LDS with contiguous loads, and lane j runs the chains of candidates
+//     j + 16 r (two at a time) reading weights from LDS, each lane keeping its best k
+//     as a sorted list;
+//  3. k rounds of a 16-lane arg-max over the lists' heads, then the fp64 weights.
+// Dynamic LDS: candidate lists [16][E] int16, union slot map [E] int16 and expert of
+// each slot [E] int16, two weight stages [E][kSelRow] and two h stages [16][kSelRow].
+constexpr int kSelK = 32;               // k per staged chunk
+constexpr int kSelItems = (kScreenMaxE * 4 + 16 * 4 + 255) / 256;  // staged 16-byte pieces per thread
+constexpr int kSelRow = kSelK * 2 + 16;  // LDS bytes per staged row (padded)
+
+size_t select_lds_bytes(int32_t E) {
+    const size_t e2 = (size_t)(E + 1) / 2 * 2;  // keep the byte arrays 4-byte aligned
+    return 16 * e2 * 2 + e2 * 2 + e2 * 2 + 2 * (size_t)E * kSelRow + 2 * 16 * kSelRow + 256;
+}
+
+template <int PER>  // logits per lane: ceil(E / 16)
+__global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
+                                                            const uint16_t *__restrict__ h,
+                                                            const uint16_t *__restrict__ wr,
+                                                            const float *__restrict__ lt,
+                                                            const double *__restrict__ hn,
+                                                            const float *__restrict__ wn,
+                                                            const float *__restrict__ bias, int32_t *__restrict__ idx,
+                                                            float *__restrict__ w) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int e2 = (E + 1) / 2 * 2;
+    int16_t *cand = reinterpret_cast<int16_t *>(lds);     // [16][e2]
+    int16_t *uslot = cand + 16 * e2;                      // [e2]: staged slot of expert e, or -1
+    int16_t *urow = uslot + e2;                           // [e2]: expert of staged slot s
+    uint8_t *wst = reinterpret_cast<uint8_t *>(urow + e2);
+    wst = reinterpret_cast<uint8_t *>((reinterpret_cast<uintptr_t>(wst) + 15) & ~(uintptr_t)15);
+    uint8_t *hst = wst + 2 * (size_t)E * kSelRow;         // [2][16][kSelRow]
+    __shared__ int32_t n_union;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int grp = lane >> 4, j = lane & 15;
+    const int tl = (tid >> 6) * 4 + grp;
+    const int t = blockIdx.x * 16 + tl;
+    const bool live = t < T;
+    const int tt = live ? t : T - 1;
+    for (int i = tid; i < e2; i += 256) uslot[i] = -1;
+
+    // ---- 1. bounds and candidates
+    const double u = 0x1p-24;
+    const double gam = (double)D * u / (1.0 - (double)D * u) + (double)D * 2 * u / (1.0 - (double)D * 2 * u);
+    const double hnorm = sqrt(hn[tt]) * (1.0 + 0x1p-30);
+    const float *lrow = lt + (int64_t)tt * Ep;
+    auto bound = [&](int e, float &lo, float &hi) {
+        const double L = lrow[e];
+        const double b = bias ? (double)bias[e] : 0.0;
+        const double d = gam * hnorm * (double)wn[e] + (double)D * 0x1p-124;
+        const double rad = d + 0x1p-23 * (fabs(L) + fabs(b) + d) + 0x1p-149;
+        const double mlo = L + b - rad, mhi = L + b + rad;
+        lo = (float)(mlo - fabs(mlo) * 0x1p-23 - 0x1p-149);  // rounds to a value <= mlo
+        hi = (float)(mhi + fabs(mhi) * 0x1p-23 + 0x1p-149);  // rounds to a value >= mhi
+    };
+    float lo[PER];
+    uint64_t taken = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        lo[i] = -INFINITY;
+        const int e = j + 16 * i;
+        if (e < E) {
+            float hi;
+            bound(e, lo[i], hi);
+        } else {
+            taken |= 1ull << i;
+        }
+    }
+    float theta = -INFINITY;
+    for (int r = 0; r < k; ++r) {
+        float bv = -INFINITY;
+        int bi = -1;
+#pragma unroll
+        for (int i = 0; i < PER; ++i)
+            if (!((taken >> i) & 1ull) && (bi < 0 || lo[i] > bv)) {
+                bv = lo[i];
+                bi = i;
+            }
+        int bl = bi < 0 ? -1 : j;
+        for (int off = 8; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 16);
+            const int ol = __shfl_xor(bl, off, 16);
+            if (ol >= 0 && (bl < 0 || ov > bv || (ov == bv && ol < bl))) {
+                bv = ov;
+                bl = ol;
+            }
+        }
+        if (bl == j && bi >= 0) taken |= 1ull << bi;
+        theta = bv;
+    }
+    __syncthreads();  // uslot cleared
+    int n = 0;
+    int16_t *my_cand = cand + tl * e2;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int e = j + 16 * i;
+        bool flag = false;
+        if (e < E) {
+            float l, hi;
+            bound(e, l, hi);
+            flag = live && hi >= theta;
+        }
+        const uint32_t bits = (uint32_t)(__ballot(flag) >> (16 * grp)) & 0xffffu;
+        if (flag) {
+            my_cand[n + __popc(bits & ((1u << j) - 1u))] = (int16_t)e;
+            uslot[e] = 0;  // member of the union (slots assigned below)
+        }
+        n += __popc(bits);
+    }
+    __syncthreads();
+    // slots of the union in expert order (wave 0: running count over 64-expert groups)
+    if (tid < 64) {
+        int base = 0;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + tid;
+            const bool in = e < E && uslot[e] == 0;
+            const uint64_t m = __ballot(in);
+            if (in) {
+                const int s = base + __popcll(m & ((1ull << tid) - 1ull));
+                uslot[e] = (int16_t)s;
+                urow[s] = (int16_t)e;
+            }
+            base += __popcll(m);
+        }
+        if (tid == 0) n_union = base;
+    }
+    __syncthreads();
+    const int nu = n_union;
+
+    // ---- 2. exact chains over LDS-staged weight rows
+    float bestv[8];
+    int besti[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+        bestv[s] = -INFINITY;
+        besti[s] = -1;
+    }
+    int n_max = n;
+    for (int off = 16; off < 64; off <<= 1) n_max = max(n_max, __shfl_xor(n_max, off));
+    // the workgroup's largest list decides the number of passes (two chains per lane each)
+    __shared__ int32_t pass_max;
+    if (tid == 0) pass_max = 0;
+    __syncthreads();
+    if (lane == 0) atomicMax(&pass_max, n_max);
+    __syncthreads();
+    const int n_pass = (pass_max + 31) / 32;
+    const int n_chunks = D / kSelK;
+    // staging items: 16-byte pieces, 4 per row (32 k = 64 bytes)
+    const int items = nu * 4 + 16 * 4;
+    for (int pass = 0; pass < n_pass; ++pass) {
+        const int c0 = pass * 32 + j, c1 = c0 + 16;
+        const bool m0 = c0 < n, m1 = c1 < n;
+        const int e0 = m0 ? my_cand[c0] : 0, e1 = m1 ? my_cand[c1] : 0;
+        const int s0 = m0 ? uslot[e0] : 0, s1 = m1 ? uslot[e1] : 0;
+        float a0 = 0.0f, a1 = 0.0f;
+        // staging: the chunk's pieces for this thread (global -> registers while the
+        // previous chunk is multiplied, registers -> LDS before the barrier)
+        u32x4 sreg[kSelItems];
+        auto load_chunk = [&](int c) {
+#pragma unroll
+            for (int i = 0; i < kSelItems; ++i) {
+                const int it = tid + 256 * i;
+                const int row = it >> 2, q = it & 3;
+                if (it < items) {
+                    const uint16_t *src = row < nu ? wr + (int64_t)urow[row] * D
+                                                   : h + (int64_t)min(blockIdx.x * 16 + (row - nu), T - 1) * D;
+                    sreg[i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
+                }
+            }
+        };
+        auto store_chunk = [&](int buf) {
+#pragma unroll
+            for (int i = 0; i < kSelItems; ++i) {
+                const int it = tid + 256 * i;
+                const int row = it >> 2, q = it & 3;
+                if (it < items) {
+                    uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
+                                            : hst + (buf * 16 + (row - nu)) * kSelRow;
+                    *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[i];
+                }
+            }
+        };
+        load_chunk(0);
+        store_chunk(0);
+        __syncthreads();
+        for (int c = 0; c < n_chunks; ++c) {
+            const int buf = c & 1;
+            if (c + 1 < n_chunks) load_chunk(c + 1);
+            const uint8_t *hrow = hst + (buf * 16 + tl) * kSelRow;
+            const uint8_t *w0 = wst + ((size_t)buf * E + s0) * kSelRow;
+            const uint8_t *w1 = wst + ((size_t)buf * E + s1) * kSelRow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
+                const u32x4 x0 = *reinterpret_cast<const u32x4 *>(w0 + 16 * q);
+                const u32x4 x1 = *reinterpret_cast<const u32x4 *>(w1 + 16 * q);
+                const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
+                const uint32_t ww0[4] = {x0.x, x0.y, x0.z, x0.w};
+                const uint32_t ww1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float hl = bf_lo(hw[i]), hh = bf_hi(hw[i]);
+                    a0 = __builtin_fmaf(hl, bf_lo(ww0[i]), a0);
+                    a0 = __builtin_fmaf(hh, bf_hi(ww0[i]), a0);
+                    a1 = __builtin_fmaf(hl, bf_lo(ww1[i]), a1);
+                    a1 = __builtin_fmaf(hh, bf_hi(ww1[i]), a1);
+                }
+            }
+            // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
+            if (c + 1 < n_chunks) store_chunk(buf ^ 1);
+            __syncthreads();
+        }
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            if (!(r ? m1 : m0)) continue;
+            const int e = r ? e1 : e0;
+            const float a = r ? a1 : a0;
+            float v = bias ? a + bias[e] : a;
+            int vi = e;
+            // insert into the sorted list (drop what falls past position k - 1)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                if (s < k && (besti[s] < 0 || ranks_before(v, vi, bestv[s], besti[s]))) {
+                    const float tv = bestv[s];
+                    const int ti = besti[s];
+                    bestv[s] = v;
+                    besti[s] = vi;
+                    v = tv;
+                    vi = ti;
+                }
+            }
+        }
+    }
+
+    // ---- 3. merge the 16 lists: k rounds over their heads
+    float selv[8];
+    int sel[8];
+    for (int r = 0; r < 8; ++r) {
+        selv[r] = 0.0f;
+        sel[r] = -1;
+    }
+    for (int r = 0; r < k; ++r) {
+        float bv = bestv[0];
+        int bi = besti[0];
+        for (int off = 8; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, 16);
+            const int oi = __shfl_xor(bi, off, 16);
+            if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (bi >= 0 && besti[0] == bi) {  // pop the winner's head
+#pragma unroll
+            for (int s = 0; s < 7; ++s) {
+                bestv[s] = bestv[s + 1];
+                besti[s] = besti[s + 1];
+            }
+            bestv[7] = -INFINITY;
+            besti[7] = -1;
+        }
+        selv[r] = bv;
+        sel[r] = bi;
+    }
+    // lane j < k computes exp(l_j - l_0); the sum runs in j order on every lane
+    double ex = 0.0;
+    int my_sel = -1;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        if (j == r && r < k) {
+            ex = exp((double)selv[r] - (double)selv[0]);
+            my_sel = sel[r];
+        }
+    double den = 0.0;
+    for (int r = 0; r < k; ++r) den += __shfl(ex, r, 16);
+    if (live && j < k) {
+        idx[(int64_t)t * k + j] = my_sel;
+        w[(int64_t)t * k + j] = (float)(ex / den);
+    }
+}
+
+// ---- top-k of full logit rows: one wave per token, logits in registers (expert
+// e = lane + 64 i), k rounds of a wave-wide arg-max, then the fp64 weights.
+template <int PER>  // logits per lane: ceil(E / 64)
 __global__ void __launch_bounds__(256) router_topk_kernel(int32_t T, int32_t E, int32_t k,
                                                           const float *__restrict__ logits,
                                                           int32_t *__restrict__ idx, float *__restrict__ w) {
@@ -189,7 +545,6 @@ __global__ void __launch_bounds__(256) router_topk_kernel(int32_t T, int32_t E, 
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     const float *row = logits + (int64_t)t * E;
-    constexpr int PER = kTopkMaxE / 64;
     float v[PER];
     uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken
 #pragma unroll
@@ -251,30 +606,92 @@ __global__ void __launch_bounds__(256) router_topk_kernel(int32_t T, int32_t E, 
     }
 }
 
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 }  // namespace
 
-hipError_t launch_router_logits(int32_t T, int32_t D, int32_t E, const uint16_t *h, const uint16_t *wr,
-                                const float *bias, float *logits, uint32_t *amax_bits, hipStream_t s) {
-    if (T >= 8192 && E <= 384) {
-        dim3 grid((T + 31) / 32, (E + 383) / 384);
-        hipLaunchKernelGGL((router_logits_kernel<8, 6, 16>), grid, dim3(256), 0, s, T, D, E, h, wr, bias, logits,
-                           amax_bits);
-    } else if (T >= 1024) {
-        dim3 grid((T + 15) / 16, (E + 127) / 128);
-        hipLaunchKernelGGL((router_logits_kernel<4, 2, 32>), grid, dim3(256), 0, s, T, D, E, h, wr, bias, logits,
-                           amax_bits);
-    } else {
-        dim3 grid((T + 3) / 4, (E + 63) / 64);
-        hipLaunchKernelGGL((router_logits_kernel<1, 1, 128>), grid, dim3(256), 0, s, T, D, E, h, wr, bias, logits,
-                           amax_bits);
+RoutePlan route_plan(int32_t T, int32_t D, int32_t E) {
+    RoutePlan p{};
+    p.screen = T >= kScreenMinT && E <= kScreenMaxE;
+    p.Ep = p.screen ? (E + 127) / 128 * 128 : (E + 63) / 64 * 64;
+    p.n_parts = D / 64;
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        const size_t o = off;
+        off += align256(n);
+        return o;
+    };
+    p.off_wk4 = take((size_t)D * p.Ep * 4);
+    p.off_logits = take((size_t)T * p.Ep * 4);  // exact logits, or the MFMA approximations
+    if (p.screen) {
+        p.off_wk8 = take((size_t)D * p.Ep * 2);
+        p.off_wpart = take((size_t)p.n_parts * p.Ep * 8);
+        p.off_hn = take((size_t)T * 8);
+        p.off_wn = take((size_t)p.Ep * 4);
     }
-    return hipGetLastError();
+    p.bytes = off;
+    return p;
 }
 
-hipError_t launch_router_topk(int32_t T, int32_t E, int32_t k, const float *logits, int32_t *idx, float *w,
-                              hipStream_t s) {
-    hipLaunchKernelGGL(router_topk_kernel, dim3((T + 3) / 4), dim3(256), 0, s, T, E, k, logits, idx, w);
-    return hipGetLastError();
+hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int32_t k, const uint16_t *h,
+                        const uint16_t *wr, const float *bias, float *logits_out, int32_t *idx, float *w,
+                        uint32_t *amax_bits, void *workspace, hipStream_t s) {
+    uint8_t *ws = static_cast<uint8_t *>(workspace);
+    float *wk4 = reinterpret_cast<float *>(ws + p.off_wk4);
+    float *scratch = reinterpret_cast<float *>(ws + p.off_logits);
+    uint16_t *wk8 = p.screen ? reinterpret_cast<uint16_t *>(ws + p.off_wk8) : nullptr;
+    double *wpart = p.screen ? reinterpret_cast<double *>(ws + p.off_wpart) : nullptr;
+    hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((p.Ep + 255) / 256), (unsigned)(D / 64)), dim3(256), 0, s,
+                       D, E, p.Ep, wr, wk4, wk8, wpart);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    auto exact = [&](float *out, uint32_t *amax) {
+        const int tpw = T <= 256 ? 1 : 4;
+        const dim3 grid((unsigned)((T + tpw - 1) / tpw), (unsigned)((p.Ep + 255) / 256));
+        if (tpw == 1)
+            hipLaunchKernelGGL((router_exact_kernel<1>), grid, dim3(256), 0, s, T, D, E, p.Ep, h, wk4, bias, out,
+                               amax);
+        else
+            hipLaunchKernelGGL((router_exact_kernel<4>), grid, dim3(256), 0, s, T, D, E, p.Ep, h, wk4, bias, out,
+                               amax);
+        return hipGetLastError();
+    };
+    if (!p.screen) {
+        float *lg = logits_out ? logits_out : scratch;
+        if ((err = exact(lg, amax_bits)) != hipSuccess) return err;
+        const dim3 grid((unsigned)((T + 3) / 4));
+        if (E <= 128)
+            hipLaunchKernelGGL((router_topk_kernel<2>), grid, dim3(256), 0, s, T, E, k, lg, idx, w);
+        else if (E <= 384)
+            hipLaunchKernelGGL((router_topk_kernel<6>), grid, dim3(256), 0, s, T, E, k, lg, idx, w);
+        else
+            hipLaunchKernelGGL((router_topk_kernel<kMaxE / 64>), grid, dim3(256), 0, s, T, E, k, lg, idx, w);
+        return hipGetLastError();
+    }
+    double *hn = reinterpret_cast<double *>(ws + p.off_hn);
+    float *wn = reinterpret_cast<float *>(ws + p.off_wn);
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)((T + 31) / 32), (unsigned)(p.Ep / 128)), dim3(256), 0, s,
+                       T, D, p.Ep, p.n_parts, h, wk8, wpart, scratch, hn, wn, amax_bits);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    {
+        const dim3 grid((unsigned)((T + 15) / 16));
+        const size_t lds = select_lds_bytes(E);
+        if (E <= 128)
+            hipLaunchKernelGGL((router_select_kernel<8>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+                               hn, wn, bias, idx, w);
+        else if (E <= 256)
+            hipLaunchKernelGGL((router_select_kernel<16>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+                               hn, wn, bias, idx, w);
+        else if (E <= 384)
+            hipLaunchKernelGGL((router_select_kernel<24>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+                               hn, wn, bias, idx, w);
+        else
+            hipLaunchKernelGGL((router_select_kernel<32>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+                               hn, wn, bias, idx, w);
+    }
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (logits_out) return exact(logits_out, nullptr);  // all exact logits on request
+    return hipSuccess;
 }
 
 }  // namespace moe

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -147,14 +147,21 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
  *                  order;
  *   topk_w[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the selected (fp64,
  *                  rounded to fp32): the softmax over all E renormalised over the top_k.
- * h: bf16 [T][D]; wr: bf16 [E][D]; bias: fp32 [E] or NULL; logits: fp32 [T][E]
- * (written; caller-owned scratch that doubles as an output); h_amax: fp32 [1] or NULL
- * (if given, receives max |h| over all of h, for moe_forward's NVFP4 tensor scale).
- * Requires 1 <= top_k <= 8, top_k <= E <= 1024. T = 0 is a no-op.
+ * h: bf16 [T][D]; wr: bf16 [E][D]; bias: fp32 [E] or NULL; logits: fp32 [T][E] or NULL
+ * (if given, receives every logit above); h_amax: fp32 [1] or NULL (if given, receives
+ * max |h| over all of h, for moe_forward's NVFP4 tensor scale). From 512 tokens on,
+ * the top_k is found by screening MFMA-computed logits with a rigorous error bound and
+ * recomputing the surviving candidates exactly, which gives the same indices and
+ * weights. workspace: device scratch of at least moe_route_workspace_bytes(T, D, E)
+ * bytes, caller-owned, contents undefined afterwards.
+ * Requires 1 <= top_k <= 8, top_k <= E <= 1024, D % 64 == 0 (else
+ * MOE_ERR_UNSUPPORTED). T = 0 is a no-op.
  */
+size_t moe_route_workspace_bytes(int32_t T, int32_t D, int32_t E);
 int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t *h,
                   const uint16_t *wr, const float *bias, float *logits, int32_t *topk_idx,
-                  float *topk_w, float *h_amax, void *stream);
+                  float *topk_w, float *h_amax, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /* Host-only check of moe_forward's arguments (everything but the workspace size). */
 int32_t moe_forward_validate(const moe_forward_args *a);

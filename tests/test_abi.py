@@ -25,11 +25,11 @@ def declared_functions():
 def test_header_functions_are_exported_and_bound():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 8, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     assert lib.moe_status_string(EWS) == b"workspace missing or too small"
 
 
@@ -104,9 +104,18 @@ def test_workspace_plan_sizes():
 def test_route_and_quantize_validate_on_the_host():
     lib = moe.lib()
     p = ctypes.c_void_p
-    assert lib.moe_route(4, 64, 16, 9, p(A16), p(A16), None, p(A16), p(A16), p(A16), None, None) == EINVAL
-    assert lib.moe_route(4, 64, 16, 8, p(A16 + 2), p(A16), None, p(A16), p(A16), p(A16), None, None) == EALIGN
-    assert lib.moe_route(0, 64, 16, 8, None, None, None, None, None, None, None, None) == OK
+    ws = lib.moe_route_workspace_bytes(4, 64, 16)
+    assert ws > 0 and lib.moe_route_workspace_bytes(4, 96, 16) == 0 and lib.moe_route_workspace_bytes(4, 64, 2000) == 0
+    r = lambda T, D, E, k, h, ws_ptr, ws_n: lib.moe_route(T, D, E, k, p(h), p(A16), None, None, p(A16), p(A16), None,
+                                                          ws_ptr, ws_n, None)
+    assert r(4, 64, 16, 9, A16, p(A16), ws) == EINVAL          # top_k > 8
+    assert r(4, 96, 16, 8, A16, p(A16), ws) == EUNSUP          # D not a multiple of 64
+    assert r(4, 64, 16, 8, A16 + 2, p(A16), ws) == EALIGN      # misaligned h
+    assert r(4, 64, 16, 8, A16, p(A16), ws - 1) == EWS         # workspace too small
+    assert r(4, 64, 16, 8, A16, None, ws) == EWS               # workspace missing
+    assert r(0, 64, 16, 8, 0, None, 0) == OK                   # empty batch: no-op
+    # the screened path (from 512 tokens) needs more room than the exact one
+    assert lib.moe_route_workspace_bytes(512, 4096, 384) > lib.moe_route_workspace_bytes(511, 4096, 384)
     bad = moe.MoePacked(1, 2, 32, 96, A16, A16, A16)   # K must be a multiple of 64 (tiled layout)
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
     bad = moe.MoePacked(2, 2, 48, 64, A16, A16, 0)     # N must be a multiple of 32 (tiled layout)

@@ -60,26 +60,61 @@ def test_quantize_weights_bitexact(fmt, shape):
 
 # ------------------------------------------------------------------ router
 ROUTER_CASES = [
-    dict(T=37, D=256, E=64, skew=False),      # small-T kernel, ragged token tile
-    dict(T=64, D=4096, E=384, skew=False),    # decode shape
-    dict(T=1030, D=512, E=384, skew=True),    # mid-T kernel, biased logits
-    dict(T=8200, D=256, E=384, skew=False),   # large-T kernel, ragged tail
+    dict(T=37, D=256, E=64, skew=False),      # exact path, ragged token tile
+    dict(T=64, D=4096, E=384, skew=False),    # decode shape (exact path)
+    dict(T=511, D=256, E=200, skew=False),    # largest exact-path batch, E not a multiple of 64
+    dict(T=512, D=256, E=200, skew=False),    # smallest screened batch, padded expert tiles
+    dict(T=1030, D=512, E=384, skew=True),    # screened, biased logits
+    dict(T=8200, D=256, E=384, skew=False),   # screened, ragged tail
+    dict(T=2048, D=4096, E=384, skew=True),   # screened at d_model 4096 with the skew bias
+    dict(T=700, D=256, E=384, skew=False, k=4),                # screened, top-4
+    dict(T=600, D=256, E=384, skew=False, adversarial=True),   # screened, exact ties
+    dict(T=40, D=256, E=64, skew=False, adversarial=True),     # exact path, exact ties
 ]
 
 
-@pytest.mark.parametrize("c", ROUTER_CASES, ids=lambda c: f"T{c['T']}_D{c['D']}_E{c['E']}")
+def _adversarial_router(h, wr):
+    """Exact ties: duplicated router rows give equal logits (lower index must win), and
+    all-zero hidden rows give every expert the same logit (plus bias)."""
+    h, wr = h.copy(), wr.copy()
+    E = wr.shape[0]
+    for dst, src in [(5, 3), (E - 1, 3), (17, 40), (E // 2, 0)]:
+        wr[dst] = wr[src]
+    h[7] = 0
+    h[-1] = 0
+    h[11] = h[12]                            # two identical tokens
+    return h, wr
+
+
+@pytest.mark.parametrize("c", ROUTER_CASES, ids=lambda c: f"T{c['T']}_D{c['D']}_E{c['E']}_k{c.get('k', 8)}"
+                         + ("_adv" if c.get("adversarial") else ""))
 def test_route_bitexact(c):
+    k = c.get("k", 8)
     wl = synth.custom("nvfp4", T=c["T"], D=c["D"], F=128, E=c["E"], skew=c["skew"], seed=11)
     h, wr, bias = wl.hidden(), wl.router_weight(), wl.router_bias()
+    if c.get("adversarial"):
+        h, wr = _adversarial_router(h, wr)
     report("route", **c)
-    idx, w, logits, amax = moe.route(to_dev(h), to_dev(wr), 8, None if bias is None else to_dev(bias), True)
+    idx, w, logits, amax = moe.route(to_dev(h), to_dev(wr), k, None if bias is None else to_dev(bias), True,
+                                     want_logits=True)
     torch.cuda.synchronize()
-    o_idx, o_w, o_lg = oracle.route(h, wr, k=8, bias=bias, want_logits=True)
+    o_idx, o_w, o_lg = oracle.route(h, wr, k=k, bias=bias, want_logits=True)
     assert np.array_equal(host(logits).view(np.uint32), o_lg.view(np.uint32)), "logits differ"
     assert np.array_equal(host(idx), o_idx), "top-k indices differ"
-    np.testing.assert_allclose(host(w), o_w, rtol=1e-6, atol=0)
+    np.testing.assert_allclose(host(w), o_w, rtol=1e-6, atol=0)  # fp64 exp of two libraries
     ref_amax = np.abs(synth.bf16_to_f32(h)).max()
     assert host(amax)[0] == ref_amax
+    # without the logits request the same indices and weights come out
+    d_bias = None if bias is None else to_dev(bias)
+    idx2, w2, _, _ = moe.route(to_dev(h), to_dev(wr), k, d_bias)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(idx2), o_idx) and np.array_equal(host(w2), host(w))
+    if c["T"] >= 512:
+        # screened batch vs the exact path on its first 256 tokens: identical bits
+        idx3, w3, _, _ = moe.route(to_dev(h[:256]), to_dev(wr), k, d_bias)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(idx3), host(idx)[:256])
+        assert np.array_equal(host(w3).view(np.uint32), host(w)[:256].view(np.uint32))
 
 
 # ------------------------------------------------------------------ layer
