@@ -7,9 +7,10 @@
 // are the fp64 softmax of the selected logits renormalised over the k. Each logit is a
 // dependent chain of D FMAs, so computing all T*E of them is VALU-bound; two paths:
 //
-//  exact (small T, or when the caller asks for all logits): one expert per lane and a
-//    few tokens per wave, h broadcast from wave-uniform loads, the router weight read
-//    from an expert-fastest fp32 copy (coalesced 16-byte loads); then the top-k kernel.
+//  exact (small T, or when the caller asks for all logits): one expert per lane and one
+//    token per workgroup, h broadcast from an fp32 copy in LDS, the router weight read
+//    from an expert-fastest bf16 copy (coalesced 16-byte loads, L2-resident); then the
+//    top-k kernel.
 //
 //  screened (large T): all logits approximated by a bf16 MFMA GEMM (exact products,
 //    fp32 sums in the hardware's order), then per token a rigorous bound on the gap to
@@ -46,13 +47,13 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
-// ---- router weight copies with the expert index fastest: wk4 fp32 [D/4][Ep][4],
-// wk8 bf16 [D/8][Ep][8] (optional), zero past E; wpart fp64 [D/64][Ep] partial sums
-// of w^2 (optional). One thread per (expert, 64-wide K block): it reads one full line
-// of its row, and consecutive threads write consecutive experts.
+// ---- router weight copy with the expert index fastest: wk8 bf16 [D/8][Ep][8], zero
+// past E (3 MiB at 384 x 4096: it stays in every XCD's L2); wpart fp64 [D/64][Ep]
+// partial sums of w^2 (optional). One thread per (expert, 64-wide K block): it reads
+// one full line of its row, and consecutive threads write consecutive experts.
 __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, int32_t Ep,
-                                                          const uint16_t *__restrict__ wr, float *__restrict__ wk4,
-                                                          uint16_t *__restrict__ wk8, double *__restrict__ wpart) {
+                                                          const uint16_t *__restrict__ wr, uint16_t *__restrict__ wk8,
+                                                          double *__restrict__ wpart) {
     const int e = blockIdx.x * 256 + threadIdx.x;
     if (e >= Ep) return;
     const int k0 = 64 * blockIdx.y;
@@ -63,96 +64,83 @@ __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, 
     double ss = 0.0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int k = k0 + 8 * i;
-        if (wk8) *reinterpret_cast<u32x4 *>(wk8 + ((int64_t)(k / 8) * Ep + e) * 8) = v[i];
-        const float f[8] = {bf_lo(v[i].x), bf_hi(v[i].x), bf_lo(v[i].y), bf_hi(v[i].y),
-                            bf_lo(v[i].z), bf_hi(v[i].z), bf_lo(v[i].w), bf_hi(v[i].w)};
-        *reinterpret_cast<float4 *>(wk4 + ((int64_t)(k / 4) * Ep + e) * 4) = make_float4(f[0], f[1], f[2], f[3]);
-        *reinterpret_cast<float4 *>(wk4 + ((int64_t)(k / 4 + 1) * Ep + e) * 4) = make_float4(f[4], f[5], f[6], f[7]);
+        *reinterpret_cast<u32x4 *>(wk8 + ((int64_t)(k0 / 8 + i) * Ep + e) * 8) = v[i];
+        const uint32_t q4[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
 #pragma unroll
-        for (int q = 0; q < 8; ++q) ss += (double)f[q] * (double)f[q];
+        for (int q = 0; q < 4; ++q) {
+            const double lo = bf_lo(q4[q]), hi = bf_hi(q4[q]);
+            ss += lo * lo + hi * hi;
+        }
     }
     if (wpart) wpart[(int64_t)blockIdx.y * Ep + e] = ss;
 }
 
-// ---- exact logits: wave = TPW tokens x 64 experts (one per lane); the chains of a
-// lane run k ascending. h is read with wave-uniform addresses (broadcast).
-template <int TPW>
+// ---- exact logits: a workgroup = one token x 256 experts, one chain per lane, k
+// ascending. The token's h row is staged once in LDS as fp32 (all lanes read the same
+// address, a broadcast); the weights stream from the L2-resident bf16 copy through a
+// four-block register ring (blocks of 32 k, loaded three blocks ahead).
 __global__ void __launch_bounds__(256) router_exact_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep,
                                                            const uint16_t *__restrict__ h,
-                                                           const float *__restrict__ wk4,
+                                                           const uint16_t *__restrict__ wk8,
                                                            const float *__restrict__ bias, float *__restrict__ logits,
                                                            uint32_t *__restrict__ amax_bits) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    extern __shared__ __attribute__((aligned(16))) float hrow[];  // [D]
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int t = blockIdx.x;
+    const uint16_t *hp = h + (int64_t)t * D;
+    uint32_t amax = 0;
+    for (int k = 8 * tid; k < D; k += 8 * 256) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(hp + k);
+        *reinterpret_cast<float4 *>(hrow + k) = make_float4(bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y));
+        *reinterpret_cast<float4 *>(hrow + k + 4) = make_float4(bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w));
+        amax = max(amax, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu), max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
+        amax = max(amax, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu), max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
+    }
+    if (amax_bits && blockIdx.y == 0) {
+        for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+        if (lane == 0 && amax) atomicMax(amax_bits, amax << 16);
+    }
+    __syncthreads();
     const int eg = blockIdx.y * 4 + wave;  // 64-expert group of this wave
     if (eg * 64 >= Ep) return;
     const int e = eg * 64 + lane;
-    const int t0 = blockIdx.x * TPW;
-    const uint16_t *hp[TPW];
+    const uint16_t *wp = wk8 + (int64_t)e * 8;
+    const int64_t wstep = (int64_t)Ep * 8;  // one k-octet
+    float acc = 0.0f;
+    constexpr int KB = 32, R = 4;
+    const int nb = D / KB;
+    u32x4 wq[R][KB / 8];
+    auto load = [&](int slot, int blk) {
 #pragma unroll
-    for (int i = 0; i < TPW; ++i) hp[i] = h + (int64_t)min(t0 + i, T - 1) * D;
-    const float *wp = wk4 + (int64_t)e * 4;
-    const int64_t wstep = (int64_t)Ep * 4;
-    const bool do_amax = amax_bits != nullptr && eg == 0;
-    uint32_t amax = 0;
-    float acc[TPW];
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) acc[i] = 0.0f;
-    // 32-k blocks, the next one loaded while the current one is multiplied
-    constexpr int KB = 32;
-    const int nb = D / KB;  // even (D % 64 == 0)
-    float4 wv[2][KB / 4];
-    u32x4 hv[2][TPW][KB / 8];
-    auto load = [&](int buf, int blk) {
-#pragma unroll
-        for (int q = 0; q < KB / 4; ++q)
-            wv[buf][q] = *reinterpret_cast<const float4 *>(wp + (int64_t)(blk * (KB / 4) + q) * wstep);
-#pragma unroll
-        for (int i = 0; i < TPW; ++i)
-#pragma unroll
-            for (int q = 0; q < KB / 8; ++q)
-                hv[buf][i][q] = *reinterpret_cast<const u32x4 *>(hp[i] + blk * KB + 8 * q);
+        for (int q = 0; q < KB / 8; ++q)
+            wq[slot][q] = *reinterpret_cast<const u32x4 *>(wp + (int64_t)(blk * (KB / 8) + q) * wstep);
     };
-    auto compute = [&](int buf) {
+    auto compute = [&](int slot, int blk) {
 #pragma unroll
         for (int q = 0; q < KB / 8; ++q) {
-            const float4 w0 = wv[buf][2 * q], w1 = wv[buf][2 * q + 1];
-#pragma unroll
-            for (int i = 0; i < TPW; ++i) {
-                const u32x4 x = hv[buf][i][q];
-                float a = acc[i];
-                a = __builtin_fmaf(bf_lo(x.x), w0.x, a);
-                a = __builtin_fmaf(bf_hi(x.x), w0.y, a);
-                a = __builtin_fmaf(bf_lo(x.y), w0.z, a);
-                a = __builtin_fmaf(bf_hi(x.y), w0.w, a);
-                a = __builtin_fmaf(bf_lo(x.z), w1.x, a);
-                a = __builtin_fmaf(bf_hi(x.z), w1.y, a);
-                a = __builtin_fmaf(bf_lo(x.w), w1.z, a);
-                a = __builtin_fmaf(bf_hi(x.w), w1.w, a);
-                acc[i] = a;
-                if (do_amax && t0 + i < T) {
-                    amax = max(amax, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu),
-                                         max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
-                    amax = max(amax, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu),
-                                         max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
-                }
-            }
+            const float4 x0 = *reinterpret_cast<const float4 *>(hrow + blk * KB + 8 * q);
+            const float4 x1 = *reinterpret_cast<const float4 *>(hrow + blk * KB + 8 * q + 4);
+            const u32x4 y = wq[slot][q];
+            acc = __builtin_fmaf(x0.x, bf_lo(y.x), acc);
+            acc = __builtin_fmaf(x0.y, bf_hi(y.x), acc);
+            acc = __builtin_fmaf(x0.z, bf_lo(y.y), acc);
+            acc = __builtin_fmaf(x0.w, bf_hi(y.y), acc);
+            acc = __builtin_fmaf(x1.x, bf_lo(y.z), acc);
+            acc = __builtin_fmaf(x1.y, bf_hi(y.z), acc);
+            acc = __builtin_fmaf(x1.z, bf_lo(y.w), acc);
+            acc = __builtin_fmaf(x1.w, bf_hi(y.w), acc);
         }
     };
-    load(0, 0);
-    for (int blk = 0; blk < nb; blk += 2) {
-        load(1, blk + 1);
-        compute(0);
-        load(0, min(blk + 2, nb - 1));  // past the end: reload the last block (unused)
-        compute(1);
-    }
-    if (e < E) {
-        const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i)
-            if (t0 + i < T) logits[(int64_t)(t0 + i) * E + e] = bias ? acc[i] + b : acc[i];
+    for (int r = 0; r < R - 1; ++r) load(r, min(r, nb - 1));
+    for (int b0 = 0; b0 < nb; b0 += R) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            load((r + R - 1) % R, min(b0 + r + R - 1, nb - 1));  // past the end: reload (unused)
+            if (b0 + r < nb) compute(r, b0 + r);
+        }
     }
-    if (do_amax && lane == 0 && amax) atomicMax(amax_bits, amax << 16);
+    if (e < E) logits[(int64_t)t * E + e] = bias ? acc + bias[e] : acc;
 }
 
 // ---- approximate logits by bf16 MFMA: workgroup = 32 tokens x 128 experts, wave =
@@ -251,55 +239,56 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
 // ---- screened selection: 16 lanes per token, 4 tokens per wave, 16 per workgroup.
 //  1. bounds lo/hi of every logit from the MFMA value (see the header), theta = k-th
 //     largest lo; candidates {e : hi_e >= theta} compacted into LDS;
-//  2. exact sequential chains for the candidates: the union of the workgroup's
-//     candidate experts is staged chunk by chunk (32 k) from the row-major router
-//     weight into LDS with contiguous loads, and lane j runs the chains of candidates
-//     j + 16 r (two at a time) reading weights from LDS, each lane keeping its best k
-//     as a sorted list;
-//  3. k rounds of a 16-lane arg-max over the lists' heads, then the fp64 weights.
-// Dynamic LDS: candidate lists [16][E] int16, union slot map [E] int16 and expert of
-// each slot [E] int16, two weight stages [E][kSelRow] and two h stages [16][kSelRow].
-constexpr int kSelK = 32;               // k per staged chunk
+//  2. exact sequential chains: each wave spreads the (token, candidate) pairs of its 4
+//     tokens over its 64 lanes, one chain per lane and pass; the union of the
+//     workgroup's candidate experts is staged chunk by chunk (32 k) from the row-major
+//     router weight into LDS with contiguous loads, so the chains read weights and h
+//     from LDS; each exact logit goes to the token's row of `lt` (no longer needed);
+//  3. per token, the 16 lanes keep sorted best-k lists of its exact logits, then k
+//     rounds of a 16-lane arg-max over the lists' heads, then the fp64 weights.
+// Dynamic LDS: candidate lists [16][E] int16, union slot map [E] int16, expert of each
+// slot [E] int16, two weight stages [E][kSelRow] and two h stages [16][kSelRow] (bf16).
+constexpr int kSelK = 32;    // k per staged chunk (64 bytes of a bf16 row)
+constexpr int kSelRow = 80;  // LDS bytes per staged row: 16-byte pieces of rows at random
+                             // slots then start on 16 different bank groups, not 4
 constexpr int kSelItems = (kScreenMaxE * 4 + 16 * 4 + 255) / 256;  // staged 16-byte pieces per thread
-constexpr int kSelRow = kSelK * 2 + 16;  // LDS bytes per staged row (padded)
 
 size_t select_lds_bytes(int32_t E) {
-    const size_t e2 = (size_t)(E + 1) / 2 * 2;  // keep the byte arrays 4-byte aligned
-    return 16 * e2 * 2 + e2 * 2 + e2 * 2 + 2 * (size_t)E * kSelRow + 2 * 16 * kSelRow + 256;
+    const size_t e2 = (size_t)(E + 1) / 2 * 2;  // keeps the byte arrays 4-byte aligned
+    return 16 * e2 * 2 + 2 * e2 * 2 + 16 + 2 * (size_t)E * kSelRow + 2 * 16 * kSelRow;
 }
 
 template <int PER>  // logits per lane: ceil(E / 16)
 __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
                                                             const uint16_t *__restrict__ h,
-                                                            const uint16_t *__restrict__ wr,
-                                                            const float *__restrict__ lt,
+                                                            const uint16_t *__restrict__ wr, float *__restrict__ lt,
                                                             const double *__restrict__ hn,
                                                             const float *__restrict__ wn,
                                                             const float *__restrict__ bias, int32_t *__restrict__ idx,
                                                             float *__restrict__ w) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int e2 = (E + 1) / 2 * 2;
-    int16_t *cand = reinterpret_cast<int16_t *>(lds);     // [16][e2]
-    int16_t *uslot = cand + 16 * e2;                      // [e2]: staged slot of expert e, or -1
-    int16_t *urow = uslot + e2;                           // [e2]: expert of staged slot s
-    uint8_t *wst = reinterpret_cast<uint8_t *>(urow + e2);
-    wst = reinterpret_cast<uint8_t *>((reinterpret_cast<uintptr_t>(wst) + 15) & ~(uintptr_t)15);
-    uint8_t *hst = wst + 2 * (size_t)E * kSelRow;         // [2][16][kSelRow]
-    __shared__ int32_t n_union;
+    int16_t *cand = reinterpret_cast<int16_t *>(lds);  // [16][e2]
+    int16_t *uslot = cand + 16 * e2;                   // [e2]: staged slot of expert e
+    int16_t *urow = uslot + e2;                        // [e2]: expert of staged slot s
+    uint8_t *wst = reinterpret_cast<uint8_t *>((reinterpret_cast<uintptr_t>(urow + e2) + 15) & ~(uintptr_t)15);
+    uint8_t *hst = wst + 2 * (size_t)E * kSelRow;      // [2][16][kSelRow]
+    __shared__ int32_t n_union, pass_max;
 
-    const int tid = threadIdx.x, lane = tid & 63;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, j = lane & 15;
-    const int tl = (tid >> 6) * 4 + grp;
+    const int tl = wave * 4 + grp;
     const int t = blockIdx.x * 16 + tl;
     const bool live = t < T;
     const int tt = live ? t : T - 1;
     for (int i = tid; i < e2; i += 256) uslot[i] = -1;
+    if (tid == 0) pass_max = 0;
 
     // ---- 1. bounds and candidates
     const double u = 0x1p-24;
     const double gam = (double)D * u / (1.0 - (double)D * u) + (double)D * 2 * u / (1.0 - (double)D * 2 * u);
     const double hnorm = sqrt(hn[tt]) * (1.0 + 0x1p-30);
-    const float *lrow = lt + (int64_t)tt * Ep;
+    float *lrow = lt + (int64_t)tt * Ep;
     auto bound = [&](int e, float &lo, float &hi) {
         const double L = lrow[e];
         const double b = bias ? (double)bias[e] : 0.0;
@@ -309,18 +298,14 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
         lo = (float)(mlo - fabs(mlo) * 0x1p-23 - 0x1p-149);  // rounds to a value <= mlo
         hi = (float)(mhi + fabs(mhi) * 0x1p-23 + 0x1p-149);  // rounds to a value >= mhi
     };
-    float lo[PER];
+    float lo[PER], hi[PER];
     uint64_t taken = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-        lo[i] = -INFINITY;
+        lo[i] = hi[i] = -INFINITY;
         const int e = j + 16 * i;
-        if (e < E) {
-            float hi;
-            bound(e, lo[i], hi);
-        } else {
-            taken |= 1ull << i;
-        }
+        if (e < E) bound(e, lo[i], hi[i]);
+        else taken |= 1ull << i;
     }
     float theta = -INFINITY;
     for (int r = 0; r < k; ++r) {
@@ -344,18 +329,13 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
         if (bl == j && bi >= 0) taken |= 1ull << bi;
         theta = bv;
     }
-    __syncthreads();  // uslot cleared
-    int n = 0;
+    __syncthreads();  // uslot cleared, pass_max zeroed
+    int n = 0;  // candidates of this lane's token (uniform in the 16-lane group)
     int16_t *my_cand = cand + tl * e2;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int e = j + 16 * i;
-        bool flag = false;
-        if (e < E) {
-            float l, hi;
-            bound(e, l, hi);
-            flag = live && hi >= theta;
-        }
+        const bool flag = live && e < E && hi[i] >= theta;
         const uint32_t bits = (uint32_t)(__ballot(flag) >> (16 * grp)) & 0xffffu;
         if (flag) {
             my_cand[n + __popc(bits & ((1u << j) - 1u))] = (int16_t)e;
@@ -363,6 +343,15 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
         }
         n += __popc(bits);
     }
+    // pairs of the wave: group g's candidates are pairs [off_g, off_g + n_g)
+    int ng[4], og[4], pw = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        ng[g] = __shfl(n, 16 * g);
+        og[g] = pw;
+        pw += ng[g];
+    }
+    if (lane == 0) atomicMax(&pass_max, (pw + 63) / 64);
     __syncthreads();
     // slots of the union in expert order (wave 0: running count over 64-expert groups)
     if (tid < 64) {
@@ -372,18 +361,88 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
             const bool in = e < E && uslot[e] == 0;
             const uint64_t m = __ballot(in);
             if (in) {
-                const int s = base + __popcll(m & ((1ull << tid) - 1ull));
-                uslot[e] = (int16_t)s;
-                urow[s] = (int16_t)e;
+                const int sl = base + __popcll(m & ((1ull << tid) - 1ull));
+                uslot[e] = (int16_t)sl;
+                urow[sl] = (int16_t)e;
             }
             base += __popcll(m);
         }
         if (tid == 0) n_union = base;
     }
     __syncthreads();
-    const int nu = n_union;
+    const int nu = n_union, n_pass = pass_max;
 
-    // ---- 2. exact chains over LDS-staged weight rows
+    // ---- 2. exact chains over LDS-staged rows
+    const int n_chunks = D / kSelK;
+    const int items = nu * 4 + 16 * 4;  // 16-byte pieces per chunk: weight rows, then h rows
+    u32x4 sreg[kSelItems];
+    auto load_chunk = [&](int c) {
+#pragma unroll
+        for (int i = 0; i < kSelItems; ++i) {
+            const int it = tid + 256 * i;
+            const int row = it >> 2, q = it & 3;
+            if (it < items) {
+                const uint16_t *src = row < nu ? wr + (int64_t)urow[row] * D
+                                               : h + (int64_t)min(blockIdx.x * 16 + (row - nu), T - 1) * D;
+                sreg[i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
+            }
+        }
+    };
+    auto store_chunk = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < kSelItems; ++i) {
+            const int it = tid + 256 * i;
+            const int row = it >> 2, q = it & 3;
+            if (it < items) {
+                uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
+                                        : hst + (buf * 16 + (row - nu)) * kSelRow;
+                *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[i];
+            }
+        }
+    };
+    for (int pass = 0; pass < n_pass; ++pass) {
+        const int pr = lane + 64 * pass;  // this lane's pair
+        const bool mine = pr < pw;
+        int g = 0;
+#pragma unroll
+        for (int q = 1; q < 4; ++q)
+            if (pr >= og[q]) g = q;
+        const int ptl = wave * 4 + g;                       // the pair's token in the workgroup
+        const int pe = mine ? cand[ptl * e2 + (pr - og[g])] : 0;  // and expert
+        const int ps = mine ? uslot[pe] : 0;
+        float a = 0.0f;
+        load_chunk(0);
+        store_chunk(0);
+        __syncthreads();
+        for (int c = 0; c < n_chunks; ++c) {
+            const int buf = c & 1;
+            if (c + 1 < n_chunks) load_chunk(c + 1);
+            const uint8_t *hrow = hst + (buf * 16 + ptl) * kSelRow;
+            const uint8_t *wrow = wst + ((size_t)buf * E + ps) * kSelRow;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
+                const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + 16 * q);
+                a = __builtin_fmaf(bf_lo(hv.x), bf_lo(wv.x), a);
+                a = __builtin_fmaf(bf_hi(hv.x), bf_hi(wv.x), a);
+                a = __builtin_fmaf(bf_lo(hv.y), bf_lo(wv.y), a);
+                a = __builtin_fmaf(bf_hi(hv.y), bf_hi(wv.y), a);
+                a = __builtin_fmaf(bf_lo(hv.z), bf_lo(wv.z), a);
+                a = __builtin_fmaf(bf_hi(hv.z), bf_hi(wv.z), a);
+                a = __builtin_fmaf(bf_lo(hv.w), bf_lo(wv.w), a);
+                a = __builtin_fmaf(bf_hi(hv.w), bf_hi(wv.w), a);
+            }
+            // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
+            if (c + 1 < n_chunks) store_chunk(buf ^ 1);
+            __syncthreads();
+        }
+        // exact logit of the pair into its token's lt row, at the candidate's position
+        const int pt = blockIdx.x * 16 + ptl;
+        if (mine && pt < T) lt[(int64_t)pt * Ep + (pr - og[g])] = bias ? a + bias[pe] : a;
+    }
+    __syncthreads();  // the exact logits are visible to the whole workgroup
+
+    // ---- 3. per token: sorted best-k lists of the 16 lanes, then merged
     float bestv[8];
     int besti[8];
 #pragma unroll
@@ -391,104 +450,21 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
         bestv[s] = -INFINITY;
         besti[s] = -1;
     }
-    int n_max = n;
-    for (int off = 16; off < 64; off <<= 1) n_max = max(n_max, __shfl_xor(n_max, off));
-    // the workgroup's largest list decides the number of passes (two chains per lane each)
-    __shared__ int32_t pass_max;
-    if (tid == 0) pass_max = 0;
-    __syncthreads();
-    if (lane == 0) atomicMax(&pass_max, n_max);
-    __syncthreads();
-    const int n_pass = (pass_max + 31) / 32;
-    const int n_chunks = D / kSelK;
-    // staging items: 16-byte pieces, 4 per row (32 k = 64 bytes)
-    const int items = nu * 4 + 16 * 4;
-    for (int pass = 0; pass < n_pass; ++pass) {
-        const int c0 = pass * 32 + j, c1 = c0 + 16;
-        const bool m0 = c0 < n, m1 = c1 < n;
-        const int e0 = m0 ? my_cand[c0] : 0, e1 = m1 ? my_cand[c1] : 0;
-        const int s0 = m0 ? uslot[e0] : 0, s1 = m1 ? uslot[e1] : 0;
-        float a0 = 0.0f, a1 = 0.0f;
-        // staging: the chunk's pieces for this thread (global -> registers while the
-        // previous chunk is multiplied, registers -> LDS before the barrier)
-        u32x4 sreg[kSelItems];
-        auto load_chunk = [&](int c) {
+    for (int c = j; c < n; c += 16) {
+        float v = lrow[c];
+        int vi = my_cand[c];
 #pragma unroll
-            for (int i = 0; i < kSelItems; ++i) {
-                const int it = tid + 256 * i;
-                const int row = it >> 2, q = it & 3;
-                if (it < items) {
-                    const uint16_t *src = row < nu ? wr + (int64_t)urow[row] * D
-                                                   : h + (int64_t)min(blockIdx.x * 16 + (row - nu), T - 1) * D;
-                    sreg[i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
-                }
-            }
-        };
-        auto store_chunk = [&](int buf) {
-#pragma unroll
-            for (int i = 0; i < kSelItems; ++i) {
-                const int it = tid + 256 * i;
-                const int row = it >> 2, q = it & 3;
-                if (it < items) {
-                    uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
-                                            : hst + (buf * 16 + (row - nu)) * kSelRow;
-                    *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[i];
-                }
-            }
-        };
-        load_chunk(0);
-        store_chunk(0);
-        __syncthreads();
-        for (int c = 0; c < n_chunks; ++c) {
-            const int buf = c & 1;
-            if (c + 1 < n_chunks) load_chunk(c + 1);
-            const uint8_t *hrow = hst + (buf * 16 + tl) * kSelRow;
-            const uint8_t *w0 = wst + ((size_t)buf * E + s0) * kSelRow;
-            const uint8_t *w1 = wst + ((size_t)buf * E + s1) * kSelRow;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
-                const u32x4 x0 = *reinterpret_cast<const u32x4 *>(w0 + 16 * q);
-                const u32x4 x1 = *reinterpret_cast<const u32x4 *>(w1 + 16 * q);
-                const uint32_t hw[4] = {hv.x, hv.y, hv.z, hv.w};
-                const uint32_t ww0[4] = {x0.x, x0.y, x0.z, x0.w};
-                const uint32_t ww1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float hl = bf_lo(hw[i]), hh = bf_hi(hw[i]);
-                    a0 = __builtin_fmaf(hl, bf_lo(ww0[i]), a0);
-                    a0 = __builtin_fmaf(hh, bf_hi(ww0[i]), a0);
-                    a1 = __builtin_fmaf(hl, bf_lo(ww1[i]), a1);
-                    a1 = __builtin_fmaf(hh, bf_hi(ww1[i]), a1);
-                }
-            }
-            // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
-            if (c + 1 < n_chunks) store_chunk(buf ^ 1);
-            __syncthreads();
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            if (!(r ? m1 : m0)) continue;
-            const int e = r ? e1 : e0;
-            const float a = r ? a1 : a0;
-            float v = bias ? a + bias[e] : a;
-            int vi = e;
-            // insert into the sorted list (drop what falls past position k - 1)
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                if (s < k && (besti[s] < 0 || ranks_before(v, vi, bestv[s], besti[s]))) {
-                    const float tv = bestv[s];
-                    const int ti = besti[s];
-                    bestv[s] = v;
-                    besti[s] = vi;
-                    v = tv;
-                    vi = ti;
-                }
+        for (int s = 0; s < 8; ++s) {
+            if (s < k && (besti[s] < 0 || ranks_before(v, vi, bestv[s], besti[s]))) {
+                const float tv = bestv[s];
+                const int ti = besti[s];
+                bestv[s] = v;
+                besti[s] = vi;
+                v = tv;
+                vi = ti;
             }
         }
     }
-
-    // ---- 3. merge the 16 lists: k rounds over their heads
     float selv[8];
     int sel[8];
     for (int r = 0; r < 8; ++r) {
@@ -621,10 +597,9 @@ RoutePlan route_plan(int32_t T, int32_t D, int32_t E) {
         off += align256(n);
         return o;
     };
-    p.off_wk4 = take((size_t)D * p.Ep * 4);
+    p.off_wk8 = take((size_t)D * p.Ep * 2);
     p.off_logits = take((size_t)T * p.Ep * 4);  // exact logits, or the MFMA approximations
     if (p.screen) {
-        p.off_wk8 = take((size_t)D * p.Ep * 2);
         p.off_wpart = take((size_t)p.n_parts * p.Ep * 8);
         p.off_hn = take((size_t)T * 8);
         p.off_wn = take((size_t)p.Ep * 4);
@@ -637,23 +612,17 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
                         const uint16_t *wr, const float *bias, float *logits_out, int32_t *idx, float *w,
                         uint32_t *amax_bits, void *workspace, hipStream_t s) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
-    float *wk4 = reinterpret_cast<float *>(ws + p.off_wk4);
+    uint16_t *wk8 = reinterpret_cast<uint16_t *>(ws + p.off_wk8);
     float *scratch = reinterpret_cast<float *>(ws + p.off_logits);
-    uint16_t *wk8 = p.screen ? reinterpret_cast<uint16_t *>(ws + p.off_wk8) : nullptr;
     double *wpart = p.screen ? reinterpret_cast<double *>(ws + p.off_wpart) : nullptr;
     hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((p.Ep + 255) / 256), (unsigned)(D / 64)), dim3(256), 0, s,
-                       D, E, p.Ep, wr, wk4, wk8, wpart);
+                       D, E, p.Ep, wr, wk8, wpart);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     auto exact = [&](float *out, uint32_t *amax) {
-        const int tpw = T <= 256 ? 1 : 4;
-        const dim3 grid((unsigned)((T + tpw - 1) / tpw), (unsigned)((p.Ep + 255) / 256));
-        if (tpw == 1)
-            hipLaunchKernelGGL((router_exact_kernel<1>), grid, dim3(256), 0, s, T, D, E, p.Ep, h, wk4, bias, out,
-                               amax);
-        else
-            hipLaunchKernelGGL((router_exact_kernel<4>), grid, dim3(256), 0, s, T, D, E, p.Ep, h, wk4, bias, out,
-                               amax);
+        const dim3 grid((unsigned)T, (unsigned)((p.Ep + 255) / 256));
+        hipLaunchKernelGGL(router_exact_kernel, grid, dim3(256), (size_t)D * 4, s, T, D, E, p.Ep, h, wk8, bias, out,
+                           amax);
         return hipGetLastError();
     };
     if (!p.screen) {
