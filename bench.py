@@ -58,6 +58,53 @@ class HipEvents:
             self.hip.hipEventDestroy(self.arr[i])
 
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "block_scaled_moe_amd", "csrc")
+# sources that decide the code of each gate_up kernel family (a traffic figure measured
+# with rocprofv3 is valid only while their hash is unchanged)
+KERNEL_SOURCES = {
+    "stream_gemm_kernel": ["gemm_stream.hip", "gemm_common.h", "layout.h", "formats.h"],
+    "tile_gemm_kernel": ["gemm_tile.hip", "gemm_common.h", "layout.h", "formats.h"],
+    "grouped_gemm_kernel": ["gemm.hip", "gemm_common.h", "layout.h", "formats.h"],
+}
+
+
+def gate_up_kernel(wl) -> str:
+    """The gate_up kernel moe_forward picks for this shape (same rule as its plan: 48+
+    slots per expert on average -> MFMA tiles when both GEMMs fit them, else the
+    streaming kernel when K allows)."""
+    if wl.T * wl.k // wl.E >= 48 and wl.D % 256 == 0 and wl.F % 256 == 0:
+        return "tile_gemm_kernel"
+    if wl.D % 512 == 0 and wl.D // 512 <= 8:
+        return "stream_gemm_kernel"
+    return "grouped_gemm_kernel"
+
+
+def kernel_source_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload: str, kernel: str):
+    """Calibrated HBM bytes per gate_up launch from profiles/<workload>_gate_up_traffic.md,
+    or None if there is no such summary or the kernel's sources changed since."""
+    import re
+    path = os.path.join(HERE, "profiles", f"{workload}_gate_up_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_b = re.search(r"traffic_bytes_per_launch:\s*(\d+)", text)
+    m_h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    m_k = re.search(r"kernel:\s*(\w+)", text)
+    if not (m_b and m_h and m_k) or m_k.group(1) != kernel or m_h.group(1) != kernel_source_hash(kernel):
+        return None
+    return int(m_b.group(1))
+
+
 def packed_bytes_per_expert(fmt: str, N: int, K: int) -> int:
     if fmt == "nvfp4":
         return N * K // 2 + N * K // 16 + 4
@@ -233,7 +280,10 @@ def main():
         achieved = gate_up_flops / (gate_up_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / mfma_peak, 4), "traffic": None}
-    roof["kernel"] = "gemm_" + wl.fmt + "_kernel (gate_up)"
+    kern = gate_up_kernel(wl)
+    roof["traffic"] = profiled_traffic(wl.name, kern)
+    roof["kernel"] = f"{kern} (gate_up)"
+    roof["kernel_source_sha256"] = kernel_source_hash(kern)
     roof["per_launch"] = {"bytes": gate_up_bytes, "flops": gate_up_flops, "ms": round(gate_up_ms, 4)}
 
     print(f"[bench] {ms_step:.3f} ms/step (forward {fwd_ms:.3f} ms: gate_up {gate_up_ms:.3f} ms, down "
