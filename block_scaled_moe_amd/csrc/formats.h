@@ -149,4 +149,11 @@ __device__ __forceinline__ int mxfp8_quant_block(const float (&x)[32], uint32_t 
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
 
+// *p = max(*p, v) for fp32 bit patterns of non-negative values (integer order). The
+// stored value only grows, so a v that does not exceed what is already there changes
+// nothing and skips the atomic: most callers of one accumulator then only read it.
+__device__ __forceinline__ void atomic_max_grow(uint32_t *p, uint32_t v) {
+    if (v > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, v);
+}
+
 }  // namespace moe

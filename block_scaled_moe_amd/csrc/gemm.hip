@@ -239,7 +239,7 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                     amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
                 }
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-        if (lane == 0 && amax) atomicMax(p.amax_bits, amax);
+        if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
     } else if (GATE_UP) {
         // MXFP8: SwiGLU into an LDS tile [BM][BN/2], then quantise each 32-wide row block
         float *epi = reinterpret_cast<float *>(smem);

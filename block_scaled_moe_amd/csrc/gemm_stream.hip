@@ -218,7 +218,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
             }
             if (NV) {
                 for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-                if (lane == 0 && amax) atomicMax(p.amax_bits, amax);
+                if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
             }
         }
         if (!NV) {

@@ -46,7 +46,7 @@ struct RoutePlan {
 };
 RoutePlan route_plan(int32_t T, int32_t D, int32_t E);
 // logits_out: fp32 [T][E] exact logits, or NULL; amax_bits: max |h| (fp32 bits, the
-// caller zeroes it first) or NULL
+// route's first kernel zeroes it) or NULL
 hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int32_t k, const uint16_t *h,
                         const uint16_t *wr, const float *bias, float *logits_out, int32_t *idx, float *w,
                         uint32_t *amax_bits, void *workspace, hipStream_t s);

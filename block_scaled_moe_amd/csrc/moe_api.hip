@@ -147,8 +147,7 @@ int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t
     if (!workspace || workspace_bytes < plan.bytes) return MOE_ERR_WORKSPACE;
     if (!aligned16(workspace)) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
-    uint32_t *amax = reinterpret_cast<uint32_t *>(h_amax);
-    if (amax) MOE_TRY(launch_fill_u32(amax, 0u, 1, s));
+    uint32_t *amax = reinterpret_cast<uint32_t *>(h_amax);  // zeroed by the route's first kernel
     return to_status(launch_route(plan, T, D, E, top_k, h, wr, bias, logits, topk_idx, topk_w, amax, workspace, s));
 }
 

@@ -46,7 +46,7 @@ __global__ void __launch_bounds__(kThreads) amax_bf16_kernel(const uint16_t *__r
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
-        if (m) atomicMax(amax_bits + g, m << 16);  // bf16 bits -> fp32 bits
+        if (m) atomic_max_grow(amax_bits + g, m << 16);  // bf16 bits -> fp32 bits
     }
 }
 

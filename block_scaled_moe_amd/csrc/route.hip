@@ -9,8 +9,8 @@
 //
 //  exact (small T, or when the caller asks for all logits): one expert per lane and one
 //    token per workgroup, h broadcast from an fp32 copy in LDS, the router weight read
-//    from an expert-fastest bf16 copy (coalesced 16-byte loads, L2-resident); then the
-//    top-k kernel.
+//    from an expert-fastest bf16 copy (coalesced 16-byte loads, L2-resident); the top k
+//    is selected in the same kernel from the row of logits in LDS.
 //
 //  screened (large T): all logits approximated by a bf16 MFMA GEMM (exact products,
 //    fp32 sums in the hardware's order), then per token a rigorous bound on the gap to
@@ -49,12 +49,14 @@ __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib)
 
 // ---- router weight copy with the expert index fastest: wk8 bf16 [D/8][Ep][8], zero
 // past E (3 MiB at 384 x 4096: it stays in every XCD's L2); wpart fp64 [D/64][Ep]
-// partial sums of w^2 (optional). One thread per (expert, 64-wide K block): it reads
-// one full line of its row, and consecutive threads write consecutive experts.
+// partial sums of w^2 (optional); also zeroes the max |h| accumulator for the kernels
+// that follow. One thread per (expert, 64-wide K block): it reads one full line of its
+// row, and consecutive threads write consecutive experts.
 __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, int32_t Ep,
                                                           const uint16_t *__restrict__ wr, uint16_t *__restrict__ wk8,
-                                                          double *__restrict__ wpart) {
+                                                          double *__restrict__ wpart, uint32_t *__restrict__ amax_bits) {
     const int e = blockIdx.x * 256 + threadIdx.x;
+    if (amax_bits && e == 0 && blockIdx.y == 0) *amax_bits = 0u;  // max |h| accumulates from here
     if (e >= Ep) return;
     const int k0 = 64 * blockIdx.y;
     u32x4 v[8];
@@ -75,35 +77,39 @@ __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, 
     if (wpart) wpart[(int64_t)blockIdx.y * Ep + e] = ss;
 }
 
-// ---- exact logits: a workgroup = one token x 256 experts, one chain per lane, k
-// ascending. The token's h row is staged once in LDS as fp32 (all lanes read the same
-// address, a broadcast); the weights stream from the L2-resident bf16 copy through a
-// four-block register ring (blocks of 32 k, loaded three blocks ahead).
-__global__ void __launch_bounds__(256) router_exact_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep,
-                                                           const uint16_t *__restrict__ h,
-                                                           const uint16_t *__restrict__ wk8,
-                                                           const float *__restrict__ bias, float *__restrict__ logits,
-                                                           uint32_t *__restrict__ amax_bits) {
-    extern __shared__ __attribute__((aligned(16))) float hrow[];  // [D]
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// ---- exact logits and top-k: a workgroup = one token x all experts (Ep / 64 waves),
+// one chain per lane, k ascending. The token's h row is staged once in LDS as fp32 (all
+// lanes read the same address, a broadcast); the weights stream from the L2-resident
+// bf16 copy through a four-block register ring (blocks of 32 k, loaded three blocks
+// ahead). The logits meet in LDS, where wave 0 selects the top k (as router_topk_kernel)
+// unless idx is NULL.
+template <int PER>  // logits per lane of wave 0: Ep / 64
+__global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
+                                                            const uint16_t *__restrict__ h,
+                                                            const uint16_t *__restrict__ wk8,
+                                                            const float *__restrict__ bias,
+                                                            float *__restrict__ logits, int32_t *__restrict__ idx,
+                                                            float *__restrict__ w, uint32_t *__restrict__ amax_bits) {
+    extern __shared__ __attribute__((aligned(16))) float lds_f[];
+    float *hrow = lds_f;       // [D]
+    float *lrow = lds_f + D;   // [Ep]
+    const int tid = threadIdx.x, lane = tid & 63;
     const int t = blockIdx.x;
     const uint16_t *hp = h + (int64_t)t * D;
     uint32_t amax = 0;
-    for (int k = 8 * tid; k < D; k += 8 * 256) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(hp + k);
-        *reinterpret_cast<float4 *>(hrow + k) = make_float4(bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y));
-        *reinterpret_cast<float4 *>(hrow + k + 4) = make_float4(bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w));
+    for (int kk = 8 * tid; kk < D; kk += 8 * blockDim.x) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(hp + kk);
+        *reinterpret_cast<float4 *>(hrow + kk) = make_float4(bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y));
+        *reinterpret_cast<float4 *>(hrow + kk + 4) = make_float4(bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w));
         amax = max(amax, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu), max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
         amax = max(amax, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu), max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
     }
-    if (amax_bits && blockIdx.y == 0) {
+    if (amax_bits) {
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-        if (lane == 0 && amax) atomicMax(amax_bits, amax << 16);
+        if (lane == 0 && amax) atomic_max_grow(amax_bits, amax << 16);
     }
     __syncthreads();
-    const int eg = blockIdx.y * 4 + wave;  // 64-expert group of this wave
-    if (eg * 64 >= Ep) return;
-    const int e = eg * 64 + lane;
+    const int e = tid;  // this lane's expert (< Ep)
     const uint16_t *wp = wk8 + (int64_t)e * 8;
     const int64_t wstep = (int64_t)Ep * 8;  // one k-octet
     float acc = 0.0f;
@@ -140,7 +146,72 @@ __global__ void __launch_bounds__(256) router_exact_kernel(int32_t T, int32_t D,
             if (b0 + r < nb) compute(r, b0 + r);
         }
     }
-    if (e < E) logits[(int64_t)t * E + e] = bias ? acc + bias[e] : acc;
+    const float lg = e < E ? (bias ? acc + bias[e] : acc) : 0.0f;
+    if (e < E && logits) logits[(int64_t)t * E + e] = lg;
+    if (!idx) return;
+    lrow[e] = lg;
+    __syncthreads();
+    if (tid >= 64) return;
+    // ---- top-k of the row: k rounds of a wave-wide arg-max, then the fp64 weights
+    float v[PER];
+    uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int ee = lane + 64 * i;
+        v[i] = 0.f;
+        if (ee < E) {
+            v[i] = lrow[ee];
+            live |= 1u << i;
+        }
+    }
+    float selv[8];
+    int sel[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        sel[r] = -1;
+        selv[r] = 0.f;
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        if (r >= k) break;
+        float bv = 0.f;
+        int bi = -1, bslot = -1;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            const int ee = lane + 64 * i;
+            if (((live >> i) & 1u) && (bi < 0 || ranks_before(v[i], ee, bv, bi))) {
+                bv = v[i];
+                bi = ee;
+                bslot = i;
+            }
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            const float ov = __shfl_xor(bv, off);
+            const int oi = __shfl_xor(bi, off);
+            if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
+                bv = ov;
+                bi = oi;
+            }
+        }
+        if (bi >= 0 && (bi & 63) == lane && bslot >= 0) live &= ~(1u << (bi >> 6));
+        sel[r] = bi;
+        selv[r] = bv;
+    }
+    // lane j < k computes exp(l_j - l_0); the sum runs in j order on every lane
+    double ex = 0.0;
+    int my_sel = -1;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (lane == j && j < k) {
+            ex = exp((double)selv[j] - (double)selv[0]);
+            my_sel = sel[j];
+        }
+    double den = 0.0;
+    for (int j = 0; j < k; ++j) den += __shfl(ex, j);
+    if (lane < k) {
+        idx[(int64_t)t * k + lane] = my_sel;
+        w[(int64_t)t * k + lane] = (float)(ex / den);
+    }
 }
 
 // ---- approximate logits by bf16 MFMA: workgroup = 32 tokens x 128 experts, wave =
@@ -232,7 +303,7 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
         for (int off = 1; off < 8; off <<= 1) ss += __shfl_xor(ss, off);
         if (q == 0 && hlive) hn[t0 + r] = ss;
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-        if (lane == 0 && amax && amax_bits) atomicMax(amax_bits, amax << 16);
+        if (lane == 0 && amax && amax_bits) atomic_max_grow(amax_bits, amax << 16);
     }
 }
 
@@ -511,77 +582,6 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
     }
 }
 
-// ---- top-k of full logit rows: one wave per token, logits in registers (expert
-// e = lane + 64 i), k rounds of a wave-wide arg-max, then the fp64 weights.
-template <int PER>  // logits per lane: ceil(E / 64)
-__global__ void __launch_bounds__(256) router_topk_kernel(int32_t T, int32_t E, int32_t k,
-                                                          const float *__restrict__ logits,
-                                                          int32_t *__restrict__ idx, float *__restrict__ w) {
-    const int lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (t >= T) return;
-    const float *row = logits + (int64_t)t * E;
-    float v[PER];
-    uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int e = lane + 64 * i;
-        v[i] = 0.f;
-        if (e < E) {
-            v[i] = row[e];
-            live |= 1u << i;
-        }
-    }
-    int sel[8];
-    float selv[8];
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        sel[r] = -1;
-        selv[r] = 0.f;
-    }
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        if (r >= k) break;
-        float bv = 0.f;
-        int bi = -1, bslot = -1;
-#pragma unroll
-        for (int i = 0; i < PER; ++i) {
-            const int e = lane + 64 * i;
-            if (((live >> i) & 1u) && (bi < 0 || ranks_before(v[i], e, bv, bi))) {
-                bv = v[i];
-                bi = e;
-                bslot = i;
-            }
-        }
-        for (int off = 32; off > 0; off >>= 1) {
-            const float ov = __shfl_xor(bv, off);
-            const int oi = __shfl_xor(bi, off);
-            if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-            }
-        }
-        if (bi >= 0 && (bi & 63) == lane && bslot >= 0) live &= ~(1u << (bi >> 6));
-        sel[r] = bi;
-        selv[r] = bv;
-    }
-    // lane j < k computes exp(l_j - l_0); the sum runs in j order on every lane
-    double ex = 0.0;
-    int my_sel = -1;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (lane == j && j < k) {
-            ex = exp((double)selv[j] - (double)selv[0]);
-            my_sel = sel[j];
-        }
-    double den = 0.0;
-    for (int j = 0; j < k; ++j) den += __shfl(ex, j);
-    if (lane < k) {
-        idx[(int64_t)t * k + lane] = my_sel;
-        w[(int64_t)t * k + lane] = (float)(ex / den);
-    }
-}
-
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -598,8 +598,8 @@ RoutePlan route_plan(int32_t T, int32_t D, int32_t E) {
         return o;
     };
     p.off_wk8 = take((size_t)D * p.Ep * 2);
-    p.off_logits = take((size_t)T * p.Ep * 4);  // exact logits, or the MFMA approximations
     if (p.screen) {
+        p.off_logits = take((size_t)T * p.Ep * 4);  // the MFMA approximations
         p.off_wpart = take((size_t)p.n_parts * p.Ep * 8);
         p.off_hn = take((size_t)T * 8);
         p.off_wn = take((size_t)p.Ep * 4);
@@ -613,30 +613,28 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
                         uint32_t *amax_bits, void *workspace, hipStream_t s) {
     uint8_t *ws = static_cast<uint8_t *>(workspace);
     uint16_t *wk8 = reinterpret_cast<uint16_t *>(ws + p.off_wk8);
-    float *scratch = reinterpret_cast<float *>(ws + p.off_logits);
+    float *scratch = p.screen ? reinterpret_cast<float *>(ws + p.off_logits) : nullptr;
     double *wpart = p.screen ? reinterpret_cast<double *>(ws + p.off_wpart) : nullptr;
     hipLaunchKernelGGL(router_prep_kernel, dim3((unsigned)((p.Ep + 255) / 256), (unsigned)(D / 64)), dim3(256), 0, s,
-                       D, E, p.Ep, wr, wk8, wpart);
+                       D, E, p.Ep, wr, wk8, wpart, amax_bits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    auto exact = [&](float *out, uint32_t *amax) {
-        const dim3 grid((unsigned)T, (unsigned)((p.Ep + 255) / 256));
-        hipLaunchKernelGGL(router_exact_kernel, grid, dim3(256), (size_t)D * 4, s, T, D, E, p.Ep, h, wk8, bias, out,
-                           amax);
+    // exact logits (to `out` if given) and, with idx, the top k: one workgroup per token
+    auto exact = [&](float *out, int32_t *ix, float *wt, uint32_t *amax) {
+        const size_t lds = ((size_t)D + p.Ep) * 4;
+        const dim3 grid((unsigned)T), block((unsigned)p.Ep);
+        if (p.Ep <= 128)
+            hipLaunchKernelGGL((router_exact_kernel<2>), grid, block, lds, s, T, D, E, p.Ep, k, h, wk8, bias, out, ix,
+                               wt, amax);
+        else if (p.Ep <= 384)
+            hipLaunchKernelGGL((router_exact_kernel<6>), grid, block, lds, s, T, D, E, p.Ep, k, h, wk8, bias, out, ix,
+                               wt, amax);
+        else
+            hipLaunchKernelGGL((router_exact_kernel<kMaxE / 64>), grid, block, lds, s, T, D, E, p.Ep, k, h, wk8, bias,
+                               out, ix, wt, amax);
         return hipGetLastError();
     };
-    if (!p.screen) {
-        float *lg = logits_out ? logits_out : scratch;
-        if ((err = exact(lg, amax_bits)) != hipSuccess) return err;
-        const dim3 grid((unsigned)((T + 3) / 4));
-        if (E <= 128)
-            hipLaunchKernelGGL((router_topk_kernel<2>), grid, dim3(256), 0, s, T, E, k, lg, idx, w);
-        else if (E <= 384)
-            hipLaunchKernelGGL((router_topk_kernel<6>), grid, dim3(256), 0, s, T, E, k, lg, idx, w);
-        else
-            hipLaunchKernelGGL((router_topk_kernel<kMaxE / 64>), grid, dim3(256), 0, s, T, E, k, lg, idx, w);
-        return hipGetLastError();
-    }
+    if (!p.screen) return exact(logits_out, idx, w, amax_bits);
     double *hn = reinterpret_cast<double *>(ws + p.off_hn);
     float *wn = reinterpret_cast<float *>(ws + p.off_wn);
     hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)((T + 31) / 32), (unsigned)(p.Ep / 128)), dim3(256), 0, s,
@@ -659,7 +657,7 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
                                hn, wn, bias, idx, w);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (logits_out) return exact(logits_out, nullptr);  // all exact logits on request
+    if (logits_out) return exact(logits_out, nullptr, nullptr, nullptr);  // all exact logits on request
     return hipSuccess;
 }
 
