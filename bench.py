@@ -194,6 +194,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=1, help="index into the five synthetic workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "
+                         "the two measured the same)")
     ap.add_argument("--cpu-target-s", type=float, default=10.0)
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (counter calibration)")
@@ -252,11 +255,35 @@ def main():
     stop.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(stop)
-    ms_step = total_ms / K
+    eager_ms_step = total_ms / K
     base = lambda i: i * moe.N_EVENTS
     gate_up_ms = float(np.mean([ev.ms(base(i) + 1, base(i) + 2) for i in range(K)]))
     down_ms = float(np.mean([ev.ms(base(i) + 3, base(i) + 4) for i in range(K)]))
     fwd_ms = float(np.mean([ev.ms(base(i) + 0, base(i) + 5) for i in range(K)]))
+    launch = "eager"
+    if args.graph:
+        # the same step (route + forward, same buffers) captured once as a HIP graph and
+        # replayed: the kernels are identical, only the per-launch host and queue gaps go
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            g_idx = step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(K):
+            graph.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        total_ms = start.elapsed_time(stop)
+        idx = g_idx
+        launch = "hip graph per step"
+    ms_step = total_ms / K
     ev.close()
 
     # algorithmic bytes and flops of the dominant kernel (the gate_up GEMM)
@@ -286,7 +313,7 @@ def main():
     roof["kernel_source_sha256"] = kernel_source_hash(kern)
     roof["per_launch"] = {"bytes": gate_up_bytes, "flops": gate_up_flops, "ms": round(gate_up_ms, 4)}
 
-    print(f"[bench] {ms_step:.3f} ms/step (forward {fwd_ms:.3f} ms: gate_up {gate_up_ms:.3f} ms, down "
+    print(f"[bench] {ms_step:.3f} ms/step ({launch}; eager {eager_ms_step:.3f}) (forward {fwd_ms:.3f} ms: gate_up {gate_up_ms:.3f} ms, down "
           f"{down_ms:.3f} ms); S={S}, {touched} experts touched, layer {layer_bytes / 1e9:.3f} GB "
           f"-> {layer_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s whole-step", file=sys.stderr, flush=True)
 
@@ -312,7 +339,7 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16 (exact NVFP4 values), fp32 accumulate" if nv else "e4m3 (MXFP8), fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": wl.name, "tokens": T, "d_model": D, "d_ff": F, "experts": E, "top_k": k,
+        "config": {"workload": wl.name, "launch": launch, "tokens": T, "d_model": D, "d_ff": F, "experts": E, "top_k": k,
                    "format": wl.fmt, "local_experts": [wl.e_begin, wl.local_end], "experts_touched": touched,
                    "slots": S, "layer_bytes": layer_bytes,
                    "layer_GBps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1)},
