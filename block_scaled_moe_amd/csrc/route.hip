@@ -511,7 +511,12 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
         const int pt = blockIdx.x * 16 + ptl;
         if (mine && pt < T) lt[(int64_t)pt * Ep + (pr - og[g])] = bias ? a + bias[pe] : a;
     }
-    __syncthreads();  // the exact logits are visible to the whole workgroup
+    // the barrier waits for the stores of the exact logits (write-through, so they are in
+    // this XCD's L2); phase 1 read the same rows through this CU's L1, which the barrier
+    // does not invalidate, so L1 is invalidated here and the values read with agent-scope
+    // loads
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 
     // ---- 3. per token: sorted best-k lists of the 16 lanes, then merged
     float bestv[8];
@@ -522,17 +527,26 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
         besti[s] = -1;
     }
     for (int c = j; c < n; c += 16) {
-        float v = lrow[c];
+        float v = __hip_atomic_load(lrow + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         int vi = my_cand[c];
+        // insert into the sorted list: pos = entries that rank before it; the tail moves
+        // down one slot (the last falls off) and pos takes the new entry. Written with
+        // selects only (a conditional-swap chain here was compiled wrongly on gfx950: the
+        // new head was lost when a lane's loop ran a second time).
+        int pos = 0;
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            if (s < k && (besti[s] < 0 || ranks_before(v, vi, bestv[s], besti[s]))) {
-                const float tv = bestv[s];
-                const int ti = besti[s];
-                bestv[s] = v;
-                besti[s] = vi;
-                v = tv;
-                vi = ti;
+        for (int s = 0; s < 8; ++s) pos += (besti[s] >= 0 && ranks_before(bestv[s], besti[s], v, vi)) ? 1 : 0;
+        if (pos < k) {
+#pragma unroll
+            for (int s = 7; s >= 1; --s) {
+                const bool down = s > pos;
+                bestv[s] = down ? bestv[s - 1] : bestv[s];
+                besti[s] = down ? besti[s - 1] : besti[s];
+            }
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                bestv[s] = s == pos ? v : bestv[s];
+                besti[s] = s == pos ? vi : besti[s];
             }
         }
     }

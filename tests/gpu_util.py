@@ -90,3 +90,26 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
     e_ind = float(np.abs(out[keep] - ref[keep]).max()) / r_ref if len(keep) else 0.0
     assert e_ind <= 2e-3, f"independent output error {e_ind:.2e} x RMS on tokens without flips"
     return e_stage, e_ind, flips, len(sel) - len(keep)
+
+
+def device_weights(wl: synth.Workload, device="cuda"):
+    """Packed gate_up and down of all experts of a workload, the bf16 masters drawn on the
+    GPU (same bytes as the host generator) in chunks of about 1 GiB and quantised there."""
+    import block_scaled_moe_amd as moe
+    E, D, F = wl.E, wl.D, wl.F
+    gu = moe.PackedWeights.empty(wl.fmt, E, 2 * F, D, device=device)
+    dn = moe.PackedWeights.empty(wl.fmt, E, D, F, device=device)
+    chunk = max(1, min(E, (1 << 30) // (2 * F * D * 2)))
+    buf = torch.empty(chunk * 2 * F * D, dtype=torch.int16, device=device)
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        n = e1 - e0
+        g = buf[: n * 2 * F * D]
+        wl.gate_up_master_device(e0, e1, g)
+        moe.quantize_weights(wl.fmt, g.view(n, 2 * F, D), out=gu.experts(e0, e1))
+        d = buf[: n * D * F]
+        wl.down_master_device(e0, e1, d)
+        moe.quantize_weights(wl.fmt, d.view(n, D, F), out=dn.experts(e0, e1))
+    torch.cuda.synchronize()
+    del buf
+    return gu, dn

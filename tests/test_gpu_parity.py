@@ -70,7 +70,20 @@ ROUTER_CASES = [
     dict(T=700, D=256, E=384, skew=False, k=4),                # screened, top-4
     dict(T=600, D=256, E=384, skew=False, adversarial=True),   # screened, exact ties
     dict(T=40, D=256, E=64, skew=False, adversarial=True),     # exact path, exact ties
+    # screened, every expert a candidate and the winners at any list position
+    dict(T=520, D=256, E=384, skew=False, clustered=True),
 ]
+
+
+def _clustered_router(wr, seed=5):
+    """Router rows all equal to row 0 except one element each, moved by 1-3 bf16 ulps:
+    the logits then differ by less than the screening bound, so nearly every expert is a
+    candidate and the winners sit anywhere in the candidate list."""
+    wr = np.repeat(wr[:1], wr.shape[0], axis=0)
+    E, D = wr.shape
+    pos = np.random.default_rng(seed).integers(0, D, size=E)
+    wr[np.arange(E), pos] = wr[0, pos] + (np.arange(E) % 3 + 1).astype(np.uint16)
+    return wr
 
 
 def _adversarial_router(h, wr):
@@ -87,13 +100,15 @@ def _adversarial_router(h, wr):
 
 
 @pytest.mark.parametrize("c", ROUTER_CASES, ids=lambda c: f"T{c['T']}_D{c['D']}_E{c['E']}_k{c.get('k', 8)}"
-                         + ("_adv" if c.get("adversarial") else ""))
+                         + ("_adv" if c.get("adversarial") else "") + ("_clustered" if c.get("clustered") else ""))
 def test_route_bitexact(c):
     k = c.get("k", 8)
     wl = synth.custom("nvfp4", T=c["T"], D=c["D"], F=128, E=c["E"], skew=c["skew"], seed=11)
     h, wr, bias = wl.hidden(), wl.router_weight(), wl.router_bias()
     if c.get("adversarial"):
         h, wr = _adversarial_router(h, wr)
+    if c.get("clustered"):
+        wr = _clustered_router(wr)
     report("route", **c)
     idx, w, logits, amax = moe.route(to_dev(h), to_dev(wr), k, None if bias is None else to_dev(bias), True,
                                      want_logits=True)
