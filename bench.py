@@ -73,7 +73,7 @@ def gate_up_kernel(wl) -> str:
     """The gate_up kernel moe_forward picks for this shape (same rule as its plan: 48+
     slots per expert on average -> MFMA tiles when both GEMMs fit them, else the
     streaming kernel when K allows)."""
-    if wl.T * wl.k // wl.E >= 48 and wl.D % 256 == 0 and wl.F % 256 == 0:
+    if wl.T * wl.k // wl.E >= 48 and wl.D % 512 == 0 and wl.F % 256 == 0:
         return "tile_gemm_kernel"
     if wl.D % 512 == 0 and wl.D // 512 <= 8:
         return "stream_gemm_kernel"

@@ -15,8 +15,9 @@
 //    (MXFP8) run and its scales one 128 / 64-byte run; the fp32 sums are unchanged up
 //    to rounding order;
 //  - software pipeline without branches: activations two chunks ahead (two register
-//    sets, LDS double buffer), weights four chunks ahead (four-slot register ring), so
-//    every wait count in the loop is partial;
+//    sets, LDS double buffer), weights WR chunks ahead (register ring), so every wait
+//    count in the loop is partial; a two-slot ring keeps three waves per SIMD, which
+//    measured faster than a deeper ring at two (and 128-row tiles at one);
 //  - gate_up tiles pair gate row f with up row F + f in the same lane and accumulator
 //    slot, so SwiGLU needs no data exchange;
 //  - work items (M-tile, N-block) are ordered in groups of 4 consecutive M-tiles, N-block
@@ -37,24 +38,34 @@ using namespace gemm_detail;
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64, kKC = 64, kThreads = 256, kGroup = 4;
+#ifndef MOE_TILE_BM
+#define MOE_TILE_BM 64
+#endif
+constexpr int kBM = MOE_TILE_BM, kKC = 64, kThreads = 256, kGroup = 4;
+constexpr int kMS = kBM / 32;  // 32-row MFMA subtiles per wave in M
 constexpr int kAStride = kKC * 2 + 16;                  // LDS bytes per activation row
 constexpr int kAStage = kBM * kAStride;                 // one LDS buffer
 constexpr int kAItems = kBM * kKC * 2 / 16 / kThreads;  // 16-byte activation loads per thread
 static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the threads");
 
+#ifndef MOE_TILE_WR
+#define MOE_TILE_WR 2  // weight chunks in flight (register ring slots)
+#endif
 #ifndef MOE_TILE_NS_NV
-#define MOE_TILE_NS_NV 2
+#define MOE_TILE_NS_NV 4
 #endif
 #ifndef MOE_TILE_NS_MX
 #define MOE_TILE_NS_MX 2
 #endif
 
+// 32-row weight subtiles per wave in N: NVFP4 4 (its expansion costs twice MXFP8's VALU,
+// so each activation fragment feeds more MFMAs; 234 registers, two waves per SIMD),
+// MXFP8 2 (three waves per SIMD; at 4 it spills)
 template <bool NV>
 constexpr int tile_ns() { return NV ? MOE_TILE_NS_NV : MOE_TILE_NS_MX; }
 
 template <bool NV, bool GATE_UP, int NS>
-__global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(const GemmArgs p) {
+__global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) tile_gemm_kernel(const GemmArgs p) {
     using Frag = typename std::conditional<NV, half8, bf16x8>::type;
     constexpr int BN = 128 * NS;        // weight rows per workgroup
     constexpr int CV = NV ? 1 : 2;      // 16-byte code loads per weight row per lane per chunk
@@ -124,20 +135,20 @@ __global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(co
         const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
         a_off[i] = arow * K * 2 + 16 * q;
     }
-    float16_t acc[2][NS];
+    float16_t acc[kMS][NS];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kMS; ++i)
 #pragma unroll
         for (int j = 0; j < NS; ++j) acc[i][j] = (float16_t){};
 
     // software pipeline: activations two chunks ahead in two register sets (chunk c + 2
     // is loaded while chunk c is multiplied, and stored to LDS at the end of chunk c + 1),
-    // weights four chunks ahead in a four-slot register ring
-    constexpr int WR = 4;
+    // weights WR chunks ahead in a WR-slot register ring
+    constexpr int WR = MOE_TILE_WR;
     u32x4 a_reg[2][kAItems];
     u32x4 wcode[WR][NS][CV];
     uint32_t wsc[WR][NS];
-    const int n_chunks = K / kKC;  // a multiple of WR (K % 256 == 0)
+    const int n_chunks = K / kKC;  // a multiple of WR (see tile_gemm_supported)
 
 #define MOE_LOAD_A(set, c)                                                                                 \
     _Pragma("unroll") for (int i = 0; i < kAItems; ++i) a_reg[set][i] =                                    \
@@ -184,9 +195,9 @@ __global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(co
             }
 #pragma unroll
             for (int s = 0; s < kKC / 16; ++s) {
-                Frag af[2];
+                Frag af[kMS];
 #pragma unroll
-                for (int ms = 0; ms < 2; ++ms)
+                for (int ms = 0; ms < kMS; ++ms)
                     af[ms] = *reinterpret_cast<const Frag *>(abuf + (32 * ms + l32) * kAStride + 64 * g2 + 16 * s);
 #pragma unroll
                 for (int ns = 0; ns < NS; ++ns) {
@@ -194,14 +205,14 @@ __global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(co
                         const _Float16 sc = sc_nv[ns][s >> 1];
                         const half8 bf = dequant_nvfp4(wcode[j][ns][0][s], sc);
 #pragma unroll
-                        for (int ms = 0; ms < 2; ++ms)
+                        for (int ms = 0; ms < kMS; ++ms)
                             acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                     } else {
                         const u32x4 q = wcode[j][ns][s >> 1];
                         const u32x2 cw = (s & 1) ? (u32x2){q.z, q.w} : (u32x2){q.x, q.y};
                         const bf16x8 bf = dequant_mxfp8(cw, sc_mx[ns]);
 #pragma unroll
-                        for (int ms = 0; ms < 2; ++ms)
+                        for (int ms = 0; ms < kMS; ++ms)
                             acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                     }
                 }
@@ -225,7 +236,7 @@ __global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(co
             const int fb = nb * (BN / 2) + wave * 16 * NS + 32 * q;  // first column of this pair
             const int f = fb + l32;
 #pragma unroll
-            for (int ms = 0; ms < 2; ++ms) {
+            for (int ms = 0; ms < kMS; ++ms) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
@@ -262,7 +273,7 @@ __global__ void __launch_bounds__(kThreads, NS == 2 ? 2 : 1) tile_gemm_kernel(co
         }
     } else {
 #pragma unroll
-        for (int ms = 0; ms < 2; ++ms)
+        for (int ms = 0; ms < kMS; ++ms)
 #pragma unroll
             for (int ns = 0; ns < NS; ++ns) {
                 const int n = nb * BN + wave * 32 * NS + 32 * ns + l32;
@@ -288,10 +299,12 @@ hipError_t launch_t(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
 
 }  // namespace
 
+int32_t tile_gemm_bm() { return kBM; }
+
 bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up) {
     // both formats must fit, since the plan picks one kernel family per layer shape
     const int bn = 128 * (MOE_TILE_NS_NV > MOE_TILE_NS_MX ? MOE_TILE_NS_NV : MOE_TILE_NS_MX);
-    return K % (4 * kKC) == 0 && (gate_up ? (N / 2) % (bn / 2) == 0 : N % bn == 0);
+    return K % (MOE_TILE_WR * kKC) == 0 && (gate_up ? (N / 2) % (bn / 2) == 0 : N % bn == 0);
 }
 
 hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s) {

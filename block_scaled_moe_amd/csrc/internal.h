@@ -100,6 +100,7 @@ hipError_t launch_grouped_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, Gemm
 int32_t gemm_bm(GemmShape shape);
 // prefill-shaped MFMA tiles (gemm_tile.hip): 64-row M-tiles, 256 weight rows per workgroup
 bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up);
+int32_t tile_gemm_bm();  // rows per M-tile of the tile kernels
 hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);
 // decode-shaped streaming variant (gemm_stream.hip): 16-row M-tiles, K a multiple of 512
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);

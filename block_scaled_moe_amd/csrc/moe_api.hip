@@ -44,7 +44,7 @@ Plan make_plan(const moe_forward_args *a) {
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
     p.tile64 = p.shape == GemmShape::Prefill && tile_gemm_supported(a->D, 2 * a->F, true) &&
                tile_gemm_supported(a->F, a->D, false);
-    p.bm = p.tile64 ? 64 : gemm_bm(p.shape);
+    p.bm = p.tile64 ? tile_gemm_bm() : gemm_bm(p.shape);
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
