@@ -80,9 +80,41 @@ __device__ __forceinline__ float nvfp4_tensor_scale(float amax) {
 }
 
 // ---------------------------------------------------------------- NVFP4 block
+// E2M1 codes of two values into byte SEL of `old` (element a in the low nibble). The
+// gfx950 convert rounds to nearest even, saturates at 6 and keeps the sign of -0; with
+// scale 1.0 it equals e2m1_encode for every finite fp32 input (checked exhaustively on
+// the device). Its scale operand only contributes an exponent, so 1.0 is passed.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float a, float b) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, a, b, 1.0f, SEL);
+}
+
+// The two E2M1 values of byte SEL of `codes`, exact.
+template <int SEL>
+__device__ __forceinline__ void e2m1_unpack2(uint32_t codes, float &a, float &b) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, SEL);
+    a = v.x;
+    b = v.y;
+}
+
+// fl(x / S) for 2^-100 <= S <= 2^100 and |x / S| in [2^-3, 2^8], one multiply and two
+// fused multiply-adds instead of a division: with R = fl(1 / S) and q0 = fl(|x| R),
+// the remainder |x| - q0 S is exact and fl(q0 + (|x| - q0 S) R) is the correctly
+// rounded quotient (Markstein's theorem; P. Markstein, IBM J. Res. Dev. 34(1), 1990).
+// Outside that quotient range the result is still within a few ulps of the quotient,
+// which is enough for the E2M1 encoding: below 2^-3 every such value encodes to a
+// signed zero, above 2^8 to the saturated code. The sign is taken from x, so -0 stays.
+__device__ __forceinline__ float quotient_by(float x, float S, float R) {
+    const float ax = fabsf(x);
+    const float q0 = ax * R;
+    return copysignf(fmaf(fmaf(-q0, S, ax), R, q0), x);
+}
+
 // One candidate of the 4-vs-6 rule: the block maximum r (already divided by the
 // tensor scale sg) is mapped to M; returns the fp32 sum of squared errors (in
 // element order) and the codes (nibbles packed, element 2i in the low nibble).
+// Element i's code is the E2M1 encoding of fl(x[i] / S), S = fl(e4m3(r / M) * sg).
 __device__ __forceinline__ float nvfp4_candidate(const float (&x)[16], float r, float sg, float M,
                                                  uint32_t &lo, uint32_t &hi, int &scode) {
     const float t = r / M;
@@ -90,6 +122,36 @@ __device__ __forceinline__ float nvfp4_candidate(const float (&x)[16], float r, 
     const float sdec = e4m3_value_pos(scode);
     const float S = sdec * sg;
     float err = 0.0f;
+    if (S >= 0x1p-100f && S <= 0x1p100f) {
+        const float R = 1.0f / S;
+        float q[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) q[i] = quotient_by(x[i], S, R);
+        lo = e2m1_pack2<0>(0u, q[0], q[1]);
+        lo = e2m1_pack2<1>(lo, q[2], q[3]);
+        lo = e2m1_pack2<2>(lo, q[4], q[5]);
+        lo = e2m1_pack2<3>(lo, q[6], q[7]);
+        hi = e2m1_pack2<0>(0u, q[8], q[9]);
+        hi = e2m1_pack2<1>(hi, q[10], q[11]);
+        hi = e2m1_pack2<2>(hi, q[12], q[13]);
+        hi = e2m1_pack2<3>(hi, q[14], q[15]);
+        float v[16];
+        e2m1_unpack2<0>(lo, v[0], v[1]);
+        e2m1_unpack2<1>(lo, v[2], v[3]);
+        e2m1_unpack2<2>(lo, v[4], v[5]);
+        e2m1_unpack2<3>(lo, v[6], v[7]);
+        e2m1_unpack2<0>(hi, v[8], v[9]);
+        e2m1_unpack2<1>(hi, v[10], v[11]);
+        e2m1_unpack2<2>(hi, v[12], v[13]);
+        e2m1_unpack2<3>(hi, v[14], v[15]);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float e = x[i] - v[i] * S;
+            err = err + e * e;
+        }
+        return err;
+    }
+    // scales at the ends of the fp32 range (including S == 0): one division per element
     lo = 0;
     hi = 0;
 #pragma unroll
@@ -128,6 +190,18 @@ __device__ __forceinline__ void nvfp4_quant_block(const float (&x)[16], float sg
 }
 
 // ---------------------------------------------------------------- MXFP8 block
+// E4M3 codes of two values into the low (HI false) or high 16 bits of `old` (a in the
+// lower byte). The gfx950 convert rounds to nearest even and equals e4m3_encode for
+// every fp32 input of magnitude <= 448 (checked exhaustively on the device); it does
+// not saturate above that, so callers clamp first (e4m3_clamp).
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3_pack2(uint32_t old, float a, float b) {
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, (int)old, HI);
+}
+
+// v clamped to [-448, 448]: the E4M3 code of the result is e4m3_encode(v)
+__device__ __forceinline__ float e4m3_clamp(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
 // Quantise one 32-block: E8M0 scale code and 32 E4M3 codes of x * 2^-exponent
 // (a power-of-two scaling, exact for every value whose code is not zero).
 __device__ __forceinline__ int mxfp8_quant_block(const float (&x)[32], uint32_t (&codes)[8]) {
@@ -138,10 +212,9 @@ __device__ __forceinline__ int mxfp8_quant_block(const float (&x)[32], uint32_t 
     const int se = sc - 127;
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
-        uint32_t v = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) v |= (uint32_t)e4m3_encode(ldexpf(x[4 * w + b], -se)) << (8 * b);
-        codes[w] = v;
+        const float v0 = e4m3_clamp(ldexpf(x[4 * w], -se)), v1 = e4m3_clamp(ldexpf(x[4 * w + 1], -se));
+        const float v2 = e4m3_clamp(ldexpf(x[4 * w + 2], -se)), v3 = e4m3_clamp(ldexpf(x[4 * w + 3], -se));
+        codes[w] = e4m3_pack2<true>(e4m3_pack2<false>(0u, v0, v1), v2, v3);
     }
     return sc;
 }

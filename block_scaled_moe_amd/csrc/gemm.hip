@@ -270,16 +270,7 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
             dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
             p.o_scales[row * (F / 32) + f / 32] = (uint8_t)sc8;
             // exact bf16 values of the codes for the down GEMM
-            const float s2 = ldexpf(1.0f, sc8 - 127);
-            uint32_t *dq = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.o_vals) + (row * F + f) * 2);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int c0 = (cw[i / 2] >> (16 * (i & 1))) & 0xff, c1 = (cw[i / 2] >> (16 * (i & 1) + 8)) & 0xff;
-                const float v0 = e4m3_value_pos(c0 & 0x7f) * s2, v1 = e4m3_value_pos(c1 & 0x7f) * s2;
-                const uint32_t b0 = (__float_as_uint(v0) >> 16) | ((uint32_t)(c0 & 0x80) << 8);
-                const uint32_t b1 = (__float_as_uint(v1) >> 16) | ((uint32_t)(c1 & 0x80) << 8);
-                dq[i] = b0 | (b1 << 16);
-            }
+            store_dequant_mxfp8_32(static_cast<uint8_t *>(p.o_vals) + (row * F + f) * 2, cw, sc8);
             if (p.o_tap) {
                 float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + f);
 #pragma unroll

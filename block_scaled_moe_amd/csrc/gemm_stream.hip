@@ -236,15 +236,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                 dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
                 dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
                 p.o_scales[row * (F / 32) + n0 / 32] = (uint8_t)sc8;
-                const float s2 = ldexpf(1.0f, sc8 - 127);
-                uint32_t *dq = reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(p.o_vals) + (row * F + n0) * 2);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int c0 = (cw[i / 2] >> (16 * (i & 1))) & 0xff, c1 = (cw[i / 2] >> (16 * (i & 1) + 8)) & 0xff;
-                    const uint32_t b0 = (__float_as_uint(e4m3_value_pos(c0 & 0x7f) * s2) >> 16) | ((uint32_t)(c0 & 0x80) << 8);
-                    const uint32_t b1 = (__float_as_uint(e4m3_value_pos(c1 & 0x7f) * s2) >> 16) | ((uint32_t)(c1 & 0x80) << 8);
-                    dq[i] = b0 | (b1 << 16);
-                }
+                store_dequant_mxfp8_32(static_cast<uint8_t *>(p.o_vals) + (row * F + n0) * 2, cw, sc8);
                 if (p.o_tap) {
                     float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + n0);
 #pragma unroll

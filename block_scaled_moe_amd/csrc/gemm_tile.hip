@@ -252,14 +252,13 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
 #pragma unroll
                         for (int off = 16; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
                         const int sc8 = e8m0_code_for_amax(a);
-                        const int code = e4m3_encode(ldexpf(hv, -(sc8 - 127)));
+                        const uint32_t code = e4m3_pack2<false>(0u, e4m3_clamp(ldexpf(hv, -(sc8 - 127))), 0.0f) & 0xffu;
                         if (m < rows) {
                             const int64_t row = p0 + m;
                             p.o_codes[row * F + f] = (uint8_t)code;
-                            const float s2 = ldexpf(1.0f, sc8 - 127);
-                            static_cast<uint16_t *>(p.o_vals)[row * F + f] =
-                                (uint16_t)((__float_as_uint(e4m3_value_pos(code & 0x7f) * s2) >> 16) |
-                                           ((uint32_t)(code & 0x80) << 8));
+                            const bf16x2 dq = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
+                                code, __uint_as_float((uint32_t)sc8 << 23), false);
+                            static_cast<__bf16 *>(p.o_vals)[row * F + f] = dq[0];
                             if (l32 == 0) p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc8;
                             if (p.o_tap) p.o_tap[row * F + f] = hv;
                         }

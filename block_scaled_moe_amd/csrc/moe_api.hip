@@ -215,7 +215,6 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     };
     MOE_TRY(mark(MOE_EV_BEGIN));
     const bool small = permute_small_ok(T, k, P.n_loc);
-    if (!small) MOE_TRY(launch_fill_u32(reinterpret_cast<uint32_t *>(ctrl), 0u, sizeof(Ctrl) / 4, s));
 
     // 1. stable grouping of the local slots and the GEMM tile list
     PermuteArgs pa{};

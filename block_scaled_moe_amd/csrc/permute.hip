@@ -9,19 +9,67 @@
 //   count   per-chunk histogram (LDS atomics; order does not matter for counts)
 //   scan    one workgroup: per-expert running sums over chunks, the exclusive
 //           prefix over experts, and the list of BM-row tiles of every expert
-//   scatter one wave per chunk walks its slots in order; a ballot over the lanes
-//           holding the same expert gives each slot its rank among equal experts,
-//           so positions are exact and stable for any routing, duplicates included.
+//   scatter one wave per chunk walks its slots in groups of 64, in order; within a
+//           group each slot's rank among the slots of the same expert comes from
+//           comparing the lanes' experts, so positions are exact and stable for any
+//           routing, duplicates included.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
+// For a group of 64 slots held one per lane (el: local expert, -1 if not local): the
+// number of lower lanes holding the same expert (rank) and of all lanes holding it
+// (total). One pass per distinct expert of the group: the lanes equal to the lowest
+// unhandled lane's expert form a 64-bit mask, which those lanes keep; rank and total
+// are bit counts of the kept mask. No LDS traffic inside the loop.
+__device__ __forceinline__ void group_rank(int el, int &rank, int &total) {
+    uint64_t rem = __ballot(el >= 0);
+    uint32_t mlo = 0, mhi = 0;
+    while (rem) {
+        const int leader = __ffsll((unsigned long long)rem) - 1;
+        const int e = __builtin_amdgcn_readlane(el, leader);
+        const bool mine = el == e;
+        const uint64_t m = __ballot(mine);
+        mlo = mine ? (uint32_t)m : mlo;
+        mhi = mine ? (uint32_t)(m >> 32) : mhi;
+        rem &= ~m;
+    }
+    rank = (int)__builtin_amdgcn_mbcnt_hi(mhi, __builtin_amdgcn_mbcnt_lo(mlo, 0u));
+    total = __popc(mlo) + __popc(mhi);
+}
+
+// Stable placement of one group of 64 consecutive slots (slot s on lane s - group
+// start; valid: s in range). cursor[e] is the next free position of local expert e for
+// this wave and is advanced by the group's count; each lane reads it before the
+// group's first lane of that expert writes it back (LDS accesses of one wave complete
+// in order).
+__device__ __forceinline__ void place_group(const PermuteArgs &a, int32_t *cursor, int64_t s, bool valid) {
+    const int el0 = valid ? a.idx[s] - a.e_begin : -1;
+    const bool local = valid && el0 >= 0 && el0 < a.n_loc;
+    const int el = local ? el0 : -1;
+    int rank, total;
+    group_rank(el, rank, total);
+    if (valid && !local) a.slot_pos[s] = -1;
+    const int32_t start = local ? cursor[el] : 0;
+    if (local) {
+        const int32_t pos = start + rank;
+        a.sorted_slot[pos] = (int32_t)s;
+        a.slot_pos[s] = pos;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (local && rank == 0) cursor[el] = start + total;
+}
+
 __global__ void __launch_bounds__(256) count_kernel(const int32_t *__restrict__ idx, int32_t n_slots,
                                                     int32_t chunk_slots, int32_t e_begin, int32_t n_loc,
-                                                    int32_t *__restrict__ chunk_counts) {
+                                                    int32_t *__restrict__ chunk_counts, Ctrl *__restrict__ ctrl) {
     extern __shared__ int32_t cnt[];
     for (int i = threadIdx.x; i < n_loc; i += 256) cnt[i] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) {  // accumulators of the later passes
+        ctrl->amax_a = 0;
+        ctrl->amax_i = 0;
+    }
     __syncthreads();
     const int64_t s0 = (int64_t)blockIdx.x * chunk_slots;
     const int64_t s1 = min<int64_t>(s0 + chunk_slots, n_slots);
@@ -35,6 +83,8 @@ __global__ void __launch_bounds__(256) count_kernel(const int32_t *__restrict__ 
 }
 
 constexpr int kScanThreads = 1024;
+constexpr int kSmallWaves = 8;  // waves of the one-workgroup permutation
+constexpr int kSmallThreads = 64 * kSmallWaves;
 
 // In-place exclusive prefix sum of v[0..n) (n <= 4 * kScanThreads) by one workgroup;
 // returns the total. part must hold kScanThreads entries.
@@ -91,7 +141,7 @@ __device__ int32_t small_scan_impl(int32_t *v, int n, int32_t *part) {
     return total;
 }
 __device__ __forceinline__ int32_t small_exclusive_scan(int32_t *v, int n, int32_t *part) {
-    return small_scan_impl<256>(v, n, part);
+    return small_scan_impl<kSmallThreads>(v, n, part);
 }
 
 __global__ void __launch_bounds__(kScanThreads) scan_kernel(PermuteArgs a) {
@@ -99,17 +149,51 @@ __global__ void __launch_bounds__(kScanThreads) scan_kernel(PermuteArgs a) {
     __shared__ int32_t tiles[4096];
     __shared__ int32_t part[kScanThreads];
     const int n = a.n_loc;
+    // Each expert's column of chunk counts is split into `segs` runs of `len` chunks,
+    // one thread per (expert, run), so the column walk is spread over the workgroup.
+    const int segs = n < kScanThreads ? kScanThreads / n : 1;
+    const int len = (a.n_chunks + segs - 1) / segs;
+    int32_t *run_sum = tiles;  // [segs][n] run totals, then run bases (n * segs <= 4096)
+    for (int u = threadIdx.x; u < n * segs; u += kScanThreads) {
+        const int el = u % n, c0 = (u / n) * len, c1 = min(c0 + len, a.n_chunks);
+        const int32_t *p = a.chunk_counts + el;
+        int32_t sum = 0;
+#pragma unroll 16
+        for (int c = c0; c < c1; ++c) sum += p[(int64_t)c * n];
+        run_sum[u] = sum;
+    }
+    __syncthreads();
     for (int el = threadIdx.x; el < n; el += kScanThreads) {
         int32_t run = 0;
-        for (int c = 0; c < a.n_chunks; ++c) {
-            int32_t *p = a.chunk_counts + (int64_t)c * n + el;
-            const int32_t v = *p;
-            *p = run;  // becomes the chunk's base within the expert
+        for (int r = 0; r < segs; ++r) {
+            const int32_t v = run_sum[r * n + el];
+            run_sum[r * n + el] = run;
             run += v;
         }
         cnt[el] = run;
-        a.counts[el] = run;
-        tiles[el] = (run + a.bm - 1) / a.bm;
+    }
+    __syncthreads();
+    // each chunk count becomes the chunk's base within its expert; loads of a batch
+    // are issued before its stores
+    for (int u = threadIdx.x; u < n * segs; u += kScanThreads) {
+        const int el = u % n, c0 = (u / n) * len, c1 = min(c0 + len, a.n_chunks);
+        int32_t *p = a.chunk_counts + el;
+        int32_t run = run_sum[u];
+        for (int c = c0; c < c1; c += 16) {
+            int32_t v[16];
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[j] = c + j < c1 ? p[(int64_t)(c + j) * n] : 0;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                if (c + j < c1) p[(int64_t)(c + j) * n] = run;
+                run += v[j];
+            }
+        }
+    }
+    __syncthreads();
+    for (int el = threadIdx.x; el < n; el += kScanThreads) {
+        a.counts[el] = cnt[el];
+        tiles[el] = (cnt[el] + a.bm - 1) / a.bm;
     }
     __syncthreads();
     const int32_t S = block_exclusive_scan(cnt, n, part);
@@ -139,50 +223,27 @@ __global__ void __launch_bounds__(64) scatter_kernel(PermuteArgs a, int32_t n_sl
     __syncthreads();
     const int64_t s0 = (int64_t)blockIdx.x * chunk_slots;
     const int64_t s1 = min<int64_t>(s0 + chunk_slots, n_slots);
-    const uint64_t lt = (1ull << lane) - 1;
-    for (int64_t g = s0; g < s1; g += 64) {
-        const int64_t s = g + lane;
-        const bool valid = s < s1;
-        const int el = valid ? a.idx[s] - a.e_begin : -1;
-        const bool local = valid && el >= 0 && el < n;
-        if (valid && !local) a.slot_pos[s] = -1;
-        uint64_t rem = __ballot(local);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int e = __shfl(el, leader);
-            const bool mine = local && el == e;
-            const uint64_t m = __ballot(mine);
-            const int32_t start = __builtin_amdgcn_readfirstlane(cursor[e]);
-            if (mine) {
-                const int32_t pos = start + __popcll(m & lt);
-                a.sorted_slot[pos] = (int32_t)s;
-                a.slot_pos[s] = pos;
-            }
-            if (lane == leader) cursor[e] = start + __popcll(m);
-            rem &= ~m;
-        }
-    }
+    for (int64_t g = s0; g < s1; g += 64) place_group(a, cursor, g + lane, g + lane < s1);
 }
 
 // Whole permutation in one workgroup for small batches (T*k <= 8192 slots, <= 1024
-// local experts): per-wave histograms of four contiguous quarters of the slots, the
-// exclusive scans and the tile list, then each wave scatters its quarter with the
-// ballot ranking, starting from its own per-expert bases. Also clears the control
-// block's accumulators, so no separate fill is needed.
-constexpr int kSmallThreads = 256;
+// local experts): per-wave histograms of kSmallWaves contiguous parts of the slots, the
+// exclusive scans and the tile list, then each wave places its part group by group,
+// starting from its own per-expert bases. Also clears the control block's
+// accumulators, so no separate fill is needed.
 constexpr int kSmallMaxLocal = 1024;
 
 __global__ void __launch_bounds__(kSmallThreads) permute_small_kernel(PermuteArgs a) {
-    __shared__ int32_t cnt[4][kSmallMaxLocal];  // per-wave counts, then per-wave bases
+    __shared__ int32_t cnt[kSmallWaves][kSmallMaxLocal];  // per-wave counts, then per-wave bases
     __shared__ int32_t tot[kSmallMaxLocal];
     __shared__ int32_t tiles[kSmallMaxLocal];
     __shared__ int32_t part[kScanThreads];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int n = a.n_loc;
     const int32_t n_slots = a.T * a.k;
-    const int32_t q = (n_slots + 3) / 4;  // slots per wave quarter
+    const int32_t q = (n_slots + kSmallWaves - 1) / kSmallWaves;  // slots per wave
     const int32_t s0 = wave * q, s1 = min(n_slots, s0 + q);
-    for (int i = tid; i < 4 * kSmallMaxLocal; i += kSmallThreads) (&cnt[0][0])[i] = 0;
+    for (int i = tid; i < kSmallWaves * kSmallMaxLocal; i += kSmallThreads) (&cnt[0][0])[i] = 0;
     if (tid == 0) {
         a.ctrl->amax_a = 0;
         a.ctrl->amax_i = 0;
@@ -196,7 +257,7 @@ __global__ void __launch_bounds__(kSmallThreads) permute_small_kernel(PermuteArg
     for (int el = tid; el < n; el += kSmallThreads) {
         int32_t run = 0;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < kSmallWaves; ++w) {
             const int32_t c = cnt[w][el];
             cnt[w][el] = run;  // base of wave w within the expert
             run += c;
@@ -217,7 +278,7 @@ __global__ void __launch_bounds__(kSmallThreads) permute_small_kernel(PermuteArg
             a.tile_row0[t] = tot[el] + (t - t0) * a.bm;
         }
 #pragma unroll
-        for (int w = 0; w < 4; ++w) cnt[w][el] += tot[el];  // absolute cursors
+        for (int w = 0; w < kSmallWaves; ++w) cnt[w][el] += tot[el];  // absolute cursors
     }
     if (tid == 0) {
         a.offsets[n] = S;
@@ -225,30 +286,8 @@ __global__ void __launch_bounds__(kSmallThreads) permute_small_kernel(PermuteArg
         a.ctrl->n_tiles = n_tiles;
     }
     __syncthreads();
-    const uint64_t lt = (1ull << lane) - 1;
     int32_t *cursor = cnt[wave];
-    for (int32_t gbase = s0; gbase < s1; gbase += 64) {
-        const int32_t s = gbase + lane;
-        const bool valid = s < s1;
-        const int el = valid ? a.idx[s] - a.e_begin : -1;
-        const bool local = valid && el >= 0 && el < n;
-        if (valid && !local) a.slot_pos[s] = -1;
-        uint64_t rem = __ballot(local);
-        while (rem) {
-            const int leader = __ffsll((unsigned long long)rem) - 1;
-            const int e = __shfl(el, leader);
-            const bool mine = local && el == e;
-            const uint64_t m = __ballot(mine);
-            const int32_t start = __builtin_amdgcn_readfirstlane(cursor[e]);
-            if (mine) {
-                const int32_t pos = start + __popcll(m & lt);
-                a.sorted_slot[pos] = s;
-                a.slot_pos[s] = pos;
-            }
-            if (lane == leader) cursor[e] = start + __popcll(m);
-            rem &= ~m;
-        }
-    }
+    for (int32_t g = s0; g < s1; g += 64) place_group(a, cursor, g + lane, g + lane < s1);
 }
 
 }  // namespace
@@ -267,7 +306,7 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t s) {
     const int32_t chunk_slots = a.chunk_tokens * a.k;
     const size_t lds = sizeof(int32_t) * (size_t)a.n_loc;
     hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks), dim3(256), lds, s, a.idx, n_slots, chunk_slots, a.e_begin,
-                       a.n_loc, a.chunk_counts);
+                       a.n_loc, a.chunk_counts, a.ctrl);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);

@@ -9,6 +9,7 @@
 // tensor scale needs the tensor's max |x| first, so NVFP4 runs as amax pass, block
 // pass, then a tiny pass turning the amax into the fp32 tensor scale.
 #include "formats.h"
+#include "gemm_common.h"
 #include "internal.h"
 #include "layout.h"
 
@@ -63,19 +64,10 @@ __device__ __forceinline__ void load16_bf16(const uint16_t *p, float (&x)[16]) {
 
 // exact fp16 of e2m1(code) * e4m3(scale) for the 16 codes of a block
 __device__ __forceinline__ void store_dequant16(_Float16 *dst, uint32_t lo, uint32_t hi, int scale) {
-    const float s = e4m3_value_pos(scale);
-    uint32_t o[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const uint32_t word = j < 4 ? lo : hi;
-        const int sh = 8 * (j & 3);
-        const _Float16 v0 = (_Float16)(e2m1_value((word >> sh) & 15) * s);
-        const _Float16 v1 = (_Float16)(e2m1_value((word >> (sh + 4)) & 15) * s);
-        o[j] = (uint32_t)__builtin_bit_cast(uint16_t, v0) | ((uint32_t)__builtin_bit_cast(uint16_t, v1) << 16);
-    }
-    uint4 *d = reinterpret_cast<uint4 *>(dst);
-    d[0] = make_uint4(o[0], o[1], o[2], o[3]);
-    d[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    const _Float16 s = gemm_detail::e4m3_to_f16((uint32_t)scale);
+    gemm_detail::half8 *d = reinterpret_cast<gemm_detail::half8 *>(dst);
+    d[0] = gemm_detail::dequant_nvfp4(lo, s);
+    d[1] = gemm_detail::dequant_nvfp4(hi, s);
 }
 
 // NVFP4 weights, in the packed tile layout (layout.h): thread b writes storage block
@@ -141,23 +133,7 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp8_bf16_kernel(const uint16
         d[0] = make_uint4(c[0], c[1], c[2], c[3]);
         d[1] = make_uint4(c[4], c[5], c[6], c[7]);
         scales[b] = (uint8_t)sc;
-        if (deq) {
-            const float s2 = ldexpf(1.0f, sc - 127);
-            uint4 *o = reinterpret_cast<uint4 *>(deq + b * 32);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                uint32_t ow[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int i = 8 * q + 2 * j;
-                    const int c0 = (c[i / 4] >> (8 * (i & 3))) & 0xff, c1 = (c[i / 4] >> (8 * (i & 3) + 8)) & 0xff;
-                    const uint32_t b0 = (__float_as_uint(e4m3_value_pos(c0 & 0x7f) * s2) >> 16) | ((uint32_t)(c0 & 0x80) << 8);
-                    const uint32_t b1 = (__float_as_uint(e4m3_value_pos(c1 & 0x7f) * s2) >> 16) | ((uint32_t)(c1 & 0x80) << 8);
-                    ow[j] = b0 | (b1 << 16);
-                }
-                o[q] = make_uint4(ow[0], ow[1], ow[2], ow[3]);
-            }
-        }
+        if (deq) gemm_detail::store_dequant_mxfp8_32(deq + b * 32, c, sc);
     }
 }
 
