@@ -256,19 +256,30 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
     uint32_t amax = 0;
     float16_t acc = {};
     const int n_chunks = D / 64;
-    u32x4 hreg = *reinterpret_cast<const u32x4 *>(hsrc);
-    u32x4 breg[2][4];
+    // software pipeline: chunk c + kRing is loaded (h piece and weight fragments into
+    // ring slot c % kRing) while chunk c is multiplied, so about kRing - 1 chunks of
+    // loads are in flight; the h piece of chunk c + 1 goes to the other LDS buffer at
+    // the end of chunk c. Loads past the end repeat the last chunk (in bounds, unused).
+    constexpr int kRing = 4;
+    u32x4 hreg[kRing];
+    u32x4 breg[kRing][4];
+    auto load = [&](int slot, int c) {
+        hreg[slot] = *reinterpret_cast<const u32x4 *>(hsrc + 64 * c);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) breg[0][s] = *reinterpret_cast<const u32x4 *>(bsrc + s * bstep);
-    *reinterpret_cast<u32x4 *>(hs[0] + hdst) = hreg;
+        for (int s = 0; s < 4; ++s)
+            breg[slot][s] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)(8 * c + s) * bstep);
+    };
+#pragma unroll
+    for (int r = 0; r < kRing; ++r) load(r, min(r, n_chunks - 1));
+    *reinterpret_cast<u32x4 *>(hs[0] + hdst) = hreg[0];
     __syncthreads();
-    for (int c0 = 0; c0 < n_chunks; c0 += 2) {
+    for (int c0 = 0; c0 < n_chunks; c0 += kRing) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
+        for (int j = 0; j < kRing; ++j) {
             const int c = c0 + j;
             if (c >= n_chunks) break;
             if (stats && hlive) {
-                const uint32_t w4[4] = {hreg.x, hreg.y, hreg.z, hreg.w};
+                const uint32_t w4[4] = {hreg[j].x, hreg[j].y, hreg[j].z, hreg[j].w};
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float a = bf_lo(w4[i]), b = bf_hi(w4[i]);
@@ -276,19 +287,16 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
                     amax = max(amax, max(w4[i] & 0x7fffu, (w4[i] >> 16) & 0x7fffu));
                 }
             }
-            const int cn = min(c + 1, n_chunks - 1);
-            hreg = *reinterpret_cast<const u32x4 *>(hsrc + 64 * cn);
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                breg[1 - j][s] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)(8 * cn + s) * bstep);
-            const uint8_t *abuf = hs[j];
+            const uint8_t *abuf = hs[c & 1];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const bf16x8 af = *reinterpret_cast<const bf16x8 *>(abuf + l32 * kHStride + 64 * g2 + 16 * s);
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, breg[j][s]), acc, 0, 0,
                                                               0);
             }
-            *reinterpret_cast<u32x4 *>(hs[1 - j] + hdst) = hreg;
+            // LDS buffer (c + 1) % 2 was last read in chunk c - 1, before the previous barrier
+            *reinterpret_cast<u32x4 *>(hs[(c + 1) & 1] + hdst) = hreg[(j + 1) % kRing];
+            load(j, min(c + kRing, n_chunks - 1));
             __syncthreads();
         }
     }
@@ -330,7 +338,7 @@ size_t select_lds_bytes(int32_t E) {
 }
 
 template <int PER>  // logits per lane: ceil(E / 16)
-__global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
+__global__ void __launch_bounds__(256, 2) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
                                                             const uint16_t *__restrict__ h,
                                                             const uint16_t *__restrict__ wr, float *__restrict__ lt,
                                                             const double *__restrict__ hn,
@@ -342,7 +350,9 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
     int16_t *cand = reinterpret_cast<int16_t *>(lds);  // [16][e2]
     int16_t *uslot = cand + 16 * e2;                   // [e2]: staged slot of expert e
     int16_t *urow = uslot + e2;                        // [e2]: expert of staged slot s
-    uint8_t *wst = reinterpret_cast<uint8_t *>((reinterpret_cast<uintptr_t>(urow + e2) + 15) & ~(uintptr_t)15);
+    // byte offsets from the LDS base (pointer arithmetic on the __shared__ array keeps
+    // the accesses ds_* instead of flat)
+    uint8_t *wst = lds + ((size_t)(18 * e2 * 2) + 15) / 16 * 16;  // [2][E][kSelRow]
     uint8_t *hst = wst + 2 * (size_t)E * kSelRow;      // [2][16][kSelRow]
     __shared__ int32_t n_union, pass_max;
 
@@ -360,10 +370,10 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
     const double gam = (double)D * u / (1.0 - (double)D * u) + (double)D * 2 * u / (1.0 - (double)D * 2 * u);
     const double hnorm = sqrt(hn[tt]) * (1.0 + 0x1p-30);
     float *lrow = lt + (int64_t)tt * Ep;
-    auto bound = [&](int e, float &lo, float &hi) {
-        const double L = lrow[e];
-        const double b = bias ? (double)bias[e] : 0.0;
-        const double d = gam * hnorm * (double)wn[e] + (double)D * 0x1p-124;
+    auto bound = [&](float Lf, float bf, float wnf, float &lo, float &hi) {
+        const double L = Lf;
+        const double b = bf;
+        const double d = gam * hnorm * (double)wnf + (double)D * 0x1p-124;
         const double rad = d + 0x1p-23 * (fabs(L) + fabs(b) + d) + 0x1p-149;
         const double mlo = L + b - rad, mhi = L + b + rad;
         lo = (float)(mlo - fabs(mlo) * 0x1p-23 - 0x1p-149);  // rounds to a value <= mlo
@@ -371,12 +381,22 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
     };
     float lo[PER], hi[PER];
     uint64_t taken = 0;
+    {
+        // all loads first (clamped indices, no branches), so they are in flight together
+        float Lv[PER], Bv[PER], Wv[PER];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        lo[i] = hi[i] = -INFINITY;
-        const int e = j + 16 * i;
-        if (e < E) bound(e, lo[i], hi[i]);
-        else taken |= 1ull << i;
+        for (int i = 0; i < PER; ++i) {
+            const int ec = min(j + 16 * i, E - 1);
+            Lv[i] = lrow[ec];
+            Bv[i] = bias ? bias[ec] : 0.0f;
+            Wv[i] = wn[ec];
+        }
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+            lo[i] = hi[i] = -INFINITY;
+            if (j + 16 * i < E) bound(Lv[i], Bv[i], Wv[i], lo[i], hi[i]);
+            else taken |= 1ull << i;
+        }
     }
     float theta = -INFINITY;
     for (int r = 0; r < k; ++r) {
@@ -446,20 +466,29 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
     // ---- 2. exact chains over LDS-staged rows
     const int n_chunks = D / kSelK;
     const int items = nu * 4 + 16 * 4;  // 16-byte pieces per chunk: weight rows, then h rows
-    u32x4 sreg[kSelItems];
-    auto load_chunk = [&](int c) {
+    // chunk c + kSelRing - 1 is loaded into register slot (c - 1) % kSelRing while chunk
+    // c is multiplied, so two chunks of loads are in flight; a slot goes to the other LDS
+    // buffer one chunk before its use. Loads past the end repeat the last chunk.
+    constexpr int kSelRing = 3;
+    u32x4 sreg[kSelRing][kSelItems];
+    int32_t src_row[kSelItems];  // the staged row of each item: an expert, else a token
+#pragma unroll
+    for (int i = 0; i < kSelItems; ++i) {
+        const int it = tid + 256 * i, row = it >> 2;
+        src_row[i] = it >= items ? 0 : row < nu ? urow[row] : min(blockIdx.x * 16 + (row - nu), T - 1);
+    }
+    auto load_chunk = [&](int slot, int c) {
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
             const int it = tid + 256 * i;
             const int row = it >> 2, q = it & 3;
             if (it < items) {
-                const uint16_t *src = row < nu ? wr + (int64_t)urow[row] * D
-                                               : h + (int64_t)min(blockIdx.x * 16 + (row - nu), T - 1) * D;
-                sreg[i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
+                const uint16_t *src = (row < nu ? wr : h) + (int64_t)src_row[i] * D;
+                sreg[slot][i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
             }
         }
     };
-    auto store_chunk = [&](int buf) {
+    auto store_chunk = [&](int buf, int slot) {
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
             const int it = tid + 256 * i;
@@ -467,7 +496,7 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
             if (it < items) {
                 uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
                                         : hst + (buf * 16 + (row - nu)) * kSelRow;
-                *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[i];
+                *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[slot][i];
             }
         }
     };
@@ -478,34 +507,40 @@ __global__ void __launch_bounds__(256) router_select_kernel(int32_t T, int32_t D
 #pragma unroll
         for (int q = 1; q < 4; ++q)
             if (pr >= og[q]) g = q;
-        const int ptl = wave * 4 + g;                       // the pair's token in the workgroup
+        const int ptl = wave * 4 + g;                             // the pair's token in the workgroup
         const int pe = mine ? cand[ptl * e2 + (pr - og[g])] : 0;  // and expert
         const int ps = mine ? uslot[pe] : 0;
         float a = 0.0f;
-        load_chunk(0);
-        store_chunk(0);
-        __syncthreads();
-        for (int c = 0; c < n_chunks; ++c) {
-            const int buf = c & 1;
-            if (c + 1 < n_chunks) load_chunk(c + 1);
-            const uint8_t *hrow = hst + (buf * 16 + ptl) * kSelRow;
-            const uint8_t *wrow = wst + ((size_t)buf * E + ps) * kSelRow;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
-                const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + 16 * q);
-                a = __builtin_fmaf(bf_lo(hv.x), bf_lo(wv.x), a);
-                a = __builtin_fmaf(bf_hi(hv.x), bf_hi(wv.x), a);
-                a = __builtin_fmaf(bf_lo(hv.y), bf_lo(wv.y), a);
-                a = __builtin_fmaf(bf_hi(hv.y), bf_hi(wv.y), a);
-                a = __builtin_fmaf(bf_lo(hv.z), bf_lo(wv.z), a);
-                a = __builtin_fmaf(bf_hi(hv.z), bf_hi(wv.z), a);
-                a = __builtin_fmaf(bf_lo(hv.w), bf_lo(wv.w), a);
-                a = __builtin_fmaf(bf_hi(hv.w), bf_hi(wv.w), a);
+        for (int r = 0; r < kSelRing; ++r) load_chunk(r, min(r, n_chunks - 1));
+        store_chunk(0, 0);
+        __syncthreads();
+        for (int c0 = 0; c0 < n_chunks; c0 += kSelRing) {
+#pragma unroll
+            for (int jj = 0; jj < kSelRing; ++jj) {
+                const int c = c0 + jj;  // register slot jj held chunk c; LDS buffer c % 2 holds it
+                if (c >= n_chunks) break;
+                const int buf = c & 1;
+                const uint8_t *hrow = hst + (buf * 16 + ptl) * kSelRow;
+                const uint8_t *wrow = wst + ((size_t)buf * E + ps) * kSelRow;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
+                    const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + 16 * q);
+                    a = __builtin_fmaf(bf_lo(hv.x), bf_lo(wv.x), a);
+                    a = __builtin_fmaf(bf_hi(hv.x), bf_hi(wv.x), a);
+                    a = __builtin_fmaf(bf_lo(hv.y), bf_lo(wv.y), a);
+                    a = __builtin_fmaf(bf_hi(hv.y), bf_hi(wv.y), a);
+                    a = __builtin_fmaf(bf_lo(hv.z), bf_lo(wv.z), a);
+                    a = __builtin_fmaf(bf_hi(hv.z), bf_hi(wv.z), a);
+                    a = __builtin_fmaf(bf_lo(hv.w), bf_lo(wv.w), a);
+                    a = __builtin_fmaf(bf_hi(hv.w), bf_hi(wv.w), a);
+                }
+                // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
+                store_chunk(buf ^ 1, (jj + 1) % kSelRing);
+                load_chunk(jj, min(c + kSelRing, n_chunks - 1));
+                __syncthreads();
             }
-            // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
-            if (c + 1 < n_chunks) store_chunk(buf ^ 1);
-            __syncthreads();
         }
         // exact logit of the pair into its token's lt row, at the candidate's position
         const int pt = blockIdx.x * 16 + ptl;
