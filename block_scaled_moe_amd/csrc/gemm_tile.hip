@@ -64,13 +64,26 @@ static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thr
 template <bool NV>
 constexpr int tile_ns() { return NV ? MOE_TILE_NS_NV : MOE_TILE_NS_MX; }
 
+// floats per row of a wave's MXFP8 epilogue tile in LDS: 16 NS columns plus one, so
+// lanes reading rows at the same column fall on different banks
+template <int NS>
+constexpr int kEpiStride() { return 16 * NS + 1; }
+
+// LDS of one workgroup: the double-buffered activation tile, or for the MXFP8 gate_up
+// epilogue the four waves' SwiGLU tiles if larger
+template <bool NV, bool GATE_UP, int NS>
+constexpr int tile_smem_bytes() {
+    return (!NV && GATE_UP && 4 * kBM * kEpiStride<NS>() * 4 > 2 * kAStage) ? 4 * kBM * kEpiStride<NS>() * 4
+                                                                             : 2 * kAStage;
+}
+
 template <bool NV, bool GATE_UP, int NS>
 __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) tile_gemm_kernel(const GemmArgs p) {
     using Frag = typename std::conditional<NV, half8, bf16x8>::type;
     constexpr int BN = 128 * NS;        // weight rows per workgroup
     constexpr int CV = NV ? 1 : 2;      // 16-byte code loads per weight row per lane per chunk
     static_assert(NS % 2 == 0, "gate_up pairs subtiles");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[2 * kAStage];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[tile_smem_bytes<NV, GATE_UP, NS>()];
 
     const int K = p.K, N = p.N, F = N / 2;
     const int NB = GATE_UP ? F / (BN / 2) : N / BN;
@@ -229,46 +242,63 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
 
     // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
     const float scl = NV ? p.a_tscale[0] * p.w_tscale[e] : 1.0f;
-    if (GATE_UP) {
+    if (GATE_UP && NV) {
         uint32_t amax = 0;
 #pragma unroll
         for (int q = 0; q < NS / 2; ++q) {
-            const int fb = nb * (BN / 2) + wave * 16 * NS + 32 * q;  // first column of this pair
-            const int f = fb + l32;
+            const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
 #pragma unroll
             for (int ms = 0; ms < kMS; ++ms) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
                     const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
-                    if (NV) {
-                        if (m < rows) {
-                            p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
-                            amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
-                        }
-                    } else {
-                        // MXFP8: the 32 columns of row m (one block) are the 32 lanes of this half-wave
-                        float a = fabsf(hv);
-#pragma unroll
-                        for (int off = 16; off > 0; off >>= 1) a = fmaxf(a, __shfl_xor(a, off));
-                        const int sc8 = e8m0_code_for_amax(a);
-                        const uint32_t code = e4m3_pack2<false>(0u, e4m3_clamp(ldexpf(hv, -(sc8 - 127))), 0.0f) & 0xffu;
-                        if (m < rows) {
-                            const int64_t row = p0 + m;
-                            p.o_codes[row * F + f] = (uint8_t)code;
-                            const bf16x2 dq = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(
-                                code, __uint_as_float((uint32_t)sc8 << 23), false);
-                            static_cast<__bf16 *>(p.o_vals)[row * F + f] = dq[0];
-                            if (l32 == 0) p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc8;
-                            if (p.o_tap) p.o_tap[row * F + f] = hv;
-                        }
+                    if (m < rows) {
+                        p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
+                        amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
                     }
                 }
             }
         }
-        if (NV) {
-            for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-            if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
+        for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+        if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
+    } else if (GATE_UP) {
+        // MXFP8: the wave's SwiGLU tile (kBM rows x 16 NS columns, 32-column blocks) goes
+        // through its own LDS region; lane r then quantises whole blocks of row r with
+        // 16-byte stores. The A stages are free: every wave passed the loop's last barrier.
+        float *epi = reinterpret_cast<float *>(smem) + wave * kBM * kEpiStride<NS>();
+#pragma unroll
+        for (int q = 0; q < NS / 2; ++q)
+#pragma unroll
+            for (int ms = 0; ms < kMS; ++ms)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                    epi[m * kEpiStride<NS>() + 32 * q + l32] = swiglu(acc[ms][q][v], acc[ms][q + NS / 2][v]);
+                }
+        __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+        for (int m = lane; m < kBM; m += 64) {
+            if (m >= rows) continue;
+            const int64_t row = p0 + m;
+#pragma unroll
+            for (int q = 0; q < NS / 2; ++q) {
+                const int fb = nb * (BN / 2) + wave * 16 * NS + 32 * q;  // first column of the block
+                float x[32];
+#pragma unroll
+                for (int i = 0; i < 32; ++i) x[i] = epi[m * kEpiStride<NS>() + 32 * q + i];
+                uint32_t cw[8];
+                const int sc8 = mxfp8_quant_block(x, cw);
+                u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + fb);
+                dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
+                p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc8;
+                store_dequant_mxfp8_32(static_cast<uint8_t *>(p.o_vals) + (row * F + fb) * 2, cw, sc8);
+                if (p.o_tap) {
+                    float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                }
+            }
         }
     } else {
 #pragma unroll

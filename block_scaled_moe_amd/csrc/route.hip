@@ -81,8 +81,8 @@ __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, 
 // one chain per lane, k ascending. The token's h row is staged once in LDS as fp32 (all
 // lanes read the same address, a broadcast); the weights stream from the L2-resident
 // bf16 copy through a four-block register ring (blocks of 32 k, loaded three blocks
-// ahead). The logits meet in LDS, where wave 0 selects the top k (as router_topk_kernel)
-// unless idx is NULL.
+// ahead). The logits meet in LDS, where wave 0 selects the top k (k rounds of a
+// wave-wide arg-max) unless idx is NULL.
 template <int PER>  // logits per lane of wave 0: Ep / 64
 __global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
                                                             const uint16_t *__restrict__ h,
