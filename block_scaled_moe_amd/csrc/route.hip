@@ -214,14 +214,19 @@ __global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D
     }
 }
 
-// ---- approximate logits by bf16 MFMA: workgroup = 32 tokens x 128 experts, wave =
-// 32 x 32 (one v_mfma_f32_32x32x16_bf16 tile); K in 64-wide chunks with the same k
+// ---- approximate logits by bf16 MFMA: workgroup = 32 kRM tokens x 128 experts, wave =
+// 32 kRM x 32 (kRM v_mfma_f32_32x32x16_bf16 tiles sharing each weight fragment, so a
+// weight fragment loaded from L2 serves kRM token tiles); K in 64-wide chunks with the same k
 // permutation for both operands (lane half g supplies k = 32g + 8s for step s). The h
 // tile goes through a double-buffered LDS tile; the weight fragments are 16-byte
 // coalesced loads from wk8. Workgroups of the first expert tile also write
 // hn[t] = sum h^2 (fp64) and max |h|; those of the first token tile write
 // wn[e] = ||w_e|| rounded up, from the partial sums.
 constexpr int kHStride = 64 * 2 + 16;  // LDS bytes per h row
+#ifndef MOE_ROUTER_RM
+#define MOE_ROUTER_RM 2
+#endif
+constexpr int kRM = MOE_ROUTER_RM;  // 32-token MFMA subtiles per workgroup (and per wave)
 
 __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, int32_t Ep, int32_t n_parts,
                                                           const uint16_t *__restrict__ h,
@@ -229,10 +234,10 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
                                                           const double *__restrict__ wpart, float *__restrict__ lt,
                                                           double *__restrict__ hn, float *__restrict__ wn,
                                                           uint32_t *__restrict__ amax_bits) {
-    __shared__ __attribute__((aligned(16))) uint8_t hs[2][32 * kHStride];
+    __shared__ __attribute__((aligned(16))) uint8_t hs[2][32 * kRM * kHStride];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g2 = lane >> 5;
-    const int t0 = blockIdx.x * 32;
+    const int t0 = blockIdx.x * 32 * kRM;
     const int e = blockIdx.y * 128 + wave * 32 + l32;  // this lane's expert (B column)
     const bool stats = blockIdx.y == 0;
 
@@ -244,72 +249,99 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
         wn[ee] = (float)(sqrt(ss) * (1.0 + 0x1p-20));
     }
 
-    // h staging: thread (row r, 16-byte piece q) of the 32 x 64 chunk
+    // h staging: thread (row r + 32 i, 16-byte piece q) of the 32 kRM x 64 chunk
     const int r = tid >> 3, q = tid & 7;
-    const uint16_t *hsrc = h + (int64_t)min(t0 + r, T - 1) * D + 8 * q;
+    const uint16_t *hsrc[kRM];
+    bool hlive[kRM];
+#pragma unroll
+    for (int i = 0; i < kRM; ++i) {
+        hsrc[i] = h + (int64_t)min(t0 + r + 32 * i, T - 1) * D + 8 * q;
+        hlive[i] = t0 + r + 32 * i < T;
+    }
     const int hdst = r * kHStride + 16 * q;
-    const bool hlive = t0 + r < T;
     const uint16_t *bsrc = wk8 + (int64_t)e * 8 + (int64_t)(4 * g2) * Ep * 8;  // k = 32 g2 within the chunk
     const int64_t bstep = (int64_t)Ep * 8;  // one k-octet
 
-    double ss = 0.0;
+    double ss[kRM] = {};
     uint32_t amax = 0;
-    float16_t acc = {};
+    float16_t acc[kRM] = {};
     const int n_chunks = D / 64;
-    // software pipeline: chunk c + kRing is loaded (h piece and weight fragments into
+    // software pipeline: chunk c + kRing is loaded (h pieces and weight fragments into
     // ring slot c % kRing) while chunk c is multiplied, so about kRing - 1 chunks of
-    // loads are in flight; the h piece of chunk c + 1 goes to the other LDS buffer at
+    // loads are in flight; the h pieces of chunk c + 1 go to the other LDS buffer at
     // the end of chunk c. Loads past the end repeat the last chunk (in bounds, unused).
-    constexpr int kRing = 4;
-    u32x4 hreg[kRing];
+#ifndef MOE_ROUTER_RING
+#define MOE_ROUTER_RING 2
+#endif
+    constexpr int kRing = MOE_ROUTER_RING;
+    u32x4 hreg[kRing][kRM];
     u32x4 breg[kRing][4];
     auto load = [&](int slot, int c) {
-        hreg[slot] = *reinterpret_cast<const u32x4 *>(hsrc + 64 * c);
+#pragma unroll
+        for (int i = 0; i < kRM; ++i) hreg[slot][i] = *reinterpret_cast<const u32x4 *>(hsrc[i] + 64 * c);
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             breg[slot][s] = *reinterpret_cast<const u32x4 *>(bsrc + (int64_t)(8 * c + s) * bstep);
     };
+    auto stage = [&](int buf, int slot) {
+#pragma unroll
+        for (int i = 0; i < kRM; ++i)
+            *reinterpret_cast<u32x4 *>(hs[buf] + hdst + 32 * i * kHStride) = hreg[slot][i];
+    };
 #pragma unroll
     for (int r = 0; r < kRing; ++r) load(r, min(r, n_chunks - 1));
-    *reinterpret_cast<u32x4 *>(hs[0] + hdst) = hreg[0];
+    stage(0, 0);
     __syncthreads();
     for (int c0 = 0; c0 < n_chunks; c0 += kRing) {
 #pragma unroll
         for (int j = 0; j < kRing; ++j) {
             const int c = c0 + j;
             if (c >= n_chunks) break;
-            if (stats && hlive) {
-                const uint32_t w4[4] = {hreg[j].x, hreg[j].y, hreg[j].z, hreg[j].w};
+            if (stats) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float a = bf_lo(w4[i]), b = bf_hi(w4[i]);
-                    ss += (double)a * a + (double)b * b;
-                    amax = max(amax, max(w4[i] & 0x7fffu, (w4[i] >> 16) & 0x7fffu));
+                for (int i = 0; i < kRM; ++i) {
+                    if (!hlive[i]) continue;
+                    const uint32_t w4[4] = {hreg[j][i].x, hreg[j][i].y, hreg[j][i].z, hreg[j][i].w};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float a = bf_lo(w4[u]), b = bf_hi(w4[u]);
+                        ss[i] += (double)a * a + (double)b * b;
+                        amax = max(amax, max(w4[u] & 0x7fffu, (w4[u] >> 16) & 0x7fffu));
+                    }
                 }
             }
             const uint8_t *abuf = hs[c & 1];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const bf16x8 af = *reinterpret_cast<const bf16x8 *>(abuf + l32 * kHStride + 64 * g2 + 16 * s);
-                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, breg[j][s]), acc, 0, 0,
-                                                              0);
+                const bf16x8 bf = __builtin_bit_cast(bf16x8, breg[j][s]);
+#pragma unroll
+                for (int i = 0; i < kRM; ++i) {
+                    const bf16x8 af =
+                        *reinterpret_cast<const bf16x8 *>(abuf + (32 * i + l32) * kHStride + 64 * g2 + 16 * s);
+                    acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, acc[i], 0, 0, 0);
+                }
             }
             // LDS buffer (c + 1) % 2 was last read in chunk c - 1, before the previous barrier
-            *reinterpret_cast<u32x4 *>(hs[(c + 1) & 1] + hdst) = hreg[(j + 1) % kRing];
+            stage((c + 1) & 1, (j + 1) % kRing);
             load(j, min(c + kRing, n_chunks - 1));
             __syncthreads();
         }
     }
-    // accumulator v of lane l: token row 8(v/4) + 4 g2 + v%4, expert column l32
+    // accumulator v of lane l: token row 32 i + 8(v/4) + 4 g2 + v%4, expert column l32
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-        const int t = t0 + 8 * (v / 4) + 4 * g2 + (v % 4);
-        if (t < T) lt[(int64_t)t * Ep + e] = acc[v];
-    }
+    for (int i = 0; i < kRM; ++i)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int t = t0 + 32 * i + 8 * (v / 4) + 4 * g2 + (v % 4);
+            if (t < T) lt[(int64_t)t * Ep + e] = acc[i][v];
+        }
     if (stats) {
         // the 8 threads of a row hold its partial sums (lanes 8r'..8r'+7 of the wave)
-        for (int off = 1; off < 8; off <<= 1) ss += __shfl_xor(ss, off);
-        if (q == 0 && hlive) hn[t0 + r] = ss;
+#pragma unroll
+        for (int i = 0; i < kRM; ++i) {
+            for (int off = 1; off < 8; off <<= 1) ss[i] += __shfl_xor(ss[i], off);
+            if (q == 0 && hlive[i]) hn[t0 + r + 32 * i] = ss[i];
+        }
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
         if (lane == 0 && amax && amax_bits) atomic_max_grow(amax_bits, amax << 16);
     }
@@ -686,7 +718,8 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
     if (!p.screen) return exact(logits_out, idx, w, amax_bits);
     double *hn = reinterpret_cast<double *>(ws + p.off_hn);
     float *wn = reinterpret_cast<float *>(ws + p.off_wn);
-    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)((T + 31) / 32), (unsigned)(p.Ep / 128)), dim3(256), 0, s,
+    hipLaunchKernelGGL(router_mfma_kernel, dim3((unsigned)((T + 32 * kRM - 1) / (32 * kRM)), (unsigned)(p.Ep / 128)),
+                       dim3(256), 0, s,
                        T, D, p.Ep, p.n_parts, h, wk8, wpart, scratch, hn, wn, amax_bits);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     {
