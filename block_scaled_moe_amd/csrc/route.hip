@@ -359,10 +359,14 @@ __global__ void __launch_bounds__(256) router_mfma_kernel(int32_t T, int32_t D, 
 //     rounds of a 16-lane arg-max over the lists' heads, then the fp64 weights.
 // Dynamic LDS: candidate lists [16][E] int16, union slot map [E] int16, expert of each
 // slot [E] int16, two weight stages [E][kSelRow] and two h stages [16][kSelRow] (bf16).
-constexpr int kSelK = 32;    // k per staged chunk (64 bytes of a bf16 row)
-constexpr int kSelRow = 80;  // LDS bytes per staged row: 16-byte pieces of rows at random
-                             // slots then start on 16 different bank groups, not 4
-constexpr int kSelItems = (kScreenMaxE * 4 + 16 * 4 + 255) / 256;  // staged 16-byte pieces per thread
+#ifndef MOE_SEL_K
+#define MOE_SEL_K 32
+#endif
+constexpr int kSelK = MOE_SEL_K;       // k per staged chunk
+constexpr int kSelP = kSelK / 8;       // 16-byte pieces per staged row
+constexpr int kSelRow = 2 * kSelK + 16;  // LDS bytes per staged row: the padding spreads the
+                                         // 16-byte pieces of rows at random slots over banks
+constexpr int kSelItems = (kScreenMaxE * kSelP + 16 * kSelP + 255) / 256;  // staged pieces per thread
 
 size_t select_lds_bytes(int32_t E) {
     const size_t e2 = (size_t)(E + 1) / 2 * 2;  // keeps the byte arrays 4-byte aligned
@@ -370,7 +374,10 @@ size_t select_lds_bytes(int32_t E) {
 }
 
 template <int PER>  // logits per lane: ceil(E / 16)
-__global__ void __launch_bounds__(256, 2) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
+#ifndef MOE_SEL_OCC
+#define MOE_SEL_OCC 2
+#endif
+__global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
                                                             const uint16_t *__restrict__ h,
                                                             const uint16_t *__restrict__ wr, float *__restrict__ lt,
                                                             const double *__restrict__ hn,
@@ -497,23 +504,26 @@ __global__ void __launch_bounds__(256, 2) router_select_kernel(int32_t T, int32_
 
     // ---- 2. exact chains over LDS-staged rows
     const int n_chunks = D / kSelK;
-    const int items = nu * 4 + 16 * 4;  // 16-byte pieces per chunk: weight rows, then h rows
+    const int items = (nu + 16) * kSelP;  // 16-byte pieces per chunk: weight rows, then h rows
     // chunk c + kSelRing - 1 is loaded into register slot (c - 1) % kSelRing while chunk
     // c is multiplied, so two chunks of loads are in flight; a slot goes to the other LDS
     // buffer one chunk before its use. Loads past the end repeat the last chunk.
-    constexpr int kSelRing = 3;
+#ifndef MOE_SEL_RING
+#define MOE_SEL_RING 2
+#endif
+    constexpr int kSelRing = MOE_SEL_RING;
     u32x4 sreg[kSelRing][kSelItems];
     int32_t src_row[kSelItems];  // the staged row of each item: an expert, else a token
 #pragma unroll
     for (int i = 0; i < kSelItems; ++i) {
-        const int it = tid + 256 * i, row = it >> 2;
+        const int it = tid + 256 * i, row = it / kSelP;
         src_row[i] = it >= items ? 0 : row < nu ? urow[row] : min(blockIdx.x * 16 + (row - nu), T - 1);
     }
     auto load_chunk = [&](int slot, int c) {
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
             const int it = tid + 256 * i;
-            const int row = it >> 2, q = it & 3;
+            const int row = it / kSelP, q = it % kSelP;
             if (it < items) {
                 const uint16_t *src = (row < nu ? wr : h) + (int64_t)src_row[i] * D;
                 sreg[slot][i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
@@ -524,7 +534,7 @@ __global__ void __launch_bounds__(256, 2) router_select_kernel(int32_t T, int32_
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
             const int it = tid + 256 * i;
-            const int row = it >> 2, q = it & 3;
+            const int row = it / kSelP, q = it % kSelP;
             if (it < items) {
                 uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
                                         : hst + (buf * 16 + (row - nu)) * kSelRow;
@@ -556,7 +566,7 @@ __global__ void __launch_bounds__(256, 2) router_select_kernel(int32_t T, int32_
                 const uint8_t *hrow = hst + (buf * 16 + ptl) * kSelRow;
                 const uint8_t *wrow = wst + ((size_t)buf * E + ps) * kSelRow;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < kSelP; ++q) {
                     const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
                     const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + 16 * q);
                     a = __builtin_fmaf(bf_lo(hv.x), bf_lo(wv.x), a);
