@@ -1,4 +1,4 @@
-"""CPU oracle of the routed-expert MoE layer (NVFP4 / MXFP8 experts).
+"""CPU oracle of the routed-expert MoE layer (NVFP4 / MXFP8 / MXFP4 experts).
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and
 by bench.py's cpu_baseline leg, never by the library. It wraps oracle.c (plain
@@ -21,8 +21,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_NONE, FMT_NVFP4, FMT_MXFP8 = 0, 1, 2
-_FMT = {"none": 0, "bf16": 0, "nvfp4": 1, "mxfp8": 2}
+FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4 = 0, 1, 2, 3
+_FMT = {"none": 0, "bf16": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3}
 
 
 def build() -> str:
@@ -77,6 +77,12 @@ def _load():
     lib.orc_quant_nvfp4_mode.restype = ctypes.c_int
     lib.orc_quant_mxfp8.argtypes = [p, i64, i64, p, p]
     lib.orc_quant_mxfp8.restype = ctypes.c_int
+    lib.orc_quant_mxfp4.argtypes = [p, i64, i64, p, p]
+    lib.orc_quant_mxfp4.restype = ctypes.c_int
+    lib.orc_dequant_mxfp4.argtypes = [p, p, i64, i64, p]
+    lib.orc_dequant_mxfp4.restype = ctypes.c_int
+    lib.orc_mxfp4_scale_code.argtypes = [flt]
+    lib.orc_mxfp4_scale_code.restype = ctypes.c_int
     lib.orc_dequant_nvfp4.argtypes = [p, p, flt, i64, i64, ctypes.c_int, p]
     lib.orc_dequant_nvfp4.restype = ctypes.c_int
     lib.orc_dequant_mxfp8.argtypes = [p, p, i64, i64, p]
@@ -129,6 +135,10 @@ def e8m0_code_for_amax(amax: float) -> int:
     return _load().orc_e8m0_code_for_amax(float(amax))
 
 
+def mxfp4_scale_code(amax: float) -> int:
+    return _load().orc_mxfp4_scale_code(float(amax))
+
+
 def nvfp4_tensor_scale(amax: float) -> float:
     return float(_load().orc_nvfp4_tensor_scale(float(amax)))
 
@@ -172,6 +182,26 @@ def dequant_nvfp4(codes, scales, tensor_scale, with_tensor=True) -> np.ndarray:
     return out
 
 
+def quant_mxfp4(x: np.ndarray):
+    """MXFP4 of a [rows, K] fp32 tensor -> (codes [rows,K/2] (element 2i in the low
+    nibble), scales [rows,K/32])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    codes = np.empty((rows, K // 2), np.uint8)
+    scales = np.empty((rows, K // 32), np.uint8)
+    _check(_load().orc_quant_mxfp4(_ptr(x), rows, K, _ptr(codes), _ptr(scales)), "quant_mxfp4")
+    return codes, scales
+
+
+def dequant_mxfp4(codes, scales) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, K = codes.shape[0], codes.shape[1] * 2
+    out = np.empty((rows, K), np.float64)
+    _check(_load().orc_dequant_mxfp4(_ptr(codes), _ptr(scales), rows, K, _ptr(out)), "dequant_mxfp4")
+    return out
+
+
 def dequant_mxfp8(codes, scales) -> np.ndarray:
     codes = np.ascontiguousarray(codes, np.uint8)
     scales = np.ascontiguousarray(scales, np.uint8)
@@ -190,6 +220,10 @@ def quantize_weights(fmt: str, w_bf16: np.ndarray):
         codes = np.empty((E, N, K // 2), np.uint8)
         scales = np.empty((E, N, K // 16), np.uint8)
         ts = np.empty(E, np.float32)
+    elif f == FMT_MXFP4:
+        codes = np.empty((E, N, K // 2), np.uint8)
+        scales = np.empty((E, N, K // 32), np.uint8)
+        ts = None
     else:
         codes = np.empty((E, N, K), np.uint8)
         scales = np.empty((E, N, K // 32), np.uint8)
@@ -236,7 +270,7 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
                 down_master=None, taps: bool = False, tok_list=None):
     """Oracle MoE forward -> out float32 [T, D] (and a dict of taps when taps=True).
 
-    gate_up/down: dicts from quantize_weights (fmt nvfp4/mxfp8); *_master: bf16 arrays (fmt none).
+    gate_up/down: dicts from quantize_weights (fmt nvfp4/mxfp8/mxfp4); *_master: bf16 arrays (fmt none).
     tok_list: compute only these tokens' outputs (others are zero)."""
     f = _FMT[fmt]
     lib = _load()
@@ -269,11 +303,11 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
         _, offs, _ = permute(idx, e_begin, e_end)
         S = int(offs[-1])
         if f != FMT_NONE:
-            tp["a_codes"] = np.zeros((T, D // 2 if f == FMT_NVFP4 else D), np.uint8)
+            tp["a_codes"] = np.zeros((T, D if f == FMT_MXFP8 else D // 2), np.uint8)
             tp["a_scales"] = np.zeros((T, D // 16 if f == FMT_NVFP4 else D // 32), np.uint8)
             tp["a_tscale"] = np.zeros(1, np.float32)
             tp["inter"] = np.zeros((S, F), np.float32)
-            tp["inter_codes"] = np.zeros((S, F // 2 if f == FMT_NVFP4 else F), np.uint8)
+            tp["inter_codes"] = np.zeros((S, F if f == FMT_MXFP8 else F // 2), np.uint8)
             tp["inter_scales"] = np.zeros((S, F // 16 if f == FMT_NVFP4 else F // 32), np.uint8)
             tp["inter_tscale"] = np.zeros(1, np.float32)
             for n in ("a_codes", "a_scales", "a_tscale", "inter", "inter_codes", "inter_scales",

@@ -1,6 +1,6 @@
 /*
  * oracle.c - plain, slow CPU oracle of the routed-expert MoE layer with
- * block-scaled (NVFP4 / MXFP8) experts.
+ * block-scaled (NVFP4 / MXFP8 / MXFP4) experts.
  *
  * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the bench's
  * CPU-baseline leg call into this file. It shares no code, header, table or
@@ -15,11 +15,17 @@
  *      maximum to 4 and to 6 and keeps the lower-error result) and section
  *      "NVFP4 and MXFP8 experts" (eight of 384 experts per token; activations
  *      quantised to match the layer's weight format).
+ *  [V] vLLM recipe "thinkingmachines/Inkling-Small", section "Variants" and the
+ *      recipe's variant list: an OCP MXFP4 checkpoint for AMD Instinct, run on
+ *      MI355X as native W4A4 MXFP4 MoE (the MXFP4 format below).
  * The pages fix neither the gate, the expert MLP, the element/scale formats'
  * bit layouts nor the arithmetic order. The readings taken here (softmax then
  * top-8 with lower-index tie-break; SwiGLU experts; E2M1 codes with an E4M3
  * scale per 16 and an fp32 tensor scale amax/(6*448); E4M3 codes with an E8M0
- * scale 2^(floor(log2 amax) - 8) per 32; fp32 logits summed in ascending k;
+ * scale 2^(floor(log2 amax) - 8) per 32; for MXFP4, E2M1 codes with an E8M0
+ * scale 2^(floor(log2 amax) - 2) per 32, activations quantised the same way (the
+ * OCP MX shared-exponent rule with E2M1's largest exponent 2, as MXFP8 uses E4M3's 8);
+ * fp32 logits summed in ascending k;
  * fp64 expert arithmetic) are the plainest ones the rest supports.
  *
  * Build: gcc -O2 -std=c11 -fopenmp -ffp-contract=off (no -ffast-math, no FTZ),
@@ -117,6 +123,16 @@ static int floor_log2(double a) {
 int orc_e8m0_code_for_amax(float amax) {
     if (!(amax > 0.0f)) return 0;
     int se = floor_log2((double)amax) - 8;
+    if (se < -127) se = -127;
+    if (se > 127) se = 127;
+    return se + 127;
+}
+
+/* MXFP4 block scale code: E8M0 of 2^(floor(log2 amax) - 2), the exponent clamped
+ * to [-127, 127]; amax == 0 gives code 0x00. */
+int orc_mxfp4_scale_code(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int se = floor_log2((double)amax) - 2;
     if (se < -127) se = -127;
     if (se > 127) se = 127;
     return se + 127;
@@ -249,6 +265,37 @@ int orc_quant_mxfp8(const float *x, int64_t rows, int64_t K, uint8_t *codes, uin
 }
 
 /* ------------------------------------------------------------------------- */
+/* MXFP4 quantiser: E2M1 elements, E8M0 scale per 32 ([V] "Variants").        */
+/* ------------------------------------------------------------------------- */
+
+/* codes16: the block's 32 E2M1 codes, element 2i in the low nibble of byte i */
+static void mxfp4_block(const float *x, uint8_t *codes16, uint8_t *scale) {
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    int sc = orc_mxfp4_scale_code(amax);
+    int se = sc - 127;
+    for (int i = 0; i < 16; ++i) {
+        int lo = orc_e2m1_encode(ldexp((double)x[2 * i], -se));
+        int hi = orc_e2m1_encode(ldexp((double)x[2 * i + 1], -se));
+        codes16[i] = (uint8_t)(lo | (hi << 4));
+    }
+    *scale = (uint8_t)sc;
+}
+
+/* codes: [rows][K/2]; scales: [rows][K/32]. K must be a multiple of 32. */
+int orc_quant_mxfp4(const float *x, int64_t rows, int64_t K, uint8_t *codes, uint8_t *scales) {
+    if (!x || !codes || !scales || rows < 0 || K <= 0 || K % 32) return ORC_EINVAL;
+    init_tables();
+    int64_t nb = rows * (K / 32);
+#pragma omp parallel for schedule(static)
+    for (int64_t b = 0; b < nb; ++b) mxfp4_block(x + b * 32, codes + b * 16, scales + b);
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Dequantisation (fp64).                                                     */
 /* ------------------------------------------------------------------------- */
 
@@ -272,17 +319,28 @@ int orc_dequant_mxfp8(const uint8_t *codes, const uint8_t *scales, int64_t rows,
     return ORC_OK;
 }
 
+/* x_hat = e2m1(code) * e8m0(scale) */
+int orc_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t K, double *out) {
+    if (!codes || !scales || !out || K % 32) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows * K; ++i) {
+        int c = (codes[i / 2] >> ((i & 1) * 4)) & 15;
+        out[i] = orc_e2m1_value(c) * orc_e8m0_value(scales[i / 32]);
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------------- */
 /* Weight quantisation over E experts (one tensor per expert per matrix).     */
 /* ------------------------------------------------------------------------- */
 
-/* fmt 1 = NVFP4, 2 = MXFP8. w: bf16 [E][N][K]. tensor_scale: fp32 [E] (NVFP4). */
+/* fmt 1 = NVFP4, 2 = MXFP8, 3 = MXFP4. w: bf16 [E][N][K]. tensor_scale: fp32 [E] (NVFP4). */
 int orc_quantize_weights(int fmt, int32_t E, int32_t N, int32_t K, const uint16_t *w, uint8_t *codes,
                          uint8_t *scales, float *tensor_scale) {
     if (!w || !codes || !scales || E <= 0 || N <= 0 || K <= 0) return ORC_EINVAL;
     if (fmt == 1 && (!tensor_scale || K % 16)) return ORC_EINVAL;
-    if (fmt == 2 && K % 32) return ORC_EINVAL;
-    if (fmt != 1 && fmt != 2) return ORC_EINVAL;
+    if ((fmt == 2 || fmt == 3) && K % 32) return ORC_EINVAL;
+    if (fmt < 1 || fmt > 3) return ORC_EINVAL;
     int64_t per = (int64_t)N * K;
     float *buf = (float *)malloc(sizeof(float) * per);
     if (!buf) return ORC_ENOMEM;
@@ -293,8 +351,10 @@ int orc_quantize_weights(int fmt, int32_t E, int32_t N, int32_t K, const uint16_
         for (int64_t i = 0; i < per; ++i) buf[i] = bf16_value(src[i]);
         if (fmt == 1)
             rc = orc_quant_nvfp4(buf, N, K, codes + e * per / 2, scales + e * per / 16, tensor_scale + e, NULL);
-        else
+        else if (fmt == 2)
             rc = orc_quant_mxfp8(buf, N, K, codes + e * per, scales + e * per / 32);
+        else
+            rc = orc_quant_mxfp4(buf, N, K, codes + e * per / 2, scales + e * per / 32);
     }
     free(buf);
     return rc;
@@ -442,8 +502,11 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
         } else if (fmt == 1) {
             int c = (codes[i / 2] >> ((i & 1) * 4)) & 15;
             out[j] = orc_e2m1_value(c) * orc_e4m3_value(scales[i / 16]);
-        } else {
+        } else if (fmt == 2) {
             out[j] = orc_e4m3_value(codes[i]) * orc_e8m0_value(scales[i / 32]);
+        } else {
+            int c = (codes[i / 2] >> ((i & 1) * 4)) & 15;
+            out[j] = orc_e2m1_value(c) * orc_e8m0_value(scales[i / 32]);
         }
     }
 }
@@ -453,7 +516,7 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
  *  1. quantise the hidden states once per token to the layer's format;
  *  2. for each local slot (t, j) routed to expert e: gate and up rows of
  *     A_t . W_gu[e]^T summed in fp64; NVFP4 multiplies the fp32-rounded sum by
- *     fl32(s_A * s_W) and rounds again; MXFP8 rounds the sum to fp32;
+ *     fl32(s_A * s_W) and rounds again; MXFP8 and MXFP4 round the sum to fp32;
  *  3. h = SwiGLU(gate, up) (fp64, rounded once to fp32);
  *  4. quantise h to the layer's format (NVFP4: one tensor = all local slots);
  *  5. y = h_hat . W_d[e]^T in fp64, scaled and rounded as in 2;
@@ -465,17 +528,17 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
 int orc_moe_forward(const orc_moe_args *a) {
     if (!a || a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->k <= 0 || a->k > a->E) return ORC_EINVAL;
     if (a->e_begin < 0 || a->e_end > a->E || a->e_end <= a->e_begin) return ORC_EINVAL;
-    if (a->fmt < 0 || a->fmt > 2) return ORC_EINVAL;
+    if (a->fmt < 0 || a->fmt > 3) return ORC_EINVAL;
     const int fmt = a->fmt;
     const int64_t T = a->T, D = a->D, F = a->F, k = a->k;
     if (fmt == 1 && (D % 16 || F % 16)) return ORC_EINVAL;
-    if (fmt == 2 && (D % 32 || F % 32)) return ORC_EINVAL;
+    if ((fmt == 2 || fmt == 3) && (D % 32 || F % 32)) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
     if (!a->h || !a->idx || !a->w || !a->out) return ORC_EINVAL;
     if (fmt == 0 && (!a->gu_master || !a->dn_master)) return ORC_EINVAL;
     if (fmt == 1 && (!a->gu_codes || !a->gu_scales || !a->gu_tscale || !a->dn_codes || !a->dn_scales || !a->dn_tscale))
         return ORC_EINVAL;
-    if (fmt == 2 && (!a->gu_codes || !a->gu_scales || !a->dn_codes || !a->dn_scales)) return ORC_EINVAL;
+    if ((fmt == 2 || fmt == 3) && (!a->gu_codes || !a->gu_scales || !a->dn_codes || !a->dn_scales)) return ORC_EINVAL;
     init_tables();
 
     const int32_t n_loc = a->e_end - a->e_begin;
@@ -520,15 +583,18 @@ int orc_moe_forward(const orc_moe_args *a) {
         if (fmt == 0) {
             for (int64_t i = 0; i < T * D; ++i) ahat[i] = hf[i];
         } else {
-            int64_t nc = fmt == 1 ? T * D / 2 : T * D, ns = fmt == 1 ? T * D / 16 : T * D / 32;
+            int64_t nc = fmt == 2 ? T * D : T * D / 2, ns = fmt == 1 ? T * D / 16 : T * D / 32;
             uint8_t *ac = (uint8_t *)malloc(nc), *as = (uint8_t *)malloc(ns);
             if (!ac || !as) { free(hf); free(ac); free(as); rc = ORC_ENOMEM; goto done; }
             if (fmt == 1) {
                 orc_quant_nvfp4(hf, T, D, ac, as, &a_ts, NULL);
                 orc_dequant_nvfp4(ac, as, a_ts, T, D, 0, ahat);
-            } else {
+            } else if (fmt == 2) {
                 orc_quant_mxfp8(hf, T, D, ac, as);
                 orc_dequant_mxfp8(ac, as, T, D, ahat);
+            } else {
+                orc_quant_mxfp4(hf, T, D, ac, as);
+                orc_dequant_mxfp4(ac, as, T, D, ahat);
             }
             if (a->a_codes) memcpy(a->a_codes, ac, nc);
             if (a->a_scales) memcpy(a->a_scales, as, ns);
@@ -628,14 +694,21 @@ int orc_moe_forward(const orc_moe_args *a) {
         free(ic);
         free(is);
     } else {
-        uint8_t *ic = (uint8_t *)malloc(F), *is = (uint8_t *)malloc(F / 32);
+        /* MXFP8 [S][F] codes, MXFP4 [S][F/2]; both [S][F/32] scales */
+        const int64_t cb = fmt == 2 ? F : F / 2;
+        uint8_t *ic = (uint8_t *)malloc(cb), *is = (uint8_t *)malloc(F / 32);
         if (!ic || !is) { free(ic); free(is); rc = ORC_ENOMEM; goto done; }
         for (int64_t p = 0; p < S; ++p) {
             int64_t c = cidx[p];
             if (c < 0) continue;
-            orc_quant_mxfp8(inter + c * F, 1, F, ic, is);
-            orc_dequant_mxfp8(ic, is, 1, F, ihat + c * F);
-            if (a->inter_codes) memcpy(a->inter_codes + p * F, ic, F);
+            if (fmt == 2) {
+                orc_quant_mxfp8(inter + c * F, 1, F, ic, is);
+                orc_dequant_mxfp8(ic, is, 1, F, ihat + c * F);
+            } else {
+                orc_quant_mxfp4(inter + c * F, 1, F, ic, is);
+                orc_dequant_mxfp4(ic, is, 1, F, ihat + c * F);
+            }
+            if (a->inter_codes) memcpy(a->inter_codes + p * cb, ic, cb);
             if (a->inter_scales) memcpy(a->inter_scales + p * F / 32, is, F / 32);
         }
         free(ic);
@@ -721,13 +794,13 @@ done:
  * out[t] = sum over the token's local slots, j ascending, of w[t][j] * y (fp64, rounded
  * to fp32). Used to check a down projection and combine on another implementation's
  * intermediate codes. i_codes / i_scales: [S][F/2] and [S][F/16] (NVFP4, tensor scale
- * i_ts) or [S][F] and [S][F/32] (MXFP8).
+ * i_ts), [S][F] and [S][F/32] (MXFP8) or [S][F/2] and [S][F/32] (MXFP4).
  */
 int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, int32_t k, int32_t e_begin,
                      int32_t e_end, const int32_t *idx, const float *w, const uint8_t *i_codes,
                      const uint8_t *i_scales, float i_ts, const uint8_t *dn_codes, const uint8_t *dn_scales,
                      const float *dn_tscale, float *out) {
-    if (fmt != 1 && fmt != 2) return ORC_EINVAL;
+    if (fmt < 1 || fmt > 3) return ORC_EINVAL;
     if (T < 0 || D <= 0 || F <= 0 || E <= 0 || k <= 0 || e_begin < 0 || e_end > E || e_end <= e_begin) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
     if (!idx || !w || !i_codes || !i_scales || !dn_codes || !dn_scales || !out || (fmt == 1 && !dn_tscale))
@@ -746,7 +819,8 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
     y64 = (double *)malloc(sizeof(double) * (S > 0 ? S : 1) * D);
     if (!ihat || !y64) { rc = ORC_ENOMEM; goto done; }
     if (fmt == 1) orc_dequant_nvfp4(i_codes, i_scales, i_ts, S, F, 0, ihat);
-    else orc_dequant_mxfp8(i_codes, i_scales, S, F, ihat);
+    else if (fmt == 2) orc_dequant_mxfp8(i_codes, i_scales, S, F, ihat);
+    else orc_dequant_mxfp4(i_codes, i_scales, S, F, ihat);
     {
         int fail = 0;
 #pragma omp parallel

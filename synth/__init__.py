@@ -159,7 +159,7 @@ class Workload:
     """One synthetic MoE-layer workload (shapes, formats, value recipe)."""
     index: int
     name: str
-    fmt: str            # "nvfp4" or "mxfp8"
+    fmt: str            # "nvfp4", "mxfp8" or "mxfp4"
     T: int              # tokens
     D: int              # d_model
     F: int              # d_ff

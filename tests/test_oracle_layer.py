@@ -118,7 +118,7 @@ def _quantised(fmt, wl):
             oracle.quantize_weights(fmt, wl.down_master(0, E)))
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 def test_quantised_layer_composes_from_pinned_parts(fmt):
     """The C pipeline equals a numpy composition of the (pinned) quantisers and BLAS matmuls."""
     T, D, F, E = 20, 64, 64, 12
@@ -127,12 +127,14 @@ def test_quantised_layer_composes_from_pinned_parts(fmt):
     idx, w = oracle.route(h, wr, k=8)
     out, tp = oracle.moe_forward(fmt, h, idx, w, D=D, F=F, E=E, gate_up=gu, down=dn, taps=True)
     H = synth.bf16_to_f32(h)
+    mxq, mxd = (oracle.quant_mxfp4, oracle.dequant_mxfp4) if fmt == "mxfp4" else (oracle.quant_mxfp8,
+                                                                                  oracle.dequant_mxfp8)
     if fmt == "nvfp4":
         ac, as_, ats = oracle.quant_nvfp4(H)
         A = oracle.dequant_nvfp4(ac, as_, ats, with_tensor=False)
     else:
-        ac, as_ = oracle.quant_mxfp8(H)
-        A, ats = oracle.dequant_mxfp8(ac, as_), f32(1)
+        ac, as_ = mxq(H)
+        A, ats = mxd(ac, as_), f32(1)
     assert np.array_equal(ac, tp["a_codes"]) and np.array_equal(as_, tp["a_scales"])
     counts, offs, ss = oracle.permute(idx, 0, E)
     S = len(ss)
@@ -144,7 +146,7 @@ def test_quantised_layer_composes_from_pinned_parts(fmt):
             sc = f32(ats * gu["tensor_scale"][e])
             gl = (W @ A[t]).astype(f32) * sc
         else:
-            W = oracle.dequant_mxfp8(gu["codes"][e], gu["scales"][e])
+            W = mxd(gu["codes"][e], gu["scales"][e])
             gl = (W @ A[t]).astype(f32)
         g, u = gl[:F].astype(np.float64), gl[F:].astype(np.float64)
         inter[p] = (g * u / (1.0 + np.exp(-g))).astype(f32)
@@ -153,8 +155,8 @@ def test_quantised_layer_composes_from_pinned_parts(fmt):
         ic, is_, its = oracle.quant_nvfp4(inter)
         I = oracle.dequant_nvfp4(ic, is_, its, with_tensor=False)
     else:
-        ic, is_ = oracle.quant_mxfp8(inter)
-        I, its = oracle.dequant_mxfp8(ic, is_), f32(1)
+        ic, is_ = mxq(inter)
+        I, its = mxd(ic, is_), f32(1)
     assert np.array_equal(ic, tp["inter_codes"]) and np.array_equal(is_, tp["inter_scales"])
     ref = np.zeros((T, D))
     for p, s in enumerate(ss):
@@ -164,7 +166,7 @@ def test_quantised_layer_composes_from_pinned_parts(fmt):
             Wd = oracle.dequant_nvfp4(dn["codes"][e], dn["scales"][e], 1.0, with_tensor=False)
             y = (Wd @ I[p]).astype(f32) * f32(its * dn["tensor_scale"][e])
         else:
-            y = (oracle.dequant_mxfp8(dn["codes"][e], dn["scales"][e]) @ I[p]).astype(f32)
+            y = (mxd(dn["codes"][e], dn["scales"][e]) @ I[p]).astype(f32)
         np.testing.assert_array_equal(y, tp["y"][p])
         ref[t] += float(w[t, j]) * y.astype(np.float64)
     np.testing.assert_allclose(out, ref.astype(f32), rtol=1e-6, atol=1e-9)
@@ -173,7 +175,7 @@ def test_quantised_layer_composes_from_pinned_parts(fmt):
 def test_quantisation_error_ordering_against_unquantised():
     T, D, F, E = 32, 128, 64, 16
     errs = {}
-    for fmt in ("nvfp4", "mxfp8"):
+    for fmt in ("nvfp4", "mxfp8", "mxfp4"):
         wl, h, wr, _ = _small(fmt, T=T, D=D, F=F, E=E, seed=12)
         gu_m, dn_m = wl.gate_up_master(0, E), wl.down_master(0, E)
         idx, w = oracle.route(h, wr, k=8)
@@ -181,11 +183,11 @@ def test_quantisation_error_ordering_against_unquantised():
         gu, dn = oracle.quantize_weights(fmt, gu_m), oracle.quantize_weights(fmt, dn_m)
         out = oracle.moe_forward(fmt, h, idx, w, D=D, F=F, E=E, gate_up=gu, down=dn)
         errs[fmt] = np.linalg.norm(out - ref) / np.linalg.norm(ref)
-    assert errs["mxfp8"] < 0.08 and errs["nvfp4"] < 0.35
-    assert errs["mxfp8"] < errs["nvfp4"] / 2
+    assert errs["mxfp8"] < 0.08 and errs["nvfp4"] < 0.35 and errs["mxfp4"] < 0.45
+    assert errs["mxfp8"] < errs["nvfp4"] / 2 and errs["nvfp4"] < errs["mxfp4"]
 
 
-@pytest.mark.parametrize("fmt", ["none", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["none", "mxfp8", "mxfp4"])
 def test_expert_parallel_shares_add_up(fmt):
     """Four expert ranges (an EP4 split) sum to the full layer. NVFP4 is excluded:
     its intermediate tensor scale is taken over each share's own slots."""
@@ -230,7 +232,7 @@ def test_empty_batch_is_a_no_op():
     assert out.shape == (0, 64)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 def test_down_combine_reproduces_the_forward(fmt):
     """The stage-wise entry point (down projection + combine from given intermediate codes),
     fed the forward's own intermediate codes, gives the forward's output bit for bit, also

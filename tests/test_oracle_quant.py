@@ -1,9 +1,10 @@
-"""Oracle NVFP4 (4-vs-6 rule) and MXFP8 quantisers pinned by hand-worked blocks,
-exact-rational brute force, a library E4M3 encoder and invariants.
+"""Oracle NVFP4 (4-vs-6 rule), MXFP8 and MXFP4 quantisers pinned by hand-worked
+blocks, exact-rational brute force, a library E4M3 encoder and invariants.
 
 4-vs-6 rule: AI Primer, "Thinking Machines releases Inkling 2 Small weights under
 Apache 2.0", section "TL;DR". Formats: vLLM recipe "thinkingmachines/Inkling-2-Small",
-section "Overview" (NVFP4 and MXFP8 experts).
+section "Overview" (NVFP4 and MXFP8 experts); vLLM recipe "thinkingmachines/Inkling-Small",
+section "Variants" (OCP MXFP4 experts for AMD Instinct).
 """
 import math
 import os
@@ -232,3 +233,87 @@ def test_quantize_weights_per_expert_tensors():
     c8, s8 = oracle.quant_mxfp8(synth.bf16_to_f32(w.reshape(E * N, K)))
     assert np.array_equal(c8, q8["codes"].reshape(E * N, K))
     assert np.array_equal(s8, q8["scales"].reshape(E * N, K // 32))
+
+
+# ------------------------------------------------------------------ MXFP4
+def test_mxfp4_hand_worked_values():
+    for r in _rows("mxfp4_values.txt"):
+        blk, vals, sbyte, cbytes = [s.strip() for s in r.split("|")]
+        x = np.zeros((1, 32), f32)
+        v = [float(s) for s in vals.split()]
+        x[0, :len(v)] = v
+        codes, scales = oracle.quant_mxfp4(x)
+        assert scales[0, 0] == int(sbyte, 16), blk
+        want = [int(b, 16) for b in cbytes.split()]
+        assert list(codes[0, :len(want)]) == want, blk
+
+
+_E2M1_MAG = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2), Fraction(3), Fraction(4),
+             Fraction(6)]
+
+
+def _e2m1_brute(v: Fraction) -> int:
+    """Nearest E2M1 magnitude by exhaustive search, ties to the even code, saturating at 6."""
+    a = abs(v)
+    if a >= 6:
+        c = 7
+    else:
+        d = [abs(a - m) for m in _E2M1_MAG]
+        best = min(d)
+        cands = [i for i, x in enumerate(d) if x == best]
+        c = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+    return c | (8 if v < 0 else 0)
+
+
+def test_mxfp4_brute_force_and_closed_form_scale():
+    h = synth.bf16_to_f32(synth.normal_bf16(6, 1, 0, 64 * 256, 1.0)).reshape(64, 256)
+    h[3, :32] *= f32(2.0 ** -120)   # tiny block
+    h[4, 32:64] = 0.0               # zero block
+    h[5, :32] = np.array([0.25 * i for i in range(32)], f32)  # many exact ties
+    codes, scales = oracle.quant_mxfp4(h)
+    blocks = h.reshape(-1, 32)
+    got = _unpack(codes).reshape(-1, 32)
+    for b in range(blocks.shape[0]):
+        amax = float(np.abs(blocks[b]).max())
+        se = 0 if amax == 0 else min(max(math.frexp(amax)[1] - 1 - 2, -127), 127)
+        assert scales.reshape(-1)[b] == (0 if amax == 0 else se + 127)
+        if amax == 0:
+            se = -127
+        for i in range(32):
+            x = float(blocks[b, i])
+            want = _e2m1_brute(Fraction(x) / Fraction(2) ** se)
+            if x == 0.0 and math.copysign(1.0, x) < 0:
+                want = 8
+            assert got[b, i] == want, (b, i, x)
+
+
+def test_mxfp4_requantises_its_own_values():
+    """Dequantised values quantise back to the same codes and scales (the scale exponent
+    is stable: the block maximum rounds to at least 4 * 2^(e - 2) = 2^e)."""
+    w = synth.bf16_to_f32(synth.normal_bf16(7, 2, 0, 128 * 512, 0.02)).reshape(128, 512)
+    c, s = oracle.quant_mxfp4(w)
+    xh = oracle.dequant_mxfp4(c, s).astype(f32)
+    c2, s2 = oracle.quant_mxfp4(xh)
+    assert np.array_equal(c, c2) and np.array_equal(s, s2)
+
+
+def test_mxfp4_error_between_nvfp4_bounds_and_mxfp8():
+    """MXFP4 (power-of-two scales, per 32) loses more than MXFP8 and more than NVFP4's
+    finer E4M3 scales per 16."""
+    w = synth.bf16_to_f32(synth.normal_bf16(9, 3, 0, 512 * 1024, 0.02)).reshape(512, 1024)
+    c4, s4 = oracle.quant_mxfp4(w)
+    cn, sn, tn = oracle.quant_nvfp4(w)
+    c8, s8 = oracle.quant_mxfp8(w)
+    err = lambda xh: np.linalg.norm(w - xh) / np.linalg.norm(w)
+    e4, en, e8 = err(oracle.dequant_mxfp4(c4, s4)), err(oracle.dequant_nvfp4(cn, sn, tn)), err(oracle.dequant_mxfp8(c8, s8))
+    assert e8 < en < e4 < 0.2
+
+
+def test_quantize_weights_mxfp4_per_row_blocks():
+    E, N, K = 3, 32, 64
+    w = synth.normal_bf16(2, 5, 0, E * N * K, 0.02).reshape(E, N, K)
+    q = oracle.quantize_weights("mxfp4", w)
+    c, s = oracle.quant_mxfp4(synth.bf16_to_f32(w.reshape(E * N, K)))
+    assert q["tensor_scale"] is None
+    assert np.array_equal(c, q["codes"].reshape(E * N, K // 2))
+    assert np.array_equal(s, q["scales"].reshape(E * N, K // 32))
