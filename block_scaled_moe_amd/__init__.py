@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-FMT = {"nvfp4": 1, "mxfp8": 2}
+FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3}
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "alignment",
           -4: "workspace", -5: "HIP launch failed"}
 
@@ -103,8 +103,8 @@ def _check(rc: int, what: str):
 @dataclasses.dataclass
 class PackedWeights:
     """Device tensors of one packed matrix kind for E experts (logically [E][N][K]) in the
-    tiled layout of include/moe.h: codes [E][N/32][K/64][32][32 | 64] and scales
-    [E][N/32][K/64][32][4 | 2] (NVFP4 | MXFP8)."""
+    tiled layout of include/moe.h: codes [E][N/32][K/64][32][32 | 64 | 32] and scales
+    [E][N/32][K/64][32][4 | 2 | 2] (NVFP4 | MXFP8 | MXFP4)."""
     fmt: str
     E: int
     N: int
@@ -115,10 +115,13 @@ class PackedWeights:
 
     @staticmethod
     def empty(fmt: str, E: int, N: int, K: int, device="cuda") -> "PackedWeights":
+        if fmt not in FMT:
+            raise ValueError(f"unknown format {fmt!r}")
         nv = fmt == "nvfp4"
         if N % 32 or K % 64:
             raise ValueError(f"packed weights need N % 32 == 0 and K % 64 == 0 (got N={N}, K={K})")
-        codes = torch.empty((E, N // 32, K // 64, 32, 32 if nv else 64), dtype=torch.uint8, device=device)
+        codes = torch.empty((E, N // 32, K // 64, 32, 64 if fmt == "mxfp8" else 32), dtype=torch.uint8,
+                            device=device)
         scales = torch.empty((E, N // 32, K // 64, 32, 4 if nv else 2), dtype=torch.uint8, device=device)
         ts = torch.empty(E, dtype=torch.float32, device=device) if nv else None
         return PackedWeights(fmt, E, N, K, codes, scales, ts)
@@ -208,10 +211,10 @@ class Layer:
         spec = {
             "counts": ((n,), torch.int32), "offsets": ((n + 1,), torch.int32),
             "sorted_slot": ((TK,), torch.int32),
-            "a_codes": ((T, D // 2 if nv else D), torch.uint8),
+            "a_codes": ((T, D if self.fmt == "mxfp8" else D // 2), torch.uint8),
             "a_scales": ((T, D // 16 if nv else D // 32), torch.uint8),
             "inter": ((TK, F), torch.float32),
-            "inter_codes": ((TK, F // 2 if nv else F), torch.uint8),
+            "inter_codes": ((TK, F if self.fmt == "mxfp8" else F // 2), torch.uint8),
             "inter_scales": ((TK, F // 16 if nv else F // 32), torch.uint8),
             "y": ((TK, D), torch.float32),
         }

@@ -3,7 +3,9 @@
 // NVFP4 (E2M1 codes, E4M3 scale per 16, fp32 tensor scale) with the 4-vs-6 block
 // rule of AI Primer, "Thinking Machines releases Inkling 2 Small weights under
 // Apache 2.0", section "TL;DR"; MXFP8 (E4M3 codes, E8M0 scale per 32) named in
-// the vLLM recipe "thinkingmachines/Inkling-2-Small", section "Overview".
+// the vLLM recipe "thinkingmachines/Inkling-2-Small", section "Overview"; MXFP4
+// (E2M1 codes, E8M0 scale per 32) as in the AMD variant of the vLLM recipe
+// "thinkingmachines/Inkling-Small", section "Variants".
 //
 // Every floating-point step below is one IEEE binary32 operation with
 // round-to-nearest-even: the library is compiled with -ffp-contract=off,
@@ -215,6 +217,38 @@ __device__ __forceinline__ int mxfp8_quant_block(const float (&x)[32], uint32_t 
         const float v0 = e4m3_clamp(ldexpf(x[4 * w], -se)), v1 = e4m3_clamp(ldexpf(x[4 * w + 1], -se));
         const float v2 = e4m3_clamp(ldexpf(x[4 * w + 2], -se)), v3 = e4m3_clamp(ldexpf(x[4 * w + 3], -se));
         codes[w] = e4m3_pack2<true>(e4m3_pack2<false>(0u, v0, v1), v2, v3);
+    }
+    return sc;
+}
+
+// ---------------------------------------------------------------- MXFP4 block
+// OCP MXFP4 (vLLM recipe "thinkingmachines/Inkling-Small", section "Variants": the AMD
+// checkpoint's W4A4 experts): E2M1 codes with one E8M0 scale per 32 values,
+// 2^(floor(log2 amax) - 2) (E2M1's largest exponent is 2), exponent clamped to
+// [-127, 127], code 0 when amax == 0.
+__device__ __forceinline__ int mxfp4_scale_code(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
+    int se = ef - 127 - 2;  // a subnormal amax (ef == 0) lands below -127 as well
+    if (se < -127) se = -127;
+    return se + 127;
+}
+
+// Quantise one 32-block: E8M0 scale code and 32 E2M1 codes of x * 2^-exponent packed
+// two per byte (element 2i in the low nibble); the power-of-two scaling is exact for
+// every value whose code is not zero, and the convert saturates at 6.
+__device__ __forceinline__ int mxfp4_quant_block(const float (&x)[32], uint32_t (&codes)[4]) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    const int sc = mxfp4_scale_code(amax);
+    const int se = sc - 127;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        uint32_t v = e2m1_pack2<0>(0u, ldexpf(x[8 * w], -se), ldexpf(x[8 * w + 1], -se));
+        v = e2m1_pack2<1>(v, ldexpf(x[8 * w + 2], -se), ldexpf(x[8 * w + 3], -se));
+        v = e2m1_pack2<2>(v, ldexpf(x[8 * w + 4], -se), ldexpf(x[8 * w + 5], -se));
+        codes[w] = e2m1_pack2<3>(v, ldexpf(x[8 * w + 6], -se), ldexpf(x[8 * w + 7], -se));
     }
     return sc;
 }

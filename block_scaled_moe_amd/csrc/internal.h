@@ -25,6 +25,11 @@ hipError_t launch_quant_weights_nvfp4(const uint16_t *w, int32_t E, int32_t N, i
 hipError_t launch_finish_tensor_scale(float *ts_inout, int32_t n, hipStream_t s);
 hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, int32_t K,
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
+hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K,
+                                      uint8_t *codes, uint8_t *scales, hipStream_t s);
+// hidden states [T][D] -> MXFP4 codes [T][D/2] and E8M0 scales [T][D/32]
+hipError_t launch_quant_act_mxfp4(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
+                                  hipStream_t s);
 // hidden states [T][D] -> NVFP4 codes/scales and the exact fp16 value codes*scale
 hipError_t launch_quant_act_nvfp4(const uint16_t *h, int32_t T, int32_t D, const uint32_t *amax_bits,
                                   uint8_t *codes, uint8_t *scales, _Float16 *deq, float *tscale_out,
@@ -83,6 +88,8 @@ struct GemmArgs {
     int32_t e_begin;          // global index of local expert 0
     // A operand: exact 16-bit values of the quantised activations, [rows][K]
     const void *a_vals;       // NVFP4: fp16; MXFP8: bf16
+    // MXFP4 A operand: the codes themselves, [rows][K/2] and E8M0 scales [rows][K/32]
+    const uint8_t *a_codes, *a_scales;
     const float *a_tscale;    // NVFP4: [1] activation tensor scale
     // weights (canonical packed layout, global expert index)
     const uint8_t *w_codes, *w_scales;
@@ -90,7 +97,7 @@ struct GemmArgs {
     // outputs
     float *out_f32;           // gate_up NVFP4: SwiGLU [S][F]; down: y [S][N]
     uint32_t *amax_bits;      // gate_up NVFP4: max |SwiGLU|
-    uint8_t *o_codes, *o_scales;  // gate_up MXFP8: quantised SwiGLU [S][F], [S][F/32]
+    uint8_t *o_codes, *o_scales;  // gate_up MXFP8 / MXFP4: quantised SwiGLU [S][F] or [S][F/2], [S][F/32]
     void *o_vals;             // gate_up MXFP8: exact bf16 values of those codes [S][F]
     float *o_tap;             // gate_up MXFP8: optional fp32 SwiGLU [S][F]
 };
@@ -105,6 +112,11 @@ hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t
 // decode-shaped streaming variant (gemm_stream.hip): 16-row M-tiles, K a multiple of 512
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
 hipError_t launch_stream_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);
+
+// native MXFP4 GEMMs on the gfx950 scaled FP4 MFMA (gemm_mx4.hip): 64-row M-tiles (the
+// tile kernels' BM), 256 weight rows per workgroup; K % 64, gate_up F % 128, down N % 256
+bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up);
+hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int32_t T, int32_t D, int32_t k, const int32_t *slot_pos, const float *w,

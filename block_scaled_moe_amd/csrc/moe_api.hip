@@ -39,11 +39,12 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 Plan make_plan(const moe_forward_args *a) {
     Plan p{};
     const int64_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
-    const bool nv = a->fmt == MOE_FMT_NVFP4;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
-    p.tile64 = p.shape == GemmShape::Prefill && tile_gemm_supported(a->D, 2 * a->F, true) &&
-               tile_gemm_supported(a->F, a->D, false);
+    // MXFP4 always runs the scaled-FP4 MFMA kernels, whose M-tiles are the tile kernels' 64 rows
+    p.tile64 = mx4 || (p.shape == GemmShape::Prefill && tile_gemm_supported(a->D, 2 * a->F, true) &&
+                       tile_gemm_supported(a->F, a->D, false));
     p.bm = p.tile64 ? tile_gemm_bm() : gemm_bm(p.shape);
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
@@ -63,21 +64,23 @@ Plan make_plan(const moe_forward_args *a) {
     p.tile_row0 = take(sizeof(int32_t) * p.max_tiles);
     p.sorted_slot = take(sizeof(int32_t) * TK);
     p.slot_pos = take(sizeof(int32_t) * TK);
-    p.a_codes = take(nv ? T * D / 2 : T * D);
+    p.a_codes = take(a->fmt == MOE_FMT_MXFP8 ? T * D : T * D / 2);
     p.a_scales = take(nv ? T * D / 16 : T * D / 32);
     p.a_tscale = take(sizeof(float));
-    p.a16 = take(2 * T * D);  // exact 16-bit values of the hidden-state codes
+    p.a16 = mx4 ? 0 : take(2 * T * D);  // exact 16-bit values of the hidden-state codes
     p.inter32 = nv ? take(sizeof(float) * TK * F) : 0;
-    p.i_codes = take(nv ? TK * F / 2 : TK * F);
+    p.i_codes = take(a->fmt == MOE_FMT_MXFP8 ? TK * F : TK * F / 2);
     p.i_scales = take(nv ? TK * F / 16 : TK * F / 32);
     p.i_tscale = take(sizeof(float));
-    p.i16 = take(2 * TK * F);  // exact 16-bit values of the intermediate codes
+    p.i16 = mx4 ? 0 : take(2 * TK * F);  // exact 16-bit values of the intermediate codes
     p.y = take(sizeof(float) * TK * D);
     p.total = off;
     return p;
 }
 
-hipError_t run_gemm(const GemmArgs &g, bool nv, bool gate_up, const Plan &P, hipStream_t s) {
+hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
+    if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.max_tiles, s);
+    const bool nv = fmt == MOE_FMT_NVFP4;
     if (P.tile64) return launch_tile_gemm(g, nv, gate_up, P.max_tiles, s);
     if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
         return launch_stream_gemm(g, nv, gate_up, P.max_tiles, s);
@@ -113,7 +116,7 @@ const char *moe_status_string(int32_t s) {
 int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     if (!out || !w) return MOE_ERR_INVALID_ARG;
     const int32_t fmt = out->fmt, E = out->E, N = out->N, K = out->K;
-    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4) return MOE_ERR_INVALID_ARG;
     if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
     if (N % 32 || K % 64) return MOE_ERR_INVALID_ARG;  // tiled layout of include/moe.h
     if (!out->codes || !out->scales || (fmt == MOE_FMT_NVFP4 && !out->tensor_scale)) return MOE_ERR_INVALID_ARG;
@@ -121,6 +124,8 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     hipStream_t s = (hipStream_t)stream;
     if (fmt == MOE_FMT_MXFP8)
         return to_status(launch_quant_weights_mxfp8(w, E, N, K, out->codes, out->scales, s));
+    if (fmt == MOE_FMT_MXFP4)
+        return to_status(launch_quant_weights_mxfp4(w, E, N, K, out->codes, out->scales, s));
     uint32_t *amax = reinterpret_cast<uint32_t *>(out->tensor_scale);  // amax bits, then the scale
     MOE_TRY(launch_fill_u32(amax, 0u, E, s));
     MOE_TRY(launch_amax_bf16_rows(w, (int64_t)E * N, K, E, amax, s));
@@ -158,12 +163,15 @@ namespace {
 // The size fields alone (what the workspace plan depends on).
 int32_t validate_shape(const moe_forward_args *a) {
     if (!a) return MOE_ERR_INVALID_ARG;
-    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8 && a->fmt != MOE_FMT_MXFP4) return MOE_ERR_INVALID_ARG;
     if (a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->E > 4096) return MOE_ERR_INVALID_ARG;
     if (a->top_k < 1 || a->top_k > 8 || a->top_k > a->E) return MOE_ERR_INVALID_ARG;
     if (a->e_begin < 0 || a->e_end <= a->e_begin || a->e_end > a->E) return MOE_ERR_INVALID_ARG;
     if ((int64_t)a->T * a->top_k > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
     if (a->D % 128 || a->F % 128) return MOE_ERR_UNSUPPORTED;
+    if (a->fmt == MOE_FMT_MXFP4 &&
+        !(mx4_gemm_supported(a->D, 2 * a->F, true) && mx4_gemm_supported(a->F, a->D, false)))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -202,7 +210,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     if (((uintptr_t)a->workspace & 255u) != 0) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = static_cast<uint8_t *>(a->workspace);
-    const bool nv = a->fmt == MOE_FMT_NVFP4;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
     const int32_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
     Ctrl *ctrl = reinterpret_cast<Ctrl *>(ws + P.ctrl);
     auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
@@ -246,6 +254,8 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         }
         MOE_TRY(launch_quant_act_nvfp4(a->h, T, D, amax, U8(P.a_codes), U8(P.a_scales), F16(P.a16),
                                        F32(P.a_tscale), s));
+    } else if (mx4) {
+        MOE_TRY(launch_quant_act_mxfp4(a->h, T, D, U8(P.a_codes), U8(P.a_scales), s));
     } else {
         MOE_TRY(launch_quant_act_mxfp8(a->h, T, D, U8(P.a_codes), U8(P.a_scales),
                                        reinterpret_cast<uint16_t *>(ws + P.a16), s));
@@ -266,24 +276,26 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     g.w_codes = a->gate_up.codes;
     g.w_scales = a->gate_up.scales;
     g.w_tscale = a->gate_up.tensor_scale;
-    g.a_vals = ws + P.a16;
+    g.a_vals = mx4 ? nullptr : ws + P.a16;
+    g.a_codes = U8(P.a_codes);
+    g.a_scales = U8(P.a_scales);
     if (nv) {
         g.a_tscale = F32(P.a_tscale);
         g.out_f32 = F32(P.inter32);
         g.amax_bits = &ctrl->amax_i;
         MOE_TRY(mark(MOE_EV_GATE_UP));
-        MOE_TRY(run_gemm(g, true, true, P, s));
+        MOE_TRY(run_gemm(g, a->fmt, true, P, s));
         MOE_TRY(mark(MOE_EV_GATE_UP_END));
         // 4. NVFP4 intermediate: one tensor scale over all S rows
         MOE_TRY(launch_quant_inter_nvfp4(F32(P.inter32), TK, F, ctrl, U8(P.i_codes), U8(P.i_scales), F16(P.i16),
                                          F32(P.i_tscale), s));
     } else {
         g.o_codes = U8(P.i_codes);
-        g.o_vals = ws + P.i16;
+        g.o_vals = mx4 ? nullptr : ws + P.i16;
         g.o_scales = U8(P.i_scales);
         g.o_tap = a->taps ? a->taps->inter : nullptr;
         MOE_TRY(mark(MOE_EV_GATE_UP));
-        MOE_TRY(run_gemm(g, false, true, P, s));
+        MOE_TRY(run_gemm(g, a->fmt, true, P, s));
         MOE_TRY(mark(MOE_EV_GATE_UP_END));
     }
 
@@ -301,10 +313,12 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     d.o_scales = nullptr;
     d.o_tap = nullptr;
     d.o_vals = nullptr;
-    d.a_vals = ws + P.i16;
+    d.a_vals = mx4 ? nullptr : ws + P.i16;
+    d.a_codes = U8(P.i_codes);
+    d.a_scales = U8(P.i_scales);
     d.a_tscale = nv ? F32(P.i_tscale) : nullptr;
     MOE_TRY(mark(MOE_EV_DOWN));
-    MOE_TRY(run_gemm(d, nv, false, P, s));
+    MOE_TRY(run_gemm(d, a->fmt, false, P, s));
     MOE_TRY(mark(MOE_EV_DOWN_END));
 
     // 6. weighted combine
@@ -320,14 +334,15 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         MOE_TRY(cp(t->counts, ws + P.counts, sizeof(int32_t) * P.n_loc));
         MOE_TRY(cp(t->offsets, ws + P.offsets, sizeof(int32_t) * (P.n_loc + 1)));
         MOE_TRY(cp(t->sorted_slot, ws + P.sorted_slot, sizeof(int32_t) * (size_t)TK));
-        MOE_TRY(cp(t->a_codes, ws + P.a_codes, nv ? (size_t)T * D / 2 : (size_t)T * D));
+        const bool mx8 = a->fmt == MOE_FMT_MXFP8;
+        MOE_TRY(cp(t->a_codes, ws + P.a_codes, mx8 ? (size_t)T * D : (size_t)T * D / 2));
         MOE_TRY(cp(t->a_scales, ws + P.a_scales, nv ? (size_t)T * D / 16 : (size_t)T * D / 32));
         if (nv) {
             MOE_TRY(cp(t->a_tscale, ws + P.a_tscale, sizeof(float)));
             MOE_TRY(cp(t->inter, ws + P.inter32, sizeof(float) * (size_t)TK * F));
             MOE_TRY(cp(t->inter_tscale, ws + P.i_tscale, sizeof(float)));
         }
-        MOE_TRY(cp(t->inter_codes, ws + P.i_codes, nv ? (size_t)TK * F / 2 : (size_t)TK * F));
+        MOE_TRY(cp(t->inter_codes, ws + P.i_codes, mx8 ? (size_t)TK * F : (size_t)TK * F / 2));
         MOE_TRY(cp(t->inter_scales, ws + P.i_scales, nv ? (size_t)TK * F / 16 : (size_t)TK * F / 32));
         MOE_TRY(cp(t->y, ws + P.y, sizeof(float) * (size_t)TK * D));
     }

@@ -137,6 +137,42 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp8_bf16_kernel(const uint16
     }
 }
 
+// MXFP4: one thread per 32-block. Hidden states (tile_K == 0): block b of a row-major
+// [rows][K] bf16 tensor, codes [rows][K/2] row-major too. Weights (tile_K == K):
+// storage block b of the packed tile layout (layout.h: 16 code bytes per 32-block,
+// two blocks per row of a 32 x 64 tile, as NVFP4's codes and MXFP8's scales), read
+// from its source row and columns of [E][N][K] masters.
+__global__ void __launch_bounds__(kThreads) quant_mxfp4_bf16_kernel(const uint16_t *__restrict__ x, int64_t n_blocks,
+                                                                    int32_t tile_K, int64_t blocks_per_expert,
+                                                                    uint8_t *__restrict__ codes,
+                                                                    uint8_t *__restrict__ scales) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
+        int64_t src_off = b * 32;
+        if (tile_K) {
+            const int64_t e = b / blocks_per_expert;
+            int64_t n, k;
+            layout::block_source(false, tile_K, b - e * blocks_per_expert, n, k);
+            src_off = (e * (blocks_per_expert / (tile_K / 32)) + n) * tile_K + k;
+        }
+        const uint4 *src = reinterpret_cast<const uint4 *>(x + src_off);
+        float v[32];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint4 u = src[q];
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * q + 2 * j] = __uint_as_float(w[j] << 16);
+                v[8 * q + 2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
+            }
+        }
+        uint32_t c[4];
+        const int sc = mxfp4_quant_block(v, c);
+        reinterpret_cast<uint4 *>(codes)[b] = make_uint4(c[0], c[1], c[2], c[3]);
+        scales[b] = (uint8_t)sc;
+    }
+}
+
 // NVFP4 hidden states: one tensor scale over all T*D values.
 __global__ void __launch_bounds__(kThreads) quant_act_nvfp4_kernel(const uint16_t *__restrict__ h, int64_t n_blocks,
                                                                    const uint32_t *__restrict__ amax_bits,
@@ -236,6 +272,24 @@ hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, i
     const int64_t nb = per * E;
     hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, K, per, codes, scales,
                        (uint16_t *)nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
+                                      uint8_t *scales, hipStream_t s) {
+    const int64_t per = (int64_t)N * (K / 32);
+    const int64_t nb = (int64_t)E * per;
+    hipLaunchKernelGGL(quant_mxfp4_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, w, nb, K, per, codes,
+                       scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_mxfp4(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
+                                  hipStream_t s) {
+    const int64_t nb = (int64_t)T * (D / 32);
+    if (nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(quant_mxfp4_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, h, nb, 0, (int64_t)0,
+                       codes, scales);
     return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -47,9 +47,12 @@ extern "C" {
 #define MOE_ERR_WORKSPACE (-4)   /* workspace missing or smaller than required   */
 #define MOE_ERR_HIP (-5)         /* a HIP launch failed                          */
 
-/* Expert formats (recipe "Overview": NVFP4 in layers 0-39, MXFP8 in 40-47). */
+/* Expert formats (recipe "Overview": NVFP4 in layers 0-39, MXFP8 in 40-47; MXFP4 is
+ * the OCP MXFP4 W4A4 variant for AMD Instinct in the vLLM recipe
+ * "thinkingmachines/Inkling-Small", section "Variants"). */
 #define MOE_FMT_NVFP4 1
 #define MOE_FMT_MXFP8 2
+#define MOE_FMT_MXFP4 3
 
 /*
  * Packed expert weights of one matrix kind for E experts, each logically [N][K]
@@ -64,8 +67,12 @@ extern "C" {
  *   MXFP8: codes  u8 [E][N/32][K/64][32][64] E4M3
  *          scales u8 [E][N/32][K/64][32][2]  E8M0 (2^(c - 127)), one per 32 columns
  *          tensor_scale unused (may be NULL)
- * Sizes are those of the row-major arrays ([E][N][K/2] / [E][N][K] codes, [E][N][K/16]
- * / [E][N][K/32] scales); only the order differs. The tiling lets one wave of the
+ *   MXFP4: codes  u8 [E][N/32][K/64][32][32] E2M1, element 2i in the low nibble of byte i
+ *          scales u8 [E][N/32][K/64][32][2]  E8M0, one per 32 columns
+ *          tensor_scale unused (may be NULL)
+ * Sizes are those of the row-major arrays ([E][N][K/2] (NVFP4, MXFP4) / [E][N][K]
+ * (MXFP8) codes, [E][N][K/16] (NVFP4) / [E][N][K/32] (MXFP8, MXFP4) scales); only the
+ * order differs. The tiling lets one wave of the
  * expert GEMMs load a 32-row weight subtile's codes for 64 columns as a single
  * contiguous 1 KiB (NVFP4) or 2 KiB (MXFP8) run.
  */
@@ -84,12 +91,12 @@ typedef struct moe_taps {
     int32_t *counts;       /* [n_loc] slots per local expert                        */
     int32_t *offsets;      /* [n_loc + 1] exclusive prefix sum of counts            */
     int32_t *sorted_slot;  /* [T*top_k] slot id t*top_k + j at each sorted position  */
-    uint8_t *a_codes;      /* hidden-state codes [T][D/2] (NVFP4) or [T][D] (MXFP8) */
-    uint8_t *a_scales;     /* [T][D/16] E4M3 (NVFP4) or [T][D/32] E8M0 (MXFP8)      */
+    uint8_t *a_codes;      /* hidden-state codes [T][D/2] (NVFP4, MXFP4) or [T][D]  */
+    uint8_t *a_scales;     /* [T][D/16] E4M3 (NVFP4) or [T][D/32] E8M0 (MX formats) */
     float *a_tscale;       /* [1] NVFP4 hidden-state tensor scale                   */
     float *inter;          /* [T*top_k][F] fp32 SwiGLU output before quantisation   */
-    uint8_t *inter_codes;  /* [T*top_k][F/2] or [T*top_k][F]                        */
-    uint8_t *inter_scales; /* [T*top_k][F/16] or [T*top_k][F/32]                    */
+    uint8_t *inter_codes;  /* [T*top_k][F/2] (NVFP4, MXFP4) or [T*top_k][F]         */
+    uint8_t *inter_scales; /* [T*top_k][F/16] (NVFP4) or [T*top_k][F/32]            */
     float *inter_tscale;   /* [1] NVFP4 intermediate tensor scale                   */
     float *y;              /* [T*top_k][D] fp32 down projection per slot (unweighted) */
 } moe_taps;
@@ -105,7 +112,7 @@ typedef struct moe_taps {
 
 /* Arguments of moe_forward. */
 typedef struct moe_forward_args {
-    int32_t fmt;              /* MOE_FMT_NVFP4 or MOE_FMT_MXFP8                         */
+    int32_t fmt;              /* MOE_FMT_NVFP4, MOE_FMT_MXFP8 or MOE_FMT_MXFP4          */
     int32_t T, D, F, E;       /* tokens, d_model, d_ff, routed experts                  */
     int32_t top_k;            /* experts per token (8)                                  */
     int32_t e_begin, e_end;   /* local expert range [e_begin, e_end) computed here      */
@@ -133,7 +140,8 @@ const char *moe_status_string(int32_t status);
  * s = amax/2688 (1 if the expert is all zero); per 16-block, r = amax_b / s, scale
  * candidates E4M3(r/6) and E4M3(r/4), codes E2M1(x / (E4M3 * s)), keep the candidate
  * with the smaller fp32 squared error (ties keep r/6). MXFP8: per 32-block, E8M0
- * exponent floor(log2 amax_b) - 8, codes E4M3(x * 2^-exponent). All roundings are
+ * exponent floor(log2 amax_b) - 8, codes E4M3(x * 2^-exponent). MXFP4: per 32-block,
+ * E8M0 exponent floor(log2 amax_b) - 2, codes E2M1(x * 2^-exponent). All roundings are
  * IEEE round-to-nearest-even with saturation to the format's largest finite value.
  * N must be a multiple of 32 and K of 64 (the tiled layout above).
  */
@@ -174,14 +182,16 @@ size_t moe_forward_workspace_bytes(const moe_forward_args *a);
  * MoE layer forward over the local experts [e_begin, e_end):
  *  1. slots (t, j) with topk_idx[t][j] local are grouped by expert, stable in t*top_k+j;
  *  2. hidden states are quantised once per token to the layer's format (NVFP4 with
- *     one tensor scale over all of h, MXFP8 per 32-block);
+ *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block);
  *  3. gate_up GEMM per expert (fp32 accumulation; NVFP4 sums are multiplied by
  *     fl32(s_h * s_gate_up[e])), then h = SwiGLU = g * u / (1 + exp(-g));
  *  4. h is quantised to the layer's format (NVFP4: one tensor scale over all S rows);
  *  5. down GEMM per expert (NVFP4: times fl32(s_inter * s_down[e])) -> y fp32;
  *  6. out[t] = sum over the token's local slots, j ascending, of topk_w[t][j] * y.
- * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), 1 <= top_k <= 8,
- * 0 <= e_begin < e_end <= E. gate_up/down must match fmt and shapes. T = 0 is a no-op.
+ * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), and for MXFP4 also D
+ * a multiple of 256 (its GEMMs run on the scaled FP4 MFMA in 256-row weight tiles),
+ * 1 <= top_k <= 8, 0 <= e_begin < e_end <= E. gate_up/down must match fmt and shapes.
+ * T = 0 is a no-op.
  */
 int32_t moe_forward(const moe_forward_args *a, void *stream);
 

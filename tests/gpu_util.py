@@ -49,6 +49,8 @@ def check_intermediate_codes(fmt: str, inter: np.ndarray, codes: np.ndarray, sca
     if fmt == "nvfp4":
         oc, os_, ots = oracle.quant_nvfp4(inter)
         assert np.float32(tscale) == ots, f"intermediate tensor scale {tscale} != {ots}"
+    elif fmt == "mxfp4":
+        oc, os_ = oracle.quant_mxfp4(inter)
     else:
         oc, os_ = oracle.quant_mxfp8(inter)
     bad_c = int(np.count_nonzero(oc != codes))
@@ -82,7 +84,7 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
     cb = gpu_inter_codes.reshape(S, -1) != oracle_inter_codes.reshape(S, -1)
     sb = gpu_inter_scales.reshape(S, -1) != oracle_inter_scales.reshape(S, -1)
     flipped_rows = np.nonzero(cb.any(1) | sb.any(1))[0]
-    flips = int(cb.sum())
+    flips = int(cb.sum())  # differing code bytes (one byte holds two E2M1 codes in the 4-bit formats)
     assert flips <= 1e-3 * S * F, f"{flips} intermediate code flips in {S * F} elements"
     bad_tokens = set((sorted_slot[flipped_rows] // k).tolist())
     keep = np.array([t for t in sel if t not in bad_tokens], dtype=np.int64)

@@ -29,7 +29,7 @@ def test_header_functions_are_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
     assert lib.moe_status_string(EWS) == b"workspace missing or too small"
 
 
@@ -54,11 +54,22 @@ def test_forward_validation_accepts_the_workloads():
     mx.gate_up = moe.MoePacked(2, 384, 5120, 4096, A16, A16, 0)
     mx.down = moe.MoePacked(2, 384, 4096, 2560, A16, A16, 0)
     assert _validate(mx) == OK
+    m4 = _args(fmt=3)
+    m4.gate_up = moe.MoePacked(3, 384, 5120, 4096, A16, A16, 0)
+    m4.down = moe.MoePacked(3, 384, 4096, 2560, A16, A16, 0)
+    assert _validate(m4) == OK
     assert _validate(_args(T=0, h=0, topk_idx=0, topk_w=0, out=0)) == OK  # empty batch
 
 
+def test_mxfp4_needs_256_wide_d_model():
+    m4 = _args(fmt=3, D=384)
+    m4.gate_up = moe.MoePacked(3, 384, 5120, 384, A16, A16, 0)
+    m4.down = moe.MoePacked(3, 384, 384, 2560, A16, A16, 0)
+    assert _validate(m4) == EUNSUP
+
+
 @pytest.mark.parametrize("over,status", [
-    (dict(fmt=3), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
+    (dict(fmt=4), EINVAL), (dict(fmt=0), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
     (dict(e_begin=10, e_end=10), EINVAL), (dict(e_end=385), EINVAL), (dict(e_begin=-1), EINVAL),
     (dict(E=5000), EINVAL), (dict(h=0), EINVAL), (dict(out=0), EINVAL),
     (dict(D=4000), EUNSUP), (dict(F=2500), EUNSUP),
@@ -122,7 +133,7 @@ def test_route_and_quantize_validate_on_the_host():
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
     bad = moe.MoePacked(1, 2, 32, 64, A16, A16, 0)     # NVFP4 needs the tensor-scale buffer
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
-    bad = moe.MoePacked(3, 2, 32, 64, A16, A16, A16)   # unknown format
+    bad = moe.MoePacked(4, 2, 32, 64, A16, A16, A16)   # unknown format
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
     bad = moe.MoePacked(2, 2, 32, 64, A16 + 8, A16, 0)  # misaligned codes
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EALIGN

@@ -43,7 +43,7 @@ def _adversarial_masters(E, N, K, seed):
     return w
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("shape", [(5, 256, 512), (2, 96, 2048)])
 def test_quantize_weights_bitexact(fmt, shape):
     E, N, K = shape
@@ -157,6 +157,14 @@ LAYER_CASES = [
     dict(name="stream-mxfp8-full-dims", wl=synth.custom("mxfp8", T=64, D=4096, F=2560, E=16, seed=35)),
     dict(name="stream-nvfp4-ep-share", wl=synth.custom("nvfp4", T=64, D=2048, F=1024, E=32, e_begin=4, e_end=12,
                                                        seed=36)),
+    # OCP MXFP4 (W4A4) on the scaled FP4 MFMA: decode and prefill batches, ragged tiles,
+    # several N blocks, an expert-parallel share, skewed routing and the full dimensions
+    dict(name="decode-mxfp4", wl=synth.custom("mxfp4", T=40, D=256, F=256, E=16, seed=51)),
+    dict(name="prefill-mxfp4", wl=synth.custom("mxfp4", T=300, D=256, F=256, E=16, seed=52)),
+    dict(name="prefill-mxfp4-k1024", wl=synth.custom("mxfp4", T=1024, D=1024, F=512, E=32, seed=53)),
+    dict(name="ep-share-mxfp4", wl=synth.custom("mxfp4", T=400, D=512, F=384, E=24, e_begin=6, e_end=15, seed=54)),
+    dict(name="skew-mxfp4", wl=synth.custom("mxfp4", T=600, D=256, F=128, E=16, skew=True, seed=55)),
+    dict(name="mxfp4-full-dims", wl=synth.custom("mxfp4", T=64, D=4096, F=2560, E=16, seed=56)),
 ]
 
 
@@ -245,6 +253,7 @@ def test_repeat_calls_are_deterministic():
 GRAPH_CASES = [
     dict(name="decode-nvfp4", wl=synth.custom("nvfp4", T=64, D=256, F=256, E=16, seed=41)),     # one-workgroup permute
     dict(name="prefill-mxfp8", wl=synth.custom("mxfp8", T=1100, D=256, F=256, E=16, seed=42)),  # count/scan/scatter + fill
+    dict(name="prefill-mxfp4", wl=synth.custom("mxfp4", T=700, D=256, F=256, E=16, seed=43)),
 ]
 
 
