@@ -5,7 +5,8 @@ weights, hidden-state amax) + moe_forward (permutation, hidden-state quantisatio
 gate_up GEMM with SwiGLU and intermediate quantisation, down GEMM, weighted
 combine), with all inputs and packed weights resident in HBM. The default workload
 is the NVFP4 decode step (64 tokens, d_model 4096, d_ff 2560, 384 experts, top-8);
---workload i selects one of the five seeded synthetic workloads.
+--workload i selects one of the seven seeded synthetic workloads (NVFP4, MXFP8 and the
+MXFP4 variant).
 
 Printed: one JSON line (rank 0). `roofline` covers the dominant kernel (the gate_up
 GEMM) timed live with HIP events recorded around its launch on the library's stream;
@@ -30,6 +31,9 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}  # dense, MI355X
+DTYPES = {"nvfp4": "f16 (exact NVFP4 values), fp32 accumulate",
+          "mxfp8": "bf16 (exact MXFP8 values), fp32 accumulate",
+          "mxfp4": "fp4 (MXFP4 codes and E8M0 scales on the scaled MFMA), fp32 accumulate"}
 METRIC = "MoE layer tokens/s; % peak HBM BW (decode), % scaled-MFMA peak (prefill)"
 
 
@@ -66,13 +70,16 @@ KERNEL_SOURCES = {
     "stream_gemm_kernel": ["gemm_stream.hip", "gemm_common.h", "layout.h", "formats.h"],
     "tile_gemm_kernel": ["gemm_tile.hip", "gemm_common.h", "layout.h", "formats.h"],
     "grouped_gemm_kernel": ["gemm.hip", "gemm_common.h", "layout.h", "formats.h"],
+    "mx4_gemm_kernel": ["gemm_mx4.hip", "gemm_common.h", "layout.h", "formats.h"],
 }
 
 
 def gate_up_kernel(wl) -> str:
     """The gate_up kernel moe_forward picks for this shape (same rule as its plan: 48+
     slots per expert on average -> MFMA tiles when both GEMMs fit them, else the
-    streaming kernel when K allows)."""
+    streaming kernel when K allows; MXFP4 always runs its scaled-FP4 MFMA kernel)."""
+    if wl.fmt == "mxfp4":
+        return "mx4_gemm_kernel"
     if wl.T * wl.k // wl.E >= 48 and wl.D % 512 == 0 and wl.F % 256 == 0:
         return "tile_gemm_kernel"
     if wl.D % 512 == 0 and wl.D // 512 <= 8:
@@ -108,6 +115,8 @@ def profiled_traffic(workload: str, kernel: str):
 def packed_bytes_per_expert(fmt: str, N: int, K: int) -> int:
     if fmt == "nvfp4":
         return N * K // 2 + N * K // 16 + 4
+    if fmt == "mxfp4":
+        return N * K // 2 + N * K // 32
     return N * K + N * K // 32
 
 
@@ -192,7 +201,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, help="index into the five synthetic workloads")
+    ap.add_argument("--workload", type=int, default=1, help="index into the seven synthetic workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "
@@ -231,6 +240,7 @@ def main():
     layer = moe.Layer(wl.fmt, T, D, F, E, gu, dn, top_k=k, e_begin=wl.e_begin, e_end=wl.local_end)
     out = torch.empty((T, D), dtype=torch.float32, device=dev)
     nv = wl.fmt == "nvfp4"
+    mx4 = wl.fmt == "mxfp4"
 
     route_ws = moe.route_workspace(T, D, E, dev)
 
@@ -293,14 +303,17 @@ def main():
     touched = int(len(np.unique(idx_h[local])))
     gu_b = packed_bytes_per_expert(wl.fmt, 2 * F, D)
     dn_b = packed_bytes_per_expert(wl.fmt, D, F)
-    act_b = lambda rows, cols: rows * (cols // 2 + cols // 16) if nv else rows * (cols + cols // 32)
+    code_b = {"nvfp4": lambda c: c // 2 + c // 16, "mxfp4": lambda c: c // 2 + c // 32,
+              "mxfp8": lambda c: c + c // 32}[wl.fmt]
+    act_b = lambda rows, cols: rows * code_b(cols)
     gate_up_bytes = touched * gu_b + act_b(T, D) + act_b(S, F)
     gate_up_flops = 4.0 * S * F * D
     layer_bytes = touched * (gu_b + dn_b) + E * D * 2 + T * D * 2 + T * D * 4
-    # the GEMMs run f16 (NVFP4) / bf16 (MXFP8) MFMAs on exactly expanded values, so that
-    # is the contraction's peak; the format's own scaled-MFMA peak is reported beside it
-    mfma_peak = MFMA_PEAK_TFLOPS["f16" if nv else "bf16"]
-    format_peak = MFMA_PEAK_TFLOPS["fp4" if nv else "fp8"]
+    # the NVFP4 / MXFP8 GEMMs run f16 / bf16 MFMAs on exactly expanded values, so that is
+    # the contraction's peak, with the format's own scaled-MFMA peak reported beside it;
+    # the MXFP4 GEMMs run the scaled FP4 MFMA itself
+    mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else "bf16")]
+    format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else "fp8"]
     decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge
     if decode:
         achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9
@@ -341,7 +354,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f16 (exact NVFP4 values), fp32 accumulate" if nv else "bf16 (exact MXFP8 values), fp32 accumulate",
+        "vs_baseline": None, "dtype": DTYPES[wl.fmt],
         "data": "synthetic",
         "config": {"workload": wl.name, "launch": launch, "tokens": T, "d_model": D, "d_ff": F, "experts": E, "top_k": k,
                    "format": wl.fmt, "local_experts": [wl.e_begin, wl.local_end], "experts_touched": touched,

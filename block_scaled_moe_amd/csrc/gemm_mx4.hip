@@ -14,9 +14,12 @@
 //
 //  - workgroup tile 64 sorted rows x 256 weight rows, 4 waves side by side in N, each
 //    64 x 64 as 2 x 2 MFMA tiles; gate_up waves pair gate row f with up row F + f;
-//  - every lane loads its A and B operands straight from global memory (the four waves
-//    of a workgroup read the same activation rows, which the L1 serves), through a
-//    register ring kMx4Ring chunks deep; no LDS and no barrier in the K loop;
+//  - the activation tile (shared by the four waves) goes through double-buffered LDS four
+//    chunks at a time, loaded as whole 128-byte pieces of the gathered token rows (a
+//    per-lane operand gather would touch 32 cache lines per load and bound the loop);
+//    each lane loads its weight operands straight from global memory into a four-chunk
+//    register ring (a 32 x 64 weight block is 1 KiB contiguous); one barrier per four
+//    chunks;
 //  - work items are grouped and dealt to the 8 XCDs as in the tile kernels;
 //  - gate_up epilogue: SwiGLU in fp32, then each wave's 64 x 32 tile goes through LDS and
 //    lane r quantises row r's 32-block to MXFP4 (16-byte code store, one scale byte).
@@ -36,11 +39,16 @@ using namespace gemm_detail;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
+constexpr int kBM = 64, kMS = 2, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
+constexpr int kGrp = 4;                        // K chunks per A tile group
 #ifndef MOE_MX4_RING
 #define MOE_MX4_RING 4
 #endif
-constexpr int kBM = 64, kMS = 2, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
-constexpr int kMx4Ring = MOE_MX4_RING;
+constexpr int kRing = MOE_MX4_RING;            // B operand ring depth in chunks
+static_assert(kRing % kGrp == 0, "the B ring turns over whole A groups");
+constexpr int kARow = 144;                     // LDS bytes per A row: 128 of codes + 16 (bank spread)
+constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [64 rows][8]
+constexpr int kABuf = kACodes + kBM * 8;
 constexpr int kEpiStride = 33;  // floats per row of a wave's SwiGLU tile (bank spread)
 constexpr int kCodeBlock = 32 * 32, kScaleBlock = 32 * 2;  // bytes per 32 x 64 weight block
 
@@ -50,7 +58,8 @@ __device__ __forceinline__ v8i fp4_operand(u32x4 c) {
 
 template <bool GATE_UP>
 __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p) {
-    __shared__ __attribute__((aligned(16))) float epi[GATE_UP ? 4 * kBM * kEpiStride : 4];
+    constexpr int kLds = (GATE_UP && 4 * kBM * kEpiStride * 4 > 2 * kABuf) ? 4 * kBM * kEpiStride * 4 : 2 * kABuf;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];  // A tiles; then the SwiGLU tiles
 
     const int K = p.K, N = p.N, F = N / 2;
     const int NB = GATE_UP ? F / (kBN / 2) : N / kBN;
@@ -94,28 +103,46 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
         bc[ns] = wc_e + blk0 * kCodeBlock + (row & 31) * 32 + 16 * g2;
         bs[ns] = ws_e + blk0 * kScaleBlock + (row & 31) * 2 + g2;
     }
-    // rows past the tile's end read the tile's first row (in bounds; never stored)
-    const uint8_t *ac[kMS];
-    const uint8_t *as[kMS];
-#pragma unroll
-    for (int ms = 0; ms < kMS; ++ms) {
-        const int r = 32 * ms + l32;
+    // ---- A tile (activations) through LDS, 4 chunks (256 k, 128 bytes of codes and 8
+    // scale bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces
+    // i = t and t + 256 (row i / 8, piece i % 8: a wave covers 8 whole 128-byte rows, so
+    // the gathered token rows are read line by line) and the two scale bytes of row t / 4,
+    // chunk t % 4. Rows past the tile's end read the tile's first row (in bounds; never
+    // stored); pieces and chunks past the end of K reread the group's first (unused).
+    const int n_chunks = K / 64;
+    const int n_groups = (n_chunks + kGrp - 1) / kGrp, n_fg = n_chunks / kGrp;
+    auto a_row = [&](int r) -> int64_t {
         const int pos = p0 + (r < rows ? r : 0);
-        const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
-        ac[ms] = p.a_codes + arow * (K / 2) + 16 * g2;
-        as[ms] = p.a_scales + arow * (K / 32) + g2;
-    }
-
-    // ---- K loop: chunk c + kMx4Ring - 1 is loaded into ring slot (c - 1) % kMx4Ring while
-    // chunk c is multiplied; loads past the end repeat the last chunk (in bounds, unused)
-    u32x4 areg[kMx4Ring][kMS], breg[kMx4Ring][kNS];
-    int asc[kMx4Ring][kMS], bsc[kMx4Ring][kNS];
-    auto load = [&](int slot, int c) {
+        return p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
+    };
+    const int piece = threadIdx.x & 7, s_chunk = threadIdx.x & 3;
+    const uint8_t *ap[2];
 #pragma unroll
-        for (int ms = 0; ms < kMS; ++ms) {
-            areg[slot][ms] = *reinterpret_cast<const u32x4 *>(ac[ms] + 32 * (int64_t)c);
-            asc[slot][ms] = as[ms][2 * c];
-        }
+    for (int q = 0; q < 2; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * (K / 2);
+    const uint8_t *sp = p.a_scales + a_row(threadIdx.x >> 2) * (K / 32);
+    u32x4 a_pf[2];
+    uint32_t s_pf;
+    auto a_load = [&](int g) {
+        g = min(g, n_groups - 1);
+        const int off = 128 * g + 16 * piece;
+        const int off_ok = off < K / 2 ? off : 128 * g;
+#pragma unroll
+        for (int q = 0; q < 2; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
+        s_pf = *reinterpret_cast<const uint16_t *>(sp + 2 * min(kGrp * g + s_chunk, n_chunks - 1));
+    };
+    auto a_store = [&](int buf) {
+        uint8_t *ab = lds + buf * kABuf;
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
+        *reinterpret_cast<uint16_t *>(ab + kACodes + (threadIdx.x >> 2) * 8 + 2 * s_chunk) = (uint16_t)s_pf;
+    };
+
+    // ---- B operand ring: chunk c + kRing - 1 is loaded into slot (c - 1) % kRing while chunk
+    // c is multiplied; loads past the end repeat the last chunk (in bounds, unused)
+    u32x4 breg[kRing][kNS];
+    int bsc[kRing][kNS];
+    auto b_load = [&](int slot, int c) {
 #pragma unroll
         for (int ns = 0; ns < kNS; ++ns) {
             breg[slot][ns] = *reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c);
@@ -127,28 +154,81 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
     for (int i = 0; i < kMS; ++i)
 #pragma unroll
         for (int j = 0; j < kNS; ++j) acc[i][j] = (float16_t){};
-    const int n_chunks = K / 64;
+    uint32_t a_sc[kMS][2];
+    auto a_scales = [&](int buf) {
+        const uint8_t *ab = lds + buf * kABuf + kACodes;
 #pragma unroll
-    for (int r = 0; r < kMx4Ring - 1; ++r) load(r, min(r, n_chunks - 1));
-    for (int c0 = 0; c0 < n_chunks; c0 += kMx4Ring) {
-#pragma unroll
-        for (int j = 0; j < kMx4Ring; ++j) {
-            const int c = c0 + j;
-            if (c >= n_chunks) break;
-            load((j + kMx4Ring - 1) % kMx4Ring, min(c + kMx4Ring - 1, n_chunks - 1));
-#pragma unroll
-            for (int ms = 0; ms < kMS; ++ms)
-#pragma unroll
-                for (int ns = 0; ns < kNS; ++ns)
-                    acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fp4_operand(areg[j][ms]), fp4_operand(breg[j][ns]), acc[ms][ns], 4, 4, 0, asc[j][ms], 0,
-                        bsc[j][ns]);
+        for (int ms = 0; ms < kMS; ++ms) {
+            const uint2 v = *reinterpret_cast<const uint2 *>(ab + (32 * ms + l32) * 8);
+            a_sc[ms][0] = v.x >> (8 * g2);
+            a_sc[ms][1] = v.y >> (8 * g2);
         }
+    };
+    // chunk j of the group in LDS buffer buf times the B operands in ring slot `slot`
+    auto mma = [&](int buf, int j, int slot) {
+        const uint8_t *ab = lds + buf * kABuf;
+        u32x4 af[kMS];
+#pragma unroll
+        for (int ms = 0; ms < kMS; ++ms)
+            af[ms] = *reinterpret_cast<const u32x4 *>(ab + (32 * ms + l32) * kARow + 32 * j + 16 * g2);
+#pragma unroll
+        for (int ms = 0; ms < kMS; ++ms) {
+            const int sa = (int)((a_sc[ms][j >> 1] >> (16 * (j & 1))) & 0xffu);
+#pragma unroll
+            for (int ns = 0; ns < kNS; ++ns)
+                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fp4_operand(af[ms]), fp4_operand(breg[slot][ns]), acc[ms][ns], 4, 4, 0, sa, 0, bsc[slot][ns]);
+        }
+    };
+    // after the last chunk of group g: group g + 1 into the other buffer (last read in group
+    // g - 1, before the previous barrier), group g + 2 into registers
+    auto next_group = [&](int g) {
+        a_store((g & 1) ^ 1);
+        a_load(g + 2);
+        __syncthreads();
+    };
+
+    a_load(0);
+    a_store(0);
+    a_load(1);
+#pragma unroll
+    for (int r = 0; r < kRing - 1; ++r) b_load(r, min(r, n_chunks - 1));
+    __syncthreads();
+    // whole ring turns without a branch inside (a conditional use would let the compiler
+    // sink the prefetches into it), then the last n_chunks % kRing chunks, already loaded
+    const int n_full = n_chunks - n_chunks % kRing;
+    for (int c0 = 0; c0 < n_full; c0 += kRing) {
+#pragma unroll
+        for (int gi = 0; gi < kRing / kGrp; ++gi) {
+            const int g = c0 / kGrp + gi;
+            a_scales(g & 1);
+#pragma unroll
+            for (int j = 0; j < kGrp; ++j) {
+                // keep each chunk's prefetch in place: left alone, the scheduler gathers
+                // the ring's loads at the end of the group and waits for them all at once
+                __builtin_amdgcn_sched_barrier(0);
+                const int slot = gi * kGrp + j;
+                b_load((slot + kRing - 1) % kRing, min(c0 + slot + kRing - 1, n_chunks - 1));
+                mma(g & 1, j, slot);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            next_group(g);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < kRing - 1; ++t) {
+        const int c = n_full + t;
+        if (c >= n_chunks) break;
+        const int g = c / kGrp;
+        if (t % kGrp == 0) a_scales(g & 1);
+        mma(g & 1, t % kGrp, t);
+        if (t % kGrp == kGrp - 1 && c + 1 < n_chunks) next_group(g);
     }
 
     // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
     if (GATE_UP) {
-        float *we = epi + wave * kBM * kEpiStride;
+        __syncthreads();  // the SwiGLU tiles reuse the A tiles' LDS
+        float *we = reinterpret_cast<float *>(lds) + wave * kBM * kEpiStride;
 #pragma unroll
         for (int ms = 0; ms < kMS; ++ms)
 #pragma unroll

@@ -230,6 +230,10 @@ WORKLOADS = [
     Workload(3, "prefill-nvfp4-ep4", "nvfp4", T=8192, D=4096, F=2560, E=384,
              e_begin=0, e_end=96, seed=3),
     Workload(4, "skewed-mxfp8", "mxfp8", T=16384, D=4096, F=2560, E=384, skew=True, seed=4),
+    # the OCP MXFP4 (W4A4) variant at the decode and expert-parallel prefill shapes
+    Workload(5, "decode-mxfp4", "mxfp4", T=64, D=4096, F=2560, E=384, seed=5),
+    Workload(6, "prefill-mxfp4-ep4", "mxfp4", T=8192, D=4096, F=2560, E=384,
+             e_begin=0, e_end=96, seed=6),
 ]
 
 

@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the four benchmarked workloads, through the same calls
+"""GPU parity at the full sizes of the six benchmarked workloads, through the same calls
 and launch configuration that bench.py times (moe.route + moe.Layer.forward).
 
 Whole-batch, bit-exact: top-k indices of every token, max |h|, the permutation, every
@@ -25,6 +25,10 @@ pytestmark = pytest.mark.gpu
 ROWS_PER_EXPERT = 16
 
 
+def _dequant_mx(fmt, codes, scales):
+    return oracle.dequant_mxfp4(codes, scales) if fmt == "mxfp4" else oracle.dequant_mxfp8(codes, scales)
+
+
 def _expert_reference(wl, e, a_rows, a_ts, inter_codes, inter_scales, inter_ts):
     """fp64 gate_up -> SwiGLU (rounded to fp32) of the given dequantised hidden rows, and
     the down projection of the given intermediate codes, for expert e (oracle weights)."""
@@ -39,9 +43,9 @@ def _expert_reference(wl, e, a_rows, a_ts, inter_codes, inter_scales, inter_ts):
         s_dn = np.float32(np.float32(inter_ts) * dn["tensor_scale"][0])
         ai = oracle.dequant_nvfp4(inter_codes, inter_scales, 1.0, with_tensor=False)
     else:
-        wg = oracle.dequant_mxfp8(gu["codes"][0], gu["scales"][0])
-        wd = oracle.dequant_mxfp8(dn["codes"][0], dn["scales"][0])
-        ai = oracle.dequant_mxfp8(inter_codes, inter_scales)
+        wg = _dequant_mx(wl.fmt, gu["codes"][0], gu["scales"][0])
+        wd = _dequant_mx(wl.fmt, dn["codes"][0], dn["scales"][0])
+        ai = _dequant_mx(wl.fmt, inter_codes, inter_scales)
     acc = a_rows @ wg.T                       # exact products, fp64 sums
     g = acc.astype(np.float32)
     if nv:
@@ -55,7 +59,7 @@ def _expert_reference(wl, e, a_rows, a_ts, inter_codes, inter_scales, inter_ts):
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("i", [1, 2, 3, 4], ids=lambda i: synth.WORKLOADS[i].name)
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6], ids=lambda i: synth.WORKLOADS[i].name)
 def test_fullsize_workload(i):
     wl = synth.WORKLOADS[i]
     T, D, F, E, k = wl.T, wl.D, wl.F, wl.E, wl.k
@@ -96,7 +100,7 @@ def test_fullsize_workload(i):
         a_c, a_s, a_ts = oracle.quant_nvfp4(hf)
         assert np.float32(tp["a_tscale"][0]) == a_ts
     else:
-        a_c, a_s = oracle.quant_mxfp8(hf)
+        a_c, a_s = oracle.quant_mxfp4(hf) if wl.fmt == "mxfp4" else oracle.quant_mxfp8(hf)
         a_ts = None
     assert np.array_equal(tp["a_codes"], a_c) and np.array_equal(tp["a_scales"], a_s), "hidden codes differ"
 
@@ -113,7 +117,7 @@ def test_fullsize_workload(i):
         rows = np.unique(np.linspace(p0, p1 - 1, min(ROWS_PER_EXPERT, p1 - p0)).round().astype(np.int64))
         tok = ss[rows] // k
         a_rows = (oracle.dequant_nvfp4(a_c[tok], a_s[tok], 1.0, with_tensor=False) if nv
-                  else oracle.dequant_mxfp8(a_c[tok], a_s[tok]))
+                  else _dequant_mx(wl.fmt, a_c[tok], a_s[tok]))
         o_gu, o_dn, inter_ref, y_ref = _expert_reference(wl, e, a_rows, a_ts, tp["inter_codes"][rows],
                                                          tp["inter_scales"][rows], i_ts)
         # packed weights of this expert, bit-exact after undoing the tiling
