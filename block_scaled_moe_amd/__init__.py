@@ -103,8 +103,9 @@ def _check(rc: int, what: str):
 @dataclasses.dataclass
 class PackedWeights:
     """Device tensors of one packed matrix kind for E experts (logically [E][N][K]) in the
-    tiled layout of include/moe.h: codes [E][N/32][K/64][32][32 | 64 | 32] and scales
-    [E][N/32][K/64][32][4 | 2 | 2] (NVFP4 | MXFP8 | MXFP4)."""
+    tiled layout of include/moe.h: codes [E][N/32][K/64][32][32 | 64] and scales
+    [E][N/32][K/64][32][4 | 2] (NVFP4 | MXFP8); MXFP4 keeps the two 32-column halves of
+    a block apart, codes [E][N/32][K/64][2][32][16] and scales [E][N/32][K/64][2][32][1]."""
     fmt: str
     E: int
     N: int
@@ -120,9 +121,13 @@ class PackedWeights:
         nv = fmt == "nvfp4"
         if N % 32 or K % 64:
             raise ValueError(f"packed weights need N % 32 == 0 and K % 64 == 0 (got N={N}, K={K})")
-        codes = torch.empty((E, N // 32, K // 64, 32, 64 if fmt == "mxfp8" else 32), dtype=torch.uint8,
-                            device=device)
-        scales = torch.empty((E, N // 32, K // 64, 32, 4 if nv else 2), dtype=torch.uint8, device=device)
+        if fmt == "mxfp4":
+            codes = torch.empty((E, N // 32, K // 64, 2, 32, 16), dtype=torch.uint8, device=device)
+            scales = torch.empty((E, N // 32, K // 64, 2, 32, 1), dtype=torch.uint8, device=device)
+        else:
+            codes = torch.empty((E, N // 32, K // 64, 32, 64 if fmt == "mxfp8" else 32), dtype=torch.uint8,
+                                device=device)
+            scales = torch.empty((E, N // 32, K // 64, 32, 4 if nv else 2), dtype=torch.uint8, device=device)
         ts = torch.empty(E, dtype=torch.float32, device=device) if nv else None
         return PackedWeights(fmt, E, N, K, codes, scales, ts)
 

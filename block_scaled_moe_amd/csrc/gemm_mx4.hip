@@ -6,8 +6,11 @@
 // The instruction takes the codes and E8M0 scales as they are stored: no expansion, no
 // tensor scale. Lane l supplies row l % 32 of its operand over k = 32 (l / 32) .. +31 of
 // the 64-wide K chunk, as 16 code bytes (element 2i in the low nibble) and the scale
-// byte of that 32-block, which is exactly one half of a row's 32-byte slot in the packed
-// weight layout (layout.h) and 16 contiguous bytes of a row-major activation row. Its
+// byte of that 32-block: in the packed MXFP4 weight layout (layout.h, halves of a 32 x 64
+// block apart) lane l's piece of a block is the l-th 16 bytes and its scale the l-th
+// byte, so a wave reads one contiguous 1 KiB and 64 bytes (the interleaved order of the
+// other formats makes every quarter-wave touch four half-used lines, and the address
+// units bound the loop); an activation's block is 16 contiguous bytes of its row. Its
 // products are exact and its fp32 accumulation measured no less accurate than a
 // sequential fp32 sum (max error 1.6e-7 of the sum of |products| over K = 4096 with
 // block exponents spread over +-12, 2.3e-8 at +-4, 0 with equal exponents).
@@ -100,8 +103,8 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
             row = nb * kBN + wave * 64 + 32 * ns + l32;
         }
         const int64_t blk0 = (int64_t)(row >> 5) * kb;
-        bc[ns] = wc_e + blk0 * kCodeBlock + (row & 31) * 32 + 16 * g2;
-        bs[ns] = ws_e + blk0 * kScaleBlock + (row & 31) * 2 + g2;
+        bc[ns] = wc_e + blk0 * kCodeBlock + g2 * 512 + (row & 31) * 16;  // = base + 16 * lane
+        bs[ns] = ws_e + blk0 * kScaleBlock + g2 * 32 + (row & 31);       // = base + lane
     }
     // ---- A tile (activations) through LDS, 4 chunks (256 k, 128 bytes of codes and 8
     // scale bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces

@@ -12,9 +12,14 @@
 // codes for one 64-column chunk are a single contiguous run instead of 32 strided
 // pieces, and its scales for the chunk one 128- or 64-byte run.
 //
-// In storage order, quantisation block r of an expert (16 values NVFP4, 32 MXFP8) has
-// its codes at byte 8r / 32r and its scale at byte r; its source row and column follow
-// from r below.
+// MXFP4 keeps the two 32-column halves of a block apart: codes [2][32 rows][16 bytes],
+// scales [2][32 rows]. The scaled FP4 MFMA takes one half-row (a whole 32-block with its
+// scale) per lane, so lane l of a wave loads half l / 32 of row l % 32 and a wave's 64
+// lanes read one contiguous 1 KiB of codes and 64 bytes of scales.
+//
+// In storage order, quantisation block r of an expert (16 values NVFP4, 32 MXFP8 and
+// MXFP4) has its codes at byte 8r / 32r / 16r and its scale at byte r; its source row
+// and column follow from r below.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,6 +56,14 @@ __host__ __device__ inline void block_source(bool nv, int64_t K, int64_t r, int6
     const int64_t kb = K >> 6;
     n = 32 * (blk / kb) + row;
     k = 64 * (blk % kb) + (nv ? 16 : 32) * piece;
+}
+
+// MXFP4: source row and first column of quantisation block r (storage order)
+__host__ __device__ inline void block_source_mx4(int64_t K, int64_t r, int64_t &n, int64_t &k) {
+    const int64_t row = r & 31, half = (r >> 5) & 1, blk = r >> 6;
+    const int64_t kb = K >> 6;
+    n = 32 * (blk / kb) + row;
+    k = 64 * (blk % kb) + 32 * half;
 }
 
 }  // namespace layout

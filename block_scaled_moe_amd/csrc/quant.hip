@@ -139,9 +139,9 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp8_bf16_kernel(const uint16
 
 // MXFP4: one thread per 32-block. Hidden states (tile_K == 0): block b of a row-major
 // [rows][K] bf16 tensor, codes [rows][K/2] row-major too. Weights (tile_K == K):
-// storage block b of the packed tile layout (layout.h: 16 code bytes per 32-block,
-// two blocks per row of a 32 x 64 tile, as NVFP4's codes and MXFP8's scales), read
-// from its source row and columns of [E][N][K] masters.
+// storage block b of the packed MXFP4 tile layout (layout.h: 16 code bytes and one
+// scale byte per 32-block, the two 32-column halves of a 32 x 64 tile apart), read from
+// its source row and columns of [E][N][K] masters.
 __global__ void __launch_bounds__(kThreads) quant_mxfp4_bf16_kernel(const uint16_t *__restrict__ x, int64_t n_blocks,
                                                                     int32_t tile_K, int64_t blocks_per_expert,
                                                                     uint8_t *__restrict__ codes,
@@ -151,7 +151,7 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp4_bf16_kernel(const uint16
         if (tile_K) {
             const int64_t e = b / blocks_per_expert;
             int64_t n, k;
-            layout::block_source(false, tile_K, b - e * blocks_per_expert, n, k);
+            layout::block_source_mx4(tile_K, b - e * blocks_per_expert, n, k);
             src_off = (e * (blocks_per_expert / (tile_K / 32)) + n) * tile_K + k;
         }
         const uint4 *src = reinterpret_cast<const uint4 *>(x + src_off);

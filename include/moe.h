@@ -67,14 +67,16 @@ extern "C" {
  *   MXFP8: codes  u8 [E][N/32][K/64][32][64] E4M3
  *          scales u8 [E][N/32][K/64][32][2]  E8M0 (2^(c - 127)), one per 32 columns
  *          tensor_scale unused (may be NULL)
- *   MXFP4: codes  u8 [E][N/32][K/64][32][32] E2M1, element 2i in the low nibble of byte i
- *          scales u8 [E][N/32][K/64][32][2]  E8M0, one per 32 columns
+ *   MXFP4: codes  u8 [E][N/32][K/64][2][32][16] E2M1, element 2i in the low nibble of
+ *          byte i: the block's 32 rows for columns 0-31, then for columns 32-63
+ *          scales u8 [E][N/32][K/64][2][32]  E8M0, one per 32 columns, same order
  *          tensor_scale unused (may be NULL)
  * Sizes are those of the row-major arrays ([E][N][K/2] (NVFP4, MXFP4) / [E][N][K]
  * (MXFP8) codes, [E][N][K/16] (NVFP4) / [E][N][K/32] (MXFP8, MXFP4) scales); only the
  * order differs. The tiling lets one wave of the
  * expert GEMMs load a 32-row weight subtile's codes for 64 columns as a single
- * contiguous 1 KiB (NVFP4) or 2 KiB (MXFP8) run.
+ * contiguous 1 KiB (NVFP4) or 2 KiB (MXFP8) run; MXFP4's half-split order gives the
+ * scaled FP4 MFMA's 64 lanes (32 rows x two 32-column halves) one contiguous 1 KiB.
  */
 typedef struct moe_packed {
     int32_t fmt;

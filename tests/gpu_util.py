@@ -22,8 +22,12 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 
 def untile(a: np.ndarray) -> np.ndarray:
-    """Packed weight bytes [E][N/32][K/64][32][b] (tiled layout of include/moe.h) ->
-    the row-major [E][N][K/64 * b] arrays the oracle produces (a pure reordering)."""
+    """Packed weight bytes [E][N/32][K/64][32][b] (tiled layout of include/moe.h), or
+    [E][N/32][K/64][2][32][b] (MXFP4: the two 32-column halves apart) -> the row-major
+    [E][N][K/64 * 2b or b] arrays the oracle produces (a pure reordering)."""
+    if a.ndim == 6:
+        E, nb, kb, h, r, b = a.shape
+        return np.ascontiguousarray(a.transpose(0, 1, 4, 2, 3, 5)).reshape(E, nb * r, kb * h * b)
     E, nb, kb, r, b = a.shape
     return np.ascontiguousarray(a.transpose(0, 1, 3, 2, 4)).reshape(E, nb * r, kb * b)
 
