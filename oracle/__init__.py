@@ -1,4 +1,5 @@
-"""CPU oracle of the routed-expert MoE layer (NVFP4 / MXFP8 / MXFP4 experts).
+"""CPU oracle of the routed-expert MoE layer (NVFP4 / MXFP8 / MXFP4 experts, and NVFP4
+weights with bf16 activations, "w4a16").
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and
 by bench.py's cpu_baseline leg, never by the library. It wraps oracle.c (plain
@@ -21,8 +22,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4 = 0, 1, 2, 3
-_FMT = {"none": 0, "bf16": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3}
+FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4, FMT_W4A16 = 0, 1, 2, 3, 4
+_FMT = {"none": 0, "bf16": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4}
 
 
 def build() -> str:
@@ -87,6 +88,8 @@ def _load():
     lib.orc_dequant_nvfp4.restype = ctypes.c_int
     lib.orc_dequant_mxfp8.argtypes = [p, p, i64, i64, p]
     lib.orc_dequant_mxfp8.restype = ctypes.c_int
+    lib.orc_round_bf16.argtypes = [p, i64, p]
+    lib.orc_round_bf16.restype = ctypes.c_int
     lib.orc_quantize_weights.argtypes = [ctypes.c_int, i32, i32, i32, p, p, p, p]
     lib.orc_quantize_weights.restype = ctypes.c_int
     lib.orc_route.argtypes = [i32, i32, i32, i32, p, p, p, p, p, p]
@@ -211,9 +214,20 @@ def dequant_mxfp8(codes, scales) -> np.ndarray:
     return out
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), nearest with ties to even."""
+    x = np.ascontiguousarray(x, np.float32)
+    out = np.empty(x.shape, np.uint16)
+    _check(_load().orc_round_bf16(_ptr(x), x.size, _ptr(out)), "round_bf16")
+    return out
+
+
 def quantize_weights(fmt: str, w_bf16: np.ndarray):
-    """Quantise bf16 masters [E, N, K] per expert -> dict(codes, scales, tensor_scale|None)."""
+    """Quantise bf16 masters [E, N, K] per expert -> dict(codes, scales, tensor_scale|None).
+    W4A16 weights are NVFP4 weights."""
     f = _FMT[fmt]
+    if f == FMT_W4A16:
+        f = FMT_NVFP4
     w = np.ascontiguousarray(w_bf16, np.uint16)
     E, N, K = w.shape
     if f == FMT_NVFP4:
@@ -302,7 +316,12 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
     if taps:
         _, offs, _ = permute(idx, e_begin, e_end)
         S = int(offs[-1])
-        if f != FMT_NONE:
+        if f == FMT_W4A16:
+            # no activation codes; the intermediate is bf16 bit patterns [S][F]
+            tp["inter"] = np.zeros((S, F), np.float32)
+            tp["inter_codes"] = np.zeros((S, F), np.uint16)
+            a.inter, a.inter_codes = _ptr(tp["inter"]), _ptr(tp["inter_codes"])
+        elif f != FMT_NONE:
             tp["a_codes"] = np.zeros((T, D if f == FMT_MXFP8 else D // 2), np.uint8)
             tp["a_scales"] = np.zeros((T, D // 16 if f == FMT_NVFP4 else D // 32), np.uint8)
             tp["a_tscale"] = np.zeros(1, np.float32)
@@ -327,14 +346,15 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
 def down_combine(fmt: str, idx, w, inter_codes, inter_scales, inter_tscale, down, *, D: int, F: int, E: int,
                  e_begin: int = 0, e_end: int | None = None):
     """Down projection and combine alone (the forward's last two steps) from given
-    intermediate codes of the S local slots in sorted order -> out float32 [T, D]."""
+    intermediate codes of the S local slots in sorted order -> out float32 [T, D].
+    W4A16: inter_codes are bf16 bit patterns [S][F] and inter_scales is None."""
     f = _FMT[fmt]
     idx = np.ascontiguousarray(idx, np.int32)
     w = np.ascontiguousarray(w, np.float32)
     T, k = idx.shape
     e_end = E if e_end is None else e_end
-    ic = np.ascontiguousarray(inter_codes, np.uint8)
-    is_ = np.ascontiguousarray(inter_scales, np.uint8)
+    ic = np.ascontiguousarray(inter_codes, np.uint16 if f == FMT_W4A16 else np.uint8)
+    is_ = None if inter_scales is None else np.ascontiguousarray(inter_scales, np.uint8)
     c = np.ascontiguousarray(down["codes"], np.uint8)
     sc = np.ascontiguousarray(down["scales"], np.uint8)
     ts = None if down.get("tensor_scale") is None else np.ascontiguousarray(down["tensor_scale"], np.float32)

@@ -17,7 +17,9 @@
  *      quantised to match the layer's weight format).
  *  [V] vLLM recipe "thinkingmachines/Inkling-Small", section "Variants" and the
  *      recipe's variant list: an OCP MXFP4 checkpoint for AMD Instinct, run on
- *      MI355X as native W4A4 MXFP4 MoE (the MXFP4 format below).
+ *      MI355X as native W4A4 MXFP4 MoE (the MXFP4 format below); and on Hopper the
+ *      NVFP4 checkpoint run as W4A16, its weights dequantised to bf16 on the fly
+ *      (format 4 below: activations stay bf16, the SwiGLU output is rounded to bf16).
  * The pages fix neither the gate, the expert MLP, the element/scale formats'
  * bit layouts nor the arithmetic order. The readings taken here (softmax then
  * top-8 with lower-index tie-break; SwiGLU experts; E2M1 codes with an E4M3
@@ -238,6 +240,17 @@ static inline float bf16_value(uint16_t u) {
     return f;
 }
 
+/* fp32 -> bf16 bit pattern, round to nearest, ties to even: the 16 dropped bits are
+ * compared with half an ulp of the kept part (inputs here are finite). */
+static uint16_t bf16_rne(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    const uint32_t kept = u >> 16, dropped = u & 0xffffu;
+    uint32_t r = kept;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) r = kept + 1u;
+    return (uint16_t)r;
+}
+
 /* ------------------------------------------------------------------------- */
 /* MXFP8 quantiser: E4M3 elements, E8M0 scale per 32 ([R] "Overview").        */
 /* ------------------------------------------------------------------------- */
@@ -333,6 +346,13 @@ int orc_dequant_mxfp4(const uint8_t *codes, const uint8_t *scales, int64_t rows,
 /* ------------------------------------------------------------------------- */
 /* Weight quantisation over E experts (one tensor per expert per matrix).     */
 /* ------------------------------------------------------------------------- */
+
+/* fp32 [n] -> bf16 bit patterns [n], nearest, ties to even. */
+int orc_round_bf16(const float *x, int64_t n, uint16_t *out) {
+    if (n < 0 || (n && (!x || !out))) return ORC_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_rne(x[i]);
+    return ORC_OK;
+}
 
 /* fmt 1 = NVFP4, 2 = MXFP8, 3 = MXFP4. w: bf16 [E][N][K]. tensor_scale: fp32 [E] (NVFP4). */
 int orc_quantize_weights(int fmt, int32_t E, int32_t N, int32_t K, const uint16_t *w, uint8_t *codes,
@@ -456,7 +476,8 @@ int64_t orc_permute(int32_t T, int32_t k, const int32_t *idx, int32_t e_begin, i
 /* ------------------------------------------------------------------------- */
 
 typedef struct {
-    int32_t fmt; /* 0 = unquantised bf16 masters (all fp64), 1 = NVFP4 W4A4, 2 = MXFP8 W8A8 */
+    int32_t fmt; /* 0 = unquantised bf16 masters (all fp64), 1 = NVFP4 W4A4, 2 = MXFP8 W8A8,
+                    3 = MXFP4 W4A4, 4 = NVFP4 weights with bf16 activations (W4A16) */
     int32_t T, D, F, E, k, e_begin, e_end;
     const uint16_t *h;  /* bf16 [T][D] */
     const int32_t *idx; /* [T][k] */
@@ -464,7 +485,7 @@ typedef struct {
     /* fmt 0 */
     const uint16_t *gu_master; /* bf16 [E][2F][D]; rows [0,F) gate, [F,2F) up */
     const uint16_t *dn_master; /* bf16 [E][D][F] */
-    /* fmt 1/2: canonical packed layout (see orc_quantize_weights) */
+    /* fmt 1-4: canonical packed layout (see orc_quantize_weights; fmt 4 uses NVFP4's) */
     const uint8_t *gu_codes, *gu_scales;
     const float *gu_tscale;
     const uint8_t *dn_codes, *dn_scales;
@@ -474,7 +495,7 @@ typedef struct {
     uint8_t *a_codes, *a_scales;
     float *a_tscale;
     float *inter; /* pre-quantisation SwiGLU output, fp32 [S][F] */
-    uint8_t *inter_codes, *inter_scales;
+    uint8_t *inter_codes, *inter_scales; /* fmt 4: bf16 bit patterns [S][F] (2 bytes each), no scales */
     float *inter_tscale;
     float *y;  /* down projection per slot (before the gate weight), fp32 [S][D] */
     double *inter_abs; /* optional: sum_k |a_k w_k| of the gate (j < F) and up (j >= F)
@@ -523,20 +544,25 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
  *  6. out[t] = sum over the token's local slots, j ascending, of w[t][j] * y
  *     (fp64, rounded to fp32); tokens without local slots get zeros.
  * fmt 0 runs the same steps on the bf16 masters entirely in fp64 (no
- * quantisation and no intermediate fp32 rounding).
+ * quantisation and no intermediate fp32 rounding). fmt 4 (W4A16: NVFP4 weights
+ * dequantised on the fly, activations kept in bf16; vLLM recipe
+ * "thinkingmachines/Inkling-Small", section "Variants") skips step 1, multiplies the
+ * fp32-rounded sums of 2 and 5 by the weight tensor scale alone, and in step 4 rounds
+ * h to bf16 (nearest, ties to even).
  */
 int orc_moe_forward(const orc_moe_args *a) {
     if (!a || a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->k <= 0 || a->k > a->E) return ORC_EINVAL;
     if (a->e_begin < 0 || a->e_end > a->E || a->e_end <= a->e_begin) return ORC_EINVAL;
-    if (a->fmt < 0 || a->fmt > 3) return ORC_EINVAL;
+    if (a->fmt < 0 || a->fmt > 4) return ORC_EINVAL;
     const int fmt = a->fmt;
+    const int wf = fmt == 4 ? 1 : fmt; /* weight format */
     const int64_t T = a->T, D = a->D, F = a->F, k = a->k;
-    if (fmt == 1 && (D % 16 || F % 16)) return ORC_EINVAL;
+    if (wf == 1 && (D % 16 || F % 16)) return ORC_EINVAL;
     if ((fmt == 2 || fmt == 3) && (D % 32 || F % 32)) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
     if (!a->h || !a->idx || !a->w || !a->out) return ORC_EINVAL;
     if (fmt == 0 && (!a->gu_master || !a->dn_master)) return ORC_EINVAL;
-    if (fmt == 1 && (!a->gu_codes || !a->gu_scales || !a->gu_tscale || !a->dn_codes || !a->dn_scales || !a->dn_tscale))
+    if (wf == 1 && (!a->gu_codes || !a->gu_scales || !a->gu_tscale || !a->dn_codes || !a->dn_scales || !a->dn_tscale))
         return ORC_EINVAL;
     if ((fmt == 2 || fmt == 3) && (!a->gu_codes || !a->gu_scales || !a->dn_codes || !a->dn_scales)) return ORC_EINVAL;
     init_tables();
@@ -580,7 +606,7 @@ int orc_moe_forward(const orc_moe_args *a) {
         float *hf = (float *)malloc(sizeof(float) * T * D);
         if (!hf) { rc = ORC_ENOMEM; goto done; }
         for (int64_t i = 0; i < T * D; ++i) hf[i] = bf16_value(a->h[i]);
-        if (fmt == 0) {
+        if (fmt == 0 || fmt == 4) {
             for (int64_t i = 0; i < T * D; ++i) ahat[i] = hf[i];
         } else {
             int64_t nc = fmt == 2 ? T * D : T * D / 2, ns = fmt == 1 ? T * D / 16 : T * D / 32;
@@ -625,7 +651,7 @@ int orc_moe_forward(const orc_moe_args *a) {
                     int any = 0;
                     for (int64_t p = offs[el]; p < offs[el + 1]; ++p) any |= cidx[p] >= 0;
                     if (!any) continue;
-                    weight_row(fmt, a->gu_master, a->gu_codes, a->gu_scales,
+                    weight_row(wf, a->gu_master, a->gu_codes, a->gu_scales,
                                (int64_t)(a->e_begin + el) * nrows + r, D, wrow);
                     for (int64_t p = offs[el]; p < offs[el + 1]; ++p) {
                         if (cidx[p] < 0) continue;
@@ -658,14 +684,14 @@ int orc_moe_forward(const orc_moe_args *a) {
         int64_t c = cidx[p];
         if (c < 0) continue;
         int32_t e = sorted[p] >= 0 ? a->idx[sorted[p]] : 0;
-        float sc = fmt == 1 ? a_ts * a->gu_tscale[e] : 1.0f;
+        float sc = fmt == 1 ? a_ts * a->gu_tscale[e] : (fmt == 4 ? a->gu_tscale[e] : 1.0f);
         for (int64_t f = 0; f < F; ++f) {
             double gr = gu_raw[c * 2 * F + f], ur = gu_raw[c * 2 * F + F + f];
             if (fmt == 0) {
                 inter64[c * F + f] = gr * ur / (1.0 + exp(-gr));
             } else {
                 float g = (float)gr, u = (float)ur;
-                if (fmt == 1) {
+                if (wf == 1) {
                     g = g * sc;
                     u = u * sc;
                 }
@@ -682,6 +708,16 @@ int orc_moe_forward(const orc_moe_args *a) {
     if (!ihat) { rc = ORC_ENOMEM; goto done; }
     if (fmt == 0) {
         memcpy(ihat, inter64, sizeof(double) * ngu * F);
+    } else if (fmt == 4) {
+        for (int64_t p = 0; p < S; ++p) {
+            int64_t c = cidx[p];
+            if (c < 0) continue;
+            for (int64_t f = 0; f < F; ++f) {
+                uint16_t b = bf16_rne(inter[c * F + f]);
+                ihat[c * F + f] = bf16_value(b);
+                if (a->inter_codes) memcpy(a->inter_codes + 2 * (p * F + f), &b, 2);
+            }
+        }
     } else if (fmt == 1) {
         /* every local slot is in the compact set, in sorted order (cidx[p] == p) */
         uint8_t *ic = (uint8_t *)malloc(S * F / 2 + 1), *is = (uint8_t *)malloc(S * F / 16 + 1);
@@ -735,8 +771,8 @@ int orc_moe_forward(const orc_moe_args *a) {
                     for (int64_t p = offs[el]; p < offs[el + 1]; ++p) any |= cdn[p] >= 0;
                     if (!any) continue;
                     int32_t e = a->e_begin + el;
-                    weight_row(fmt, a->dn_master, a->dn_codes, a->dn_scales, (int64_t)e * D + n, F, wrow);
-                    float sc = fmt == 1 ? i_ts * a->dn_tscale[e] : 1.0f;
+                    weight_row(wf, a->dn_master, a->dn_codes, a->dn_scales, (int64_t)e * D + n, F, wrow);
+                    float sc = fmt == 1 ? i_ts * a->dn_tscale[e] : (fmt == 4 ? a->dn_tscale[e] : 1.0f);
                     for (int64_t p = offs[el]; p < offs[el + 1]; ++p) {
                         if (cdn[p] < 0) continue;
                         const double *irow = ihat + cidx[p] * F;
@@ -744,7 +780,7 @@ int orc_moe_forward(const orc_moe_args *a) {
                         for (int64_t f = 0; f < F; ++f) s += irow[f] * wrow[f];
                         double yv;
                         if (fmt == 0) yv = s;
-                        else if (fmt == 1) yv = (float)((float)s * sc);
+                        else if (wf == 1) yv = (float)((float)s * sc);
                         else yv = (float)s;
                         y64[cdn[p] * D + n] = yv;
                         if (a->y) a->y[p * D + n] = (float)yv;
@@ -794,16 +830,18 @@ done:
  * out[t] = sum over the token's local slots, j ascending, of w[t][j] * y (fp64, rounded
  * to fp32). Used to check a down projection and combine on another implementation's
  * intermediate codes. i_codes / i_scales: [S][F/2] and [S][F/16] (NVFP4, tensor scale
- * i_ts), [S][F] and [S][F/32] (MXFP8) or [S][F/2] and [S][F/32] (MXFP4).
+ * i_ts), [S][F] and [S][F/32] (MXFP8), [S][F/2] and [S][F/32] (MXFP4), or bf16 bit
+ * patterns [S][F] (2 bytes each) and no scales (W4A16, fmt 4).
  */
 int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, int32_t k, int32_t e_begin,
                      int32_t e_end, const int32_t *idx, const float *w, const uint8_t *i_codes,
                      const uint8_t *i_scales, float i_ts, const uint8_t *dn_codes, const uint8_t *dn_scales,
                      const float *dn_tscale, float *out) {
-    if (fmt < 1 || fmt > 3) return ORC_EINVAL;
+    if (fmt < 1 || fmt > 4) return ORC_EINVAL;
+    const int wf = fmt == 4 ? 1 : fmt;
     if (T < 0 || D <= 0 || F <= 0 || E <= 0 || k <= 0 || e_begin < 0 || e_end > E || e_end <= e_begin) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
-    if (!idx || !w || !i_codes || !i_scales || !dn_codes || !dn_scales || !out || (fmt == 1 && !dn_tscale))
+    if (!idx || !w || !i_codes || (fmt != 4 && !i_scales) || !dn_codes || !dn_scales || !out || (wf == 1 && !dn_tscale))
         return ORC_EINVAL;
     init_tables();
     const int32_t n_loc = e_end - e_begin;
@@ -820,7 +858,13 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
     if (!ihat || !y64) { rc = ORC_ENOMEM; goto done; }
     if (fmt == 1) orc_dequant_nvfp4(i_codes, i_scales, i_ts, S, F, 0, ihat);
     else if (fmt == 2) orc_dequant_mxfp8(i_codes, i_scales, S, F, ihat);
-    else orc_dequant_mxfp4(i_codes, i_scales, S, F, ihat);
+    else if (fmt == 3) orc_dequant_mxfp4(i_codes, i_scales, S, F, ihat);
+    else
+        for (int64_t i = 0; i < S * F; ++i) {
+            uint16_t b;
+            memcpy(&b, i_codes + 2 * i, 2);
+            ihat[i] = bf16_value(b);
+        }
     {
         int fail = 0;
 #pragma omp parallel
@@ -836,13 +880,13 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
                     int64_t n = it % D;
                     if (offs[el] == offs[el + 1]) continue;
                     int32_t e = e_begin + el;
-                    weight_row(fmt, NULL, dn_codes, dn_scales, (int64_t)e * D + n, F, wrow);
-                    float sc = fmt == 1 ? i_ts * dn_tscale[e] : 1.0f;
+                    weight_row(wf, NULL, dn_codes, dn_scales, (int64_t)e * D + n, F, wrow);
+                    float sc = fmt == 1 ? i_ts * dn_tscale[e] : (fmt == 4 ? dn_tscale[e] : 1.0f);
                     for (int64_t p = offs[el]; p < offs[el + 1]; ++p) {
                         const double *irow = ihat + p * F;
                         double s = 0.0;
                         for (int64_t f = 0; f < F; ++f) s += irow[f] * wrow[f];
-                        y64[p * D + n] = fmt == 1 ? (double)(float)((float)s * sc) : (double)(float)s;
+                        y64[p * D + n] = wf == 1 ? (double)(float)((float)s * sc) : (double)(float)s;
                     }
                 }
             }

@@ -132,3 +132,20 @@ def test_nvfp4_tensor_scale():
     assert oracle.nvfp4_tensor_scale(0.0) == 1.0
     a = np.float32(0.1103515625)
     assert oracle.nvfp4_tensor_scale(float(a)) == float(np.float32(a) / np.float32(2688.0))
+
+
+def test_bf16_rounding_matches_torch():
+    """fp32 -> bf16 (nearest, ties to even), the W4A16 intermediate's rounding, against
+    torch's CPU conversion: random values over the whole exponent range, exact ties of
+    both parities, values one ulp either side of a tie, subnormals and signed zeros."""
+    rng = np.random.default_rng(5)
+    bits = rng.integers(0, 0x7F800000, 200_000, dtype=np.uint32)  # finite, non-negative
+    x = bits.view(np.float32)
+    kept = (bits >> 16).astype(np.uint32)
+    ties = ((kept << 16) | 0x8000).view(np.float32)                # exactly half an ulp
+    near = np.concatenate([((kept << 16) | 0x7FFF).view(np.float32), ((kept << 16) | 0x8001).view(np.float32)])
+    special = np.array([0.0, -0.0, 1e-45, -1e-45, 1e-40, 1.0, -1.0, 3.0e38, -3.0e38], np.float32)
+    allx = np.concatenate([x, -x, ties, -ties, near, special]).astype(np.float32)
+    got = oracle.round_bf16(allx)
+    ref = torch.from_numpy(allx).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, ref)

@@ -175,7 +175,7 @@ def test_quantised_layer_composes_from_pinned_parts(fmt):
 def test_quantisation_error_ordering_against_unquantised():
     T, D, F, E = 32, 128, 64, 16
     errs = {}
-    for fmt in ("nvfp4", "mxfp8", "mxfp4"):
+    for fmt in ("nvfp4", "mxfp8", "mxfp4", "w4a16"):
         wl, h, wr, _ = _small(fmt, T=T, D=D, F=F, E=E, seed=12)
         gu_m, dn_m = wl.gate_up_master(0, E), wl.down_master(0, E)
         idx, w = oracle.route(h, wr, k=8)
@@ -185,9 +185,12 @@ def test_quantisation_error_ordering_against_unquantised():
         errs[fmt] = np.linalg.norm(out - ref) / np.linalg.norm(ref)
     assert errs["mxfp8"] < 0.08 and errs["nvfp4"] < 0.35 and errs["mxfp4"] < 0.45
     assert errs["mxfp8"] < errs["nvfp4"] / 2 and errs["nvfp4"] < errs["mxfp4"]
+    # bf16 activations: only the weights' rounding is left; removing one of two independent
+    # errors of similar size shrinks the total by about sqrt(2)
+    assert errs["w4a16"] < errs["nvfp4"] / 1.25 and errs["w4a16"] < 0.25
 
 
-@pytest.mark.parametrize("fmt", ["none", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["none", "mxfp8", "mxfp4", "w4a16"])
 def test_expert_parallel_shares_add_up(fmt):
     """Four expert ranges (an EP4 split) sum to the full layer. NVFP4 is excluded:
     its intermediate tensor scale is taken over each share's own slots."""
@@ -232,7 +235,7 @@ def test_empty_batch_is_a_no_op():
     assert out.shape == (0, 64)
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "w4a16"])
 def test_down_combine_reproduces_the_forward(fmt):
     """The stage-wise entry point (down projection + combine from given intermediate codes),
     fed the forward's own intermediate codes, gives the forward's output bit for bit, also
@@ -245,6 +248,84 @@ def test_down_combine_reproduces_the_forward(fmt):
         out, tp = oracle.moe_forward(fmt, h, idx, w, D=D, F=F, E=E, e_begin=eb, e_end=ee, gate_up=gu, down=dn,
                                      taps=True)
         ts = tp["inter_tscale"][0] if fmt == "nvfp4" else None
-        got = oracle.down_combine(fmt, idx, w, tp["inter_codes"], tp["inter_scales"], ts, dn, D=D, F=F, E=E,
+        got = oracle.down_combine(fmt, idx, w, tp["inter_codes"], tp.get("inter_scales"), ts, dn, D=D, F=F, E=E,
                                   e_begin=eb, e_end=ee)
         assert np.array_equal(got.view(np.uint32), out.view(np.uint32))
+
+
+# ------------------------------------------------------------------ W4A16
+def _bf16_bits(x) -> np.ndarray:
+    """torch's fp32 -> bf16 conversion (nearest, ties to even) as uint16 bit patterns."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x, f32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_w4a16_composes_from_pinned_parts():
+    """NVFP4 weights with bf16 activations (vLLM recipe "thinkingmachines/Inkling-Small",
+    section "Variants": the weights dequantised on the fly): the C pipeline equals a numpy
+    composition of the pinned NVFP4 dequantiser, BLAS matmuls on the unquantised bf16
+    hidden states, the weight tensor scale on the fp32 sums, and torch's bf16 rounding of
+    the SwiGLU output."""
+    T, D, F, E = 20, 64, 64, 12
+    wl, h, wr, _ = _small("nvfp4", T=T, D=D, F=F, E=E, seed=9)
+    gu, dn = _quantised("w4a16", wl)
+    idx, w = oracle.route(h, wr, k=8)
+    out, tp = oracle.moe_forward("w4a16", h, idx, w, D=D, F=F, E=E, gate_up=gu, down=dn, taps=True)
+    assert "a_codes" not in tp  # hidden states are not quantised
+    H = synth.bf16_to_f32(h).astype(np.float64)
+    counts, offs, ss = oracle.permute(idx, 0, E)
+    S = len(ss)
+    inter = np.zeros((S, F), f32)
+    for p, s in enumerate(ss):
+        t, e = s // 8, idx.reshape(-1)[s]
+        W = oracle.dequant_nvfp4(gu["codes"][e], gu["scales"][e], 1.0, with_tensor=False)
+        gl = (W @ H[t]).astype(f32) * f32(gu["tensor_scale"][e])
+        g, u = gl[:F].astype(np.float64), gl[F:].astype(np.float64)
+        inter[p] = (g * u / (1.0 + np.exp(-g))).astype(f32)
+    np.testing.assert_array_equal(inter, tp["inter"])
+    ib = _bf16_bits(inter)
+    assert np.array_equal(ib, tp["inter_codes"])
+    I = synth.bf16_to_f32(ib).astype(np.float64)
+    ref = np.zeros((T, D))
+    for p, s in enumerate(ss):
+        t, j = divmod(int(s), 8)
+        e = idx[t, j]
+        Wd = oracle.dequant_nvfp4(dn["codes"][e], dn["scales"][e], 1.0, with_tensor=False)
+        y = (Wd @ I[p]).astype(f32) * f32(dn["tensor_scale"][e])
+        np.testing.assert_array_equal(y, tp["y"][p])
+        ref[t] += float(w[t, j]) * y.astype(np.float64)
+    np.testing.assert_allclose(out, ref.astype(f32), rtol=1e-6, atol=1e-9)
+
+
+def _grid_masters(E, N, K, seed):
+    """bf16 masters whose NVFP4 encoding is exact up to the tensor scale's rounding: every
+    value is c * 2^-7 with c on the E2M1 grid, and every 16-block holds a +-6 (so each block
+    and the tensor share amax 6 * 2^-7 and the block scale is E4M3's 448)."""
+    rng = np.random.default_rng(seed)
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], np.float64)
+    c = grid[rng.integers(0, 8, (E, N, K))] * rng.choice([-1.0, 1.0], (E, N, K))
+    blocks = c.reshape(E, N, K // 16, 16)
+    pos = rng.integers(0, 16, (E, N, K // 16))
+    np.put_along_axis(blocks, pos[..., None], 6.0 * rng.choice([-1.0, 1.0], (E, N, K // 16, 1)), axis=3)
+    return _bf16_bits((blocks.reshape(E, N, K) * 2.0 ** -7).astype(f32))
+
+
+def test_w4a16_on_exactly_encodable_weights_is_the_bf16_layer():
+    """When the NVFP4 weights reproduce the masters, W4A16 is the unquantised layer up to
+    the bf16 rounding of the SwiGLU output (and ulp-level tensor-scale rounding), while
+    W4A4 still carries the activation quantisation error."""
+    T, D, F, E = 24, 128, 64, 12
+    wl, h, wr, _ = _small("nvfp4", T=T, D=D, F=F, E=E, seed=14)
+    gu_m, dn_m = _grid_masters(E, 2 * F, D, 1), _grid_masters(E, D, F, 2)
+    idx, w = oracle.route(h, wr, k=8)
+    ref = oracle.moe_forward("none", h, idx, w, D=D, F=F, E=E, gate_up_master=gu_m, down_master=dn_m)
+    gu, dn = oracle.quantize_weights("nvfp4", gu_m), oracle.quantize_weights("nvfp4", dn_m)
+    W = oracle.dequant_nvfp4(gu["codes"].reshape(-1, D // 2), gu["scales"].reshape(-1, D // 16),
+                             float(gu["tensor_scale"][0]))
+    np.testing.assert_allclose(W.reshape(E, 2 * F, D), synth.bf16_to_f32(gu_m), rtol=2e-7, atol=0)
+    a16 = oracle.moe_forward("w4a16", h, idx, w, D=D, F=F, E=E, gate_up=gu, down=dn)
+    a4 = oracle.moe_forward("nvfp4", h, idx, w, D=D, F=F, E=E, gate_up=gu, down=dn)
+    err16 = np.linalg.norm(a16 - ref) / np.linalg.norm(ref)
+    err4 = np.linalg.norm(a4 - ref) / np.linalg.norm(ref)
+    assert err16 < 3e-3, err16      # bf16 rounding of the intermediate only (2^-9 relative)
+    assert err4 > 10 * err16, (err4, err16)
