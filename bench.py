@@ -5,8 +5,8 @@ weights, hidden-state amax) + moe_forward (permutation, hidden-state quantisatio
 gate_up GEMM with SwiGLU and intermediate quantisation, down GEMM, weighted
 combine), with all inputs and packed weights resident in HBM. The default workload
 is the NVFP4 decode step (64 tokens, d_model 4096, d_ff 2560, 384 experts, top-8);
---workload i selects one of the seven seeded synthetic workloads (NVFP4, MXFP8 and the
-MXFP4 variant).
+--workload i selects one of the nine seeded synthetic workloads (NVFP4, MXFP8, and the
+MXFP4 and W4A16 variants).
 
 Printed: one JSON line (rank 0). `roofline` covers the dominant kernel (the gate_up
 GEMM) timed live with HIP events recorded around its launch on the library's stream;
@@ -33,7 +33,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}  # dense, MI355X
 DTYPES = {"nvfp4": "f16 (exact NVFP4 values), fp32 accumulate",
           "mxfp8": "bf16 (exact MXFP8 values), fp32 accumulate",
-          "mxfp4": "fp4 (MXFP4 codes and E8M0 scales on the scaled MFMA), fp32 accumulate"}
+          "mxfp4": "fp4 (MXFP4 codes and E8M0 scales on the scaled MFMA), fp32 accumulate",
+          "w4a16": "bf16 (bf16 activations, NVFP4 weights expanded exactly), fp32 accumulate"}
 METRIC = "MoE layer tokens/s; % peak HBM BW (decode), % scaled-MFMA peak (prefill)"
 
 
@@ -113,7 +114,7 @@ def profiled_traffic(workload: str, kernel: str):
 
 
 def packed_bytes_per_expert(fmt: str, N: int, K: int) -> int:
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "w4a16"):
         return N * K // 2 + N * K // 16 + 4
     if fmt == "mxfp4":
         return N * K // 2 + N * K // 32
@@ -201,7 +202,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, help="index into the seven synthetic workloads")
+    ap.add_argument("--workload", type=int, default=1, help="index into the nine synthetic workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "
@@ -304,7 +305,7 @@ def main():
     gu_b = packed_bytes_per_expert(wl.fmt, 2 * F, D)
     dn_b = packed_bytes_per_expert(wl.fmt, D, F)
     code_b = {"nvfp4": lambda c: c // 2 + c // 16, "mxfp4": lambda c: c // 2 + c // 32,
-              "mxfp8": lambda c: c + c // 32}[wl.fmt]
+              "mxfp8": lambda c: c + c // 32, "w4a16": lambda c: 2 * c}[wl.fmt]
     act_b = lambda rows, cols: rows * code_b(cols)
     gate_up_bytes = touched * gu_b + act_b(T, D) + act_b(S, F)
     gate_up_flops = 4.0 * S * F * D
@@ -313,7 +314,7 @@ def main():
     # the contraction's peak, with the format's own scaled-MFMA peak reported beside it;
     # the MXFP4 GEMMs run the scaled FP4 MFMA itself
     mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else "bf16")]
-    format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else "fp8"]
+    format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt == "w4a16" else "fp8")]
     decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge
     if decode:
         achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9

@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3}
+FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4}  # w4a16: moe_forward only (NVFP4 weights)
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "alignment",
           -4: "workspace", -5: "HIP launch failed"}
 
@@ -116,7 +116,9 @@ class PackedWeights:
 
     @staticmethod
     def empty(fmt: str, E: int, N: int, K: int, device="cuda") -> "PackedWeights":
-        if fmt not in FMT:
+        if fmt == "w4a16":  # a W4A16 layer's weights are NVFP4
+            fmt = "nvfp4"
+        if fmt not in FMT or fmt == "w4a16":
             raise ValueError(f"unknown format {fmt!r}")
         nv = fmt == "nvfp4"
         if N % 32 or K % 64:
@@ -152,7 +154,10 @@ def _bf16_view(t: torch.Tensor) -> torch.Tensor:
 
 
 def quantize_weights(fmt: str, w: torch.Tensor, out: PackedWeights | None = None) -> PackedWeights:
-    """bf16 masters w [E, N, K] (device) -> PackedWeights (moe_quantize_weights)."""
+    """bf16 masters w [E, N, K] (device) -> PackedWeights (moe_quantize_weights); "w4a16"
+    gives the NVFP4 packing its layers use."""
+    if fmt == "w4a16":
+        fmt = "nvfp4"
     w = _bf16_view(w)
     E, N, K = w.shape
     if out is None:
@@ -209,20 +214,26 @@ class Layer:
         self._tap_tensors: dict = {}
 
     def enable_taps(self):
-        """Allocate every debug output of moe_forward (sized for S <= T*top_k)."""
+        """Allocate every debug output of moe_forward (sized for S <= T*top_k). W4A16 has no
+        hidden-state codes and its intermediate codes are bf16 bit patterns (int16)."""
         T, D, F, k, n = self.T, self.D, self.F, self.top_k, self.e_end - self.e_begin
         nv, dev = self.fmt == "nvfp4", self.device
         TK = T * k
         spec = {
             "counts": ((n,), torch.int32), "offsets": ((n + 1,), torch.int32),
             "sorted_slot": ((TK,), torch.int32),
-            "a_codes": ((T, D if self.fmt == "mxfp8" else D // 2), torch.uint8),
-            "a_scales": ((T, D // 16 if nv else D // 32), torch.uint8),
             "inter": ((TK, F), torch.float32),
-            "inter_codes": ((TK, F if self.fmt == "mxfp8" else F // 2), torch.uint8),
-            "inter_scales": ((TK, F // 16 if nv else F // 32), torch.uint8),
             "y": ((TK, D), torch.float32),
         }
+        if self.fmt == "w4a16":
+            spec["inter_codes"] = ((TK, F), torch.int16)
+        else:
+            spec.update({
+                "a_codes": ((T, D if self.fmt == "mxfp8" else D // 2), torch.uint8),
+                "a_scales": ((T, D // 16 if nv else D // 32), torch.uint8),
+                "inter_codes": ((TK, F if self.fmt == "mxfp8" else F // 2), torch.uint8),
+                "inter_scales": ((TK, F // 16 if nv else F // 32), torch.uint8),
+            })
         if nv:
             spec["a_tscale"] = ((4,), torch.float32)
             spec["inter_tscale"] = ((4,), torch.float32)

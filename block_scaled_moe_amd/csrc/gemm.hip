@@ -5,7 +5,9 @@
 // AI Primer "Thinking Machines releases Inkling 2 Small weights under Apache 2.0",
 // section "NVFP4 and MXFP8 experts"): NVFP4 = E2M1 codes, an E4M3 scale per 16 and an
 // fp32 tensor scale; MXFP8 = E4M3 codes and an E8M0 scale per 32. Activations arrive
-// in the same format, already expanded to their exact 16-bit values.
+// in the same format, already expanded to their exact 16-bit values; or, for NVFP4
+// weights with bf16 activations (W4A16, vLLM recipe "thinkingmachines/Inkling-Small",
+// section "Variants"), as the bf16 values themselves, with the weights expanded to bf16.
 //
 // Arithmetic: every weight value is formed EXACTLY in a 16-bit float and fed to a
 // 16x16x32 MFMA with fp32 accumulation, so all products are exact and the sums are
@@ -41,8 +43,9 @@ namespace {
 
 using namespace gemm_detail;
 
-template <bool NV, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
+template <int FM, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
 struct Cfg {
+    static constexpr bool NV = FM != kFmtMX8;         // NVFP4 weights
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MS = WTM / 16, NS = WTN / 16;
@@ -69,10 +72,13 @@ struct Cfg {
     static_assert(!GATE_UP || NS % 2 == 0, "gate and up halves");
 };
 
-template <bool NV, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
+template <int FM, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
 __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmArgs p) {
-    using C = Cfg<NV, BM, BN, KC, WM, WN, GATE_UP>;
-    using Frag = typename std::conditional<NV, half8, bf16x8>::type;
+    using C = Cfg<FM, BM, BN, KC, WM, WN, GATE_UP>;
+    constexpr bool NV = C::NV;                   // NVFP4 weights (W4A4 or W4A16)
+    constexpr bool BF = FM != kFmtNV;            // bf16 operands and MFMA
+    constexpr bool A16 = FM == kFmtA16;
+    using Frag = typename std::conditional<BF, bf16x8, half8>::type;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
     const int tile = blockIdx.x;
@@ -166,6 +172,7 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
 #pragma unroll
             for (int jj = 0; jj < KC / 128; ++jj) {
                 _Float16 sh[C::NS][2];
+                float sf[C::NS][2];
                 float sm[C::NS];
 #pragma unroll
                 for (int ns = 0; ns < C::NS; ++ns) {
@@ -174,6 +181,8 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                         const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
                         sh[ns][0] = e4m3_to_f16(two & 0xff);
                         sh[ns][1] = e4m3_to_f16(two >> 8);
+                        sf[ns][0] = (float)sh[ns][0];
+                        sf[ns][1] = (float)sh[ns][1];
                     } else {
                         sm[ns] = __uint_as_float((uint32_t)srow[4 * jj + g] << 23);
                     }
@@ -189,12 +198,18 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
 #pragma unroll
                     for (int ns = 0; ns < C::NS; ++ns) {
                         const uint8_t *brow = smem + C::B_OFF + MOE_BROW(ns) * C::B_STRIDE;
-                        if constexpr (NV) {
+                        if constexpr (NV && !BF) {
                             const half8 bf = dequant_nvfp4(*reinterpret_cast<const uint32_t *>(brow + kk / 2),
                                                            sh[ns][j >> 1]);
 #pragma unroll
                             for (int ms = 0; ms < C::MS; ++ms)
                                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                        } else if constexpr (A16) {
+                            const bf16x8 bf = dequant_nvfp4_bf16(*reinterpret_cast<const uint32_t *>(brow + kk / 2),
+                                                                 sf[ns][j >> 1]);
+#pragma unroll
+                            for (int ms = 0; ms < C::MS; ++ms)
+                                acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                         } else {
                             const bf16x8 bf = dequant_mxfp8(*reinterpret_cast<const u32x2 *>(brow + kk), sm[ns]);
 #pragma unroll
@@ -222,8 +237,8 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
     }
 
     // ---- epilogue: C fragment of a lane = rows 4g..4g+3, column r16 of each 16x16 subtile
-    const float sc = NV ? p.a_tscale[0] * p.w_tscale[e] : 1.0f;
-    if (GATE_UP && NV) {
+    const float sc = FM == kFmtNV ? p.a_tscale[0] * p.w_tscale[e] : (A16 ? p.w_tscale[e] : 1.0f);
+    if (GATE_UP && FM == kFmtNV) {
         uint32_t amax = 0;
 #pragma unroll
         for (int ms = 0; ms < C::MS; ++ms)
@@ -240,6 +255,21 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                 }
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
         if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
+    } else if (GATE_UP && A16) {
+        // W4A16: the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
+#pragma unroll
+        for (int ms = 0; ms < C::MS; ++ms)
+#pragma unroll
+            for (int ns = 0; ns < C::NS / 2; ++ns)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = wm * C::WTM + 16 * ms + 4 * g + i;
+                    if (m >= rows) continue;
+                    const int64_t o = (int64_t)(p0 + m) * F + n0 + wn * (C::WTN / 2) + 16 * ns + r16;
+                    const float hv = swiglu(acc[ms][ns][i] * sc, acc[ms][ns + C::NS / 2][i] * sc);
+                    static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
+                    if (p.o_tap) p.o_tap[o] = hv;
+                }
     } else if (GATE_UP) {
         // MXFP8: SwiGLU into an LDS tile [BM][BN/2], then quantise each 32-wide row block
         float *epi = reinterpret_cast<float *>(smem);
@@ -293,34 +323,39 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
 #undef MOE_BROW
 }
 
-template <bool NV, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
+template <int FM, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
 hipError_t launch(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
     const int n_tiles_n = GATE_UP ? (a.N / 2) / (BN / 2) : a.N / BN;
     dim3 grid((unsigned)max_tiles, (unsigned)n_tiles_n);
-    hipLaunchKernelGGL((grouped_gemm_kernel<NV, BM, BN, KC, WM, WN, GATE_UP>), grid, dim3(WM * WN * 64), 0, s, a);
+    hipLaunchKernelGGL((grouped_gemm_kernel<FM, BM, BN, KC, WM, WN, GATE_UP>), grid, dim3(WM * WN * 64), 0, s, a);
     return hipGetLastError();
 }
 
-template <bool NV>
+template <int FM>
 hipError_t dispatch(const GemmArgs &a, bool gate_up, GemmShape shape, int32_t max_tiles, hipStream_t s) {
     if (shape == GemmShape::Decode) {
         if (a.K % 256 == 0)
-            return gate_up ? launch<NV, 16, 128, 256, 1, 4, true>(a, max_tiles, s)
-                           : launch<NV, 16, 128, 256, 1, 4, false>(a, max_tiles, s);
-        return gate_up ? launch<NV, 16, 128, 128, 1, 4, true>(a, max_tiles, s)
-                       : launch<NV, 16, 128, 128, 1, 4, false>(a, max_tiles, s);
+            return gate_up ? launch<FM, 16, 128, 256, 1, 4, true>(a, max_tiles, s)
+                           : launch<FM, 16, 128, 256, 1, 4, false>(a, max_tiles, s);
+        return gate_up ? launch<FM, 16, 128, 128, 1, 4, true>(a, max_tiles, s)
+                       : launch<FM, 16, 128, 128, 1, 4, false>(a, max_tiles, s);
     }
-    return gate_up ? launch<NV, 128, 128, 128, 2, 2, true>(a, max_tiles, s)
-                   : launch<NV, 128, 128, 128, 2, 2, false>(a, max_tiles, s);
+    return gate_up ? launch<FM, 128, 128, 128, 2, 2, true>(a, max_tiles, s)
+                   : launch<FM, 128, 128, 128, 2, 2, false>(a, max_tiles, s);
 }
 
 }  // namespace
 
 int32_t gemm_bm(GemmShape shape) { return shape == GemmShape::Decode ? 16 : 128; }
 
-hipError_t launch_grouped_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, GemmShape shape, int32_t max_tiles,
+hipError_t launch_grouped_gemm(const GemmArgs &a, int fm, bool gate_up, GemmShape shape, int32_t max_tiles,
                                hipStream_t s) {
-    return nvfp4 ? dispatch<true>(a, gate_up, shape, max_tiles, s) : dispatch<false>(a, gate_up, shape, max_tiles, s);
+    switch (fm) {
+        case kFmtNV: return dispatch<kFmtNV>(a, gate_up, shape, max_tiles, s);
+        case kFmtMX8: return dispatch<kFmtMX8>(a, gate_up, shape, max_tiles, s);
+        case kFmtA16: return dispatch<kFmtA16>(a, gate_up, shape, max_tiles, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe

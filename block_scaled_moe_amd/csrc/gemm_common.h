@@ -1,5 +1,6 @@
 // gemm_common.h - exact 16-bit expansion of NVFP4 / MXFP8 codes for the gfx950 MFMAs,
-// shared by the grouped GEMM kernels (tiled and streaming).
+// shared by the grouped GEMM kernels (tiled and streaming), for W4A4 / W8A8 layers and
+// for NVFP4 weights with bf16 activations (W4A16).
 //
 // NVFP4 (E2M1 codes, E4M3 scale per 16; vLLM recipe "thinkingmachines/Inkling-2-Small",
 // section "Overview"): c * s has at most 6 significant bits and lies in [2^-10, 2688],
@@ -39,6 +40,24 @@ __device__ __forceinline__ half8 dequant_nvfp4(uint32_t codes, _Float16 s) {
     half8 r;
     r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
     r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+}
+
+// 8 E2M1 codes (element i in nibble i) times the E4M3 scale value s -> 8 exact bf16
+// (c * s has at most 6 significant bits). gfx950 has no packed bf16 multiply: two codes
+// go to fp32 with the convert at scale 1, the two products are exact in fp32, and the
+// pack to bf16 is exact.
+__device__ __forceinline__ bf16x8 dequant_nvfp4_bf16(uint32_t codes, float s) {
+    typedef float float2_t __attribute__((ext_vector_type(2)));
+    const float2_t c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
+    const float2_t c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
+    const float2_t c2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
+    const float2_t c3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
+    bf16x8 r;
+    r[0] = (__bf16)(c0[0] * s); r[1] = (__bf16)(c0[1] * s);
+    r[2] = (__bf16)(c1[0] * s); r[3] = (__bf16)(c1[1] * s);
+    r[4] = (__bf16)(c2[0] * s); r[5] = (__bf16)(c2[1] * s);
+    r[6] = (__bf16)(c3[0] * s); r[7] = (__bf16)(c3[1] * s);
     return r;
 }
 

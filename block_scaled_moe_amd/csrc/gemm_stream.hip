@@ -2,7 +2,8 @@
 // so the layer is bound by streaming the packed expert weights from HBM once.
 //
 // Same arithmetic as the tiled kernels (exact 16-bit expansion of NVFP4 / MXFP8 codes,
-// 16x16x32 MFMA, fp32 accumulation; see gemm_common.h), organised for bandwidth:
+// 16x16x32 MFMA, fp32 accumulation; see gemm_common.h; for W4A16 the NVFP4 weights are
+// expanded to bf16 and the activations are the bf16 values), organised for bandwidth:
 //  - a workgroup owns one M-tile (<= 16 sorted rows of one expert) and 64 weight rows
 //    (gate_up: 32 gate rows and the 32 matching up rows; down: 64 output columns);
 //  - its 4 waves split K into quarters, and each lane streams its weight bytes straight
@@ -48,9 +49,12 @@ constexpr int kRows = 64;  // weight rows per workgroup
 #define MOE_STREAM_OCCUPANCY
 #endif
 
-template <bool NV, bool GATE_UP, int G>  // G = 128-wide K groups per wave (K = 512 G)
+template <int FM, bool GATE_UP, int G>  // G = 128-wide K groups per wave (K = 512 G)
 __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(const GemmArgs p) {
-    using Frag = typename std::conditional<NV, half8, bf16x8>::type;
+    constexpr bool NV = FM != kFmtMX8;  // NVFP4 weights (W4A4 or W4A16)
+    constexpr bool BF = FM != kFmtNV;   // bf16 operands and MFMA
+    constexpr bool A16 = FM == kFmtA16;
+    using Frag = typename std::conditional<BF, bf16x8, half8>::type;
     constexpr int NQ = NV ? 1 : 2;                 // 16-byte code loads per lane, group and subtile
     constexpr int W = NV ? MOE_STREAM_W_NV : MOE_STREAM_W_MX;  // groups of loads in flight
     constexpr int BLK = NV ? 16 : 32;
@@ -155,6 +159,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     for (int jj = 0; jj < G; ++jj) {
         if (jj + W < G) load_group(jj + W);
         _Float16 sh[kSub][2];
+        float sf[kSub][2];
         float sm[kSub];
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
@@ -163,6 +168,8 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                 const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
                 sh[s][0] = e4m3_to_f16(two & 0xff);
                 sh[s][1] = e4m3_to_f16(two >> 8);
+                sf[s][0] = (float)sh[s][0];
+                sf[s][1] = (float)sh[s][1];
             } else {
                 sm[s] = __uint_as_float((uint32_t)srow[4 * jj + g] << 23);
             }
@@ -172,9 +179,12 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
             const Frag af = __builtin_bit_cast(Frag, aq[jj][j]);
 #pragma unroll
             for (int s = 0; s < kSub; ++s) {
-                if constexpr (NV) {
+                if constexpr (NV && !BF) {
                     const half8 bf = dequant_nvfp4(bq[jj][s][0][j], sh[s][j >> 1]);
                     acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[s], 0, 0, 0);
+                } else if constexpr (A16) {
+                    const bf16x8 bf = dequant_nvfp4_bf16(bq[jj][s][0][j], sf[s][j >> 1]);
+                    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[s], 0, 0, 0);
                 } else {
                     const u32x4 w4 = bq[jj][s][j >> 1];
                     const u32x2 w2 = (j & 1) ? (u32x2){w4.z, w4.w} : (u32x2){w4.x, w4.y};
@@ -196,7 +206,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
         for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const float4_t *>(&s_red[w][s][lane][0]);
         return v;
     };
-    const float sc = NV ? p.a_tscale[0] * p.w_tscale[e] : 1.0f;
+    const float sc = FM == kFmtNV ? p.a_tscale[0] * p.w_tscale[e] : (A16 ? p.w_tscale[e] : 1.0f);
     if (GATE_UP) {
         // waves 0 and 1: gate subtile w with up subtile w + 2 (16 f columns each)
         if (wave < 2) {
@@ -207,7 +217,14 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * g + i;
                 const float hv = swiglu(gv[i] * sc, uv[i] * sc);
-                if (NV) {
+                if (A16) {
+                    // the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
+                    if (m < rows) {
+                        const int64_t o = (int64_t)(p0 + m) * F + n0 + fl;
+                        static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
+                        if (p.o_tap) p.o_tap[o] = hv;
+                    }
+                } else if (NV) {
                     if (m < rows) {
                         p.out_f32[(int64_t)(p0 + m) * F + n0 + fl] = hv;
                         amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
@@ -216,7 +233,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                     s_epi[m][fl] = hv;
                 }
             }
-            if (NV) {
+            if (FM == kFmtNV) {
                 for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
                 if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
             }
@@ -256,25 +273,25 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     }
 }
 
-template <bool NV, bool GATE_UP, int G>
+template <int FM, bool GATE_UP, int G>
 hipError_t launch_g(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
     const int n_tiles_n = GATE_UP ? (a.N / 2) / (kRows / 2) : a.N / kRows;
-    hipLaunchKernelGGL((stream_gemm_kernel<NV, GATE_UP, G>), dim3((unsigned)max_tiles, (unsigned)n_tiles_n),
+    hipLaunchKernelGGL((stream_gemm_kernel<FM, GATE_UP, G>), dim3((unsigned)max_tiles, (unsigned)n_tiles_n),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
-template <bool NV, bool GATE_UP>
+template <int FM, bool GATE_UP>
 hipError_t launch_k(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
     switch (a.K / 512) {
-        case 1: return launch_g<NV, GATE_UP, 1>(a, max_tiles, s);
-        case 2: return launch_g<NV, GATE_UP, 2>(a, max_tiles, s);
-        case 3: return launch_g<NV, GATE_UP, 3>(a, max_tiles, s);
-        case 4: return launch_g<NV, GATE_UP, 4>(a, max_tiles, s);
-        case 5: return launch_g<NV, GATE_UP, 5>(a, max_tiles, s);
-        case 6: return launch_g<NV, GATE_UP, 6>(a, max_tiles, s);
-        case 7: return launch_g<NV, GATE_UP, 7>(a, max_tiles, s);
-        case 8: return launch_g<NV, GATE_UP, 8>(a, max_tiles, s);
+        case 1: return launch_g<FM, GATE_UP, 1>(a, max_tiles, s);
+        case 2: return launch_g<FM, GATE_UP, 2>(a, max_tiles, s);
+        case 3: return launch_g<FM, GATE_UP, 3>(a, max_tiles, s);
+        case 4: return launch_g<FM, GATE_UP, 4>(a, max_tiles, s);
+        case 5: return launch_g<FM, GATE_UP, 5>(a, max_tiles, s);
+        case 6: return launch_g<FM, GATE_UP, 6>(a, max_tiles, s);
+        case 7: return launch_g<FM, GATE_UP, 7>(a, max_tiles, s);
+        case 8: return launch_g<FM, GATE_UP, 8>(a, max_tiles, s);
         default: return hipErrorInvalidValue;
     }
 }
@@ -285,9 +302,13 @@ bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up) {
     return K % 512 == 0 && K / 512 >= 1 && K / 512 <= 8 && (gate_up ? (N / 2) % 32 == 0 : N % 64 == 0);
 }
 
-hipError_t launch_stream_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s) {
-    if (nvfp4) return gate_up ? launch_k<true, true>(a, max_tiles, s) : launch_k<true, false>(a, max_tiles, s);
-    return gate_up ? launch_k<false, true>(a, max_tiles, s) : launch_k<false, false>(a, max_tiles, s);
+hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s) {
+    switch (fm) {
+        case kFmtNV: return gate_up ? launch_k<kFmtNV, true>(a, max_tiles, s) : launch_k<kFmtNV, false>(a, max_tiles, s);
+        case kFmtMX8: return gate_up ? launch_k<kFmtMX8, true>(a, max_tiles, s) : launch_k<kFmtMX8, false>(a, max_tiles, s);
+        case kFmtA16: return gate_up ? launch_k<kFmtA16, true>(a, max_tiles, s) : launch_k<kFmtA16, false>(a, max_tiles, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe

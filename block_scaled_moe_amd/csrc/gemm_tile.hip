@@ -57,12 +57,15 @@ static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thr
 #ifndef MOE_TILE_NS_MX
 #define MOE_TILE_NS_MX 2
 #endif
+#ifndef MOE_TILE_NS_A16
+#define MOE_TILE_NS_A16 4
+#endif
 
 // 32-row weight subtiles per wave in N: NVFP4 4 (its expansion costs twice MXFP8's VALU,
 // so each activation fragment feeds more MFMAs; 234 registers, two waves per SIMD),
-// MXFP8 2 (three waves per SIMD; at 4 it spills)
-template <bool NV>
-constexpr int tile_ns() { return NV ? MOE_TILE_NS_NV : MOE_TILE_NS_MX; }
+// MXFP8 2 (three waves per SIMD; at 4 it spills), W4A16 as NVFP4
+template <int FM>
+constexpr int tile_ns() { return FM == kFmtMX8 ? MOE_TILE_NS_MX : (FM == kFmtNV ? MOE_TILE_NS_NV : MOE_TILE_NS_A16); }
 
 // floats per row of a wave's MXFP8 epilogue tile in LDS: 16 NS columns plus one, so
 // lanes reading rows at the same column fall on different banks
@@ -71,19 +74,22 @@ constexpr int kEpiStride() { return 16 * NS + 1; }
 
 // LDS of one workgroup: the double-buffered activation tile, or for the MXFP8 gate_up
 // epilogue the four waves' SwiGLU tiles if larger
-template <bool NV, bool GATE_UP, int NS>
+template <int FM, bool GATE_UP, int NS>
 constexpr int tile_smem_bytes() {
-    return (!NV && GATE_UP && 4 * kBM * kEpiStride<NS>() * 4 > 2 * kAStage) ? 4 * kBM * kEpiStride<NS>() * 4
+    return (FM == kFmtMX8 && GATE_UP && 4 * kBM * kEpiStride<NS>() * 4 > 2 * kAStage) ? 4 * kBM * kEpiStride<NS>() * 4
                                                                              : 2 * kAStage;
 }
 
-template <bool NV, bool GATE_UP, int NS>
+template <int FM, bool GATE_UP, int NS>
 __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) tile_gemm_kernel(const GemmArgs p) {
-    using Frag = typename std::conditional<NV, half8, bf16x8>::type;
+    constexpr bool NV = FM != kFmtMX8;  // NVFP4 weights (W4A4 or W4A16)
+    constexpr bool BF = FM != kFmtNV;   // bf16 operands and MFMA
+    constexpr bool A16 = FM == kFmtA16;
+    using Frag = typename std::conditional<BF, bf16x8, half8>::type;
     constexpr int BN = 128 * NS;        // weight rows per workgroup
     constexpr int CV = NV ? 1 : 2;      // 16-byte code loads per weight row per lane per chunk
     static_assert(NS % 2 == 0, "gate_up pairs subtiles");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[tile_smem_bytes<NV, GATE_UP, NS>()];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[tile_smem_bytes<FM, GATE_UP, NS>()];
 
     const int K = p.K, N = p.N, F = N / 2;
     const int NB = GATE_UP ? F / (BN / 2) : N / BN;
@@ -215,11 +221,18 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
 #pragma unroll
                 for (int ns = 0; ns < NS; ++ns) {
                     if constexpr (NV) {
-                        const _Float16 sc = sc_nv[ns][s >> 1];
-                        const half8 bf = dequant_nvfp4(wcode[j][ns][0][s], sc);
+                        if constexpr (A16) {
+                            const bf16x8 bf = dequant_nvfp4_bf16(wcode[j][ns][0][s], (float)sc_nv[ns][s >> 1]);
 #pragma unroll
-                        for (int ms = 0; ms < kMS; ++ms)
-                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                            for (int ms = 0; ms < kMS; ++ms)
+                                acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                        } else {
+                            const _Float16 sc = sc_nv[ns][s >> 1];
+                            const half8 bf = dequant_nvfp4(wcode[j][ns][0][s], sc);
+#pragma unroll
+                            for (int ms = 0; ms < kMS; ++ms)
+                                acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                        }
                     } else {
                         const u32x4 q = wcode[j][ns][s >> 1];
                         const u32x2 cw = (s & 1) ? (u32x2){q.z, q.w} : (u32x2){q.x, q.y};
@@ -241,8 +254,26 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
 #undef MOE_LOAD_W
 
     // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
-    const float scl = NV ? p.a_tscale[0] * p.w_tscale[e] : 1.0f;
-    if (GATE_UP && NV) {
+    const float scl = FM == kFmtNV ? p.a_tscale[0] * p.w_tscale[e] : (A16 ? p.w_tscale[e] : 1.0f);
+    if (GATE_UP && A16) {
+        // W4A16: the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
+#pragma unroll
+        for (int q = 0; q < NS / 2; ++q) {
+            const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+#pragma unroll
+            for (int ms = 0; ms < kMS; ++ms)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                    if (m < rows) {
+                        const int64_t o = (int64_t)(p0 + m) * F + f;
+                        const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
+                        static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
+                        if (p.o_tap) p.o_tap[o] = hv;
+                    }
+                }
+        }
+    } else if (GATE_UP && NV) {
         uint32_t amax = 0;
 #pragma unroll
         for (int q = 0; q < NS / 2; ++q) {
@@ -315,14 +346,14 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
     }
 }
 
-template <bool NV, bool GATE_UP>
+template <int FM, bool GATE_UP>
 hipError_t launch_t(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
-    constexpr int NS = tile_ns<NV>();
+    constexpr int NS = tile_ns<FM>();
     constexpr int BN = 128 * NS;
     const int64_t nb = GATE_UP ? (a.N / 2) / (BN / 2) : a.N / BN;
     const int64_t items = (int64_t)(max_tiles + kGroup - 1) / kGroup * kGroup * nb;
     const int64_t grid = (items + 7) / 8 * 8;
-    hipLaunchKernelGGL((tile_gemm_kernel<NV, GATE_UP, NS>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((tile_gemm_kernel<FM, GATE_UP, NS>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
@@ -331,14 +362,19 @@ hipError_t launch_t(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
 int32_t tile_gemm_bm() { return kBM; }
 
 bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up) {
-    // both formats must fit, since the plan picks one kernel family per layer shape
-    const int bn = 128 * (MOE_TILE_NS_NV > MOE_TILE_NS_MX ? MOE_TILE_NS_NV : MOE_TILE_NS_MX);
+    // every format must fit, since the plan picks one kernel family per layer shape
+    constexpr int ns_max = MOE_TILE_NS_NV > MOE_TILE_NS_MX ? MOE_TILE_NS_NV : MOE_TILE_NS_MX;
+    const int bn = 128 * (ns_max > MOE_TILE_NS_A16 ? ns_max : MOE_TILE_NS_A16);
     return K % (MOE_TILE_WR * kKC) == 0 && (gate_up ? (N / 2) % (bn / 2) == 0 : N % bn == 0);
 }
 
-hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s) {
-    if (nvfp4) return gate_up ? launch_t<true, true>(a, max_tiles, s) : launch_t<true, false>(a, max_tiles, s);
-    return gate_up ? launch_t<false, true>(a, max_tiles, s) : launch_t<false, false>(a, max_tiles, s);
+hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s) {
+    switch (fm) {
+        case kFmtNV: return gate_up ? launch_t<kFmtNV, true>(a, max_tiles, s) : launch_t<kFmtNV, false>(a, max_tiles, s);
+        case kFmtMX8: return gate_up ? launch_t<kFmtMX8, true>(a, max_tiles, s) : launch_t<kFmtMX8, false>(a, max_tiles, s);
+        case kFmtA16: return gate_up ? launch_t<kFmtA16, true>(a, max_tiles, s) : launch_t<kFmtA16, false>(a, max_tiles, s);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace moe

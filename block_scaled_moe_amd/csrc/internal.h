@@ -79,6 +79,16 @@ bool permute_small_ok(int32_t T, int32_t k, int32_t n_loc);
 hipError_t launch_permute_small(const PermuteArgs &a, hipStream_t s);
 
 // ---- grouped GEMMs (gemm.hip)
+// Operand formats of the 16-bit-expansion kernels.
+//  kFmtNV:  NVFP4 weights and activations (W4A4): fp16 operands, f16 MFMA
+//  kFmtMX8: MXFP8 weights and activations: bf16 operands, bf16 MFMA
+//  kFmtA16: NVFP4 weights with bf16 activations (W4A16; vLLM recipe
+//           "thinkingmachines/Inkling-Small", section "Variants": the weights are
+//           dequantised to bf16 on the fly): bf16 operands, bf16 MFMA. A bf16
+//           activation is not exact in fp16 in general (range, and 8 significant bits
+//           below 2^-14), so the weights are expanded to bf16 instead.
+constexpr int kFmtNV = 0, kFmtMX8 = 1, kFmtA16 = 2;
+
 struct GemmArgs {
     const Ctrl *ctrl;
     const int32_t *tile_expert, *tile_row0, *offsets, *sorted_slot;
@@ -87,31 +97,31 @@ struct GemmArgs {
     int32_t N, K;             // weight matrix [N][K] per expert; gate_up: N = 2F
     int32_t e_begin;          // global index of local expert 0
     // A operand: exact 16-bit values of the quantised activations, [rows][K]
-    const void *a_vals;       // NVFP4: fp16; MXFP8: bf16
+    const void *a_vals;       // NVFP4: fp16; MXFP8: bf16; W4A16: the bf16 activations themselves
     // MXFP4 A operand: the codes themselves, [rows][K/2] and E8M0 scales [rows][K/32]
     const uint8_t *a_codes, *a_scales;
     const float *a_tscale;    // NVFP4: [1] activation tensor scale
     // weights (canonical packed layout, global expert index)
     const uint8_t *w_codes, *w_scales;
-    const float *w_tscale;    // NVFP4: [E]
+    const float *w_tscale;    // NVFP4 and W4A16: [E]
     // outputs
     float *out_f32;           // gate_up NVFP4: SwiGLU [S][F]; down: y [S][N]
     uint32_t *amax_bits;      // gate_up NVFP4: max |SwiGLU|
     uint8_t *o_codes, *o_scales;  // gate_up MXFP8 / MXFP4: quantised SwiGLU [S][F] or [S][F/2], [S][F/32]
-    void *o_vals;             // gate_up MXFP8: exact bf16 values of those codes [S][F]
-    float *o_tap;             // gate_up MXFP8: optional fp32 SwiGLU [S][F]
+    void *o_vals;             // gate_up MXFP8: exact bf16 values of those codes [S][F]; W4A16: bf16 SwiGLU
+    float *o_tap;             // gate_up MXFP8 / MXFP4 / W4A16: optional fp32 SwiGLU [S][F]
 };
 enum class GemmShape { Decode, Prefill };
-hipError_t launch_grouped_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, GemmShape shape,
+hipError_t launch_grouped_gemm(const GemmArgs &a, int fm, bool gate_up, GemmShape shape,
                                int32_t max_tiles, hipStream_t s);
 int32_t gemm_bm(GemmShape shape);
 // prefill-shaped MFMA tiles (gemm_tile.hip): 64-row M-tiles, 256 weight rows per workgroup
 bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up);
 int32_t tile_gemm_bm();  // rows per M-tile of the tile kernels
-hipError_t launch_tile_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);
+hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s);
 // decode-shaped streaming variant (gemm_stream.hip): 16-row M-tiles, K a multiple of 512
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
-hipError_t launch_stream_gemm(const GemmArgs &a, bool nvfp4, bool gate_up, int32_t max_tiles, hipStream_t s);
+hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s);
 
 // native MXFP4 GEMMs on the gfx950 scaled FP4 MFMA (gemm_mx4.hip): 64-row M-tiles (the
 // tile kernels' BM), 256 weight rows per workgroup; K % 64, gate_up F % 128, down N % 256

@@ -39,7 +39,7 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 Plan make_plan(const moe_forward_args *a) {
     Plan p{};
     const int64_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
-    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4, a16 = a->fmt == MOE_FMT_W4A16;
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
     // MXFP4 always runs the scaled-FP4 MFMA kernels, whose M-tiles are the tile kernels' 64 rows
@@ -64,15 +64,16 @@ Plan make_plan(const moe_forward_args *a) {
     p.tile_row0 = take(sizeof(int32_t) * p.max_tiles);
     p.sorted_slot = take(sizeof(int32_t) * TK);
     p.slot_pos = take(sizeof(int32_t) * TK);
-    p.a_codes = take(a->fmt == MOE_FMT_MXFP8 ? T * D : T * D / 2);
-    p.a_scales = take(nv ? T * D / 16 : T * D / 32);
+    // W4A16 keeps the hidden states as they are and its intermediate in bf16 (i16 only)
+    p.a_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? T * D : T * D / 2);
+    p.a_scales = a16 ? 0 : take(nv ? T * D / 16 : T * D / 32);
     p.a_tscale = take(sizeof(float));
-    p.a16 = mx4 ? 0 : take(2 * T * D);  // exact 16-bit values of the hidden-state codes
+    p.a16 = (mx4 || a16) ? 0 : take(2 * T * D);  // exact 16-bit values of the hidden-state codes
     p.inter32 = nv ? take(sizeof(float) * TK * F) : 0;
-    p.i_codes = take(a->fmt == MOE_FMT_MXFP8 ? TK * F : TK * F / 2);
-    p.i_scales = take(nv ? TK * F / 16 : TK * F / 32);
+    p.i_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? TK * F : TK * F / 2);
+    p.i_scales = a16 ? 0 : take(nv ? TK * F / 16 : TK * F / 32);
     p.i_tscale = take(sizeof(float));
-    p.i16 = mx4 ? 0 : take(2 * TK * F);  // exact 16-bit values of the intermediate codes
+    p.i16 = mx4 ? 0 : take(2 * TK * F);  // exact 16-bit values of the intermediate (codes)
     p.y = take(sizeof(float) * TK * D);
     p.total = off;
     return p;
@@ -80,11 +81,11 @@ Plan make_plan(const moe_forward_args *a) {
 
 hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
     if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.max_tiles, s);
-    const bool nv = fmt == MOE_FMT_NVFP4;
-    if (P.tile64) return launch_tile_gemm(g, nv, gate_up, P.max_tiles, s);
+    const int fm = fmt == MOE_FMT_NVFP4 ? kFmtNV : (fmt == MOE_FMT_W4A16 ? kFmtA16 : kFmtMX8);
+    if (P.tile64) return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
     if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
-        return launch_stream_gemm(g, nv, gate_up, P.max_tiles, s);
-    return launch_grouped_gemm(g, nv, gate_up, P.shape, P.max_tiles, s);
+        return launch_stream_gemm(g, fm, gate_up, P.max_tiles, s);
+    return launch_grouped_gemm(g, fm, gate_up, P.shape, P.max_tiles, s);
 }
 
 int32_t check_packed(const moe_packed &w, int32_t fmt, int32_t E, int32_t N, int32_t K) {
@@ -163,7 +164,8 @@ namespace {
 // The size fields alone (what the workspace plan depends on).
 int32_t validate_shape(const moe_forward_args *a) {
     if (!a) return MOE_ERR_INVALID_ARG;
-    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8 && a->fmt != MOE_FMT_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8 && a->fmt != MOE_FMT_MXFP4 && a->fmt != MOE_FMT_W4A16)
+        return MOE_ERR_INVALID_ARG;
     if (a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->E > 4096) return MOE_ERR_INVALID_ARG;
     if (a->top_k < 1 || a->top_k > 8 || a->top_k > a->E) return MOE_ERR_INVALID_ARG;
     if (a->e_begin < 0 || a->e_end <= a->e_begin || a->e_end > a->E) return MOE_ERR_INVALID_ARG;
@@ -184,9 +186,10 @@ int32_t moe_forward_validate(const moe_forward_args *a) {
     if (shape != MOE_OK) return shape;
     if (a->T == 0) return MOE_OK;
     if (!a->h || !a->topk_idx || !a->topk_w || !a->out) return MOE_ERR_INVALID_ARG;
-    int32_t rc = check_packed(a->gate_up, a->fmt, a->E, 2 * a->F, a->D);
+    const int32_t wfmt = a->fmt == MOE_FMT_W4A16 ? MOE_FMT_NVFP4 : a->fmt;  // packed weights' format
+    int32_t rc = check_packed(a->gate_up, wfmt, a->E, 2 * a->F, a->D);
     if (rc != MOE_OK) return rc;
-    rc = check_packed(a->down, a->fmt, a->E, a->D, a->F);
+    rc = check_packed(a->down, wfmt, a->E, a->D, a->F);
     if (rc != MOE_OK) return rc;
     if (!aligned16(a->h) || !aligned16(a->topk_idx) || !aligned16(a->topk_w) || !aligned16(a->out) ||
         (a->h_amax && !aligned16(a->h_amax)))
@@ -210,7 +213,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     if (((uintptr_t)a->workspace & 255u) != 0) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = static_cast<uint8_t *>(a->workspace);
-    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4, a16 = a->fmt == MOE_FMT_W4A16;
     const int32_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
     Ctrl *ctrl = reinterpret_cast<Ctrl *>(ws + P.ctrl);
     auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
@@ -256,6 +259,8 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
                                        F32(P.a_tscale), s));
     } else if (mx4) {
         MOE_TRY(launch_quant_act_mxfp4(a->h, T, D, U8(P.a_codes), U8(P.a_scales), s));
+    } else if (a16) {
+        // W4A16: the GEMM reads the bf16 hidden states directly
     } else {
         MOE_TRY(launch_quant_act_mxfp8(a->h, T, D, U8(P.a_codes), U8(P.a_scales),
                                        reinterpret_cast<uint16_t *>(ws + P.a16), s));
@@ -276,9 +281,9 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     g.w_codes = a->gate_up.codes;
     g.w_scales = a->gate_up.scales;
     g.w_tscale = a->gate_up.tensor_scale;
-    g.a_vals = mx4 ? nullptr : ws + P.a16;
-    g.a_codes = U8(P.a_codes);
-    g.a_scales = U8(P.a_scales);
+    g.a_vals = mx4 ? nullptr : (a16 ? static_cast<const void *>(a->h) : ws + P.a16);
+    g.a_codes = a16 ? nullptr : U8(P.a_codes);
+    g.a_scales = a16 ? nullptr : U8(P.a_scales);
     if (nv) {
         g.a_tscale = F32(P.a_tscale);
         g.out_f32 = F32(P.inter32);
@@ -290,9 +295,9 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         MOE_TRY(launch_quant_inter_nvfp4(F32(P.inter32), TK, F, ctrl, U8(P.i_codes), U8(P.i_scales), F16(P.i16),
                                          F32(P.i_tscale), s));
     } else {
-        g.o_codes = U8(P.i_codes);
+        g.o_codes = a16 ? nullptr : U8(P.i_codes);
         g.o_vals = mx4 ? nullptr : ws + P.i16;
-        g.o_scales = U8(P.i_scales);
+        g.o_scales = a16 ? nullptr : U8(P.i_scales);
         g.o_tap = a->taps ? a->taps->inter : nullptr;
         MOE_TRY(mark(MOE_EV_GATE_UP));
         MOE_TRY(run_gemm(g, a->fmt, true, P, s));
@@ -314,8 +319,8 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     d.o_tap = nullptr;
     d.o_vals = nullptr;
     d.a_vals = mx4 ? nullptr : ws + P.i16;
-    d.a_codes = U8(P.i_codes);
-    d.a_scales = U8(P.i_scales);
+    d.a_codes = a16 ? nullptr : U8(P.i_codes);
+    d.a_scales = a16 ? nullptr : U8(P.i_scales);
     d.a_tscale = nv ? F32(P.i_tscale) : nullptr;
     MOE_TRY(mark(MOE_EV_DOWN));
     MOE_TRY(run_gemm(d, a->fmt, false, P, s));
@@ -335,15 +340,21 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         MOE_TRY(cp(t->offsets, ws + P.offsets, sizeof(int32_t) * (P.n_loc + 1)));
         MOE_TRY(cp(t->sorted_slot, ws + P.sorted_slot, sizeof(int32_t) * (size_t)TK));
         const bool mx8 = a->fmt == MOE_FMT_MXFP8;
-        MOE_TRY(cp(t->a_codes, ws + P.a_codes, mx8 ? (size_t)T * D : (size_t)T * D / 2));
-        MOE_TRY(cp(t->a_scales, ws + P.a_scales, nv ? (size_t)T * D / 16 : (size_t)T * D / 32));
+        if (!a16) {
+            MOE_TRY(cp(t->a_codes, ws + P.a_codes, mx8 ? (size_t)T * D : (size_t)T * D / 2));
+            MOE_TRY(cp(t->a_scales, ws + P.a_scales, nv ? (size_t)T * D / 16 : (size_t)T * D / 32));
+        }
         if (nv) {
             MOE_TRY(cp(t->a_tscale, ws + P.a_tscale, sizeof(float)));
             MOE_TRY(cp(t->inter, ws + P.inter32, sizeof(float) * (size_t)TK * F));
             MOE_TRY(cp(t->inter_tscale, ws + P.i_tscale, sizeof(float)));
         }
-        MOE_TRY(cp(t->inter_codes, ws + P.i_codes, mx8 ? (size_t)TK * F : (size_t)TK * F / 2));
-        MOE_TRY(cp(t->inter_scales, ws + P.i_scales, nv ? (size_t)TK * F / 16 : (size_t)TK * F / 32));
+        if (a16) {
+            MOE_TRY(cp(t->inter_codes, ws + P.i16, 2 * (size_t)TK * F));  // bf16 bit patterns
+        } else {
+            MOE_TRY(cp(t->inter_codes, ws + P.i_codes, mx8 ? (size_t)TK * F : (size_t)TK * F / 2));
+            MOE_TRY(cp(t->inter_scales, ws + P.i_scales, nv ? (size_t)TK * F / 16 : (size_t)TK * F / 32));
+        }
         MOE_TRY(cp(t->y, ws + P.y, sizeof(float) * (size_t)TK * D));
     }
     return MOE_OK;

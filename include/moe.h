@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -49,10 +49,13 @@ extern "C" {
 
 /* Expert formats (recipe "Overview": NVFP4 in layers 0-39, MXFP8 in 40-47; MXFP4 is
  * the OCP MXFP4 W4A4 variant for AMD Instinct in the vLLM recipe
- * "thinkingmachines/Inkling-Small", section "Variants"). */
+ * "thinkingmachines/Inkling-Small", section "Variants"; W4A16 is the NVFP4 checkpoint
+ * run with bf16 activations, its weights dequantised on the fly, same section).
+ * MOE_FMT_W4A16 is a moe_forward format only: its packed weights are MOE_FMT_NVFP4. */
 #define MOE_FMT_NVFP4 1
 #define MOE_FMT_MXFP8 2
 #define MOE_FMT_MXFP4 3
+#define MOE_FMT_W4A16 4
 
 /*
  * Packed expert weights of one matrix kind for E experts, each logically [N][K]
@@ -93,11 +96,13 @@ typedef struct moe_taps {
     int32_t *counts;       /* [n_loc] slots per local expert                        */
     int32_t *offsets;      /* [n_loc + 1] exclusive prefix sum of counts            */
     int32_t *sorted_slot;  /* [T*top_k] slot id t*top_k + j at each sorted position  */
-    uint8_t *a_codes;      /* hidden-state codes [T][D/2] (NVFP4, MXFP4) or [T][D]  */
+    uint8_t *a_codes;      /* hidden-state codes [T][D/2] (NVFP4, MXFP4) or [T][D]
+                              (MXFP8); W4A16 writes neither these nor a_scales     */
     uint8_t *a_scales;     /* [T][D/16] E4M3 (NVFP4) or [T][D/32] E8M0 (MX formats) */
     float *a_tscale;       /* [1] NVFP4 hidden-state tensor scale                   */
     float *inter;          /* [T*top_k][F] fp32 SwiGLU output before quantisation   */
-    uint8_t *inter_codes;  /* [T*top_k][F/2] (NVFP4, MXFP4) or [T*top_k][F]         */
+    uint8_t *inter_codes;  /* [T*top_k][F/2] (NVFP4, MXFP4) or [T*top_k][F] (MXFP8);
+                              W4A16: bf16 bit patterns [T*top_k][F], 2 bytes each */
     uint8_t *inter_scales; /* [T*top_k][F/16] (NVFP4) or [T*top_k][F/32]            */
     float *inter_tscale;   /* [1] NVFP4 intermediate tensor scale                   */
     float *y;              /* [T*top_k][D] fp32 down projection per slot (unweighted) */
@@ -114,7 +119,7 @@ typedef struct moe_taps {
 
 /* Arguments of moe_forward. */
 typedef struct moe_forward_args {
-    int32_t fmt;              /* MOE_FMT_NVFP4, MOE_FMT_MXFP8 or MOE_FMT_MXFP4          */
+    int32_t fmt;              /* MOE_FMT_NVFP4, _MXFP8, _MXFP4 or _W4A16                */
     int32_t T, D, F, E;       /* tokens, d_model, d_ff, routed experts                  */
     int32_t top_k;            /* experts per token (8)                                  */
     int32_t e_begin, e_end;   /* local expert range [e_begin, e_end) computed here      */
@@ -184,15 +189,20 @@ size_t moe_forward_workspace_bytes(const moe_forward_args *a);
  * MoE layer forward over the local experts [e_begin, e_end):
  *  1. slots (t, j) with topk_idx[t][j] local are grouped by expert, stable in t*top_k+j;
  *  2. hidden states are quantised once per token to the layer's format (NVFP4 with
- *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block);
+ *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block); W4A16 uses the
+ *     bf16 hidden states as they are;
  *  3. gate_up GEMM per expert (fp32 accumulation; NVFP4 sums are multiplied by
- *     fl32(s_h * s_gate_up[e])), then h = SwiGLU = g * u / (1 + exp(-g));
+ *     fl32(s_h * s_gate_up[e]), W4A16 sums by s_gate_up[e]), then
+ *     h = SwiGLU = g * u / (1 + exp(-g));
  *  4. h is quantised to the layer's format (NVFP4: one tensor scale over all S rows);
- *  5. down GEMM per expert (NVFP4: times fl32(s_inter * s_down[e])) -> y fp32;
+ *     W4A16 rounds it to bf16 (nearest, ties to even);
+ *  5. down GEMM per expert (NVFP4: times fl32(s_inter * s_down[e]); W4A16: times
+ *     s_down[e]) -> y fp32;
  *  6. out[t] = sum over the token's local slots, j ascending, of topk_w[t][j] * y.
  * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), and for MXFP4 also D
  * a multiple of 256 (its GEMMs run on the scaled FP4 MFMA in 256-row weight tiles),
- * 1 <= top_k <= 8, 0 <= e_begin < e_end <= E. gate_up/down must match fmt and shapes.
+ * 1 <= top_k <= 8, 0 <= e_begin < e_end <= E. gate_up/down must match fmt (NVFP4 for
+ * W4A16) and shapes.
  * T = 0 is a no-op.
  */
 int32_t moe_forward(const moe_forward_args *a, void *stream);

@@ -159,7 +159,7 @@ class Workload:
     """One synthetic MoE-layer workload (shapes, formats, value recipe)."""
     index: int
     name: str
-    fmt: str            # "nvfp4", "mxfp8" or "mxfp4"
+    fmt: str            # "nvfp4", "mxfp8", "mxfp4" or "w4a16"
     T: int              # tokens
     D: int              # d_model
     F: int              # d_ff
@@ -234,6 +234,10 @@ WORKLOADS = [
     Workload(5, "decode-mxfp4", "mxfp4", T=64, D=4096, F=2560, E=384, seed=5),
     Workload(6, "prefill-mxfp4-ep4", "mxfp4", T=8192, D=4096, F=2560, E=384,
              e_begin=0, e_end=96, seed=6),
+    # NVFP4 weights with bf16 activations (W4A16) at the same two shapes
+    Workload(7, "decode-w4a16", "w4a16", T=64, D=4096, F=2560, E=384, seed=7),
+    Workload(8, "prefill-w4a16-ep4", "w4a16", T=8192, D=4096, F=2560, E=384,
+             e_begin=0, e_end=96, seed=8),
 ]
 
 

@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the six benchmarked workloads, through the same calls
+"""GPU parity at the full sizes of the eight benchmarked workloads, through the same calls
 and launch configuration that bench.py times (moe.route + moe.Layer.forward).
 
 Whole-batch, bit-exact: top-k indices of every token, max |h|, the permutation, every
@@ -33,6 +33,7 @@ def _expert_reference(wl, e, a_rows, a_ts, inter_codes, inter_scales, inter_ts):
     """fp64 gate_up -> SwiGLU (rounded to fp32) of the given dequantised hidden rows, and
     the down projection of the given intermediate codes, for expert e (oracle weights)."""
     nv = wl.fmt == "nvfp4"
+    a16 = wl.fmt == "w4a16"
     F = wl.F
     gu = oracle.quantize_weights(wl.fmt, wl.gate_up_master(e))
     dn = oracle.quantize_weights(wl.fmt, wl.down_master(e))
@@ -42,24 +43,29 @@ def _expert_reference(wl, e, a_rows, a_ts, inter_codes, inter_scales, inter_ts):
         s_gu = np.float32(np.float32(a_ts) * gu["tensor_scale"][0])
         s_dn = np.float32(np.float32(inter_ts) * dn["tensor_scale"][0])
         ai = oracle.dequant_nvfp4(inter_codes, inter_scales, 1.0, with_tensor=False)
+    elif a16:
+        wg = oracle.dequant_nvfp4(gu["codes"][0], gu["scales"][0], 1.0, with_tensor=False)
+        wd = oracle.dequant_nvfp4(dn["codes"][0], dn["scales"][0], 1.0, with_tensor=False)
+        s_gu, s_dn = np.float32(gu["tensor_scale"][0]), np.float32(dn["tensor_scale"][0])
+        ai = synth.bf16_to_f32(np.asarray(inter_codes).view(np.uint16)).astype(np.float64)
     else:
         wg = _dequant_mx(wl.fmt, gu["codes"][0], gu["scales"][0])
         wd = _dequant_mx(wl.fmt, dn["codes"][0], dn["scales"][0])
         ai = _dequant_mx(wl.fmt, inter_codes, inter_scales)
     acc = a_rows @ wg.T                       # exact products, fp64 sums
     g = acc.astype(np.float32)
-    if nv:
-        g = (g * s_gu).astype(np.float32)     # fl32(fl32(sum) * fl32(s_a * s_w))
+    if nv or a16:
+        g = (g * s_gu).astype(np.float32)     # fl32(fl32(sum) * fl32(s_a * s_w)), W4A16 s_w alone
     gate, up = g[:, :F].astype(np.float64), g[:, F:].astype(np.float64)
     inter = (gate * up / (1.0 + np.exp(-gate))).astype(np.float32)
     y = (ai @ wd.T).astype(np.float32)
-    if nv:
+    if nv or a16:
         y = (y * s_dn).astype(np.float32)
     return gu, dn, inter, y
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6], ids=lambda i: synth.WORKLOADS[i].name)
+@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6, 7, 8], ids=lambda i: synth.WORKLOADS[i].name)
 def test_fullsize_workload(i):
     wl = synth.WORKLOADS[i]
     T, D, F, E, k = wl.T, wl.D, wl.F, wl.E, wl.k
@@ -96,17 +102,20 @@ def test_fullsize_workload(i):
 
     # hidden-state codes (all tokens)
     hf = synth.bf16_to_f32(h)
+    a16 = wl.fmt == "w4a16"
+    a_ts = None
     if nv:
         a_c, a_s, a_ts = oracle.quant_nvfp4(hf)
         assert np.float32(tp["a_tscale"][0]) == a_ts
-    else:
+    elif not a16:
         a_c, a_s = oracle.quant_mxfp4(hf) if wl.fmt == "mxfp4" else oracle.quant_mxfp8(hf)
-        a_ts = None
-    assert np.array_equal(tp["a_codes"], a_c) and np.array_equal(tp["a_scales"], a_s), "hidden codes differ"
+    if not a16:  # W4A16 keeps the hidden states in bf16
+        assert np.array_equal(tp["a_codes"], a_c) and np.array_equal(tp["a_scales"], a_s), "hidden codes differ"
 
     # intermediate codes given the GPU's fp32 values (all S rows)
     i_ts = tp["inter_tscale"][0] if nv else None
-    check_intermediate_codes(wl.fmt, tp["inter"][:S], tp["inter_codes"][:S], tp["inter_scales"][:S], i_ts)
+    i_sc = tp["inter_scales"] if "inter_scales" in tp else None
+    check_intermediate_codes(wl.fmt, tp["inter"][:S], tp["inter_codes"][:S], None if i_sc is None else i_sc[:S], i_ts)
 
     # ---- expert arithmetic on sampled rows of three experts
     live = np.nonzero(counts)[0]
@@ -116,10 +125,14 @@ def test_fullsize_workload(i):
         p0, p1 = int(offsets[el]), int(offsets[el + 1])
         rows = np.unique(np.linspace(p0, p1 - 1, min(ROWS_PER_EXPERT, p1 - p0)).round().astype(np.int64))
         tok = ss[rows] // k
-        a_rows = (oracle.dequant_nvfp4(a_c[tok], a_s[tok], 1.0, with_tensor=False) if nv
-                  else _dequant_mx(wl.fmt, a_c[tok], a_s[tok]))
+        if a16:
+            a_rows = hf[tok].astype(np.float64)
+        elif nv:
+            a_rows = oracle.dequant_nvfp4(a_c[tok], a_s[tok], 1.0, with_tensor=False)
+        else:
+            a_rows = _dequant_mx(wl.fmt, a_c[tok], a_s[tok])
         o_gu, o_dn, inter_ref, y_ref = _expert_reference(wl, e, a_rows, a_ts, tp["inter_codes"][rows],
-                                                         tp["inter_scales"][rows], i_ts)
+                                                         None if i_sc is None else i_sc[rows], i_ts)
         # packed weights of this expert, bit-exact after undoing the tiling
         for dev_w, ref in ((gu, o_gu), (dn, o_dn)):
             assert np.array_equal(untile(host(dev_w.codes[e:e + 1])), ref["codes"]), f"expert {e} codes differ"
