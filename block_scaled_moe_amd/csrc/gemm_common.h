@@ -84,6 +84,36 @@ __device__ __forceinline__ void store_dequant_mxfp8_32(void *dst, const uint32_t
     for (int q = 0; q < 4; ++q) d[q] = dequant_mxfp8((u32x2){cw[2 * q], cw[2 * q + 1]}, scale);
 }
 
+// Work item w of a grouped GEMM's (M-tile, N-block) grid, expert-major: the items of one
+// local expert are consecutive, and within it its M-tiles go in groups of up to G, each
+// group sweeping every N-block (N-block outer, the group's tiles inner). Dealt to the
+// XCDs in contiguous ranges, an expert's weight panel is fetched from HBM once per group
+// and served to the group's other tiles by that XCD's L2, and a group's activation rows
+// stay in L2 across its N-blocks. (Groups of G consecutive tiles regardless of expert
+// re-fetched every panel a group straddling two experts touched: about twice the
+// algorithmic weight traffic at prefill; one group per expert re-read a hot expert's
+// activation rows once per N-block.) The tile list holds an expert's tiles
+// consecutively, tile t starting at sorted row offsets[el] + (t - t0) bm, so the
+// expert's first tile t0 and tile count te follow from any one of its tiles.
+// Returns false for w past the n_tiles * NB items.
+template <int G>
+__device__ __forceinline__ bool expert_major_item(int w, int NB, int bm, int n_tiles, const int32_t *tile_expert,
+                                                  const int32_t *tile_row0, const int32_t *offsets, int &tile,
+                                                  int &nb) {
+    if (w >= n_tiles * NB) return false;
+    const int tq = w / NB;  // a tile of the expert that owns item w
+    const int el = tile_expert[tq];
+    const int o0 = offsets[el];
+    const int t0 = tq - (tile_row0[tq] - o0) / bm;
+    const int te = (offsets[el + 1] - o0 + bm - 1) / bm;
+    const int local = w - NB * t0;             // < te * NB
+    const int g = local / (G * NB), r = local % (G * NB);
+    const int gs = min(G, te - g * G);         // tiles in group g (the last may be short)
+    tile = t0 + g * G + r % gs;
+    nb = r / gs;
+    return true;
+}
+
 // SwiGLU g * u / (1 + exp(-g)) in fp32 from the hardware exp2 and reciprocal (about
 // 1 ulp each). Rounding -g log2(e) adds about |g| 2^-24 relative error to exp(-g),
 // which reaches the result weighted by exp(-g) / (1 + exp(-g)): the result is within

@@ -23,7 +23,8 @@
 //    each lane loads its weight operands straight from global memory into a four-chunk
 //    register ring (a 32 x 64 weight block is 1 KiB contiguous); one barrier per four
 //    chunks;
-//  - work items are grouped and dealt to the 8 XCDs as in the tile kernels;
+//  - work items are ordered expert-major and dealt to the 8 XCDs in contiguous ranges, as
+//    in the tile kernels;
 //  - gate_up epilogue: SwiGLU in fp32, then each wave's 64 x 32 tile goes through LDS and
 //    lane r quantises row r's 32-block to MXFP4 (16-byte code store, one scale byte).
 // 32x32x64 operand layout (checked on gfx950 against an exact product): lane l holds row
@@ -69,16 +70,13 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
 
     // ---- work item of this workgroup (XCD-contiguous ranges, as in the tile kernels)
     const int n_tiles = p.ctrl->n_tiles;
-    const int total = (n_tiles + kGroup - 1) / kGroup * kGroup * NB;
-    const int per_xcd = (total + 7) / 8;
+    const int per_xcd = (n_tiles * NB + 7) / 8;
     const int b = blockIdx.x;
     if ((b >> 3) >= per_xcd) return;
-    const int w = (b & 7) * per_xcd + (b >> 3);
-    if (w >= total) return;
-    const int grp = w / (kGroup * NB), rem = w % (kGroup * NB);
-    const int nb = rem / kGroup;
-    const int tile = grp * kGroup + rem % kGroup;
-    if (tile >= n_tiles) return;
+    int tile, nb;
+    if (!expert_major_item<kGroup>((b & 7) * per_xcd + (b >> 3), NB, kBM, n_tiles, p.tile_expert, p.tile_row0, p.offsets,
+                           tile, nb))
+        return;
 
     const int el = p.tile_expert[tile];
     const int p0 = p.tile_row0[tile];
@@ -283,7 +281,7 @@ bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up) {
 
 hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s) {
     const int64_t nb = gate_up ? (a.N / 2) / (kBN / 2) : a.N / kBN;
-    const int64_t items = (int64_t)(max_tiles + kGroup - 1) / kGroup * kGroup * nb;
+    const int64_t items = (int64_t)max_tiles * nb;
     const int64_t grid = (items + 7) / 8 * 8;
     if (gate_up)
         hipLaunchKernelGGL((mx4_gemm_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);

@@ -20,9 +20,9 @@
 //    measured faster than a deeper ring at two (and 128-row tiles at one);
 //  - gate_up tiles pair gate row f with up row F + f in the same lane and accumulator
 //    slot, so SwiGLU needs no data exchange;
-//  - work items (M-tile, N-block) are ordered in groups of 4 consecutive M-tiles, N-block
-//    next, and dealt to the 8 XCDs in contiguous ranges, so one XCD's L2 holds the
-//    activation rows of a few M-tiles while it sweeps their weight rows once.
+//  - work items (M-tile, N-block) are ordered expert-major (gemm_common.h) and dealt to
+//    the 8 XCDs in contiguous ranges, so one XCD's L2 serves an expert's weight panel to
+//    all of its M-tiles and the activation rows of those tiles across its N-blocks.
 // 32x32x16 operand layout (measured on gfx950): A lane l holds row l%32, k 8(l/32)..+7;
 // B lane l holds k 8(l/32)..+7 of column l%32; accumulator v of lane l is row
 // 8(v/4) + 4(l/32) + v%4, column l%32.
@@ -96,16 +96,13 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
 
     // ---- work item of this workgroup (XCD-contiguous ranges; see the header)
     const int n_tiles = p.ctrl->n_tiles;
-    const int total = (n_tiles + kGroup - 1) / kGroup * kGroup * NB;
-    const int per_xcd = (total + 7) / 8;
+    const int per_xcd = (n_tiles * NB + 7) / 8;
     const int b = blockIdx.x;
     if ((b >> 3) >= per_xcd) return;
-    const int w = (b & 7) * per_xcd + (b >> 3);
-    if (w >= total) return;
-    const int grp = w / (kGroup * NB), rem = w % (kGroup * NB);
-    const int nb = rem / kGroup;
-    const int tile = grp * kGroup + rem % kGroup;
-    if (tile >= n_tiles) return;
+    int tile, nb;
+    if (!expert_major_item<kGroup>((b & 7) * per_xcd + (b >> 3), NB, kBM, n_tiles, p.tile_expert, p.tile_row0, p.offsets,
+                           tile, nb))
+        return;
 
     const int el = p.tile_expert[tile];
     const int p0 = p.tile_row0[tile];
@@ -351,7 +348,7 @@ hipError_t launch_t(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
     constexpr int NS = tile_ns<FM>();
     constexpr int BN = 128 * NS;
     const int64_t nb = GATE_UP ? (a.N / 2) / (BN / 2) : a.N / BN;
-    const int64_t items = (int64_t)(max_tiles + kGroup - 1) / kGroup * kGroup * nb;
+    const int64_t items = (int64_t)max_tiles * nb;
     const int64_t grid = (items + 7) / 8 * 8;
     hipLaunchKernelGGL((tile_gemm_kernel<FM, GATE_UP, NS>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
