@@ -47,7 +47,7 @@ hipError_t launch_quant_inter_nvfp4(const float *x, int32_t max_rows, int32_t F,
 struct RoutePlan {
     bool screen;          // MFMA screening + exact candidates (large T), else all exact
     int32_t Ep, n_parts;  // padded expert count; 64-wide K blocks of the weight norms
-    size_t off_wk8, off_logits, off_wpart, off_hn, off_wn, bytes;
+    size_t off_wk8, off_exact, off_logits, off_wpart, off_hn, off_wn, bytes;
 };
 RoutePlan route_plan(int32_t T, int32_t D, int32_t E);
 // logits_out: fp32 [T][E] exact logits, or NULL; amax_bits: max |h| (fp32 bits, the

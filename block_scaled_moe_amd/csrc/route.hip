@@ -77,55 +77,61 @@ __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, 
     if (wpart) wpart[(int64_t)blockIdx.y * Ep + e] = ss;
 }
 
-// ---- exact logits and top-k: a workgroup = one token x all experts (Ep / 64 waves),
-// one chain per lane, k ascending. The token's h row is staged once in LDS as fp32 (all
-// lanes read the same address, a broadcast); the weights stream from the L2-resident
-// bf16 copy through a four-block register ring (blocks of 32 k, loaded three blocks
-// ahead). The logits meet in LDS, where wave 0 selects the top k (k rounds of a
-// wave-wide arg-max) unless idx is NULL.
-template <int PER>  // logits per lane of wave 0: Ep / 64
-__global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
-                                                            const uint16_t *__restrict__ h,
-                                                            const uint16_t *__restrict__ wk8,
-                                                            const float *__restrict__ bias,
-                                                            float *__restrict__ logits, int32_t *__restrict__ idx,
-                                                            float *__restrict__ w, uint32_t *__restrict__ amax_bits) {
-    extern __shared__ __attribute__((aligned(16))) float lds_f[];
-    float *hrow = lds_f;       // [D]
-    float *lrow = lds_f + D;   // [Ep]
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int t = blockIdx.x;
+#ifndef MOE_CHAIN_RING
+#define MOE_CHAIN_RING 4  // weight blocks (32 k each) in the exact chain's register ring
+#endif
+static_assert(MOE_CHAIN_RING % 2 == 0, "h buffers alternate with the ring slots");
+
+// ---- exact logits: a workgroup = one wave = one token x 64 experts, one chain per lane,
+// k ascending (grid T x Ep/64, so a decode batch spreads its Ep/64 chains per token over
+// the whole chip instead of one CU per token). The token's h row is staged in LDS as
+// fp32 (all lanes read the same address, a broadcast); the weights stream from the
+// L2-resident bf16 copy through a four-block register ring (blocks of 32 k, loaded three
+// blocks ahead). Logits go to lg_ws [T][Ep] (for the selection kernel) and/or to the
+// caller's logits [T][E]; the workgroups of expert group 0 also fold max |h|.
+__global__ void __launch_bounds__(64) router_chain_kernel(int32_t D, int32_t E, int32_t Ep,
+                                                          const uint16_t *__restrict__ h,
+                                                          const uint16_t *__restrict__ wk8,
+                                                          const float *__restrict__ bias, float *__restrict__ lg_ws,
+                                                          float *__restrict__ logits,
+                                                          uint32_t *__restrict__ amax_bits) {
+    extern __shared__ __attribute__((aligned(16))) float hrow[];  // [D]
+    const int lane = threadIdx.x;
+    const int t = blockIdx.x, e = blockIdx.y * 64 + lane;  // e < Ep
     const uint16_t *hp = h + (int64_t)t * D;
     uint32_t amax = 0;
-    for (int kk = 8 * tid; kk < D; kk += 8 * blockDim.x) {
+    for (int kk = 8 * lane; kk < D; kk += 8 * 64) {
         const u32x4 x = *reinterpret_cast<const u32x4 *>(hp + kk);
         *reinterpret_cast<float4 *>(hrow + kk) = make_float4(bf_lo(x.x), bf_hi(x.x), bf_lo(x.y), bf_hi(x.y));
         *reinterpret_cast<float4 *>(hrow + kk + 4) = make_float4(bf_lo(x.z), bf_hi(x.z), bf_lo(x.w), bf_hi(x.w));
         amax = max(amax, max(max(x.x & 0x7fffu, (x.x >> 16) & 0x7fffu), max(x.y & 0x7fffu, (x.y >> 16) & 0x7fffu)));
         amax = max(amax, max(max(x.z & 0x7fffu, (x.z >> 16) & 0x7fffu), max(x.w & 0x7fffu, (x.w >> 16) & 0x7fffu)));
     }
-    if (amax_bits) {
+    if (amax_bits && blockIdx.y == 0) {
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
         if (lane == 0 && amax) atomic_max_grow(amax_bits, amax << 16);
     }
     __syncthreads();
-    const int e = tid;  // this lane's expert (< Ep)
     const uint16_t *wp = wk8 + (int64_t)e * 8;
     const int64_t wstep = (int64_t)Ep * 8;  // one k-octet
     float acc = 0.0f;
-    constexpr int KB = 32, R = 4;
-    const int nb = D / KB;
-    u32x4 wq[R][KB / 8];
+    constexpr int KB = 32, R = MOE_CHAIN_RING;
+    const int nb = D / KB;  // D % 64 == 0: even
+    u32x4 wq[R][KB / 8];    // weight ring, R blocks
+    float4 hq[2][KB / 4];   // h of the current and the next block (read from LDS one block ahead)
     auto load = [&](int slot, int blk) {
 #pragma unroll
         for (int q = 0; q < KB / 8; ++q)
             wq[slot][q] = *reinterpret_cast<const u32x4 *>(wp + (int64_t)(blk * (KB / 8) + q) * wstep);
     };
-    auto compute = [&](int slot, int blk) {
+    auto hload = [&](int buf, int blk) {
+#pragma unroll
+        for (int q = 0; q < KB / 4; ++q) hq[buf][q] = *reinterpret_cast<const float4 *>(hrow + blk * KB + 4 * q);
+    };
+    auto compute = [&](int slot, int buf) {
 #pragma unroll
         for (int q = 0; q < KB / 8; ++q) {
-            const float4 x0 = *reinterpret_cast<const float4 *>(hrow + blk * KB + 8 * q);
-            const float4 x1 = *reinterpret_cast<const float4 *>(hrow + blk * KB + 8 * q + 4);
+            const float4 x0 = hq[buf][2 * q], x1 = hq[buf][2 * q + 1];
             const u32x4 y = wq[slot][q];
             acc = __builtin_fmaf(x0.x, bf_lo(y.x), acc);
             acc = __builtin_fmaf(x0.y, bf_hi(y.x), acc);
@@ -137,22 +143,45 @@ __global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D
             acc = __builtin_fmaf(x1.w, bf_hi(y.w), acc);
         }
     };
+    // block b sits in weight slot b % R and h buffer b % 2. Whole ring turns run without a
+    // branch inside (a conditional use would let the compiler sink the prefetches into it),
+    // each step's prefetches pinned in place; then the last nb % R blocks, already loaded.
 #pragma unroll
     for (int r = 0; r < R - 1; ++r) load(r, min(r, nb - 1));
-    for (int b0 = 0; b0 < nb; b0 += R) {
+    hload(0, 0);
+    const int n_full = nb - nb % R;
+    for (int b0 = 0; b0 < n_full; b0 += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
+            __builtin_amdgcn_sched_barrier(0);
             load((r + R - 1) % R, min(b0 + r + R - 1, nb - 1));  // past the end: reload (unused)
-            if (b0 + r < nb) compute(r, b0 + r);
+            hload((r + 1) & 1, min(b0 + r + 1, nb - 1));
+            __builtin_amdgcn_sched_barrier(0);  // the next block's h reads go out first
+            compute(r, r & 1);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int r = 0; r < R - 1; ++r) {
+        if (n_full + r >= nb) break;
+        hload((r + 1) & 1, min(n_full + r + 1, nb - 1));
+        compute(r, r & 1);
+    }
     const float lg = e < E ? (bias ? acc + bias[e] : acc) : 0.0f;
-    if (e < E && logits) logits[(int64_t)t * E + e] = lg;
-    if (!idx) return;
-    lrow[e] = lg;
-    __syncthreads();
-    if (tid >= 64) return;
-    // ---- top-k of the row: k rounds of a wave-wide arg-max, then the fp64 weights
+    if (lg_ws) lg_ws[(int64_t)t * Ep + e] = lg;
+    if (logits && e < E) logits[(int64_t)t * E + e] = lg;
+}
+
+// ---- top-k of exact logit rows: one wave per token, k rounds of a wave-wide arg-max
+// (larger logit first, ties to the lower index), then the fp64 softmax weights over the
+// k selected: lane j < k computes exp(l_j - l_0) and the sum runs in j order.
+template <int PER>  // logits per lane: Ep / 64
+__global__ void __launch_bounds__(256) router_topk_kernel(int32_t T, int32_t E, int32_t Ep, int32_t k,
+                                                          const float *__restrict__ lg_ws, int32_t *__restrict__ idx,
+                                                          float *__restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
     float v[PER];
     uint32_t live = 0;  // bit i: expert lane + 64 i exists and is not taken
 #pragma unroll
@@ -160,7 +189,7 @@ __global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D
         const int ee = lane + 64 * i;
         v[i] = 0.f;
         if (ee < E) {
-            v[i] = lrow[ee];
+            v[i] = lg_ws[(int64_t)t * Ep + ee];
             live |= 1u << i;
         }
     }
@@ -176,28 +205,29 @@ __global__ void __launch_bounds__(1024) router_exact_kernel(int32_t T, int32_t D
         if (r >= k) break;
         float bv = 0.f;
         int bi = -1, bslot = -1;
+        // selects only (no divergent branches): take a candidate that exists and ranks
+        // before the current best (an empty best, index -1, ranks after everything)
 #pragma unroll
         for (int i = 0; i < PER; ++i) {
             const int ee = lane + 64 * i;
-            if (((live >> i) & 1u) && (bi < 0 || ranks_before(v[i], ee, bv, bi))) {
-                bv = v[i];
-                bi = ee;
-                bslot = i;
-            }
+            const bool take = (((live >> i) & 1u) != 0) & ((bi < 0) | (v[i] > bv) | ((v[i] == bv) & (ee < bi)));
+            bv = take ? v[i] : bv;
+            bi = take ? ee : bi;
+            bslot = take ? i : bslot;
         }
+#pragma unroll
         for (int off = 32; off > 0; off >>= 1) {
             const float ov = __shfl_xor(bv, off);
             const int oi = __shfl_xor(bi, off);
-            if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, bv, bi))) {
-                bv = ov;
-                bi = oi;
-            }
+            const bool take = (oi >= 0) & ((bi < 0) | (ov > bv) | ((ov == bv) & (oi < bi)));
+            bv = take ? ov : bv;
+            bi = take ? oi : bi;
         }
-        if (bi >= 0 && (bi & 63) == lane && bslot >= 0) live &= ~(1u << (bi >> 6));
+        const bool mine = (bi >= 0) & ((bi & 63) == lane) & (bslot >= 0);
+        live = mine ? (live & ~(1u << (bi >> 6))) : live;
         sel[r] = bi;
         selv[r] = bv;
     }
-    // lane j < k computes exp(l_j - l_0); the sum runs in j order on every lane
     double ex = 0.0;
     int my_sel = -1;
 #pragma unroll
@@ -689,6 +719,7 @@ RoutePlan route_plan(int32_t T, int32_t D, int32_t E) {
         return o;
     };
     p.off_wk8 = take((size_t)D * p.Ep * 2);
+    if (!p.screen) p.off_exact = take((size_t)T * p.Ep * 4);  // exact logits for the selection
     if (p.screen) {
         p.off_logits = take((size_t)T * p.Ep * 4);  // the MFMA approximations
         p.off_wpart = take((size_t)p.n_parts * p.Ep * 8);
@@ -710,19 +741,20 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
                        D, E, p.Ep, wr, wk8, wpart, amax_bits);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    // exact logits (to `out` if given) and, with idx, the top k: one workgroup per token
+    // exact logits (to `out` if given) and, with idx, the top k of each row
     auto exact = [&](float *out, int32_t *ix, float *wt, uint32_t *amax) {
-        const size_t lds = ((size_t)D + p.Ep) * 4;
-        const dim3 grid((unsigned)T), block((unsigned)p.Ep);
+        float *lg_ws = ix ? reinterpret_cast<float *>(ws + p.off_exact) : nullptr;
+        hipLaunchKernelGGL(router_chain_kernel, dim3((unsigned)T, (unsigned)(p.Ep / 64)), dim3(64),
+                           (size_t)D * 4, s, D, E, p.Ep, h, wk8, bias, lg_ws, out, amax);
+        hipError_t e2 = hipGetLastError();
+        if (e2 != hipSuccess || !ix) return e2;
+        const dim3 grid((unsigned)((T + 3) / 4)), block(256);
         if (p.Ep <= 128)
-            hipLaunchKernelGGL((router_exact_kernel<2>), grid, block, lds, s, T, D, E, p.Ep, k, h, wk8, bias, out, ix,
-                               wt, amax);
+            hipLaunchKernelGGL((router_topk_kernel<2>), grid, block, 0, s, T, E, p.Ep, k, lg_ws, ix, wt);
         else if (p.Ep <= 384)
-            hipLaunchKernelGGL((router_exact_kernel<6>), grid, block, lds, s, T, D, E, p.Ep, k, h, wk8, bias, out, ix,
-                               wt, amax);
+            hipLaunchKernelGGL((router_topk_kernel<6>), grid, block, 0, s, T, E, p.Ep, k, lg_ws, ix, wt);
         else
-            hipLaunchKernelGGL((router_exact_kernel<kMaxE / 64>), grid, block, lds, s, T, D, E, p.Ep, k, h, wk8, bias,
-                               out, ix, wt, amax);
+            hipLaunchKernelGGL((router_topk_kernel<kMaxE / 64>), grid, block, 0, s, T, E, p.Ep, k, lg_ws, ix, wt);
         return hipGetLastError();
     };
     if (!p.screen) return exact(logits_out, idx, w, amax_bits);
