@@ -173,6 +173,14 @@ LAYER_CASES = [
     dict(name="stream-w4a16-full-dims", wl=synth.custom("w4a16", T=64, D=4096, F=2560, E=16, seed=65)),
     dict(name="ep-share-w4a16", wl=synth.custom("w4a16", T=400, D=512, F=384, E=24, e_begin=6, e_end=15, seed=66)),
     dict(name="skew-w4a16", wl=synth.custom("w4a16", T=600, D=256, F=128, E=16, skew=True, seed=67)),
+    # degenerate and extreme cases: one token, top-1, every expert taken by every token,
+    # top-2 on an expert-parallel share, and 1024 experts (the router's largest table)
+    dict(name="single-token-nvfp4", wl=synth.custom("nvfp4", T=1, D=256, F=128, E=16, seed=71)),
+    dict(name="top1-mxfp8", wl=synth.custom("mxfp8", T=200, D=256, F=128, E=16, k=1, seed=72)),
+    dict(name="all-experts-w4a16", wl=synth.custom("w4a16", T=48, D=256, F=128, E=8, seed=73)),
+    dict(name="top2-ep-share-mxfp4", wl=synth.custom("mxfp4", T=300, D=256, F=128, E=32, k=2, e_begin=3, e_end=11,
+                                                     seed=74)),
+    dict(name="e1024-nvfp4", wl=synth.custom("nvfp4", T=64, D=128, F=128, E=1024, seed=75)),
 ]
 
 
