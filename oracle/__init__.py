@@ -22,8 +22,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4, FMT_W4A16 = 0, 1, 2, 3, 4
-_FMT = {"none": 0, "bf16": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4}
+FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4, FMT_W4A16, FMT_BF16 = 0, 1, 2, 3, 4, 5
+# "none": the textbook layer in fp64 on the bf16 masters; "bf16": bf16 experts with the
+# GPU's roundings (fp32 sums, bf16 intermediate)
+_FMT = {"none": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4, "bf16": 5}
 
 
 def build() -> str:
@@ -284,7 +286,8 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
                 down_master=None, taps: bool = False, tok_list=None):
     """Oracle MoE forward -> out float32 [T, D] (and a dict of taps when taps=True).
 
-    gate_up/down: dicts from quantize_weights (fmt nvfp4/mxfp8/mxfp4); *_master: bf16 arrays (fmt none).
+    gate_up/down: dicts from quantize_weights (fmt nvfp4/mxfp8/mxfp4/w4a16); *_master: bf16 arrays
+    (fmt none and bf16).
     tok_list: compute only these tokens' outputs (others are zero)."""
     f = _FMT[fmt]
     lib = _load()
@@ -298,7 +301,7 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
     a = _Args()
     a.fmt, a.T, a.D, a.F, a.E, a.k, a.e_begin, a.e_end = f, T, D, F, E, k, e_begin, e_end
     a.h, a.idx, a.w, a.out = _ptr(h), _ptr(idx), _ptr(w), _ptr(out)
-    if f == FMT_NONE:
+    if f in (FMT_NONE, FMT_BF16):
         gm = np.ascontiguousarray(gate_up_master, np.uint16)
         dm = np.ascontiguousarray(down_master, np.uint16)
         keep += [gm, dm]
@@ -316,7 +319,7 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
     if taps:
         _, offs, _ = permute(idx, e_begin, e_end)
         S = int(offs[-1])
-        if f == FMT_W4A16:
+        if f in (FMT_W4A16, FMT_BF16):
             # no activation codes; the intermediate is bf16 bit patterns [S][F]
             tp["inter"] = np.zeros((S, F), np.float32)
             tp["inter_codes"] = np.zeros((S, F), np.uint16)
@@ -353,11 +356,15 @@ def down_combine(fmt: str, idx, w, inter_codes, inter_scales, inter_tscale, down
     w = np.ascontiguousarray(w, np.float32)
     T, k = idx.shape
     e_end = E if e_end is None else e_end
-    ic = np.ascontiguousarray(inter_codes, np.uint16 if f == FMT_W4A16 else np.uint8)
+    ic = np.ascontiguousarray(inter_codes, np.uint16 if f in (FMT_W4A16, FMT_BF16) else np.uint8)
     is_ = None if inter_scales is None else np.ascontiguousarray(inter_scales, np.uint8)
-    c = np.ascontiguousarray(down["codes"], np.uint8)
-    sc = np.ascontiguousarray(down["scales"], np.uint8)
-    ts = None if down.get("tensor_scale") is None else np.ascontiguousarray(down["tensor_scale"], np.float32)
+    if f == FMT_BF16:  # down is the bf16 master [E][D][F]
+        c, sc = np.ascontiguousarray(down, np.uint16), None
+    else:
+        c = np.ascontiguousarray(down["codes"], np.uint8)
+        sc = np.ascontiguousarray(down["scales"], np.uint8)
+    ts = (None if f == FMT_BF16 or down.get("tensor_scale") is None
+          else np.ascontiguousarray(down["tensor_scale"], np.float32))
     out = np.empty((T, D), np.float32)
     _check(_load().orc_down_combine(f, T, D, F, E, k, e_begin, e_end, _ptr(idx), _ptr(w), _ptr(ic), _ptr(is_),
                                     float(inter_tscale if inter_tscale is not None else 1.0), _ptr(c), _ptr(sc),

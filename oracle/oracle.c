@@ -477,12 +477,13 @@ int64_t orc_permute(int32_t T, int32_t k, const int32_t *idx, int32_t e_begin, i
 
 typedef struct {
     int32_t fmt; /* 0 = unquantised bf16 masters (all fp64), 1 = NVFP4 W4A4, 2 = MXFP8 W8A8,
-                    3 = MXFP4 W4A4, 4 = NVFP4 weights with bf16 activations (W4A16) */
+                    3 = MXFP4 W4A4, 4 = NVFP4 weights with bf16 activations (W4A16),
+                    5 = bf16 experts: the bf16 masters with fp32 sums and a bf16 intermediate */
     int32_t T, D, F, E, k, e_begin, e_end;
     const uint16_t *h;  /* bf16 [T][D] */
     const int32_t *idx; /* [T][k] */
     const float *w;     /* [T][k] */
-    /* fmt 0 */
+    /* fmt 0 and 5 */
     const uint16_t *gu_master; /* bf16 [E][2F][D]; rows [0,F) gate, [F,2F) up */
     const uint16_t *dn_master; /* bf16 [E][D][F] */
     /* fmt 1-4: canonical packed layout (see orc_quantize_weights; fmt 4 uses NVFP4's) */
@@ -548,20 +549,23 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
  * dequantised on the fly, activations kept in bf16; vLLM recipe
  * "thinkingmachines/Inkling-Small", section "Variants") skips step 1, multiplies the
  * fp32-rounded sums of 2 and 5 by the weight tensor scale alone, and in step 4 rounds
- * h to bf16 (nearest, ties to even).
+ * h to bf16 (nearest, ties to even). fmt 5 (bf16 experts, the checkpoint's BF16 variant
+ * in the same section) runs fmt 4's steps on the bf16 masters: exact products, sums rounded
+ * to fp32 with no scale, h rounded to bf16.
  */
 int orc_moe_forward(const orc_moe_args *a) {
     if (!a || a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->k <= 0 || a->k > a->E) return ORC_EINVAL;
     if (a->e_begin < 0 || a->e_end > a->E || a->e_end <= a->e_begin) return ORC_EINVAL;
-    if (a->fmt < 0 || a->fmt > 4) return ORC_EINVAL;
+    if (a->fmt < 0 || a->fmt > 5) return ORC_EINVAL;
     const int fmt = a->fmt;
-    const int wf = fmt == 4 ? 1 : fmt; /* weight format */
+    const int wf = fmt == 4 ? 1 : (fmt == 5 ? 0 : fmt); /* weight format (0: the bf16 masters) */
+    const int a16 = fmt == 4 || fmt == 5;               /* bf16 activations, bf16 intermediate */
     const int64_t T = a->T, D = a->D, F = a->F, k = a->k;
     if (wf == 1 && (D % 16 || F % 16)) return ORC_EINVAL;
     if ((fmt == 2 || fmt == 3) && (D % 32 || F % 32)) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
     if (!a->h || !a->idx || !a->w || !a->out) return ORC_EINVAL;
-    if (fmt == 0 && (!a->gu_master || !a->dn_master)) return ORC_EINVAL;
+    if (wf == 0 && (!a->gu_master || !a->dn_master)) return ORC_EINVAL;
     if (wf == 1 && (!a->gu_codes || !a->gu_scales || !a->gu_tscale || !a->dn_codes || !a->dn_scales || !a->dn_tscale))
         return ORC_EINVAL;
     if ((fmt == 2 || fmt == 3) && (!a->gu_codes || !a->gu_scales || !a->dn_codes || !a->dn_scales)) return ORC_EINVAL;
@@ -606,7 +610,7 @@ int orc_moe_forward(const orc_moe_args *a) {
         float *hf = (float *)malloc(sizeof(float) * T * D);
         if (!hf) { rc = ORC_ENOMEM; goto done; }
         for (int64_t i = 0; i < T * D; ++i) hf[i] = bf16_value(a->h[i]);
-        if (fmt == 0 || fmt == 4) {
+        if (fmt == 0 || a16) {
             for (int64_t i = 0; i < T * D; ++i) ahat[i] = hf[i];
         } else {
             int64_t nc = fmt == 2 ? T * D : T * D / 2, ns = fmt == 1 ? T * D / 16 : T * D / 32;
@@ -708,7 +712,7 @@ int orc_moe_forward(const orc_moe_args *a) {
     if (!ihat) { rc = ORC_ENOMEM; goto done; }
     if (fmt == 0) {
         memcpy(ihat, inter64, sizeof(double) * ngu * F);
-    } else if (fmt == 4) {
+    } else if (a16) {
         for (int64_t p = 0; p < S; ++p) {
             int64_t c = cidx[p];
             if (c < 0) continue;
@@ -831,17 +835,19 @@ done:
  * to fp32). Used to check a down projection and combine on another implementation's
  * intermediate codes. i_codes / i_scales: [S][F/2] and [S][F/16] (NVFP4, tensor scale
  * i_ts), [S][F] and [S][F/32] (MXFP8), [S][F/2] and [S][F/32] (MXFP4), or bf16 bit
- * patterns [S][F] (2 bytes each) and no scales (W4A16, fmt 4).
+ * patterns [S][F] (2 bytes each) and no scales (W4A16, fmt 4, and bf16 experts, fmt 5,
+ * whose dn_codes are the bf16 masters [E][D][F] and dn_scales may be NULL).
  */
 int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, int32_t k, int32_t e_begin,
                      int32_t e_end, const int32_t *idx, const float *w, const uint8_t *i_codes,
                      const uint8_t *i_scales, float i_ts, const uint8_t *dn_codes, const uint8_t *dn_scales,
                      const float *dn_tscale, float *out) {
-    if (fmt < 1 || fmt > 4) return ORC_EINVAL;
-    const int wf = fmt == 4 ? 1 : fmt;
+    if (fmt < 1 || fmt > 5) return ORC_EINVAL;
+    const int wf = fmt == 4 ? 1 : (fmt == 5 ? 0 : fmt);
     if (T < 0 || D <= 0 || F <= 0 || E <= 0 || k <= 0 || e_begin < 0 || e_end > E || e_end <= e_begin) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
-    if (!idx || !w || !i_codes || (fmt != 4 && !i_scales) || !dn_codes || !dn_scales || !out || (wf == 1 && !dn_tscale))
+    if (!idx || !w || !i_codes || (fmt < 4 && !i_scales) || !dn_codes || (wf != 0 && !dn_scales) || !out ||
+        (wf == 1 && !dn_tscale))
         return ORC_EINVAL;
     init_tables();
     const int32_t n_loc = e_end - e_begin;
@@ -859,7 +865,7 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
     if (fmt == 1) orc_dequant_nvfp4(i_codes, i_scales, i_ts, S, F, 0, ihat);
     else if (fmt == 2) orc_dequant_mxfp8(i_codes, i_scales, S, F, ihat);
     else if (fmt == 3) orc_dequant_mxfp4(i_codes, i_scales, S, F, ihat);
-    else
+    else /* fmt 4 and 5: bf16 */
         for (int64_t i = 0; i < S * F; ++i) {
             uint16_t b;
             memcpy(&b, i_codes + 2 * i, 2);
@@ -880,7 +886,7 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
                     int64_t n = it % D;
                     if (offs[el] == offs[el + 1]) continue;
                     int32_t e = e_begin + el;
-                    weight_row(wf, NULL, dn_codes, dn_scales, (int64_t)e * D + n, F, wrow);
+                    weight_row(wf, (const uint16_t *)dn_codes, dn_codes, dn_scales, (int64_t)e * D + n, F, wrow);
                     float sc = fmt == 1 ? i_ts * dn_tscale[e] : (fmt == 4 ? dn_tscale[e] : 1.0f);
                     for (int64_t p = offs[el]; p < offs[el + 1]; ++p) {
                         const double *irow = ihat + p * F;

@@ -329,3 +329,72 @@ def test_w4a16_on_exactly_encodable_weights_is_the_bf16_layer():
     err4 = np.linalg.norm(a4 - ref) / np.linalg.norm(ref)
     assert err16 < 3e-3, err16      # bf16 rounding of the intermediate only (2^-9 relative)
     assert err4 > 10 * err16, (err4, err16)
+
+
+# ------------------------------------------------------------------ bf16 experts
+def test_bf16_experts_compose_from_library_routines():
+    """bf16 experts (the checkpoint's BF16 variant, vLLM recipe "thinkingmachines/Inkling-Small",
+    section "Variants"): a BLAS composition on the unquantised bf16 masters with the fp32
+    rounding of each sum and torch's bf16 rounding of the SwiGLU output."""
+    T, D, F, E = 20, 64, 64, 12
+    wl, h, wr, _ = _small("nvfp4", T=T, D=D, F=F, E=E, seed=10)
+    gu_m, dn_m = wl.gate_up_master(0, E), wl.down_master(0, E)
+    idx, w = oracle.route(h, wr, k=8)
+    out, tp = oracle.moe_forward("bf16", h, idx, w, D=D, F=F, E=E, gate_up_master=gu_m, down_master=dn_m,
+                                 taps=True)
+    H = synth.bf16_to_f32(h).astype(np.float64)
+    counts, offs, ss = oracle.permute(idx, 0, E)
+    inter = np.zeros((len(ss), F), f32)
+    for p, s in enumerate(ss):
+        t, e = s // 8, idx.reshape(-1)[s]
+        gl = (synth.bf16_to_f32(gu_m[e]).astype(np.float64) @ H[t]).astype(f32)
+        g, u = gl[:F].astype(np.float64), gl[F:].astype(np.float64)
+        inter[p] = (g * u / (1.0 + np.exp(-g))).astype(f32)
+    np.testing.assert_array_equal(inter, tp["inter"])
+    ib = _bf16_bits(inter)
+    assert np.array_equal(ib, tp["inter_codes"])
+    I = synth.bf16_to_f32(ib).astype(np.float64)
+    ref = np.zeros((T, D))
+    for p, s in enumerate(ss):
+        t, j = divmod(int(s), 8)
+        y = (synth.bf16_to_f32(dn_m[idx[t, j]]).astype(np.float64) @ I[p]).astype(f32)
+        np.testing.assert_array_equal(y, tp["y"][p])
+        ref[t] += float(w[t, j]) * y.astype(np.float64)
+    np.testing.assert_allclose(out, ref.astype(f32), rtol=1e-6, atol=1e-9)
+
+
+def test_bf16_experts_match_w4a16_on_exactly_encodable_weights():
+    """Where NVFP4 reproduces the masters, W4A16 and bf16 experts run the same arithmetic
+    up to the ulp-level rounding of the NVFP4 tensor scale; both stay within the
+    intermediate's bf16 rounding of the fp64 textbook layer."""
+    T, D, F, E = 24, 128, 64, 12
+    wl, h, wr, _ = _small("nvfp4", T=T, D=D, F=F, E=E, seed=15)
+    gu_m, dn_m = _grid_masters(E, 2 * F, D, 3), _grid_masters(E, D, F, 4)
+    idx, w = oracle.route(h, wr, k=8)
+    kw = dict(D=D, F=F, E=E)
+    b16 = oracle.moe_forward("bf16", h, idx, w, gate_up_master=gu_m, down_master=dn_m, **kw)
+    gu, dn = oracle.quantize_weights("nvfp4", gu_m), oracle.quantize_weights("nvfp4", dn_m)
+    a16 = oracle.moe_forward("w4a16", h, idx, w, gate_up=gu, down=dn, **kw)
+    ref = oracle.moe_forward("none", h, idx, w, gate_up_master=gu_m, down_master=dn_m, **kw)
+    rms = float(np.sqrt(np.mean(ref.astype(np.float64) ** 2)))
+    assert float(np.abs(b16 - a16).max()) / rms < 1e-4
+    assert np.linalg.norm(b16 - ref) / np.linalg.norm(ref) < 3e-3
+
+
+def test_bf16_experts_shares_and_stagewise():
+    """Four expert ranges add up to the full layer, and the stage-wise entry point fed the
+    forward's own bf16 intermediate reproduces it bit for bit."""
+    T, D, F, E = 16, 64, 96, 16
+    wl, h, wr, _ = _small("nvfp4", T=T, D=D, F=F, E=E, seed=23)
+    gu_m, dn_m = wl.gate_up_master(0, E), wl.down_master(0, E)
+    idx, w = oracle.route(h, wr, k=8)
+    kw = dict(D=D, F=F, E=E, gate_up_master=gu_m, down_master=dn_m)
+    full = oracle.moe_forward("bf16", h, idx, w, **kw)
+    parts = sum(oracle.moe_forward("bf16", h, idx, w, e_begin=4 * r, e_end=4 * r + 4, **kw).astype(np.float64)
+                for r in range(4))
+    np.testing.assert_allclose(parts, full, rtol=2e-6, atol=1e-6 * np.abs(full).max())
+    for eb, ee in ((0, E), (3, 9)):
+        out, tp = oracle.moe_forward("bf16", h, idx, w, e_begin=eb, e_end=ee, taps=True, **kw)
+        got = oracle.down_combine("bf16", idx, w, tp["inter_codes"], None, None, dn_m, D=D, F=F, E=E,
+                                  e_begin=eb, e_end=ee)
+        assert np.array_equal(got.view(np.uint32), out.view(np.uint32))
