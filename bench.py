@@ -5,8 +5,8 @@ weights, hidden-state amax) + moe_forward (permutation, hidden-state quantisatio
 gate_up GEMM with SwiGLU and intermediate quantisation, down GEMM, weighted
 combine), with all inputs and packed weights resident in HBM. The default workload
 is the NVFP4 decode step (64 tokens, d_model 4096, d_ff 2560, 384 experts, top-8);
---workload i selects one of the nine seeded synthetic workloads (NVFP4, MXFP8, and the
-MXFP4 and W4A16 variants).
+--workload i selects one of the eleven seeded synthetic workloads (NVFP4, MXFP8, and the
+MXFP4, W4A16 and bf16-expert variants).
 
 Printed: one JSON line (rank 0). `roofline` covers the dominant kernel (the gate_up
 GEMM) timed live with HIP events recorded around its launch on the library's stream;
@@ -34,7 +34,8 @@ MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "fp4": 10066.3
 DTYPES = {"nvfp4": "f16 (exact NVFP4 values), fp32 accumulate",
           "mxfp8": "bf16 (exact MXFP8 values), fp32 accumulate",
           "mxfp4": "fp4 (MXFP4 codes and E8M0 scales on the scaled MFMA), fp32 accumulate",
-          "w4a16": "bf16 (bf16 activations, NVFP4 weights expanded exactly), fp32 accumulate"}
+          "w4a16": "bf16 (bf16 activations, NVFP4 weights expanded exactly), fp32 accumulate",
+          "bf16": "bf16 (bf16 weights and activations), fp32 accumulate"}
 METRIC = "MoE layer tokens/s; % peak HBM BW (decode), % scaled-MFMA peak (prefill)"
 
 
@@ -116,6 +117,8 @@ def profiled_traffic(workload: str, kernel: str):
 def packed_bytes_per_expert(fmt: str, N: int, K: int) -> int:
     if fmt in ("nvfp4", "w4a16"):
         return N * K // 2 + N * K // 16 + 4
+    if fmt == "bf16":
+        return 2 * N * K
     if fmt == "mxfp4":
         return N * K // 2 + N * K // 32
     return N * K + N * K // 32
@@ -162,6 +165,21 @@ def cpu_baseline(wl, h, wr, bias, target_s: float = 10.0):
         remap[used] = np.arange(len(used), dtype=np.int32)
         cidx = np.where(local, remap[idx], len(used)).astype(np.int32)  # non-local -> outside [0, m)
         m = len(used)
+        if wl.fmt == "bf16":  # unquantised: the touched experts' masters plus one zero expert
+            z = lambda a: np.concatenate([a, np.zeros((1,) + a.shape[1:], a.dtype)])
+            gm = z(np.stack([wl.gate_up_master(int(e))[0] for e in used]))
+            dm = z(np.stack([wl.down_master(int(e))[0] for e in used]))
+            t1 = time.perf_counter()
+            oracle.moe_forward("bf16", hs, cidx, w, D=wl.D, F=wl.F, E=m + 1, e_begin=0, e_end=m,
+                               gate_up_master=gm, down_master=dm)
+            t_fwd = time.perf_counter() - t1
+            total = t_route + t_fwd
+            if total >= target_s or n >= wl.T:
+                return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                        "sample": f"first {n} of {wl.T} tokens of the workload, route + forward, "
+                                  f"{m} touched experts, {total:.1f} s"}
+            n = min(wl.T, max(n * 2, int(n * target_s / max(total, 1e-3)) + 1))
+            continue
         gu = {"codes": [], "scales": [], "tensor_scale": []}
         dn = {"codes": [], "scales": [], "tensor_scale": []}
         for e in used:
@@ -202,7 +220,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, help="index into the nine synthetic workloads")
+    ap.add_argument("--workload", type=int, default=1, help="index into the eleven synthetic workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "
@@ -305,7 +323,7 @@ def main():
     gu_b = packed_bytes_per_expert(wl.fmt, 2 * F, D)
     dn_b = packed_bytes_per_expert(wl.fmt, D, F)
     code_b = {"nvfp4": lambda c: c // 2 + c // 16, "mxfp4": lambda c: c // 2 + c // 32,
-              "mxfp8": lambda c: c + c // 32, "w4a16": lambda c: 2 * c}[wl.fmt]
+              "mxfp8": lambda c: c + c // 32, "w4a16": lambda c: 2 * c, "bf16": lambda c: 2 * c}[wl.fmt]
     act_b = lambda rows, cols: rows * code_b(cols)
     gate_up_bytes = touched * gu_b + act_b(T, D) + act_b(S, F)
     gate_up_flops = 4.0 * S * F * D
@@ -314,7 +332,7 @@ def main():
     # the contraction's peak, with the format's own scaled-MFMA peak reported beside it;
     # the MXFP4 GEMMs run the scaled FP4 MFMA itself
     mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else "bf16")]
-    format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt == "w4a16" else "fp8")]
+    format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt in ("w4a16", "bf16") else "fp8")]
     decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge
     if decode:
         achieved = gate_up_bytes / (gate_up_ms * 1e-3) / 1e9

@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4}  # w4a16: moe_forward only (NVFP4 weights)
+FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4, "bf16": 5}  # w4a16: moe_forward only (NVFP4 weights)
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "alignment",
           -4: "workspace", -5: "HIP launch failed"}
 
@@ -123,7 +123,10 @@ class PackedWeights:
         nv = fmt == "nvfp4"
         if N % 32 or K % 64:
             raise ValueError(f"packed weights need N % 32 == 0 and K % 64 == 0 (got N={N}, K={K})")
-        if fmt == "mxfp4":
+        if fmt == "bf16":  # bf16 values in the tile layout, no scales
+            codes = torch.empty((E, N // 32, K // 64, 32, 128), dtype=torch.uint8, device=device)
+            scales = torch.empty((0,), dtype=torch.uint8, device=device)
+        elif fmt == "mxfp4":
             codes = torch.empty((E, N // 32, K // 64, 2, 32, 16), dtype=torch.uint8, device=device)
             scales = torch.empty((E, N // 32, K // 64, 2, 32, 1), dtype=torch.uint8, device=device)
         else:
@@ -140,7 +143,7 @@ class PackedWeights:
 
     def struct(self) -> MoePacked:
         return MoePacked(FMT[self.fmt], self.E, self.N, self.K, self.codes.data_ptr(),
-                         self.scales.data_ptr(),
+                         self.scales.data_ptr() if self.scales.numel() else 0,
                          0 if self.tensor_scale is None else self.tensor_scale.data_ptr())
 
     def nbytes(self) -> int:
@@ -225,7 +228,7 @@ class Layer:
             "inter": ((TK, F), torch.float32),
             "y": ((TK, D), torch.float32),
         }
-        if self.fmt == "w4a16":
+        if self.fmt in ("w4a16", "bf16"):
             spec["inter_codes"] = ((TK, F), torch.int16)
         else:
             spec.update({

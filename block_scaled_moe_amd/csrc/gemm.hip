@@ -45,12 +45,13 @@ using namespace gemm_detail;
 
 template <int FM, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
 struct Cfg {
-    static constexpr bool NV = FM != kFmtMX8;         // NVFP4 weights
+    static constexpr bool NV = FM == kFmtNV || FM == kFmtA16;  // NVFP4 weights
+    static constexpr bool BW = FM == kFmtBF;                    // bf16 weights (no scales)
     static constexpr int NT = WM * WN * 64;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
     static constexpr int MS = WTM / 16, NS = WTN / 16;
     static constexpr int BLK = NV ? 16 : 32;          // values per block scale
-    static constexpr int B_ROW = NV ? KC / 2 : KC;    // code bytes per weight row per chunk
+    static constexpr int B_ROW = NV ? KC / 2 : (BW ? 2 * KC : KC);  // code bytes per weight row per chunk
     static constexpr int SB = KC / BLK;               // scale bytes per weight row per chunk
     static constexpr int A_STRIDE = KC * 2 + 16;      // bytes per LDS A row (16-bit values)
     static constexpr int B_STRIDE = B_ROW + 16;
@@ -59,7 +60,7 @@ struct Cfg {
     static constexpr int S_OFF = B_OFF + BN * B_STRIDE;
     static constexpr int MAIN = S_OFF + BN * SB;
     static constexpr int EPI_STRIDE = BN / 2 + 4;     // floats per row of the MXFP8 SwiGLU tile
-    static constexpr int EPI = (GATE_UP && !NV) ? BM * EPI_STRIDE * 4 : 0;
+    static constexpr int EPI = (GATE_UP && FM == kFmtMX8) ? BM * EPI_STRIDE * 4 : 0;
     static constexpr int LDS = MAIN > EPI ? MAIN : EPI;
     static constexpr int A_TOTAL = BM * KC / 8;       // 16-byte loads of A per chunk
     static constexpr int A_ITEMS = (A_TOTAL + NT - 1) / NT;
@@ -76,8 +77,10 @@ template <int FM, int BM, int BN, int KC, int WM, int WN, bool GATE_UP>
 __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmArgs p) {
     using C = Cfg<FM, BM, BN, KC, WM, WN, GATE_UP>;
     constexpr bool NV = C::NV;                   // NVFP4 weights (W4A4 or W4A16)
+    constexpr bool BW = C::BW;                   // bf16 weights
     constexpr bool BF = FM != kFmtNV;            // bf16 operands and MFMA
     constexpr bool A16 = FM == kFmtA16;
+    constexpr bool O16 = FM == kFmtA16 || FM == kFmtBF;  // bf16 intermediate out of gate_up
     using Frag = typename std::conditional<BF, bf16x8, half8>::type;
     __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS];
 
@@ -93,7 +96,7 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
     const int K = p.K;
     const int F = p.N / 2;  // gate_up only
     const int n0 = GATE_UP ? blockIdx.y * (BN / 2) : blockIdx.y * BN;
-    const int64_t w_row_bytes = NV ? K / 2 : K;
+    const int64_t w_row_bytes = NV ? K / 2 : (BW ? 2 * K : K);
 
     // ---- per-thread global sources, fixed over the K loop
     const uint8_t *a_src[C::A_ITEMS];
@@ -119,11 +122,12 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
         const int wrow = GATE_UP ? (r < BN / 2 ? n0 + r : F + n0 + (r - BN / 2)) : n0 + r;
         b_dst[i] = C::B_OFF + r * C::B_STRIDE + 16 * q;
         // packed tile layout (layout.h): a 16-byte piece stays inside one row's 64-wide slot
-        b_src[i] = p.w_codes + (int64_t)e * p.N * w_row_bytes + layout::code_offset(NV, K, wrow, (NV ? 32 : 16) * q);
+        b_src[i] = p.w_codes + (int64_t)e * p.N * w_row_bytes +
+                   (BW ? layout::code_offset_bf16(K, wrow, 8 * q) : layout::code_offset(NV, K, wrow, (NV ? 32 : 16) * q));
     }
     const uint8_t *s_src = nullptr;
     int s_dst = 0;
-    if (tid < BN) {
+    if (tid < BN && !BW) {
         const int wrow = GATE_UP ? (tid < BN / 2 ? n0 + tid : F + n0 + (tid - BN / 2)) : n0 + tid;
         s_src = p.w_scales + (int64_t)e * p.N * (K / C::BLK) + layout::scale_offset(NV, K, wrow, 0);
         s_dst = C::S_OFF + tid * C::SB;
@@ -152,7 +156,8 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                 a_reg[i] = a_src[i] ? *reinterpret_cast<const u32x4 *>(a_src[i] + 2 * kn) : (u32x4){0u, 0u, 0u, 0u};
 #pragma unroll
             for (int i = 0; i < C::B_ITEMS; ++i)
-                b_reg[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (int64_t)(kn / 64) * layout::code_block_bytes(NV));
+                b_reg[i] = *reinterpret_cast<const u32x4 *>(b_src[i] + (int64_t)(kn / 64) *
+                                                                       (BW ? 4096 : layout::code_block_bytes(NV)));
             if (s_src) {
                 // the chunk's KC/64 block slots of this row, gathered in column order
                 constexpr int NBLK = KC / 64, SBW = layout::scale_bytes_per_row(NV);
@@ -210,6 +215,11 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
 #pragma unroll
                             for (int ms = 0; ms < C::MS; ++ms)
                                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                        } else if constexpr (BW) {
+                            const bf16x8 bf = *reinterpret_cast<const bf16x8 *>(brow + 2 * kk);  // the stored values
+#pragma unroll
+                            for (int ms = 0; ms < C::MS; ++ms)
+                                acc[ms][ns] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                         } else {
                             const bf16x8 bf = dequant_mxfp8(*reinterpret_cast<const u32x2 *>(brow + kk), sm[ns]);
 #pragma unroll
@@ -255,8 +265,9 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                 }
         for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
         if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
-    } else if (GATE_UP && A16) {
-        // W4A16: the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
+    } else if (GATE_UP && O16) {
+        // W4A16 and bf16 experts: the SwiGLU output rounded to bf16 (nearest even) is the
+        // down GEMM's input
 #pragma unroll
         for (int ms = 0; ms < C::MS; ++ms)
 #pragma unroll
@@ -354,6 +365,7 @@ hipError_t launch_grouped_gemm(const GemmArgs &a, int fm, bool gate_up, GemmShap
         case kFmtNV: return dispatch<kFmtNV>(a, gate_up, shape, max_tiles, s);
         case kFmtMX8: return dispatch<kFmtMX8>(a, gate_up, shape, max_tiles, s);
         case kFmtA16: return dispatch<kFmtA16>(a, gate_up, shape, max_tiles, s);
+        case kFmtBF: return dispatch<kFmtBF>(a, gate_up, shape, max_tiles, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -51,11 +51,13 @@ constexpr int kRows = 64;  // weight rows per workgroup
 
 template <int FM, bool GATE_UP, int G>  // G = 128-wide K groups per wave (K = 512 G)
 __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(const GemmArgs p) {
-    constexpr bool NV = FM != kFmtMX8;  // NVFP4 weights (W4A4 or W4A16)
-    constexpr bool BF = FM != kFmtNV;   // bf16 operands and MFMA
+    constexpr bool NV = FM == kFmtNV || FM == kFmtA16;  // NVFP4 weights (W4A4 or W4A16)
+    constexpr bool BW = FM == kFmtBF;                    // bf16 weights (no scales)
+    constexpr bool BF = FM != kFmtNV;                    // bf16 operands and MFMA
     constexpr bool A16 = FM == kFmtA16;
+    constexpr bool O16 = FM == kFmtA16 || FM == kFmtBF;  // bf16 intermediate out of gate_up
     using Frag = typename std::conditional<BF, bf16x8, half8>::type;
-    constexpr int NQ = NV ? 1 : 2;                 // 16-byte code loads per lane, group and subtile
+    constexpr int NQ = NV ? 1 : (BW ? 4 : 2);      // 16-byte code loads per lane, group and subtile
     constexpr int W = NV ? MOE_STREAM_W_NV : MOE_STREAM_W_MX;  // groups of loads in flight
     constexpr int BLK = NV ? 16 : 32;
     constexpr int SBW = G * 128 / BLK;             // scale bytes per weight row in a wave's K quarter
@@ -75,15 +77,15 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     const int F = p.N / 2;
     const int n0 = GATE_UP ? blockIdx.y * (kRows / 2) : blockIdx.y * kRows;
     const int kw = wave * G * 128;  // first k of this wave's quarter
-    const int64_t row_bytes = NV ? K / 2 : K;
+    const int64_t row_bytes = NV ? K / 2 : (BW ? 2 * K : K);
 
     auto wrow_of = [&](int r) -> int {  // weight row of tile row r (0..63)
         return GATE_UP ? (r < kRows / 2 ? n0 + r : F + n0 + (r - kRows / 2)) : n0 + r;
     };
 
     // packed tile layout (layout.h): rows in groups of 32, K in blocks of 64
-    constexpr int CB = layout::code_bytes_per_row(NV);
-    constexpr int CBLK = layout::code_block_bytes(NV), SBLK = layout::scale_block_bytes(NV);
+    constexpr int CB = BW ? 128 : layout::code_bytes_per_row(NV);
+    constexpr int CBLK = 32 * CB, SBLK = layout::scale_block_bytes(NV);
     const int64_t kb = K / 64;
     const uint8_t *w_codes_e = p.w_codes + (int64_t)e * p.N * row_bytes;
     const uint8_t *w_scales_e = p.w_scales + (int64_t)e * p.N * (K / BLK);
@@ -97,7 +99,9 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     uint32_t sreg[SREG];
 #pragma unroll
     for (int i = 0; i < SREG; ++i) {
-        if (NV) {
+        if (BW) {
+            sreg[i] = 0;  // no scales
+        } else if (NV) {
             const int r = lane, row = wrow_of(r);
             sreg[i] = *reinterpret_cast<const uint32_t *>(w_scales_e + ((row >> 5) * kb + kw / 64 + i) * SBLK +
                                                           4 * (row & 31));
@@ -144,7 +148,8 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     for (int jj = 0; jj < W && jj < G; ++jj) load_group(jj);
 #pragma unroll
     for (int i = 0; i < SREG; ++i) {
-        if (NV) {
+        if (BW) {
+        } else if (NV) {
             *reinterpret_cast<uint32_t *>(&s_scale[wave][lane * SBW + 4 * i]) = sreg[i];
         } else {
             const int r = 2 * (lane & 31), cl = 2 * i + (lane >> 5);
@@ -164,7 +169,9 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
             const uint8_t *srow = &s_scale[wave][(16 * s + r16) * SBW];
-            if (NV) {
+            if (BW) {
+                sm[s] = 1.0f;
+            } else if (NV) {
                 const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
                 sh[s][0] = e4m3_to_f16(two & 0xff);
                 sh[s][1] = e4m3_to_f16(two >> 8);
@@ -184,6 +191,9 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                     acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf, acc[s], 0, 0, 0);
                 } else if constexpr (A16) {
                     const bf16x8 bf = dequant_nvfp4_bf16(bq[jj][s][0][j], sf[s][j >> 1]);
+                    acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[s], 0, 0, 0);
+                } else if constexpr (BW) {
+                    const bf16x8 bf = __builtin_bit_cast(bf16x8, bq[jj][s][j]);  // the stored values
                     acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[s], 0, 0, 0);
                 } else {
                     const u32x4 w4 = bq[jj][s][j >> 1];
@@ -217,7 +227,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
             for (int i = 0; i < 4; ++i) {
                 const int m = 4 * g + i;
                 const float hv = swiglu(gv[i] * sc, uv[i] * sc);
-                if (A16) {
+                if (O16) {
                     // the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
                     if (m < rows) {
                         const int64_t o = (int64_t)(p0 + m) * F + n0 + fl;
@@ -238,7 +248,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                 if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
             }
         }
-        if (!NV) {
+        if (FM == kFmtMX8) {
             __syncthreads();
             // one 32-block of the MXFP8 intermediate per tile row
             const int m = threadIdx.x;
@@ -307,6 +317,7 @@ hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t m
         case kFmtNV: return gate_up ? launch_k<kFmtNV, true>(a, max_tiles, s) : launch_k<kFmtNV, false>(a, max_tiles, s);
         case kFmtMX8: return gate_up ? launch_k<kFmtMX8, true>(a, max_tiles, s) : launch_k<kFmtMX8, false>(a, max_tiles, s);
         case kFmtA16: return gate_up ? launch_k<kFmtA16, true>(a, max_tiles, s) : launch_k<kFmtA16, false>(a, max_tiles, s);
+        case kFmtBF: return gate_up ? launch_k<kFmtBF, true>(a, max_tiles, s) : launch_k<kFmtBF, false>(a, max_tiles, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -65,7 +65,9 @@ static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thr
 // so each activation fragment feeds more MFMAs; 234 registers, two waves per SIMD),
 // MXFP8 2 (three waves per SIMD; at 4 it spills), W4A16 as NVFP4
 template <int FM>
-constexpr int tile_ns() { return FM == kFmtMX8 ? MOE_TILE_NS_MX : (FM == kFmtNV ? MOE_TILE_NS_NV : MOE_TILE_NS_A16); }
+constexpr int tile_ns() {
+    return (FM == kFmtMX8 || FM == kFmtBF) ? MOE_TILE_NS_MX : (FM == kFmtNV ? MOE_TILE_NS_NV : MOE_TILE_NS_A16);
+}
 
 // floats per row of a wave's MXFP8 epilogue tile in LDS: 16 NS columns plus one, so
 // lanes reading rows at the same column fall on different banks
@@ -82,12 +84,14 @@ constexpr int tile_smem_bytes() {
 
 template <int FM, bool GATE_UP, int NS>
 __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) tile_gemm_kernel(const GemmArgs p) {
-    constexpr bool NV = FM != kFmtMX8;  // NVFP4 weights (W4A4 or W4A16)
-    constexpr bool BF = FM != kFmtNV;   // bf16 operands and MFMA
+    constexpr bool NV = FM == kFmtNV || FM == kFmtA16;  // NVFP4 weights (W4A4 or W4A16)
+    constexpr bool BW = FM == kFmtBF;                    // bf16 weights (no scales)
+    constexpr bool BF = FM != kFmtNV;                    // bf16 operands and MFMA
     constexpr bool A16 = FM == kFmtA16;
+    constexpr bool O16 = FM == kFmtA16 || FM == kFmtBF;  // bf16 intermediate out of gate_up
     using Frag = typename std::conditional<BF, bf16x8, half8>::type;
-    constexpr int BN = 128 * NS;        // weight rows per workgroup
-    constexpr int CV = NV ? 1 : 2;      // 16-byte code loads per weight row per lane per chunk
+    constexpr int BN = 128 * NS;              // weight rows per workgroup
+    constexpr int CV = NV ? 1 : (BW ? 4 : 2);  // 16-byte code loads per weight row per lane per chunk
     static_assert(NS % 2 == 0, "gate_up pairs subtiles");
     __shared__ __attribute__((aligned(16))) uint8_t smem[tile_smem_bytes<FM, GATE_UP, NS>()];
 
@@ -113,10 +117,10 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
     // packed tile layout (layout.h): per chunk, a lane's 32 codes sit at byte
     // (row % 32) * CB + CB/2 * g of the chunk's block of its row group, and its scales in
     // the block's 4-byte (NVFP4) or 2-byte (MXFP8) row slot
-    constexpr int CB = layout::code_bytes_per_row(NV);
-    constexpr int CBLK = layout::code_block_bytes(NV), SBLK = layout::scale_block_bytes(NV);
+    constexpr int CB = BW ? 128 : layout::code_bytes_per_row(NV);
+    constexpr int CBLK = 32 * CB, SBLK = layout::scale_block_bytes(NV);
     const int64_t kb = K / 64;  // blocks per row group
-    const uint8_t *w_codes_e = p.w_codes + (int64_t)e * N * (NV ? K / 2 : K);
+    const uint8_t *w_codes_e = p.w_codes + (int64_t)e * N * (NV ? K / 2 : (BW ? 2 * K : K));
     const uint8_t *w_scales_e = p.w_scales + (int64_t)e * N * (NV ? K / 16 : K / 32);
 
     // ---- this lane's weight rows, one per N subtile (each subtile is one row group)
@@ -133,7 +137,7 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
         }
         const int64_t blk0 = (int64_t)(row >> 5) * kb;
         wc[ns] = w_codes_e + blk0 * CBLK + l32 * CB + (CB / 2) * g2;
-        ws[ns] = w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
+        ws[ns] = BW ? nullptr : w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
     }
 
     // ---- activation staging: global -> registers -> LDS. Rows past the tile's end load
@@ -176,7 +180,7 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
     _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                    \
         _Pragma("unroll") for (int v = 0; v < CV; ++v) wcode[slot][ns][v] =                                \
             *reinterpret_cast<const u32x4 *>(wc[ns] + (int64_t)CBLK * (c) + 16 * v);                       \
-        wsc[slot][ns] = *reinterpret_cast<const uint32_t *>(ws[ns] + (int64_t)SBLK * (c));                \
+        wsc[slot][ns] = BW ? 0u : *reinterpret_cast<const uint32_t *>(ws[ns] + (int64_t)SBLK * (c));      \
     }
 
     MOE_LOAD_A(0, 0);
@@ -205,7 +209,7 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
             for (int ns = 0; ns < NS; ++ns) {
                 if constexpr (NV) {
                     sc_nv[ns] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsc[j][ns] >> (16 * g2), 1.0f, false);
-                } else {
+                } else if constexpr (!BW) {
                     sc_mx[ns] = __uint_as_float(((wsc[j][ns] >> (8 * (2 * (l32 & 1) + g2))) & 0xffu) << 23);
                 }
             }
@@ -230,6 +234,11 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
                             for (int ms = 0; ms < kMS; ++ms)
                                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                         }
+                    } else if constexpr (BW) {
+                        const bf16x8 bf = __builtin_bit_cast(bf16x8, wcode[j][ns][s]);  // the stored values
+#pragma unroll
+                        for (int ms = 0; ms < kMS; ++ms)
+                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                     } else {
                         const u32x4 q = wcode[j][ns][s >> 1];
                         const u32x2 cw = (s & 1) ? (u32x2){q.z, q.w} : (u32x2){q.x, q.y};
@@ -252,8 +261,9 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
 
     // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
     const float scl = FM == kFmtNV ? p.a_tscale[0] * p.w_tscale[e] : (A16 ? p.w_tscale[e] : 1.0f);
-    if (GATE_UP && A16) {
-        // W4A16: the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
+    if (GATE_UP && O16) {
+        // W4A16 and bf16 experts: the SwiGLU output rounded to bf16 (nearest even) is the
+        // down GEMM's input
 #pragma unroll
         for (int q = 0; q < NS / 2; ++q) {
             const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
@@ -370,6 +380,7 @@ hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max
         case kFmtNV: return gate_up ? launch_t<kFmtNV, true>(a, max_tiles, s) : launch_t<kFmtNV, false>(a, max_tiles, s);
         case kFmtMX8: return gate_up ? launch_t<kFmtMX8, true>(a, max_tiles, s) : launch_t<kFmtMX8, false>(a, max_tiles, s);
         case kFmtA16: return gate_up ? launch_t<kFmtA16, true>(a, max_tiles, s) : launch_t<kFmtA16, false>(a, max_tiles, s);
+        case kFmtBF: return gate_up ? launch_t<kFmtBF, true>(a, max_tiles, s) : launch_t<kFmtBF, false>(a, max_tiles, s);
         default: return hipErrorInvalidValue;
     }
 }

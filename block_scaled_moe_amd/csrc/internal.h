@@ -25,6 +25,8 @@ hipError_t launch_quant_weights_nvfp4(const uint16_t *w, int32_t E, int32_t N, i
 hipError_t launch_finish_tensor_scale(float *ts_inout, int32_t n, hipStream_t s);
 hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, int32_t K,
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
+// bf16 weights copied into the packed tile layout (layout.h, 128 bytes per row slot)
+hipError_t launch_pack_weights_bf16(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes, hipStream_t s);
 hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K,
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
 // hidden states [T][D] -> MXFP4 codes [T][D/2] and E8M0 scales [T][D/32]
@@ -87,7 +89,9 @@ hipError_t launch_permute_small(const PermuteArgs &a, hipStream_t s);
 //           dequantised to bf16 on the fly): bf16 operands, bf16 MFMA. A bf16
 //           activation is not exact in fp16 in general (range, and 8 significant bits
 //           below 2^-14), so the weights are expanded to bf16 instead.
-constexpr int kFmtNV = 0, kFmtMX8 = 1, kFmtA16 = 2;
+//  kFmtBF:  bf16 weights and activations (the checkpoint's BF16 variant, same section):
+//           bf16 operands as stored, no expansion, bf16 MFMA.
+constexpr int kFmtNV = 0, kFmtMX8 = 1, kFmtA16 = 2, kFmtBF = 3;
 
 struct GemmArgs {
     const Ctrl *ctrl;

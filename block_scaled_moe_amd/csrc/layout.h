@@ -58,6 +58,20 @@ __host__ __device__ inline void block_source(bool nv, int64_t K, int64_t r, int6
     k = 64 * (blk % kb) + (nv ? 16 : 32) * piece;
 }
 
+// bf16 weights (no quantisation) use the same 32 x 64 blocks with 128-byte row slots
+// (element k of the block at bytes 2k, 2k + 1): a 4 KiB block. Storage piece r of an
+// expert (16 bytes, 8 values) sits at byte 16r; its source row and first column:
+__host__ __device__ inline void piece_source_bf16(int64_t K, int64_t r, int64_t &n, int64_t &k) {
+    const int64_t piece = r & 7, row = (r >> 3) & 31, blk = r >> 8;
+    const int64_t kb = K >> 6;
+    n = 32 * (blk / kb) + row;
+    k = 64 * (blk % kb) + 8 * piece;
+}
+// byte offset inside one expert's bf16 codes of element (n, k)
+__host__ __device__ inline int64_t code_offset_bf16(int64_t K, int64_t n, int64_t k) {
+    return block_index(K, n, k) * 4096 + (n & 31) * 128 + 2 * (k & 63);
+}
+
 // MXFP4: source row and first column of quantisation block r (storage order)
 __host__ __device__ inline void block_source_mx4(int64_t K, int64_t r, int64_t &n, int64_t &k) {
     const int64_t row = r & 31, half = (r >> 5) & 1, blk = r >> 6;

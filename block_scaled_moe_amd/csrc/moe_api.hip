@@ -39,7 +39,8 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 Plan make_plan(const moe_forward_args *a) {
     Plan p{};
     const int64_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
-    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4, a16 = a->fmt == MOE_FMT_W4A16;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
+    const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
     // MXFP4 always runs the scaled-FP4 MFMA kernels, whose M-tiles are the tile kernels' 64 rows
@@ -64,7 +65,8 @@ Plan make_plan(const moe_forward_args *a) {
     p.tile_row0 = take(sizeof(int32_t) * p.max_tiles);
     p.sorted_slot = take(sizeof(int32_t) * TK);
     p.slot_pos = take(sizeof(int32_t) * TK);
-    // W4A16 keeps the hidden states as they are and its intermediate in bf16 (i16 only)
+    // W4A16 and bf16 experts keep the hidden states as they are and the intermediate in
+    // bf16 (i16 only)
     p.a_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? T * D : T * D / 2);
     p.a_scales = a16 ? 0 : take(nv ? T * D / 16 : T * D / 32);
     p.a_tscale = take(sizeof(float));
@@ -81,7 +83,10 @@ Plan make_plan(const moe_forward_args *a) {
 
 hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
     if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.max_tiles, s);
-    const int fm = fmt == MOE_FMT_NVFP4 ? kFmtNV : (fmt == MOE_FMT_W4A16 ? kFmtA16 : kFmtMX8);
+    const int fm = fmt == MOE_FMT_NVFP4 ? kFmtNV
+                   : fmt == MOE_FMT_W4A16 ? kFmtA16
+                   : fmt == MOE_FMT_BF16  ? kFmtBF
+                                          : kFmtMX8;
     if (P.tile64) return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
     if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
         return launch_stream_gemm(g, fm, gate_up, P.max_tiles, s);
@@ -90,8 +95,10 @@ hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P,
 
 int32_t check_packed(const moe_packed &w, int32_t fmt, int32_t E, int32_t N, int32_t K) {
     if (w.fmt != fmt || w.E != E || w.N != N || w.K != K) return MOE_ERR_INVALID_ARG;
-    if (!w.codes || !w.scales || (fmt == MOE_FMT_NVFP4 && !w.tensor_scale)) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(w.codes) || !aligned16(w.scales) || (w.tensor_scale && ((uintptr_t)w.tensor_scale & 3u)))
+    const bool need_scales = fmt != MOE_FMT_BF16;  // bf16 weights have none
+    if (!w.codes || (need_scales && !w.scales) || (fmt == MOE_FMT_NVFP4 && !w.tensor_scale)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w.codes) || (w.scales && !aligned16(w.scales)) ||
+        (w.tensor_scale && ((uintptr_t)w.tensor_scale & 3u)))
         return MOE_ERR_ALIGNMENT;
     return MOE_OK;
 }
@@ -117,12 +124,15 @@ const char *moe_status_string(int32_t s) {
 int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     if (!out || !w) return MOE_ERR_INVALID_ARG;
     const int32_t fmt = out->fmt, E = out->E, N = out->N, K = out->K;
-    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_BF16)
+        return MOE_ERR_INVALID_ARG;
     if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
     if (N % 32 || K % 64) return MOE_ERR_INVALID_ARG;  // tiled layout of include/moe.h
-    if (!out->codes || !out->scales || (fmt == MOE_FMT_NVFP4 && !out->tensor_scale)) return MOE_ERR_INVALID_ARG;
+    if (!out->codes || (fmt != MOE_FMT_BF16 && !out->scales) || (fmt == MOE_FMT_NVFP4 && !out->tensor_scale))
+        return MOE_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(out->codes) || ((uintptr_t)out->tensor_scale & 3u)) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
+    if (fmt == MOE_FMT_BF16) return to_status(launch_pack_weights_bf16(w, E, N, K, out->codes, s));
     if (fmt == MOE_FMT_MXFP8)
         return to_status(launch_quant_weights_mxfp8(w, E, N, K, out->codes, out->scales, s));
     if (fmt == MOE_FMT_MXFP4)
@@ -164,7 +174,8 @@ namespace {
 // The size fields alone (what the workspace plan depends on).
 int32_t validate_shape(const moe_forward_args *a) {
     if (!a) return MOE_ERR_INVALID_ARG;
-    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8 && a->fmt != MOE_FMT_MXFP4 && a->fmt != MOE_FMT_W4A16)
+    if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8 && a->fmt != MOE_FMT_MXFP4 && a->fmt != MOE_FMT_W4A16 &&
+        a->fmt != MOE_FMT_BF16)
         return MOE_ERR_INVALID_ARG;
     if (a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->E > 4096) return MOE_ERR_INVALID_ARG;
     if (a->top_k < 1 || a->top_k > 8 || a->top_k > a->E) return MOE_ERR_INVALID_ARG;
@@ -213,7 +224,8 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     if (((uintptr_t)a->workspace & 255u) != 0) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
     uint8_t *ws = static_cast<uint8_t *>(a->workspace);
-    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4, a16 = a->fmt == MOE_FMT_W4A16;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
+    const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     const int32_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
     Ctrl *ctrl = reinterpret_cast<Ctrl *>(ws + P.ctrl);
     auto I32 = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
@@ -260,7 +272,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     } else if (mx4) {
         MOE_TRY(launch_quant_act_mxfp4(a->h, T, D, U8(P.a_codes), U8(P.a_scales), s));
     } else if (a16) {
-        // W4A16: the GEMM reads the bf16 hidden states directly
+        // W4A16 and bf16 experts: the GEMM reads the bf16 hidden states directly
     } else {
         MOE_TRY(launch_quant_act_mxfp8(a->h, T, D, U8(P.a_codes), U8(P.a_scales),
                                        reinterpret_cast<uint16_t *>(ws + P.a16), s));

@@ -275,6 +275,27 @@ hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, i
     return hipGetLastError();
 }
 
+// bf16 weights into the packed tile layout: one thread per 16-byte piece
+__global__ void __launch_bounds__(kThreads) pack_bf16_kernel(const uint16_t *__restrict__ w, int64_t n_pieces,
+                                                             int32_t K, int64_t pieces_per_expert,
+                                                             uint8_t *__restrict__ codes) {
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < n_pieces; r += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = r / pieces_per_expert;
+        int64_t n, k;
+        layout::piece_source_bf16(K, r - e * pieces_per_expert, n, k);
+        const int64_t rows = pieces_per_expert / (K / 8);
+        reinterpret_cast<uint4 *>(codes)[r] = *reinterpret_cast<const uint4 *>(w + (e * rows + n) * K + k);
+    }
+}
+
+hipError_t launch_pack_weights_bf16(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
+                                    hipStream_t s) {
+    const int64_t per = (int64_t)N * (K / 8);
+    const int64_t np = (int64_t)E * per;
+    hipLaunchKernelGGL(pack_bf16_kernel, dim3(grid_for(np)), dim3(kThreads), 0, s, w, np, K, per, codes);
+    return hipGetLastError();
+}
+
 hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
                                       uint8_t *scales, hipStream_t s) {
     const int64_t per = (int64_t)N * (K / 32);

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -51,11 +51,14 @@ extern "C" {
  * the OCP MXFP4 W4A4 variant for AMD Instinct in the vLLM recipe
  * "thinkingmachines/Inkling-Small", section "Variants"; W4A16 is the NVFP4 checkpoint
  * run with bf16 activations, its weights dequantised on the fly, same section).
- * MOE_FMT_W4A16 is a moe_forward format only: its packed weights are MOE_FMT_NVFP4. */
+ * MOE_FMT_W4A16 is a moe_forward format only: its packed weights are MOE_FMT_NVFP4.
+ * MOE_FMT_BF16 is the checkpoint's BF16 variant (same section): bf16 weights and
+ * activations, fp32 accumulation, the SwiGLU output rounded to bf16. */
 #define MOE_FMT_NVFP4 1
 #define MOE_FMT_MXFP8 2
 #define MOE_FMT_MXFP4 3
 #define MOE_FMT_W4A16 4
+#define MOE_FMT_BF16 5
 
 /*
  * Packed expert weights of one matrix kind for E experts, each logically [N][K]
@@ -73,6 +76,8 @@ extern "C" {
  *   MXFP4: codes  u8 [E][N/32][K/64][2][32][16] E2M1, element 2i in the low nibble of
  *          byte i: the block's 32 rows for columns 0-31, then for columns 32-63
  *          scales u8 [E][N/32][K/64][2][32]  E8M0, one per 32 columns, same order
+ *   BF16:  codes  u8 [E][N/32][K/64][32][128] bf16 values (column c at bytes 2c, 2c+1)
+ *          scales, tensor_scale unused (may be NULL)
  *          tensor_scale unused (may be NULL)
  * Sizes are those of the row-major arrays ([E][N][K/2] (NVFP4, MXFP4) / [E][N][K]
  * (MXFP8) codes, [E][N][K/16] (NVFP4) / [E][N][K/32] (MXFP8, MXFP4) scales); only the
@@ -119,7 +124,7 @@ typedef struct moe_taps {
 
 /* Arguments of moe_forward. */
 typedef struct moe_forward_args {
-    int32_t fmt;              /* MOE_FMT_NVFP4, _MXFP8, _MXFP4 or _W4A16                */
+    int32_t fmt;              /* MOE_FMT_NVFP4, _MXFP8, _MXFP4, _W4A16 or _BF16         */
     int32_t T, D, F, E;       /* tokens, d_model, d_ff, routed experts                  */
     int32_t top_k;            /* experts per token (8)                                  */
     int32_t e_begin, e_end;   /* local expert range [e_begin, e_end) computed here      */
@@ -189,13 +194,13 @@ size_t moe_forward_workspace_bytes(const moe_forward_args *a);
  * MoE layer forward over the local experts [e_begin, e_end):
  *  1. slots (t, j) with topk_idx[t][j] local are grouped by expert, stable in t*top_k+j;
  *  2. hidden states are quantised once per token to the layer's format (NVFP4 with
- *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block); W4A16 uses the
- *     bf16 hidden states as they are;
+ *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block); W4A16 and BF16
+ *     use the bf16 hidden states as they are;
  *  3. gate_up GEMM per expert (fp32 accumulation; NVFP4 sums are multiplied by
  *     fl32(s_h * s_gate_up[e]), W4A16 sums by s_gate_up[e]), then
  *     h = SwiGLU = g * u / (1 + exp(-g));
  *  4. h is quantised to the layer's format (NVFP4: one tensor scale over all S rows);
- *     W4A16 rounds it to bf16 (nearest, ties to even);
+ *     W4A16 and BF16 round it to bf16 (nearest, ties to even);
  *  5. down GEMM per expert (NVFP4: times fl32(s_inter * s_down[e]); W4A16: times
  *     s_down[e]) -> y fp32;
  *  6. out[t] = sum over the token's local slots, j ascending, of topk_w[t][j] * y.

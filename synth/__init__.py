@@ -159,7 +159,7 @@ class Workload:
     """One synthetic MoE-layer workload (shapes, formats, value recipe)."""
     index: int
     name: str
-    fmt: str            # "nvfp4", "mxfp8", "mxfp4" or "w4a16"
+    fmt: str            # "nvfp4", "mxfp8", "mxfp4", "w4a16" or "bf16"
     T: int              # tokens
     D: int              # d_model
     F: int              # d_ff
@@ -238,6 +238,10 @@ WORKLOADS = [
     Workload(7, "decode-w4a16", "w4a16", T=64, D=4096, F=2560, E=384, seed=7),
     Workload(8, "prefill-w4a16-ep4", "w4a16", T=8192, D=4096, F=2560, E=384,
              e_begin=0, e_end=96, seed=8),
+    # bf16 experts (unquantised) at the same two shapes
+    Workload(9, "decode-bf16", "bf16", T=64, D=4096, F=2560, E=384, seed=9),
+    Workload(10, "prefill-bf16-ep4", "bf16", T=8192, D=4096, F=2560, E=384,
+             e_begin=0, e_end=96, seed=10),
 ]
 
 

@@ -50,7 +50,7 @@ def check_intermediate_codes(fmt: str, inter: np.ndarray, codes: np.ndarray, sca
                              tscale: float | None):
     """The GPU's intermediate codes equal the oracle quantiser applied to the GPU's own
     pre-quantisation fp32 values (bit-exact), for the S computed rows."""
-    if fmt == "w4a16":
+    if fmt in ("w4a16", "bf16"):
         # bf16 rounding of the GPU's own fp32 values (no scales)
         oc = oracle.round_bf16(inter)
         bad = int(np.count_nonzero(oc != np.asarray(codes).view(np.uint16)))
@@ -91,7 +91,7 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
     r_stage = rms(stage[sel])
     e_stage = float(np.abs(out[sel] - stage[sel]).max()) / r_stage
     assert e_stage <= 2e-3, f"stage-wise output error {e_stage:.2e} x RMS"
-    if fmt == "w4a16":
+    if fmt in ("w4a16", "bf16"):
         gpu_inter_codes = np.asarray(gpu_inter_codes).view(np.uint16)
         oracle_inter_codes = np.asarray(oracle_inter_codes).view(np.uint16)
     cb = gpu_inter_codes.reshape(S, -1) != oracle_inter_codes.reshape(S, -1)

@@ -29,7 +29,7 @@ def test_header_functions_are_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 4
+    assert lib.moe_abi_version() == 5
     assert lib.moe_status_string(EWS) == b"workspace missing or too small"
 
 
@@ -59,6 +59,10 @@ def test_forward_validation_accepts_the_workloads():
     m4.down = moe.MoePacked(3, 384, 4096, 2560, A16, A16, 0)
     assert _validate(m4) == OK
     assert _validate(_args(fmt=4)) == OK  # W4A16 on NVFP4-packed weights
+    b16 = _args(fmt=5)
+    b16.gate_up = moe.MoePacked(5, 384, 5120, 4096, A16, 0, 0)  # bf16 weights: no scales
+    b16.down = moe.MoePacked(5, 384, 4096, 2560, A16, 0, 0)
+    assert _validate(b16) == OK
     assert _validate(_args(T=0, h=0, topk_idx=0, topk_w=0, out=0)) == OK  # empty batch
 
 
@@ -79,7 +83,7 @@ def test_mxfp4_needs_256_wide_d_model():
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(fmt=5), EINVAL), (dict(fmt=0), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
+    (dict(fmt=6), EINVAL), (dict(fmt=0), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
     (dict(e_begin=10, e_end=10), EINVAL), (dict(e_end=385), EINVAL), (dict(e_begin=-1), EINVAL),
     (dict(E=5000), EINVAL), (dict(h=0), EINVAL), (dict(out=0), EINVAL),
     (dict(D=4000), EUNSUP), (dict(F=2500), EUNSUP),

@@ -43,6 +43,14 @@ def _adversarial_masters(E, N, K, seed):
     return w
 
 
+def test_pack_bf16_weights_bitexact():
+    """bf16 experts: the packing is a pure reordering into the tile layout."""
+    w = _adversarial_masters(5, 256, 512, seed=8)
+    got = moe.quantize_weights("bf16", to_dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(untile(host(got.codes)).view(np.uint16), w), "packed bf16 weights differ"
+
+
 @pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
 @pytest.mark.parametrize("shape", [(5, 256, 512), (2, 96, 2048)])
 def test_quantize_weights_bitexact(fmt, shape):
@@ -181,6 +189,12 @@ LAYER_CASES = [
     dict(name="top2-ep-share-mxfp4", wl=synth.custom("mxfp4", T=300, D=256, F=128, E=32, k=2, e_begin=3, e_end=11,
                                                      seed=74)),
     dict(name="e1024-nvfp4", wl=synth.custom("nvfp4", T=64, D=128, F=128, E=1024, seed=75)),
+    # bf16 experts (unquantised weights and activations) on all three kernel families
+    dict(name="decode-bf16", wl=synth.custom("bf16", T=40, D=256, F=256, E=16, seed=81)),
+    dict(name="prefill-bf16", wl=synth.custom("bf16", T=300, D=256, F=256, E=16, seed=82)),
+    dict(name="prefill-bf16-k1024", wl=synth.custom("bf16", T=1024, D=1024, F=512, E=32, seed=83)),
+    dict(name="stream-bf16-k2048", wl=synth.custom("bf16", T=48, D=2048, F=1536, E=16, seed=84)),
+    dict(name="ep-share-bf16", wl=synth.custom("bf16", T=400, D=512, F=384, E=24, e_begin=6, e_end=15, seed=85)),
 ]
 
 
@@ -203,12 +217,16 @@ def test_forward_parity(c):
     torch.cuda.synchronize()
     tp = {k_: host(v) for k_, v in taps.items()}
 
-    # oracle: its own quantised weights, routing and layer
-    o_gu, o_dn = oracle.quantize_weights(fmt, gu_m), oracle.quantize_weights(fmt, dn_m)
+    # oracle: its own quantised weights (bf16 experts: the masters), routing and layer
+    if fmt == "bf16":
+        o_dn = dn_m
+        wkw = dict(gate_up_master=gu_m, down_master=dn_m)
+    else:
+        o_gu, o_dn = oracle.quantize_weights(fmt, gu_m), oracle.quantize_weights(fmt, dn_m)
+        wkw = dict(gate_up=o_gu, down=o_dn)
     o_idx, o_w = oracle.route(h, wr, k=k, bias=bias)
     assert np.array_equal(host(idx), o_idx)
-    ref, otp = oracle.moe_forward(fmt, h, o_idx, o_w, D=D, F=F, E=E, e_begin=eb, e_end=ee, gate_up=o_gu,
-                                  down=o_dn, taps=True)
+    ref, otp = oracle.moe_forward(fmt, h, o_idx, o_w, D=D, F=F, E=E, e_begin=eb, e_end=ee, taps=True, **wkw)
     counts, offs, ss = oracle.permute(o_idx, eb, ee)
     S = int(offs[-1])
 
@@ -216,7 +234,7 @@ def test_forward_parity(c):
     assert np.array_equal(tp["counts"], counts)
     assert np.array_equal(tp["offsets"], offs)
     assert np.array_equal(tp["sorted_slot"][:S], ss)
-    if fmt != "w4a16":  # W4A16 keeps the hidden states in bf16
+    if fmt not in ("w4a16", "bf16"):  # W4A16 and bf16 experts keep the hidden states in bf16
         assert np.array_equal(tp["a_codes"], otp["a_codes"]), "hidden-state codes differ"
         assert np.array_equal(tp["a_scales"], otp["a_scales"]), "hidden-state scales differ"
     if fmt == "nvfp4":
