@@ -82,7 +82,9 @@ def gate_up_kernel(wl) -> str:
     streaming kernel when K allows; MXFP4 always runs its scaled-FP4 MFMA kernel)."""
     if wl.fmt == "mxfp4":
         return "mx4_gemm_kernel"
-    if wl.T * wl.k // wl.E >= 48 and wl.D % 512 == 0 and wl.F % 256 == 0:
+    # the tile kernels' N-blocks: MXFP8 256 weight rows (128-row M-tiles), the others 512
+    d_blk, f_blk = (256, 128) if wl.fmt == "mxfp8" else (512, 256)
+    if wl.T * wl.k // wl.E >= 48 and wl.D % d_blk == 0 and wl.F % f_blk == 0:
         return "tile_gemm_kernel"
     if wl.D % 512 == 0 and wl.D // 512 <= 8:
         return "stream_gemm_kernel"

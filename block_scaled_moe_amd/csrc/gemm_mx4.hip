@@ -272,7 +272,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
 
 }  // namespace
 
-static_assert(kBM == 64, "the MXFP4 kernels share the tile kernels' 64-row M-tiles");
+static_assert(kBM == 64, "the plan gives MXFP4 layers 64-row M-tiles");
 
 bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up) {
     if (K <= 0 || N <= 0 || K % 64) return false;

@@ -38,21 +38,32 @@ using namespace gemm_detail;
 
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-#ifndef MOE_TILE_BM
-#define MOE_TILE_BM 64
+constexpr int kKC = 64, kThreads = 256, kGroup = 4;
+constexpr int kAStride = kKC * 2 + 16;  // LDS bytes per activation row
+
+// rows per M-tile: 128 for NVFP4 W4A4 and MXFP8 (each expanded weight fragment feeds four
+// 32-row MFMAs, halving the expansion VALU per MFMA), 64 for the others
+#ifndef MOE_TILE_BM_NV
+#define MOE_TILE_BM_NV 64
 #endif
-constexpr int kBM = MOE_TILE_BM, kKC = 64, kThreads = 256, kGroup = 4;
-constexpr int kMS = kBM / 32;  // 32-row MFMA subtiles per wave in M
-constexpr int kAStride = kKC * 2 + 16;                  // LDS bytes per activation row
-constexpr int kAStage = kBM * kAStride;                 // one LDS buffer
-constexpr int kAItems = kBM * kKC * 2 / 16 / kThreads;  // 16-byte activation loads per thread
-static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the threads");
+#ifndef MOE_TILE_BM_MX
+#define MOE_TILE_BM_MX 128
+#endif
+template <int FM>
+constexpr int tile_bm() {
+    return FM == kFmtNV ? MOE_TILE_BM_NV : (FM == kFmtMX8 ? MOE_TILE_BM_MX : 64);
+}
+template <int BM>
+constexpr int a_stage() { return BM * kAStride; }  // one LDS activation buffer
+template <int BM>
+constexpr int a_items() { return BM * kKC * 2 / 16 / kThreads; }  // 16-byte activation loads per thread
+static_assert(64 * kKC * 2 / 16 % kThreads == 0, "activation loads tile the threads");
 
 #ifndef MOE_TILE_WR
 #define MOE_TILE_WR 2  // weight chunks in flight (register ring slots)
 #endif
 #ifndef MOE_TILE_NS_NV
-#define MOE_TILE_NS_NV 4
+#define MOE_TILE_NS_NV (MOE_TILE_BM_NV == 128 ? 2 : 4)
 #endif
 #ifndef MOE_TILE_NS_MX
 #define MOE_TILE_NS_MX 2
@@ -61,8 +72,9 @@ static_assert(kBM * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thr
 #define MOE_TILE_NS_A16 4
 #endif
 
-// 32-row weight subtiles per wave in N: NVFP4 4 (its expansion costs twice MXFP8's VALU,
-// so each activation fragment feeds more MFMAs; 234 registers, two waves per SIMD),
+// 32-row weight subtiles per wave in N: 2 with 128-row tiles (128 accumulator registers,
+// two waves per SIMD); with 64-row tiles NVFP4 4 (its expansion costs twice MXFP8's
+// VALU, so each activation fragment feeds more MFMAs; 234 registers, two waves per SIMD),
 // MXFP8 2 (three waves per SIMD; at 4 it spills), W4A16 as NVFP4
 template <int FM>
 constexpr int tile_ns() {
@@ -76,24 +88,37 @@ constexpr int kEpiStride() { return 16 * NS + 1; }
 
 // LDS of one workgroup: the double-buffered activation tile, or for the MXFP8 gate_up
 // epilogue the four waves' SwiGLU tiles if larger
-template <int FM, bool GATE_UP, int NS>
+template <int FM, bool GATE_UP, int NS, int BM>
 constexpr int tile_smem_bytes() {
-    return (FM == kFmtMX8 && GATE_UP && 4 * kBM * kEpiStride<NS>() * 4 > 2 * kAStage) ? 4 * kBM * kEpiStride<NS>() * 4
-                                                                             : 2 * kAStage;
+    return (FM == kFmtMX8 && GATE_UP && 4 * BM * kEpiStride<NS>() * 4 > 2 * a_stage<BM>()) ? 4 * BM * kEpiStride<NS>() * 4
+                                                                                     : 2 * a_stage<BM>();
 }
 
-template <int FM, bool GATE_UP, int NS>
-__global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) tile_gemm_kernel(const GemmArgs p) {
+// waves per SIMD the register budget is set for
+template <int NS, int BM>
+constexpr int tile_waves_per_simd() { return BM == 64 ? (NS == 2 ? 3 : 2) : (NS == 2 ? 2 : 1); }
+
+// An expert's last 128-row tile often holds at most 64 rows. Such a half tile runs half
+// the M-subtiles; for NVFP4 weights it covers two N-blocks instead (the work item of the
+// even N-block takes both, the odd one exits), keeping the 64-row kernel's operand reuse:
+// each expanded weight fragment feeds two MFMAs and each activation fragment 2 NS.
+template <int FM>
+constexpr bool half_tile_doubles_n() { return FM == kFmtNV || FM == kFmtA16; }
+
+template <int FM, bool GATE_UP, int NS, int BM>
+__global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) tile_gemm_kernel(const GemmArgs p) {
+    constexpr int kBM = BM, kMS = BM / 32;  // rows per M-tile, 32-row MFMA subtiles per wave
+    constexpr int kAStage = a_stage<BM>(), kAItems = a_items<BM>();
     constexpr bool NV = FM == kFmtNV || FM == kFmtA16;  // NVFP4 weights (W4A4 or W4A16)
     constexpr bool BW = FM == kFmtBF;                    // bf16 weights (no scales)
     constexpr bool BF = FM != kFmtNV;                    // bf16 operands and MFMA
     constexpr bool A16 = FM == kFmtA16;
     constexpr bool O16 = FM == kFmtA16 || FM == kFmtBF;  // bf16 intermediate out of gate_up
     using Frag = typename std::conditional<BF, bf16x8, half8>::type;
-    constexpr int BN = 128 * NS;              // weight rows per workgroup
+    constexpr int BN = 128 * NS;              // weight rows per workgroup (one N-block)
     constexpr int CV = NV ? 1 : (BW ? 4 : 2);  // 16-byte code loads per weight row per lane per chunk
     static_assert(NS % 2 == 0, "gate_up pairs subtiles");
-    __shared__ __attribute__((aligned(16))) uint8_t smem[tile_smem_bytes<FM, GATE_UP, NS>()];
+    __shared__ __attribute__((aligned(16))) uint8_t smem[tile_smem_bytes<FM, GATE_UP, NS, BM>()];
 
     const int K = p.K, N = p.N, F = N / 2;
     const int NB = GATE_UP ? F / (BN / 2) : N / BN;
@@ -123,23 +148,6 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
     const uint8_t *w_codes_e = p.w_codes + (int64_t)e * N * (NV ? K / 2 : (BW ? 2 * K : K));
     const uint8_t *w_scales_e = p.w_scales + (int64_t)e * N * (NV ? K / 16 : K / 32);
 
-    // ---- this lane's weight rows, one per N subtile (each subtile is one row group)
-    const uint8_t *wc[NS];
-    const uint8_t *ws[NS];
-#pragma unroll
-    for (int ns = 0; ns < NS; ++ns) {
-        int row;
-        if (GATE_UP) {
-            const int col = nb * (BN / 2) + wave * 16 * NS + 32 * (ns % (NS / 2)) + l32;
-            row = ns < NS / 2 ? col : F + col;
-        } else {
-            row = nb * BN + wave * 32 * NS + 32 * ns + l32;
-        }
-        const int64_t blk0 = (int64_t)(row >> 5) * kb;
-        wc[ns] = w_codes_e + blk0 * CBLK + l32 * CB + (CB / 2) * g2;
-        ws[ns] = BW ? nullptr : w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
-    }
-
     // ---- activation staging: global -> registers -> LDS. Rows past the tile's end load
     // the tile's first row instead of zeros: their accumulators are never stored, and
     // unconditional loads from one global base keep the wait counts per chunk.
@@ -155,224 +163,293 @@ __global__ void __launch_bounds__(kThreads, kMS == 2 ? (NS == 2 ? 3 : 2) : 1) ti
         const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
         a_off[i] = arow * K * 2 + 16 * q;
     }
-    float16_t acc[kMS][NS];
-#pragma unroll
-    for (int i = 0; i < kMS; ++i)
-#pragma unroll
-        for (int j = 0; j < NS; ++j) acc[i][j] = (float16_t){};
+    const float scl = FM == kFmtNV ? p.a_tscale[0] * p.w_tscale[e] : (A16 ? p.w_tscale[e] : 1.0f);
 
     // software pipeline: activations two chunks ahead in two register sets (chunk c + 2
     // is loaded while chunk c is multiplied, and stored to LDS at the end of chunk c + 1),
     // weights WR chunks ahead in a WR-slot register ring
     constexpr int WR = MOE_TILE_WR;
-    u32x4 a_reg[2][kAItems];
-    u32x4 wcode[WR][NS][CV];
-    uint32_t wsc[WR][NS];
     const int n_chunks = K / kKC;  // a multiple of WR (see tile_gemm_supported)
 
 #define MOE_LOAD_A(set, c)                                                                                 \
-    _Pragma("unroll") for (int i = 0; i < kAItems; ++i) a_reg[set][i] =                                    \
+    _Pragma("unroll") for (int i = 0; i < AI; ++i) a_reg[set][i] =                                        \
         *reinterpret_cast<const u32x4 *>(a_base + a_off[i] + 2 * kKC * (c));
 #define MOE_STORE_A(buf, set)                                                                              \
-    _Pragma("unroll") for (int i = 0; i < kAItems; ++i)                                                    \
+    _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                         \
         *reinterpret_cast<u32x4 *>(smem + (buf) * kAStage + a_dst[i]) = a_reg[set][i];
 #define MOE_LOAD_W(slot, c)                                                                                \
-    _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                    \
+    _Pragma("unroll") for (int ns = 0; ns < NSA; ++ns) {                                                   \
         _Pragma("unroll") for (int v = 0; v < CV; ++v) wcode[slot][ns][v] =                                \
             *reinterpret_cast<const u32x4 *>(wc[ns] + (int64_t)CBLK * (c) + 16 * v);                       \
         wsc[slot][ns] = BW ? 0u : *reinterpret_cast<const uint32_t *>(ws[ns] + (int64_t)SBLK * (c));      \
     }
 
-    MOE_LOAD_A(0, 0);
-    MOE_STORE_A(0, 0);
-    MOE_LOAD_A(1, 1);
-#pragma unroll
-    for (int r = 0; r < WR; ++r) { MOE_LOAD_W(r, r); }
-    __syncthreads();
+    // The tile for MSA 32-row M-subtiles (rows 0 .. 32 MSA - 1) and NSA 32-row weight
+    // subtiles per wave: NS of N-block nb, and for a doubled half tile NS more of nb + 1.
+    // Subtile ns belongs to N-block nb + ns / NS; within a block, gate_up pairs gate
+    // subtile q with up subtile q + NS / 2.
+    auto run = [&](auto msa_c, auto nsa_c) __attribute__((always_inline)) {
+        constexpr int MSA = decltype(msa_c)::value, NSA = decltype(nsa_c)::value;
+        constexpr int NBW = NSA / NS;            // N-blocks covered
+        constexpr int AI = kAItems * MSA / kMS;  // activation loads per thread per chunk
 
-    for (int c0 = 0; c0 < n_chunks; c0 += WR) {
+        // ---- this lane's weight rows, one per N subtile (each subtile is one row group)
+        const uint8_t *wc[NSA];
+        const uint8_t *ws[NSA];
 #pragma unroll
-        for (int j = 0; j < WR; ++j) {
-            const int c = c0 + j;
-            // LDS buffer c%2 holds chunk c, register set (c+1)%2 chunk c + 1, weight slot j
-            // chunk c. Prefetches past the end reload chunk n - 1 (in bounds, unused), so
-            // the body has no branches and every wait count is exact.
-            MOE_LOAD_A(j & 1, min(c + 2, n_chunks - 1));
-            __builtin_amdgcn_sched_barrier(0);
-            const uint8_t *abuf = smem + (j & 1) * kAStage;
-            // scale words: NVFP4 holds the row's 4 block scales of the chunk (this lane's
-            // pair is bytes 2g, 2g+1); MXFP8 holds two rows' 2 block scales (this lane's
-            // is byte 2 (row % 2) + g)
-            half2_t sc_nv[NS];
-            float sc_mx[NS];
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-                if constexpr (NV) {
-                    sc_nv[ns] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsc[j][ns] >> (16 * g2), 1.0f, false);
-                } else if constexpr (!BW) {
-                    sc_mx[ns] = __uint_as_float(((wsc[j][ns] >> (8 * (2 * (l32 & 1) + g2))) & 0xffu) << 23);
-                }
+        for (int ns = 0; ns < NSA; ++ns) {
+            const int bn = nb + ns / NS, ls = ns % NS;
+            int row;
+            if (GATE_UP) {
+                const int col = bn * (BN / 2) + wave * 16 * NS + 32 * (ls % (NS / 2)) + l32;
+                row = ls < NS / 2 ? col : F + col;
+            } else {
+                row = bn * BN + wave * 32 * NS + 32 * ls + l32;
             }
+            const int64_t blk0 = (int64_t)(row >> 5) * kb;
+            wc[ns] = w_codes_e + blk0 * CBLK + l32 * CB + (CB / 2) * g2;
+            ws[ns] = BW ? nullptr : w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
+        }
+
+        float16_t acc[MSA][NSA];
 #pragma unroll
-            for (int s = 0; s < kKC / 16; ++s) {
-                Frag af[kMS];
+        for (int i = 0; i < MSA; ++i)
 #pragma unroll
-                for (int ms = 0; ms < kMS; ++ms)
-                    af[ms] = *reinterpret_cast<const Frag *>(abuf + (32 * ms + l32) * kAStride + 64 * g2 + 16 * s);
+            for (int j = 0; j < NSA; ++j) acc[i][j] = (float16_t){};
+
+        u32x4 a_reg[2][AI];
+        u32x4 wcode[WR][NSA][CV];
+        uint32_t wsc[WR][NSA];
+        MOE_LOAD_A(0, 0);
+        MOE_STORE_A(0, 0);
+        MOE_LOAD_A(1, 1);
 #pragma unroll
-                for (int ns = 0; ns < NS; ++ns) {
+        for (int r = 0; r < WR; ++r) { MOE_LOAD_W(r, r); }
+        __syncthreads();
+
+        for (int c0 = 0; c0 < n_chunks; c0 += WR) {
+#pragma unroll
+            for (int j = 0; j < WR; ++j) {
+                const int c = c0 + j;
+                // LDS buffer c%2 holds chunk c, register set (c+1)%2 chunk c + 1, weight slot
+                // j chunk c. Prefetches past the end reload chunk n - 1 (in bounds, unused),
+                // so the body has no branches and every wait count is exact.
+                MOE_LOAD_A(j & 1, min(c + 2, n_chunks - 1));
+                __builtin_amdgcn_sched_barrier(0);
+                const uint8_t *abuf = smem + (j & 1) * kAStage;
+                // scale words: NVFP4 holds the row's 4 block scales of the chunk (this lane's
+                // pair is bytes 2g, 2g+1); MXFP8 holds two rows' 2 block scales (this lane's
+                // is byte 2 (row % 2) + g)
+                half2_t sc_nv[NSA];
+                float sc_mx[NSA];
+#pragma unroll
+                for (int ns = 0; ns < NSA; ++ns) {
                     if constexpr (NV) {
-                        if constexpr (A16) {
-                            const bf16x8 bf = dequant_nvfp4_bf16(wcode[j][ns][0][s], (float)sc_nv[ns][s >> 1]);
+                        sc_nv[ns] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsc[j][ns] >> (16 * g2), 1.0f, false);
+                    } else if constexpr (!BW) {
+                        sc_mx[ns] = __uint_as_float(((wsc[j][ns] >> (8 * (2 * (l32 & 1) + g2))) & 0xffu) << 23);
+                    }
+                }
 #pragma unroll
-                            for (int ms = 0; ms < kMS; ++ms)
+                for (int s = 0; s < kKC / 16; ++s) {
+                    Frag af[MSA];
+#pragma unroll
+                    for (int ms = 0; ms < MSA; ++ms)
+                        af[ms] = *reinterpret_cast<const Frag *>(abuf + (32 * ms + l32) * kAStride + 64 * g2 + 16 * s);
+#pragma unroll
+                    for (int ns = 0; ns < NSA; ++ns) {
+                        if constexpr (NV) {
+                            if constexpr (A16) {
+                                const bf16x8 bf = dequant_nvfp4_bf16(wcode[j][ns][0][s], (float)sc_nv[ns][s >> 1]);
+#pragma unroll
+                                for (int ms = 0; ms < MSA; ++ms)
+                                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                            } else {
+                                const _Float16 sc = sc_nv[ns][s >> 1];
+                                const half8 bf = dequant_nvfp4(wcode[j][ns][0][s], sc);
+#pragma unroll
+                                for (int ms = 0; ms < MSA; ++ms)
+                                    acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                            }
+                        } else if constexpr (BW) {
+                            const bf16x8 bf = __builtin_bit_cast(bf16x8, wcode[j][ns][s]);  // the stored values
+#pragma unroll
+                            for (int ms = 0; ms < MSA; ++ms)
                                 acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                         } else {
-                            const _Float16 sc = sc_nv[ns][s >> 1];
-                            const half8 bf = dequant_nvfp4(wcode[j][ns][0][s], sc);
+                            const u32x4 q = wcode[j][ns][s >> 1];
+                            const u32x2 cw = (s & 1) ? (u32x2){q.z, q.w} : (u32x2){q.x, q.y};
+                            const bf16x8 bf = dequant_mxfp8(cw, sc_mx[ns]);
 #pragma unroll
-                            for (int ms = 0; ms < kMS; ++ms)
-                                acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                            for (int ms = 0; ms < MSA; ++ms)
+                                acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
                         }
-                    } else if constexpr (BW) {
-                        const bf16x8 bf = __builtin_bit_cast(bf16x8, wcode[j][ns][s]);  // the stored values
+                    }
+                }
+                MOE_LOAD_W(j, min(c + WR, n_chunks - 1));
+                // buffer (c+1)%2 was last read in chunk c - 1, before the previous barrier
+                MOE_STORE_A((j + 1) & 1, (j + 1) & 1);
+                __syncthreads();
+            }
+        }
+
+        // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
+        if (GATE_UP && O16) {
+            // W4A16 and bf16 experts: the SwiGLU output rounded to bf16 (nearest even) is
+            // the down GEMM's input
 #pragma unroll
-                        for (int ms = 0; ms < kMS; ++ms)
-                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
-                    } else {
-                        const u32x4 q = wcode[j][ns][s >> 1];
-                        const u32x2 cw = (s & 1) ? (u32x2){q.z, q.w} : (u32x2){q.x, q.y};
-                        const bf16x8 bf = dequant_mxfp8(cw, sc_mx[ns]);
+            for (int bw = 0; bw < NBW; ++bw)
 #pragma unroll
-                        for (int ms = 0; ms < kMS; ++ms)
-                            acc[ms][ns] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ms], bf, acc[ms][ns], 0, 0, 0);
+                for (int q = 0; q < NS / 2; ++q) {
+                    const int f = (nb + bw) * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+#pragma unroll
+                    for (int ms = 0; ms < MSA; ++ms)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                            if (m < rows) {
+                                const int64_t o = (int64_t)(p0 + m) * F + f;
+                                const float hv = swiglu(acc[ms][bw * NS + q][v] * scl, acc[ms][bw * NS + q + NS / 2][v] * scl);
+                                static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
+                                if (p.o_tap) p.o_tap[o] = hv;
+                            }
+                        }
+                }
+        } else if (GATE_UP && NV) {
+            uint32_t amax = 0;
+#pragma unroll
+            for (int bw = 0; bw < NBW; ++bw)
+#pragma unroll
+                for (int q = 0; q < NS / 2; ++q) {
+                    const int f = (nb + bw) * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+#pragma unroll
+                    for (int ms = 0; ms < MSA; ++ms) {
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                            const float hv = swiglu(acc[ms][bw * NS + q][v] * scl, acc[ms][bw * NS + q + NS / 2][v] * scl);
+                            if (m < rows) {
+                                p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
+                                amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
+                            }
+                        }
+                    }
+                }
+            for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+            if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
+        } else if (GATE_UP) {
+            // MXFP8: the wave's SwiGLU tile (32 MSA rows x 16 NS columns, 32-column
+            // blocks) goes through its own LDS region; lane r then quantises whole blocks
+            // of row r with 16-byte stores. The A stages are free: every wave passed the
+            // loop's last barrier.
+            static_assert(FM != kFmtMX8 || !half_tile_doubles_n<FM>(), "one N-block per MXFP8 tile");
+            float *epi = reinterpret_cast<float *>(smem) + wave * kBM * kEpiStride<NS>();
+#pragma unroll
+            for (int q = 0; q < NS / 2; ++q)
+#pragma unroll
+                for (int ms = 0; ms < MSA; ++ms)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                        epi[m * kEpiStride<NS>() + 32 * q + l32] = swiglu(acc[ms][q][v], acc[ms][q + NS / 2][v]);
+                    }
+            __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+            for (int m = lane; m < 32 * MSA; m += 64) {
+                if (m >= rows) continue;
+                const int64_t row = p0 + m;
+#pragma unroll
+                for (int q = 0; q < NS / 2; ++q) {
+                    const int fb = nb * (BN / 2) + wave * 16 * NS + 32 * q;  // first column of the block
+                    float x[32];
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) x[i] = epi[m * kEpiStride<NS>() + 32 * q + i];
+                    uint32_t cw[8];
+                    const int sc8 = mxfp8_quant_block(x, cw);
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + fb);
+                    dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                    dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
+                    p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc8;
+                    store_dequant_mxfp8_32(static_cast<uint8_t *>(p.o_vals) + (row * F + fb) * 2, cw, sc8);
+                    if (p.o_tap) {
+                        float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
                     }
                 }
             }
-            MOE_LOAD_W(j, min(c + WR, n_chunks - 1));
-            // buffer (c+1)%2 was last read in chunk c - 1, before the previous barrier
-            MOE_STORE_A((j + 1) & 1, (j + 1) & 1);
-            __syncthreads();
+        } else {
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < NSA; ++ns) {
+                    const int n = (nb + ns / NS) * BN + wave * 32 * NS + 32 * (ns % NS) + l32;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                        if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = NV ? acc[ms][ns][v] * scl : acc[ms][ns][v];
+                    }
+                }
         }
-    }
+    };
 #undef MOE_LOAD_A
 #undef MOE_STORE_A
 #undef MOE_LOAD_W
 
-    // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
-    const float scl = FM == kFmtNV ? p.a_tscale[0] * p.w_tscale[e] : (A16 ? p.w_tscale[e] : 1.0f);
-    if (GATE_UP && O16) {
-        // W4A16 and bf16 experts: the SwiGLU output rounded to bf16 (nearest even) is the
-        // down GEMM's input
-#pragma unroll
-        for (int q = 0; q < NS / 2; ++q) {
-            const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
-#pragma unroll
-            for (int ms = 0; ms < kMS; ++ms)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                    if (m < rows) {
-                        const int64_t o = (int64_t)(p0 + m) * F + f;
-                        const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
-                        static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
-                        if (p.o_tap) p.o_tap[o] = hv;
-                    }
-                }
-        }
-    } else if (GATE_UP && NV) {
-        uint32_t amax = 0;
-#pragma unroll
-        for (int q = 0; q < NS / 2; ++q) {
-            const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
-#pragma unroll
-            for (int ms = 0; ms < kMS; ++ms) {
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                    const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
-                    if (m < rows) {
-                        p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
-                        amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
-                    }
-                }
+    if constexpr (kMS == 4) {
+        if (rows <= 64) {
+            if constexpr (half_tile_doubles_n<FM>()) {
+                if (nb & 1) return;  // the even N-block's item covers this one
+                run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2 * NS>{});
+            } else {
+                run(std::integral_constant<int, 2>{}, std::integral_constant<int, NS>{});
             }
-        }
-        for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
-        if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
-    } else if (GATE_UP) {
-        // MXFP8: the wave's SwiGLU tile (kBM rows x 16 NS columns, 32-column blocks) goes
-        // through its own LDS region; lane r then quantises whole blocks of row r with
-        // 16-byte stores. The A stages are free: every wave passed the loop's last barrier.
-        float *epi = reinterpret_cast<float *>(smem) + wave * kBM * kEpiStride<NS>();
-#pragma unroll
-        for (int q = 0; q < NS / 2; ++q)
-#pragma unroll
-            for (int ms = 0; ms < kMS; ++ms)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                    epi[m * kEpiStride<NS>() + 32 * q + l32] = swiglu(acc[ms][q][v], acc[ms][q + NS / 2][v]);
-                }
-        __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
-        for (int m = lane; m < kBM; m += 64) {
-            if (m >= rows) continue;
-            const int64_t row = p0 + m;
-#pragma unroll
-            for (int q = 0; q < NS / 2; ++q) {
-                const int fb = nb * (BN / 2) + wave * 16 * NS + 32 * q;  // first column of the block
-                float x[32];
-#pragma unroll
-                for (int i = 0; i < 32; ++i) x[i] = epi[m * kEpiStride<NS>() + 32 * q + i];
-                uint32_t cw[8];
-                const int sc8 = mxfp8_quant_block(x, cw);
-                u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + fb);
-                dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
-                dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
-                p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc8;
-                store_dequant_mxfp8_32(static_cast<uint8_t *>(p.o_vals) + (row * F + fb) * 2, cw, sc8);
-                if (p.o_tap) {
-                    float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
-                }
-            }
+        } else {
+            run(std::integral_constant<int, 4>{}, std::integral_constant<int, NS>{});
         }
     } else {
-#pragma unroll
-        for (int ms = 0; ms < kMS; ++ms)
-#pragma unroll
-            for (int ns = 0; ns < NS; ++ns) {
-                const int n = nb * BN + wave * 32 * NS + 32 * ns + l32;
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                    if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = NV ? acc[ms][ns][v] * scl : acc[ms][ns][v];
-                }
-            }
+        run(std::integral_constant<int, kMS>{}, std::integral_constant<int, NS>{});
     }
 }
 
 template <int FM, bool GATE_UP>
 hipError_t launch_t(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
-    constexpr int NS = tile_ns<FM>();
+    constexpr int NS = tile_ns<FM>(), BM = tile_bm<FM>();
     constexpr int BN = 128 * NS;
     const int64_t nb = GATE_UP ? (a.N / 2) / (BN / 2) : a.N / BN;
     const int64_t items = (int64_t)max_tiles * nb;
     const int64_t grid = (items + 7) / 8 * 8;
-    hipLaunchKernelGGL((tile_gemm_kernel<FM, GATE_UP, NS>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((tile_gemm_kernel<FM, GATE_UP, NS, BM>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int32_t tile_gemm_bm() { return kBM; }
+int32_t tile_gemm_bm(int fm) {
+    switch (fm) {
+        case kFmtNV: return tile_bm<kFmtNV>();
+        case kFmtMX8: return tile_bm<kFmtMX8>();
+        case kFmtA16: return tile_bm<kFmtA16>();
+        case kFmtBF: return tile_bm<kFmtBF>();
+        default: return 64;
+    }
+}
 
-bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up) {
-    // every format must fit, since the plan picks one kernel family per layer shape
-    constexpr int ns_max = MOE_TILE_NS_NV > MOE_TILE_NS_MX ? MOE_TILE_NS_NV : MOE_TILE_NS_MX;
-    const int bn = 128 * (ns_max > MOE_TILE_NS_A16 ? ns_max : MOE_TILE_NS_A16);
-    return K % (MOE_TILE_WR * kKC) == 0 && (gate_up ? (N / 2) % (bn / 2) == 0 : N % bn == 0);
+template <int FM>
+bool supported_t(int32_t K, int32_t N, bool gate_up) {
+    constexpr int BM = tile_bm<FM>(), BN = 128 * tile_ns<FM>();
+    // a doubled half tile takes two N-blocks, so their count must be even
+    constexpr int W = (BM == 128 && half_tile_doubles_n<FM>()) ? 2 * BN : BN;
+    return K > 0 && N > 0 && K % (MOE_TILE_WR * kKC) == 0 && (gate_up ? (N / 2) % (W / 2) == 0 : N % W == 0);
+}
+
+bool tile_gemm_supported(int fm, int32_t K, int32_t N, bool gate_up) {
+    switch (fm) {
+        case kFmtNV: return supported_t<kFmtNV>(K, N, gate_up);
+        case kFmtMX8: return supported_t<kFmtMX8>(K, N, gate_up);
+        case kFmtA16: return supported_t<kFmtA16>(K, N, gate_up);
+        case kFmtBF: return supported_t<kFmtBF>(K, N, gate_up);
+        default: return false;
+    }
 }
 
 hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s) {

@@ -119,16 +119,17 @@ enum class GemmShape { Decode, Prefill };
 hipError_t launch_grouped_gemm(const GemmArgs &a, int fm, bool gate_up, GemmShape shape,
                                int32_t max_tiles, hipStream_t s);
 int32_t gemm_bm(GemmShape shape);
-// prefill-shaped MFMA tiles (gemm_tile.hip): 64-row M-tiles, 256 weight rows per workgroup
-bool tile_gemm_supported(int32_t K, int32_t N, bool gate_up);
-int32_t tile_gemm_bm();  // rows per M-tile of the tile kernels
+// prefill-shaped MFMA tiles (gemm_tile.hip): 64- or 128-row M-tiles (by format), 256 or
+// 512 weight rows per workgroup
+bool tile_gemm_supported(int fm, int32_t K, int32_t N, bool gate_up);
+int32_t tile_gemm_bm(int fm);  // rows per M-tile of the tile kernels for operand format fm
 hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s);
 // decode-shaped streaming variant (gemm_stream.hip): 16-row M-tiles, K a multiple of 512
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
 hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s);
 
-// native MXFP4 GEMMs on the gfx950 scaled FP4 MFMA (gemm_mx4.hip): 64-row M-tiles (the
-// tile kernels' BM), 256 weight rows per workgroup; K % 64, gate_up F % 128, down N % 256
+// native MXFP4 GEMMs on the gfx950 scaled FP4 MFMA (gemm_mx4.hip): 64-row M-tiles, 256
+// weight rows per workgroup; K % 64, gate_up F % 128, down N % 256
 bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up);
 hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s);
 

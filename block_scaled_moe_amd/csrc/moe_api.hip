@@ -26,7 +26,7 @@ constexpr int32_t kPrefillRowsPerExpert = 48;
 
 struct Plan {
     GemmShape shape;
-    bool tile64;  // prefill on the 64-row MFMA tile kernels
+    bool tiled;  // prefill on the MFMA tile kernels (64- or 128-row M-tiles)
     int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
     size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
     size_t a_codes, a_scales, a_tscale, a16;
@@ -36,6 +36,11 @@ struct Plan {
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// operand format of the 16-bit-expansion GEMM kernels for a layer format (not MXFP4)
+int gemm_fm(int32_t fmt) {
+    return fmt == MOE_FMT_NVFP4 ? kFmtNV : fmt == MOE_FMT_W4A16 ? kFmtA16 : fmt == MOE_FMT_BF16 ? kFmtBF : kFmtMX8;
+}
+
 Plan make_plan(const moe_forward_args *a) {
     Plan p{};
     const int64_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
@@ -43,10 +48,10 @@ Plan make_plan(const moe_forward_args *a) {
     const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
-    // MXFP4 always runs the scaled-FP4 MFMA kernels, whose M-tiles are the tile kernels' 64 rows
-    p.tile64 = mx4 || (p.shape == GemmShape::Prefill && tile_gemm_supported(a->D, 2 * a->F, true) &&
-                       tile_gemm_supported(a->F, a->D, false));
-    p.bm = p.tile64 ? tile_gemm_bm() : gemm_bm(p.shape);
+    // MXFP4 always runs the scaled-FP4 MFMA kernels (64-row M-tiles)
+    p.tiled = mx4 || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
+                      tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
+    p.bm = mx4 ? 64 : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
@@ -83,11 +88,8 @@ Plan make_plan(const moe_forward_args *a) {
 
 hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
     if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.max_tiles, s);
-    const int fm = fmt == MOE_FMT_NVFP4 ? kFmtNV
-                   : fmt == MOE_FMT_W4A16 ? kFmtA16
-                   : fmt == MOE_FMT_BF16  ? kFmtBF
-                                          : kFmtMX8;
-    if (P.tile64) return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
+    const int fm = gemm_fm(fmt);
+    if (P.tiled) return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
     if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
         return launch_stream_gemm(g, fm, gate_up, P.max_tiles, s);
     return launch_grouped_gemm(g, fm, gate_up, P.shape, P.max_tiles, s);
