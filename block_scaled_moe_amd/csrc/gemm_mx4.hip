@@ -60,7 +60,9 @@ __device__ __forceinline__ v8i fp4_operand(u32x4 c) {
     return (v8i){(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
 }
 
-template <bool GATE_UP>
+// NT: the weight code loads are marked non-temporal. At decode each (expert, weight row)
+// panel is read by a single M-tile, and a wave's load is one contiguous 1 KiB.
+template <bool GATE_UP, bool NT>
 __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p) {
     constexpr int kLds = (GATE_UP && 4 * kBM * kEpiStride * 4 > 2 * kABuf) ? 4 * kBM * kEpiStride * 4 : 2 * kABuf;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];  // A tiles; then the SwiGLU tiles
@@ -146,7 +148,11 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
     auto b_load = [&](int slot, int c) {
 #pragma unroll
         for (int ns = 0; ns < kNS; ++ns) {
-            breg[slot][ns] = *reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c);
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c);
+            if constexpr (NT)
+                breg[slot][ns] = __builtin_nontemporal_load(src);
+            else
+                breg[slot][ns] = *src;
             bsc[slot][ns] = bs[ns][(int64_t)kScaleBlock * c];
         }
     };
@@ -279,14 +285,21 @@ bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up) {
     return gate_up ? (N % 2 == 0 && (N / 2) % (kBN / 2) == 0) : N % kBN == 0;
 }
 
-hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s) {
+hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, bool stream_once, int32_t max_tiles, hipStream_t s) {
     const int64_t nb = gate_up ? (a.N / 2) / (kBN / 2) : a.N / kBN;
     const int64_t items = (int64_t)max_tiles * nb;
-    const int64_t grid = (items + 7) / 8 * 8;
-    if (gate_up)
-        hipLaunchKernelGGL((mx4_gemm_kernel<true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-    else
-        hipLaunchKernelGGL((mx4_gemm_kernel<false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)((items + 7) / 8 * 8)), block(kThreads);
+    if (gate_up) {
+        if (stream_once)
+            hipLaunchKernelGGL((mx4_gemm_kernel<true, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((mx4_gemm_kernel<true, false>), grid, block, 0, s, a);
+    } else {
+        if (stream_once)
+            hipLaunchKernelGGL((mx4_gemm_kernel<false, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((mx4_gemm_kernel<false, false>), grid, block, 0, s, a);
+    }
     return hipGetLastError();
 }
 

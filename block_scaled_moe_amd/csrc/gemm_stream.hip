@@ -16,9 +16,14 @@
 //  - the wave's block scales are staged once in LDS with contiguous loads;
 //  - the four partial sums are added in a fixed order through LDS before the epilogue,
 //    so results are deterministic.
-// K-slot mapping inside a 128-wide group of a wave's K quarter: lane group g = lane/16
-// holds k = 32g + 8j .. 32g + 8j + 7 for MFMA step j; the activation fragment of lane
-// (row r, g) is read at the same k from the exact 16-bit activation row.
+// K-slot mapping inside a 128-wide group of a wave's K quarter (two 64-wide chunks of the
+// tile layout), chosen so that one weight load instruction of a wave reads whole rows of
+// a chunk: lane group g = lane/16 holds, for MFMA step j, the 8 values at
+//   NVFP4  k = 32g + 8j                        (one 16-byte load: chunk g/2, half g%2)
+//   MXFP8  k = 64(j/2) + 16g + 8(j%2)          (load q = j/2: bytes 16g.. of chunk q)
+//   bf16   k = 64(j/2) + 32(j%2) + 8g          (load q = j: bytes 64(q%2) + 16g.. of chunk q/2)
+// (a summation-order permutation only); the activation fragment of lane (row r, g) is
+// read at the same k from the exact 16-bit activation row.
 #include "formats.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -50,10 +55,16 @@ constexpr int kRows = 64;  // weight rows per workgroup
 #endif
 
 // weight loads: at decode each (expert, weight row) panel is read by one workgroup exactly
-// once, so where one load instruction covers whole cache lines (NVFP4 codes: one 16-byte
-// load per lane and group, 512-byte runs) they are marked non-temporal, which measured
-// 3-6% faster; where a lane's piece takes several loads (MXFP8, bf16) each instruction
-// touches parts of lines and the hint made them 8-10% slower, so they stay ordinary.
+// once, so where one load instruction covers whole cache lines (NVFP4: 16 rows x 64
+// bytes of two chunks; MXFP8: 16 rows x 64 bytes of one chunk) they are marked
+// non-temporal, which measured 3-6% faster on NVFP4. bf16 rows are 128 bytes per chunk,
+// so an instruction covers half lines and the loads stay ordinary.
+#ifndef MOE_STREAM_NT_MX
+#define MOE_STREAM_NT_MX 1
+#endif
+#ifndef MOE_STREAM_NT_BF
+#define MOE_STREAM_NT_BF 0
+#endif
 template <bool NT>
 __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
     if constexpr (NT) return __builtin_nontemporal_load(p);
@@ -123,19 +134,26 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
         }
     }
 
-    // ---- weight code pointers of this lane (one per subtile; lane group g reads half g%2
-    //      of the row's slot in 64-wide chunk g/2 of each 128-wide group) and activation row
+    // ---- weight code pointers of this lane (one per subtile, at its first load of the
+    //      wave's first group; see the K mapping in the header) and activation row
     const uint8_t *bsrc[kSub];
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
         const int row = wrow_of(16 * s + r16);
-        bsrc[s] = w_codes_e + ((row >> 5) * kb + kw / 64 + (g >> 1)) * CBLK + (row & 31) * CB + (CB / 2) * (g & 1);
+        bsrc[s] = w_codes_e + ((row >> 5) * kb + kw / 64) * CBLK + (row & 31) * CB +
+                  (NV ? (g >> 1) * CBLK + (CB / 2) * (g & 1) : 16 * g);
     }
+    // byte offset of load q of a group from the lane's pointer
+    auto wq_off = [&](int q) -> int { return NV ? 0 : (BW ? (q >> 1) * CBLK + 64 * (q & 1) : q * CBLK); };
+    // k of MFMA step j inside a group, for lane group g
+    auto k_of = [&](int j) -> int {
+        return NV ? 32 * g + 8 * j : (BW ? 64 * (j >> 1) + 32 * (j & 1) + 8 * g : 64 * (j >> 1) + 16 * g + 8 * (j & 1));
+    };
     const uint8_t *asrc = nullptr;
     if (r16 < rows) {
         const int pos = p0 + r16;
         const int64_t arow = p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
-        asrc = static_cast<const uint8_t *>(p.a_vals) + (arow * K + kw + 32 * g) * 2;
+        asrc = static_cast<const uint8_t *>(p.a_vals) + (arow * K + kw) * 2;
     }
 
     u32x4 bq[G][kSub][NQ];
@@ -145,10 +163,11 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
         for (int s = 0; s < kSub; ++s)
 #pragma unroll
             for (int q = 0; q < NQ; ++q)
-                bq[jj][s][q] = load_w<NQ == 1>(reinterpret_cast<const u32x4 *>(bsrc[s] + 2 * CBLK * jj + 16 * q));
+                bq[jj][s][q] = load_w<NV || (BW ? MOE_STREAM_NT_BF : MOE_STREAM_NT_MX)>(
+                    reinterpret_cast<const u32x4 *>(bsrc[s] + 2 * CBLK * jj + wq_off(q)));
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            aq[jj][j] = asrc ? *reinterpret_cast<const u32x4 *>(asrc + 256 * jj + 16 * j) : (u32x4){0u, 0u, 0u, 0u};
+            aq[jj][j] = asrc ? *reinterpret_cast<const u32x4 *>(asrc + 256 * jj + 2 * k_of(j)) : (u32x4){0u, 0u, 0u, 0u};
     };
 
     float4_t acc[kSub];
@@ -176,12 +195,12 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
         if (jj + W < G) load_group(jj + W);
         _Float16 sh[kSub][2];
         float sf[kSub][2];
-        float sm[kSub];
+        float sm[kSub][2];
 #pragma unroll
         for (int s = 0; s < kSub; ++s) {
             const uint8_t *srow = &s_scale[wave][(16 * s + r16) * SBW];
             if (BW) {
-                sm[s] = 1.0f;
+                sm[s][0] = sm[s][1] = 1.0f;
             } else if (NV) {
                 const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
                 sh[s][0] = e4m3_to_f16(two & 0xff);
@@ -189,7 +208,9 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                 sf[s][0] = (float)sh[s][0];
                 sf[s][1] = (float)sh[s][1];
             } else {
-                sm[s] = __uint_as_float((uint32_t)srow[4 * jj + g] << 23);
+                // steps 2h, 2h + 1 lie in 32-block 2h + g/2 of the group
+                sm[s][0] = __uint_as_float((uint32_t)srow[4 * jj + (g >> 1)] << 23);
+                sm[s][1] = __uint_as_float((uint32_t)srow[4 * jj + 2 + (g >> 1)] << 23);
             }
         }
 #pragma unroll
@@ -209,7 +230,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
                 } else {
                     const u32x4 w4 = bq[jj][s][j >> 1];
                     const u32x2 w2 = (j & 1) ? (u32x2){w4.z, w4.w} : (u32x2){w4.x, w4.y};
-                    const bf16x8 bf = dequant_mxfp8(w2, sm[s]);
+                    const bf16x8 bf = dequant_mxfp8(w2, sm[s][j >> 1]);
                     acc[s] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af, bf, acc[s], 0, 0, 0);
                 }
             }

@@ -87,7 +87,7 @@ Plan make_plan(const moe_forward_args *a) {
 }
 
 hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
-    if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.max_tiles, s);
+    if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.shape == GemmShape::Decode, P.max_tiles, s);
     const int fm = gemm_fm(fmt);
     if (P.tiled) return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
     if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))

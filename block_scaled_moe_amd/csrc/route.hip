@@ -228,14 +228,15 @@ __global__ void __launch_bounds__(256) router_topk_kernel(int32_t T, int32_t E, 
         sel[r] = bi;
         selv[r] = bv;
     }
-    double ex = 0.0;
-    int my_sel = -1;
+    // lane j < k takes the j-th selection (selects, so the k exps run in parallel)
+    float my_v = selv[0];
+    int my_sel = sel[0];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        if (lane == j && j < k) {
-            ex = exp((double)selv[j] - (double)selv[0]);
-            my_sel = sel[j];
-        }
+    for (int j = 1; j < 8; ++j) {
+        my_v = lane == j ? selv[j] : my_v;
+        my_sel = lane == j ? sel[j] : my_sel;
+    }
+    const double ex = lane < k ? exp((double)my_v - (double)selv[0]) : 0.0;
     double den = 0.0;
     for (int j = 0; j < k; ++j) den += __shfl(ex, j);
     if (lane < k) {
