@@ -37,22 +37,36 @@ using namespace gemm_detail;
 constexpr int kSub = 4;    // 16-row weight subtiles per workgroup
 constexpr int kRows = 64;  // weight rows per workgroup
 
-// Tuning: K groups of weight loads in flight per wave, and an optional occupancy
-// target (waves per SIMD) that caps the registers the compiler may use.
+// Tuning: K groups of weight loads in flight per wave, and the occupancy (waves per SIMD)
+// the register budget is set for. A workgroup streams one panel and exits, so its start
+// (first loads in flight) and end (cross-wave sum, epilogue) leave its slot idle; more
+// resident workgroups per CU cover those phases. Measured on the NVFP4 decode layer: two
+// groups at three waves per SIMD beat four groups at two (gate_up 0.536 -> 0.498 ms,
+// down 0.287 -> 0.270 ms); three groups at three waves spill and lose. MXFP8 (twice the
+// bytes per lane) keeps two groups at two waves (one group at three measured slower);
+// bf16 takes one group at two waves (2% faster than two groups at one).
 #ifndef MOE_STREAM_W_NV
-#define MOE_STREAM_W_NV 4
+#define MOE_STREAM_W_NV 2
 #endif
 #ifndef MOE_STREAM_W_MX
 #define MOE_STREAM_W_MX 2
 #endif
-#ifndef MOE_STREAM_WAVES_PER_EU
-#define MOE_STREAM_WAVES_PER_EU 0
+#ifndef MOE_STREAM_W_BF
+#define MOE_STREAM_W_BF 1
 #endif
-#if MOE_STREAM_WAVES_PER_EU > 0
-#define MOE_STREAM_OCCUPANCY __attribute__((amdgpu_waves_per_eu(MOE_STREAM_WAVES_PER_EU)))
-#else
-#define MOE_STREAM_OCCUPANCY
+#ifndef MOE_STREAM_OCC_NV
+#define MOE_STREAM_OCC_NV 3
 #endif
+#ifndef MOE_STREAM_OCC_MX
+#define MOE_STREAM_OCC_MX 2
+#endif
+#ifndef MOE_STREAM_OCC_BF
+#define MOE_STREAM_OCC_BF 2
+#endif
+template <int FM>
+constexpr int stream_occupancy() {
+    return (FM == kFmtNV || FM == kFmtA16) ? MOE_STREAM_OCC_NV : (FM == kFmtMX8 ? MOE_STREAM_OCC_MX : MOE_STREAM_OCC_BF);
+}
 
 // weight loads: at decode each (expert, weight row) panel is read by one workgroup exactly
 // once, so where one load instruction covers whole cache lines (NVFP4: 16 rows x 64
@@ -72,7 +86,7 @@ __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
 }
 
 template <int FM, bool GATE_UP, int G>  // G = 128-wide K groups per wave (K = 512 G)
-__global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(const GemmArgs p) {
+__global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_kernel(const GemmArgs p) {
     constexpr bool NV = FM == kFmtNV || FM == kFmtA16;  // NVFP4 weights (W4A4 or W4A16)
     constexpr bool BW = FM == kFmtBF;                    // bf16 weights (no scales)
     constexpr bool BF = FM != kFmtNV;                    // bf16 operands and MFMA
@@ -80,7 +94,7 @@ __global__ void __launch_bounds__(256) MOE_STREAM_OCCUPANCY stream_gemm_kernel(c
     constexpr bool O16 = FM == kFmtA16 || FM == kFmtBF;  // bf16 intermediate out of gate_up
     using Frag = typename std::conditional<BF, bf16x8, half8>::type;
     constexpr int NQ = NV ? 1 : (BW ? 4 : 2);      // 16-byte code loads per lane, group and subtile
-    constexpr int W = NV ? MOE_STREAM_W_NV : MOE_STREAM_W_MX;  // groups of loads in flight
+    constexpr int W = NV ? MOE_STREAM_W_NV : (BW ? MOE_STREAM_W_BF : MOE_STREAM_W_MX);  // groups of loads in flight
     constexpr int BLK = NV ? 16 : 32;
     constexpr int SBW = G * 128 / BLK;             // scale bytes per weight row in a wave's K quarter
     __shared__ __attribute__((aligned(16))) uint8_t s_scale[4][kRows * SBW];
