@@ -157,6 +157,11 @@ LAYER_CASES = [
     # prefill shapes with longer K on the 64-row MFMA tiles
     dict(name="prefill-nvfp4-k1024", wl=synth.custom("nvfp4", T=1024, D=1024, F=512, E=32, seed=37)),
     dict(name="prefill-mxfp8-k1024", wl=synth.custom("mxfp8", T=1024, D=1024, F=512, E=32, seed=38)),
+    # skewed routing on the MFMA tile kernels: hot experts fill several M-tiles while cold
+    # ones end in short tails (MXFP8's 128-row tiles run tails of <= 64 rows on half the
+    # subtiles, longer tails on all of them)
+    dict(name="prefill-mxfp8-skew-tiles", wl=synth.custom("mxfp8", T=1100, D=512, F=256, E=24, skew=True, seed=39)),
+    dict(name="prefill-nvfp4-skew-tiles", wl=synth.custom("nvfp4", T=1100, D=512, F=256, E=24, skew=True, seed=40)),
     # decode shapes with K a multiple of 512 run the streaming kernels
     dict(name="stream-nvfp4-k2048", wl=synth.custom("nvfp4", T=48, D=2048, F=1536, E=16, seed=31)),
     dict(name="stream-mxfp8-k2048", wl=synth.custom("mxfp8", T=48, D=2048, F=1536, E=16, seed=32)),
