@@ -233,7 +233,9 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer is built for one "
-              "GPU's expert share; see DESIGN.md for how it shards.", file=sys.stderr)
+              "GPU's expert share (moe_forward takes a local expert range; N ranks would each run the "
+              "same router, compute their experts' slots and sum the fp32 partial outputs with one "
+              "all-reduce).", file=sys.stderr)
         sys.exit(2)
 
     import torch
