@@ -62,6 +62,12 @@ static_assert(64 * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thre
 #ifndef MOE_TILE_WR
 #define MOE_TILE_WR 2  // weight chunks in flight (register ring slots)
 #endif
+#ifndef MOE_TILE_SHORT
+#define MOE_TILE_SHORT 1  // short tiles run only the M-subtiles holding rows
+#endif
+#ifndef MOE_TILE_SHORT3
+#define MOE_TILE_SHORT3 0  // 128-row tiles: also a three-subtile mode for 65..96 rows (measured: no gain)
+#endif
 #ifndef MOE_TILE_NS_NV
 #define MOE_TILE_NS_NV (MOE_TILE_BM_NV == 128 ? 2 : 4)
 #endif
@@ -395,19 +401,33 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
 #undef MOE_STORE_A
 #undef MOE_LOAD_W
 
+    // A tile runs only as many 32-row M-subtiles as it has rows (an expert's last tile is
+    // usually short: at about 170 rows per expert half of the last 64-row tiles hold at
+    // most 32 rows).
+    using I1 = std::integral_constant<int, 1>;
+    using INS = std::integral_constant<int, NS>;
+    constexpr bool SHORT = MOE_TILE_SHORT && FM != kFmtBF;  // bf16: no gain, and more spills
     if constexpr (kMS == 4) {
-        if (rows <= 64) {
+        if (SHORT && rows <= 32) {
+            run(I1{}, INS{});
+        } else if (rows <= 64) {
             if constexpr (half_tile_doubles_n<FM>()) {
                 if (nb & 1) return;  // the even N-block's item covers this one
                 run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2 * NS>{});
             } else {
-                run(std::integral_constant<int, 2>{}, std::integral_constant<int, NS>{});
+                run(std::integral_constant<int, 2>{}, INS{});
             }
+        } else if (SHORT && MOE_TILE_SHORT3 && rows <= 96) {
+            run(std::integral_constant<int, 3>{}, INS{});
         } else {
-            run(std::integral_constant<int, 4>{}, std::integral_constant<int, NS>{});
+            run(std::integral_constant<int, 4>{}, INS{});
         }
     } else {
-        run(std::integral_constant<int, kMS>{}, std::integral_constant<int, NS>{});
+        static_assert(kMS == 2, "64- or 128-row tiles");
+        if (SHORT && rows <= 32)
+            run(I1{}, INS{});
+        else
+            run(std::integral_constant<int, 2>{}, INS{});
     }
 }
 
