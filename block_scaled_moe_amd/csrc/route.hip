@@ -397,18 +397,23 @@ constexpr int kSelK = MOE_SEL_K;       // k per staged chunk
 constexpr int kSelP = kSelK / 8;       // 16-byte pieces per staged row
 constexpr int kSelRow = 2 * kSelK + 16;  // LDS bytes per staged row: the padding spreads the
                                          // 16-byte pieces of rows at random slots over banks
-constexpr int kSelItems = (kScreenMaxE * kSelP + 16 * kSelP + 255) / 256;  // staged pieces per thread
+#ifndef MOE_SEL_TOK
+#define MOE_SEL_TOK 16
+#endif
+constexpr int kSelTok = MOE_SEL_TOK;        // tokens per workgroup (16 lanes each)
+constexpr int kSelThreads = 16 * kSelTok;   // threads per workgroup
+constexpr int kSelItems = (kScreenMaxE * kSelP + kSelTok * kSelP + kSelThreads - 1) / kSelThreads;  // staged pieces per thread
 
 size_t select_lds_bytes(int32_t E) {
     const size_t e2 = (size_t)(E + 1) / 2 * 2;  // keeps the byte arrays 4-byte aligned
-    return 16 * e2 * 2 + 2 * e2 * 2 + 16 + 2 * (size_t)E * kSelRow + 2 * 16 * kSelRow;
+    return kSelTok * e2 * 2 + 2 * e2 * 2 + 16 + 2 * (size_t)E * kSelRow + 2 * kSelTok * kSelRow;
 }
 
 template <int PER>  // logits per lane: ceil(E / 16)
 #ifndef MOE_SEL_OCC
 #define MOE_SEL_OCC 2
 #endif
-__global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
+__global__ void __launch_bounds__(kSelThreads, MOE_SEL_OCC) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
                                                             const uint16_t *__restrict__ h,
                                                             const uint16_t *__restrict__ wr, float *__restrict__ lt,
                                                             const double *__restrict__ hn,
@@ -417,22 +422,22 @@ __global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t
                                                             float *__restrict__ w) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     const int e2 = (E + 1) / 2 * 2;
-    int16_t *cand = reinterpret_cast<int16_t *>(lds);  // [16][e2]
-    int16_t *uslot = cand + 16 * e2;                   // [e2]: staged slot of expert e
+    int16_t *cand = reinterpret_cast<int16_t *>(lds);  // [kSelTok][e2]
+    int16_t *uslot = cand + kSelTok * e2;              // [e2]: staged slot of expert e
     int16_t *urow = uslot + e2;                        // [e2]: expert of staged slot s
     // byte offsets from the LDS base (pointer arithmetic on the __shared__ array keeps
     // the accesses ds_* instead of flat)
-    uint8_t *wst = lds + ((size_t)(18 * e2 * 2) + 15) / 16 * 16;  // [2][E][kSelRow]
-    uint8_t *hst = wst + 2 * (size_t)E * kSelRow;      // [2][16][kSelRow]
+    uint8_t *wst = lds + ((size_t)((kSelTok + 2) * e2 * 2) + 15) / 16 * 16;  // [2][E][kSelRow]
+    uint8_t *hst = wst + 2 * (size_t)E * kSelRow;      // [2][kSelTok][kSelRow]
     __shared__ int32_t n_union, pass_max;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int grp = lane >> 4, j = lane & 15;
     const int tl = wave * 4 + grp;
-    const int t = blockIdx.x * 16 + tl;
+    const int t = blockIdx.x * kSelTok + tl;
     const bool live = t < T;
     const int tt = live ? t : T - 1;
-    for (int i = tid; i < e2; i += 256) uslot[i] = -1;
+    for (int i = tid; i < e2; i += kSelThreads) uslot[i] = -1;
     if (tid == 0) pass_max = 0;
 
     // ---- 1. bounds and candidates
@@ -535,7 +540,7 @@ __global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t
 
     // ---- 2. exact chains over LDS-staged rows
     const int n_chunks = D / kSelK;
-    const int items = (nu + 16) * kSelP;  // 16-byte pieces per chunk: weight rows, then h rows
+    const int items = (nu + kSelTok) * kSelP;  // 16-byte pieces per chunk: weight rows, then h rows
     // chunk c + kSelRing - 1 is loaded into register slot (c - 1) % kSelRing while chunk
     // c is multiplied, so two chunks of loads are in flight; a slot goes to the other LDS
     // buffer one chunk before its use. Loads past the end repeat the last chunk.
@@ -547,13 +552,13 @@ __global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t
     int32_t src_row[kSelItems];  // the staged row of each item: an expert, else a token
 #pragma unroll
     for (int i = 0; i < kSelItems; ++i) {
-        const int it = tid + 256 * i, row = it / kSelP;
-        src_row[i] = it >= items ? 0 : row < nu ? urow[row] : min(blockIdx.x * 16 + (row - nu), T - 1);
+        const int it = tid + kSelThreads * i, row = it / kSelP;
+        src_row[i] = it >= items ? 0 : row < nu ? urow[row] : min(blockIdx.x * kSelTok + (row - nu), T - 1);
     }
     auto load_chunk = [&](int slot, int c) {
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
-            const int it = tid + 256 * i;
+            const int it = tid + kSelThreads * i;
             const int row = it / kSelP, q = it % kSelP;
             if (it < items) {
                 const uint16_t *src = (row < nu ? wr : h) + (int64_t)src_row[i] * D;
@@ -564,11 +569,11 @@ __global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t
     auto store_chunk = [&](int buf, int slot) {
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
-            const int it = tid + 256 * i;
+            const int it = tid + kSelThreads * i;
             const int row = it / kSelP, q = it % kSelP;
             if (it < items) {
                 uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
-                                        : hst + (buf * 16 + (row - nu)) * kSelRow;
+                                        : hst + (buf * kSelTok + (row - nu)) * kSelRow;
                 *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[slot][i];
             }
         }
@@ -594,7 +599,7 @@ __global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t
                 const int c = c0 + jj;  // register slot jj held chunk c; LDS buffer c % 2 holds it
                 if (c >= n_chunks) break;
                 const int buf = c & 1;
-                const uint8_t *hrow = hst + (buf * 16 + ptl) * kSelRow;
+                const uint8_t *hrow = hst + (buf * kSelTok + ptl) * kSelRow;
                 const uint8_t *wrow = wst + ((size_t)buf * E + ps) * kSelRow;
 #pragma unroll
                 for (int q = 0; q < kSelP; ++q) {
@@ -616,7 +621,7 @@ __global__ void __launch_bounds__(256, MOE_SEL_OCC) router_select_kernel(int32_t
             }
         }
         // exact logit of the pair into its token's lt row, at the candidate's position
-        const int pt = blockIdx.x * 16 + ptl;
+        const int pt = blockIdx.x * kSelTok + ptl;
         if (mine && pt < T) lt[(int64_t)pt * Ep + (pr - og[g])] = bias ? a + bias[pe] : a;
     }
     // the barrier waits for the stores of the exact logits (write-through, so they are in
@@ -766,19 +771,19 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
                        T, D, p.Ep, p.n_parts, h, wk8, wpart, scratch, hn, wn, amax_bits);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     {
-        const dim3 grid((unsigned)((T + 15) / 16));
+        const dim3 grid((unsigned)((T + kSelTok - 1) / kSelTok));
         const size_t lds = select_lds_bytes(E);
         if (E <= 128)
-            hipLaunchKernelGGL((router_select_kernel<8>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+            hipLaunchKernelGGL((router_select_kernel<8>), grid, dim3(kSelThreads), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
                                hn, wn, bias, idx, w);
         else if (E <= 256)
-            hipLaunchKernelGGL((router_select_kernel<16>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+            hipLaunchKernelGGL((router_select_kernel<16>), grid, dim3(kSelThreads), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
                                hn, wn, bias, idx, w);
         else if (E <= 384)
-            hipLaunchKernelGGL((router_select_kernel<24>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+            hipLaunchKernelGGL((router_select_kernel<24>), grid, dim3(kSelThreads), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
                                hn, wn, bias, idx, w);
         else
-            hipLaunchKernelGGL((router_select_kernel<32>), grid, dim3(256), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
+            hipLaunchKernelGGL((router_select_kernel<32>), grid, dim3(kSelThreads), lds, s, T, D, E, p.Ep, k, h, wr, scratch,
                                hn, wn, bias, idx, w);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
