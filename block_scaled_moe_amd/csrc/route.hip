@@ -402,18 +402,29 @@ constexpr int kSelRow = 2 * kSelK + 16;  // LDS bytes per staged row: the paddin
 #endif
 constexpr int kSelTok = MOE_SEL_TOK;        // tokens per workgroup (16 lanes each)
 constexpr int kSelThreads = 16 * kSelTok;   // threads per workgroup
-constexpr int kSelItems = (kScreenMaxE * kSelP + kSelTok * kSelP + kSelThreads - 1) / kSelThreads;  // staged pieces per thread
+// union rows staged at a time: about 150 candidate experts for 16 tokens at decode-like
+// spreads; a larger union is processed in windows of kSelCap rows. Sizing the stages by
+// the cap instead of E frees LDS for a third workgroup per CU.
+#ifndef MOE_SEL_CAP
+#define MOE_SEL_CAP 224
+#endif
+constexpr int kSelCap = MOE_SEL_CAP;
+constexpr int kSelItems = (kSelCap * kSelP + kSelTok * kSelP + kSelThreads - 1) / kSelThreads;  // staged pieces per thread
 
 size_t select_lds_bytes(int32_t E) {
     const size_t e2 = (size_t)(E + 1) / 2 * 2;  // keeps the byte arrays 4-byte aligned
-    return kSelTok * e2 * 2 + 2 * e2 * 2 + 16 + 2 * (size_t)E * kSelRow + 2 * kSelTok * kSelRow;
+    const size_t cap = E < kSelCap ? (size_t)E : (size_t)kSelCap;
+    return kSelTok * e2 * 2 + 2 * e2 * 2 + 16 + 2 * cap * kSelRow + 2 * kSelTok * kSelRow;
 }
 
-template <int PER>  // logits per lane: ceil(E / 16)
 #ifndef MOE_SEL_OCC
-#define MOE_SEL_OCC 2
+#define MOE_SEL_OCC 3  // waves per SIMD for up to 384 experts (LDS: three workgroups per CU)
 #endif
-__global__ void __launch_bounds__(kSelThreads, MOE_SEL_OCC) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
+template <int PER>
+constexpr int sel_occupancy() { return PER <= 24 ? MOE_SEL_OCC : 2; }
+
+template <int PER>  // logits per lane: ceil(E / 16)
+__global__ void __launch_bounds__(kSelThreads, (sel_occupancy<PER>())) router_select_kernel(int32_t T, int32_t D, int32_t E, int32_t Ep, int32_t k,
                                                             const uint16_t *__restrict__ h,
                                                             const uint16_t *__restrict__ wr, float *__restrict__ lt,
                                                             const double *__restrict__ hn,
@@ -427,8 +438,9 @@ __global__ void __launch_bounds__(kSelThreads, MOE_SEL_OCC) router_select_kernel
     int16_t *urow = uslot + e2;                        // [e2]: expert of staged slot s
     // byte offsets from the LDS base (pointer arithmetic on the __shared__ array keeps
     // the accesses ds_* instead of flat)
-    uint8_t *wst = lds + ((size_t)((kSelTok + 2) * e2 * 2) + 15) / 16 * 16;  // [2][E][kSelRow]
-    uint8_t *hst = wst + 2 * (size_t)E * kSelRow;      // [2][kSelTok][kSelRow]
+    const int cap = min(E, kSelCap);                   // union rows per staged window
+    uint8_t *wst = lds + ((size_t)((kSelTok + 2) * e2 * 2) + 15) / 16 * 16;  // [2][cap][kSelRow]
+    uint8_t *hst = wst + 2 * (size_t)cap * kSelRow;    // [2][kSelTok][kSelRow]
     __shared__ int32_t n_union, pass_max;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -538,9 +550,8 @@ __global__ void __launch_bounds__(kSelThreads, MOE_SEL_OCC) router_select_kernel
     __syncthreads();
     const int nu = n_union, n_pass = pass_max;
 
-    // ---- 2. exact chains over LDS-staged rows
+    // ---- 2. exact chains over LDS-staged rows, the union in windows of at most cap rows
     const int n_chunks = D / kSelK;
-    const int items = (nu + kSelTok) * kSelP;  // 16-byte pieces per chunk: weight rows, then h rows
     // chunk c + kSelRing - 1 is loaded into register slot (c - 1) % kSelRing while chunk
     // c is multiplied, so two chunks of loads are in flight; a slot goes to the other LDS
     // buffer one chunk before its use. Loads past the end repeat the last chunk.
@@ -548,81 +559,88 @@ __global__ void __launch_bounds__(kSelThreads, MOE_SEL_OCC) router_select_kernel
 #define MOE_SEL_RING 2
 #endif
     constexpr int kSelRing = MOE_SEL_RING;
-    u32x4 sreg[kSelRing][kSelItems];
-    int32_t src_row[kSelItems];  // the staged row of each item: an expert, else a token
-#pragma unroll
-    for (int i = 0; i < kSelItems; ++i) {
-        const int it = tid + kSelThreads * i, row = it / kSelP;
-        src_row[i] = it >= items ? 0 : row < nu ? urow[row] : min(blockIdx.x * kSelTok + (row - nu), T - 1);
-    }
-    auto load_chunk = [&](int slot, int c) {
+    const int n_win = (nu + cap - 1) / cap;
+    for (int win = 0; win < n_win; ++win) {
+        const int r0 = win * cap, nw = min(cap, nu - r0);  // union slots [r0, r0 + nw)
+        const int items = (nw + kSelTok) * kSelP;  // 16-byte pieces per chunk: weight rows, then h rows
+        u32x4 sreg[kSelRing][kSelItems];
+        int32_t src_row[kSelItems];  // the staged row of each item: an expert, else a token
 #pragma unroll
         for (int i = 0; i < kSelItems; ++i) {
-            const int it = tid + kSelThreads * i;
-            const int row = it / kSelP, q = it % kSelP;
-            if (it < items) {
-                const uint16_t *src = (row < nu ? wr : h) + (int64_t)src_row[i] * D;
-                sreg[slot][i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
-            }
+            const int it = tid + kSelThreads * i, row = it / kSelP;
+            src_row[i] = it >= items ? 0 : row < nw ? urow[r0 + row] : min(blockIdx.x * kSelTok + (row - nw), T - 1);
         }
-    };
-    auto store_chunk = [&](int buf, int slot) {
+        auto load_chunk = [&](int slot, int c) {
 #pragma unroll
-        for (int i = 0; i < kSelItems; ++i) {
-            const int it = tid + kSelThreads * i;
-            const int row = it / kSelP, q = it % kSelP;
-            if (it < items) {
-                uint8_t *dst = row < nu ? wst + ((size_t)buf * E + row) * kSelRow
-                                        : hst + (buf * kSelTok + (row - nu)) * kSelRow;
-                *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[slot][i];
-            }
-        }
-    };
-    for (int pass = 0; pass < n_pass; ++pass) {
-        const int pr = lane + 64 * pass;  // this lane's pair
-        const bool mine = pr < pw;
-        int g = 0;
-#pragma unroll
-        for (int q = 1; q < 4; ++q)
-            if (pr >= og[q]) g = q;
-        const int ptl = wave * 4 + g;                             // the pair's token in the workgroup
-        const int pe = mine ? cand[ptl * e2 + (pr - og[g])] : 0;  // and expert
-        const int ps = mine ? uslot[pe] : 0;
-        float a = 0.0f;
-#pragma unroll
-        for (int r = 0; r < kSelRing; ++r) load_chunk(r, min(r, n_chunks - 1));
-        store_chunk(0, 0);
-        __syncthreads();
-        for (int c0 = 0; c0 < n_chunks; c0 += kSelRing) {
-#pragma unroll
-            for (int jj = 0; jj < kSelRing; ++jj) {
-                const int c = c0 + jj;  // register slot jj held chunk c; LDS buffer c % 2 holds it
-                if (c >= n_chunks) break;
-                const int buf = c & 1;
-                const uint8_t *hrow = hst + (buf * kSelTok + ptl) * kSelRow;
-                const uint8_t *wrow = wst + ((size_t)buf * E + ps) * kSelRow;
-#pragma unroll
-                for (int q = 0; q < kSelP; ++q) {
-                    const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
-                    const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + 16 * q);
-                    a = __builtin_fmaf(bf_lo(hv.x), bf_lo(wv.x), a);
-                    a = __builtin_fmaf(bf_hi(hv.x), bf_hi(wv.x), a);
-                    a = __builtin_fmaf(bf_lo(hv.y), bf_lo(wv.y), a);
-                    a = __builtin_fmaf(bf_hi(hv.y), bf_hi(wv.y), a);
-                    a = __builtin_fmaf(bf_lo(hv.z), bf_lo(wv.z), a);
-                    a = __builtin_fmaf(bf_hi(hv.z), bf_hi(wv.z), a);
-                    a = __builtin_fmaf(bf_lo(hv.w), bf_lo(wv.w), a);
-                    a = __builtin_fmaf(bf_hi(hv.w), bf_hi(wv.w), a);
+            for (int i = 0; i < kSelItems; ++i) {
+                const int it = tid + kSelThreads * i;
+                const int row = it / kSelP, q = it % kSelP;
+                if (it < items) {
+                    const uint16_t *src = (row < nw ? wr : h) + (int64_t)src_row[i] * D;
+                    sreg[slot][i] = *reinterpret_cast<const u32x4 *>(src + c * kSelK + 8 * q);
                 }
-                // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
-                store_chunk(buf ^ 1, (jj + 1) % kSelRing);
-                load_chunk(jj, min(c + kSelRing, n_chunks - 1));
-                __syncthreads();
             }
+        };
+        auto store_chunk = [&](int buf, int slot) {
+#pragma unroll
+            for (int i = 0; i < kSelItems; ++i) {
+                const int it = tid + kSelThreads * i;
+                const int row = it / kSelP, q = it % kSelP;
+                if (it < items) {
+                    uint8_t *dst = row < nw ? wst + ((size_t)buf * cap + row) * kSelRow
+                                            : hst + (buf * kSelTok + (row - nw)) * kSelRow;
+                    *reinterpret_cast<u32x4 *>(dst + 16 * q) = sreg[slot][i];
+                }
+            }
+        };
+        for (int pass = 0; pass < n_pass; ++pass) {
+            const int pr = lane + 64 * pass;  // this lane's pair
+            const bool mine = pr < pw;
+            int g = 0;
+#pragma unroll
+            for (int q = 1; q < 4; ++q)
+                if (pr >= og[q]) g = q;
+            const int ptl = wave * 4 + g;                             // the pair's token in the workgroup
+            const int pe = mine ? cand[ptl * e2 + (pr - og[g])] : 0;  // and expert
+            const int ps = mine ? uslot[pe] : 0;
+            const bool in_win = mine && ps >= r0 && ps < r0 + nw;     // its row is staged in this window
+            const int wsl = in_win ? ps - r0 : 0;
+            float a = 0.0f;
+#pragma unroll
+            for (int r = 0; r < kSelRing; ++r) load_chunk(r, min(r, n_chunks - 1));
+            store_chunk(0, 0);
+            __syncthreads();
+            for (int c0 = 0; c0 < n_chunks; c0 += kSelRing) {
+#pragma unroll
+                for (int jj = 0; jj < kSelRing; ++jj) {
+                    const int c = c0 + jj;  // register slot jj held chunk c; LDS buffer c % 2 holds it
+                    if (c >= n_chunks) break;
+                    const int buf = c & 1;
+                    const uint8_t *hrow = hst + (buf * kSelTok + ptl) * kSelRow;
+                    const uint8_t *wrow = wst + ((size_t)buf * cap + wsl) * kSelRow;
+#pragma unroll
+                    for (int q = 0; q < kSelP; ++q) {
+                        const u32x4 hv = *reinterpret_cast<const u32x4 *>(hrow + 16 * q);
+                        const u32x4 wv = *reinterpret_cast<const u32x4 *>(wrow + 16 * q);
+                        a = __builtin_fmaf(bf_lo(hv.x), bf_lo(wv.x), a);
+                        a = __builtin_fmaf(bf_hi(hv.x), bf_hi(wv.x), a);
+                        a = __builtin_fmaf(bf_lo(hv.y), bf_lo(wv.y), a);
+                        a = __builtin_fmaf(bf_hi(hv.y), bf_hi(wv.y), a);
+                        a = __builtin_fmaf(bf_lo(hv.z), bf_lo(wv.z), a);
+                        a = __builtin_fmaf(bf_hi(hv.z), bf_hi(wv.z), a);
+                        a = __builtin_fmaf(bf_lo(hv.w), bf_lo(wv.w), a);
+                        a = __builtin_fmaf(bf_hi(hv.w), bf_hi(wv.w), a);
+                    }
+                    // buffer buf ^ 1 was last read in chunk c - 1, before the previous barrier
+                    store_chunk(buf ^ 1, (jj + 1) % kSelRing);
+                    load_chunk(jj, min(c + kSelRing, n_chunks - 1));
+                    __syncthreads();
+                }
+            }
+            // exact logit of the pair into its token's lt row, at the candidate's position
+            const int pt = blockIdx.x * kSelTok + ptl;
+            if (in_win && pt < T) lt[(int64_t)pt * Ep + (pr - og[g])] = bias ? a + bias[pe] : a;
         }
-        // exact logit of the pair into its token's lt row, at the candidate's position
-        const int pt = blockIdx.x * kSelTok + ptl;
-        if (mine && pt < T) lt[(int64_t)pt * Ep + (pr - og[g])] = bias ? a + bias[pe] : a;
     }
     // the barrier waits for the stores of the exact logits (write-through, so they are in
     // this XCD's L2); phase 1 read the same rows through this CU's L1, which the barrier
