@@ -124,7 +124,7 @@ class PackedWeights:
         if N % 32 or K % 64:
             raise ValueError(f"packed weights need N % 32 == 0 and K % 64 == 0 (got N={N}, K={K})")
         if fmt == "bf16":  # bf16 values in the tile layout, no scales
-            codes = torch.empty((E, N // 32, K // 64, 32, 128), dtype=torch.uint8, device=device)
+            codes = torch.empty((E, N // 32, K // 64, 2, 32, 64), dtype=torch.uint8, device=device)
             scales = torch.empty((0,), dtype=torch.uint8, device=device)
         elif fmt == "mxfp4":
             codes = torch.empty((E, N // 32, K // 64, 2, 32, 16), dtype=torch.uint8, device=device)

@@ -21,7 +21,7 @@
 // a chunk: lane group g = lane/16 holds, for MFMA step j, the 8 values at
 //   NVFP4  k = 32g + 8j                        (one 16-byte load: chunk g/2, half g%2)
 //   MXFP8  k = 64(j/2) + 16g + 8(j%2)          (load q = j/2: bytes 16g.. of chunk q)
-//   bf16   k = 64(j/2) + 32(j%2) + 8g          (load q = j: bytes 64(q%2) + 16g.. of chunk q/2)
+//   bf16   k = 64(j/2) + 32(j%2) + 8g          (load q = j: bytes 16g.. of half q%2 of chunk q/2)
 // (a summation-order permutation only); the activation fragment of lane (row r, g) is
 // read at the same k from the exact 16-bit activation row.
 #include "formats.h"
@@ -70,14 +70,14 @@ constexpr int stream_occupancy() {
 
 // weight loads: at decode each (expert, weight row) panel is read by one workgroup exactly
 // once, so where one load instruction covers whole cache lines (NVFP4: 16 rows x 64
-// bytes of two chunks; MXFP8: 16 rows x 64 bytes of one chunk) they are marked
-// non-temporal, which measured 3-6% faster on NVFP4. bf16 rows are 128 bytes per chunk,
-// so an instruction covers half lines and the loads stay ordinary.
+// bytes of two chunks; MXFP8: 16 rows x 64 bytes of one chunk; bf16: 16 rows x 64 bytes
+// of one half-chunk) they can be marked non-temporal, which measured 3-6% faster on
+// NVFP4 and 13% on MXFP8.
 #ifndef MOE_STREAM_NT_MX
 #define MOE_STREAM_NT_MX 1
 #endif
 #ifndef MOE_STREAM_NT_BF
-#define MOE_STREAM_NT_BF 0
+#define MOE_STREAM_NT_BF 1
 #endif
 template <bool NT>
 __device__ __forceinline__ u32x4 load_w(const u32x4 *p) {
@@ -154,11 +154,11 @@ __global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_ker
 #pragma unroll
     for (int s = 0; s < kSub; ++s) {
         const int row = wrow_of(16 * s + r16);
-        bsrc[s] = w_codes_e + ((row >> 5) * kb + kw / 64) * CBLK + (row & 31) * CB +
-                  (NV ? (g >> 1) * CBLK + (CB / 2) * (g & 1) : 16 * g);
+        bsrc[s] = w_codes_e + ((row >> 5) * kb + kw / 64) * CBLK +
+                  (NV ? (row & 31) * CB + (g >> 1) * CBLK + (CB / 2) * (g & 1) : (row & 31) * (BW ? 64 : CB) + 16 * g);
     }
     // byte offset of load q of a group from the lane's pointer
-    auto wq_off = [&](int q) -> int { return NV ? 0 : (BW ? (q >> 1) * CBLK + 64 * (q & 1) : q * CBLK); };
+    auto wq_off = [&](int q) -> int { return NV ? 0 : (BW ? (q >> 1) * CBLK + 2048 * (q & 1) : q * CBLK); };
     // k of MFMA step j inside a group, for lane group g
     auto k_of = [&](int j) -> int {
         return NV ? 32 * g + 8 * j : (BW ? 64 * (j >> 1) + 32 * (j & 1) + 8 * g : 64 * (j >> 1) + 16 * g + 8 * (j & 1));

@@ -146,8 +146,9 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g2 = lane >> 5;
     // packed tile layout (layout.h): per chunk, a lane's 32 codes sit at byte
-    // (row % 32) * CB + CB/2 * g of the chunk's block of its row group, and its scales in
-    // the block's 4-byte (NVFP4) or 2-byte (MXFP8) row slot
+    // (row % 32) * CB + CB/2 * g of the chunk's block of its row group (bf16: half g of
+    // the block, 64 bytes per row), and its scales in the block's 4-byte (NVFP4) or
+    // 2-byte (MXFP8) row slot
     constexpr int CB = BW ? 128 : layout::code_bytes_per_row(NV);
     constexpr int CBLK = 32 * CB, SBLK = layout::scale_block_bytes(NV);
     const int64_t kb = K / 64;  // blocks per row group
@@ -213,7 +214,7 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
                 row = bn * BN + wave * 32 * NS + 32 * ls + l32;
             }
             const int64_t blk0 = (int64_t)(row >> 5) * kb;
-            wc[ns] = w_codes_e + blk0 * CBLK + l32 * CB + (CB / 2) * g2;
+            wc[ns] = w_codes_e + blk0 * CBLK + (BW ? 2048 * g2 + 64 * l32 : l32 * CB + (CB / 2) * g2);
             ws[ns] = BW ? nullptr : w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
         }
 

@@ -58,18 +58,20 @@ __host__ __device__ inline void block_source(bool nv, int64_t K, int64_t r, int6
     k = 64 * (blk % kb) + (nv ? 16 : 32) * piece;
 }
 
-// bf16 weights (no quantisation) use the same 32 x 64 blocks with 128-byte row slots
-// (element k of the block at bytes 2k, 2k + 1): a 4 KiB block. Storage piece r of an
-// expert (16 bytes, 8 values) sits at byte 16r; its source row and first column:
+// bf16 weights (no quantisation) use the same 32 x 64 blocks (4 KiB), with the two
+// 32-column halves kept apart like MXFP4: [2][32 rows][64 bytes], element k of a half at
+// bytes 2k, 2k + 1. A lane's 32 values of a half are then one contiguous 64 bytes, and a
+// wave load of 16 rows x 64 bytes covers whole cache lines. Storage piece r of an expert
+// (16 bytes, 8 values) sits at byte 16r; its source row and first column:
 __host__ __device__ inline void piece_source_bf16(int64_t K, int64_t r, int64_t &n, int64_t &k) {
-    const int64_t piece = r & 7, row = (r >> 3) & 31, blk = r >> 8;
+    const int64_t piece = r & 3, row = (r >> 2) & 31, half = (r >> 7) & 1, blk = r >> 8;
     const int64_t kb = K >> 6;
     n = 32 * (blk / kb) + row;
-    k = 64 * (blk % kb) + 8 * piece;
+    k = 64 * (blk % kb) + 32 * half + 8 * piece;
 }
 // byte offset inside one expert's bf16 codes of element (n, k)
 __host__ __device__ inline int64_t code_offset_bf16(int64_t K, int64_t n, int64_t k) {
-    return block_index(K, n, k) * 4096 + (n & 31) * 128 + 2 * (k & 63);
+    return block_index(K, n, k) * 4096 + ((k & 63) >> 5) * 2048 + (n & 31) * 64 + 2 * (k & 31);
 }
 
 // MXFP4: source row and first column of quantisation block r (storage order)

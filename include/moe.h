@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -76,7 +76,8 @@ extern "C" {
  *   MXFP4: codes  u8 [E][N/32][K/64][2][32][16] E2M1, element 2i in the low nibble of
  *          byte i: the block's 32 rows for columns 0-31, then for columns 32-63
  *          scales u8 [E][N/32][K/64][2][32]  E8M0, one per 32 columns, same order
- *   BF16:  codes  u8 [E][N/32][K/64][32][128] bf16 values (column c at bytes 2c, 2c+1)
+ *   BF16:  codes  u8 [E][N/32][K/64][2][32][64] bf16 values, the two 32-column halves
+ *          of a block apart (column 32h + c at bytes 2c, 2c+1 of half h)
  *          scales, tensor_scale unused (may be NULL)
  *          tensor_scale unused (may be NULL)
  * Sizes are those of the row-major arrays ([E][N][K/2] (NVFP4, MXFP4) / [E][N][K]

@@ -29,7 +29,7 @@ def test_header_functions_are_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 5
+    assert lib.moe_abi_version() == 6
     assert lib.moe_status_string(EWS) == b"workspace missing or too small"
 
 
