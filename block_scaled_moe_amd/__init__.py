@@ -103,9 +103,11 @@ def _check(rc: int, what: str):
 @dataclasses.dataclass
 class PackedWeights:
     """Device tensors of one packed matrix kind for E experts (logically [E][N][K]) in the
-    tiled layout of include/moe.h: codes [E][N/32][K/64][32][32 | 64] and scales
+    tiled layout of include/moe.h: NVFP4 codes [E][N/32][K/64][32][32], MXFP8 codes
+    [E][N/32][K/64][4][32][16] (the four 16-column quarters of a block apart), scales
     [E][N/32][K/64][32][4 | 2] (NVFP4 | MXFP8); MXFP4 keeps the two 32-column halves of
-    a block apart, codes [E][N/32][K/64][2][32][16] and scales [E][N/32][K/64][2][32][1]."""
+    a block apart, codes [E][N/32][K/64][2][32][16] and scales [E][N/32][K/64][2][32][1];
+    bf16 codes [E][N/32][K/64][2][32][64]."""
     fmt: str
     E: int
     N: int
@@ -130,7 +132,8 @@ class PackedWeights:
             codes = torch.empty((E, N // 32, K // 64, 2, 32, 16), dtype=torch.uint8, device=device)
             scales = torch.empty((E, N // 32, K // 64, 2, 32, 1), dtype=torch.uint8, device=device)
         else:
-            codes = torch.empty((E, N // 32, K // 64, 32, 64 if fmt == "mxfp8" else 32), dtype=torch.uint8,
+            codes = torch.empty((E, N // 32, K // 64, 4, 32, 16) if fmt == "mxfp8" else (E, N // 32, K // 64, 32, 32),
+                                dtype=torch.uint8,
                                 device=device)
             scales = torch.empty((E, N // 32, K // 64, 32, 4 if nv else 2), dtype=torch.uint8, device=device)
         ts = torch.empty(E, dtype=torch.float32, device=device) if nv else None

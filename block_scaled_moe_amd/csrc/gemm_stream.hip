@@ -20,7 +20,7 @@
 // tile layout), chosen so that one weight load instruction of a wave reads whole rows of
 // a chunk: lane group g = lane/16 holds, for MFMA step j, the 8 values at
 //   NVFP4  k = 32g + 8j                        (one 16-byte load: chunk g/2, half g%2)
-//   MXFP8  k = 64(j/2) + 16g + 8(j%2)          (load q = j/2: bytes 16g.. of chunk q)
+//   MXFP8  k = 64(j/2) + 16g + 8(j%2)          (load q = j/2: quarter g of chunk q)
 //   bf16   k = 64(j/2) + 32(j%2) + 8g          (load q = j: bytes 16g.. of half q%2 of chunk q/2)
 // (a summation-order permutation only); the activation fragment of lane (row r, g) is
 // read at the same k from the exact 16-bit activation row.
@@ -70,9 +70,9 @@ constexpr int stream_occupancy() {
 
 // weight loads: at decode each (expert, weight row) panel is read by one workgroup exactly
 // once, so where one load instruction covers whole cache lines (NVFP4: 16 rows x 64
-// bytes of two chunks; MXFP8: 16 rows x 64 bytes of one chunk; bf16: 16 rows x 64 bytes
-// of one half-chunk) they can be marked non-temporal, which measured 3-6% faster on
-// NVFP4 and 13% on MXFP8.
+// bytes of two chunks; MXFP8: 16 rows x 16 bytes of each quarter of one chunk; bf16:
+// 16 rows x 64 bytes of one half-chunk) they can be marked non-temporal, which measured
+// 3-6% faster on NVFP4 and 13% on MXFP8.
 #ifndef MOE_STREAM_NT_MX
 #define MOE_STREAM_NT_MX 1
 #endif
@@ -155,7 +155,8 @@ __global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_ker
     for (int s = 0; s < kSub; ++s) {
         const int row = wrow_of(16 * s + r16);
         bsrc[s] = w_codes_e + ((row >> 5) * kb + kw / 64) * CBLK +
-                  (NV ? (row & 31) * CB + (g >> 1) * CBLK + (CB / 2) * (g & 1) : (row & 31) * (BW ? 64 : CB) + 16 * g);
+                  (NV ? (row & 31) * CB + (g >> 1) * CBLK + (CB / 2) * (g & 1)
+                      : (BW ? (row & 31) * 64 + 16 * g : 512 * g + (row & 31) * 16));
     }
     // byte offset of load q of a group from the lane's pointer
     auto wq_off = [&](int q) -> int { return NV ? 0 : (BW ? (q >> 1) * CBLK + 2048 * (q & 1) : q * CBLK); };

@@ -145,12 +145,14 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
     const int e = p.e_begin + el;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, g2 = lane >> 5;
-    // packed tile layout (layout.h): per chunk, a lane's 32 codes sit at byte
-    // (row % 32) * CB + CB/2 * g of the chunk's block of its row group (bf16: half g of
-    // the block, 64 bytes per row), and its scales in the block's 4-byte (NVFP4) or
-    // 2-byte (MXFP8) row slot
+    // packed tile layout (layout.h): per chunk, a lane's 32 codes sit in the chunk's block
+    // of its row group at byte (row % 32) * CB + CB/2 * g (NVFP4), in quarters 2g and 2g + 1
+    // at 16 (row % 32) (MXFP8: each load of a half-wave one contiguous 512 bytes), or in
+    // half g at 64 (row % 32) (bf16); its scales in the block's 4-byte (NVFP4) or 2-byte
+    // (MXFP8) row slot
     constexpr int CB = BW ? 128 : layout::code_bytes_per_row(NV);
     constexpr int CBLK = 32 * CB, SBLK = layout::scale_block_bytes(NV);
+    constexpr int WSTEP = BW ? 16 : 512;  // bytes between a lane's 16-byte loads of one chunk
     const int64_t kb = K / 64;  // blocks per row group
     const uint8_t *w_codes_e = p.w_codes + (int64_t)e * N * (NV ? K / 2 : (BW ? 2 * K : K));
     const uint8_t *w_scales_e = p.w_scales + (int64_t)e * N * (NV ? K / 16 : K / 32);
@@ -187,7 +189,7 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
 #define MOE_LOAD_W(slot, c)                                                                                \
     _Pragma("unroll") for (int ns = 0; ns < NSA; ++ns) {                                                   \
         _Pragma("unroll") for (int v = 0; v < CV; ++v) wcode[slot][ns][v] =                                \
-            *reinterpret_cast<const u32x4 *>(wc[ns] + (int64_t)CBLK * (c) + 16 * v);                       \
+            *reinterpret_cast<const u32x4 *>(wc[ns] + (int64_t)CBLK * (c) + WSTEP * v);                    \
         wsc[slot][ns] = BW ? 0u : *reinterpret_cast<const uint32_t *>(ws[ns] + (int64_t)SBLK * (c));      \
     }
 
@@ -214,7 +216,8 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
                 row = bn * BN + wave * 32 * NS + 32 * ls + l32;
             }
             const int64_t blk0 = (int64_t)(row >> 5) * kb;
-            wc[ns] = w_codes_e + blk0 * CBLK + (BW ? 2048 * g2 + 64 * l32 : l32 * CB + (CB / 2) * g2);
+            wc[ns] = w_codes_e + blk0 * CBLK +
+                     (BW ? 2048 * g2 + 64 * l32 : (NV ? l32 * CB + (CB / 2) * g2 : 1024 * g2 + 16 * l32));
             ws[ns] = BW ? nullptr : w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
         }
 

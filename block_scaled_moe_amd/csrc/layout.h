@@ -2,11 +2,13 @@
 // the weight quantiser and the grouped GEMM kernels.
 //
 // Per expert, a weight matrix [N][K] (N % 32 == 0, K % 64 == 0) is cut into blocks of
-// 32 rows x 64 columns, stored block-row-major ([N/32][K/64]). Inside a block the 32
-// rows follow each other, each holding its 64 columns' codes: 32 bytes for NVFP4 (E2M1,
-// element 2i in the low nibble of byte i) or 64 bytes for MXFP8 (E4M3), so one block is
-// 1 KiB or 2 KiB of contiguous memory. The block scales follow the same block order,
-// 4 bytes (four E4M3 scales of 16) or 2 bytes (two E8M0 scales of 32) per row.
+// 32 rows x 64 columns, stored block-row-major ([N/32][K/64]). NVFP4: inside a block the
+// 32 rows follow each other, each holding its 64 columns' codes in 32 bytes (E2M1,
+// element 2i in the low nibble of byte i): 1 KiB. MXFP8 (E4M3, one byte per value): the
+// block's four 16-column quarters are kept apart, [4][32 rows][16 bytes] (2 KiB), so
+// that a wave's load of one quarter (or of two, one per half-wave) reads whole cache
+// lines. The block scales follow the same block order, 4 bytes (four E4M3 scales of
+// 16) or 2 bytes (two E8M0 scales of 32) per row.
 //
 // The GEMM kernels give each lane one weight row of a 32-row MFMA subtile, so a wave's
 // codes for one 64-column chunk are a single contiguous run instead of 32 strided
@@ -18,8 +20,9 @@
 // lanes read one contiguous 1 KiB of codes and 64 bytes of scales.
 //
 // In storage order, quantisation block r of an expert (16 values NVFP4, 32 MXFP8 and
-// MXFP4) has its codes at byte 8r / 32r / 16r and its scale at byte r; its source row
-// and column follow from r below.
+// MXFP4) has its scale at byte r and, for NVFP4 and MXFP4, its codes at byte 8r / 16r
+// (MXFP8: at code_offset of its row and first column, two 16-byte quarters); its source
+// row and column follow from r below.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -37,10 +40,12 @@ __host__ __device__ inline int64_t block_index(int64_t K, int64_t n, int64_t k) 
     return (n >> 5) * (K >> 6) + (k >> 6);
 }
 
-// byte offset inside one expert's codes of element (n, k); k even for NVFP4
+// byte offset inside one expert's codes of element (n, k); k even for NVFP4. MXFP8 keeps
+// the four 16-column quarters of a block apart ([4][32 rows][16 bytes]).
 __host__ __device__ inline int64_t code_offset(bool nv, int64_t K, int64_t n, int64_t k) {
     const int cb = code_bytes_per_row(nv);
-    return block_index(K, n, k) * (32 * cb) + (n & 31) * cb + (nv ? (k & 63) >> 1 : (k & 63));
+    if (nv) return block_index(K, n, k) * (32 * cb) + (n & 31) * cb + ((k & 63) >> 1);
+    return block_index(K, n, k) * (32 * cb) + ((k & 63) >> 4) * 512 + (n & 31) * 16 + (k & 15);
 }
 
 // byte offset inside one expert's scales of the block scale covering (n, k)

@@ -129,9 +129,17 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp8_bf16_kernel(const uint16
         }
         uint32_t c[8];
         const int sc = mxfp8_quant_block(v, c);
-        uint4 *d = reinterpret_cast<uint4 *>(codes + b * 32);
-        d[0] = make_uint4(c[0], c[1], c[2], c[3]);
-        d[1] = make_uint4(c[4], c[5], c[6], c[7]);
+        uint4 *d0 = reinterpret_cast<uint4 *>(codes + b * 32), *d1 = d0 + 1;
+        if (tile_K) {  // packed weights: the block's two 16-column quarters (layout.h)
+            const int64_t e = b / blocks_per_expert;
+            int64_t n, k;
+            layout::block_source(false, tile_K, b - e * blocks_per_expert, n, k);
+            uint8_t *ce = codes + e * blocks_per_expert * 32;
+            d0 = reinterpret_cast<uint4 *>(ce + layout::code_offset(false, tile_K, n, k));
+            d1 = reinterpret_cast<uint4 *>(ce + layout::code_offset(false, tile_K, n, k + 16));
+        }
+        *d0 = make_uint4(c[0], c[1], c[2], c[3]);
+        *d1 = make_uint4(c[4], c[5], c[6], c[7]);
         scales[b] = (uint8_t)sc;
         if (deq) gemm_detail::store_dequant_mxfp8_32(deq + b * 32, c, sc);
     }

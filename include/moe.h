@@ -70,7 +70,8 @@ extern "C" {
  *          scales u8 [E][N/32][K/64][32][4]  E4M3 (OCP "FN": bias 7, max 448, no inf),
  *                                            one per 16 columns
  *          tensor_scale fp32 [E]  one per expert and matrix (amax / 2688, or 1)
- *   MXFP8: codes  u8 [E][N/32][K/64][32][64] E4M3
+ *   MXFP8: codes  u8 [E][N/32][K/64][4][32][16] E4M3: the block's 32 rows for columns
+ *          0-15, then 16-31, 32-47, 48-63
  *          scales u8 [E][N/32][K/64][32][2]  E8M0 (2^(c - 127)), one per 32 columns
  *          tensor_scale unused (may be NULL)
  *   MXFP4: codes  u8 [E][N/32][K/64][2][32][16] E2M1, element 2i in the low nibble of
@@ -79,13 +80,13 @@ extern "C" {
  *   BF16:  codes  u8 [E][N/32][K/64][2][32][64] bf16 values, the two 32-column halves
  *          of a block apart (column 32h + c at bytes 2c, 2c+1 of half h)
  *          scales, tensor_scale unused (may be NULL)
- *          tensor_scale unused (may be NULL)
  * Sizes are those of the row-major arrays ([E][N][K/2] (NVFP4, MXFP4) / [E][N][K]
  * (MXFP8) codes, [E][N][K/16] (NVFP4) / [E][N][K/32] (MXFP8, MXFP4) scales); only the
  * order differs. The tiling lets one wave of the
  * expert GEMMs load a 32-row weight subtile's codes for 64 columns as a single
- * contiguous 1 KiB (NVFP4) or 2 KiB (MXFP8) run; MXFP4's half-split order gives the
- * scaled FP4 MFMA's 64 lanes (32 rows x two 32-column halves) one contiguous 1 KiB.
+ * contiguous 1 KiB (NVFP4) or 2 KiB (MXFP8) run, each load instruction reading whole
+ * cache lines; MXFP4's half-split order gives the scaled FP4 MFMA's 64 lanes (32 rows x
+ * two 32-column halves) one contiguous 1 KiB.
  */
 typedef struct moe_packed {
     int32_t fmt;
