@@ -15,8 +15,11 @@
 // sequential fp32 sum (max error 1.6e-7 of the sum of |products| over K = 4096 with
 // block exponents spread over +-12, 2.3e-8 at +-4, 0 with equal exponents).
 //
-//  - workgroup tile 64 sorted rows x 256 weight rows, 4 waves side by side in N, each
-//    64 x 64 as 2 x 2 MFMA tiles; gate_up waves pair gate row f with up row F + f;
+//  - workgroup tile 128 sorted rows x 256 weight rows, 4 waves side by side in N, each
+//    128 x 64 as 4 x 2 MFMA tiles (each weight operand feeds four MFMAs: the loop is
+//    bound by the vector-memory path, and 64-row tiles fed two); a tile runs only the
+//    32-row subtiles that hold rows (an expert's last tile, every tile at decode); gate_up
+//    waves pair gate row f with up row F + f;
 //  - the activation tile (shared by the four waves) goes through double-buffered LDS four
 //    chunks at a time, loaded as whole 128-byte pieces of the gathered token rows (a
 //    per-lane operand gather would touch 32 cache lines per load and bound the loop);
@@ -25,8 +28,9 @@
 //    chunks;
 //  - work items are ordered expert-major and dealt to the 8 XCDs in contiguous ranges, as
 //    in the tile kernels;
-//  - gate_up epilogue: SwiGLU in fp32, then each wave's 64 x 32 tile goes through LDS and
-//    lane r quantises row r's 32-block to MXFP4 (16-byte code store, one scale byte).
+//  - gate_up epilogue: SwiGLU in fp32, then each wave's rows x 32 tile goes through LDS and
+//    lane r quantises rows r and r + 64's 32-blocks to MXFP4 (16-byte code store, one
+//    scale byte).
 // 32x32x64 operand layout (checked on gfx950 against an exact product): lane l holds row
 // (or column) l % 32, k 32 (l / 32) .. +31; accumulator v of lane l is row 8(v/4) +
 // 4(l/32) + v%4, column l%32.
@@ -43,7 +47,11 @@ using namespace gemm_detail;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 64, kMS = 2, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
+#ifndef MOE_MX4_BM
+#define MOE_MX4_BM 128
+#endif
+constexpr int kBM = MOE_MX4_BM, kMS = kBM / 32, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
+static_assert(kBM == 64 || kBM == 128, "64- or 128-row M-tiles");
 constexpr int kGrp = 4;                        // K chunks per A tile group
 #ifndef MOE_MX4_RING
 #define MOE_MX4_RING 4
@@ -51,7 +59,7 @@ constexpr int kGrp = 4;                        // K chunks per A tile group
 constexpr int kRing = MOE_MX4_RING;            // B operand ring depth in chunks
 static_assert(kRing % kGrp == 0, "the B ring turns over whole A groups");
 constexpr int kARow = 144;                     // LDS bytes per A row: 128 of codes + 16 (bank spread)
-constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [64 rows][8]
+constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [kBM rows][8]
 constexpr int kABuf = kACodes + kBM * 8;
 constexpr int kEpiStride = 33;  // floats per row of a wave's SwiGLU tile (bank spread)
 constexpr int kCodeBlock = 32 * 32, kScaleBlock = 32 * 2;  // bytes per 32 x 64 weight block
@@ -90,7 +98,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
     const uint8_t *wc_e = p.w_codes + (int64_t)e * N * (K / 2);
     const uint8_t *ws_e = p.w_scales + (int64_t)e * N * (K / 32);
 
-    // ---- this lane's B operand rows (weights) and A operand rows (activations)
+    // ---- this lane's B operand rows (weights)
     const uint8_t *bc[kNS];
     const uint8_t *bs[kNS];
 #pragma unroll
@@ -106,179 +114,206 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
         bc[ns] = wc_e + blk0 * kCodeBlock + g2 * 512 + (row & 31) * 16;  // = base + 16 * lane
         bs[ns] = ws_e + blk0 * kScaleBlock + g2 * 32 + (row & 31);       // = base + lane
     }
-    // ---- A tile (activations) through LDS, 4 chunks (256 k, 128 bytes of codes and 8
-    // scale bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces
-    // i = t and t + 256 (row i / 8, piece i % 8: a wave covers 8 whole 128-byte rows, so
-    // the gathered token rows are read line by line) and the two scale bytes of row t / 4,
-    // chunk t % 4. Rows past the tile's end read the tile's first row (in bounds; never
-    // stored); pieces and chunks past the end of K reread the group's first (unused).
     const int n_chunks = K / 64;
-    const int n_groups = (n_chunks + kGrp - 1) / kGrp, n_fg = n_chunks / kGrp;
+    const int n_groups = (n_chunks + kGrp - 1) / kGrp;
     auto a_row = [&](int r) -> int64_t {
         const int pos = p0 + (r < rows ? r : 0);
         return p.gather_by_token ? p.sorted_slot[pos] / p.top_k : pos;
     };
-    const int piece = threadIdx.x & 7, s_chunk = threadIdx.x & 3;
-    const uint8_t *ap[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * (K / 2);
-    const uint8_t *sp = p.a_scales + a_row(threadIdx.x >> 2) * (K / 32);
-    u32x4 a_pf[2];
-    uint32_t s_pf;
-    auto a_load = [&](int g) {
-        g = min(g, n_groups - 1);
-        const int off = 128 * g + 16 * piece;
-        const int off_ok = off < K / 2 ? off : 128 * g;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
-        s_pf = *reinterpret_cast<const uint16_t *>(sp + 2 * min(kGrp * g + s_chunk, n_chunks - 1));
-    };
-    auto a_store = [&](int buf) {
-        uint8_t *ab = lds + buf * kABuf;
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-            *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
-        *reinterpret_cast<uint16_t *>(ab + kACodes + (threadIdx.x >> 2) * 8 + 2 * s_chunk) = (uint16_t)s_pf;
-    };
 
-    // ---- B operand ring: chunk c + kRing - 1 is loaded into slot (c - 1) % kRing while chunk
-    // c is multiplied; loads past the end repeat the last chunk (in bounds, unused)
-    u32x4 breg[kRing][kNS];
-    int bsc[kRing][kNS];
-    auto b_load = [&](int slot, int c) {
+    // The tile for its first MSA 32-row M-subtiles (rows 0 .. 32 MSA - 1): an expert's last
+    // tile (and every tile at decode) usually holds fewer than kBM rows, and its loop only
+    // loads and multiplies the subtiles holding rows.
+    auto run = [&](auto msa_c) __attribute__((always_inline)) {
+        constexpr int MSA = decltype(msa_c)::value;
+        constexpr int AQ = MSA;                    // 16-byte A pieces per thread per group (32 rows each)
+        constexpr int SQ = MSA > 2 ? 2 : 1;        // A scale words per thread per group (64 rows each)
+        // ---- A tile (activations) through LDS, 4 chunks (256 k, 128 bytes of codes and 8
+        // scale bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces
+        // i = t + 256 q (row i / 8, piece i % 8: a wave covers 8 whole 128-byte rows, so
+        // the gathered token rows are read line by line) and the two scale bytes of rows
+        // t / 4 + 64 q, chunk t % 4. Rows past the tile's end read the tile's first row
+        // (in bounds; never stored); pieces and chunks past the end of K reread the
+        // group's first (unused).
+        const int piece = threadIdx.x & 7, s_chunk = threadIdx.x & 3;
+        const uint8_t *ap[AQ];
 #pragma unroll
-        for (int ns = 0; ns < kNS; ++ns) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c);
-            if constexpr (NT)
-                breg[slot][ns] = __builtin_nontemporal_load(src);
-            else
-                breg[slot][ns] = *src;
-            bsc[slot][ns] = bs[ns][(int64_t)kScaleBlock * c];
-        }
-    };
-    float16_t acc[kMS][kNS];
+        for (int q = 0; q < AQ; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * (K / 2);
+        const uint8_t *sp[SQ];
 #pragma unroll
-    for (int i = 0; i < kMS; ++i)
+        for (int q = 0; q < SQ; ++q) sp[q] = p.a_scales + a_row(64 * q + (threadIdx.x >> 2)) * (K / 32);
+        u32x4 a_pf[AQ];
+        uint32_t s_pf[SQ];
+        auto a_load = [&](int g) {
+            g = min(g, n_groups - 1);
+            const int off = 128 * g + 16 * piece;
+            const int off_ok = off < K / 2 ? off : 128 * g;
 #pragma unroll
-        for (int j = 0; j < kNS; ++j) acc[i][j] = (float16_t){};
-    uint32_t a_sc[kMS][2];
-    auto a_scales = [&](int buf) {
-        const uint8_t *ab = lds + buf * kABuf + kACodes;
+            for (int q = 0; q < AQ; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
 #pragma unroll
-        for (int ms = 0; ms < kMS; ++ms) {
-            const uint2 v = *reinterpret_cast<const uint2 *>(ab + (32 * ms + l32) * 8);
-            a_sc[ms][0] = v.x >> (8 * g2);
-            a_sc[ms][1] = v.y >> (8 * g2);
-        }
-    };
-    // chunk j of the group in LDS buffer buf times the B operands in ring slot `slot`
-    auto mma = [&](int buf, int j, int slot) {
-        const uint8_t *ab = lds + buf * kABuf;
-        u32x4 af[kMS];
+            for (int q = 0; q < SQ; ++q)
+                s_pf[q] = *reinterpret_cast<const uint16_t *>(sp[q] + 2 * min(kGrp * g + s_chunk, n_chunks - 1));
+        };
+        auto a_store = [&](int buf) {
+            uint8_t *ab = lds + buf * kABuf;
 #pragma unroll
-        for (int ms = 0; ms < kMS; ++ms)
-            af[ms] = *reinterpret_cast<const u32x4 *>(ab + (32 * ms + l32) * kARow + 32 * j + 16 * g2);
+            for (int q = 0; q < AQ; ++q)
+                *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
 #pragma unroll
-        for (int ms = 0; ms < kMS; ++ms) {
-            const int sa = (int)((a_sc[ms][j >> 1] >> (16 * (j & 1))) & 0xffu);
-#pragma unroll
-            for (int ns = 0; ns < kNS; ++ns)
-                acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    fp4_operand(af[ms]), fp4_operand(breg[slot][ns]), acc[ms][ns], 4, 4, 0, sa, 0, bsc[slot][ns]);
-        }
-    };
-    // after the last chunk of group g: group g + 1 into the other buffer (last read in group
-    // g - 1, before the previous barrier), group g + 2 into registers
-    auto next_group = [&](int g) {
-        a_store((g & 1) ^ 1);
-        a_load(g + 2);
-        __syncthreads();
-    };
+            for (int q = 0; q < SQ; ++q)
+                *reinterpret_cast<uint16_t *>(ab + kACodes + (64 * q + (threadIdx.x >> 2)) * 8 + 2 * s_chunk) =
+                    (uint16_t)s_pf[q];
+        };
 
-    a_load(0);
-    a_store(0);
-    a_load(1);
-#pragma unroll
-    for (int r = 0; r < kRing - 1; ++r) b_load(r, min(r, n_chunks - 1));
-    __syncthreads();
-    // whole ring turns without a branch inside (a conditional use would let the compiler
-    // sink the prefetches into it), then the last n_chunks % kRing chunks, already loaded
-    const int n_full = n_chunks - n_chunks % kRing;
-    for (int c0 = 0; c0 < n_full; c0 += kRing) {
-#pragma unroll
-        for (int gi = 0; gi < kRing / kGrp; ++gi) {
-            const int g = c0 / kGrp + gi;
-            a_scales(g & 1);
-#pragma unroll
-            for (int j = 0; j < kGrp; ++j) {
-                // keep each chunk's prefetch in place: left alone, the scheduler gathers
-                // the ring's loads at the end of the group and waits for them all at once
-                __builtin_amdgcn_sched_barrier(0);
-                const int slot = gi * kGrp + j;
-                b_load((slot + kRing - 1) % kRing, min(c0 + slot + kRing - 1, n_chunks - 1));
-                mma(g & 1, j, slot);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-            next_group(g);
-        }
-    }
-#pragma unroll
-    for (int t = 0; t < kRing - 1; ++t) {
-        const int c = n_full + t;
-        if (c >= n_chunks) break;
-        const int g = c / kGrp;
-        if (t % kGrp == 0) a_scales(g & 1);
-        mma(g & 1, t % kGrp, t);
-        if (t % kGrp == kGrp - 1 && c + 1 < n_chunks) next_group(g);
-    }
-
-    // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
-    if (GATE_UP) {
-        __syncthreads();  // the SwiGLU tiles reuse the A tiles' LDS
-        float *we = reinterpret_cast<float *>(lds) + wave * kBM * kEpiStride;
-#pragma unroll
-        for (int ms = 0; ms < kMS; ++ms)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                we[m * kEpiStride + l32] = swiglu(acc[ms][0][v], acc[ms][1][v]);
-            }
-        __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
-        const int m = lane;  // kBM == 64: one row per lane
-        if (m < rows) {
-            const int64_t row = p0 + m;
-            const int fb = nb * (kBN / 2) + wave * 32;  // first column of this wave's block
-            float x[32];
-#pragma unroll
-            for (int i = 0; i < 32; ++i) x[i] = we[m * kEpiStride + i];
-            uint32_t cw[4];
-            const int sc = mxfp4_quant_block(x, cw);
-            *reinterpret_cast<u32x4 *>(p.o_codes + row * (F / 2) + fb / 2) = (u32x4){cw[0], cw[1], cw[2], cw[3]};
-            p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
-            if (p.o_tap) {
-                float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
-            }
-        }
-    } else {
-#pragma unroll
-        for (int ms = 0; ms < kMS; ++ms)
+        // ---- B operand ring: chunk c + kRing - 1 is loaded into slot (c - 1) % kRing while
+        // chunk c is multiplied; loads past the end repeat the last chunk (in bounds, unused)
+        u32x4 breg[kRing][kNS];
+        int bsc[kRing][kNS];
+        auto b_load = [&](int slot, int c) {
 #pragma unroll
             for (int ns = 0; ns < kNS; ++ns) {
-                const int n = nb * kBN + wave * 64 + 32 * ns + l32;
+                const u32x4 *src = reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c);
+                if constexpr (NT)
+                    breg[slot][ns] = __builtin_nontemporal_load(src);
+                else
+                    breg[slot][ns] = *src;
+                bsc[slot][ns] = bs[ns][(int64_t)kScaleBlock * c];
+            }
+        };
+        float16_t acc[MSA][kNS];
+#pragma unroll
+        for (int i = 0; i < MSA; ++i)
+#pragma unroll
+            for (int j = 0; j < kNS; ++j) acc[i][j] = (float16_t){};
+        uint32_t a_sc[MSA][2];
+        auto a_scales = [&](int buf) {
+            const uint8_t *ab = lds + buf * kABuf + kACodes;
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms) {
+                const uint2 v = *reinterpret_cast<const uint2 *>(ab + (32 * ms + l32) * 8);
+                a_sc[ms][0] = v.x >> (8 * g2);
+                a_sc[ms][1] = v.y >> (8 * g2);
+            }
+        };
+        // chunk j of the group in LDS buffer buf times the B operands in ring slot `slot`
+        auto mma = [&](int buf, int j, int slot) {
+            const uint8_t *ab = lds + buf * kABuf;
+            u32x4 af[MSA];
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms)
+                af[ms] = *reinterpret_cast<const u32x4 *>(ab + (32 * ms + l32) * kARow + 32 * j + 16 * g2);
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms) {
+                const int sa = (int)((a_sc[ms][j >> 1] >> (16 * (j & 1))) & 0xffu);
+#pragma unroll
+                for (int ns = 0; ns < kNS; ++ns)
+                    acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        fp4_operand(af[ms]), fp4_operand(breg[slot][ns]), acc[ms][ns], 4, 4, 0, sa, 0, bsc[slot][ns]);
+            }
+        };
+        // after the last chunk of group g: group g + 1 into the other buffer (last read in
+        // group g - 1, before the previous barrier), group g + 2 into registers
+        auto next_group = [&](int g) {
+            a_store((g & 1) ^ 1);
+            a_load(g + 2);
+            __syncthreads();
+        };
+
+        a_load(0);
+        a_store(0);
+        a_load(1);
+#pragma unroll
+        for (int r = 0; r < kRing - 1; ++r) b_load(r, min(r, n_chunks - 1));
+        __syncthreads();
+        // whole ring turns without a branch inside (a conditional use would let the
+        // compiler sink the prefetches into it), then the last n_chunks % kRing chunks,
+        // already loaded
+        const int n_full = n_chunks - n_chunks % kRing;
+        for (int c0 = 0; c0 < n_full; c0 += kRing) {
+#pragma unroll
+            for (int gi = 0; gi < kRing / kGrp; ++gi) {
+                const int g = c0 / kGrp + gi;
+                a_scales(g & 1);
+#pragma unroll
+                for (int j = 0; j < kGrp; ++j) {
+                    // keep each chunk's prefetch in place: left alone, the scheduler gathers
+                    // the ring's loads at the end of the group and waits for them all at once
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int slot = gi * kGrp + j;
+                    b_load((slot + kRing - 1) % kRing, min(c0 + slot + kRing - 1, n_chunks - 1));
+                    mma(g & 1, j, slot);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                next_group(g);
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < kRing - 1; ++t) {
+            const int c = n_full + t;
+            if (c >= n_chunks) break;
+            const int g = c / kGrp;
+            if (t % kGrp == 0) a_scales(g & 1);
+            mma(g & 1, t % kGrp, t);
+            if (t % kGrp == kGrp - 1 && c + 1 < n_chunks) next_group(g);
+        }
+
+        // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
+        if (GATE_UP) {
+            __syncthreads();  // the SwiGLU tiles reuse the A tiles' LDS
+            float *we = reinterpret_cast<float *>(lds) + wave * kBM * kEpiStride;
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                    if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = acc[ms][ns][v];
+                    we[m * kEpiStride + l32] = swiglu(acc[ms][0][v], acc[ms][1][v]);
+                }
+            __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+            const int fb = nb * (kBN / 2) + wave * 32;  // first column of this wave's block
+#pragma unroll
+            for (int m0 = 0; m0 < 32 * MSA; m0 += 64) {
+                const int m = m0 + lane;  // one row per lane
+                if (m < rows && m < 32 * MSA) {
+                    const int64_t row = p0 + m;
+                    float x[32];
+#pragma unroll
+                    for (int i = 0; i < 32; ++i) x[i] = we[m * kEpiStride + i];
+                    uint32_t cw[4];
+                    const int sc = mxfp4_quant_block(x, cw);
+                    *reinterpret_cast<u32x4 *>(p.o_codes + row * (F / 2) + fb / 2) = (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                    p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                    if (p.o_tap) {
+                        float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
+#pragma unroll
+                        for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                    }
                 }
             }
-    }
+        } else {
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms)
+#pragma unroll
+                for (int ns = 0; ns < kNS; ++ns) {
+                    const int n = nb * kBN + wave * 64 + 32 * ns + l32;
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                        if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = acc[ms][ns][v];
+                    }
+                }
+        }
+    };
+    if (rows <= 32)
+        run(std::integral_constant<int, 1>{});
+    else if (kMS == 4 && rows <= 64)
+        run(std::integral_constant<int, 2>{});
+    else
+        run(std::integral_constant<int, kMS>{});
 }
 
 }  // namespace
 
-static_assert(kBM == 64, "the plan gives MXFP4 layers 64-row M-tiles");
+int32_t mx4_gemm_bm() { return kBM; }
 
 bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up) {
     if (K <= 0 || N <= 0 || K % 64) return false;

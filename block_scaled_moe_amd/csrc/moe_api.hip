@@ -48,10 +48,10 @@ Plan make_plan(const moe_forward_args *a) {
     const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
-    // MXFP4 always runs the scaled-FP4 MFMA kernels (64-row M-tiles)
+    // MXFP4 always runs the scaled-FP4 MFMA kernels
     p.tiled = mx4 || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
                       tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
-    p.bm = mx4 ? 64 : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
+    p.bm = mx4 ? mx4_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
