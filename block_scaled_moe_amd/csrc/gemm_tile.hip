@@ -49,9 +49,12 @@ constexpr int kAStride = kKC * 2 + 16;  // LDS bytes per activation row
 #ifndef MOE_TILE_BM_MX
 #define MOE_TILE_BM_MX 128
 #endif
+#ifndef MOE_TILE_BM_BF
+#define MOE_TILE_BM_BF 64
+#endif
 template <int FM>
 constexpr int tile_bm() {
-    return FM == kFmtNV ? MOE_TILE_BM_NV : (FM == kFmtMX8 ? MOE_TILE_BM_MX : 64);
+    return FM == kFmtNV ? MOE_TILE_BM_NV : (FM == kFmtMX8 ? MOE_TILE_BM_MX : (FM == kFmtBF ? MOE_TILE_BM_BF : 64));
 }
 template <int BM>
 constexpr int a_stage() { return BM * kAStride; }  // one LDS activation buffer
@@ -410,7 +413,7 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
     // most 32 rows).
     using I1 = std::integral_constant<int, 1>;
     using INS = std::integral_constant<int, NS>;
-    constexpr bool SHORT = MOE_TILE_SHORT && FM != kFmtBF;  // bf16: no gain, and more spills
+    constexpr bool SHORT = MOE_TILE_SHORT && (FM != kFmtBF || kMS == 4);  // bf16 64-row: no gain, more spills
     if constexpr (kMS == 4) {
         if (SHORT && rows <= 32) {
             run(I1{}, INS{});
