@@ -52,9 +52,13 @@ constexpr int kAStride = kKC * 2 + 16;  // LDS bytes per activation row
 #ifndef MOE_TILE_BM_BF
 #define MOE_TILE_BM_BF 64
 #endif
+#ifndef MOE_TILE_BM_A16
+#define MOE_TILE_BM_A16 64
+#endif
 template <int FM>
 constexpr int tile_bm() {
-    return FM == kFmtNV ? MOE_TILE_BM_NV : (FM == kFmtMX8 ? MOE_TILE_BM_MX : (FM == kFmtBF ? MOE_TILE_BM_BF : 64));
+    return FM == kFmtNV ? MOE_TILE_BM_NV
+                        : (FM == kFmtMX8 ? MOE_TILE_BM_MX : (FM == kFmtBF ? MOE_TILE_BM_BF : MOE_TILE_BM_A16));
 }
 template <int BM>
 constexpr int a_stage() { return BM * kAStride; }  // one LDS activation buffer
