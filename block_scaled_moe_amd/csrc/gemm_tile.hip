@@ -72,9 +72,6 @@ static_assert(64 * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thre
 #ifndef MOE_TILE_SHORT
 #define MOE_TILE_SHORT 1  // short tiles run only the M-subtiles holding rows
 #endif
-#ifndef MOE_TILE_SHORT3
-#define MOE_TILE_SHORT3 0  // 128-row tiles: also a three-subtile mode for 65..96 rows (measured: no gain)
-#endif
 #ifndef MOE_TILE_NS_NV
 #define MOE_TILE_NS_NV (MOE_TILE_BM_NV == 128 ? 2 : 4)
 #endif
@@ -110,13 +107,6 @@ constexpr int tile_smem_bytes() {
 // waves per SIMD the register budget is set for
 template <int NS, int BM>
 constexpr int tile_waves_per_simd() { return BM == 64 ? (NS == 2 ? 3 : 2) : (NS == 2 ? 2 : 1); }
-
-// An expert's last 128-row tile often holds at most 64 rows. Such a half tile runs half
-// the M-subtiles; for NVFP4 weights it covers two N-blocks instead (the work item of the
-// even N-block takes both, the odd one exits), keeping the 64-row kernel's operand reuse:
-// each expanded weight fragment feeds two MFMAs and each activation fragment 2 NS.
-template <int FM>
-constexpr bool half_tile_doubles_n() { return FM == kFmtNV || FM == kFmtA16; }
 
 template <int FM, bool GATE_UP, int NS, int BM>
 __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) tile_gemm_kernel(const GemmArgs p) {
@@ -194,33 +184,30 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
     _Pragma("unroll") for (int i = 0; i < AI; ++i)                                                         \
         *reinterpret_cast<u32x4 *>(smem + (buf) * kAStage + a_dst[i]) = a_reg[set][i];
 #define MOE_LOAD_W(slot, c)                                                                                \
-    _Pragma("unroll") for (int ns = 0; ns < NSA; ++ns) {                                                   \
+    _Pragma("unroll") for (int ns = 0; ns < NS; ++ns) {                                                    \
         _Pragma("unroll") for (int v = 0; v < CV; ++v) wcode[slot][ns][v] =                                \
             *reinterpret_cast<const u32x4 *>(wc[ns] + (int64_t)CBLK * (c) + WSTEP * v);                    \
         wsc[slot][ns] = BW ? 0u : *reinterpret_cast<const uint32_t *>(ws[ns] + (int64_t)SBLK * (c));      \
     }
 
-    // The tile for MSA 32-row M-subtiles (rows 0 .. 32 MSA - 1) and NSA 32-row weight
-    // subtiles per wave: NS of N-block nb, and for a doubled half tile NS more of nb + 1.
-    // Subtile ns belongs to N-block nb + ns / NS; within a block, gate_up pairs gate
-    // subtile q with up subtile q + NS / 2.
-    auto run = [&](auto msa_c, auto nsa_c) __attribute__((always_inline)) {
-        constexpr int MSA = decltype(msa_c)::value, NSA = decltype(nsa_c)::value;
-        constexpr int NBW = NSA / NS;            // N-blocks covered
+    // The tile for its first MSA 32-row M-subtiles (rows 0 .. 32 MSA - 1) and the NS
+    // 32-row weight subtiles of each wave; gate_up pairs gate subtile q with up subtile
+    // q + NS / 2.
+    auto run = [&](auto msa_c) __attribute__((always_inline)) {
+        constexpr int MSA = decltype(msa_c)::value;
         constexpr int AI = kAItems * MSA / kMS;  // activation loads per thread per chunk
 
         // ---- this lane's weight rows, one per N subtile (each subtile is one row group)
-        const uint8_t *wc[NSA];
-        const uint8_t *ws[NSA];
+        const uint8_t *wc[NS];
+        const uint8_t *ws[NS];
 #pragma unroll
-        for (int ns = 0; ns < NSA; ++ns) {
-            const int bn = nb + ns / NS, ls = ns % NS;
+        for (int ns = 0; ns < NS; ++ns) {
             int row;
             if (GATE_UP) {
-                const int col = bn * (BN / 2) + wave * 16 * NS + 32 * (ls % (NS / 2)) + l32;
-                row = ls < NS / 2 ? col : F + col;
+                const int col = nb * (BN / 2) + wave * 16 * NS + 32 * (ns % (NS / 2)) + l32;
+                row = ns < NS / 2 ? col : F + col;
             } else {
-                row = bn * BN + wave * 32 * NS + 32 * ls + l32;
+                row = nb * BN + wave * 32 * NS + 32 * ns + l32;
             }
             const int64_t blk0 = (int64_t)(row >> 5) * kb;
             wc[ns] = w_codes_e + blk0 * CBLK +
@@ -228,15 +215,15 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
             ws[ns] = BW ? nullptr : w_scales_e + blk0 * SBLK + (NV ? 4 * l32 : 4 * (l32 >> 1));
         }
 
-        float16_t acc[MSA][NSA];
+        float16_t acc[MSA][NS];
 #pragma unroll
         for (int i = 0; i < MSA; ++i)
 #pragma unroll
-            for (int j = 0; j < NSA; ++j) acc[i][j] = (float16_t){};
+            for (int j = 0; j < NS; ++j) acc[i][j] = (float16_t){};
 
         u32x4 a_reg[2][AI];
-        u32x4 wcode[WR][NSA][CV];
-        uint32_t wsc[WR][NSA];
+        u32x4 wcode[WR][NS][CV];
+        uint32_t wsc[WR][NS];
         MOE_LOAD_A(0, 0);
         MOE_STORE_A(0, 0);
         MOE_LOAD_A(1, 1);
@@ -257,10 +244,10 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
                 // scale words: NVFP4 holds the row's 4 block scales of the chunk (this lane's
                 // pair is bytes 2g, 2g+1); MXFP8 holds two rows' 2 block scales (this lane's
                 // is byte 2 (row % 2) + g)
-                half2_t sc_nv[NSA];
-                float sc_mx[NSA];
+                half2_t sc_nv[NS];
+                float sc_mx[NS];
 #pragma unroll
-                for (int ns = 0; ns < NSA; ++ns) {
+                for (int ns = 0; ns < NS; ++ns) {
                     if constexpr (NV) {
                         sc_nv[ns] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(wsc[j][ns] >> (16 * g2), 1.0f, false);
                     } else if constexpr (!BW) {
@@ -274,7 +261,7 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
                     for (int ms = 0; ms < MSA; ++ms)
                         af[ms] = *reinterpret_cast<const Frag *>(abuf + (32 * ms + l32) * kAStride + 64 * g2 + 16 * s);
 #pragma unroll
-                    for (int ns = 0; ns < NSA; ++ns) {
+                    for (int ns = 0; ns < NS; ++ns) {
                         if constexpr (NV) {
                             if constexpr (A16) {
                                 const bf16x8 bf = dequant_nvfp4_bf16(wcode[j][ns][0][s], (float)sc_nv[ns][s >> 1]);
@@ -315,43 +302,39 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
             // W4A16 and bf16 experts: the SwiGLU output rounded to bf16 (nearest even) is
             // the down GEMM's input
 #pragma unroll
-            for (int bw = 0; bw < NBW; ++bw)
+            for (int q = 0; q < NS / 2; ++q) {
+                const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
 #pragma unroll
-                for (int q = 0; q < NS / 2; ++q) {
-                    const int f = (nb + bw) * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+                for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
-                    for (int ms = 0; ms < MSA; ++ms)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                            if (m < rows) {
-                                const int64_t o = (int64_t)(p0 + m) * F + f;
-                                const float hv = swiglu(acc[ms][bw * NS + q][v] * scl, acc[ms][bw * NS + q + NS / 2][v] * scl);
-                                static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
-                                if (p.o_tap) p.o_tap[o] = hv;
-                            }
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                        if (m < rows) {
+                            const int64_t o = (int64_t)(p0 + m) * F + f;
+                            const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
+                            static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
+                            if (p.o_tap) p.o_tap[o] = hv;
                         }
-                }
+                    }
+            }
         } else if (GATE_UP && NV) {
             uint32_t amax = 0;
 #pragma unroll
-            for (int bw = 0; bw < NBW; ++bw)
+            for (int q = 0; q < NS / 2; ++q) {
+                const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
 #pragma unroll
-                for (int q = 0; q < NS / 2; ++q) {
-                    const int f = (nb + bw) * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+                for (int ms = 0; ms < MSA; ++ms) {
 #pragma unroll
-                    for (int ms = 0; ms < MSA; ++ms) {
-#pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                            const float hv = swiglu(acc[ms][bw * NS + q][v] * scl, acc[ms][bw * NS + q + NS / 2][v] * scl);
-                            if (m < rows) {
-                                p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
-                                amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
-                            }
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                        const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
+                        if (m < rows) {
+                            p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
+                            amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
                         }
                     }
                 }
+            }
             for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
             if (lane == 0 && amax) atomic_max_grow(p.amax_bits, amax);
         } else if (GATE_UP) {
@@ -359,7 +342,6 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
             // blocks) goes through its own LDS region; lane r then quantises whole blocks
             // of row r with 16-byte stores. The A stages are free: every wave passed the
             // loop's last barrier.
-            static_assert(FM != kFmtMX8 || !half_tile_doubles_n<FM>(), "one N-block per MXFP8 tile");
             float *epi = reinterpret_cast<float *>(smem) + wave * kBM * kEpiStride<NS>();
 #pragma unroll
             for (int q = 0; q < NS / 2; ++q)
@@ -398,8 +380,8 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
-                for (int ns = 0; ns < NSA; ++ns) {
-                    const int n = (nb + ns / NS) * BN + wave * 32 * NS + 32 * (ns % NS) + l32;
+                for (int ns = 0; ns < NS; ++ns) {
+                    const int n = nb * BN + wave * 32 * NS + 32 * ns + l32;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
@@ -415,31 +397,13 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
     // A tile runs only as many 32-row M-subtiles as it has rows (an expert's last tile is
     // usually short: at about 170 rows per expert half of the last 64-row tiles hold at
     // most 32 rows).
-    using I1 = std::integral_constant<int, 1>;
-    using INS = std::integral_constant<int, NS>;
     constexpr bool SHORT = MOE_TILE_SHORT && (FM != kFmtBF || kMS == 4);  // bf16 64-row: no gain, more spills
-    if constexpr (kMS == 4) {
-        if (SHORT && rows <= 32) {
-            run(I1{}, INS{});
-        } else if (rows <= 64) {
-            if constexpr (half_tile_doubles_n<FM>()) {
-                if (nb & 1) return;  // the even N-block's item covers this one
-                run(std::integral_constant<int, 2>{}, std::integral_constant<int, 2 * NS>{});
-            } else {
-                run(std::integral_constant<int, 2>{}, INS{});
-            }
-        } else if (SHORT && MOE_TILE_SHORT3 && rows <= 96) {
-            run(std::integral_constant<int, 3>{}, INS{});
-        } else {
-            run(std::integral_constant<int, 4>{}, INS{});
-        }
-    } else {
-        static_assert(kMS == 2, "64- or 128-row tiles");
-        if (SHORT && rows <= 32)
-            run(I1{}, INS{});
-        else
-            run(std::integral_constant<int, 2>{}, INS{});
-    }
+    if (SHORT && rows <= 32)
+        run(std::integral_constant<int, 1>{});
+    else if (kMS == 4 && rows <= 64)
+        run(std::integral_constant<int, kMS == 4 ? 2 : kMS>{});
+    else
+        run(std::integral_constant<int, kMS>{});
 }
 
 template <int FM, bool GATE_UP>
@@ -467,10 +431,8 @@ int32_t tile_gemm_bm(int fm) {
 
 template <int FM>
 bool supported_t(int32_t K, int32_t N, bool gate_up) {
-    constexpr int BM = tile_bm<FM>(), BN = 128 * tile_ns<FM>();
-    // a doubled half tile takes two N-blocks, so their count must be even
-    constexpr int W = (BM == 128 && half_tile_doubles_n<FM>()) ? 2 * BN : BN;
-    return K > 0 && N > 0 && K % (MOE_TILE_WR * kKC) == 0 && (gate_up ? (N / 2) % (W / 2) == 0 : N % W == 0);
+    constexpr int BN = 128 * tile_ns<FM>();
+    return K > 0 && N > 0 && K % (MOE_TILE_WR * kKC) == 0 && (gate_up ? (N / 2) % (BN / 2) == 0 : N % BN == 0);
 }
 
 bool tile_gemm_supported(int fm, int32_t K, int32_t N, bool gate_up) {
