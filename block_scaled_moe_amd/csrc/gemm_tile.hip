@@ -3,8 +3,13 @@
 //
 // Same arithmetic as the other grouped GEMMs (exact 16-bit expansion of NVFP4 / MXFP8
 // codes, fp32 accumulation; see gemm_common.h), tiled for MFMA throughput:
-//  - workgroup tile 64 sorted rows x (128 NS) weight rows, 4 waves side by side in N,
-//    each wave 64 x 32NS as 2 x NS tiles of v_mfma_f32_32x32x16_{f16,bf16};
+//  - workgroup tile BM sorted rows x (128 NS) weight rows, 4 waves side by side in N,
+//    each wave BM x 32NS as BM/32 x NS tiles of v_mfma_f32_32x32x16_{f16,bf16}; per
+//    format (tile_bm, tile_ns) BM = 64, NS = 4 for NVFP4 and W4A16, BM = 128, NS = 2 for
+//    MXFP8, BM = 64, NS = 2 for bf16. Per MFMA a wave issues 256 / BM expansion
+//    instructions (NVFP4) and 1/NS activation reads from LDS; the shapes are the measured
+//    best trade between the two at the register budget of two or three waves per SIMD;
+//  - a tile runs only the 32-row M-subtiles that hold rows (short tiles);
 //  - the waves own disjoint weight rows, so weights never pass through LDS: each lane
 //    loads its weight row's codes straight into registers and expands them into the
 //    MFMA B operand; only the shared activation tile is staged in LDS;
@@ -12,12 +17,12 @@
 //    g (lanes 32g..32g+31) supplies k = 32g..32g+31 over the chunk's four MFMA steps
 //    (step s: k = 32g + 8s .. +7). With the packed tile layout (layout.h) a wave's codes
 //    for one chunk and 32-row subtile are then one contiguous 1 KiB (NVFP4) / 2 KiB
-//    (MXFP8) run and its scales one 128 / 64-byte run; the fp32 sums are unchanged up
-//    to rounding order;
+//    (MXFP8: two 512-byte runs per load instruction, its quarters being apart) and its
+//    scales one 128 / 64-byte run; the fp32 sums are unchanged up to rounding order;
 //  - software pipeline without branches: activations two chunks ahead (two register
 //    sets, LDS double buffer), weights WR chunks ahead (register ring), so every wait
-//    count in the loop is partial; a two-slot ring keeps three waves per SIMD, which
-//    measured faster than a deeper ring at two (and 128-row tiles at one);
+//    count in the loop is partial; a two-slot ring measured faster than deeper rings at
+//    fewer waves per SIMD;
 //  - gate_up tiles pair gate row f with up row F + f in the same lane and accumulator
 //    slot, so SwiGLU needs no data exchange;
 //  - work items (M-tile, N-block) are ordered expert-major (gemm_common.h) and dealt to
