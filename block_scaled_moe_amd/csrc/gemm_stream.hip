@@ -42,11 +42,13 @@ constexpr int kRows = 64;  // weight rows per workgroup
 // (first loads in flight) and end (cross-wave sum, epilogue) leave its slot idle; more
 // resident workgroups per CU cover those phases. Measured on the NVFP4 decode layer: two
 // groups at three waves per SIMD beat four groups at two (gate_up 0.536 -> 0.498 ms,
-// down 0.287 -> 0.270 ms); three groups at three waves spill and lose. MXFP8 (twice the
+// down 0.287 -> 0.270 ms); three groups at three waves spill and lose; one group at four
+// waves matches two at three on NVFP4 and is 3% faster on W4A16 (more expansion VALU
+// per byte to hide). MXFP8 (twice the
 // bytes per lane) keeps two groups at two waves (one group at three measured slower);
 // bf16 takes one group at two waves (2% faster than two groups at one).
 #ifndef MOE_STREAM_W_NV
-#define MOE_STREAM_W_NV 2
+#define MOE_STREAM_W_NV 1
 #endif
 #ifndef MOE_STREAM_W_MX
 #define MOE_STREAM_W_MX 2
@@ -55,7 +57,7 @@ constexpr int kRows = 64;  // weight rows per workgroup
 #define MOE_STREAM_W_BF 1
 #endif
 #ifndef MOE_STREAM_OCC_NV
-#define MOE_STREAM_OCC_NV 3
+#define MOE_STREAM_OCC_NV 4
 #endif
 #ifndef MOE_STREAM_OCC_MX
 #define MOE_STREAM_OCC_MX 2
