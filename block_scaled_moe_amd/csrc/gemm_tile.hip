@@ -74,6 +74,9 @@ static_assert(64 * kKC * 2 / 16 % kThreads == 0, "activation loads tile the thre
 #ifndef MOE_TILE_WR
 #define MOE_TILE_WR 2  // weight chunks in flight (register ring slots)
 #endif
+// The loop picks the activation register set and LDS buffer of chunk c = c0 + j by j & 1,
+// which equals c & 1 only while c0 (a multiple of the ring size) is even.
+static_assert(MOE_TILE_WR % 2 == 0, "the weight ring size must be even");
 #ifndef MOE_TILE_SHORT
 #define MOE_TILE_SHORT 1  // short tiles run only the M-subtiles holding rows
 #endif

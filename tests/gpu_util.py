@@ -80,7 +80,13 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
         codes match the GPU output on every token, to 2e-3 x RMS;
      2. independent: tokens none of whose slots holds a flipped intermediate row match
         the fully independent oracle output, to 2e-3 x RMS;
-     3. flips stay rare (< 1e-3 of the intermediate elements).
+     3. flips stay rare (< 1e-3 of the intermediate elements); for the 4- and 8-bit code
+        formats at least half of the compared tokens have no flipped row (so check 2
+        covers most of the batch). A bf16 intermediate (W4A16, bf16 experts) flips by one
+        bf16 ulp (2^-8 relative) wherever the two sums straddle a rounding boundary,
+        which reaches most tokens of a batch: check 4 is the one that bounds it;
+     4. over all tokens, flipped ones included, the RMS of the difference from the fully
+        independent output stays within 2e-3 x RMS.
     rows: optional token subset to compare (the others are not computed by the oracle).
     Returns (stage error / RMS, independent error / RMS, flips, tokens excluded)."""
     k = idx.shape[1]
@@ -102,9 +108,13 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
     assert flips <= 1e-3 * S * F, f"{flips} intermediate code flips in {S * F} elements"
     bad_tokens = set((sorted_slot[flipped_rows] // k).tolist())
     keep = np.array([t for t in sel if t not in bad_tokens], dtype=np.int64)
+    if fmt not in ("w4a16", "bf16"):
+        assert 2 * len(keep) >= len(sel), f"{len(sel) - len(keep)} of {len(sel)} tokens reach a flipped row"
     r_ref = rms(ref[sel])
     e_ind = float(np.abs(out[keep] - ref[keep]).max()) / r_ref if len(keep) else 0.0
     assert e_ind <= 2e-3, f"independent output error {e_ind:.2e} x RMS on tokens without flips"
+    rel_rms = rms(out[sel] - ref[sel]) / r_ref
+    assert rel_rms <= 2e-3, f"independent output RMS error {rel_rms:.2e} x RMS"
     return e_stage, e_ind, flips, len(sel) - len(keep)
 
 
