@@ -32,7 +32,7 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "fp8": 5033.2, "fp4": 10066.3}  # dense, MI355X
 DTYPES = {"nvfp4": "f16 (exact NVFP4 values), fp32 accumulate",
-          "mxfp8": "bf16 (exact MXFP8 values), fp32 accumulate",
+          "mxfp8": "fp8 (MXFP8 codes and E8M0 scales on the scaled MFMA), fp32 accumulate",
           "mxfp4": "fp4 (MXFP4 codes and E8M0 scales on the scaled MFMA), fp32 accumulate",
           "w4a16": "bf16 (bf16 activations, NVFP4 weights expanded exactly), fp32 accumulate",
           "bf16": "bf16 (bf16 weights and activations), fp32 accumulate"}
@@ -72,23 +72,8 @@ KERNEL_SOURCES = {
     "stream_gemm_kernel": ["gemm_stream.hip", "gemm_common.h", "layout.h", "formats.h"],
     "tile_gemm_kernel": ["gemm_tile.hip", "gemm_common.h", "layout.h", "formats.h"],
     "grouped_gemm_kernel": ["gemm.hip", "gemm_common.h", "layout.h", "formats.h"],
-    "mx4_gemm_kernel": ["gemm_mx4.hip", "gemm_common.h", "layout.h", "formats.h"],
+    "mx_gemm_kernel": ["gemm_mx.hip", "gemm_common.h", "layout.h", "formats.h"],
 }
-
-
-def gate_up_kernel(wl) -> str:
-    """The gate_up kernel moe_forward picks for this shape (same rule as its plan: 48+
-    slots per expert on average -> MFMA tiles when both GEMMs fit them, else the
-    streaming kernel when K allows; MXFP4 always runs its scaled-FP4 MFMA kernel)."""
-    if wl.fmt == "mxfp4":
-        return "mx4_gemm_kernel"
-    # the tile kernels' N-blocks: MXFP8 256 weight rows (128-row M-tiles), the others 512
-    d_blk, f_blk = (256, 128) if wl.fmt == "mxfp8" else (512, 256)
-    if wl.T * wl.k // wl.E >= 48 and wl.D % d_blk == 0 and wl.F % f_blk == 0:
-        return "tile_gemm_kernel"
-    if wl.D % 512 == 0 and wl.D // 512 <= 8:
-        return "stream_gemm_kernel"
-    return "grouped_gemm_kernel"
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -335,7 +320,9 @@ def main():
     # the NVFP4 / MXFP8 GEMMs run f16 / bf16 MFMAs on exactly expanded values, so that is
     # the contraction's peak, with the format's own scaled-MFMA peak reported beside it;
     # the MXFP4 GEMMs run the scaled FP4 MFMA itself
-    mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else "bf16")]
+    kern = layer.plan()["gate_up_kernel"]  # what moe_forward dispatched (its own plan)
+    native8 = wl.fmt == "mxfp8" and kern == "mx_gemm_kernel"
+    mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else ("fp8" if native8 else "bf16"))]
     format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt in ("w4a16", "bf16") else "fp8")]
     decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge
     if decode:
@@ -347,7 +334,6 @@ def main():
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                 "frac": round(achieved / mfma_peak, 4), "traffic": None,
                 "format_scaled_mfma": {"peak": format_peak, "frac": round(achieved / format_peak, 4)}}
-    kern = gate_up_kernel(wl)
     roof["traffic"] = profiled_traffic(wl.name, kern)
     roof["kernel"] = f"{kern} (gate_up)"
     roof["kernel_source_sha256"] = kernel_source_hash(kern)

@@ -54,9 +54,16 @@ class MoeForwardArgs(ctypes.Structure):
                 ("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
                 ("gate_up", MoePacked), ("down", MoePacked), ("out", ctypes.c_void_p),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("taps", ctypes.POINTER(MoeTaps)), ("events", ctypes.c_void_p)]
+                ("taps", ctypes.POINTER(MoeTaps)), ("events", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
+
+
+class MoePlanInfo(ctypes.Structure):
+    _fields_ = [("gate_up_kernel", ctypes.c_char_p), ("down_kernel", ctypes.c_char_p),
+                ("m_tile_rows", ctypes.c_int32), ("workspace_bytes", ctypes.c_size_t)]
+
 
 N_EVENTS = 6  # MOE_EV_BEGIN, GATE_UP, GATE_UP_END, DOWN, DOWN_END, END
+FLAG_EXACT_SUMS = 1  # MXFP8: exact bf16 expansion on the bf16 MFMA instead of the scaled FP8 MFMA
 
 
 # every symbol include/moe.h declares, with its ctypes signature
@@ -69,6 +76,7 @@ SIGNATURES = {
     "moe_forward_validate": ([ctypes.POINTER(MoeForwardArgs)], ctypes.c_int32),
     "moe_forward_workspace_bytes": ([ctypes.POINTER(MoeForwardArgs)], ctypes.c_size_t),
     "moe_forward": ([ctypes.POINTER(MoeForwardArgs), ctypes.c_void_p], ctypes.c_int32),
+    "moe_forward_plan": ([ctypes.POINTER(MoeForwardArgs), ctypes.POINTER(MoePlanInfo)], ctypes.c_int32),
 }
 
 
@@ -202,14 +210,14 @@ class Layer:
     """Arguments of one moe_forward call, with its workspace and optional taps kept alive."""
 
     def __init__(self, fmt: str, T: int, D: int, F: int, E: int, gate_up: PackedWeights, down: PackedWeights,
-                 top_k: int = 8, e_begin: int = 0, e_end: int | None = None, device="cuda"):
+                 top_k: int = 8, e_begin: int = 0, e_end: int | None = None, device="cuda", flags: int = 0):
         self.fmt, self.T, self.D, self.F, self.E, self.top_k = fmt, T, D, F, E, top_k
         self.e_begin, self.e_end = e_begin, E if e_end is None else e_end
         self.gate_up, self.down, self.device = gate_up, down, torch.device(device)
         self.args = MoeForwardArgs()
         a = self.args
         a.fmt, a.T, a.D, a.F, a.E, a.top_k = FMT[fmt], T, D, F, E, top_k
-        a.e_begin, a.e_end = self.e_begin, self.e_end
+        a.e_begin, a.e_end, a.flags = self.e_begin, self.e_end, flags
         a.gate_up, a.down = gate_up.struct(), down.struct()
         self.workspace_bytes = int(lib().moe_forward_workspace_bytes(ctypes.byref(a)))
         if T > 0 and self.workspace_bytes == 0:
@@ -268,3 +276,10 @@ class Layer:
     @property
     def taps(self) -> dict:
         return self._tap_tensors
+
+    def plan(self) -> dict:
+        """moe_forward_plan: the kernel family of each GEMM, M-tile rows, workspace bytes."""
+        info = MoePlanInfo()
+        _check(lib().moe_forward_plan(ctypes.byref(self.args), ctypes.byref(info)), "moe_forward_plan")
+        return {"gate_up_kernel": info.gate_up_kernel.decode(), "down_kernel": info.down_kernel.decode(),
+                "m_tile_rows": int(info.m_tile_rows), "workspace_bytes": int(info.workspace_bytes)}

@@ -1,39 +1,42 @@
-// gemm_mx4.hip - grouped expert GEMMs for OCP MXFP4 experts (W4A4: E2M1 codes with an
-// E8M0 scale per 32 values for both weights and activations; the AMD variant of the vLLM
-// recipe "thinkingmachines/Inkling-Small", section "Variants") on the gfx950 scaled
-// MFMA, v_mfma_scale_f32_32x32x64_f8f6f4 with FP4 operands.
+// gemm_mx.hip - grouped expert GEMMs for the OCP MX formats on the gfx950 scaled MFMA
+// v_mfma_scale_f32_32x32x64_f8f6f4: MXFP8 (E4M3 codes with an E8M0 scale per 32 values,
+// the layers 40-47 experts of the vLLM recipe "thinkingmachines/Inkling-2-Small",
+// section "Overview") and MXFP4 (E2M1 codes, same scales; the AMD variant of the vLLM
+// recipe "thinkingmachines/Inkling-Small", section "Variants"), weights and activations
+// both in the format.
 //
 // The instruction takes the codes and E8M0 scales as they are stored: no expansion, no
-// tensor scale. Lane l supplies row l % 32 of its operand over k = 32 (l / 32) .. +31 of
-// the 64-wide K chunk, as 16 code bytes (element 2i in the low nibble) and the scale
-// byte of that 32-block: in the packed MXFP4 weight layout (layout.h, halves of a 32 x 64
-// block apart) lane l's piece of a block is the l-th 16 bytes and its scale the l-th
-// byte, so a wave reads one contiguous 1 KiB and 64 bytes (the interleaved order of the
-// other formats makes every quarter-wave touch four half-used lines, and the address
-// units bound the loop); an activation's block is 16 contiguous bytes of its row. Its
-// products are exact and its fp32 accumulation measured no less accurate than a
-// sequential fp32 sum (max error 1.6e-7 of the sum of |products| over K = 4096 with
-// block exponents spread over +-12, 2.3e-8 at +-4, 0 with equal exponents).
+// tensor scale. Per 64-wide K chunk lane l supplies row (column) l % 32 with the scale
+// byte of block l / 32 of that row:
+//  - FP4: the 32 values of block l / 32 (16 code bytes, element 2i in the low nibble);
+//  - FP8: registers 0-3 take 16 values of the chunk's first 32-block and registers 4-7
+//    16 values of the second (measured on gfx950 by tests/test_gpu_fp8_mfma_accuracy.py:
+//    the scale byte of lane l applies to block l / 32 of its row, and a lane's registers
+//    0-3 belong to the first block whatever l / 32 is). Lane half g takes k = 16g .. +15
+//    and 32 + 16g .. +15, two 16-byte pieces.
+// In the packed weight layouts (layout.h) a wave's operand of one chunk is then one
+// contiguous run: MXFP4 keeps a block's two 32-column halves apart ([2][32 rows][16 B],
+// lane l the l-th 16 bytes), MXFP8 its four 16-column quarters ([4][32 rows][16 B]:
+// lane half g reads quarters g and 2 + g, each load instruction 1 KiB contiguous); the
+// scales are one 64-byte run. The products are exact; the sums are not those of a
+// sequential fp32 chain: the same test measures the FP8 sums within about 2e-6 of the
+// sum of |products| (the 16-bit route: 2e-8), an error made inside each instruction,
+// and FP4 within 1.6e-7 (0 with equal block exponents).
 //
 //  - workgroup tile 128 sorted rows x 256 weight rows, 4 waves side by side in N, each
-//    128 x 64 as 4 x 2 MFMA tiles (each weight operand feeds four MFMAs: the loop is
-//    bound by the vector-memory path, and 64-row tiles fed two); a tile runs only the
-//    32-row subtiles that hold rows (an expert's last tile, every tile at decode); gate_up
-//    waves pair gate row f with up row F + f;
-//  - the activation tile (shared by the four waves) goes through double-buffered LDS four
-//    chunks at a time, loaded as whole 128-byte pieces of the gathered token rows (a
-//    per-lane operand gather would touch 32 cache lines per load and bound the loop);
-//    each lane loads its weight operands straight from global memory into a four-chunk
-//    register ring (a 32 x 64 weight block is 1 KiB contiguous); one barrier per four
-//    chunks;
+//    128 x 64 as 4 x 2 MFMA tiles (each weight operand feeds four MFMAs); a tile runs only
+//    the 32-row subtiles that hold rows (an expert's last tile, every tile at decode);
+//    gate_up waves pair gate row f with up row F + f;
+//  - the activation tile (shared by the four waves) goes through double-buffered LDS in
+//    groups of 128 code bytes per row (four FP4 chunks, two FP8 chunks), loaded as whole
+//    128-byte pieces of the gathered token rows; each lane loads its weight operands
+//    straight from global memory into a register ring; one barrier per group;
 //  - work items are ordered expert-major and dealt to the 8 XCDs in contiguous ranges, as
 //    in the tile kernels;
 //  - gate_up epilogue: SwiGLU in fp32, then each wave's rows x 32 tile goes through LDS and
-//    lane r quantises rows r and r + 64's 32-blocks to MXFP4 (16-byte code store, one
-//    scale byte).
-// 32x32x64 operand layout (checked on gfx950 against an exact product): lane l holds row
-// (or column) l % 32, k 32 (l / 32) .. +31; accumulator v of lane l is row 8(v/4) +
-// 4(l/32) + v%4, column l%32.
+//    lane r quantises row r's 32-block to the layer's format (16- or 32-byte code store,
+//    one scale byte).
+// Accumulator v of lane l is row 8(v/4) + 4(l/32) + v%4, column l%32.
 #include "formats.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -47,31 +50,41 @@ using namespace gemm_detail;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-#ifndef MOE_MX4_BM
-#define MOE_MX4_BM 128
-#endif
-constexpr int kBM = MOE_MX4_BM, kMS = kBM / 32, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
-static_assert(kBM == 64 || kBM == 128, "64- or 128-row M-tiles");
-constexpr int kGrp = 4;                        // K chunks per A tile group
-#ifndef MOE_MX4_RING
-#define MOE_MX4_RING 4
-#endif
-constexpr int kRing = MOE_MX4_RING;            // B operand ring depth in chunks
-static_assert(kRing % kGrp == 0, "the B ring turns over whole A groups");
+constexpr int kBM = 128, kMS = kBM / 32, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
 constexpr int kARow = 144;                     // LDS bytes per A row: 128 of codes + 16 (bank spread)
 constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [kBM rows][8]
 constexpr int kABuf = kACodes + kBM * 8;
 constexpr int kEpiStride = 33;  // floats per row of a wave's SwiGLU tile (bank spread)
-constexpr int kCodeBlock = 32 * 32, kScaleBlock = 32 * 2;  // bytes per 32 x 64 weight block
 
-__device__ __forceinline__ v8i fp4_operand(u32x4 c) {
-    return (v8i){(int)c.x, (int)c.y, (int)c.z, (int)c.w, 0, 0, 0, 0};
+#ifndef MOE_MX4_RING
+#define MOE_MX4_RING 4
+#endif
+#ifndef MOE_MX8_RING
+#define MOE_MX8_RING 2  // FP8 operands are twice as wide: a deeper ring spills at two waves per SIMD
+#endif
+
+// per-format constants: code bytes per row per 64-wide chunk, chunks per A group (128
+// code bytes per row), weight ring depth in chunks, bytes of one 32 x 64 weight block
+template <bool FP8>
+struct Mx {
+    static constexpr int CB = FP8 ? 64 : 32;
+    static constexpr int kGrp = 128 / CB;
+    static constexpr int kRing = FP8 ? MOE_MX8_RING : MOE_MX4_RING;
+    static constexpr int kCodeBlock = 32 * CB, kScaleBlock = 64;
+    static constexpr int kFmt = FP8 ? 0 : 4;  // cbsz / blgp: E4M3 or E2M1 operands
+    static_assert(kRing % kGrp == 0, "the B ring turns over whole A groups");
+};
+
+__device__ __forceinline__ v8i operand(u32x4 lo, u32x4 hi) {
+    return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
 // NT: the weight code loads are marked non-temporal. At decode each (expert, weight row)
-// panel is read by a single M-tile, and a wave's load is one contiguous 1 KiB.
-template <bool GATE_UP, bool NT>
-__global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p) {
+// panel is read by a single M-tile, and a wave's load covers whole lines.
+template <bool FP8, bool GATE_UP, bool NT>
+__global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) {
+    using X = Mx<FP8>;
+    constexpr int kGrp = X::kGrp, kRing = X::kRing, kCodeBlock = X::kCodeBlock, kScaleBlock = X::kScaleBlock;
     constexpr int kLds = (GATE_UP && 4 * kBM * kEpiStride * 4 > 2 * kABuf) ? 4 * kBM * kEpiStride * 4 : 2 * kABuf;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];  // A tiles; then the SwiGLU tiles
 
@@ -94,11 +107,14 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
     const int e = p.e_begin + el;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int l32 = lane & 31, g2 = lane >> 5;
-    const int64_t kb = K / 64;  // 64-wide blocks per weight row group
-    const uint8_t *wc_e = p.w_codes + (int64_t)e * N * (K / 2);
+    const int64_t kb = K / 64;                  // 64-wide blocks per weight row group
+    const int64_t row_bytes = FP8 ? K : K / 2;  // code bytes of one activation or weight row
+    const uint8_t *wc_e = p.w_codes + (int64_t)e * N * row_bytes;
     const uint8_t *ws_e = p.w_scales + (int64_t)e * N * (K / 32);
 
-    // ---- this lane's B operand rows (weights)
+    // ---- this lane's B operand rows (weights): the first of its (one or two) 16-byte
+    // pieces of a chunk and its scale byte (MXFP4: half g2 at 512 g2, scale at 32 g2 +
+    // row; MXFP8: quarters g2 and 2 + g2 at 512 g2 and 512 g2 + 1024, scale at 2 row + g2)
     const uint8_t *bc[kNS];
     const uint8_t *bs[kNS];
 #pragma unroll
@@ -111,8 +127,8 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
             row = nb * kBN + wave * 64 + 32 * ns + l32;
         }
         const int64_t blk0 = (int64_t)(row >> 5) * kb;
-        bc[ns] = wc_e + blk0 * kCodeBlock + g2 * 512 + (row & 31) * 16;  // = base + 16 * lane
-        bs[ns] = ws_e + blk0 * kScaleBlock + g2 * 32 + (row & 31);       // = base + lane
+        bc[ns] = wc_e + blk0 * kCodeBlock + g2 * 512 + (row & 31) * 16;
+        bs[ns] = ws_e + blk0 * kScaleBlock + (FP8 ? 2 * (row & 31) + g2 : g2 * 32 + (row & 31));
     }
     const int n_chunks = K / 64;
     const int n_groups = (n_chunks + kGrp - 1) / kGrp;
@@ -126,28 +142,29 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
     // loads and multiplies the subtiles holding rows.
     auto run = [&](auto msa_c) __attribute__((always_inline)) {
         constexpr int MSA = decltype(msa_c)::value;
-        constexpr int AQ = MSA;                    // 16-byte A pieces per thread per group (32 rows each)
-        constexpr int SQ = MSA > 2 ? 2 : 1;        // A scale words per thread per group (64 rows each)
-        // ---- A tile (activations) through LDS, 4 chunks (256 k, 128 bytes of codes and 8
-        // scale bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces
-        // i = t + 256 q (row i / 8, piece i % 8: a wave covers 8 whole 128-byte rows, so
+        constexpr int AQ = MSA;                   // 16-byte A pieces per thread per group (32 rows each)
+        constexpr int SROWS = kThreads / kGrp;    // rows whose scales one pass of the threads loads
+        constexpr int SQ = (32 * MSA + SROWS - 1) / SROWS;  // A scale loads per thread per group
+        // ---- A tile (activations) through LDS, one group (128 code bytes and 2 kGrp scale
+        // bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces i = t +
+        // 256 q (row i / 8, piece i % 8: a wave covers 8 whole 128-byte pieces of rows, so
         // the gathered token rows are read line by line) and the two scale bytes of rows
-        // t / 4 + 64 q, chunk t % 4. Rows past the tile's end read the tile's first row
-        // (in bounds; never stored); pieces and chunks past the end of K reread the
+        // t / kGrp + SROWS q, chunk t % kGrp. Rows past the tile's end read the tile's first
+        // row (in bounds; never stored); pieces and chunks past the end of K reread the
         // group's first (unused).
-        const int piece = threadIdx.x & 7, s_chunk = threadIdx.x & 3;
+        const int piece = threadIdx.x & 7, s_chunk = threadIdx.x % kGrp;
         const uint8_t *ap[AQ];
 #pragma unroll
-        for (int q = 0; q < AQ; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * (K / 2);
+        for (int q = 0; q < AQ; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * row_bytes;
         const uint8_t *sp[SQ];
 #pragma unroll
-        for (int q = 0; q < SQ; ++q) sp[q] = p.a_scales + a_row(64 * q + (threadIdx.x >> 2)) * (K / 32);
+        for (int q = 0; q < SQ; ++q) sp[q] = p.a_scales + a_row(SROWS * q + threadIdx.x / kGrp) * (K / 32);
         u32x4 a_pf[AQ];
         uint32_t s_pf[SQ];
         auto a_load = [&](int g) {
             g = min(g, n_groups - 1);
             const int off = 128 * g + 16 * piece;
-            const int off_ok = off < K / 2 ? off : 128 * g;
+            const int off_ok = off < row_bytes ? off : 128 * g;
 #pragma unroll
             for (int q = 0; q < AQ; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
 #pragma unroll
@@ -160,23 +177,28 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
             for (int q = 0; q < AQ; ++q)
                 *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
 #pragma unroll
-            for (int q = 0; q < SQ; ++q)
-                *reinterpret_cast<uint16_t *>(ab + kACodes + (64 * q + (threadIdx.x >> 2)) * 8 + 2 * s_chunk) =
-                    (uint16_t)s_pf[q];
+            for (int q = 0; q < SQ; ++q) {
+                const int r = SROWS * q + threadIdx.x / kGrp;
+                if (SROWS * (q + 1) <= kBM || r < kBM)
+                    *reinterpret_cast<uint16_t *>(ab + kACodes + r * 8 + 2 * s_chunk) = (uint16_t)s_pf[q];
+            }
         };
 
         // ---- B operand ring: chunk c + kRing - 1 is loaded into slot (c - 1) % kRing while
         // chunk c is multiplied; loads past the end repeat the last chunk (in bounds, unused)
-        u32x4 breg[kRing][kNS];
+        u32x4 breg[kRing][kNS][FP8 ? 2 : 1];
         int bsc[kRing][kNS];
         auto b_load = [&](int slot, int c) {
 #pragma unroll
             for (int ns = 0; ns < kNS; ++ns) {
-                const u32x4 *src = reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c);
-                if constexpr (NT)
-                    breg[slot][ns] = __builtin_nontemporal_load(src);
-                else
-                    breg[slot][ns] = *src;
+#pragma unroll
+                for (int h = 0; h < (FP8 ? 2 : 1); ++h) {
+                    const u32x4 *src = reinterpret_cast<const u32x4 *>(bc[ns] + (int64_t)kCodeBlock * c + 1024 * h);
+                    if constexpr (NT)
+                        breg[slot][ns][h] = __builtin_nontemporal_load(src);
+                    else
+                        breg[slot][ns][h] = *src;
+                }
                 bsc[slot][ns] = bs[ns][(int64_t)kScaleBlock * c];
             }
         };
@@ -198,17 +220,30 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
         // chunk j of the group in LDS buffer buf times the B operands in ring slot `slot`
         auto mma = [&](int buf, int j, int slot) {
             const uint8_t *ab = lds + buf * kABuf;
-            u32x4 af[MSA];
-#pragma unroll
-            for (int ms = 0; ms < MSA; ++ms)
-                af[ms] = *reinterpret_cast<const u32x4 *>(ab + (32 * ms + l32) * kARow + 32 * j + 16 * g2);
+            v8i af[MSA];
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms) {
+                const uint8_t *ar = ab + (32 * ms + l32) * kARow + X::CB * j + 16 * g2;
+                const u32x4 lo = *reinterpret_cast<const u32x4 *>(ar);
+                if constexpr (FP8)
+                    af[ms] = operand(lo, *reinterpret_cast<const u32x4 *>(ar + 32));
+                else
+                    af[ms] = operand(lo, (u32x4){});
+            }
+#pragma unroll
+            for (int ms = 0; ms < MSA; ++ms) {
+                // scale byte of chunk j, block g2: byte 2 j + g2 of the row's scales
                 const int sa = (int)((a_sc[ms][j >> 1] >> (16 * (j & 1))) & 0xffu);
 #pragma unroll
-                for (int ns = 0; ns < kNS; ++ns)
+                for (int ns = 0; ns < kNS; ++ns) {
+                    v8i bf;
+                    if constexpr (FP8)
+                        bf = operand(breg[slot][ns][0], breg[slot][ns][FP8 ? 1 : 0]);
+                    else
+                        bf = operand(breg[slot][ns][0], (u32x4){});
                     acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        fp4_operand(af[ms]), fp4_operand(breg[slot][ns]), acc[ms][ns], 4, 4, 0, sa, 0, bsc[slot][ns]);
+                        af[ms], bf, acc[ms][ns], X::kFmt, X::kFmt, 0, sa, 0, bsc[slot][ns]);
+                }
             }
         };
         // after the last chunk of group g: group g + 1 into the other buffer (last read in
@@ -278,10 +313,20 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
                     float x[32];
 #pragma unroll
                     for (int i = 0; i < 32; ++i) x[i] = we[m * kEpiStride + i];
-                    uint32_t cw[4];
-                    const int sc = mxfp4_quant_block(x, cw);
-                    *reinterpret_cast<u32x4 *>(p.o_codes + row * (F / 2) + fb / 2) = (u32x4){cw[0], cw[1], cw[2], cw[3]};
-                    p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                    if constexpr (FP8) {
+                        uint32_t cw[8];
+                        const int sc = mxfp8_quant_block(x, cw);
+                        u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + fb);
+                        dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                        dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
+                        p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                    } else {
+                        uint32_t cw[4];
+                        const int sc = mxfp4_quant_block(x, cw);
+                        *reinterpret_cast<u32x4 *>(p.o_codes + row * (F / 2) + fb / 2) =
+                            (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                        p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                    }
                     if (p.o_tap) {
                         float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
 #pragma unroll
@@ -305,35 +350,40 @@ __global__ void __launch_bounds__(kThreads, 2) mx4_gemm_kernel(const GemmArgs p)
     };
     if (rows <= 32)
         run(std::integral_constant<int, 1>{});
-    else if (kMS == 4 && rows <= 64)
+    else if (rows <= 64)
         run(std::integral_constant<int, 2>{});
     else
         run(std::integral_constant<int, kMS>{});
 }
 
+template <bool FP8, bool GATE_UP>
+void launch_t(const GemmArgs &a, bool stream_once, dim3 grid, hipStream_t s) {
+    if (stream_once)
+        hipLaunchKernelGGL((mx_gemm_kernel<FP8, GATE_UP, true>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((mx_gemm_kernel<FP8, GATE_UP, false>), grid, dim3(kThreads), 0, s, a);
+}
+
 }  // namespace
 
-int32_t mx4_gemm_bm() { return kBM; }
+int32_t mx_gemm_bm() { return kBM; }
 
-bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up) {
+bool mx_gemm_supported(int32_t K, int32_t N, bool gate_up) {
     if (K <= 0 || N <= 0 || K % 64) return false;
     return gate_up ? (N % 2 == 0 && (N / 2) % (kBN / 2) == 0) : N % kBN == 0;
 }
 
-hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, bool stream_once, int32_t max_tiles, hipStream_t s) {
+hipError_t launch_mx_gemm(const GemmArgs &a, bool fp8, bool gate_up, bool stream_once, int32_t max_tiles,
+                          hipStream_t s) {
     const int64_t nb = gate_up ? (a.N / 2) / (kBN / 2) : a.N / kBN;
     const int64_t items = (int64_t)max_tiles * nb;
-    const dim3 grid((unsigned)((items + 7) / 8 * 8)), block(kThreads);
-    if (gate_up) {
-        if (stream_once)
-            hipLaunchKernelGGL((mx4_gemm_kernel<true, true>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((mx4_gemm_kernel<true, false>), grid, block, 0, s, a);
+    const dim3 grid((unsigned)((items + 7) / 8 * 8));
+    if (fp8) {
+        if (gate_up) launch_t<true, true>(a, stream_once, grid, s);
+        else launch_t<true, false>(a, stream_once, grid, s);
     } else {
-        if (stream_once)
-            hipLaunchKernelGGL((mx4_gemm_kernel<false, true>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((mx4_gemm_kernel<false, false>), grid, block, 0, s, a);
+        if (gate_up) launch_t<false, true>(a, stream_once, grid, s);
+        else launch_t<false, false>(a, stream_once, grid, s);
     }
     return hipGetLastError();
 }

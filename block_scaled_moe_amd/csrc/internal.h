@@ -128,12 +128,16 @@ hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
 hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s);
 
-// native MXFP4 GEMMs on the gfx950 scaled FP4 MFMA (gemm_mx4.hip): 128-row M-tiles
-// (mx4_gemm_bm), 256 weight rows per workgroup; K % 64, gate_up F % 128, down N % 256
-bool mx4_gemm_supported(int32_t K, int32_t N, bool gate_up);
-int32_t mx4_gemm_bm();
-// stream_once: decode batches, where each weight panel is read by one M-tile (non-temporal loads)
-hipError_t launch_mx4_gemm(const GemmArgs &a, bool gate_up, bool stream_once, int32_t max_tiles, hipStream_t s);
+// MXFP4 and MXFP8 GEMMs on the gfx950 scaled MFMA with the codes and E8M0 scales as
+// stored (gemm_mx.hip): 128-row M-tiles (mx_gemm_bm), 256 weight rows per workgroup;
+// K % 64, gate_up F % 128, down N % 256. A operand: a_codes / a_scales; gate_up writes
+// o_codes / o_scales (and o_tap).
+bool mx_gemm_supported(int32_t K, int32_t N, bool gate_up);
+int32_t mx_gemm_bm();
+// fp8: MXFP8 (else MXFP4); stream_once: decode batches, where each weight panel is read
+// by one M-tile (non-temporal weight loads)
+hipError_t launch_mx_gemm(const GemmArgs &a, bool fp8, bool gate_up, bool stream_once, int32_t max_tiles,
+                          hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int32_t T, int32_t D, int32_t k, const int32_t *slot_pos, const float *w,

@@ -24,9 +24,16 @@ int32_t to_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 // Rows per expert above which the grouped GEMMs use the 128-row tile.
 constexpr int32_t kPrefillRowsPerExpert = 48;
 
+// MXFP8 decode batches on the scaled FP8 MFMA kernel (1) or on the streaming kernel with
+// the exact bf16 expansion (0)
+#ifndef MOE_MX8_DECODE_NATIVE
+#define MOE_MX8_DECODE_NATIVE 1
+#endif
+
 struct Plan {
     GemmShape shape;
-    bool tiled;  // prefill on the MFMA tile kernels (64- or 128-row M-tiles)
+    bool scaled;  // MXFP4 / MXFP8 on the scaled MFMA with the codes as stored (gemm_mx.hip)
+    bool tiled;   // prefill on the MFMA tile kernels (64- or 128-row M-tiles), or scaled
     int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
     size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
     size_t a_codes, a_scales, a_tscale, a16;
@@ -48,10 +55,14 @@ Plan make_plan(const moe_forward_args *a) {
     const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
-    // MXFP4 always runs the scaled-FP4 MFMA kernels
-    p.tiled = mx4 || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
-                      tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
-    p.bm = mx4 ? mx4_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
+    // MXFP4 always runs the scaled-FP4 MFMA kernels; MXFP8 the scaled-FP8 ones unless the
+    // caller asks for exact sums or the shape does not fit them
+    const bool mx_fit = mx_gemm_supported(a->D, 2 * a->F, true) && mx_gemm_supported(a->F, a->D, false);
+    p.scaled = mx4 || (a->fmt == MOE_FMT_MXFP8 && !(a->flags & MOE_FLAG_EXACT_SUMS) && mx_fit &&
+                       (p.shape == GemmShape::Prefill || MOE_MX8_DECODE_NATIVE));
+    p.tiled = p.scaled || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
+                           tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
+    p.bm = p.scaled ? mx_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
@@ -75,24 +86,45 @@ Plan make_plan(const moe_forward_args *a) {
     p.a_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? T * D : T * D / 2);
     p.a_scales = a16 ? 0 : take(nv ? T * D / 16 : T * D / 32);
     p.a_tscale = take(sizeof(float));
-    p.a16 = (mx4 || a16) ? 0 : take(2 * T * D);  // exact 16-bit values of the hidden-state codes
+    p.a16 = (p.scaled || a16) ? 0 : take(2 * T * D);  // exact 16-bit values of the hidden-state codes
     p.inter32 = nv ? take(sizeof(float) * TK * F) : 0;
     p.i_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? TK * F : TK * F / 2);
     p.i_scales = a16 ? 0 : take(nv ? TK * F / 16 : TK * F / 32);
     p.i_tscale = take(sizeof(float));
-    p.i16 = mx4 ? 0 : take(2 * TK * F);  // exact 16-bit values of the intermediate (codes)
+    p.i16 = p.scaled ? 0 : take(2 * TK * F);  // exact 16-bit values of the intermediate (codes)
     p.y = take(sizeof(float) * TK * D);
     p.total = off;
     return p;
 }
 
+// The kernel family each GEMM of a plan runs (what run_gemm launches).
+enum class Kernel { Scaled, Tile, Stream, Grouped };
+
+Kernel gemm_kernel(const Plan &P, int32_t K, int32_t N, bool gate_up) {
+    if (P.scaled) return Kernel::Scaled;
+    if (P.tiled) return Kernel::Tile;
+    if (P.shape == GemmShape::Decode && stream_gemm_supported(K, N, gate_up)) return Kernel::Stream;
+    return Kernel::Grouped;
+}
+
+const char *kernel_name(Kernel k) {
+    switch (k) {
+        case Kernel::Scaled: return "mx_gemm_kernel";
+        case Kernel::Tile: return "tile_gemm_kernel";
+        case Kernel::Stream: return "stream_gemm_kernel";
+        default: return "grouped_gemm_kernel";
+    }
+}
+
 hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
-    if (fmt == MOE_FMT_MXFP4) return launch_mx4_gemm(g, gate_up, P.shape == GemmShape::Decode, P.max_tiles, s);
     const int fm = gemm_fm(fmt);
-    if (P.tiled) return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
-    if (P.shape == GemmShape::Decode && stream_gemm_supported(g.K, g.N, gate_up))
-        return launch_stream_gemm(g, fm, gate_up, P.max_tiles, s);
-    return launch_grouped_gemm(g, fm, gate_up, P.shape, P.max_tiles, s);
+    switch (gemm_kernel(P, g.K, g.N, gate_up)) {
+        case Kernel::Scaled:
+            return launch_mx_gemm(g, fmt == MOE_FMT_MXFP8, gate_up, P.shape == GemmShape::Decode, P.max_tiles, s);
+        case Kernel::Tile: return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
+        case Kernel::Stream: return launch_stream_gemm(g, fm, gate_up, P.max_tiles, s);
+        default: return launch_grouped_gemm(g, fm, gate_up, P.shape, P.max_tiles, s);
+    }
 }
 
 int32_t check_packed(const moe_packed &w, int32_t fmt, int32_t E, int32_t N, int32_t K) {
@@ -184,8 +216,9 @@ int32_t validate_shape(const moe_forward_args *a) {
     if (a->e_begin < 0 || a->e_end <= a->e_begin || a->e_end > a->E) return MOE_ERR_INVALID_ARG;
     if ((int64_t)a->T * a->top_k > INT32_MAX / 2) return MOE_ERR_INVALID_ARG;
     if (a->D % 128 || a->F % 128) return MOE_ERR_UNSUPPORTED;
+    if (a->flags & ~(uint32_t)MOE_FLAG_EXACT_SUMS) return MOE_ERR_INVALID_ARG;
     if (a->fmt == MOE_FMT_MXFP4 &&
-        !(mx4_gemm_supported(a->D, 2 * a->F, true) && mx4_gemm_supported(a->F, a->D, false)))
+        !(mx_gemm_supported(a->D, 2 * a->F, true) && mx_gemm_supported(a->F, a->D, false)))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -215,6 +248,23 @@ size_t moe_forward_workspace_bytes(const moe_forward_args *a) {
     if (validate_shape(a) != MOE_OK) return 0;
     if (a->T == 0) return 0;
     return make_plan(a).total;
+}
+
+int32_t moe_forward_plan(const moe_forward_args *a, moe_plan_info *info) {
+    if (!info) return MOE_ERR_INVALID_ARG;
+    const int32_t rc = validate_shape(a);
+    if (rc != MOE_OK) return rc;
+    memset(info, 0, sizeof(*info));
+    if (a->T == 0) {
+        info->gate_up_kernel = info->down_kernel = "none";
+        return MOE_OK;
+    }
+    const Plan P = make_plan(a);
+    info->gate_up_kernel = kernel_name(gemm_kernel(P, a->D, 2 * a->F, true));
+    info->down_kernel = kernel_name(gemm_kernel(P, a->F, a->D, false));
+    info->m_tile_rows = P.bm;
+    info->workspace_bytes = P.total;
+    return MOE_OK;
 }
 
 int32_t moe_forward(const moe_forward_args *a, void *stream) {
@@ -276,8 +326,9 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     } else if (a16) {
         // W4A16 and bf16 experts: the GEMM reads the bf16 hidden states directly
     } else {
+        // MXFP8: the scaled MFMA reads the codes; the exact route their bf16 values
         MOE_TRY(launch_quant_act_mxfp8(a->h, T, D, U8(P.a_codes), U8(P.a_scales),
-                                       reinterpret_cast<uint16_t *>(ws + P.a16), s));
+                                       P.scaled ? nullptr : reinterpret_cast<uint16_t *>(ws + P.a16), s));
     }
 
     // 3. gate_up GEMM + SwiGLU (+ MXFP8 intermediate quantisation)
@@ -295,7 +346,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     g.w_codes = a->gate_up.codes;
     g.w_scales = a->gate_up.scales;
     g.w_tscale = a->gate_up.tensor_scale;
-    g.a_vals = mx4 ? nullptr : (a16 ? static_cast<const void *>(a->h) : ws + P.a16);
+    g.a_vals = P.scaled ? nullptr : (a16 ? static_cast<const void *>(a->h) : ws + P.a16);
     g.a_codes = a16 ? nullptr : U8(P.a_codes);
     g.a_scales = a16 ? nullptr : U8(P.a_scales);
     if (nv) {
@@ -310,7 +361,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
                                          F32(P.i_tscale), s));
     } else {
         g.o_codes = a16 ? nullptr : U8(P.i_codes);
-        g.o_vals = mx4 ? nullptr : ws + P.i16;
+        g.o_vals = P.scaled ? nullptr : ws + P.i16;
         g.o_scales = a16 ? nullptr : U8(P.i_scales);
         g.o_tap = a->taps ? a->taps->inter : nullptr;
         MOE_TRY(mark(MOE_EV_GATE_UP));
@@ -332,7 +383,7 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
     d.o_scales = nullptr;
     d.o_tap = nullptr;
     d.o_vals = nullptr;
-    d.a_vals = mx4 ? nullptr : ws + P.i16;
+    d.a_vals = P.scaled ? nullptr : ws + P.i16;
     d.a_codes = a16 ? nullptr : U8(P.i_codes);
     d.a_scales = a16 ? nullptr : U8(P.i_scales);
     d.a_tscale = nv ? F32(P.i_tscale) : nullptr;

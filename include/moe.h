@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -115,6 +115,15 @@ typedef struct moe_taps {
     float *y;              /* [T*top_k][D] fp32 down projection per slot (unweighted) */
 } moe_taps;
 
+/* moe_forward flags.
+ * MOE_FLAG_EXACT_SUMS - MXFP8 layers: run the expert GEMMs on the codes expanded exactly
+ *   to bf16 (the bf16 MFMA, fp32 sums with sequential-chain accuracy, about 2e-8 of the
+ *   sum of |products| over K = 4096) instead of the gfx950 scaled FP8 MFMA on the codes
+ *   and E8M0 scales as stored (twice the multiply rate; its sums are within about 2e-6 of
+ *   the sum of |products|, so intermediate codes on a rounding boundary take the
+ *   neighbouring code about 100 times as often). Other formats ignore it. */
+#define MOE_FLAG_EXACT_SUMS 1u
+
 /* Stage boundaries at which moe_forward records caller-created events (timing). */
 #define MOE_EV_BEGIN 0        /* before the first kernel of the call          */
 #define MOE_EV_GATE_UP 1      /* just before the gate_up GEMM                 */
@@ -142,7 +151,19 @@ typedef struct moe_forward_args {
     const moe_taps *taps;     /* host pointer to a moe_taps, or NULL                    */
     void *const *events;      /* NULL, or a host array of MOE_N_EVENTS hipEvent_t that are
                                  recorded on the stream at the MOE_EV_* boundaries      */
+    uint32_t flags;           /* MOE_FLAG_* (0: the default routes)                     */
 } moe_forward_args;
+
+/* What moe_forward runs for given arguments (host only, from the size fields, fmt and
+ * flags): the kernel family of each GEMM ("mx_gemm_kernel", "tile_gemm_kernel",
+ * "stream_gemm_kernel", "grouped_gemm_kernel"; static strings), rows per M-tile and the
+ * workspace size. */
+typedef struct moe_plan_info {
+    const char *gate_up_kernel;
+    const char *down_kernel;
+    int32_t m_tile_rows;
+    size_t workspace_bytes;
+} moe_plan_info;
 
 /* ABI version (MOE_ABI_VERSION) and a static description of a status code. */
 int32_t moe_abi_version(void);
@@ -189,8 +210,12 @@ int32_t moe_route(int32_t T, int32_t D, int32_t E, int32_t top_k, const uint16_t
 int32_t moe_forward_validate(const moe_forward_args *a);
 
 /* Bytes of device workspace moe_forward needs; depends on the size fields only (fmt, T, D,
- * F, E, top_k, e_begin, e_end) and is 0 if those are invalid or T = 0. */
+ * F, E, top_k, e_begin, e_end) and flags, and is 0 if those are invalid or T = 0. */
 size_t moe_forward_workspace_bytes(const moe_forward_args *a);
+
+/* Fills *info for these arguments (the size fields, fmt and flags; pointers unused).
+ * Returns MOE_OK or the status moe_forward would return for them. Host only. */
+int32_t moe_forward_plan(const moe_forward_args *a, moe_plan_info *info);
 
 /*
  * MoE layer forward over the local experts [e_begin, e_end):

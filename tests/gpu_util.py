@@ -70,7 +70,8 @@ def check_intermediate_codes(fmt: str, inter: np.ndarray, codes: np.ndarray, sca
 
 def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w: np.ndarray, gpu_inter_codes,
                   gpu_inter_scales, gpu_inter_tscale, oracle_inter_codes, oracle_inter_scales, sorted_slot,
-                  down: dict, *, D: int, F: int, E: int, e_begin: int, e_end: int, rows=None):
+                  down: dict, *, D: int, F: int, E: int, e_begin: int, e_end: int, rows=None,
+                  min_clean_frac: float = 0.5, max_flip_frac: float = 1e-3, max_rel_rms: float = 2e-3):
     """Output parity with intermediate-code flips accounted for.
 
     The intermediate codes are a rounding of fp32 sums; the GPU sums in a different order
@@ -80,13 +81,15 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
         codes match the GPU output on every token, to 2e-3 x RMS;
      2. independent: tokens none of whose slots holds a flipped intermediate row match
         the fully independent oracle output, to 2e-3 x RMS;
-     3. flips stay rare (< 1e-3 of the intermediate elements); for the 4- and 8-bit code
-        formats at least half of the compared tokens have no flipped row (so check 2
-        covers most of the batch). A bf16 intermediate (W4A16, bf16 experts) flips by one
-        bf16 ulp (2^-8 relative) wherever the two sums straddle a rounding boundary,
-        which reaches most tokens of a batch: check 4 is the one that bounds it;
+     3. flips stay rare (< max_flip_frac of the intermediate elements); for the 4- and 8-bit code
+        formats at least min_clean_frac of the compared tokens have no flipped row (so
+        check 2 covers most of the batch). A bf16 intermediate (W4A16, bf16 experts) flips
+        by one bf16 ulp (2^-8 relative) wherever the two sums straddle a rounding
+        boundary, which reaches most tokens of a batch, and so do the MXFP8 sums of the
+        scaled FP8 MFMA (callers pass min_clean_frac 0): check 4 is the one that bounds
+        them;
      4. over all tokens, flipped ones included, the RMS of the difference from the fully
-        independent output stays within 2e-3 x RMS.
+        independent output stays within max_rel_rms x RMS.
     rows: optional token subset to compare (the others are not computed by the oracle).
     Returns (stage error / RMS, independent error / RMS, flips, tokens excluded)."""
     k = idx.shape[1]
@@ -105,16 +108,16 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
           else gpu_inter_scales.reshape(S, -1) != oracle_inter_scales.reshape(S, -1))
     flipped_rows = np.nonzero(cb.any(1) | sb.any(1))[0]
     flips = int(cb.sum())  # differing code bytes (one byte holds two E2M1 codes in the 4-bit formats)
-    assert flips <= 1e-3 * S * F, f"{flips} intermediate code flips in {S * F} elements"
+    assert flips <= max_flip_frac * S * F, f"{flips} intermediate code flips in {S * F} elements"
     bad_tokens = set((sorted_slot[flipped_rows] // k).tolist())
     keep = np.array([t for t in sel if t not in bad_tokens], dtype=np.int64)
     if fmt not in ("w4a16", "bf16"):
-        assert 2 * len(keep) >= len(sel), f"{len(sel) - len(keep)} of {len(sel)} tokens reach a flipped row"
+        assert len(keep) >= min_clean_frac * len(sel), f"{len(sel) - len(keep)} of {len(sel)} tokens reach a flipped row"
     r_ref = rms(ref[sel])
     e_ind = float(np.abs(out[keep] - ref[keep]).max()) / r_ref if len(keep) else 0.0
     assert e_ind <= 2e-3, f"independent output error {e_ind:.2e} x RMS on tokens without flips"
     rel_rms = rms(out[sel] - ref[sel]) / r_ref
-    assert rel_rms <= 2e-3, f"independent output RMS error {rel_rms:.2e} x RMS"
+    assert rel_rms <= max_rel_rms, f"independent output RMS error {rel_rms:.2e} x RMS"
     return e_stage, e_ind, flips, len(sel) - len(keep)
 
 
@@ -139,3 +142,39 @@ def device_weights(wl: synth.Workload, device="cuda"):
     torch.cuda.synchronize()
     del buf
     return gu, dn
+
+
+# Bound on the SwiGLU intermediate's difference from the oracle's fp64 sums, relative to
+# its largest value: fp32 sums of exact products (every route but one) stay near 1e-7;
+# the scaled FP8 MFMA's sums are within about 2e-6 of the sum of |products|
+# (tests/test_gpu_fp8_mfma_accuracy.py), which is 1e-5 to 3e-5 of the intermediate's
+# maximum at K = 256 to 4096.
+INTER_TOL_EXACT = 1e-5
+INTER_TOL_SCALED_FP8 = 1e-4
+# Bound on intermediate code flips per element. fp32 sums of exact products flip about
+# 1e-6 to 1e-5 of the elements (a sum within an ulp of a rounding boundary). The scaled
+# FP8 MFMA's error per 64-wide chunk is about 2e-6 of the chunk's sum of |products| and
+# averages over chunks only as 1 / sqrt(chunks), so at K = 256 (4 chunks) an element's
+# error is about 1e-6 of the sum of |products| and 1e-3 to 1.5e-3 of the elements flip
+# (5e-4 at K = 4096).
+FLIP_FRAC_EXACT = 1e-3
+FLIP_FRAC_SCALED_FP8 = 5e-3
+# Bound on the RMS of the output's difference from the fully independent oracle output,
+# relative to its RMS. A flip moves one intermediate element by one code step (1/16 to
+# 1/8 of its value), so the RMS difference grows as about 0.1 x sqrt(flip fraction):
+# 3.4e-3 at the 1.4e-3 flips of K = 256 on the scaled FP8 MFMA; the exact routes stay
+# below 2e-4.
+REL_RMS_EXACT = 2e-3
+REL_RMS_SCALED_FP8 = 1e-2
+
+
+def scaled_fp8(layer) -> bool:
+    """The layer's GEMMs run MXFP8 on the scaled FP8 MFMA (moe_forward's own plan)."""
+    return layer.fmt == "mxfp8" and layer.plan()["gate_up_kernel"] == "mx_gemm_kernel"
+
+
+def output_bounds(native8: bool) -> dict:
+    """check_outputs bounds for a layer on the scaled FP8 MFMA or on an exact-sum route."""
+    if native8:
+        return dict(min_clean_frac=0.0, max_flip_frac=FLIP_FRAC_SCALED_FP8, max_rel_rms=REL_RMS_SCALED_FP8)
+    return dict(min_clean_frac=0.5, max_flip_frac=FLIP_FRAC_EXACT, max_rel_rms=REL_RMS_EXACT)

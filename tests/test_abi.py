@@ -25,11 +25,11 @@ def declared_functions():
 def test_header_functions_are_exported_and_bound():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 8, names
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 6
+    assert lib.moe_abi_version() == 7
     assert lib.moe_status_string(EWS) == b"workspace missing or too small"
 
 
@@ -151,3 +151,40 @@ def test_route_and_quantize_validate_on_the_host():
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EINVAL
     bad = moe.MoePacked(2, 2, 32, 64, A16 + 8, A16, 0)  # misaligned codes
     assert lib.moe_quantize_weights(p(A16), ctypes.byref(bad), None) == EALIGN
+
+
+def _plan(a):
+    info = moe.MoePlanInfo()
+    rc = moe.lib().moe_forward_plan(ctypes.byref(a), ctypes.byref(info))
+    return rc, info
+
+
+def _mx8(**over):
+    a = _args(fmt=2, **over)
+    a.gate_up = moe.MoePacked(2, 384, 5120, 4096, A16, A16, 0)
+    a.down = moe.MoePacked(2, 384, 4096, 2560, A16, A16, 0)
+    return a
+
+
+def test_forward_plan_names_the_kernels():
+    """moe_forward_plan reports the dispatch of moe_forward (the same host plan)."""
+    rc, info = _plan(_args())                                   # NVFP4 decode: streaming kernels
+    assert rc == OK and info.gate_up_kernel == b"stream_gemm_kernel" and info.down_kernel == b"stream_gemm_kernel"
+    rc, info = _plan(_args(T=8192, e_end=96))                   # NVFP4 EP4 prefill: MFMA tiles
+    assert rc == OK and info.gate_up_kernel == b"tile_gemm_kernel" and info.m_tile_rows == 64
+    assert info.workspace_bytes == moe.lib().moe_forward_workspace_bytes(ctypes.byref(_args(T=8192, e_end=96)))
+    rc, info = _plan(_mx8(T=16384))                             # MXFP8 prefill: scaled FP8 MFMA
+    assert rc == OK and info.gate_up_kernel == b"mx_gemm_kernel" and info.m_tile_rows == 128
+    rc, info = _plan(_mx8(T=16384, flags=1))                    # exact sums: the bf16 expansion
+    assert rc == OK and info.gate_up_kernel == b"tile_gemm_kernel"
+    rc, info = _plan(_mx8(T=256, flags=1))
+    assert rc == OK and info.gate_up_kernel == b"stream_gemm_kernel"
+    # the exact route keeps 16-bit operand copies, the scaled route needs none
+    ws = moe.lib().moe_forward_workspace_bytes
+    assert ws(ctypes.byref(_mx8(T=16384, flags=1))) > ws(ctypes.byref(_mx8(T=16384)))
+    rc, info = _plan(_mx8(T=256, D=384))                        # no 256-wide down blocks: bf16 route
+    assert rc == OK and info.gate_up_kernel != b"mx_gemm_kernel"
+    assert _plan(_args(flags=2))[0] == EINVAL                   # unknown flag
+    assert _validate(_args(flags=2)) == EINVAL
+    rc, info = _plan(_args(T=0))
+    assert rc == OK and info.gate_up_kernel == b"none"

@@ -8,7 +8,8 @@ intermediate, and the packed weight bytes of every expert the batch touches.
 Expert arithmetic, every slot of every touched local expert, one expert at a time with
 fp64 BLAS on the oracle's dequantised operands (its quantised weights, the verified
 hidden-state codes):
- - the fp32 SwiGLU intermediate within 1e-5 of the expert's largest value;
+ - the fp32 SwiGLU intermediate within 1e-5 of the expert's largest value (1e-4 on the
+   scaled FP8 MFMA);
  - the per-slot down projection y stage-wise (from the GPU's intermediate codes) within
    2e-3 x the RMS of the expert's y;
  - the layer output stage-wise (that down projection combined in fp64) within 2e-3 x RMS
@@ -18,7 +19,8 @@ hidden-state codes):
    whose codes differ from the GPU's ("flips": the GPU's fp32 sums and the oracle's fp64
    sums round to neighbouring codes) are counted and reported with the error of the
    tokens they reach; tokens without a flipped row must match within 2e-3 x RMS, and the
-   relative RMS error over all tokens must stay within 2e-3.
+   relative RMS error over all tokens must stay within 2e-3 (1e-2 for MXFP8 on the
+   scaled FP8 MFMA, whose sums flip about 100 times as many codes; tests/gpu_util.py).
 The decode NVFP4 and MXFP8 workloads are also run through the oracle's own forward (its
 routing, permutation, quantisers and fp64 experts) on the experts the batch touches, and
 compared with the GPU output stage-wise and independently.
@@ -32,7 +34,8 @@ import torch
 import block_scaled_moe_amd as moe
 import oracle
 import synth
-from gpu_util import check_intermediate_codes, check_outputs, device_weights, host, report, rms, to_dev, untile
+from gpu_util import (INTER_TOL_EXACT, INTER_TOL_SCALED_FP8, check_intermediate_codes, check_outputs, device_weights,
+                      host, output_bounds, report, rms, scaled_fp8, to_dev, untile)
 
 pytestmark = pytest.mark.gpu
 
@@ -96,9 +99,15 @@ def _combine(T, D, k, ss, w, y):
     return out
 
 
+# (workload, moe_forward flags): the ten workloads on their default routes, and the
+# skewed MXFP8 workload once more with exact sums (the bf16 expansion) for comparison
+CASES = [(i, 0) for i in range(1, 11)] + [(4, moe.FLAG_EXACT_SUMS)]
+
+
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("i", [1, 2, 3, 4, 5, 6, 7, 8, 9, 10], ids=lambda i: synth.WORKLOADS[i].name)
-def test_fullsize_workload(i):
+@pytest.mark.parametrize("i,flags", CASES,
+                         ids=[synth.WORKLOADS[i].name + ("-exact" if f else "") for i, f in CASES])
+def test_fullsize_workload(i, flags):
     t_start = time.perf_counter()
     wl = synth.WORKLOADS[i]
     fmt, T, D, F, E, k = wl.fmt, wl.T, wl.D, wl.F, wl.E, wl.k
@@ -121,7 +130,10 @@ def test_fullsize_workload(i):
         assert host(amax)[0] == np.abs(synth.bf16_to_f32(h)).max()
 
     # ---- forward with taps (the bench's layer)
-    layer = moe.Layer(fmt, T, D, F, E, gu, dn, top_k=k, e_begin=eb, e_end=ee)
+    layer = moe.Layer(fmt, T, D, F, E, gu, dn, top_k=k, e_begin=eb, e_end=ee, flags=flags)
+    native8 = scaled_fp8(layer)
+    inter_tol = INTER_TOL_SCALED_FP8 if native8 else INTER_TOL_EXACT
+    report("  plan", **layer.plan())
     layer.enable_taps()
     out = host(layer.forward(d_h, idx, w, h_amax=amax))
     torch.cuda.synchronize()
@@ -162,7 +174,7 @@ def test_fullsize_workload(i):
     y_stage = np.empty((S, D), np.float32)
     down_of = {}        # expert -> the oracle's down weights (for the independent pass)
     experts = {}        # expert -> (gate_up, down) of the oracle, decode workloads 1 and 2
-    keep_gate_up = i in (1, 2)
+    keep_gate_up = i in (1, 2) and not flags
     worst_inter = worst_y = 0.0
     live = np.nonzero(counts)[0]
     for n_done, el in enumerate(live):
@@ -202,7 +214,7 @@ def test_fullsize_workload(i):
         e_inter = float(np.abs(g_inter[p0:p1] - inter_ref[p0:p1]).max()) / max(scale_i, 1e-30)
         e_y = float(np.abs(g_y[p0:p1] - y).max()) / max(rms(y), 1e-30)
         worst_inter, worst_y = max(worst_inter, e_inter), max(worst_y, e_y)
-        assert e_inter < 1e-5, f"expert {e}: SwiGLU intermediate differs by {e_inter:.2e} of its max"
+        assert e_inter < inter_tol, f"expert {e}: SwiGLU intermediate differs by {e_inter:.2e} of its max"
         assert e_y <= 2e-3, f"expert {e}: down projection differs by {e_y:.2e} x RMS"
         if (n_done + 1) % 32 == 0:
             report("  progress", experts=f"{n_done + 1}/{len(live)}", s=f"{time.perf_counter() - t_start:.0f}")
@@ -257,15 +269,16 @@ def test_fullsize_workload(i):
     e_clean = float(err[~bad_tok].max()) if (~bad_tok).any() else 0.0
     e_flipped = float(err[bad_tok].max()) if bad_tok.any() else 0.0
     rel_rms = float(np.sqrt(np.mean((out - out_ind) ** 2))) / r_ind
-    report("  flips", workload=wl.name, elements=S * F, code_flips=flips,
+    report("  flips", workload=wl.name + ("-exact" if flags else ""), elements=S * F, code_flips=flips,
            scale_flips=int(rows_s.sum()), tensor_scale_same=ts_same, rows_with_flips=int(flipped.sum()),
            tokens_with_flips=int(bad_tok.sum()), tokens=T)
     report("  output", stage_err=f"{e_stage:.2e}", independent_clean_err=f"{e_clean:.2e}",
            independent_flipped_tokens_err=f"{e_flipped:.2e}", independent_rel_rms=f"{rel_rms:.2e}",
            combine_err=f"{e_comb:.2e}")
-    assert flips <= 1e-3 * S * F, f"{flips} intermediate code flips in {S * F} elements"
+    bounds = output_bounds(native8)
+    assert flips <= bounds["max_flip_frac"] * S * F, f"{flips} intermediate code flips in {S * F} elements"
     assert e_clean <= 2e-3, f"independent output error {e_clean:.2e} x RMS on tokens without flips"
-    assert rel_rms <= 2e-3, f"independent output RMS error {rel_rms:.2e} x RMS"
+    assert rel_rms <= bounds["max_rel_rms"], f"independent output RMS error {rel_rms:.2e} x RMS"
 
     # ---- decode NVFP4 / MXFP8: the oracle's own forward on the experts the batch touches
     if keep_gate_up:
@@ -284,7 +297,7 @@ def test_fullsize_workload(i):
         t_orc = time.perf_counter() - t0
         e_s, e_i, fl, excl = check_outputs(fmt, out, ref, cidx, o_w, g_codes, g_scales, g_its, otp["inter_codes"],
                                            otp.get("inter_scales"), ss, o_dn, D=D, F=F, E=len(used), e_begin=0,
-                                           e_end=len(used))
+                                           e_end=len(used), **output_bounds(native8))
         inter_vs_oracle = float(np.abs(otp["inter"] - inter_ref).max()) / float(np.abs(inter_ref).max())
         report("  oracle forward", seconds=f"{t_orc:.1f}", stage_err=f"{e_s:.2e}", independent_err=f"{e_i:.2e}",
                code_flips=fl, tokens_with_flips=excl, composed_vs_oracle_inter=f"{inter_vs_oracle:.1e}")

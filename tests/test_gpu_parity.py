@@ -16,7 +16,8 @@ import torch
 import block_scaled_moe_amd as moe
 import oracle
 import synth
-from gpu_util import case_inputs, check_intermediate_codes, check_outputs, host, report, rms, to_dev, untile
+from gpu_util import (INTER_TOL_EXACT, INTER_TOL_SCALED_FP8, case_inputs, check_intermediate_codes, check_outputs, host,
+                      output_bounds, report, rms, scaled_fp8, to_dev, untile)
 
 pytestmark = pytest.mark.gpu
 
@@ -200,6 +201,22 @@ LAYER_CASES = [
     dict(name="prefill-bf16-k1024", wl=synth.custom("bf16", T=1024, D=1024, F=512, E=32, seed=83)),
     dict(name="stream-bf16-k2048", wl=synth.custom("bf16", T=48, D=2048, F=1536, E=16, seed=84)),
     dict(name="ep-share-bf16", wl=synth.custom("bf16", T=400, D=512, F=384, E=24, e_begin=6, e_end=15, seed=85)),
+    # MXFP8 with exact sums (MOE_FLAG_EXACT_SUMS): the bf16 expansion on the grouped,
+    # tile and streaming kernels instead of the scaled FP8 MFMA
+    dict(name="decode-mxfp8-exact", wl=synth.custom("mxfp8", T=40, D=256, F=256, E=16, seed=22), flags=1),
+    dict(name="prefill-mxfp8-exact", wl=synth.custom("mxfp8", T=300, D=256, F=256, E=16, seed=26), flags=1),
+    dict(name="prefill-mxfp8-k1024-exact", wl=synth.custom("mxfp8", T=1024, D=1024, F=512, E=32, seed=38), flags=1),
+    dict(name="prefill-mxfp8-skew-tiles-exact",
+         wl=synth.custom("mxfp8", T=1100, D=512, F=256, E=24, skew=True, seed=39), flags=1),
+    dict(name="ep-share-prefill-mxfp8-exact",
+         wl=synth.custom("mxfp8", T=400, D=256, F=128, E=24, e_begin=0, e_end=6, seed=28), flags=1),
+    dict(name="stream-mxfp8-k2048-exact", wl=synth.custom("mxfp8", T=48, D=2048, F=1536, E=16, seed=32), flags=1),
+    dict(name="stream-mxfp8-full-dims-exact", wl=synth.custom("mxfp8", T=64, D=4096, F=2560, E=16, seed=35),
+         flags=1),
+    # the scaled FP8 MFMA at the full dimensions (decode tiles) and at widths that are not
+    # powers of two (5 gate_up N-blocks, 3 down N-blocks, 12 and 10 K chunks)
+    dict(name="mxfp8-full-dims", wl=synth.custom("mxfp8", T=64, D=4096, F=2560, E=16, seed=57)),
+    dict(name="prefill-mxfp8-d768-f640", wl=synth.custom("mxfp8", T=700, D=768, F=640, E=12, seed=58)),
 ]
 
 
@@ -216,7 +233,9 @@ def test_forward_parity(c):
     dn = moe.quantize_weights(fmt, to_dev(dn_m))
     d_h = to_dev(h)
     idx, w, _, amax = moe.route(d_h, to_dev(wr), k, None if bias is None else to_dev(bias), True)
-    layer = moe.Layer(fmt, T, D, F, E, gu, dn, top_k=k, e_begin=eb, e_end=ee)
+    layer = moe.Layer(fmt, T, D, F, E, gu, dn, top_k=k, e_begin=eb, e_end=ee, flags=c.get("flags", 0))
+    native8 = scaled_fp8(layer)
+    report("  plan", **layer.plan())
     taps = layer.enable_taps()
     out = host(layer.forward(d_h, idx, w, h_amax=amax if fmt == "nvfp4" else None))
     torch.cuda.synchronize()
@@ -252,12 +271,13 @@ def test_forward_parity(c):
     g_its = tp["inter_tscale"][0] if fmt == "nvfp4" else None
     g_iscales = tp["inter_scales"][:S] if "inter_scales" in tp else None
     check_intermediate_codes(fmt, g_inter, tp["inter_codes"][:S], g_iscales, g_its)
-    assert inter_err < 1e-5, f"SwiGLU intermediate differs by {inter_err:.2e} of its max"
+    inter_tol = INTER_TOL_SCALED_FP8 if native8 else INTER_TOL_EXACT
+    assert inter_err < inter_tol, f"SwiGLU intermediate differs by {inter_err:.2e} of its max"
 
     # output: stage-wise on every token, independent on tokens without intermediate flips
     e_stage, e_ind, flips, excluded = check_outputs(
         fmt, out, ref, o_idx, o_w, tp["inter_codes"][:S], g_iscales, g_its, otp["inter_codes"],
-        otp.get("inter_scales"), ss, o_dn, D=D, F=F, E=E, e_begin=eb, e_end=ee)
+        otp.get("inter_scales"), ss, o_dn, D=D, F=F, E=E, e_begin=eb, e_end=ee, **output_bounds(native8))
     report("  result", S=S, inter_rel=f"{inter_err:.2e}", code_flips=flips, tokens_with_flips=excluded,
            stage_err=f"{e_stage:.2e}", independent_err=f"{e_ind:.2e}")
     has_local = ((o_idx >= eb) & (o_idx < ee)).any(1)
