@@ -3,10 +3,15 @@
 One step = the whole hot path over one batch: moe_route (router logits, top-8, gate
 weights, hidden-state amax) + moe_forward (permutation, hidden-state quantisation,
 gate_up GEMM with SwiGLU and intermediate quantisation, down GEMM, weighted
-combine), with all inputs and packed weights resident in HBM. The default workload
-is the NVFP4 decode step (64 tokens, d_model 4096, d_ff 2560, 384 experts, top-8);
---workload i selects one of the eleven seeded synthetic workloads (NVFP4, MXFP8, and the
-MXFP4, W4A16 and bf16-expert variants).
+combine), with all inputs and packed weights resident in HBM.
+
+By default the five seeded workloads of the layer's configurations run one after the
+other: tiny-nvfp4 (16 tokens, d_model 256), decode-nvfp4 (64 tokens, d_model 4096,
+d_ff 2560, 384 experts, top-8), decode-mxfp8 (256 tokens), prefill-nvfp4-ep4 (8192
+tokens, one expert-parallel rank's 96 experts) and skewed-mxfp8 (16384 tokens, Zipf-like
+router bias). The headline fields of the JSON line are decode-nvfp4's; `configs` holds
+every workload's line. --workload i runs one of the eleven synthetic workloads alone
+(the five plus the MXFP4, W4A16 and bf16-expert variants).
 
 Printed: one JSON line (rank 0). `roofline` covers the dominant kernel (the gate_up
 GEMM) timed live with HIP events recorded around its launch on the library's stream;
@@ -132,14 +137,25 @@ def make_weights(moe, torch, wl, dev):
     return gu, dn
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, h, wr, bias, target_s: float = 10.0):
     """The oracle (route + forward, fp64 experts) on the first tokens of the workload,
     timed on this host; the sample grows until it takes about target_s seconds.
     Experts are compacted to those the sample touches (weights quantised by the
-    oracle itself, untimed)."""
+    oracle itself once per expert, untimed)."""
     import oracle
 
     cores = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    quantised = {}  # expert -> (gate_up, down) of the oracle's quantiser
     n = 2
     while True:
         hs = np.ascontiguousarray(h[:n])
@@ -152,17 +168,22 @@ def cpu_baseline(wl, h, wr, bias, target_s: float = 10.0):
         remap[used] = np.arange(len(used), dtype=np.int32)
         cidx = np.where(local, remap[idx], len(used)).astype(np.int32)  # non-local -> outside [0, m)
         m = len(used)
-        if wl.fmt == "bf16":  # unquantised: the touched experts' masters plus one zero expert
-            z = lambda a: np.concatenate([a, np.zeros((1,) + a.shape[1:], a.dtype)])
+        if m == 0 and n < wl.T:  # no local slot in the sample yet (an expert-parallel share)
+            n = min(wl.T, 2 * n)
+            continue
+        if wl.fmt == "bf16":  # unquantised: the touched experts' masters plus zero experts
+            pad = max(1, wl.k - m)
+            z = lambda a: np.concatenate([a, np.zeros((pad,) + a.shape[1:], a.dtype)])
             gm = z(np.stack([wl.gate_up_master(int(e))[0] for e in used]))
             dm = z(np.stack([wl.down_master(int(e))[0] for e in used]))
             t1 = time.perf_counter()
-            oracle.moe_forward("bf16", hs, cidx, w, D=wl.D, F=wl.F, E=m + 1, e_begin=0, e_end=m,
+            oracle.moe_forward("bf16", hs, cidx, w, D=wl.D, F=wl.F, E=m + pad, e_begin=0, e_end=m,
                                gate_up_master=gm, down_master=dm)
             t_fwd = time.perf_counter() - t1
             total = t_route + t_fwd
             if total >= target_s or n >= wl.T:
-                return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                return {"value": n / total, "unit": "tokens/s", "cores": cores, "cpu_model": cpu_model(),
+                        "kind": "oracle",
                         "sample": f"first {n} of {wl.T} tokens of the workload, route + forward, "
                                   f"{m} touched experts, {total:.1f} s"}
             n = min(wl.T, max(n * 2, int(n * target_s / max(total, 1e-3)) + 1))
@@ -170,66 +191,46 @@ def cpu_baseline(wl, h, wr, bias, target_s: float = 10.0):
         gu = {"codes": [], "scales": [], "tensor_scale": []}
         dn = {"codes": [], "scales": [], "tensor_scale": []}
         for e in used:
-            for d, master in ((gu, wl.gate_up_master(int(e))), (dn, wl.down_master(int(e)))):
-                q = oracle.quantize_weights(wl.fmt, master)
+            e = int(e)
+            if e not in quantised:
+                quantised[e] = (oracle.quantize_weights(wl.fmt, wl.gate_up_master(e)),
+                                oracle.quantize_weights(wl.fmt, wl.down_master(e)))
+            for d, q in zip((gu, dn), quantised[e]):
                 for key in d:
                     d[key].append(q[key])
         cat = lambda d: {k_: (None if v[0] is None else np.concatenate(v)) for k_, v in d.items()}
         gu, dn = cat(gu), cat(dn)
+        pad = max(1, wl.k - m)  # all-zero experts after the m touched ones (the oracle needs E >= top_k)
         t1 = time.perf_counter()
-        oracle.moe_forward(wl.fmt, hs, cidx, w, D=wl.D, F=wl.F, E=m + 1, e_begin=0, e_end=m,
-                           gate_up=_pad_expert(gu, wl.fmt), down=_pad_expert(dn, wl.fmt))
+        oracle.moe_forward(wl.fmt, hs, cidx, w, D=wl.D, F=wl.F, E=m + pad, e_begin=0, e_end=m,
+                           gate_up=_pad_experts(gu, pad), down=_pad_experts(dn, pad))
         t_fwd = time.perf_counter() - t1
         total = t_route + t_fwd
         if total >= target_s or n >= wl.T:
-            return {"value": n / total, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            return {"value": n / total, "unit": "tokens/s", "cores": cores, "cpu_model": cpu_model(),
+                    "kind": "oracle",
                     "sample": f"first {n} of {wl.T} tokens of the workload, route + forward, "
                               f"{m} touched experts, {total:.1f} s"}
         n = min(wl.T, max(n * 2, int(n * target_s / max(total, 1e-3)) + 1))
 
 
-def _pad_expert(d, fmt):
-    """Append one all-zero expert (the non-local slot target of the compacted table)."""
+def _pad_experts(d, count):
+    """Append `count` all-zero experts (the non-local slot target of the compacted table)."""
     out = {}
     for k_, v in d.items():
         if v is None:
             out[k_] = None
             continue
-        pad = np.zeros((1,) + v.shape[1:], v.dtype)
+        pad = np.zeros((count,) + v.shape[1:], v.dtype)
         if k_ == "tensor_scale":
-            pad = np.ones(1, v.dtype)
+            pad = np.ones(count, v.dtype)
         out[k_] = np.concatenate([v, pad])
     return out
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=1, help="index into the eleven synthetic workloads")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", action="store_true",
-                    help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "
-                         "the two measured the same)")
-    ap.add_argument("--cpu-target-s", type=float, default=10.0)
-    ap.add_argument("--calib-copy-mb", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer is built for one "
-              "GPU's expert share (moe_forward takes a local expert range; N ranks would each run the "
-              "same router, compute their experts' slots and sum the fp32 partial outputs with one "
-              "all-reduce).", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-
-    import block_scaled_moe_amd as moe
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
-    wl = synth.WORKLOADS[args.workload]
+def run_workload(moe, torch, wl, args, dev):
+    """Times one workload: warm-up, then args.steps steps (eager, or one HIP graph replayed per
+    step with --graph). Returns its JSON fields."""
     T, D, F, E, k = wl.T, wl.D, wl.F, wl.E, wl.k
     print(f"[bench] workload {wl.index} {wl.name}: T={T} D={D} F={F} E={E} local=[{wl.e_begin},{wl.local_end})",
           file=sys.stderr, flush=True)
@@ -246,6 +247,7 @@ def main():
           f"({(gu.nbytes() + dn.nbytes()) / 1e9:.2f} GB)", file=sys.stderr, flush=True)
 
     layer = moe.Layer(wl.fmt, T, D, F, E, gu, dn, top_k=k, e_begin=wl.e_begin, e_end=wl.local_end)
+    plan = layer.plan()  # the kernels moe_forward dispatches (its own plan)
     out = torch.empty((T, D), dtype=torch.float32, device=dev)
     nv = wl.fmt == "nvfp4"
     mx4 = wl.fmt == "mxfp4"
@@ -317,10 +319,10 @@ def main():
     gate_up_bytes = touched * gu_b + act_b(T, D) + act_b(S, F)
     gate_up_flops = 4.0 * S * F * D
     layer_bytes = touched * (gu_b + dn_b) + E * D * 2 + T * D * 2 + T * D * 4
-    # the NVFP4 / MXFP8 GEMMs run f16 / bf16 MFMAs on exactly expanded values, so that is
-    # the contraction's peak, with the format's own scaled-MFMA peak reported beside it;
-    # the MXFP4 GEMMs run the scaled FP4 MFMA itself
-    kern = layer.plan()["gate_up_kernel"]  # what moe_forward dispatched (its own plan)
+    # the contraction's own peak: NVFP4 runs the f16 MFMA on exactly expanded values, W4A16
+    # and bf16 experts the bf16 MFMA, MXFP4 the scaled FP4 MFMA, MXFP8 the scaled FP8 MFMA
+    # (or, with exact sums, the bf16 MFMA); the format's scaled-MFMA peak is reported beside it
+    kern = plan["gate_up_kernel"]
     native8 = wl.fmt == "mxfp8" and kern == "mx_gemm_kernel"
     mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else ("fp8" if native8 else "bf16"))]
     format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt in ("w4a16", "bf16") else "fp8")]
@@ -339,9 +341,10 @@ def main():
     roof["kernel_source_sha256"] = kernel_source_hash(kern)
     roof["per_launch"] = {"bytes": gate_up_bytes, "flops": gate_up_flops, "ms": round(gate_up_ms, 4)}
 
-    print(f"[bench] {ms_step:.3f} ms/step ({launch}; eager {eager_ms_step:.3f}) (forward {fwd_ms:.3f} ms: gate_up {gate_up_ms:.3f} ms, down "
-          f"{down_ms:.3f} ms); S={S}, {touched} experts touched, layer {layer_bytes / 1e9:.3f} GB "
-          f"-> {layer_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s whole-step", file=sys.stderr, flush=True)
+    print(f"[bench] {wl.name}: {ms_step:.3f} ms/step ({launch}; eager {eager_ms_step:.3f}) (forward {fwd_ms:.3f} ms: "
+          f"gate_up {gate_up_ms:.3f} ms, down {down_ms:.3f} ms); S={S}, {touched} experts touched, layer "
+          f"{layer_bytes / 1e9:.3f} GB -> {layer_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s whole-step; "
+          f"{plan['gate_up_kernel']} / {plan['down_kernel']}", file=sys.stderr, flush=True)
 
     if args.calib_copy_mb:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE calibrate the counters
@@ -354,24 +357,80 @@ def main():
         print(f"[bench] calibration copy of {n} bytes done", file=sys.stderr, flush=True)
         del src, dst
 
+    del layer, gu, dn, out, route_ws, d_h, d_wr, d_bias
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, h, wr, bias, args.cpu_target_s)
-        print(f"[bench] cpu baseline: {cpu}", file=sys.stderr, flush=True)
+        print(f"[bench] {wl.name} cpu baseline: {cpu}", file=sys.stderr, flush=True)
 
-    value = T * K / (total_ms * 1e-3)
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": DTYPES[wl.fmt],
-        "data": "synthetic",
-        "config": {"workload": wl.name, "launch": launch, "tokens": T, "d_model": D, "d_ff": F, "experts": E, "top_k": k,
-                   "format": wl.fmt, "local_experts": [wl.e_begin, wl.local_end], "experts_touched": touched,
-                   "slots": S, "layer_bytes": layer_bytes,
-                   "layer_GBps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1)},
+    return {
+        "value": round(T * K / (total_ms * 1e-3), 1), "unit": "tokens/s", "ms_per_step": round(ms_step, 4),
+        "dtype": DTYPES[wl.fmt] if wl.fmt != "mxfp8" or native8 else "bf16 (exact MXFP8 values), fp32 accumulate",
+        "config": {"workload": wl.name, "launch": launch, "tokens": T, "d_model": D, "d_ff": F, "experts": E,
+                   "top_k": k, "format": wl.fmt, "local_experts": [wl.e_begin, wl.local_end],
+                   "experts_touched": touched, "slots": S, "layer_bytes": layer_bytes,
+                   "layer_GBps": round(layer_bytes / (ms_step * 1e-3) / 1e9, 1),
+                   "kernels": {"gate_up": plan["gate_up_kernel"], "down": plan["down_kernel"]},
+                   "stage_ms": {"forward": round(fwd_ms, 4), "gate_up": round(gate_up_ms, 4),
+                                "down": round(down_ms, 4)}},
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+
+
+# the layer's five configurations (bench workloads 0-4); decode-nvfp4 is the headline
+DEFAULT_WORKLOADS = [0, 1, 2, 3, 4]
+HEADLINE = 1
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=None,
+                    help="run one of the eleven synthetic workloads alone (default: the five configurations)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "
+                         "the two measured the same)")
+    ap.add_argument("--cpu-target-s", type=float, default=None,
+                    help="seconds of oracle work per workload (default: 10 for one workload, 6 each for the five)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested): the layer is built for one "
+              "GPU's expert share (moe_forward takes a local expert range; N ranks would each run the "
+              "same router, compute their experts' slots and sum the fp32 partial outputs with one "
+              "all-reduce).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_scaled_moe_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    workloads = DEFAULT_WORKLOADS if args.workload is None else [args.workload]
+    if args.cpu_target_s is None:
+        args.cpu_target_s = 10.0 if len(workloads) == 1 else 6.0
+    results = [run_workload(moe, torch, synth.WORKLOADS[i], args, dev) for i in workloads]
+    head = results[workloads.index(HEADLINE)] if HEADLINE in workloads else results[0]
+
+    line = {
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": head["dtype"], "data": "synthetic",
+        "config": head["config"], "roofline": head["roofline"], "cpu_baseline": head["cpu_baseline"],
+    }
+    if len(results) > 1:
+        line["configs"] = [{"workload": r["config"]["workload"], "value": r["value"], "unit": r["unit"],
+                            "ms_per_step": r["ms_per_step"], "dtype": r["dtype"], "config": r["config"],
+                            "roofline": r["roofline"], "cpu_baseline": r["cpu_baseline"]} for r in results]
     print(json.dumps(line), flush=True)
 
 
