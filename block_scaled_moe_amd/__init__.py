@@ -77,7 +77,9 @@ SIGNATURES = {
     "moe_forward_workspace_bytes": ([ctypes.POINTER(MoeForwardArgs)], ctypes.c_size_t),
     "moe_forward": ([ctypes.POINTER(MoeForwardArgs), ctypes.c_void_p], ctypes.c_int32),
     "moe_forward_plan": ([ctypes.POINTER(MoeForwardArgs), ctypes.POINTER(MoePlanInfo)], ctypes.c_int32),
+    "moe_forward_static": ([ctypes.POINTER(MoeForwardArgs), ctypes.c_void_p], ctypes.c_int32),
 }
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_STATIC_SCRATCH_BYTES: moe_forward_static's device array
 
 
 def lib():
@@ -271,6 +273,19 @@ class Layer:
         a.h, a.topk_idx, a.topk_w, a.out = h.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(), out.data_ptr()
         a.h_amax = None if h_amax is None else h_amax.data_ptr()
         _check(lib().moe_forward(ctypes.byref(a), _stream(self.device)), "moe_forward")
+        return out
+
+    def forward_static(self, h: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor,
+                       out: torch.Tensor | None = None, h_amax: torch.Tensor | None = None) -> torch.Tensor:
+        """moe_forward_static on the current stream (the library's static scratch instead of
+        this layer's workspace) -> out fp32 [T, D]."""
+        a = MoeForwardArgs.from_buffer_copy(self.args)
+        a.workspace, a.workspace_bytes, a.events, a.taps = None, 0, None, None
+        if out is None:
+            out = torch.empty((self.T, self.D), dtype=torch.float32, device=self.device)
+        a.h, a.topk_idx, a.topk_w, a.out = h.data_ptr(), topk_idx.data_ptr(), topk_w.data_ptr(), out.data_ptr()
+        a.h_amax = None if h_amax is None else h_amax.data_ptr()
+        _check(lib().moe_forward_static(ctypes.byref(a), _stream(self.device)), "moe_forward_static")
         return out
 
     @property

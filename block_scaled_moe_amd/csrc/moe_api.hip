@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "internal.h"
 
@@ -267,15 +269,13 @@ int32_t moe_forward_plan(const moe_forward_args *a, moe_plan_info *info) {
     return MOE_OK;
 }
 
-int32_t moe_forward(const moe_forward_args *a, void *stream) {
-    int32_t rc = moe_forward_validate(a);
-    if (rc != MOE_OK) return rc;
-    if (a->T == 0) return MOE_OK;
-    const Plan P = make_plan(a);
-    if (!a->workspace || a->workspace_bytes < P.total) return MOE_ERR_WORKSPACE;
-    if (((uintptr_t)a->workspace & 255u) != 0) return MOE_ERR_ALIGNMENT;
-    hipStream_t s = (hipStream_t)stream;
-    uint8_t *ws = static_cast<uint8_t *>(a->workspace);
+}  // extern "C"
+
+namespace {
+
+// The launch sequence of one forward call on the validated arguments `a` with the plan P
+// and P.total bytes of device workspace at ws (256-byte aligned).
+int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipStream_t s) {
     const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
     const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     const int32_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
@@ -423,6 +423,57 @@ int32_t moe_forward(const moe_forward_args *a, void *stream) {
         MOE_TRY(cp(t->y, ws + P.y, sizeof(float) * (size_t)TK * D));
     }
     return MOE_OK;
+}
+
+// Device scratch of moe_forward_static: a file-scope array, so that the call allocates
+// nothing. Each GPU the library runs on holds its own copy for the life of the process;
+// host code addresses it only through the per-device pointer from hipGetSymbolAddress.
+constexpr size_t kStaticScratchBytes = MOE_STATIC_SCRATCH_BYTES;
+__device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+int32_t static_scratch(uint8_t **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = static_cast<uint8_t *>(g_scratch_ptr[dev]);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t moe_forward(const moe_forward_args *a, void *stream) {
+    int32_t rc = moe_forward_validate(a);
+    if (rc != MOE_OK) return rc;
+    if (a->T == 0) return MOE_OK;
+    const Plan P = make_plan(a);
+    if (!a->workspace || a->workspace_bytes < P.total) return MOE_ERR_WORKSPACE;
+    if (((uintptr_t)a->workspace & 255u) != 0) return MOE_ERR_ALIGNMENT;
+    return run_forward(a, P, static_cast<uint8_t *>(a->workspace), (hipStream_t)stream);
+}
+
+int32_t moe_forward_static(const moe_forward_args *a, void *stream) {
+    int32_t rc = moe_forward_validate(a);
+    if (rc != MOE_OK) return rc;
+    if (a->T == 0) return MOE_OK;
+    const Plan P = make_plan(a);
+    if (P.total > kStaticScratchBytes) return MOE_ERR_WORKSPACE;
+    uint8_t *ws = nullptr;
+    rc = static_scratch(&ws);
+    if (rc != MOE_OK) return rc;
+    return run_forward(a, P, ws, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -239,6 +239,23 @@ int32_t moe_forward_plan(const moe_forward_args *a, moe_plan_info *info);
  */
 int32_t moe_forward(const moe_forward_args *a, void *stream);
 
+/*
+ * moe_forward for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same layer and
+ * kernels, with the workspace taken from the library's own static device array of
+ * MOE_STATIC_SCRATCH_BYTES bytes instead of a->workspace (ignored, may be NULL).
+ * It calls no allocating routine. Each GPU the library runs on holds its own copy of
+ * the array until the process ends; its address on the current device is looked up on
+ * the first call there, so `stream` must belong to the current device.
+ * Returns MOE_ERR_WORKSPACE if moe_forward_workspace_bytes(a) exceeds the array (64 MiB
+ * covers decode batches of up to about 400 tokens at d_model 4096, d_ff 2560, top-8),
+ * otherwise what moe_forward returns. Every call on a GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that overlap on one GPU (different streams, or
+ * different host threads) race and must be serialised by the caller.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int32_t moe_forward_static(const moe_forward_args *a, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_functions_are_exported_and_bound():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
@@ -188,3 +188,19 @@ def test_forward_plan_names_the_kernels():
     assert _validate(_args(flags=2)) == EINVAL
     rc, info = _plan(_args(T=0))
     assert rc == OK and info.gate_up_kernel == b"none"
+
+
+def test_forward_static_validates_on_the_host():
+    """moe_forward_static: the static scratch's limit and the argument checks come first."""
+    lib = moe.lib()
+    assert lib.moe_forward_static(ctypes.byref(_args(top_k=9)), None) == EINVAL
+    assert lib.moe_forward_static(ctypes.byref(_args(h=A16 + 2)), None) == EALIGN
+    big = _args(T=8192, e_end=96)   # about 1.4 GB of workspace: beyond the 64 MiB array
+    assert moe.lib().moe_forward_workspace_bytes(ctypes.byref(big)) > moe.STATIC_SCRATCH_BYTES
+    assert lib.moe_forward_static(ctypes.byref(big), None) == EWS
+    assert moe.lib().moe_forward_workspace_bytes(ctypes.byref(_args())) <= moe.STATIC_SCRATCH_BYTES
+    mx = _args(fmt=2, T=256)
+    mx.gate_up = moe.MoePacked(2, 384, 5120, 4096, A16, A16, 0)
+    mx.down = moe.MoePacked(2, 384, 4096, 2560, A16, A16, 0)
+    assert moe.lib().moe_forward_workspace_bytes(ctypes.byref(mx)) <= moe.STATIC_SCRATCH_BYTES
+    assert lib.moe_forward_static(ctypes.byref(_args(T=0, h=0, topk_idx=0, topk_w=0, out=0)), None) == OK
