@@ -40,6 +40,12 @@ class MoePacked(ctypes.Structure):
                 ("tensor_scale", ctypes.c_void_p)]
 
 
+class MoeRowMajor(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("tensor_scale", ctypes.c_void_p)]
+
+
 class MoeTaps(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "counts", "offsets", "sorted_slot", "a_codes", "a_scales", "a_tscale", "inter",
@@ -71,6 +77,7 @@ SIGNATURES = {
     "moe_abi_version": ([], ctypes.c_int32),
     "moe_status_string": ([ctypes.c_int32], ctypes.c_char_p),
     "moe_quantize_weights": ([ctypes.c_void_p, ctypes.POINTER(MoePacked), ctypes.c_void_p], ctypes.c_int32),
+    "moe_pack_weights": ([ctypes.POINTER(MoeRowMajor), ctypes.POINTER(MoePacked), ctypes.c_void_p], ctypes.c_int32),
     "moe_route_workspace_bytes": ([ctypes.c_int32] * 3, ctypes.c_size_t),
     "moe_route": ([ctypes.c_int32] * 4 + [ctypes.c_void_p] * 8 + [ctypes.c_size_t, ctypes.c_void_p], ctypes.c_int32),
     "moe_forward_validate": ([ctypes.POINTER(MoeForwardArgs)], ctypes.c_int32),
@@ -180,6 +187,24 @@ def quantize_weights(fmt: str, w: torch.Tensor, out: PackedWeights | None = None
         out = PackedWeights.empty(fmt, E, N, K, device=w.device)
     st = out.struct()
     _check(lib().moe_quantize_weights(_ptr(w), ctypes.byref(st), _stream(w.device)), "moe_quantize_weights")
+    return out
+
+
+def pack_weights(fmt: str, codes: torch.Tensor, scales: torch.Tensor | None = None,
+                 tensor_scale: torch.Tensor | None = None, out: PackedWeights | None = None) -> PackedWeights:
+    """Pre-quantised row-major weights (device tensors: codes [E, N, K/2] NVFP4 / MXFP4,
+    [E, N, K] MXFP8 (uint8) or bf16 (2-byte); scales [E, N, K/16 or K/32]; NVFP4 tensor
+    scales [E]) -> PackedWeights (moe_pack_weights); "w4a16" packs as NVFP4."""
+    if fmt == "w4a16":
+        fmt = "nvfp4"
+    E, N = codes.shape[0], codes.shape[1]
+    K = codes.shape[2] * (2 if fmt in ("nvfp4", "mxfp4") else 1)
+    if out is None:
+        out = PackedWeights.empty(fmt, E, N, K, device=codes.device)
+    src = MoeRowMajor(FMT[fmt], E, N, K, codes.data_ptr(), None if scales is None else scales.data_ptr(),
+                      None if tensor_scale is None else tensor_scale.data_ptr())
+    st = out.struct()
+    _check(lib().moe_pack_weights(ctypes.byref(src), ctypes.byref(st), _stream(codes.device)), "moe_pack_weights")
     return out
 
 

@@ -27,6 +27,10 @@ hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, i
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
 // bf16 weights copied into the packed tile layout (layout.h, 128 bytes per row slot)
 hipError_t launch_pack_weights_bf16(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes, hipStream_t s);
+// row-major pre-quantised codes and scales (fmt 1 NVFP4, 2 MXFP8, 3 MXFP4) into the packed
+// tile layout (layout.h); a pure byte reordering
+hipError_t launch_pack_rowmajor(int fmt, const uint8_t *src_codes, const uint8_t *src_scales, int32_t E, int32_t N,
+                                int32_t K, uint8_t *codes, uint8_t *scales, hipStream_t s);
 hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K,
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
 // hidden states [T][D] -> MXFP4 codes [T][D/2] and E8M0 scales [T][D/32]

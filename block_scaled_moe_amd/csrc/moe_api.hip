@@ -180,6 +180,28 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     return to_status(launch_finish_tensor_scale(out->tensor_scale, E, s));
 }
 
+int32_t moe_pack_weights(const moe_rowmajor *in, moe_packed *out, void *stream) {
+    if (!in || !out) return MOE_ERR_INVALID_ARG;
+    const int32_t fmt = in->fmt, E = in->E, N = in->N, K = in->K;
+    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_BF16)
+        return MOE_ERR_INVALID_ARG;
+    if (out->fmt != fmt || out->E != E || out->N != N || out->K != K) return MOE_ERR_INVALID_ARG;
+    if (E <= 0 || N <= 0 || K <= 0 || N % 32 || K % 64) return MOE_ERR_INVALID_ARG;
+    const bool scaled = fmt != MOE_FMT_BF16, nv = fmt == MOE_FMT_NVFP4;
+    if (!in->codes || !out->codes || (scaled && (!in->scales || !out->scales)) ||
+        (nv && (!in->tensor_scale || !out->tensor_scale)))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned16(in->codes) || !aligned16(out->codes) || (out->scales && !aligned16(out->scales)) ||
+        (nv && (((uintptr_t)in->tensor_scale | (uintptr_t)out->tensor_scale) & 3u)))
+        return MOE_ERR_ALIGNMENT;
+    hipStream_t s = (hipStream_t)stream;
+    if (!scaled)
+        return to_status(launch_pack_weights_bf16(reinterpret_cast<const uint16_t *>(in->codes), E, N, K, out->codes, s));
+    MOE_TRY(launch_pack_rowmajor(fmt, in->codes, in->scales, E, N, K, out->codes, out->scales, s));
+    if (nv) MOE_TRY(hipMemcpyAsync(out->tensor_scale, in->tensor_scale, sizeof(float) * E, hipMemcpyDeviceToDevice, s));
+    return MOE_OK;
+}
+
 size_t moe_route_workspace_bytes(int32_t T, int32_t D, int32_t E) {
     if (T <= 0 || D <= 0 || D % 64 || E <= 0 || E > 1024) return 0;
     return route_plan(T, D, E).bytes;

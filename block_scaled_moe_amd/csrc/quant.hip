@@ -283,6 +283,49 @@ hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, i
     return hipGetLastError();
 }
 
+// Row-major pre-quantised weights (codes [E][N][K/2] NVFP4 and MXFP4, [E][N][K] MXFP8;
+// scales [E][N][K/16] or [E][N][K/32]) into the packed tile layout: one thread per
+// quantisation block in storage order, the same mapping the quantisers write (layout.h).
+// fmt: 1 NVFP4, 2 MXFP8, 3 MXFP4 (the MOE_FMT_* values).
+__global__ void __launch_bounds__(kThreads) pack_rowmajor_kernel(int fmt, const uint8_t *__restrict__ src_codes,
+                                                                 const uint8_t *__restrict__ src_scales,
+                                                                 int64_t n_blocks, int64_t blocks_per_expert,
+                                                                 int32_t K, uint8_t *__restrict__ codes,
+                                                                 uint8_t *__restrict__ scales) {
+    const int blk = fmt == 1 ? 16 : 32;              // values per quantisation block
+    const int64_t row_bytes = fmt == 2 ? K : K / 2;  // code bytes per weight row
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = b / blocks_per_expert, r = b - e * blocks_per_expert;
+        int64_t n, k;
+        if (fmt == 3)
+            layout::block_source_mx4(K, r, n, k);
+        else
+            layout::block_source(fmt == 1, K, r, n, k);
+        const int64_t row = e * (blocks_per_expert / (K / blk)) + n;  // weight row over all experts
+        const uint8_t *src = src_codes + row * row_bytes + (fmt == 2 ? k : k / 2);
+        if (fmt == 1) {
+            reinterpret_cast<uint2 *>(codes)[b] = *reinterpret_cast<const uint2 *>(src);
+        } else if (fmt == 3) {
+            reinterpret_cast<uint4 *>(codes)[b] = *reinterpret_cast<const uint4 *>(src);
+        } else {
+            uint8_t *ce = codes + e * blocks_per_expert * 32;
+            *reinterpret_cast<uint4 *>(ce + layout::code_offset(false, K, n, k)) = *reinterpret_cast<const uint4 *>(src);
+            *reinterpret_cast<uint4 *>(ce + layout::code_offset(false, K, n, k + 16)) =
+                *reinterpret_cast<const uint4 *>(src + 16);
+        }
+        scales[b] = src_scales[row * (K / blk) + k / blk];
+    }
+}
+
+hipError_t launch_pack_rowmajor(int fmt, const uint8_t *src_codes, const uint8_t *src_scales, int32_t E, int32_t N,
+                                int32_t K, uint8_t *codes, uint8_t *scales, hipStream_t s) {
+    const int64_t per = (int64_t)N * (K / (fmt == 1 ? 16 : 32));
+    const int64_t nb = per * E;
+    hipLaunchKernelGGL(pack_rowmajor_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, fmt, src_codes, src_scales, nb,
+                       per, K, codes, scales);
+    return hipGetLastError();
+}
+
 // bf16 weights into the packed tile layout: one thread per 16-byte piece
 __global__ void __launch_bounds__(kThreads) pack_bf16_kernel(const uint16_t *__restrict__ w, int64_t n_pieces,
                                                              int32_t K, int64_t pieces_per_expert,

@@ -96,6 +96,21 @@ typedef struct moe_packed {
     float *tensor_scale;
 } moe_packed;
 
+/* Expert weights already quantised, in plain row-major arrays (a checkpoint's own
+ * layout), one matrix kind [N][K] per expert for E experts:
+ *   NVFP4: codes [E][N][K/2] E2M1, element 2i in the low nibble of byte i;
+ *          scales [E][N][K/16] E4M3; tensor_scale fp32 [E]
+ *   MXFP8: codes [E][N][K] E4M3; scales [E][N][K/32] E8M0; tensor_scale NULL
+ *   MXFP4: codes [E][N][K/2] E2M1 (as NVFP4); scales [E][N][K/32] E8M0
+ *   BF16:  codes [E][N][K] bf16 values (2 bytes each); scales, tensor_scale NULL */
+typedef struct moe_rowmajor {
+    int32_t fmt;
+    int32_t E, N, K;
+    const uint8_t *codes;
+    const uint8_t *scales;
+    const float *tensor_scale;
+} moe_rowmajor;
+
 /* Optional debug outputs of moe_forward (each pointer NULL = not written).
  * S = number of local token-slots (known on the device only; read offsets[n_loc]).
  * Slot-indexed arrays are in sorted (expert-grouped) order, sized for S <= T*top_k. */
@@ -181,6 +196,18 @@ const char *moe_status_string(int32_t status);
  * N must be a multiple of 32 and K of 64 (the tiled layout above).
  */
 int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
+
+/*
+ * Pack pre-quantised row-major weights `in` (a checkpoint in the format's plain layout,
+ * vLLM recipe "thinkingmachines/Inkling-2-Small", section "Overview": the native NVFP4 /
+ * MXFP8 checkpoint) into the tiled layout of `out` (fmt, E, N, K equal to in's; buffers
+ * set by the caller): a pure reordering of the code and scale bytes, the tensor scales
+ * copied. The bytes moe_quantize_weights writes for bf16 masters are the packing of the
+ * row-major quantisation of the same masters. N % 32 == 0 and K % 64 == 0; in->codes and
+ * out's code and scale buffers 16-byte aligned (MOE_ERR_ALIGNMENT), tensor scales
+ * 4-byte aligned. `in` and `out` must not overlap.
+ */
+int32_t moe_pack_weights(const moe_rowmajor *in, moe_packed *out, void *stream);
 
 /*
  * Router (softmax-then-top-k gate, recipe "Overview": 8 of 384 experts per token):

@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_functions_are_exported_and_bound():
     lib = moe.lib()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
@@ -204,3 +204,18 @@ def test_forward_static_validates_on_the_host():
     mx.down = moe.MoePacked(2, 384, 4096, 2560, A16, A16, 0)
     assert moe.lib().moe_forward_workspace_bytes(ctypes.byref(mx)) <= moe.STATIC_SCRATCH_BYTES
     assert lib.moe_forward_static(ctypes.byref(_args(T=0, h=0, topk_idx=0, topk_w=0, out=0)), None) == OK
+
+
+def test_pack_weights_validates_on_the_host():
+    lib = moe.lib()
+    p = lambda *a: moe.MoeRowMajor(*a)
+    ok_out = moe.MoePacked(1, 2, 64, 128, A16, A16, A16)
+    assert lib.moe_pack_weights(None, ctypes.byref(ok_out), None) == EINVAL
+    assert lib.moe_pack_weights(ctypes.byref(p(1, 2, 64, 128, A16, A16, 0)), ctypes.byref(ok_out), None) == EINVAL
+    assert lib.moe_pack_weights(ctypes.byref(p(2, 2, 64, 128, A16, A16, 0)), ctypes.byref(ok_out), None) == EINVAL
+    assert lib.moe_pack_weights(ctypes.byref(p(1, 2, 64, 96, A16, A16, A16)),
+                                ctypes.byref(moe.MoePacked(1, 2, 64, 96, A16, A16, A16)), None) == EINVAL
+    assert lib.moe_pack_weights(ctypes.byref(p(1, 2, 64, 128, A16 + 8, A16, A16)), ctypes.byref(ok_out),
+                                None) == EALIGN
+    mx = moe.MoePacked(2, 2, 64, 128, A16, 0, 0)
+    assert lib.moe_pack_weights(ctypes.byref(p(2, 2, 64, 128, A16, A16, 0)), ctypes.byref(mx), None) == EINVAL

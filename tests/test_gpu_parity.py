@@ -67,6 +67,33 @@ def test_quantize_weights_bitexact(fmt, shape):
         assert np.array_equal(host(got.tensor_scale).view(np.uint32), ref["tensor_scale"].view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "bf16"])
+@pytest.mark.parametrize("shape", [(3, 96, 512), (2, 256, 2048)])
+def test_pack_rowmajor_checkpoint_bitexact(fmt, shape):
+    """moe_pack_weights on the oracle's row-major quantisation (a pre-quantised checkpoint)
+    gives the bytes moe_quantize_weights writes for the same masters, and untiles to it."""
+    E, N, K = shape
+    w = _adversarial_masters(E, N, K, seed=17)
+    report("pack_weights", fmt=fmt, E=E, N=N, K=K)
+    if fmt == "bf16":
+        got = moe.pack_weights(fmt, to_dev(w))
+    else:
+        o = oracle.quantize_weights(fmt, w)
+        ts = None if o["tensor_scale"] is None else to_dev(o["tensor_scale"])
+        got = moe.pack_weights(fmt, to_dev(o["codes"]), to_dev(o["scales"]), ts)
+    ref = moe.quantize_weights(fmt, to_dev(w))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got.codes), host(ref.codes)), "packed codes differ"
+    assert np.array_equal(host(got.scales), host(ref.scales)), "packed scales differ"
+    if fmt == "nvfp4":
+        assert np.array_equal(host(got.tensor_scale).view(np.uint32), host(ref.tensor_scale).view(np.uint32))
+    if fmt == "bf16":
+        assert np.array_equal(untile(host(got.codes)).view(np.uint16), w)
+    else:
+        assert np.array_equal(untile(host(got.codes)), o["codes"]) and np.array_equal(untile(host(got.scales)),
+                                                                                     o["scales"])
+
+
 # ------------------------------------------------------------------ router
 ROUTER_CASES = [
     dict(T=37, D=256, E=64, skew=False),      # exact path, ragged token tile
