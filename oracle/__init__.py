@@ -216,6 +216,22 @@ def dequant_mxfp8(codes, scales) -> np.ndarray:
     return out
 
 
+def fold_to_mx(values: np.ndarray, fmt: str = "mxfp8") -> np.ndarray:
+    """The values a scaled MFMA that takes one E8M0 scale per 32 values would see if exact
+    values [rows, K] (e.g. NVFP4 codes times their per-16 E4M3 block scales, each exact in
+    fp32) were folded into its operands: each 32-block re-encoded by the OCP MX rule (E8M0
+    scale 2^(floor(log2 amax) - 8) for E4M3 elements, - 2 for E2M1, elements rounded to
+    nearest even, saturating), fp64. Test-side emulation of the alternative to the exact
+    16-bit expansion; the MX quantisers and dequantisers below do the work."""
+    x = np.ascontiguousarray(values, np.float32)
+    assert np.array_equal(x.astype(np.float64), np.asarray(values, np.float64)), "values must be exact in fp32"
+    if fmt == "mxfp8":
+        return dequant_mxfp8(*quant_mxfp8(x))
+    if fmt == "mxfp4":
+        return dequant_mxfp4(*quant_mxfp4(x))
+    raise ValueError(fmt)
+
+
 def round_bf16(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns (uint16), nearest with ties to even."""
     x = np.ascontiguousarray(x, np.float32)
