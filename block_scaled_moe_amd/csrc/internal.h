@@ -15,6 +15,21 @@ struct Ctrl {
     int32_t pad[60];
 };
 
+// Quantisation of the hidden states h [T][D] to the layer's format (act_quant.h): run by
+// its own launch or by extra workgroups of the permutation's first launch.
+constexpr int32_t kActNone = 0, kActNVFP4 = 1, kActMXFP8 = 2, kActMXFP4 = 3;
+struct ActQuant {
+    int32_t fmt;                // kAct*; kActNone: no job
+    int32_t T, D;
+    const uint16_t *h;          // bf16 [T][D]
+    const uint32_t *amax_bits;  // NVFP4: max |h| (fp32 bits)
+    uint8_t *codes, *scales;    // [T][D/2] or [T][D]; [T][D/16] or [T][D/32]
+    void *deq;                  // NVFP4: exact fp16 values [T][D]; MXFP8: exact bf16 values or NULL
+    float *tscale_out;          // NVFP4: [1] the tensor scale
+};
+// the job on its own launch
+hipError_t launch_act_quant(const ActQuant &q, hipStream_t s);
+
 // ---- weight / activation quantisers (quant.hip)
 hipError_t launch_fill_u32(uint32_t *p, uint32_t v, int64_t n, hipStream_t s);
 hipError_t launch_amax_bf16_rows(const uint16_t *x, int64_t rows, int64_t K, int64_t groups,
@@ -33,16 +48,6 @@ hipError_t launch_pack_rowmajor(int fmt, const uint8_t *src_codes, const uint8_t
                                 int32_t K, uint8_t *codes, uint8_t *scales, hipStream_t s);
 hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K,
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
-// hidden states [T][D] -> MXFP4 codes [T][D/2] and E8M0 scales [T][D/32]
-hipError_t launch_quant_act_mxfp4(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
-                                  hipStream_t s);
-// hidden states [T][D] -> NVFP4 codes/scales and the exact fp16 value codes*scale
-hipError_t launch_quant_act_nvfp4(const uint16_t *h, int32_t T, int32_t D, const uint32_t *amax_bits,
-                                  uint8_t *codes, uint8_t *scales, _Float16 *deq, float *tscale_out,
-                                  hipStream_t s);
-// hidden states [T][D] -> MXFP8 codes/scales and the exact bf16 value code*2^scale
-hipError_t launch_quant_act_mxfp8(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes,
-                                  uint8_t *scales, uint16_t *deq_bf16, hipStream_t s);
 // intermediate [rows <= ctrl->S][F] fp32 -> NVFP4 (tensor scale from ctrl->amax_i)
 hipError_t launch_quant_inter_nvfp4(const float *x, int32_t max_rows, int32_t F, const Ctrl *ctrl,
                                     uint8_t *codes, uint8_t *scales, _Float16 *deq, float *tscale_out,
@@ -77,6 +82,8 @@ struct PermuteArgs {
     int32_t *sorted_slot;   // [T*k]
     int32_t *slot_pos;      // [T*k]  sorted position of each slot or -1
     Ctrl *ctrl;
+    ActQuant quant;         // hidden-state quantisation carried by extra workgroups of the
+                            // first launch (fmt kActNone: none)
 };
 hipError_t launch_permute(const PermuteArgs &a, hipStream_t s);
 // one-workgroup variant for T*k <= 8192 and <= 1024 local experts; also clears the

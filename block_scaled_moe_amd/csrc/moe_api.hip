@@ -332,25 +332,28 @@ int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipSt
     pa.sorted_slot = I32(P.sorted_slot);
     pa.slot_pos = I32(P.slot_pos);
     pa.ctrl = ctrl;
-    MOE_TRY(small ? launch_permute_small(pa, s) : launch_permute(pa, s));
 
-    // 2. hidden states quantised once per token
-    if (nv) {
-        const uint32_t *amax = reinterpret_cast<const uint32_t *>(a->h_amax);
-        if (!amax) {
-            MOE_TRY(launch_amax_bf16_rows(a->h, T, D, 1, &ctrl->amax_a, s));
-            amax = &ctrl->amax_a;
-        }
-        MOE_TRY(launch_quant_act_nvfp4(a->h, T, D, amax, U8(P.a_codes), U8(P.a_scales), F16(P.a16),
-                                       F32(P.a_tscale), s));
-    } else if (mx4) {
-        MOE_TRY(launch_quant_act_mxfp4(a->h, T, D, U8(P.a_codes), U8(P.a_scales), s));
-    } else if (a16) {
-        // W4A16 and bf16 experts: the GEMM reads the bf16 hidden states directly
-    } else {
-        // MXFP8: the scaled MFMA reads the codes; the exact route their bf16 values
-        MOE_TRY(launch_quant_act_mxfp8(a->h, T, D, U8(P.a_codes), U8(P.a_scales),
-                                       P.scaled ? nullptr : reinterpret_cast<uint16_t *>(ws + P.a16), s));
+    // 2. hidden states quantised once per token (W4A16 and bf16 experts read them as they
+    // are): NVFP4 with one tensor scale over all of h from the router's max |h|; MXFP8
+    // also writes its exact bf16 values for the exact route. The job rides in extra
+    // workgroups of the permutation's first launch; without the router's max |h| an
+    // NVFP4 layer takes an amax pass after the permutation and quantises on its own.
+    ActQuant q{};
+    q.fmt = nv ? kActNVFP4 : (mx4 ? kActMXFP4 : (a16 ? kActNone : kActMXFP8));
+    q.T = T;
+    q.D = D;
+    q.h = a->h;
+    q.amax_bits = nv ? (a->h_amax ? reinterpret_cast<const uint32_t *>(a->h_amax) : &ctrl->amax_a) : nullptr;
+    q.codes = a16 ? nullptr : U8(P.a_codes);
+    q.scales = a16 ? nullptr : U8(P.a_scales);
+    q.deq = nv ? static_cast<void *>(F16(P.a16)) : ((mx4 || a16 || P.scaled) ? nullptr : static_cast<void *>(ws + P.a16));
+    q.tscale_out = nv ? F32(P.a_tscale) : nullptr;
+    const bool carried = !(nv && !a->h_amax);
+    if (carried) pa.quant = q;
+    MOE_TRY(small ? launch_permute_small(pa, s) : launch_permute(pa, s));
+    if (!carried) {
+        MOE_TRY(launch_amax_bf16_rows(a->h, T, D, 1, &ctrl->amax_a, s));  // amax_a cleared by the permutation
+        MOE_TRY(launch_act_quant(q, s));
     }
 
     // 3. gate_up GEMM + SwiGLU (+ MXFP8 intermediate quantisation)

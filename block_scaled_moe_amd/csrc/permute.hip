@@ -6,17 +6,37 @@
 // "thinkingmachines/Inkling-2-Small", section "Overview": expert parallelism follows
 // the tensor-parallel group). Local slots are ordered by expert and by s within an
 // expert (a stable counting sort) in three passes over chunks of consecutive tokens:
-//   count   per-chunk histogram (LDS atomics; order does not matter for counts)
+//   count   per-chunk histogram (LDS atomics; order does not matter for counts); extra
+//           workgroups of this launch quantise the hidden states (act_quant.h)
 //   scan    one workgroup: per-expert running sums over chunks, the exclusive
 //           prefix over experts, and the list of BM-row tiles of every expert
 //   scatter one wave per chunk walks its slots in groups of 64, in order; within a
 //           group each slot's rank among the slots of the same expert comes from
 //           comparing the lanes' experts, so positions are exact and stable for any
 //           routing, duplicates included.
+#include "act_quant.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
+
+// The hidden-state quantisation carried by a permutation launch: workgroups `first` and
+// on quantise blocks in a grid-stride loop (the permutation's own workgroups come first;
+// the two jobs share no data, so the launch costs the longer of them instead of both
+// plus a launch boundary).
+__device__ __forceinline__ void carried_quant(const ActQuant &q, int first) {
+    const int64_t n = act_quant_blocks(q);
+    const int64_t stride = (int64_t)(gridDim.x - first) * blockDim.x;
+    for (int64_t b = (int64_t)(blockIdx.x - first) * blockDim.x + threadIdx.x; b < n; b += stride)
+        act_quant_block(q, b);
+}
+
+// workgroups of a permutation launch given to the quantisation job
+inline int32_t quant_groups(const ActQuant &q, int threads) {
+    if (q.fmt == kActNone) return 0;
+    const int64_t g = (act_quant_blocks(q) + threads - 1) / threads;
+    return (int32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
+}
 
 // For a group of 64 slots held one per lane (el: local expert, -1 if not local): the
 // number of lower lanes holding the same expert (rank) and of all lanes holding it
@@ -63,7 +83,12 @@ __device__ __forceinline__ void place_group(const PermuteArgs &a, int32_t *curso
 
 __global__ void __launch_bounds__(256) count_kernel(const int32_t *__restrict__ idx, int32_t n_slots,
                                                     int32_t chunk_slots, int32_t e_begin, int32_t n_loc,
-                                                    int32_t *__restrict__ chunk_counts, Ctrl *__restrict__ ctrl) {
+                                                    int32_t *__restrict__ chunk_counts, Ctrl *__restrict__ ctrl,
+                                                    int32_t n_chunks, const ActQuant quant) {
+    if ((int32_t)blockIdx.x >= n_chunks) {  // the carried hidden-state quantisation
+        carried_quant(quant, n_chunks);
+        return;
+    }
     extern __shared__ int32_t cnt[];
     for (int i = threadIdx.x; i < n_loc; i += 256) cnt[i] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0) {  // accumulators of the later passes
@@ -230,10 +255,15 @@ __global__ void __launch_bounds__(64) scatter_kernel(PermuteArgs a, int32_t n_sl
 // local experts): per-wave histograms of kSmallWaves contiguous parts of the slots, the
 // exclusive scans and the tile list, then each wave places its part group by group,
 // starting from its own per-expert bases. Also clears the control block's
-// accumulators, so no separate fill is needed.
+// accumulators, so no separate fill is needed. Workgroups 1 and on quantise the hidden
+// states (act_quant.h).
 constexpr int kSmallMaxLocal = 1024;
 
 __global__ void __launch_bounds__(kSmallThreads) permute_small_kernel(PermuteArgs a) {
+    if (blockIdx.x > 0) {  // the carried hidden-state quantisation
+        carried_quant(a.quant, 1);
+        return;
+    }
     __shared__ int32_t cnt[kSmallWaves][kSmallMaxLocal];  // per-wave counts, then per-wave bases
     __shared__ int32_t tot[kSmallMaxLocal];
     __shared__ int32_t tiles[kSmallMaxLocal];
@@ -297,7 +327,8 @@ bool permute_small_ok(int32_t T, int32_t k, int32_t n_loc) {
 }
 
 hipError_t launch_permute_small(const PermuteArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL(permute_small_kernel, dim3(1), dim3(kSmallThreads), 0, s, a);
+    hipLaunchKernelGGL(permute_small_kernel, dim3(1 + quant_groups(a.quant, kSmallThreads)), dim3(kSmallThreads), 0, s,
+                       a);
     return hipGetLastError();
 }
 
@@ -305,8 +336,8 @@ hipError_t launch_permute(const PermuteArgs &a, hipStream_t s) {
     const int32_t n_slots = a.T * a.k;
     const int32_t chunk_slots = a.chunk_tokens * a.k;
     const size_t lds = sizeof(int32_t) * (size_t)a.n_loc;
-    hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks), dim3(256), lds, s, a.idx, n_slots, chunk_slots, a.e_begin,
-                       a.n_loc, a.chunk_counts, a.ctrl);
+    hipLaunchKernelGGL(count_kernel, dim3(a.n_chunks + quant_groups(a.quant, 256)), dim3(256), lds, s, a.idx, n_slots,
+                       chunk_slots, a.e_begin, a.n_loc, a.chunk_counts, a.ctrl, a.n_chunks, a.quant);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a);

@@ -8,6 +8,7 @@
 // 16-byte loads, quantised in registers and written as packed bytes. Each NVFP4
 // tensor scale needs the tensor's max |x| first, so NVFP4 runs as amax pass, block
 // pass, then a tiny pass turning the amax into the fp32 tensor scale.
+#include "act_quant.h"
 #include "formats.h"
 #include "gemm_common.h"
 #include "internal.h"
@@ -49,25 +50,6 @@ __global__ void __launch_bounds__(kThreads) amax_bf16_kernel(const uint16_t *__r
         for (int i = 1; i < kThreads / 64; ++i) m = max(m, red[i]);
         if (m) atomic_max_grow(amax_bits + g, m << 16);  // bf16 bits -> fp32 bits
     }
-}
-
-__device__ __forceinline__ void load16_bf16(const uint16_t *p, float (&x)[16]) {
-    const uint4 *q = reinterpret_cast<const uint4 *>(p);
-    const uint4 a = q[0], b = q[1];
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        x[2 * j] = __uint_as_float(w[j] << 16);
-        x[2 * j + 1] = __uint_as_float(w[j] & 0xffff0000u);
-    }
-}
-
-// exact fp16 of e2m1(code) * e4m3(scale) for the 16 codes of a block
-__device__ __forceinline__ void store_dequant16(_Float16 *dst, uint32_t lo, uint32_t hi, int scale) {
-    const _Float16 s = gemm_detail::e4m3_to_f16((uint32_t)scale);
-    gemm_detail::half8 *d = reinterpret_cast<gemm_detail::half8 *>(dst);
-    d[0] = gemm_detail::dequant_nvfp4(lo, s);
-    d[1] = gemm_detail::dequant_nvfp4(hi, s);
 }
 
 // NVFP4 weights, in the packed tile layout (layout.h): thread b writes storage block
@@ -181,25 +163,10 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp4_bf16_kernel(const uint16
     }
 }
 
-// NVFP4 hidden states: one tensor scale over all T*D values.
-__global__ void __launch_bounds__(kThreads) quant_act_nvfp4_kernel(const uint16_t *__restrict__ h, int64_t n_blocks,
-                                                                   const uint32_t *__restrict__ amax_bits,
-                                                                   uint8_t *__restrict__ codes,
-                                                                   uint8_t *__restrict__ scales,
-                                                                   _Float16 *__restrict__ deq,
-                                                                   float *__restrict__ tscale_out) {
-    const float sg = nvfp4_tensor_scale(__uint_as_float(amax_bits[0]));
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b == 0 && tscale_out) tscale_out[0] = sg;
-    if (b >= n_blocks) return;
-    float x[16];
-    load16_bf16(h + b * 16, x);
-    uint32_t lo, hi;
-    int sc;
-    nvfp4_quant_block(x, sg, lo, hi, sc);
-    reinterpret_cast<uint2 *>(codes)[b] = make_uint2(lo, hi);
-    scales[b] = (uint8_t)sc;
-    store_dequant16(deq + b * 16, lo, hi, sc);
+// Hidden states to the layer's format, one thread per block (act_quant.h).
+__global__ void __launch_bounds__(kThreads) act_quant_kernel(const ActQuant q, int64_t n_blocks) {
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x)
+        act_quant_block(q, b);
 }
 
 // NVFP4 SwiGLU intermediate: rows [0, S) of x [*][F] fp32, one tensor scale over
@@ -356,28 +323,13 @@ hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, i
     return hipGetLastError();
 }
 
-hipError_t launch_quant_act_mxfp4(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
-                                  hipStream_t s) {
-    const int64_t nb = (int64_t)T * (D / 32);
-    if (nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(quant_mxfp4_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, h, nb, 0, (int64_t)0,
-                       codes, scales);
-    return hipGetLastError();
-}
 
-hipError_t launch_quant_act_nvfp4(const uint16_t *h, int32_t T, int32_t D, const uint32_t *amax_bits, uint8_t *codes,
-                                  uint8_t *scales, _Float16 *deq, float *tscale_out, hipStream_t s) {
-    const int64_t nb = (int64_t)T * (D / 16);
-    hipLaunchKernelGGL(quant_act_nvfp4_kernel, dim3((unsigned)((nb + kThreads - 1) / kThreads)), dim3(kThreads), 0, s,
-                       h, nb, amax_bits, codes, scales, deq, tscale_out);
-    return hipGetLastError();
-}
 
-hipError_t launch_quant_act_mxfp8(const uint16_t *h, int32_t T, int32_t D, uint8_t *codes, uint8_t *scales,
-                                  uint16_t *deq_bf16, hipStream_t s) {
-    const int64_t nb = (int64_t)T * (D / 32);
-    hipLaunchKernelGGL(quant_mxfp8_bf16_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, h, nb, 0, (int64_t)0, codes,
-                       scales, deq_bf16);
+
+hipError_t launch_act_quant(const ActQuant &q, hipStream_t s) {
+    const int64_t nb = act_quant_blocks(q);
+    if (q.fmt == kActNone || nb == 0) return hipSuccess;
+    hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, q, nb);
     return hipGetLastError();
 }
 
