@@ -19,7 +19,8 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# ORACLE_LIB selects another build of oracle.c (the sanitizer build of build_sanitized())
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4, FMT_W4A16, FMT_BF16 = 0, 1, 2, 3, 4, 5
@@ -34,6 +35,16 @@ def build() -> str:
     subprocess.run(cmd, check=True)
     os.replace(_LIB_PATH + ".tmp", _LIB_PATH)
     return _LIB_PATH
+
+
+def build_sanitized(path: str) -> str:
+    """oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer (every UB report fatal),
+    for loading through ORACLE_LIB in a process started with the ASan runtime preloaded."""
+    cmd = ["gcc", "-O1", "-g", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-ffp-contract=off", "-Wall",
+           "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer",
+           os.path.join(_HERE, "oracle.c"), "-o", path, "-lm"]
+    subprocess.run(cmd, check=True)
+    return path
 
 
 class _Args(ctypes.Structure):
