@@ -1,5 +1,6 @@
-"""CPU oracle of the routed-expert MoE layer (NVFP4 / MXFP8 / MXFP4 experts, and NVFP4
-weights with bf16 activations, "w4a16").
+"""CPU oracle of the routed-expert MoE layer (NVFP4 / MXFP8 / MXFP4 experts, NVFP4
+weights with bf16 activations, "w4a16", bf16 experts, and FP8 experts with a scale per
+weight channel and a dynamic scale per activation row, "fp8").
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and
 by bench.py's cpu_baseline leg, never by the library. It wraps oracle.c (plain
@@ -23,10 +24,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lib = None
 
-FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4, FMT_W4A16, FMT_BF16 = 0, 1, 2, 3, 4, 5
+FMT_NONE, FMT_NVFP4, FMT_MXFP8, FMT_MXFP4, FMT_W4A16, FMT_BF16, FMT_FP8 = 0, 1, 2, 3, 4, 5, 6
 # "none": the textbook layer in fp64 on the bf16 masters; "bf16": bf16 experts with the
 # GPU's roundings (fp32 sums, bf16 intermediate)
-_FMT = {"none": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4, "bf16": 5}
+_FMT = {"none": 0, "nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4, "bf16": 5, "fp8": 6}
 
 
 def build() -> str:
@@ -111,7 +112,13 @@ def _load():
     lib.orc_permute.restype = i64
     lib.orc_moe_forward.argtypes = [ctypes.POINTER(_Args)]
     lib.orc_moe_forward.restype = ctypes.c_int
-    lib.orc_down_combine.argtypes = [i32] * 8 + [p, p, p, p, flt, p, p, p, p]
+    lib.orc_down_combine.argtypes = [i32] * 8 + [p, p, p, p, flt, p, p, p, p, p]
+    lib.orc_fp8_row_scale.argtypes = [flt]
+    lib.orc_fp8_row_scale.restype = flt
+    lib.orc_quant_fp8_rows.argtypes = [p, i64, i64, p, p]
+    lib.orc_quant_fp8_rows.restype = ctypes.c_int
+    lib.orc_dequant_fp8_rows.argtypes = [p, p, i64, i64, ctypes.c_int, p]
+    lib.orc_dequant_fp8_rows.restype = ctypes.c_int
     lib.orc_down_combine.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -188,6 +195,33 @@ def quant_mxfp8(x: np.ndarray):
     return codes, scales
 
 
+def fp8_row_scale(amax: float) -> float:
+    """The FP8 row scale for a row whose largest magnitude is amax (fp32)."""
+    return float(_load().orc_fp8_row_scale(amax))
+
+
+def quant_fp8_rows(x: np.ndarray):
+    """E4M3 with one fp32 scale per row of a [rows, K] fp32 tensor -> (codes [rows,K],
+    scales float32 [rows])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    rows, K = x.shape
+    codes = np.empty((rows, K), np.uint8)
+    scales = np.empty(rows, np.float32)
+    _check(_load().orc_quant_fp8_rows(_ptr(x), rows, K, _ptr(codes), _ptr(scales)), "quant_fp8_rows")
+    return codes, scales
+
+
+def dequant_fp8_rows(codes, scales=None) -> np.ndarray:
+    """codes [rows, K] -> fp64 values, times the row scales when given."""
+    codes = np.ascontiguousarray(codes, np.uint8)
+    rows, K = codes.shape
+    sc = None if scales is None else np.ascontiguousarray(scales, np.float32)
+    out = np.empty((rows, K), np.float64)
+    _check(_load().orc_dequant_fp8_rows(_ptr(codes), _ptr(sc), rows, K, 0 if sc is None else 1, _ptr(out)),
+           "dequant_fp8_rows")
+    return out
+
+
 def dequant_nvfp4(codes, scales, tensor_scale, with_tensor=True) -> np.ndarray:
     codes = np.ascontiguousarray(codes, np.uint8)
     scales = np.ascontiguousarray(scales, np.uint8)
@@ -253,7 +287,8 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 def quantize_weights(fmt: str, w_bf16: np.ndarray):
     """Quantise bf16 masters [E, N, K] per expert -> dict(codes, scales, tensor_scale|None).
-    W4A16 weights are NVFP4 weights."""
+    W4A16 weights are NVFP4 weights; FP8 weights have no block scales (scales None) and one
+    fp32 scale per output channel (tensor_scale [E, N])."""
     f = _FMT[fmt]
     if f == FMT_W4A16:
         f = FMT_NVFP4
@@ -267,6 +302,10 @@ def quantize_weights(fmt: str, w_bf16: np.ndarray):
         codes = np.empty((E, N, K // 2), np.uint8)
         scales = np.empty((E, N, K // 32), np.uint8)
         ts = None
+    elif f == FMT_FP8:
+        codes = np.empty((E, N, K), np.uint8)
+        scales = None
+        ts = np.empty((E, N), np.float32)
     else:
         codes = np.empty((E, N, K), np.uint8)
         scales = np.empty((E, N, K // 32), np.uint8)
@@ -313,8 +352,8 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
                 down_master=None, taps: bool = False, tok_list=None):
     """Oracle MoE forward -> out float32 [T, D] (and a dict of taps when taps=True).
 
-    gate_up/down: dicts from quantize_weights (fmt nvfp4/mxfp8/mxfp4/w4a16); *_master: bf16 arrays
-    (fmt none and bf16).
+    gate_up/down: dicts from quantize_weights (fmt nvfp4/mxfp8/mxfp4/w4a16/fp8); *_master: bf16
+    arrays (fmt none and bf16). FP8 taps: a_tscale [T] and inter_tscale [S] are the row scales.
     tok_list: compute only these tokens' outputs (others are zero)."""
     f = _FMT[fmt]
     lib = _load()
@@ -336,7 +375,7 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
     else:
         for name, d in (("gu", gate_up), ("dn", down)):
             c = np.ascontiguousarray(d["codes"], np.uint8)
-            s = np.ascontiguousarray(d["scales"], np.uint8)
+            s = None if d.get("scales") is None else np.ascontiguousarray(d["scales"], np.uint8)
             ts = None if d.get("tensor_scale") is None else np.ascontiguousarray(d["tensor_scale"], np.float32)
             keep += [c, s, ts]
             setattr(a, f"{name}_codes", _ptr(c))
@@ -351,6 +390,14 @@ def moe_forward(fmt: str, h_bf16, idx, w, *, D: int, F: int, E: int, e_begin: in
             tp["inter"] = np.zeros((S, F), np.float32)
             tp["inter_codes"] = np.zeros((S, F), np.uint16)
             a.inter, a.inter_codes = _ptr(tp["inter"]), _ptr(tp["inter_codes"])
+        elif f == FMT_FP8:
+            tp["a_codes"] = np.zeros((T, D), np.uint8)
+            tp["a_tscale"] = np.zeros(T, np.float32)
+            tp["inter"] = np.zeros((S, F), np.float32)
+            tp["inter_codes"] = np.zeros((S, F), np.uint8)
+            tp["inter_tscale"] = np.zeros(S, np.float32)
+            for n in ("a_codes", "a_tscale", "inter", "inter_codes", "inter_tscale"):
+                setattr(a, n, _ptr(tp[n]))
         elif f != FMT_NONE:
             tp["a_codes"] = np.zeros((T, D if f == FMT_MXFP8 else D // 2), np.uint8)
             tp["a_scales"] = np.zeros((T, D // 16 if f == FMT_NVFP4 else D // 32), np.uint8)
@@ -377,7 +424,8 @@ def down_combine(fmt: str, idx, w, inter_codes, inter_scales, inter_tscale, down
                  e_begin: int = 0, e_end: int | None = None):
     """Down projection and combine alone (the forward's last two steps) from given
     intermediate codes of the S local slots in sorted order -> out float32 [T, D].
-    W4A16: inter_codes are bf16 bit patterns [S][F] and inter_scales is None."""
+    W4A16: inter_codes are bf16 bit patterns [S][F] and inter_scales is None. FP8:
+    inter_codes are E4M3 [S][F] and inter_tscale is the row scales [S]."""
     f = _FMT[fmt]
     idx = np.ascontiguousarray(idx, np.int32)
     w = np.ascontiguousarray(w, np.float32)
@@ -389,11 +437,15 @@ def down_combine(fmt: str, idx, w, inter_codes, inter_scales, inter_tscale, down
         c, sc = np.ascontiguousarray(down, np.uint16), None
     else:
         c = np.ascontiguousarray(down["codes"], np.uint8)
-        sc = np.ascontiguousarray(down["scales"], np.uint8)
+        sc = None if down.get("scales") is None else np.ascontiguousarray(down["scales"], np.uint8)
     ts = (None if f == FMT_BF16 or down.get("tensor_scale") is None
           else np.ascontiguousarray(down["tensor_scale"], np.float32))
+    rs = None
+    if f == FMT_FP8:
+        rs = np.ascontiguousarray(inter_tscale, np.float32)
+        inter_tscale = None
     out = np.empty((T, D), np.float32)
     _check(_load().orc_down_combine(f, T, D, F, E, k, e_begin, e_end, _ptr(idx), _ptr(w), _ptr(ic), _ptr(is_),
                                     float(inter_tscale if inter_tscale is not None else 1.0), _ptr(c), _ptr(sc),
-                                    _ptr(ts), _ptr(out)), "down_combine")
+                                    _ptr(ts), _ptr(rs), _ptr(out)), "down_combine")
     return out

@@ -309,8 +309,54 @@ int orc_quant_mxfp4(const float *x, int64_t rows, int64_t K, uint8_t *codes, uin
 }
 
 /* ------------------------------------------------------------------------- */
+/* FP8 with one fp32 scale per row ([V] "Variants", variants.fp8: E4M3 with    */
+/* dynamic per-token activation quantisation; weights: one scale per output   */
+/* channel, i.e. per row of W [N][K]).                                        */
+/* ------------------------------------------------------------------------- */
+
+/* Row scale: fp32 amax / 448 (E4M3's largest value), or 1 for an all-zero row. */
+float orc_fp8_row_scale(float amax) {
+    return amax > 0.0f ? amax / 448.0f : 1.0f;
+}
+
+/* codes [rows][K]: E4M3 (nearest, ties to even, saturating, sign kept) of the fp32
+ * quotient x / s_row; scales [rows] fp32. */
+int orc_quant_fp8_rows(const float *x, int64_t rows, int64_t K, uint8_t *codes, float *scales) {
+    if (!x || !codes || !scales || rows < 0 || K <= 0) return ORC_EINVAL;
+    init_tables();
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const float *xr = x + r * K;
+        float amax = 0.0f;
+        for (int64_t i = 0; i < K; ++i) {
+            float a = fabsf(xr[i]);
+            if (a > amax) amax = a;
+        }
+        float s = orc_fp8_row_scale(amax);
+        for (int64_t i = 0; i < K; ++i) {
+            float q = xr[i] / s;
+            codes[r * K + i] = (uint8_t)orc_e4m3_encode((double)q);
+        }
+        scales[r] = s;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Dequantisation (fp64).                                                     */
 /* ------------------------------------------------------------------------- */
+
+/* x_hat = e4m3(code) [* scale of its row if with_scale]. */
+int orc_dequant_fp8_rows(const uint8_t *codes, const float *scales, int64_t rows, int64_t K, int with_scale,
+                         double *out) {
+    if (!codes || !out || (with_scale && !scales) || rows < 0 || K <= 0) return ORC_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows * K; ++i) {
+        double v = orc_e4m3_value(codes[i]);
+        out[i] = with_scale ? v * (double)scales[i / K] : v;
+    }
+    return ORC_OK;
+}
 
 /* x_hat = e2m1(code) * e4m3(scale) [* tensor_scale if with_tensor]. */
 int orc_dequant_nvfp4(const uint8_t *codes, const uint8_t *scales, float tensor_scale, int64_t rows,
@@ -354,13 +400,16 @@ int orc_round_bf16(const float *x, int64_t n, uint16_t *out) {
     return ORC_OK;
 }
 
-/* fmt 1 = NVFP4, 2 = MXFP8, 3 = MXFP4. w: bf16 [E][N][K]. tensor_scale: fp32 [E] (NVFP4). */
+/* fmt 1 = NVFP4, 2 = MXFP8, 3 = MXFP4, 6 = FP8 per channel. w: bf16 [E][N][K].
+ * tensor_scale: fp32 [E] (NVFP4) or fp32 [E][N], one per output channel (FP8); scales
+ * unused by FP8 (may be NULL). */
 int orc_quantize_weights(int fmt, int32_t E, int32_t N, int32_t K, const uint16_t *w, uint8_t *codes,
                          uint8_t *scales, float *tensor_scale) {
-    if (!w || !codes || !scales || E <= 0 || N <= 0 || K <= 0) return ORC_EINVAL;
-    if (fmt == 1 && (!tensor_scale || K % 16)) return ORC_EINVAL;
+    if (!w || !codes || (!scales && fmt != 6) || E <= 0 || N <= 0 || K <= 0) return ORC_EINVAL;
+    if ((fmt == 1 || fmt == 6) && !tensor_scale) return ORC_EINVAL;
+    if (fmt == 1 && K % 16) return ORC_EINVAL;
     if ((fmt == 2 || fmt == 3) && K % 32) return ORC_EINVAL;
-    if (fmt < 1 || fmt > 3) return ORC_EINVAL;
+    if (fmt < 1 || (fmt > 3 && fmt != 6)) return ORC_EINVAL;
     int64_t per = (int64_t)N * K;
     float *buf = (float *)malloc(sizeof(float) * per);
     if (!buf) return ORC_ENOMEM;
@@ -373,6 +422,8 @@ int orc_quantize_weights(int fmt, int32_t E, int32_t N, int32_t K, const uint16_
             rc = orc_quant_nvfp4(buf, N, K, codes + e * per / 2, scales + e * per / 16, tensor_scale + e, NULL);
         else if (fmt == 2)
             rc = orc_quant_mxfp8(buf, N, K, codes + e * per, scales + e * per / 32);
+        else if (fmt == 6) /* one scale per output channel (row) */
+            rc = orc_quant_fp8_rows(buf, N, K, codes + e * per, tensor_scale + e * N);
         else
             rc = orc_quant_mxfp4(buf, N, K, codes + e * per / 2, scales + e * per / 32);
     }
@@ -478,7 +529,10 @@ int64_t orc_permute(int32_t T, int32_t k, const int32_t *idx, int32_t e_begin, i
 typedef struct {
     int32_t fmt; /* 0 = unquantised bf16 masters (all fp64), 1 = NVFP4 W4A4, 2 = MXFP8 W8A8,
                     3 = MXFP4 W4A4, 4 = NVFP4 weights with bf16 activations (W4A16),
-                    5 = bf16 experts: the bf16 masters with fp32 sums and a bf16 intermediate */
+                    5 = bf16 experts: the bf16 masters with fp32 sums and a bf16 intermediate,
+                    6 = FP8: E4M3 weights with a scale per output channel (gu_tscale [E][2F],
+                        dn_tscale [E][D]) and E4M3 activations with a dynamic scale per row
+                        (taps: a_tscale [T] and inter_tscale [S] hold the row scales) */
     int32_t T, D, F, E, k, e_begin, e_end;
     const uint16_t *h;  /* bf16 [T][D] */
     const int32_t *idx; /* [T][k] */
@@ -513,7 +567,8 @@ static float swiglu_f32(float g, float u) {
 }
 
 /* Weight row r of expert e for the given matrix, dequantised to fp64 WITHOUT
- * the NVFP4 tensor scale (that factor is applied to the fp32 sum). */
+ * the NVFP4 tensor scale or the FP8 channel scale (those factors are applied to the
+ * fp32 sum). */
 static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, const uint8_t *scales,
                        int64_t row_index, int64_t K, double *out) {
     int64_t base = row_index * K;
@@ -526,6 +581,8 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
             out[j] = orc_e2m1_value(c) * orc_e4m3_value(scales[i / 16]);
         } else if (fmt == 2) {
             out[j] = orc_e4m3_value(codes[i]) * orc_e8m0_value(scales[i / 32]);
+        } else if (fmt == 6) { /* the channel scale is applied to the fp32 sum */
+            out[j] = orc_e4m3_value(codes[i]);
         } else {
             int c = (codes[i / 2] >> ((i & 1) * 4)) & 15;
             out[j] = orc_e2m1_value(c) * orc_e8m0_value(scales[i / 32]);
@@ -551,12 +608,15 @@ static void weight_row(int fmt, const uint16_t *master, const uint8_t *codes, co
  * fp32-rounded sums of 2 and 5 by the weight tensor scale alone, and in step 4 rounds
  * h to bf16 (nearest, ties to even). fmt 5 (bf16 experts, the checkpoint's BF16 variant
  * in the same section) runs fmt 4's steps on the bf16 masters: exact products, sums rounded
- * to fp32 with no scale, h rounded to bf16.
+ * to fp32 with no scale, h rounded to bf16. fmt 6 (FP8 with dynamic per-token activation
+ * scales, same recipe, variants.fp8) quantises h per token row and the intermediate per
+ * slot row (scale = row max / 448), and multiplies the fp32-rounded sums of 2 and 5 by
+ * fl32(row scale * the weight row's channel scale).
  */
 int orc_moe_forward(const orc_moe_args *a) {
     if (!a || a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->k <= 0 || a->k > a->E) return ORC_EINVAL;
     if (a->e_begin < 0 || a->e_end > a->E || a->e_end <= a->e_begin) return ORC_EINVAL;
-    if (a->fmt < 0 || a->fmt > 5) return ORC_EINVAL;
+    if (a->fmt < 0 || a->fmt > 6) return ORC_EINVAL;
     const int fmt = a->fmt;
     const int wf = fmt == 4 ? 1 : (fmt == 5 ? 0 : fmt); /* weight format (0: the bf16 masters) */
     const int a16 = fmt == 4 || fmt == 5;               /* bf16 activations, bf16 intermediate */
@@ -569,6 +629,7 @@ int orc_moe_forward(const orc_moe_args *a) {
     if (wf == 1 && (!a->gu_codes || !a->gu_scales || !a->gu_tscale || !a->dn_codes || !a->dn_scales || !a->dn_tscale))
         return ORC_EINVAL;
     if ((fmt == 2 || fmt == 3) && (!a->gu_codes || !a->gu_scales || !a->dn_codes || !a->dn_scales)) return ORC_EINVAL;
+    if (fmt == 6 && (!a->gu_codes || !a->gu_tscale || !a->dn_codes || !a->dn_tscale)) return ORC_EINVAL;
     init_tables();
 
     const int32_t n_loc = a->e_end - a->e_begin;
@@ -580,7 +641,7 @@ int orc_moe_forward(const orc_moe_args *a) {
     double *ahat = (double *)malloc(sizeof(double) * T * D);
     int64_t *cidx = NULL, *cdn = NULL;
     double *gu_raw = NULL, *ihat = NULL, *y64 = NULL, *inter64 = NULL;
-    float *inter = NULL;
+    float *inter = NULL, *a_rs = NULL, *i_rs = NULL; /* FP8 row scales of h and of the intermediate */
     if (!counts || !offs || !sorted || !want_tok || !ahat) { rc = ORC_ENOMEM; goto done; }
     const int64_t S = orc_permute(a->T, a->k, a->idx, a->e_begin, a->e_end, counts, offs, sorted);
 
@@ -612,6 +673,15 @@ int orc_moe_forward(const orc_moe_args *a) {
         for (int64_t i = 0; i < T * D; ++i) hf[i] = bf16_value(a->h[i]);
         if (fmt == 0 || a16) {
             for (int64_t i = 0; i < T * D; ++i) ahat[i] = hf[i];
+        } else if (fmt == 6) {
+            uint8_t *ac = (uint8_t *)malloc(T * D);
+            a_rs = (float *)malloc(sizeof(float) * T);
+            if (!ac || !a_rs) { free(hf); free(ac); rc = ORC_ENOMEM; goto done; }
+            orc_quant_fp8_rows(hf, T, D, ac, a_rs);
+            orc_dequant_fp8_rows(ac, a_rs, T, D, 0, ahat);
+            if (a->a_codes) memcpy(a->a_codes, ac, T * D);
+            if (a->a_tscale) memcpy(a->a_tscale, a_rs, sizeof(float) * T);
+            free(ac);
         } else {
             int64_t nc = fmt == 2 ? T * D : T * D / 2, ns = fmt == 1 ? T * D / 16 : T * D / 32;
             uint8_t *ac = (uint8_t *)malloc(nc), *as = (uint8_t *)malloc(ns);
@@ -698,6 +768,10 @@ int orc_moe_forward(const orc_moe_args *a) {
                 if (wf == 1) {
                     g = g * sc;
                     u = u * sc;
+                } else if (fmt == 6) { /* token scale times the gate / up channel scale */
+                    const float st = a_rs[sorted[p] / k];
+                    g = g * (st * a->gu_tscale[(int64_t)e * 2 * F + f]);
+                    u = u * (st * a->gu_tscale[(int64_t)e * 2 * F + F + f]);
                 }
                 float hv = swiglu_f32(g, u);
                 inter[c * F + f] = hv;
@@ -733,6 +807,20 @@ int orc_moe_forward(const orc_moe_args *a) {
         if (a->inter_tscale) *a->inter_tscale = i_ts;
         free(ic);
         free(is);
+    } else if (fmt == 6) {
+        /* every local slot's row with its own dynamic scale */
+        uint8_t *ic = (uint8_t *)malloc(F);
+        i_rs = (float *)malloc(sizeof(float) * (S > 0 ? S : 1));
+        if (!ic || !i_rs) { free(ic); rc = ORC_ENOMEM; goto done; }
+        for (int64_t p = 0; p < S; ++p) {
+            int64_t c = cidx[p];
+            if (c < 0) continue;
+            orc_quant_fp8_rows(inter + c * F, 1, F, ic, i_rs + p);
+            orc_dequant_fp8_rows(ic, i_rs + p, 1, F, 0, ihat + c * F);
+            if (a->inter_codes) memcpy(a->inter_codes + p * F, ic, F);
+            if (a->inter_tscale) a->inter_tscale[p] = i_rs[p];
+        }
+        free(ic);
     } else {
         /* MXFP8 [S][F] codes, MXFP4 [S][F/2]; both [S][F/32] scales */
         const int64_t cb = fmt == 2 ? F : F / 2;
@@ -785,6 +873,7 @@ int orc_moe_forward(const orc_moe_args *a) {
                         double yv;
                         if (fmt == 0) yv = s;
                         else if (wf == 1) yv = (float)((float)s * sc);
+                        else if (fmt == 6) yv = (float)((float)s * (i_rs[p] * a->dn_tscale[(int64_t)e * D + n]));
                         else yv = (float)s;
                         y64[cdn[p] * D + n] = yv;
                         if (a->y) a->y[p * D + n] = (float)yv;
@@ -824,6 +913,7 @@ int orc_moe_forward(const orc_moe_args *a) {
 done:
     free(counts); free(offs); free(sorted); free(want_tok); free(ahat);
     free(cidx); free(cdn); free(gu_raw); free(ihat); free(y64); free(inter64); free(inter);
+    free(a_rs); free(i_rs);
     return rc;
 }
 
@@ -836,18 +926,20 @@ done:
  * intermediate codes. i_codes / i_scales: [S][F/2] and [S][F/16] (NVFP4, tensor scale
  * i_ts), [S][F] and [S][F/32] (MXFP8), [S][F/2] and [S][F/32] (MXFP4), or bf16 bit
  * patterns [S][F] (2 bytes each) and no scales (W4A16, fmt 4, and bf16 experts, fmt 5,
- * whose dn_codes are the bf16 masters [E][D][F] and dn_scales may be NULL).
+ * whose dn_codes are the bf16 masters [E][D][F] and dn_scales may be NULL), or E4M3 codes
+ * [S][F] with fp32 row scales i_row_scales [S] (FP8, fmt 6: dn_tscale holds the channel
+ * scales [E][D]; dn_scales unused).
  */
 int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, int32_t k, int32_t e_begin,
                      int32_t e_end, const int32_t *idx, const float *w, const uint8_t *i_codes,
                      const uint8_t *i_scales, float i_ts, const uint8_t *dn_codes, const uint8_t *dn_scales,
-                     const float *dn_tscale, float *out) {
-    if (fmt < 1 || fmt > 5) return ORC_EINVAL;
+                     const float *dn_tscale, const float *i_row_scales, float *out) {
+    if (fmt < 1 || fmt > 6) return ORC_EINVAL;
     const int wf = fmt == 4 ? 1 : (fmt == 5 ? 0 : fmt);
     if (T < 0 || D <= 0 || F <= 0 || E <= 0 || k <= 0 || e_begin < 0 || e_end > E || e_end <= e_begin) return ORC_EINVAL;
     if (T == 0) return ORC_OK;
-    if (!idx || !w || !i_codes || (fmt < 4 && !i_scales) || !dn_codes || (wf != 0 && !dn_scales) || !out ||
-        (wf == 1 && !dn_tscale))
+    if (!idx || !w || !i_codes || (fmt < 4 && !i_scales) || !dn_codes || (wf != 0 && wf != 6 && !dn_scales) ||
+        !out || ((wf == 1 || wf == 6) && !dn_tscale) || (fmt == 6 && !i_row_scales))
         return ORC_EINVAL;
     init_tables();
     const int32_t n_loc = e_end - e_begin;
@@ -865,6 +957,7 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
     if (fmt == 1) orc_dequant_nvfp4(i_codes, i_scales, i_ts, S, F, 0, ihat);
     else if (fmt == 2) orc_dequant_mxfp8(i_codes, i_scales, S, F, ihat);
     else if (fmt == 3) orc_dequant_mxfp4(i_codes, i_scales, S, F, ihat);
+    else if (fmt == 6) orc_dequant_fp8_rows(i_codes, i_row_scales, S, F, 0, ihat);
     else /* fmt 4 and 5: bf16 */
         for (int64_t i = 0; i < S * F; ++i) {
             uint16_t b;
@@ -892,7 +985,10 @@ int orc_down_combine(int32_t fmt, int32_t T, int32_t D, int32_t F, int32_t E, in
                         const double *irow = ihat + p * F;
                         double s = 0.0;
                         for (int64_t f = 0; f < F; ++f) s += irow[f] * wrow[f];
-                        y64[p * D + n] = wf == 1 ? (double)(float)((float)s * sc) : (double)(float)s;
+                        if (fmt == 6)
+                            y64[p * D + n] = (double)(float)((float)s * (i_row_scales[p] * dn_tscale[(int64_t)e * D + n]));
+                        else
+                            y64[p * D + n] = wf == 1 ? (double)(float)((float)s * sc) : (double)(float)s;
                     }
                 }
             }

@@ -25,7 +25,7 @@ def test_oracle_pins_under_asan_and_ubsan(tmp_path):
     env = dict(os.environ, ORACLE_LIB=lib, LD_PRELOAD=f"{asan} {ubsan}", OMP_NUM_THREADS="4",
                ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="print_stacktrace=1")
     tests = [os.path.join(ROOT, "tests", f) for f in
-             ("test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_layer.py")]
+             ("test_oracle_formats.py", "test_oracle_quant.py", "test_oracle_layer.py", "test_oracle_fp8.py")]
     p = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", "-m", "not gpu",
                         *tests], cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert p.returncode == 0, p.stdout[-3000:] + p.stderr[-3000:]
