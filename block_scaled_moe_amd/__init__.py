@@ -21,7 +21,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4, "bf16": 5}  # w4a16: moe_forward only (NVFP4 weights)
+FMT = {"nvfp4": 1, "mxfp8": 2, "mxfp4": 3, "w4a16": 4, "bf16": 5, "fp8": 6}  # w4a16: moe_forward only (NVFP4 weights)
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape", -3: "alignment",
           -4: "workspace", -5: "HIP launch failed"}
 
@@ -124,7 +124,8 @@ class PackedWeights:
     [E][N/32][K/64][4][32][16] (the four 16-column quarters of a block apart), scales
     [E][N/32][K/64][32][4 | 2] (NVFP4 | MXFP8); MXFP4 keeps the two 32-column halves of
     a block apart, codes [E][N/32][K/64][2][32][16] and scales [E][N/32][K/64][2][32][1];
-    bf16 codes [E][N/32][K/64][2][32][64]."""
+    bf16 codes [E][N/32][K/64][2][32][64]; FP8 codes as MXFP8's, no block scales and the
+    channel scales in tensor_scale [E][N]."""
     fmt: str
     E: int
     N: int
@@ -139,7 +140,7 @@ class PackedWeights:
             fmt = "nvfp4"
         if fmt not in FMT or fmt == "w4a16":
             raise ValueError(f"unknown format {fmt!r}")
-        nv = fmt == "nvfp4"
+        nv, f8 = fmt == "nvfp4", fmt == "fp8"
         if N % 32 or K % 64:
             raise ValueError(f"packed weights need N % 32 == 0 and K % 64 == 0 (got N={N}, K={K})")
         if fmt == "bf16":  # bf16 values in the tile layout, no scales
@@ -148,12 +149,16 @@ class PackedWeights:
         elif fmt == "mxfp4":
             codes = torch.empty((E, N // 32, K // 64, 2, 32, 16), dtype=torch.uint8, device=device)
             scales = torch.empty((E, N // 32, K // 64, 2, 32, 1), dtype=torch.uint8, device=device)
+        elif f8:  # E4M3 codes in MXFP8's order; one fp32 scale per output channel
+            codes = torch.empty((E, N // 32, K // 64, 4, 32, 16), dtype=torch.uint8, device=device)
+            scales = torch.empty((E, 0), dtype=torch.uint8, device=device)
         else:
             codes = torch.empty((E, N // 32, K // 64, 4, 32, 16) if fmt == "mxfp8" else (E, N // 32, K // 64, 32, 32),
                                 dtype=torch.uint8,
                                 device=device)
             scales = torch.empty((E, N // 32, K // 64, 32, 4 if nv else 2), dtype=torch.uint8, device=device)
-        ts = torch.empty(E, dtype=torch.float32, device=device) if nv else None
+        ts = (torch.empty(E, dtype=torch.float32, device=device) if nv else
+              torch.empty((E, N), dtype=torch.float32, device=device) if f8 else None)
         return PackedWeights(fmt, E, N, K, codes, scales, ts)
 
     def experts(self, e0: int, e1: int) -> "PackedWeights":
@@ -193,8 +198,9 @@ def quantize_weights(fmt: str, w: torch.Tensor, out: PackedWeights | None = None
 def pack_weights(fmt: str, codes: torch.Tensor, scales: torch.Tensor | None = None,
                  tensor_scale: torch.Tensor | None = None, out: PackedWeights | None = None) -> PackedWeights:
     """Pre-quantised row-major weights (device tensors: codes [E, N, K/2] NVFP4 / MXFP4,
-    [E, N, K] MXFP8 (uint8) or bf16 (2-byte); scales [E, N, K/16 or K/32]; NVFP4 tensor
-    scales [E]) -> PackedWeights (moe_pack_weights); "w4a16" packs as NVFP4."""
+    [E, N, K] MXFP8 and FP8 (uint8) or bf16 (2-byte); scales [E, N, K/16 or K/32]; NVFP4
+    tensor scales [E], FP8 channel scales [E, N]) -> PackedWeights (moe_pack_weights);
+    "w4a16" packs as NVFP4."""
     if fmt == "w4a16":
         fmt = "nvfp4"
     E, N = codes.shape[0], codes.shape[1]
@@ -256,7 +262,8 @@ class Layer:
 
     def enable_taps(self):
         """Allocate every debug output of moe_forward (sized for S <= T*top_k). W4A16 has no
-        hidden-state codes and its intermediate codes are bf16 bit patterns (int16)."""
+        hidden-state codes and its intermediate codes are bf16 bit patterns (int16); FP8 has
+        row scales (a_tscale [T], inter_tscale [T*top_k]) instead of block scales."""
         T, D, F, k, n = self.T, self.D, self.F, self.top_k, self.e_end - self.e_begin
         nv, dev = self.fmt == "nvfp4", self.device
         TK = T * k
@@ -268,6 +275,9 @@ class Layer:
         }
         if self.fmt in ("w4a16", "bf16"):
             spec["inter_codes"] = ((TK, F), torch.int16)
+        elif self.fmt == "fp8":
+            spec.update({"a_codes": ((T, D), torch.uint8), "inter_codes": ((TK, F), torch.uint8),
+                         "a_tscale": ((T,), torch.float32), "inter_tscale": ((TK,), torch.float32)})
         else:
             spec.update({
                 "a_codes": ((T, D if self.fmt == "mxfp8" else D // 2), torch.uint8),

@@ -36,6 +36,11 @@
 //  - gate_up epilogue: SwiGLU in fp32, then each wave's rows x 32 tile goes through LDS and
 //    lane r quantises row r's 32-block to the layer's format (16- or 32-byte code store,
 //    one scale byte).
+// FP8 rows (ROWS; E4M3 with one fp32 scale per activation row and per weight channel, the
+// fp8 variant of the vLLM recipe "thinkingmachines/Inkling-Small") runs the FP8 kernel
+// with every E8M0 scale operand 127 (2^0) and no scale loads; its epilogues multiply the
+// sums by fl32(row scale * channel scale) (the row scales staged in LDS), and gate_up
+// writes the fp32 SwiGLU output, whose per-row scale needs the whole row (quant.hip).
 // Accumulator v of lane l is row 8(v/4) + 4(l/32) + v%4, column l%32.
 #include "formats.h"
 #include "gemm_common.h"
@@ -50,7 +55,10 @@ using namespace gemm_detail;
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128, kMS = kBM / 32, kNS = 2, kBN = 128 * kNS, kThreads = 256, kGroup = 4;
+#ifndef MOE_MX_GROUP
+#define MOE_MX_GROUP 4  // M-tiles per expert-major work group (gemm_common.h)
+#endif
+constexpr int kBM = 128, kMS = kBM / 32, kThreads = 256, kGroup = MOE_MX_GROUP;
 constexpr int kARow = 144;                     // LDS bytes per A row: 128 of codes + 16 (bank spread)
 constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [kBM rows][8]
 constexpr int kABuf = kACodes + kBM * 8;
@@ -62,9 +70,20 @@ constexpr int kEpiStride = 33;  // floats per row of a wave's SwiGLU tile (bank 
 #ifndef MOE_MX8_RING
 #define MOE_MX8_RING 2  // FP8 operands are twice as wide: a deeper ring spills at two waves per SIMD
 #endif
+#ifndef MOE_MX4_NS
+#define MOE_MX4_NS 2
+#endif
+#ifndef MOE_MX8_NS
+#define MOE_MX8_NS 2
+#endif
+#ifndef MOE_MX8_WAVES
+#define MOE_MX8_WAVES 2
+#endif
 
 // per-format constants: code bytes per row per 64-wide chunk, chunks per A group (128
-// code bytes per row), weight ring depth in chunks, bytes of one 32 x 64 weight block
+// code bytes per row), weight ring depth in chunks, bytes of one 32 x 64 weight block,
+// 32-row weight subtiles per wave (NS; a workgroup covers 128 NS weight rows) and the
+// waves per SIMD the register budget is set for
 template <bool FP8>
 struct Mx {
     static constexpr int CB = FP8 ? 64 : 32;
@@ -72,7 +91,11 @@ struct Mx {
     static constexpr int kRing = FP8 ? MOE_MX8_RING : MOE_MX4_RING;
     static constexpr int kCodeBlock = 32 * CB, kScaleBlock = 64;
     static constexpr int kFmt = FP8 ? 0 : 4;  // cbsz / blgp: E4M3 or E2M1 operands
+    static constexpr int NS = FP8 ? MOE_MX8_NS : MOE_MX4_NS;
+    static constexpr int kBN = 128 * NS;
+    static constexpr int kWaves = FP8 ? MOE_MX8_WAVES : 2;
     static_assert(kRing % kGrp == 0, "the B ring turns over whole A groups");
+    static_assert(NS % 2 == 0, "gate_up pairs subtiles");
 };
 
 __device__ __forceinline__ v8i operand(u32x4 lo, u32x4 hi) {
@@ -81,11 +104,13 @@ __device__ __forceinline__ v8i operand(u32x4 lo, u32x4 hi) {
 
 // NT: the weight code loads are marked non-temporal. At decode each (expert, weight row)
 // panel is read by a single M-tile, and a wave's load covers whole lines.
-template <bool FP8, bool GATE_UP, bool NT>
-__global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) {
+template <bool FP8, bool ROWS, bool GATE_UP, bool NT>
+__global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(const GemmArgs p) {
+    static_assert(FP8 || !ROWS, "row scales come with E4M3 codes");
     using X = Mx<FP8>;
     constexpr int kGrp = X::kGrp, kRing = X::kRing, kCodeBlock = X::kCodeBlock, kScaleBlock = X::kScaleBlock;
-    constexpr int kLds = (GATE_UP && 4 * kBM * kEpiStride * 4 > 2 * kABuf) ? 4 * kBM * kEpiStride * 4 : 2 * kABuf;
+    constexpr int kNS = X::NS, kBN = X::kBN;
+    constexpr int kLds = (GATE_UP && !ROWS && 4 * kBM * kEpiStride * 4 > 2 * kABuf) ? 4 * kBM * kEpiStride * 4 : 2 * kABuf;
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];  // A tiles; then the SwiGLU tiles
 
     const int K = p.K, N = p.N, F = N / 2;
@@ -110,7 +135,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
     const int64_t kb = K / 64;                  // 64-wide blocks per weight row group
     const int64_t row_bytes = FP8 ? K : K / 2;  // code bytes of one activation or weight row
     const uint8_t *wc_e = p.w_codes + (int64_t)e * N * row_bytes;
-    const uint8_t *ws_e = p.w_scales + (int64_t)e * N * (K / 32);
+    const uint8_t *ws_e = ROWS ? nullptr : p.w_scales + (int64_t)e * N * (K / 32);
 
     // ---- this lane's B operand rows (weights): the first of its (one or two) 16-byte
     // pieces of a chunk and its scale byte (MXFP4: half g2 at 512 g2, scale at 32 g2 +
@@ -121,14 +146,14 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
     for (int ns = 0; ns < kNS; ++ns) {
         int row;
         if (GATE_UP) {
-            const int col = nb * (kBN / 2) + wave * 32 + l32;
-            row = ns == 0 ? col : F + col;
+            const int col = nb * (kBN / 2) + wave * 16 * kNS + 32 * (ns % (kNS / 2)) + l32;
+            row = ns < kNS / 2 ? col : F + col;
         } else {
-            row = nb * kBN + wave * 64 + 32 * ns + l32;
+            row = nb * kBN + wave * 32 * kNS + 32 * ns + l32;
         }
         const int64_t blk0 = (int64_t)(row >> 5) * kb;
         bc[ns] = wc_e + blk0 * kCodeBlock + g2 * 512 + (row & 31) * 16;
-        bs[ns] = ws_e + blk0 * kScaleBlock + (FP8 ? 2 * (row & 31) + g2 : g2 * 32 + (row & 31));
+        bs[ns] = ROWS ? nullptr : ws_e + blk0 * kScaleBlock + (FP8 ? 2 * (row & 31) + g2 : g2 * 32 + (row & 31));
     }
     const int n_chunks = K / 64;
     const int n_groups = (n_chunks + kGrp - 1) / kGrp;
@@ -158,7 +183,8 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
         for (int q = 0; q < AQ; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * row_bytes;
         const uint8_t *sp[SQ];
 #pragma unroll
-        for (int q = 0; q < SQ; ++q) sp[q] = p.a_scales + a_row(SROWS * q + threadIdx.x / kGrp) * (K / 32);
+        for (int q = 0; q < SQ; ++q)
+            sp[q] = ROWS ? nullptr : p.a_scales + a_row(SROWS * q + threadIdx.x / kGrp) * (K / 32);
         u32x4 a_pf[AQ];
         uint32_t s_pf[SQ];
         auto a_load = [&](int g) {
@@ -167,20 +193,24 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
             const int off_ok = off < row_bytes ? off : 128 * g;
 #pragma unroll
             for (int q = 0; q < AQ; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
+            if constexpr (!ROWS) {
 #pragma unroll
-            for (int q = 0; q < SQ; ++q)
-                s_pf[q] = *reinterpret_cast<const uint16_t *>(sp[q] + 2 * min(kGrp * g + s_chunk, n_chunks - 1));
+                for (int q = 0; q < SQ; ++q)
+                    s_pf[q] = *reinterpret_cast<const uint16_t *>(sp[q] + 2 * min(kGrp * g + s_chunk, n_chunks - 1));
+            }
         };
         auto a_store = [&](int buf) {
             uint8_t *ab = lds + buf * kABuf;
 #pragma unroll
             for (int q = 0; q < AQ; ++q)
                 *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
+            if constexpr (!ROWS) {
 #pragma unroll
-            for (int q = 0; q < SQ; ++q) {
-                const int r = SROWS * q + threadIdx.x / kGrp;
-                if (SROWS * (q + 1) <= kBM || r < kBM)
-                    *reinterpret_cast<uint16_t *>(ab + kACodes + r * 8 + 2 * s_chunk) = (uint16_t)s_pf[q];
+                for (int q = 0; q < SQ; ++q) {
+                    const int r = SROWS * q + threadIdx.x / kGrp;
+                    if (SROWS * (q + 1) <= kBM || r < kBM)
+                        *reinterpret_cast<uint16_t *>(ab + kACodes + r * 8 + 2 * s_chunk) = (uint16_t)s_pf[q];
+                }
             }
         };
 
@@ -199,7 +229,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
                     else
                         breg[slot][ns][h] = *src;
                 }
-                bsc[slot][ns] = bs[ns][(int64_t)kScaleBlock * c];
+                bsc[slot][ns] = ROWS ? 127 : bs[ns][(int64_t)kScaleBlock * c];
             }
         };
         float16_t acc[MSA][kNS];
@@ -209,6 +239,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
             for (int j = 0; j < kNS; ++j) acc[i][j] = (float16_t){};
         uint32_t a_sc[MSA][2];
         auto a_scales = [&](int buf) {
+            if constexpr (ROWS) return;
             const uint8_t *ab = lds + buf * kABuf + kACodes;
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms) {
@@ -233,7 +264,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms) {
                 // scale byte of chunk j, block g2: byte 2 j + g2 of the row's scales
-                const int sa = (int)((a_sc[ms][j >> 1] >> (16 * (j & 1))) & 0xffu);
+                const int sa = ROWS ? 127 : (int)((a_sc[ms][j >> 1] >> (16 * (j & 1))) & 0xffu);
 #pragma unroll
                 for (int ns = 0; ns < kNS; ++ns) {
                     v8i bf;
@@ -293,44 +324,87 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
         }
 
         // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
-        if (GATE_UP) {
+        if constexpr (ROWS) {
+            // the tile's row scales through LDS (the A tiles are done with)
+            __syncthreads();
+            float *rs = reinterpret_cast<float *>(lds);
+            if (threadIdx.x < 32 * MSA) rs[threadIdx.x] = p.a_rscale[a_row(threadIdx.x)];
+            __syncthreads();
+            const float *ch = p.w_tscale + (int64_t)e * N;
+            if (GATE_UP) {
+#pragma unroll
+                for (int q = 0; q < kNS / 2; ++q) {
+                    const int col = nb * (kBN / 2) + wave * 16 * kNS + 32 * q + l32;
+                    const float cg = ch[col], cu = ch[F + col];
+#pragma unroll
+                    for (int ms = 0; ms < MSA; ++ms)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                            if (m < rows) {
+                                const float sr = rs[m];
+                                const float g = acc[ms][q][v] * (sr * cg), u = acc[ms][q + kNS / 2][v] * (sr * cu);
+                                p.out_f32[(int64_t)(p0 + m) * F + col] = swiglu(g, u);
+                            }
+                        }
+                }
+            } else {
+#pragma unroll
+                for (int ns = 0; ns < kNS; ++ns) {
+                    const int n = nb * kBN + wave * 32 * kNS + 32 * ns + l32;
+                    const float cn = ch[n];
+#pragma unroll
+                    for (int ms = 0; ms < MSA; ++ms)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) {
+                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                            if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = acc[ms][ns][v] * (rs[m] * cn);
+                        }
+                }
+            }
+        } else if (GATE_UP) {
             __syncthreads();  // the SwiGLU tiles reuse the A tiles' LDS
             float *we = reinterpret_cast<float *>(lds) + wave * kBM * kEpiStride;
 #pragma unroll
-            for (int ms = 0; ms < MSA; ++ms)
+            for (int q = 0; q < kNS / 2; ++q) {  // one 32-column block of the wave per pass
+                if (q) __builtin_amdgcn_wave_barrier();  // the previous block's reads first
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                    we[m * kEpiStride + l32] = swiglu(acc[ms][0][v], acc[ms][1][v]);
-                }
-            __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
-            const int fb = nb * (kBN / 2) + wave * 32;  // first column of this wave's block
+                for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
-            for (int m0 = 0; m0 < 32 * MSA; m0 += 64) {
-                const int m = m0 + lane;  // one row per lane
-                if (m < rows && m < 32 * MSA) {
-                    const int64_t row = p0 + m;
-                    float x[32];
-#pragma unroll
-                    for (int i = 0; i < 32; ++i) x[i] = we[m * kEpiStride + i];
-                    if constexpr (FP8) {
-                        uint32_t cw[8];
-                        const int sc = mxfp8_quant_block(x, cw);
-                        u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + fb);
-                        dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
-                        dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
-                        p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
-                    } else {
-                        uint32_t cw[4];
-                        const int sc = mxfp4_quant_block(x, cw);
-                        *reinterpret_cast<u32x4 *>(p.o_codes + row * (F / 2) + fb / 2) =
-                            (u32x4){cw[0], cw[1], cw[2], cw[3]};
-                        p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                        we[m * kEpiStride + l32] = swiglu(acc[ms][q][v], acc[ms][q + kNS / 2][v]);
                     }
-                    if (p.o_tap) {
-                        float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
+                __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+                const int fb = nb * (kBN / 2) + wave * 16 * kNS + 32 * q;  // first column of the block
 #pragma unroll
-                        for (int i = 0; i < 8; ++i) t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                for (int m0 = 0; m0 < 32 * MSA; m0 += 64) {
+                    const int m = m0 + lane;  // one row per lane
+                    if (m < rows && m < 32 * MSA) {
+                        const int64_t row = p0 + m;
+                        float x[32];
+#pragma unroll
+                        for (int i = 0; i < 32; ++i) x[i] = we[m * kEpiStride + i];
+                        if constexpr (FP8) {
+                            uint32_t cw[8];
+                            const int sc = mxfp8_quant_block(x, cw);
+                            u32x4 *dst = reinterpret_cast<u32x4 *>(p.o_codes + row * F + fb);
+                            dst[0] = (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                            dst[1] = (u32x4){cw[4], cw[5], cw[6], cw[7]};
+                            p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                        } else {
+                            uint32_t cw[4];
+                            const int sc = mxfp4_quant_block(x, cw);
+                            *reinterpret_cast<u32x4 *>(p.o_codes + row * (F / 2) + fb / 2) =
+                                (u32x4){cw[0], cw[1], cw[2], cw[3]};
+                            p.o_scales[row * (F / 32) + fb / 32] = (uint8_t)sc;
+                        }
+                        if (p.o_tap) {
+                            float4 *t = reinterpret_cast<float4 *>(p.o_tap + row * F + fb);
+#pragma unroll
+                            for (int i = 0; i < 8; ++i)
+                                t[i] = make_float4(x[4 * i], x[4 * i + 1], x[4 * i + 2], x[4 * i + 3]);
+                        }
                     }
                 }
             }
@@ -339,7 +413,7 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
             for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
                 for (int ns = 0; ns < kNS; ++ns) {
-                    const int n = nb * kBN + wave * 64 + 32 * ns + l32;
+                    const int n = nb * kBN + wave * 32 * kNS + 32 * ns + l32;
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
@@ -356,34 +430,39 @@ __global__ void __launch_bounds__(kThreads, 2) mx_gemm_kernel(const GemmArgs p) 
         run(std::integral_constant<int, kMS>{});
 }
 
-template <bool FP8, bool GATE_UP>
+template <bool FP8, bool ROWS, bool GATE_UP>
 void launch_t(const GemmArgs &a, bool stream_once, dim3 grid, hipStream_t s) {
     if (stream_once)
-        hipLaunchKernelGGL((mx_gemm_kernel<FP8, GATE_UP, true>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((mx_gemm_kernel<FP8, ROWS, GATE_UP, true>), grid, dim3(kThreads), 0, s, a);
     else
-        hipLaunchKernelGGL((mx_gemm_kernel<FP8, GATE_UP, false>), grid, dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((mx_gemm_kernel<FP8, ROWS, GATE_UP, false>), grid, dim3(kThreads), 0, s, a);
 }
 
 }  // namespace
 
 int32_t mx_gemm_bm() { return kBM; }
 
-bool mx_gemm_supported(int32_t K, int32_t N, bool gate_up) {
+bool mx_gemm_supported(bool fp8, int32_t K, int32_t N, bool gate_up) {
+    const int bn = fp8 ? Mx<true>::kBN : Mx<false>::kBN;
     if (K <= 0 || N <= 0 || K % 64) return false;
-    return gate_up ? (N % 2 == 0 && (N / 2) % (kBN / 2) == 0) : N % kBN == 0;
+    return gate_up ? (N % 2 == 0 && (N / 2) % (bn / 2) == 0) : N % bn == 0;
 }
 
-hipError_t launch_mx_gemm(const GemmArgs &a, bool fp8, bool gate_up, bool stream_once, int32_t max_tiles,
+hipError_t launch_mx_gemm(const GemmArgs &a, int mode, bool gate_up, bool stream_once, int32_t max_tiles,
                           hipStream_t s) {
-    const int64_t nb = gate_up ? (a.N / 2) / (kBN / 2) : a.N / kBN;
+    const int bn = mode != kMxFP4 ? Mx<true>::kBN : Mx<false>::kBN;
+    const int64_t nb = gate_up ? (a.N / 2) / (bn / 2) : a.N / bn;
     const int64_t items = (int64_t)max_tiles * nb;
     const dim3 grid((unsigned)((items + 7) / 8 * 8));
-    if (fp8) {
-        if (gate_up) launch_t<true, true>(a, stream_once, grid, s);
-        else launch_t<true, false>(a, stream_once, grid, s);
+    if (mode == kMxFP8Rows) {
+        if (gate_up) launch_t<true, true, true>(a, stream_once, grid, s);
+        else launch_t<true, true, false>(a, stream_once, grid, s);
+    } else if (mode == kMxFP8) {
+        if (gate_up) launch_t<true, false, true>(a, stream_once, grid, s);
+        else launch_t<true, false, false>(a, stream_once, grid, s);
     } else {
-        if (gate_up) launch_t<false, true>(a, stream_once, grid, s);
-        else launch_t<false, false>(a, stream_once, grid, s);
+        if (gate_up) launch_t<false, false, true>(a, stream_once, grid, s);
+        else launch_t<false, false, false>(a, stream_once, grid, s);
     }
     return hipGetLastError();
 }

@@ -16,16 +16,18 @@ struct Ctrl {
 };
 
 // Quantisation of the hidden states h [T][D] to the layer's format (act_quant.h): run by
-// its own launch or by extra workgroups of the permutation's first launch.
-constexpr int32_t kActNone = 0, kActNVFP4 = 1, kActMXFP8 = 2, kActMXFP4 = 3;
+// its own launch or by extra workgroups of the permutation's first launch. kActFP8 is E4M3
+// with one fp32 scale per token row, one wave per row; the others one thread per block.
+constexpr int32_t kActNone = 0, kActNVFP4 = 1, kActMXFP8 = 2, kActMXFP4 = 3, kActFP8 = 4;
 struct ActQuant {
     int32_t fmt;                // kAct*; kActNone: no job
     int32_t T, D;
     const uint16_t *h;          // bf16 [T][D]
     const uint32_t *amax_bits;  // NVFP4: max |h| (fp32 bits)
-    uint8_t *codes, *scales;    // [T][D/2] or [T][D]; [T][D/16] or [T][D/32]
+    uint8_t *codes, *scales;    // [T][D/2] or [T][D]; [T][D/16] or [T][D/32] (FP8: no scales)
     void *deq;                  // NVFP4: exact fp16 values [T][D]; MXFP8: exact bf16 values or NULL
     float *tscale_out;          // NVFP4: [1] the tensor scale
+    float *row_scales;          // FP8: [T] the row scales
 };
 // the job on its own launch
 hipError_t launch_act_quant(const ActQuant &q, hipStream_t s);
@@ -42,12 +44,19 @@ hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, i
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
 // bf16 weights copied into the packed tile layout (layout.h, 128 bytes per row slot)
 hipError_t launch_pack_weights_bf16(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes, hipStream_t s);
-// row-major pre-quantised codes and scales (fmt 1 NVFP4, 2 MXFP8, 3 MXFP4) into the packed
-// tile layout (layout.h); a pure byte reordering
+// row-major pre-quantised codes and scales (fmt 1 NVFP4, 2 MXFP8, 3 MXFP4; 6 FP8: codes
+// only, in the MXFP8 order) into the packed tile layout (layout.h); a pure byte reordering
 hipError_t launch_pack_rowmajor(int fmt, const uint8_t *src_codes, const uint8_t *src_scales, int32_t E, int32_t N,
                                 int32_t K, uint8_t *codes, uint8_t *scales, hipStream_t s);
 hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, int32_t K,
                                       uint8_t *codes, uint8_t *scales, hipStream_t s);
+// FP8 weights: E4M3 codes in the MXFP8 tile layout and one fp32 scale per output channel
+// (row), channel_scales [E][N]
+hipError_t launch_quant_weights_fp8(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
+                                    float *channel_scales, hipStream_t s);
+// FP8 intermediate: rows [0, ctrl->S) of x [*][F] fp32 -> E4M3 codes [S][F] and fp32 row scales [S]
+hipError_t launch_quant_inter_fp8(const float *x, int32_t max_rows, int32_t F, const Ctrl *ctrl, uint8_t *codes,
+                                  float *row_scales, hipStream_t s);
 // intermediate [rows <= ctrl->S][F] fp32 -> NVFP4 (tensor scale from ctrl->amax_i)
 hipError_t launch_quant_inter_nvfp4(const float *x, int32_t max_rows, int32_t F, const Ctrl *ctrl,
                                     uint8_t *codes, uint8_t *scales, _Float16 *deq, float *tscale_out,
@@ -116,11 +125,12 @@ struct GemmArgs {
     // MXFP4 A operand: the codes themselves, [rows][K/2] and E8M0 scales [rows][K/32]
     const uint8_t *a_codes, *a_scales;
     const float *a_tscale;    // NVFP4: [1] activation tensor scale
+    const float *a_rscale;    // FP8: fp32 scale of each A row, indexed like the a_codes rows
     // weights (canonical packed layout, global expert index)
     const uint8_t *w_codes, *w_scales;
-    const float *w_tscale;    // NVFP4 and W4A16: [E]
+    const float *w_tscale;    // NVFP4 and W4A16: [E]; FP8: [E][N] channel scales
     // outputs
-    float *out_f32;           // gate_up NVFP4: SwiGLU [S][F]; down: y [S][N]
+    float *out_f32;           // gate_up NVFP4 and FP8: SwiGLU [S][F]; down: y [S][N]
     uint32_t *amax_bits;      // gate_up NVFP4: max |SwiGLU|
     uint8_t *o_codes, *o_scales;  // gate_up MXFP8 / MXFP4: quantised SwiGLU [S][F] or [S][F/2], [S][F/32]
     void *o_vals;             // gate_up MXFP8: exact bf16 values of those codes [S][F]; W4A16: bf16 SwiGLU
@@ -139,15 +149,18 @@ hipError_t launch_tile_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max
 bool stream_gemm_supported(int32_t K, int32_t N, bool gate_up);
 hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t max_tiles, hipStream_t s);
 
-// MXFP4 and MXFP8 GEMMs on the gfx950 scaled MFMA with the codes and E8M0 scales as
-// stored (gemm_mx.hip): 128-row M-tiles (mx_gemm_bm), 256 weight rows per workgroup;
-// K % 64, gate_up F % 128, down N % 256. A operand: a_codes / a_scales; gate_up writes
-// o_codes / o_scales (and o_tap).
-bool mx_gemm_supported(int32_t K, int32_t N, bool gate_up);
+// MXFP4, MXFP8 and FP8 GEMMs on the gfx950 scaled MFMA with the codes (and E8M0 scales)
+// as stored (gemm_mx.hip): 128-row M-tiles (mx_gemm_bm), 128 NS weight rows per workgroup
+// (mx_gemm_supported checks K % 64 and the N-block fit); A operand: a_codes / a_scales
+// (FP8: a_codes / a_rscale). gate_up writes o_codes / o_scales (and o_tap); FP8 writes the
+// SwiGLU output to out_f32 for the row quantiser, its sums times fl32(row scale * channel
+// scale).
+constexpr int kMxFP4 = 0, kMxFP8 = 1, kMxFP8Rows = 2;
+bool mx_gemm_supported(bool fp8, int32_t K, int32_t N, bool gate_up);
 int32_t mx_gemm_bm();
-// fp8: MXFP8 (else MXFP4); stream_once: decode batches, where each weight panel is read
-// by one M-tile (non-temporal weight loads)
-hipError_t launch_mx_gemm(const GemmArgs &a, bool fp8, bool gate_up, bool stream_once, int32_t max_tiles,
+// mode: kMx*; stream_once: decode batches, where each weight panel is read by one M-tile
+// (non-temporal weight loads)
+hipError_t launch_mx_gemm(const GemmArgs &a, int mode, bool gate_up, bool stream_once, int32_t max_tiles,
                           hipStream_t s);
 
 // ---- combine (combine.hip)

@@ -34,7 +34,7 @@ constexpr int32_t kPrefillRowsPerExpert = 48;
 
 struct Plan {
     GemmShape shape;
-    bool scaled;  // MXFP4 / MXFP8 on the scaled MFMA with the codes as stored (gemm_mx.hip)
+    bool scaled;  // MXFP4 / MXFP8 / FP8 on the scaled MFMA with the codes as stored (gemm_mx.hip)
     bool tiled;   // prefill on the MFMA tile kernels (64- or 128-row M-tiles), or scaled
     int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
     size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
@@ -53,15 +53,19 @@ int gemm_fm(int32_t fmt) {
 Plan make_plan(const moe_forward_args *a) {
     Plan p{};
     const int64_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
-    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4, f8 = a->fmt == MOE_FMT_FP8;
     const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
+    const bool byte_codes = a->fmt == MOE_FMT_MXFP8 || f8;               // one code byte per value
     p.n_loc = a->e_end - a->e_begin;
     p.shape = (TK / a->E >= kPrefillRowsPerExpert) ? GemmShape::Prefill : GemmShape::Decode;
-    // MXFP4 always runs the scaled-FP4 MFMA kernels; MXFP8 the scaled-FP8 ones unless the
-    // caller asks for exact sums or the shape does not fit them
-    const bool mx_fit = mx_gemm_supported(a->D, 2 * a->F, true) && mx_gemm_supported(a->F, a->D, false);
-    p.scaled = mx4 || (a->fmt == MOE_FMT_MXFP8 && !(a->flags & MOE_FLAG_EXACT_SUMS) && mx_fit &&
-                       (p.shape == GemmShape::Prefill || MOE_MX8_DECODE_NATIVE));
+    // MXFP4 and FP8 always run the scaled MFMA kernels (validate_shape checks the fit);
+    // MXFP8 the scaled-FP8 ones unless the caller asks for exact sums or the shape does not
+    // fit them
+    const bool fp8 = byte_codes;
+    const bool mx_fit = mx_gemm_supported(fp8, a->D, 2 * a->F, true) && mx_gemm_supported(fp8, a->F, a->D, false);
+    p.scaled = mx4 || f8 ||
+               (a->fmt == MOE_FMT_MXFP8 && !(a->flags & MOE_FLAG_EXACT_SUMS) && mx_fit &&
+                (p.shape == GemmShape::Prefill || MOE_MX8_DECODE_NATIVE));
     p.tiled = p.scaled || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
                            tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
     p.bm = p.scaled ? mx_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
@@ -84,14 +88,14 @@ Plan make_plan(const moe_forward_args *a) {
     p.sorted_slot = take(sizeof(int32_t) * TK);
     p.slot_pos = take(sizeof(int32_t) * TK);
     // W4A16 and bf16 experts keep the hidden states as they are and the intermediate in
-    // bf16 (i16 only)
-    p.a_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? T * D : T * D / 2);
-    p.a_scales = a16 ? 0 : take(nv ? T * D / 16 : T * D / 32);
+    // bf16 (i16 only); FP8's scales are one fp32 per row
+    p.a_codes = a16 ? 0 : take(byte_codes ? T * D : T * D / 2);
+    p.a_scales = a16 ? 0 : take(f8 ? sizeof(float) * T : (nv ? T * D / 16 : T * D / 32));
     p.a_tscale = take(sizeof(float));
     p.a16 = (p.scaled || a16) ? 0 : take(2 * T * D);  // exact 16-bit values of the hidden-state codes
-    p.inter32 = nv ? take(sizeof(float) * TK * F) : 0;
-    p.i_codes = a16 ? 0 : take(a->fmt == MOE_FMT_MXFP8 ? TK * F : TK * F / 2);
-    p.i_scales = a16 ? 0 : take(nv ? TK * F / 16 : TK * F / 32);
+    p.inter32 = (nv || f8) ? take(sizeof(float) * TK * F) : 0;
+    p.i_codes = a16 ? 0 : take(byte_codes ? TK * F : TK * F / 2);
+    p.i_scales = a16 ? 0 : take(f8 ? sizeof(float) * TK : (nv ? TK * F / 16 : TK * F / 32));
     p.i_tscale = take(sizeof(float));
     p.i16 = p.scaled ? 0 : take(2 * TK * F);  // exact 16-bit values of the intermediate (codes)
     p.y = take(sizeof(float) * TK * D);
@@ -122,7 +126,8 @@ hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P,
     const int fm = gemm_fm(fmt);
     switch (gemm_kernel(P, g.K, g.N, gate_up)) {
         case Kernel::Scaled:
-            return launch_mx_gemm(g, fmt == MOE_FMT_MXFP8, gate_up, P.shape == GemmShape::Decode, P.max_tiles, s);
+            return launch_mx_gemm(g, fmt == MOE_FMT_MXFP8 ? kMxFP8 : (fmt == MOE_FMT_FP8 ? kMxFP8Rows : kMxFP4), gate_up,
+                                  P.shape == GemmShape::Decode, P.max_tiles, s);
         case Kernel::Tile: return launch_tile_gemm(g, fm, gate_up, P.max_tiles, s);
         case Kernel::Stream: return launch_stream_gemm(g, fm, gate_up, P.max_tiles, s);
         default: return launch_grouped_gemm(g, fm, gate_up, P.shape, P.max_tiles, s);
@@ -131,8 +136,9 @@ hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P,
 
 int32_t check_packed(const moe_packed &w, int32_t fmt, int32_t E, int32_t N, int32_t K) {
     if (w.fmt != fmt || w.E != E || w.N != N || w.K != K) return MOE_ERR_INVALID_ARG;
-    const bool need_scales = fmt != MOE_FMT_BF16;  // bf16 weights have none
-    if (!w.codes || (need_scales && !w.scales) || (fmt == MOE_FMT_NVFP4 && !w.tensor_scale)) return MOE_ERR_INVALID_ARG;
+    const bool need_scales = fmt != MOE_FMT_BF16 && fmt != MOE_FMT_FP8;  // bf16 and FP8 have no block scales
+    const bool need_tscale = fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_FP8;
+    if (!w.codes || (need_scales && !w.scales) || (need_tscale && !w.tensor_scale)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w.codes) || (w.scales && !aligned16(w.scales)) ||
         (w.tensor_scale && ((uintptr_t)w.tensor_scale & 3u)))
         return MOE_ERR_ALIGNMENT;
@@ -160,15 +166,19 @@ const char *moe_status_string(int32_t s) {
 int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
     if (!out || !w) return MOE_ERR_INVALID_ARG;
     const int32_t fmt = out->fmt, E = out->E, N = out->N, K = out->K;
-    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_BF16)
+    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_BF16 &&
+        fmt != MOE_FMT_FP8)
         return MOE_ERR_INVALID_ARG;
     if (E <= 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID_ARG;
     if (N % 32 || K % 64) return MOE_ERR_INVALID_ARG;  // tiled layout of include/moe.h
-    if (!out->codes || (fmt != MOE_FMT_BF16 && !out->scales) || (fmt == MOE_FMT_NVFP4 && !out->tensor_scale))
+    const bool need_scales = fmt != MOE_FMT_BF16 && fmt != MOE_FMT_FP8;
+    if (!out->codes || (need_scales && !out->scales) ||
+        ((fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_FP8) && !out->tensor_scale))
         return MOE_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(out->codes) || ((uintptr_t)out->tensor_scale & 3u)) return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
     if (fmt == MOE_FMT_BF16) return to_status(launch_pack_weights_bf16(w, E, N, K, out->codes, s));
+    if (fmt == MOE_FMT_FP8) return to_status(launch_quant_weights_fp8(w, E, N, K, out->codes, out->tensor_scale, s));
     if (fmt == MOE_FMT_MXFP8)
         return to_status(launch_quant_weights_mxfp8(w, E, N, K, out->codes, out->scales, s));
     if (fmt == MOE_FMT_MXFP4)
@@ -183,22 +193,28 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream) {
 int32_t moe_pack_weights(const moe_rowmajor *in, moe_packed *out, void *stream) {
     if (!in || !out) return MOE_ERR_INVALID_ARG;
     const int32_t fmt = in->fmt, E = in->E, N = in->N, K = in->K;
-    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_BF16)
+    if (fmt != MOE_FMT_NVFP4 && fmt != MOE_FMT_MXFP8 && fmt != MOE_FMT_MXFP4 && fmt != MOE_FMT_BF16 &&
+        fmt != MOE_FMT_FP8)
         return MOE_ERR_INVALID_ARG;
     if (out->fmt != fmt || out->E != E || out->N != N || out->K != K) return MOE_ERR_INVALID_ARG;
     if (E <= 0 || N <= 0 || K <= 0 || N % 32 || K % 64) return MOE_ERR_INVALID_ARG;
-    const bool scaled = fmt != MOE_FMT_BF16, nv = fmt == MOE_FMT_NVFP4;
+    const bool scaled = fmt != MOE_FMT_BF16 && fmt != MOE_FMT_FP8;  // block scales to move
+    const bool ts = fmt == MOE_FMT_NVFP4 || fmt == MOE_FMT_FP8;      // tensor / channel scales to copy
     if (!in->codes || !out->codes || (scaled && (!in->scales || !out->scales)) ||
-        (nv && (!in->tensor_scale || !out->tensor_scale)))
+        (ts && (!in->tensor_scale || !out->tensor_scale)))
         return MOE_ERR_INVALID_ARG;
-    if (!aligned16(in->codes) || !aligned16(out->codes) || (out->scales && !aligned16(out->scales)) ||
-        (nv && (((uintptr_t)in->tensor_scale | (uintptr_t)out->tensor_scale) & 3u)))
+    if (!aligned16(in->codes) || !aligned16(out->codes) || (scaled && !aligned16(out->scales)) ||
+        (ts && (((uintptr_t)in->tensor_scale | (uintptr_t)out->tensor_scale) & 3u)))
         return MOE_ERR_ALIGNMENT;
     hipStream_t s = (hipStream_t)stream;
-    if (!scaled)
+    if (fmt == MOE_FMT_BF16)
         return to_status(launch_pack_weights_bf16(reinterpret_cast<const uint16_t *>(in->codes), E, N, K, out->codes, s));
-    MOE_TRY(launch_pack_rowmajor(fmt, in->codes, in->scales, E, N, K, out->codes, out->scales, s));
-    if (nv) MOE_TRY(hipMemcpyAsync(out->tensor_scale, in->tensor_scale, sizeof(float) * E, hipMemcpyDeviceToDevice, s));
+    MOE_TRY(launch_pack_rowmajor(fmt, in->codes, scaled ? in->scales : nullptr, E, N, K, out->codes,
+                                 scaled ? out->scales : nullptr, s));
+    if (ts) {
+        const size_t n = fmt == MOE_FMT_FP8 ? (size_t)E * N : (size_t)E;  // FP8: one per channel
+        MOE_TRY(hipMemcpyAsync(out->tensor_scale, in->tensor_scale, sizeof(float) * n, hipMemcpyDeviceToDevice, s));
+    }
     return MOE_OK;
 }
 
@@ -233,7 +249,7 @@ namespace {
 int32_t validate_shape(const moe_forward_args *a) {
     if (!a) return MOE_ERR_INVALID_ARG;
     if (a->fmt != MOE_FMT_NVFP4 && a->fmt != MOE_FMT_MXFP8 && a->fmt != MOE_FMT_MXFP4 && a->fmt != MOE_FMT_W4A16 &&
-        a->fmt != MOE_FMT_BF16)
+        a->fmt != MOE_FMT_BF16 && a->fmt != MOE_FMT_FP8)
         return MOE_ERR_INVALID_ARG;
     if (a->T < 0 || a->D <= 0 || a->F <= 0 || a->E <= 0 || a->E > 4096) return MOE_ERR_INVALID_ARG;
     if (a->top_k < 1 || a->top_k > 8 || a->top_k > a->E) return MOE_ERR_INVALID_ARG;
@@ -242,7 +258,12 @@ int32_t validate_shape(const moe_forward_args *a) {
     if (a->D % 128 || a->F % 128) return MOE_ERR_UNSUPPORTED;
     if (a->flags & ~(uint32_t)MOE_FLAG_EXACT_SUMS) return MOE_ERR_INVALID_ARG;
     if (a->fmt == MOE_FMT_MXFP4 &&
-        !(mx_gemm_supported(a->D, 2 * a->F, true) && mx_gemm_supported(a->F, a->D, false)))
+        !(mx_gemm_supported(false, a->D, 2 * a->F, true) && mx_gemm_supported(false, a->F, a->D, false)))
+        return MOE_ERR_UNSUPPORTED;
+    // FP8 runs on the scaled FP8 MFMA only (no exact-sum route)
+    if (a->fmt == MOE_FMT_FP8 &&
+        ((a->flags & MOE_FLAG_EXACT_SUMS) ||
+         !(mx_gemm_supported(true, a->D, 2 * a->F, true) && mx_gemm_supported(true, a->F, a->D, false))))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -298,7 +319,7 @@ namespace {
 // The launch sequence of one forward call on the validated arguments `a` with the plan P
 // and P.total bytes of device workspace at ws (256-byte aligned).
 int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipStream_t s) {
-    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4;
+    const bool nv = a->fmt == MOE_FMT_NVFP4, mx4 = a->fmt == MOE_FMT_MXFP4, f8 = a->fmt == MOE_FMT_FP8;
     const bool a16 = a->fmt == MOE_FMT_W4A16 || a->fmt == MOE_FMT_BF16;  // bf16 activations
     const int32_t T = a->T, D = a->D, F = a->F, k = a->top_k, TK = T * k;
     Ctrl *ctrl = reinterpret_cast<Ctrl *>(ws + P.ctrl);
@@ -335,17 +356,19 @@ int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipSt
 
     // 2. hidden states quantised once per token (W4A16 and bf16 experts read them as they
     // are): NVFP4 with one tensor scale over all of h from the router's max |h|; MXFP8
-    // also writes its exact bf16 values for the exact route. The job rides in extra
-    // workgroups of the permutation's first launch; without the router's max |h| an
-    // NVFP4 layer takes an amax pass after the permutation and quantises on its own.
+    // also writes its exact bf16 values for the exact route; FP8 one scale per token row.
+    // The job rides in extra workgroups of the permutation's first launch; without the
+    // router's max |h| an NVFP4 layer takes an amax pass after the permutation and
+    // quantises on its own.
     ActQuant q{};
-    q.fmt = nv ? kActNVFP4 : (mx4 ? kActMXFP4 : (a16 ? kActNone : kActMXFP8));
+    q.fmt = nv ? kActNVFP4 : (mx4 ? kActMXFP4 : (a16 ? kActNone : (f8 ? kActFP8 : kActMXFP8)));
     q.T = T;
     q.D = D;
     q.h = a->h;
     q.amax_bits = nv ? (a->h_amax ? reinterpret_cast<const uint32_t *>(a->h_amax) : &ctrl->amax_a) : nullptr;
     q.codes = a16 ? nullptr : U8(P.a_codes);
-    q.scales = a16 ? nullptr : U8(P.a_scales);
+    q.scales = (a16 || f8) ? nullptr : U8(P.a_scales);
+    q.row_scales = f8 ? F32(P.a_scales) : nullptr;
     q.deq = nv ? static_cast<void *>(F16(P.a16)) : ((mx4 || a16 || P.scaled) ? nullptr : static_cast<void *>(ws + P.a16));
     q.tscale_out = nv ? F32(P.a_tscale) : nullptr;
     const bool carried = !(nv && !a->h_amax);
@@ -373,8 +396,16 @@ int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipSt
     g.w_tscale = a->gate_up.tensor_scale;
     g.a_vals = P.scaled ? nullptr : (a16 ? static_cast<const void *>(a->h) : ws + P.a16);
     g.a_codes = a16 ? nullptr : U8(P.a_codes);
-    g.a_scales = a16 ? nullptr : U8(P.a_scales);
-    if (nv) {
+    g.a_scales = (a16 || f8) ? nullptr : U8(P.a_scales);
+    g.a_rscale = f8 ? F32(P.a_scales) : nullptr;
+    if (f8) {
+        g.out_f32 = F32(P.inter32);
+        MOE_TRY(mark(MOE_EV_GATE_UP));
+        MOE_TRY(run_gemm(g, a->fmt, true, P, s));
+        MOE_TRY(mark(MOE_EV_GATE_UP_END));
+        // 4. FP8 intermediate: one scale per slot row
+        MOE_TRY(launch_quant_inter_fp8(F32(P.inter32), TK, F, ctrl, U8(P.i_codes), F32(P.i_scales), s));
+    } else if (nv) {
         g.a_tscale = F32(P.a_tscale);
         g.out_f32 = F32(P.inter32);
         g.amax_bits = &ctrl->amax_i;
@@ -410,7 +441,8 @@ int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipSt
     d.o_vals = nullptr;
     d.a_vals = P.scaled ? nullptr : ws + P.i16;
     d.a_codes = a16 ? nullptr : U8(P.i_codes);
-    d.a_scales = a16 ? nullptr : U8(P.i_scales);
+    d.a_scales = (a16 || f8) ? nullptr : U8(P.i_scales);
+    d.a_rscale = f8 ? F32(P.i_scales) : nullptr;
     d.a_tscale = nv ? F32(P.i_tscale) : nullptr;
     MOE_TRY(mark(MOE_EV_DOWN));
     MOE_TRY(run_gemm(d, a->fmt, false, P, s));
@@ -429,21 +461,23 @@ int32_t run_forward(const moe_forward_args *a, const Plan &P, uint8_t *ws, hipSt
         MOE_TRY(cp(t->counts, ws + P.counts, sizeof(int32_t) * P.n_loc));
         MOE_TRY(cp(t->offsets, ws + P.offsets, sizeof(int32_t) * (P.n_loc + 1)));
         MOE_TRY(cp(t->sorted_slot, ws + P.sorted_slot, sizeof(int32_t) * (size_t)TK));
-        const bool mx8 = a->fmt == MOE_FMT_MXFP8;
-        if (!a16) {
-            MOE_TRY(cp(t->a_codes, ws + P.a_codes, mx8 ? (size_t)T * D : (size_t)T * D / 2));
-            MOE_TRY(cp(t->a_scales, ws + P.a_scales, nv ? (size_t)T * D / 16 : (size_t)T * D / 32));
-        }
+        const bool b8 = a->fmt == MOE_FMT_MXFP8 || f8;  // one code byte per value
+        if (!a16) MOE_TRY(cp(t->a_codes, ws + P.a_codes, b8 ? (size_t)T * D : (size_t)T * D / 2));
+        if (!a16 && !f8) MOE_TRY(cp(t->a_scales, ws + P.a_scales, nv ? (size_t)T * D / 16 : (size_t)T * D / 32));
         if (nv) {
             MOE_TRY(cp(t->a_tscale, ws + P.a_tscale, sizeof(float)));
-            MOE_TRY(cp(t->inter, ws + P.inter32, sizeof(float) * (size_t)TK * F));
             MOE_TRY(cp(t->inter_tscale, ws + P.i_tscale, sizeof(float)));
         }
+        if (f8) {  // the row scales
+            MOE_TRY(cp(t->a_tscale, ws + P.a_scales, sizeof(float) * (size_t)T));
+            MOE_TRY(cp(t->inter_tscale, ws + P.i_scales, sizeof(float) * (size_t)TK));
+        }
+        if (nv || f8) MOE_TRY(cp(t->inter, ws + P.inter32, sizeof(float) * (size_t)TK * F));
         if (a16) {
             MOE_TRY(cp(t->inter_codes, ws + P.i16, 2 * (size_t)TK * F));  // bf16 bit patterns
         } else {
-            MOE_TRY(cp(t->inter_codes, ws + P.i_codes, mx8 ? (size_t)TK * F : (size_t)TK * F / 2));
-            MOE_TRY(cp(t->inter_scales, ws + P.i_scales, nv ? (size_t)TK * F / 16 : (size_t)TK * F / 32));
+            MOE_TRY(cp(t->inter_codes, ws + P.i_codes, b8 ? (size_t)TK * F : (size_t)TK * F / 2));
+            if (!f8) MOE_TRY(cp(t->inter_scales, ws + P.i_scales, nv ? (size_t)TK * F / 16 : (size_t)TK * F / 32));
         }
         MOE_TRY(cp(t->y, ws + P.y, sizeof(float) * (size_t)TK * D));
     }

@@ -25,16 +25,14 @@ namespace {
 // the two jobs share no data, so the launch costs the longer of them instead of both
 // plus a launch boundary).
 __device__ __forceinline__ void carried_quant(const ActQuant &q, int first) {
-    const int64_t n = act_quant_blocks(q);
-    const int64_t stride = (int64_t)(gridDim.x - first) * blockDim.x;
-    for (int64_t b = (int64_t)(blockIdx.x - first) * blockDim.x + threadIdx.x; b < n; b += stride)
-        act_quant_block(q, b);
+    act_quant_range(q, (int64_t)(blockIdx.x - first) * blockDim.x + threadIdx.x, (int64_t)(gridDim.x - first) * blockDim.x);
 }
 
 // workgroups of a permutation launch given to the quantisation job
 inline int32_t quant_groups(const ActQuant &q, int threads) {
     if (q.fmt == kActNone) return 0;
-    const int64_t g = (act_quant_blocks(q) + threads - 1) / threads;
+    const int units = threads / act_quant_unit_threads(q);
+    const int64_t g = (act_quant_blocks(q) + units - 1) / units;
     return (int32_t)(g < 1 ? 1 : (g > 2048 ? 2048 : g));
 }
 

@@ -163,10 +163,44 @@ __global__ void __launch_bounds__(kThreads) quant_mxfp4_bf16_kernel(const uint16
     }
 }
 
-// Hidden states to the layer's format, one thread per block (act_quant.h).
-__global__ void __launch_bounds__(kThreads) act_quant_kernel(const ActQuant q, int64_t n_blocks) {
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x)
-        act_quant_block(q, b);
+// FP8 weights (the fp8 variant of the vLLM recipe "thinkingmachines/Inkling-Small"): one
+// wave per output channel (row n of expert e) of the bf16 masters [E][N][K]: the channel
+// scale fl32(max |w| / 448) into channel_scales[e][n] and the E4M3 codes, each 16-column
+// piece to its place in the MXFP8 tile layout (layout.h).
+__global__ void __launch_bounds__(kThreads) quant_w_fp8_kernel(const uint16_t *__restrict__ w, int64_t n_rows,
+                                                               int32_t N, int32_t K, uint8_t *__restrict__ codes,
+                                                               float *__restrict__ channel_scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t waves = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < n_rows; r += waves) {
+        const int64_t e = r / N, n = r - e * N;
+        uint8_t *ce = codes + e * N * (int64_t)K;
+        const float s = fp8_row_quant(w + r * K, K, lane, [&](int i, uint4 c) {
+            *reinterpret_cast<uint4 *>(ce + layout::code_offset(false, K, n, 16 * (int64_t)i)) = c;
+        });
+        if (lane == 0) channel_scales[r] = s;
+    }
+}
+
+// FP8 SwiGLU intermediate: rows [0, S) of x [*][F] fp32, one wave per row: codes [S][F]
+// row-major and the row scales [S].
+__global__ void __launch_bounds__(kThreads) quant_inter_fp8_kernel(const float *__restrict__ x, int32_t F,
+                                                                   const Ctrl *__restrict__ ctrl,
+                                                                   uint8_t *__restrict__ codes,
+                                                                   float *__restrict__ row_scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t n_rows = ctrl->S, waves = (int64_t)gridDim.x * (kThreads / 64);
+    for (int64_t r = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6); r < n_rows; r += waves) {
+        uint8_t *dst = codes + r * F;
+        const float s = fp8_row_quant(x + r * F, F, lane, [&](int i, uint4 c) { reinterpret_cast<uint4 *>(dst)[i] = c; });
+        if (lane == 0) row_scales[r] = s;
+    }
+}
+
+// Hidden states to the layer's format, one thread per block or one wave per FP8 row
+// (act_quant.h).
+__global__ void __launch_bounds__(kThreads) act_quant_kernel(const ActQuant q) {
+    act_quant_range(q, (int64_t)blockIdx.x * blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
 }
 
 // NVFP4 SwiGLU intermediate: rows [0, S) of x [*][F] fp32, one tensor scale over
@@ -250,17 +284,18 @@ hipError_t launch_quant_weights_mxfp8(const uint16_t *w, int32_t E, int32_t N, i
     return hipGetLastError();
 }
 
-// Row-major pre-quantised weights (codes [E][N][K/2] NVFP4 and MXFP4, [E][N][K] MXFP8;
-// scales [E][N][K/16] or [E][N][K/32]) into the packed tile layout: one thread per
+// Row-major pre-quantised weights (codes [E][N][K/2] NVFP4 and MXFP4, [E][N][K] MXFP8 and
+// FP8; scales [E][N][K/16] or [E][N][K/32]) into the packed tile layout: one thread per
 // quantisation block in storage order, the same mapping the quantisers write (layout.h).
-// fmt: 1 NVFP4, 2 MXFP8, 3 MXFP4 (the MOE_FMT_* values).
+// fmt: 1 NVFP4, 2 MXFP8, 3 MXFP4, 6 FP8 (the MOE_FMT_* values; FP8 has no block scales and
+// moves its codes in MXFP8's 32-value pieces).
 __global__ void __launch_bounds__(kThreads) pack_rowmajor_kernel(int fmt, const uint8_t *__restrict__ src_codes,
                                                                  const uint8_t *__restrict__ src_scales,
                                                                  int64_t n_blocks, int64_t blocks_per_expert,
                                                                  int32_t K, uint8_t *__restrict__ codes,
                                                                  uint8_t *__restrict__ scales) {
-    const int blk = fmt == 1 ? 16 : 32;              // values per quantisation block
-    const int64_t row_bytes = fmt == 2 ? K : K / 2;  // code bytes per weight row
+    const int blk = fmt == 1 ? 16 : 32;                          // values per quantisation block
+    const int64_t row_bytes = (fmt == 2 || fmt == 6) ? K : K / 2;  // code bytes per weight row
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < n_blocks; b += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e = b / blocks_per_expert, r = b - e * blocks_per_expert;
         int64_t n, k;
@@ -269,7 +304,7 @@ __global__ void __launch_bounds__(kThreads) pack_rowmajor_kernel(int fmt, const 
         else
             layout::block_source(fmt == 1, K, r, n, k);
         const int64_t row = e * (blocks_per_expert / (K / blk)) + n;  // weight row over all experts
-        const uint8_t *src = src_codes + row * row_bytes + (fmt == 2 ? k : k / 2);
+        const uint8_t *src = src_codes + row * row_bytes + ((fmt == 2 || fmt == 6) ? k : k / 2);
         if (fmt == 1) {
             reinterpret_cast<uint2 *>(codes)[b] = *reinterpret_cast<const uint2 *>(src);
         } else if (fmt == 3) {
@@ -280,7 +315,7 @@ __global__ void __launch_bounds__(kThreads) pack_rowmajor_kernel(int fmt, const 
             *reinterpret_cast<uint4 *>(ce + layout::code_offset(false, K, n, k + 16)) =
                 *reinterpret_cast<const uint4 *>(src + 16);
         }
-        scales[b] = src_scales[row * (K / blk) + k / blk];
+        if (fmt != 6) scales[b] = src_scales[row * (K / blk) + k / blk];
     }
 }
 
@@ -329,7 +364,22 @@ hipError_t launch_quant_weights_mxfp4(const uint16_t *w, int32_t E, int32_t N, i
 hipError_t launch_act_quant(const ActQuant &q, hipStream_t s) {
     const int64_t nb = act_quant_blocks(q);
     if (q.fmt == kActNone || nb == 0) return hipSuccess;
-    hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(nb)), dim3(kThreads), 0, s, q, nb);
+    hipLaunchKernelGGL(act_quant_kernel, dim3(grid_for(nb * act_quant_unit_threads(q))), dim3(kThreads), 0, s, q);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_weights_fp8(const uint16_t *w, int32_t E, int32_t N, int32_t K, uint8_t *codes,
+                                    float *channel_scales, hipStream_t s) {
+    const int64_t rows = (int64_t)E * N;
+    hipLaunchKernelGGL(quant_w_fp8_kernel, dim3(grid_for(rows * 64)), dim3(kThreads), 0, s, w, rows, N, K, codes,
+                       channel_scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_inter_fp8(const float *x, int32_t max_rows, int32_t F, const Ctrl *ctrl, uint8_t *codes,
+                                  float *row_scales, hipStream_t s) {
+    hipLaunchKernelGGL(quant_inter_fp8_kernel, dim3(grid_for((int64_t)max_rows * 64, 4096)), dim3(kThreads), 0, s, x,
+                       F, ctrl, codes, row_scales);
     return hipGetLastError();
 }
 

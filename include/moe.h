@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 7
+#define MOE_ABI_VERSION 8
 
 /* Status codes (0 = success). */
 #define MOE_OK 0
@@ -53,12 +53,17 @@ extern "C" {
  * run with bf16 activations, its weights dequantised on the fly, same section).
  * MOE_FMT_W4A16 is a moe_forward format only: its packed weights are MOE_FMT_NVFP4.
  * MOE_FMT_BF16 is the checkpoint's BF16 variant (same section): bf16 weights and
- * activations, fp32 accumulation, the SwiGLU output rounded to bf16. */
+ * activations, fp32 accumulation, the SwiGLU output rounded to bf16.
+ * MOE_FMT_FP8 is the FP8 variant of the same recipe (E4M3 with dynamic per-token
+ * activation quantisation), read here as: E4M3 weights with one fp32 scale per output
+ * channel, hidden states and the SwiGLU output E4M3 with one fp32 scale per row computed
+ * at run time; every scale is fl32(max |row| / 448), 1 for an all-zero row. */
 #define MOE_FMT_NVFP4 1
 #define MOE_FMT_MXFP8 2
 #define MOE_FMT_MXFP4 3
 #define MOE_FMT_W4A16 4
 #define MOE_FMT_BF16 5
+#define MOE_FMT_FP8 6
 
 /*
  * Packed expert weights of one matrix kind for E experts, each logically [N][K]
@@ -80,6 +85,9 @@ extern "C" {
  *   BF16:  codes  u8 [E][N/32][K/64][2][32][64] bf16 values, the two 32-column halves
  *          of a block apart (column 32h + c at bytes 2c, 2c+1 of half h)
  *          scales, tensor_scale unused (may be NULL)
+ *   FP8:   codes  u8 [E][N/32][K/64][4][32][16] E4M3, MXFP8's order
+ *          scales unused (may be NULL)
+ *          tensor_scale fp32 [E][N]  one per output channel (row): max |row| / 448, or 1
  * Sizes are those of the row-major arrays ([E][N][K/2] (NVFP4, MXFP4) / [E][N][K]
  * (MXFP8) codes, [E][N][K/16] (NVFP4) / [E][N][K/32] (MXFP8, MXFP4) scales); only the
  * order differs. The tiling lets one wave of the
@@ -102,7 +110,8 @@ typedef struct moe_packed {
  *          scales [E][N][K/16] E4M3; tensor_scale fp32 [E]
  *   MXFP8: codes [E][N][K] E4M3; scales [E][N][K/32] E8M0; tensor_scale NULL
  *   MXFP4: codes [E][N][K/2] E2M1 (as NVFP4); scales [E][N][K/32] E8M0
- *   BF16:  codes [E][N][K] bf16 values (2 bytes each); scales, tensor_scale NULL */
+ *   BF16:  codes [E][N][K] bf16 values (2 bytes each); scales, tensor_scale NULL
+ *   FP8:   codes [E][N][K] E4M3; scales NULL; tensor_scale fp32 [E][N] channel scales */
 typedef struct moe_rowmajor {
     int32_t fmt;
     int32_t E, N, K;
@@ -119,14 +128,16 @@ typedef struct moe_taps {
     int32_t *offsets;      /* [n_loc + 1] exclusive prefix sum of counts            */
     int32_t *sorted_slot;  /* [T*top_k] slot id t*top_k + j at each sorted position  */
     uint8_t *a_codes;      /* hidden-state codes [T][D/2] (NVFP4, MXFP4) or [T][D]
-                              (MXFP8); W4A16 writes neither these nor a_scales     */
-    uint8_t *a_scales;     /* [T][D/16] E4M3 (NVFP4) or [T][D/32] E8M0 (MX formats) */
-    float *a_tscale;       /* [1] NVFP4 hidden-state tensor scale                   */
+                              (MXFP8, FP8); W4A16 writes neither these nor a_scales */
+    uint8_t *a_scales;     /* [T][D/16] E4M3 (NVFP4) or [T][D/32] E8M0 (MX formats);
+                              FP8 writes none                                      */
+    float *a_tscale;       /* [1] NVFP4 hidden-state tensor scale; FP8: [T] row scales */
     float *inter;          /* [T*top_k][F] fp32 SwiGLU output before quantisation   */
-    uint8_t *inter_codes;  /* [T*top_k][F/2] (NVFP4, MXFP4) or [T*top_k][F] (MXFP8);
-                              W4A16: bf16 bit patterns [T*top_k][F], 2 bytes each */
-    uint8_t *inter_scales; /* [T*top_k][F/16] (NVFP4) or [T*top_k][F/32]            */
-    float *inter_tscale;   /* [1] NVFP4 intermediate tensor scale                   */
+    uint8_t *inter_codes;  /* [T*top_k][F/2] (NVFP4, MXFP4) or [T*top_k][F] (MXFP8,
+                              FP8); W4A16: bf16 bit patterns [T*top_k][F], 2 bytes */
+    uint8_t *inter_scales; /* [T*top_k][F/16] (NVFP4) or [T*top_k][F/32]; FP8: none  */
+    float *inter_tscale;   /* [1] NVFP4 intermediate tensor scale; FP8: [T*top_k] row
+                              scales in sorted order                               */
     float *y;              /* [T*top_k][D] fp32 down projection per slot (unweighted) */
 } moe_taps;
 
@@ -136,7 +147,8 @@ typedef struct moe_taps {
  *   sum of |products| over K = 4096) instead of the gfx950 scaled FP8 MFMA on the codes
  *   and E8M0 scales as stored (twice the multiply rate; its sums are within about 2e-6 of
  *   the sum of |products|, so intermediate codes on a rounding boundary take the
- *   neighbouring code about 100 times as often). Other formats ignore it. */
+ *   neighbouring code about 100 times as often). FP8 layers run on the scaled FP8 MFMA
+ *   only and reject the flag (MOE_ERR_UNSUPPORTED). Other formats ignore it. */
 #define MOE_FLAG_EXACT_SUMS 1u
 
 /* Stage boundaries at which moe_forward records caller-created events (timing). */
@@ -150,7 +162,7 @@ typedef struct moe_taps {
 
 /* Arguments of moe_forward. */
 typedef struct moe_forward_args {
-    int32_t fmt;              /* MOE_FMT_NVFP4, _MXFP8, _MXFP4, _W4A16 or _BF16         */
+    int32_t fmt;              /* MOE_FMT_NVFP4, _MXFP8, _MXFP4, _W4A16, _BF16 or _FP8   */
     int32_t T, D, F, E;       /* tokens, d_model, d_ff, routed experts                  */
     int32_t top_k;            /* experts per token (8)                                  */
     int32_t e_begin, e_end;   /* local expert range [e_begin, e_end) computed here      */
@@ -191,8 +203,10 @@ const char *moe_status_string(int32_t status);
  * candidates E4M3(r/6) and E4M3(r/4), codes E2M1(x / (E4M3 * s)), keep the candidate
  * with the smaller fp32 squared error (ties keep r/6). MXFP8: per 32-block, E8M0
  * exponent floor(log2 amax_b) - 8, codes E4M3(x * 2^-exponent). MXFP4: per 32-block,
- * E8M0 exponent floor(log2 amax_b) - 2, codes E2M1(x * 2^-exponent). All roundings are
- * IEEE round-to-nearest-even with saturation to the format's largest finite value.
+ * E8M0 exponent floor(log2 amax_b) - 2, codes E2M1(x * 2^-exponent). FP8: per output
+ * channel (row), scale s = fl32(amax_row / 448) (1 for an all-zero row) into
+ * tensor_scale[e][n], codes E4M3(fl32(x / s)). All roundings are IEEE
+ * round-to-nearest-even with saturation to the format's largest finite value.
  * N must be a multiple of 32 and K of 64 (the tiled layout above).
  */
 int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
@@ -203,9 +217,10 @@ int32_t moe_quantize_weights(const uint16_t *w, moe_packed *out, void *stream);
  * MXFP8 checkpoint) into the tiled layout of `out` (fmt, E, N, K equal to in's; buffers
  * set by the caller): a pure reordering of the code and scale bytes, the tensor scales
  * copied. The bytes moe_quantize_weights writes for bf16 masters are the packing of the
- * row-major quantisation of the same masters. N % 32 == 0 and K % 64 == 0; in->codes and
- * out's code and scale buffers 16-byte aligned (MOE_ERR_ALIGNMENT), tensor scales
- * 4-byte aligned. `in` and `out` must not overlap.
+ * row-major quantisation of the same masters (FP8: codes reordered, the E*N channel
+ * scales copied). N % 32 == 0 and K % 64 == 0; in->codes and out's code and scale
+ * buffers 16-byte aligned (MOE_ERR_ALIGNMENT), tensor scales 4-byte aligned. `in` and
+ * `out` must not overlap.
  */
 int32_t moe_pack_weights(const moe_rowmajor *in, moe_packed *out, void *stream);
 
@@ -248,18 +263,19 @@ int32_t moe_forward_plan(const moe_forward_args *a, moe_plan_info *info);
  * MoE layer forward over the local experts [e_begin, e_end):
  *  1. slots (t, j) with topk_idx[t][j] local are grouped by expert, stable in t*top_k+j;
  *  2. hidden states are quantised once per token to the layer's format (NVFP4 with
- *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block); W4A16 and BF16
- *     use the bf16 hidden states as they are;
+ *     one tensor scale over all of h, MXFP8 and MXFP4 per 32-block, FP8 per token row);
+ *     W4A16 and BF16 use the bf16 hidden states as they are;
  *  3. gate_up GEMM per expert (fp32 accumulation; NVFP4 sums are multiplied by
- *     fl32(s_h * s_gate_up[e]), W4A16 sums by s_gate_up[e]), then
- *     h = SwiGLU = g * u / (1 + exp(-g));
- *  4. h is quantised to the layer's format (NVFP4: one tensor scale over all S rows);
- *     W4A16 and BF16 round it to bf16 (nearest, ties to even);
+ *     fl32(s_h * s_gate_up[e]), W4A16 sums by s_gate_up[e], FP8 sums by
+ *     fl32(s_token * s_channel)), then h = SwiGLU = g * u / (1 + exp(-g));
+ *  4. h is quantised to the layer's format (NVFP4: one tensor scale over all S rows;
+ *     FP8: one scale per slot row); W4A16 and BF16 round it to bf16 (nearest, ties to
+ *     even);
  *  5. down GEMM per expert (NVFP4: times fl32(s_inter * s_down[e]); W4A16: times
- *     s_down[e]) -> y fp32;
+ *     s_down[e]; FP8: times fl32(s_row * s_channel)) -> y fp32;
  *  6. out[t] = sum over the token's local slots, j ascending, of topk_w[t][j] * y.
- * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), and for MXFP4 also D
- * a multiple of 256 (its GEMMs run on the scaled FP4 MFMA in 256-row weight tiles),
+ * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), and for MXFP4 and FP8
+ * also D a multiple of 256 (their GEMMs run on the scaled MFMA in 256-row weight tiles),
  * 1 <= top_k <= 8, 0 <= e_begin < e_end <= E. gate_up/down must match fmt (NVFP4 for
  * W4A16) and shapes.
  * T = 0 is a no-op.

@@ -159,7 +159,7 @@ class Workload:
     """One synthetic MoE-layer workload (shapes, formats, value recipe)."""
     index: int
     name: str
-    fmt: str            # "nvfp4", "mxfp8", "mxfp4", "w4a16" or "bf16"
+    fmt: str            # "nvfp4", "mxfp8", "mxfp4", "w4a16", "bf16" or "fp8"
     T: int              # tokens
     D: int              # d_model
     F: int              # d_ff
@@ -242,6 +242,10 @@ WORKLOADS = [
     Workload(9, "decode-bf16", "bf16", T=64, D=4096, F=2560, E=384, seed=9),
     Workload(10, "prefill-bf16-ep4", "bf16", T=8192, D=4096, F=2560, E=384,
              e_begin=0, e_end=96, seed=10),
+    # FP8 experts (E4M3, a scale per weight channel and per activation row) at the same shapes
+    Workload(11, "decode-fp8", "fp8", T=64, D=4096, F=2560, E=384, seed=11),
+    Workload(12, "prefill-fp8-ep4", "fp8", T=8192, D=4096, F=2560, E=384,
+             e_begin=0, e_end=96, seed=12),
 ]
 
 

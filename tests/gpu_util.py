@@ -56,6 +56,12 @@ def check_intermediate_codes(fmt: str, inter: np.ndarray, codes: np.ndarray, sca
         bad = int(np.count_nonzero(oc != np.asarray(codes).view(np.uint16)))
         assert bad == 0, f"intermediate bf16 values differ: {bad}"
         return
+    if fmt == "fp8":  # scales: the fp32 row scales
+        oc, ors = oracle.quant_fp8_rows(inter)
+        bad_c = int(np.count_nonzero(oc != codes))
+        bad_s = int(np.count_nonzero(ors.view(np.uint32) != np.asarray(scales, np.float32).view(np.uint32)))
+        assert bad_c == 0 and bad_s == 0, f"intermediate codes differ: {bad_c} code bytes, {bad_s} row scales"
+        return
     if fmt == "nvfp4":
         oc, os_, ots = oracle.quant_nvfp4(inter)
         assert np.float32(tscale) == ots, f"intermediate tensor scale {tscale} != {ots}"
@@ -91,11 +97,16 @@ def check_outputs(fmt: str, out: np.ndarray, ref: np.ndarray, idx: np.ndarray, w
      4. over all tokens, flipped ones included, the RMS of the difference from the fully
         independent output stays within max_rel_rms x RMS.
     rows: optional token subset to compare (the others are not computed by the oracle).
+    FP8: the *_inter_scales are the fp32 row scales [S] (a differing one flips its row).
     Returns (stage error / RMS, independent error / RMS, flips, tokens excluded)."""
     k = idx.shape[1]
     S = len(sorted_slot)
-    stage = oracle.down_combine(fmt, idx, w, gpu_inter_codes, gpu_inter_scales, gpu_inter_tscale, down, D=D, F=F,
-                                E=E, e_begin=e_begin, e_end=e_end)
+    if fmt == "fp8":
+        stage = oracle.down_combine(fmt, idx, w, gpu_inter_codes, None, gpu_inter_scales, down, D=D, F=F, E=E,
+                                    e_begin=e_begin, e_end=e_end)
+    else:
+        stage = oracle.down_combine(fmt, idx, w, gpu_inter_codes, gpu_inter_scales, gpu_inter_tscale, down, D=D, F=F,
+                                    E=E, e_begin=e_begin, e_end=e_end)
     sel = np.arange(out.shape[0]) if rows is None else np.asarray(rows)
     r_stage = rms(stage[sel])
     e_stage = float(np.abs(out[sel] - stage[sel]).max()) / r_stage
@@ -169,8 +180,9 @@ REL_RMS_SCALED_FP8 = 1e-2
 
 
 def scaled_fp8(layer) -> bool:
-    """The layer's GEMMs run MXFP8 on the scaled FP8 MFMA (moe_forward's own plan)."""
-    return layer.fmt == "mxfp8" and layer.plan()["gate_up_kernel"] == "mx_gemm_kernel"
+    """The layer's GEMMs run E4M3 codes (MXFP8 or FP8) on the scaled FP8 MFMA (moe_forward's
+    own plan)."""
+    return layer.fmt in ("mxfp8", "fp8") and layer.plan()["gate_up_kernel"] == "mx_gemm_kernel"
 
 
 def output_bounds(native8: bool) -> dict:

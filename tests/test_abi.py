@@ -29,7 +29,7 @@ def test_header_functions_are_exported_and_bound():
     for n in names:
         assert hasattr(lib, n), f"{n} not exported by libmoe.so"
         assert n in moe.SIGNATURES, f"{n} has no binding"
-    assert lib.moe_abi_version() == 7
+    assert lib.moe_abi_version() == 8
     assert lib.moe_status_string(EWS) == b"workspace missing or too small"
 
 
@@ -63,7 +63,40 @@ def test_forward_validation_accepts_the_workloads():
     b16.gate_up = moe.MoePacked(5, 384, 5120, 4096, A16, 0, 0)  # bf16 weights: no scales
     b16.down = moe.MoePacked(5, 384, 4096, 2560, A16, 0, 0)
     assert _validate(b16) == OK
+    assert _validate(_fp8()) == OK
     assert _validate(_args(T=0, h=0, topk_idx=0, topk_w=0, out=0)) == OK  # empty batch
+
+
+def _fp8(**over):
+    """FP8 layer: E4M3 codes, no block scales, channel scales in tensor_scale."""
+    a = _args(fmt=6, **over)
+    a.gate_up = moe.MoePacked(6, a.E, 2 * a.F, a.D, A16, 0, A16)
+    a.down = moe.MoePacked(6, a.E, a.D, a.F, A16, 0, A16)
+    return a
+
+
+def test_fp8_layer_host_checks():
+    lib = moe.lib()
+    a = _fp8()
+    a.gate_up = moe.MoePacked(6, 384, 5120, 4096, A16, 0, 0)    # channel scales missing
+    assert _validate(a) == EINVAL
+    assert _validate(_fp8(flags=moe.FLAG_EXACT_SUMS)) == EUNSUP  # no exact-sum route
+    assert _validate(_fp8(D=384)) == EUNSUP                       # 256-row weight tiles of the scaled MFMA
+    info = moe.MoePlanInfo()
+    assert lib.moe_forward_plan(ctypes.byref(_fp8()), ctypes.byref(info)) == OK
+    assert info.gate_up_kernel == b"mx_gemm_kernel" and info.down_kernel == b"mx_gemm_kernel"
+    # fp32 row scales of the hidden states and of the slots, and the fp32 intermediate
+    ws = lib.moe_forward_workspace_bytes
+    assert ws(ctypes.byref(_fp8())) > 64 * 8 * 2560 * 4 + 64 * 8 * 4096 * 4
+    # quantise / pack: FP8 takes no block scales but needs the channel scales
+    p = ctypes.c_void_p
+    out = moe.MoePacked(6, 2, 64, 128, A16, 0, 0)
+    assert lib.moe_quantize_weights(p(A16), ctypes.byref(out), None) == EINVAL
+    src = moe.MoeRowMajor(6, 2, 64, 128, A16, 0, 0)
+    out = moe.MoePacked(6, 2, 64, 128, A16, 0, A16)
+    assert lib.moe_pack_weights(ctypes.byref(src), ctypes.byref(out), None) == EINVAL
+    src = moe.MoeRowMajor(6, 2, 64, 128, A16, 0, A16 + 2)
+    assert lib.moe_pack_weights(ctypes.byref(src), ctypes.byref(out), None) == EALIGN
 
 
 def test_w4a16_takes_nvfp4_packed_weights():
@@ -83,7 +116,7 @@ def test_mxfp4_needs_256_wide_d_model():
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(fmt=6), EINVAL), (dict(fmt=0), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
+    (dict(fmt=7), EINVAL), (dict(fmt=0), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
     (dict(e_begin=10, e_end=10), EINVAL), (dict(e_end=385), EINVAL), (dict(e_begin=-1), EINVAL),
     (dict(E=5000), EINVAL), (dict(h=0), EINVAL), (dict(out=0), EINVAL),
     (dict(D=4000), EUNSUP), (dict(F=2500), EUNSUP),

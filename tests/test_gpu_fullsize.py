@@ -1,4 +1,4 @@
-"""GPU parity at the full sizes of the ten benchmarked workloads, through the same calls
+"""GPU parity at the full sizes of the twelve benchmarked workloads, through the same calls
 and launch configuration that bench.py times (moe.route + moe.Layer.forward).
 
 Bit-exact, whole batch: top-k indices of every token, max |h|, the permutation, every
@@ -21,9 +21,11 @@ hidden-state codes):
    tokens they reach; tokens without a flipped row must match within 2e-3 x RMS, and the
    relative RMS error over all tokens must stay within 2e-3 (1e-2 for MXFP8 on the
    scaled FP8 MFMA, whose sums flip about 100 times as many codes; tests/gpu_util.py).
-The decode NVFP4 and MXFP8 workloads are also run through the oracle's own forward (its
-routing, permutation, quantisers and fp64 experts) on the experts the batch touches, and
-compared with the GPU output stage-wise and independently.
+The decode NVFP4, MXFP8 and FP8 workloads are also run through the oracle's own forward
+(its routing, permutation, quantisers and fp64 experts) on the experts the batch touches,
+and compared with the GPU output stage-wise and independently. FP8's scales are fp32 per
+row (tokens, slots) and per weight channel: its "scales" below are those row scales, and
+its sums are multiplied by fl32(row scale * channel scale).
 """
 import time
 
@@ -41,7 +43,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _dequant(fmt, codes, scales):
-    """fp64 values of packed codes (NVFP4 without its tensor scale)."""
+    """fp64 values of packed codes (NVFP4 without its tensor scale, FP8 without its row or
+    channel scales)."""
+    if fmt == "fp8":
+        return oracle.dequant_fp8_rows(codes)
     if fmt in ("nvfp4", "w4a16"):
         return oracle.dequant_nvfp4(codes, scales, 1.0, with_tensor=False)
     if fmt == "mxfp4":
@@ -59,10 +64,26 @@ def _oracle_expert(wl, e):
 
 
 def _values(fmt, w):
-    """fp64 [N, K] values of one expert's packed matrix (without the NVFP4 tensor scale)."""
+    """fp64 [N, K] values of one expert's packed matrix (without the NVFP4 tensor scale or
+    the FP8 channel scales)."""
     if fmt == "bf16":
         return synth.bf16_to_f32(w["codes"][0]).astype(np.float64)
-    return _dequant(fmt, w["codes"][0], w["scales"][0])
+    return _dequant(fmt, w["codes"][0], None if w["scales"] is None else w["scales"][0])
+
+
+def _scale_sums(fmt, sums, w, row_scales, tscale):
+    """fp32 sums [rows, N] of one expert times the format's scales, rounded to fp32:
+    NVFP4 fl32(tensor scale of the operand * the weights'), W4A16 the weights' tensor scale,
+    FP8 fl32(row scale * channel scale); the others none."""
+    sums = sums.astype(np.float32)
+    if fmt == "nvfp4":
+        return (sums * np.float32(np.float32(tscale) * w["tensor_scale"][0])).astype(np.float32)
+    if fmt == "w4a16":
+        return (sums * np.float32(w["tensor_scale"][0])).astype(np.float32)
+    if fmt == "fp8":
+        f = (np.asarray(row_scales, np.float32)[:, None] * w["tensor_scale"][0][None, :]).astype(np.float32)
+        return (sums * f).astype(np.float32)
+    return sums
 
 
 def _inter_values(fmt, codes, scales):
@@ -99,9 +120,9 @@ def _combine(T, D, k, ss, w, y):
     return out
 
 
-# (workload, moe_forward flags): the ten workloads on their default routes, and the
+# (workload, moe_forward flags): the twelve workloads on their default routes, and the
 # skewed MXFP8 workload once more with exact sums (the bf16 expansion) for comparison
-CASES = [(i, 0) for i in range(1, 11)] + [(4, moe.FLAG_EXACT_SUMS)]
+CASES = [(i, 0) for i in range(1, 13)] + [(4, moe.FLAG_EXACT_SUMS)]
 
 
 @pytest.mark.timeout(900)
@@ -112,7 +133,7 @@ def test_fullsize_workload(i, flags):
     wl = synth.WORKLOADS[i]
     fmt, T, D, F, E, k = wl.fmt, wl.T, wl.D, wl.F, wl.E, wl.k
     eb, ee = wl.e_begin, wl.local_end
-    nv, a16 = fmt == "nvfp4", fmt in ("w4a16", "bf16")
+    nv, a16, f8 = fmt == "nvfp4", fmt in ("w4a16", "bf16"), fmt == "fp8"
     report("fullsize", workload=wl.name, T=T, D=D, F=F, E=E, local=f"[{eb},{ee})")
     h, wr, bias = wl.hidden(), wl.router_weight(), wl.router_bias()
     d_h, d_wr = to_dev(h), to_dev(wr)
@@ -148,14 +169,20 @@ def test_fullsize_workload(i, flags):
 
     # hidden-state codes (all tokens) and the exact activation values of every token
     hf = synth.bf16_to_f32(h)
-    a_ts = None
+    a_ts = a_rs = None
     if nv:
         a_c, a_s, a_ts = oracle.quant_nvfp4(hf)
         assert np.float32(tp["a_tscale"][0]) == a_ts
+    elif f8:
+        a_c, a_rs = oracle.quant_fp8_rows(hf)
+        assert np.array_equal(tp["a_tscale"].view(np.uint32), a_rs.view(np.uint32)), "hidden row scales differ"
     elif not a16:
         a_c, a_s = oracle.quant_mxfp4(hf) if fmt == "mxfp4" else oracle.quant_mxfp8(hf)
     if a16:  # W4A16 and bf16 experts keep the hidden states in bf16
         act = hf.astype(np.float64)
+    elif f8:
+        assert np.array_equal(tp["a_codes"], a_c), "hidden codes differ"
+        act = oracle.dequant_fp8_rows(a_c)
     else:
         assert np.array_equal(tp["a_codes"], a_c) and np.array_equal(tp["a_scales"], a_s), "hidden codes differ"
         act = _dequant(fmt, a_c, a_s)
@@ -165,6 +192,8 @@ def test_fullsize_workload(i, flags):
     g_inter = tp["inter"][:S]
     g_codes = tp["inter_codes"][:S]
     g_scales = tp["inter_scales"][:S] if "inter_scales" in tp else None
+    if f8:  # the fp32 row scales
+        g_scales = tp["inter_tscale"][:S]
     g_its = tp["inter_tscale"][0] if nv else None
     check_intermediate_codes(fmt, g_inter, g_codes, g_scales, g_its)
     g_y = tp["y"][:S]
@@ -174,7 +203,7 @@ def test_fullsize_workload(i, flags):
     y_stage = np.empty((S, D), np.float32)
     down_of = {}        # expert -> the oracle's down weights (for the independent pass)
     experts = {}        # expert -> (gate_up, down) of the oracle, decode workloads 1 and 2
-    keep_gate_up = i in (1, 2) and not flags
+    keep_gate_up = i in (1, 2, 11) and not flags
     worst_inter = worst_y = 0.0
     live = np.nonzero(counts)[0]
     for n_done, el in enumerate(live):
@@ -188,6 +217,10 @@ def test_fullsize_workload(i, flags):
                     f"expert {e} weights differ"
                 continue
             assert np.array_equal(untile(host(dev_w.codes[e:e + 1])), ref["codes"]), f"expert {e} codes differ"
+            if f8:
+                assert np.array_equal(host(dev_w.tensor_scale[e:e + 1]).view(np.uint32),
+                                      ref["tensor_scale"].view(np.uint32)), f"expert {e} channel scales differ"
+                continue
             assert np.array_equal(untile(host(dev_w.scales[e:e + 1])), ref["scales"]), f"expert {e} scales differ"
             if nv or fmt == "w4a16":
                 assert host(dev_w.tensor_scale[e:e + 1])[0] == ref["tensor_scale"][0]
@@ -196,19 +229,12 @@ def test_fullsize_workload(i, flags):
             experts[e] = (o_gu, o_dn)
         wg, wd = _values(fmt, o_gu), _values(fmt, o_dn)
         tok = ss[p0:p1] // k
-        g = (act[tok] @ wg.T).astype(np.float32)  # exact products, fp64 sums, rounded to fp32
-        if nv:
-            g = (g * np.float32(np.float32(a_ts) * o_gu["tensor_scale"][0])).astype(np.float32)
-        elif fmt == "w4a16":
-            g = (g * np.float32(o_gu["tensor_scale"][0])).astype(np.float32)
+        # exact products, fp64 sums, rounded to fp32, then the format's scales
+        g = _scale_sums(fmt, act[tok] @ wg.T, o_gu, None if a_rs is None else a_rs[tok], a_ts)
         gate, up = g[:, :F].astype(np.float64), g[:, F:].astype(np.float64)
         inter_ref[p0:p1] = (gate * up / (1.0 + np.exp(-gate))).astype(np.float32)
-        y = (_inter_values(fmt, g_codes[p0:p1], None if g_scales is None else g_scales[p0:p1]) @ wd.T)
-        y = y.astype(np.float32)
-        if nv:
-            y = (y * np.float32(np.float32(g_its) * o_dn["tensor_scale"][0])).astype(np.float32)
-        elif fmt == "w4a16":
-            y = (y * np.float32(o_dn["tensor_scale"][0])).astype(np.float32)
+        gs = None if g_scales is None else g_scales[p0:p1]
+        y = _scale_sums(fmt, _inter_values(fmt, g_codes[p0:p1], None if f8 else gs) @ wd.T, o_dn, gs, g_its)
         y_stage[p0:p1] = y
         scale_i = float(np.abs(inter_ref[p0:p1]).max())
         e_inter = float(np.abs(g_inter[p0:p1] - inter_ref[p0:p1]).max()) / max(scale_i, 1e-30)
@@ -240,10 +266,12 @@ def test_fullsize_workload(i, flags):
         i_codes, i_scales, i_ts = oracle.quant_nvfp4(inter_ref)
     elif fmt == "mxfp4":
         (i_codes, i_scales), i_ts = oracle.quant_mxfp4(inter_ref), None
+    elif f8:  # i_scales: the row scales [S]
+        (i_codes, i_scales), i_ts = oracle.quant_fp8_rows(inter_ref), None
     else:
         (i_codes, i_scales), i_ts = oracle.quant_mxfp8(inter_ref), None
     rows_c, flips = _code_flips(fmt, g_codes, i_codes)
-    rows_s = np.zeros(S, bool) if i_scales is None else (g_scales != i_scales).any(1)
+    rows_s = np.zeros(S, bool) if i_scales is None else (g_scales.reshape(S, -1) != i_scales.reshape(S, -1)).any(1)
     ts_same = (not nv) or np.float32(g_its) == np.float32(i_ts)
     flipped = rows_c | rows_s if ts_same else np.ones(S, bool)
     y_ind = y_stage.copy()
@@ -254,13 +282,9 @@ def test_fullsize_workload(i, flags):
         if len(sel) == 0:
             continue
         o_dn = down_of[e]
-        y = (_inter_values(fmt, i_codes[sel], None if i_scales is None else i_scales[sel]) @ _values(fmt, o_dn).T)
-        y = y.astype(np.float32)
-        if nv:
-            y = (y * np.float32(np.float32(i_ts) * o_dn["tensor_scale"][0])).astype(np.float32)
-        elif fmt == "w4a16":
-            y = (y * np.float32(o_dn["tensor_scale"][0])).astype(np.float32)
-        y_ind[sel] = y
+        isc = None if i_scales is None else i_scales[sel]
+        y_ind[sel] = _scale_sums(fmt, _inter_values(fmt, i_codes[sel], None if f8 else isc) @ _values(fmt, o_dn).T,
+                                 o_dn, isc, i_ts)
     out_ind = _combine(T, D, k, ss, wf, y_ind)
     r_ind = rms(out_ind)
     bad_tok = np.zeros(T, bool)
@@ -295,8 +319,9 @@ def test_fullsize_workload(i, flags):
         ref, otp = oracle.moe_forward(fmt, h, cidx, o_w, D=D, F=F, E=len(used), taps=True, gate_up=o_gu,
                                       down=o_dn)
         t_orc = time.perf_counter() - t0
+        o_isc = otp["inter_tscale"] if f8 else otp.get("inter_scales")
         e_s, e_i, fl, excl = check_outputs(fmt, out, ref, cidx, o_w, g_codes, g_scales, g_its, otp["inter_codes"],
-                                           otp.get("inter_scales"), ss, o_dn, D=D, F=F, E=len(used), e_begin=0,
+                                           o_isc, ss, o_dn, D=D, F=F, E=len(used), e_begin=0,
                                            e_end=len(used), **output_bounds(native8))
         inter_vs_oracle = float(np.abs(otp["inter"] - inter_ref).max()) / float(np.abs(inter_ref).max())
         report("  oracle forward", seconds=f"{t_orc:.1f}", stage_err=f"{e_s:.2e}", independent_err=f"{e_i:.2e}",

@@ -52,7 +52,7 @@ def test_pack_bf16_weights_bitexact():
     assert np.array_equal(untile(host(got.codes)).view(np.uint16), w), "packed bf16 weights differ"
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "fp8"])
 @pytest.mark.parametrize("shape", [(5, 256, 512), (2, 96, 2048)])
 def test_quantize_weights_bitexact(fmt, shape):
     E, N, K = shape
@@ -62,12 +62,13 @@ def test_quantize_weights_bitexact(fmt, shape):
     torch.cuda.synchronize()
     ref = oracle.quantize_weights(fmt, w)
     assert np.array_equal(untile(host(got.codes)), ref["codes"]), "codes differ"
-    assert np.array_equal(untile(host(got.scales)), ref["scales"]), "scales differ"
-    if fmt == "nvfp4":
+    if fmt != "fp8":
+        assert np.array_equal(untile(host(got.scales)), ref["scales"]), "scales differ"
+    if fmt in ("nvfp4", "fp8"):  # FP8: the channel scales [E][N]
         assert np.array_equal(host(got.tensor_scale).view(np.uint32), ref["tensor_scale"].view(np.uint32))
 
 
-@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "bf16"])
+@pytest.mark.parametrize("fmt", ["nvfp4", "mxfp8", "mxfp4", "bf16", "fp8"])
 @pytest.mark.parametrize("shape", [(3, 96, 512), (2, 256, 2048)])
 def test_pack_rowmajor_checkpoint_bitexact(fmt, shape):
     """moe_pack_weights on the oracle's row-major quantisation (a pre-quantised checkpoint)
@@ -80,15 +81,18 @@ def test_pack_rowmajor_checkpoint_bitexact(fmt, shape):
     else:
         o = oracle.quantize_weights(fmt, w)
         ts = None if o["tensor_scale"] is None else to_dev(o["tensor_scale"])
-        got = moe.pack_weights(fmt, to_dev(o["codes"]), to_dev(o["scales"]), ts)
+        got = moe.pack_weights(fmt, to_dev(o["codes"]), None if o["scales"] is None else to_dev(o["scales"]), ts)
     ref = moe.quantize_weights(fmt, to_dev(w))
     torch.cuda.synchronize()
     assert np.array_equal(host(got.codes), host(ref.codes)), "packed codes differ"
     assert np.array_equal(host(got.scales), host(ref.scales)), "packed scales differ"
-    if fmt == "nvfp4":
+    if fmt in ("nvfp4", "fp8"):
         assert np.array_equal(host(got.tensor_scale).view(np.uint32), host(ref.tensor_scale).view(np.uint32))
     if fmt == "bf16":
         assert np.array_equal(untile(host(got.codes)).view(np.uint16), w)
+    elif fmt == "fp8":
+        assert np.array_equal(untile(host(got.codes)), o["codes"])
+        assert np.array_equal(host(got.tensor_scale).view(np.uint32), o["tensor_scale"].view(np.uint32))
     else:
         assert np.array_equal(untile(host(got.codes)), o["codes"]) and np.array_equal(untile(host(got.scales)),
                                                                                      o["scales"])
@@ -244,7 +248,30 @@ LAYER_CASES = [
     # powers of two (5 gate_up N-blocks, 3 down N-blocks, 12 and 10 K chunks)
     dict(name="mxfp8-full-dims", wl=synth.custom("mxfp8", T=64, D=4096, F=2560, E=16, seed=57)),
     dict(name="prefill-mxfp8-d768-f640", wl=synth.custom("mxfp8", T=700, D=768, F=640, E=12, seed=58)),
+    # FP8 (E4M3, a scale per weight channel and per activation row) on the scaled FP8 MFMA
+    # with unit E8M0 scales: decode and prefill tiles, an expert-parallel share, skewed
+    # routing, top-1, the full dimensions, widths that are not powers of two, and hidden
+    # states with an all-zero row, a tiny row and a row with one huge outlier
+    dict(name="decode-fp8", wl=synth.custom("fp8", T=40, D=256, F=256, E=16, seed=80)),
+    dict(name="prefill-fp8", wl=synth.custom("fp8", T=300, D=256, F=256, E=16, seed=81)),
+    dict(name="prefill-fp8-ep", wl=synth.custom("fp8", T=400, D=256, F=128, E=24, e_begin=0, e_end=6, seed=82)),
+    dict(name="skew-fp8", wl=synth.custom("fp8", T=1100, D=512, F=256, E=24, skew=True, seed=83)),
+    dict(name="top1-fp8", wl=synth.custom("fp8", T=200, D=256, F=128, E=16, k=1, seed=84)),
+    dict(name="fp8-full-dims", wl=synth.custom("fp8", T=64, D=4096, F=2560, E=16, seed=85)),
+    dict(name="prefill-fp8-d768-f640", wl=synth.custom("fp8", T=700, D=768, F=640, E=12, seed=86)),
+    dict(name="fp8-edge-rows", wl=synth.custom("fp8", T=96, D=512, F=256, E=16, seed=87), edge_rows=True),
 ]
+
+
+def _edge_rows(h: np.ndarray) -> np.ndarray:
+    """Hidden states with an all-zero row (row scale 1, every code 0), a row scaled by
+    2^-60 (a tiny row scale) and a row whose one huge value pushes the rest of it into
+    E4M3's subnormals."""
+    h = h.copy()
+    h[3] = 0
+    h[7] = synth.normal_bf16(1, 11, 0, h.shape[1], 2.0 ** -60)
+    h[11, 5] = 0x4B00  # 2^23 in bf16
+    return h
 
 
 @pytest.mark.parametrize("c", LAYER_CASES, ids=lambda c: c["name"])
@@ -253,6 +280,8 @@ def test_forward_parity(c):
     fmt, T, D, F, E, k = wl.fmt, wl.T, wl.D, wl.F, wl.E, wl.k
     eb, ee = wl.e_begin, wl.local_end
     h, wr, bias, gu_m, dn_m = case_inputs(wl)
+    if c.get("edge_rows"):
+        h = _edge_rows(h)
     report("forward", case=c["name"], fmt=fmt, T=T, D=D, F=F, E=E, local=(eb, ee))
 
     # GPU: quantise, route, forward with every tap
@@ -287,6 +316,9 @@ def test_forward_parity(c):
     assert np.array_equal(tp["sorted_slot"][:S], ss)
     if fmt not in ("w4a16", "bf16"):  # W4A16 and bf16 experts keep the hidden states in bf16
         assert np.array_equal(tp["a_codes"], otp["a_codes"]), "hidden-state codes differ"
+    if fmt == "fp8":  # the row scales
+        assert np.array_equal(tp["a_tscale"].view(np.uint32), otp["a_tscale"].view(np.uint32)), "row scales differ"
+    elif fmt not in ("w4a16", "bf16"):
         assert np.array_equal(tp["a_scales"], otp["a_scales"]), "hidden-state scales differ"
     if fmt == "nvfp4":
         assert tp["a_tscale"][0] == otp["a_tscale"][0]
@@ -297,6 +329,9 @@ def test_forward_parity(c):
     inter_err = float(np.abs(g_inter - otp["inter"]).max()) / scale_i
     g_its = tp["inter_tscale"][0] if fmt == "nvfp4" else None
     g_iscales = tp["inter_scales"][:S] if "inter_scales" in tp else None
+    o_iscales = otp.get("inter_scales")
+    if fmt == "fp8":  # fp32 row scales in place of block scales
+        g_iscales, o_iscales = tp["inter_tscale"][:S], otp["inter_tscale"]
     check_intermediate_codes(fmt, g_inter, tp["inter_codes"][:S], g_iscales, g_its)
     inter_tol = INTER_TOL_SCALED_FP8 if native8 else INTER_TOL_EXACT
     assert inter_err < inter_tol, f"SwiGLU intermediate differs by {inter_err:.2e} of its max"
@@ -304,7 +339,7 @@ def test_forward_parity(c):
     # output: stage-wise on every token, independent on tokens without intermediate flips
     e_stage, e_ind, flips, excluded = check_outputs(
         fmt, out, ref, o_idx, o_w, tp["inter_codes"][:S], g_iscales, g_its, otp["inter_codes"],
-        otp.get("inter_scales"), ss, o_dn, D=D, F=F, E=E, e_begin=eb, e_end=ee, **output_bounds(native8))
+        o_iscales, ss, o_dn, D=D, F=F, E=E, e_begin=eb, e_end=ee, **output_bounds(native8))
     report("  result", S=S, inter_rel=f"{inter_err:.2e}", code_flips=flips, tokens_with_flips=excluded,
            stage_err=f"{e_stage:.2e}", independent_err=f"{e_ind:.2e}")
     has_local = ((o_idx >= eb) & (o_idx < ee)).any(1)
@@ -343,6 +378,7 @@ GRAPH_CASES = [
     dict(name="prefill-mxfp8", wl=synth.custom("mxfp8", T=1100, D=256, F=256, E=16, seed=42)),  # count/scan/scatter + fill
     dict(name="prefill-mxfp4", wl=synth.custom("mxfp4", T=700, D=256, F=256, E=16, seed=43)),
     dict(name="decode-w4a16", wl=synth.custom("w4a16", T=64, D=512, F=256, E=16, seed=44)),
+    dict(name="prefill-fp8", wl=synth.custom("fp8", T=700, D=256, F=256, E=16, seed=45)),
 ]
 
 
