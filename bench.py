@@ -10,8 +10,8 @@ other: tiny-nvfp4 (16 tokens, d_model 256), decode-nvfp4 (64 tokens, d_model 409
 d_ff 2560, 384 experts, top-8), decode-mxfp8 (256 tokens), prefill-nvfp4-ep4 (8192
 tokens, one expert-parallel rank's 96 experts) and skewed-mxfp8 (16384 tokens, Zipf-like
 router bias). The headline fields of the JSON line are decode-nvfp4's; `configs` holds
-every workload's line. --workload i runs one of the eleven synthetic workloads alone
-(the five plus the MXFP4, W4A16 and bf16-expert variants).
+every workload's line. --workload i runs one of the thirteen synthetic workloads alone
+(the five plus the MXFP4, W4A16, bf16-expert and FP8 variants).
 
 Printed: one JSON line (rank 0). `roofline` covers the dominant kernel (the gate_up
 GEMM) timed live with HIP events recorded around its launch on the library's stream;
@@ -40,7 +40,9 @@ DTYPES = {"nvfp4": "f16 (exact NVFP4 values), fp32 accumulate",
           "mxfp8": "fp8 (MXFP8 codes and E8M0 scales on the scaled MFMA), fp32 accumulate",
           "mxfp4": "fp4 (MXFP4 codes and E8M0 scales on the scaled MFMA), fp32 accumulate",
           "w4a16": "bf16 (bf16 activations, NVFP4 weights expanded exactly), fp32 accumulate",
-          "bf16": "bf16 (bf16 weights and activations), fp32 accumulate"}
+          "bf16": "bf16 (bf16 weights and activations), fp32 accumulate",
+          "fp8": "fp8 (E4M3 codes on the scaled MFMA with unit scales, fp32 row and channel scales applied "
+                 "to the sums), fp32 accumulate"}
 METRIC = "MoE layer tokens/s; % peak HBM BW (decode), % scaled-MFMA peak (prefill)"
 
 
@@ -113,6 +115,8 @@ def packed_bytes_per_expert(fmt: str, N: int, K: int) -> int:
         return 2 * N * K
     if fmt == "mxfp4":
         return N * K // 2 + N * K // 32
+    if fmt == "fp8":
+        return N * K + 4 * N
     return N * K + N * K // 32
 
 
@@ -222,8 +226,8 @@ def _pad_experts(d, count):
             out[k_] = None
             continue
         pad = np.zeros((count,) + v.shape[1:], v.dtype)
-        if k_ == "tensor_scale":
-            pad = np.ones(count, v.dtype)
+        if k_ == "tensor_scale":  # [E] NVFP4, [E][N] FP8 channel scales
+            pad = np.ones((count,) + v.shape[1:], v.dtype)
         out[k_] = np.concatenate([v, pad])
     return out
 
@@ -314,16 +318,18 @@ def run_workload(moe, torch, wl, args, dev):
     gu_b = packed_bytes_per_expert(wl.fmt, 2 * F, D)
     dn_b = packed_bytes_per_expert(wl.fmt, D, F)
     code_b = {"nvfp4": lambda c: c // 2 + c // 16, "mxfp4": lambda c: c // 2 + c // 32,
-              "mxfp8": lambda c: c + c // 32, "w4a16": lambda c: 2 * c, "bf16": lambda c: 2 * c}[wl.fmt]
+              "mxfp8": lambda c: c + c // 32, "w4a16": lambda c: 2 * c, "bf16": lambda c: 2 * c,
+              "fp8": lambda c: c + 4}[wl.fmt]
     act_b = lambda rows, cols: rows * code_b(cols)
     gate_up_bytes = touched * gu_b + act_b(T, D) + act_b(S, F)
     gate_up_flops = 4.0 * S * F * D
     layer_bytes = touched * (gu_b + dn_b) + E * D * 2 + T * D * 2 + T * D * 4
     # the contraction's own peak: NVFP4 runs the f16 MFMA on exactly expanded values, W4A16
-    # and bf16 experts the bf16 MFMA, MXFP4 the scaled FP4 MFMA, MXFP8 the scaled FP8 MFMA
-    # (or, with exact sums, the bf16 MFMA); the format's scaled-MFMA peak is reported beside it
+    # and bf16 experts the bf16 MFMA, MXFP4 the scaled FP4 MFMA, MXFP8 and FP8 the scaled FP8
+    # MFMA (MXFP8 with exact sums: the bf16 MFMA); the format's scaled-MFMA peak is reported
+    # beside it
     kern = plan["gate_up_kernel"]
-    native8 = wl.fmt == "mxfp8" and kern == "mx_gemm_kernel"
+    native8 = wl.fmt in ("mxfp8", "fp8") and kern == "mx_gemm_kernel"
     mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else ("fp8" if native8 else "bf16"))]
     format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt in ("w4a16", "bf16") else "fp8")]
     decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge
@@ -392,7 +398,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=None,
-                    help="run one of the eleven synthetic workloads alone (default: the five configurations)")
+                    help="run one of the thirteen synthetic workloads alone (default: the five configurations)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time one captured HIP graph per step, replayed (default: eager launches; on MI355X "

@@ -12,7 +12,8 @@ def test_cpu_baseline_small_samples():
     cases = [synth.WORKLOADS[0],
              synth.custom("nvfp4", T=512, D=256, F=128, E=64, e_begin=0, e_end=16, seed=5),
              synth.custom("mxfp8", T=512, D=256, F=128, E=64, skew=True, seed=6),
-             synth.custom("bf16", T=64, D=256, F=128, E=64, e_begin=0, e_end=8, seed=7)]
+             synth.custom("bf16", T=64, D=256, F=128, E=64, e_begin=0, e_end=8, seed=7),
+             synth.custom("fp8", T=64, D=256, F=128, E=64, seed=8)]
     for wl in cases:
         r = bench.cpu_baseline(wl, wl.hidden(), wl.router_weight(), wl.router_bias(), target_s=0.2)
         assert r["kind"] == "oracle" and r["value"] > 0 and r["cores"] >= 1 and r["cpu_model"]
