@@ -16,6 +16,17 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+// y is read once and out written once: both marked non-temporal (skewed-mxfp8, whose
+// 2.15 GB of y this kernel reads, measured 6.19 -> 6.13 ms per step; no change elsewhere)
+__device__ __forceinline__ float4 load_y(const float4 *p) {
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_out(float4 *p, float4 a) {
+    __builtin_nontemporal_store((f4v){a.x, a.y, a.z, a.w}, reinterpret_cast<f4v *>(p));
+}
 
 __global__ void __launch_bounds__(kThreads) combine_kernel(int32_t D, int32_t k,
                                                            const int32_t *__restrict__ slot_pos,
@@ -38,7 +49,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int32_t D, int32_t k,
         float4 v[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-            v[j] = pos[j] >= 0 ? y4[(int64_t)pos[j] * n4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+            v[j] = pos[j] >= 0 ? load_y(y4 + (int64_t)pos[j] * n4 + c) : make_float4(0.f, 0.f, 0.f, 0.f);
         float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -48,7 +59,7 @@ __global__ void __launch_bounds__(kThreads) combine_kernel(int32_t D, int32_t k,
             acc.z = fmaf(wj[j], v[j].z, acc.z);
             acc.w = fmaf(wj[j], v[j].w, acc.w);
         }
-        o4[c] = acc;
+        store_out(o4 + c, acc);
     }
 }
 
