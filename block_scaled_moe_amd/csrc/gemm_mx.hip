@@ -358,7 +358,7 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
 #pragma unroll
                         for (int v = 0; v < 16; ++v) {
                             const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                            if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = acc[ms][ns][v] * (rs[m] * cn);
+                            if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, acc[ms][ns][v] * (rs[m] * cn));
                         }
                 }
             }
@@ -417,7 +417,7 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                        if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = acc[ms][ns][v];
+                        if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, acc[ms][ns][v]);
                     }
                 }
         }

@@ -393,7 +393,7 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                        if (m < rows) p.out_f32[(int64_t)(p0 + m) * N + n] = NV ? acc[ms][ns][v] * scl : acc[ms][ns][v];
+                        if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, NV ? acc[ms][ns][v] * scl : acc[ms][ns][v]);
                     }
                 }
         }
