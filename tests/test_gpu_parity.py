@@ -372,6 +372,30 @@ def test_repeat_calls_are_deterministic():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", ["mxfp8", "mxfp4", "fp8", "w4a16", "bf16"])
+def test_expert_parallel_shares_add_up(fmt):
+    """The expert-parallel contract on the GPU: four expert ranges (an EP4 split, each one
+    rank's moe_forward) sum to the whole layer's output, and every share's tokens without a
+    local slot are zero. NVFP4 is excluded: its intermediate tensor scale is taken over
+    each share's own slots, as the oracle's is."""
+    wl = synth.custom(fmt, T=300, D=256, F=256, E=32, seed=95)
+    h, wr, bias, gu_m, dn_m = case_inputs(wl)
+    report("ep shares", fmt=fmt, T=wl.T, E=wl.E)
+    gu, dn = moe.quantize_weights(fmt, to_dev(gu_m)), moe.quantize_weights(fmt, to_dev(dn_m))
+    d_h = to_dev(h)
+    idx, w, _, _ = moe.route(d_h, to_dev(wr), wl.k)
+    full = host(moe.Layer(fmt, wl.T, wl.D, wl.F, wl.E, gu, dn).forward(d_h, idx, w)).astype(np.float64)
+    o_idx = host(idx)
+    parts = np.zeros_like(full)
+    for r in range(4):
+        eb, ee = 8 * r, 8 * r + 8
+        part = host(moe.Layer(fmt, wl.T, wl.D, wl.F, wl.E, gu, dn, e_begin=eb, e_end=ee).forward(d_h, idx, w))
+        local = ((o_idx >= eb) & (o_idx < ee)).any(1)
+        assert not part[~local].any(), f"share {r}: tokens without a local slot must be zero"
+        parts += part
+    np.testing.assert_allclose(parts, full, rtol=0, atol=2e-6 * np.abs(full).max())
+
+
 # ------------------------------------------------------------------ graph replay
 GRAPH_CASES = [
     dict(name="decode-nvfp4", wl=synth.custom("nvfp4", T=64, D=256, F=256, E=16, seed=41)),     # one-workgroup permute
