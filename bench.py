@@ -80,6 +80,7 @@ KERNEL_SOURCES = {
     "tile_gemm_kernel": ["gemm_tile.hip", "gemm_common.h", "layout.h", "formats.h"],
     "grouped_gemm_kernel": ["gemm.hip", "gemm_common.h", "layout.h", "formats.h"],
     "mx_gemm_kernel": ["gemm_mx.hip", "gemm_common.h", "layout.h", "formats.h"],
+    "fp8_wide_gemm_kernel": ["gemm_fp8_wide.hip", "gemm_common.h", "layout.h", "formats.h"],
 }
 
 
@@ -331,7 +332,7 @@ def run_workload(moe, torch, wl, args, dev):
     # MFMA (MXFP8 with exact sums: the bf16 MFMA); the format's scaled-MFMA peak is reported
     # beside it
     kern = plan["gate_up_kernel"]
-    native8 = wl.fmt in ("mxfp8", "fp8") and kern == "mx_gemm_kernel"
+    native8 = wl.fmt in ("mxfp8", "fp8") and kern in ("mx_gemm_kernel", "fp8_wide_gemm_kernel")
     mfma_peak = MFMA_PEAK_TFLOPS["fp4" if mx4 else ("f16" if nv else ("fp8" if native8 else "bf16"))]
     format_peak = MFMA_PEAK_TFLOPS["fp4" if nv or mx4 else ("bf16" if wl.fmt in ("w4a16", "bf16") else "fp8")]
     decode = 6.0 * S * D * F / max(layer_bytes, 1) < mfma_peak / HBM_PEAK_GBS * 1e3  # below the ridge

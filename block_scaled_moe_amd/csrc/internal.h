@@ -162,6 +162,11 @@ int32_t mx_gemm_bm();
 // (non-temporal weight loads)
 hipError_t launch_mx_gemm(const GemmArgs &a, int mode, bool gate_up, bool stream_once, int32_t max_tiles,
                           hipStream_t s);
+// The prefill FP8 GEMMs on 256 x 256 workgroup tiles (gemm_fp8_wide.hip): same operands,
+// shapes (mx_gemm_supported) and results as launch_mx_gemm's kMxFP8Rows, 256-row M-tiles
+// (fp8_wide_gemm_bm).
+int32_t fp8_wide_gemm_bm();
+hipError_t launch_fp8_wide_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int32_t T, int32_t D, int32_t k, const int32_t *slot_pos, const float *w,

@@ -31,10 +31,17 @@ constexpr int32_t kPrefillRowsPerExpert = 48;
 #ifndef MOE_MX8_DECODE_NATIVE
 #define MOE_MX8_DECODE_NATIVE 1
 #endif
+// FP8 outside decode on the 256 x 256 tiles of gemm_fp8_wide.hip (1) or on the 128-row
+// tiles of gemm_mx.hip (0). The same tiles for MXFP8 (weight and activation scales staged
+// alongside) measured slower than gemm_mx.hip on the skewed 16K-token layer.
+#ifndef MOE_FP8_WIDE
+#define MOE_FP8_WIDE 1
+#endif
 
 struct Plan {
     GemmShape shape;
     bool scaled;  // MXFP4 / MXFP8 / FP8 on the scaled MFMA with the codes as stored (gemm_mx.hip)
+    bool wide;    // FP8 outside decode: the 256 x 256 tiles (gemm_fp8_wide.hip)
     bool tiled;   // prefill on the MFMA tile kernels (64- or 128-row M-tiles), or scaled
     int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
     size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
@@ -68,7 +75,8 @@ Plan make_plan(const moe_forward_args *a) {
                 (p.shape == GemmShape::Prefill || MOE_MX8_DECODE_NATIVE));
     p.tiled = p.scaled || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
                            tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
-    p.bm = p.scaled ? mx_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
+    p.wide = f8 && p.shape == GemmShape::Prefill && MOE_FP8_WIDE;
+    p.bm = p.wide ? fp8_wide_gemm_bm() : p.scaled ? mx_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
@@ -104,9 +112,10 @@ Plan make_plan(const moe_forward_args *a) {
 }
 
 // The kernel family each GEMM of a plan runs (what run_gemm launches).
-enum class Kernel { Scaled, Tile, Stream, Grouped };
+enum class Kernel { Wide, Scaled, Tile, Stream, Grouped };
 
 Kernel gemm_kernel(const Plan &P, int32_t K, int32_t N, bool gate_up) {
+    if (P.wide) return Kernel::Wide;
     if (P.scaled) return Kernel::Scaled;
     if (P.tiled) return Kernel::Tile;
     if (P.shape == GemmShape::Decode && stream_gemm_supported(K, N, gate_up)) return Kernel::Stream;
@@ -115,6 +124,7 @@ Kernel gemm_kernel(const Plan &P, int32_t K, int32_t N, bool gate_up) {
 
 const char *kernel_name(Kernel k) {
     switch (k) {
+        case Kernel::Wide: return "fp8_wide_gemm_kernel";
         case Kernel::Scaled: return "mx_gemm_kernel";
         case Kernel::Tile: return "tile_gemm_kernel";
         case Kernel::Stream: return "stream_gemm_kernel";
@@ -125,6 +135,7 @@ const char *kernel_name(Kernel k) {
 hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P, hipStream_t s) {
     const int fm = gemm_fm(fmt);
     switch (gemm_kernel(P, g.K, g.N, gate_up)) {
+        case Kernel::Wide: return launch_fp8_wide_gemm(g, gate_up, P.max_tiles, s);
         case Kernel::Scaled:
             return launch_mx_gemm(g, fmt == MOE_FMT_MXFP8 ? kMxFP8 : (fmt == MOE_FMT_FP8 ? kMxFP8Rows : kMxFP4), gate_up,
                                   P.shape == GemmShape::Decode, P.max_tiles, s);

@@ -182,7 +182,8 @@ REL_RMS_SCALED_FP8 = 1e-2
 def scaled_fp8(layer) -> bool:
     """The layer's GEMMs run E4M3 codes (MXFP8 or FP8) on the scaled FP8 MFMA (moe_forward's
     own plan)."""
-    return layer.fmt in ("mxfp8", "fp8") and layer.plan()["gate_up_kernel"] == "mx_gemm_kernel"
+    return layer.fmt in ("mxfp8", "fp8") and layer.plan()["gate_up_kernel"] in ("mx_gemm_kernel",
+                                                                                "fp8_wide_gemm_kernel")
 
 
 def output_bounds(native8: bool) -> dict:

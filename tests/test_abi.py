@@ -208,6 +208,11 @@ def test_forward_plan_names_the_kernels():
     assert info.workspace_bytes == moe.lib().moe_forward_workspace_bytes(ctypes.byref(_args(T=8192, e_end=96)))
     rc, info = _plan(_mx8(T=16384))                             # MXFP8 prefill: scaled FP8 MFMA
     assert rc == OK and info.gate_up_kernel == b"mx_gemm_kernel" and info.m_tile_rows == 128
+    rc, info = _plan(_fp8(T=8192, e_end=96))                    # FP8 prefill: 256 x 256 tiles
+    assert rc == OK and info.gate_up_kernel == b"fp8_wide_gemm_kernel" and info.m_tile_rows == 256
+    assert info.down_kernel == b"fp8_wide_gemm_kernel"
+    rc, info = _plan(_fp8())                                    # FP8 decode: 128-row tiles
+    assert rc == OK and info.gate_up_kernel == b"mx_gemm_kernel" and info.m_tile_rows == 128
     rc, info = _plan(_mx8(T=16384, flags=1))                    # exact sums: the bf16 expansion
     assert rc == OK and info.gate_up_kernel == b"tile_gemm_kernel"
     rc, info = _plan(_mx8(T=256, flags=1))
