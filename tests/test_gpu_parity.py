@@ -194,6 +194,9 @@ LAYER_CASES = [
     # subtiles, longer tails on all of them)
     dict(name="prefill-mxfp8-skew-tiles", wl=synth.custom("mxfp8", T=1100, D=512, F=256, E=24, skew=True, seed=39)),
     dict(name="prefill-nvfp4-skew-tiles", wl=synth.custom("nvfp4", T=1100, D=512, F=256, E=24, skew=True, seed=40)),
+    # NVFP4 prefill on the 256 x 256 tiles at widths that are not powers of two (5 gate_up
+    # N-blocks, 3 down N-blocks, 12 and 10 K chunks; about 470 rows per expert: two tiles)
+    dict(name="prefill-nvfp4-d768-f640", wl=synth.custom("nvfp4", T=700, D=768, F=640, E=12, seed=59)),
     # decode shapes with K a multiple of 512 run the streaming kernels
     dict(name="stream-nvfp4-k2048", wl=synth.custom("nvfp4", T=48, D=2048, F=1536, E=16, seed=31)),
     dict(name="stream-mxfp8-k2048", wl=synth.custom("mxfp8", T=48, D=2048, F=1536, E=16, seed=32)),
