@@ -103,7 +103,7 @@ __global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_ker
     __shared__ __attribute__((aligned(16))) float s_red[4][kSub][64][4];
     __shared__ float s_epi[16][33];                // MXFP8 gate_up: SwiGLU tile, 16 rows x 32 f
 
-    const int tile = blockIdx.x;
+    const int tile = blockIdx.y;  // the slow grid axis: see launch_g
     if (tile >= p.ctrl->n_tiles) return;
     const int el = p.tile_expert[tile];
     const int p0 = p.tile_row0[tile];
@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_ker
     const int r16 = lane & 15, g = lane >> 4;
     const int K = p.K;
     const int F = p.N / 2;
-    const int n0 = GATE_UP ? blockIdx.y * (kRows / 2) : blockIdx.y * kRows;
+    const int n0 = GATE_UP ? blockIdx.x * (kRows / 2) : blockIdx.x * kRows;
     const int kw = wave * G * 128;  // first k of this wave's quarter
     const int64_t row_bytes = NV ? K / 2 : (BW ? 2 * K : K);
 
@@ -332,10 +332,17 @@ __global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_ker
     }
 }
 
+// The grid covers the host's bound on the M-tiles (max_tiles; the device's count is
+// ctrl->n_tiles, about 70% of it at decode). With the tile on the slow axis the
+// workgroups of tiles past the count come after all the real ones instead of among them:
+// decode-nvfp4 gate_up 0.502 -> 0.496 ms, down 0.269 -> 0.256 ms.
 template <int FM, bool GATE_UP, int G>
 hipError_t launch_g(const GemmArgs &a, int32_t max_tiles, hipStream_t s) {
     const int n_tiles_n = GATE_UP ? (a.N / 2) / (kRows / 2) : a.N / kRows;
-    hipLaunchKernelGGL((stream_gemm_kernel<FM, GATE_UP, G>), dim3((unsigned)max_tiles, (unsigned)n_tiles_n),
+    // decode shapes (fewer than 48 slots per expert, at most 4096 experts) bound max_tiles
+    // far below the 65535 limit of the y axis
+    if (max_tiles > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((stream_gemm_kernel<FM, GATE_UP, G>), dim3((unsigned)n_tiles_n, (unsigned)max_tiles),
                        dim3(256), 0, s, a);
     return hipGetLastError();
 }
