@@ -81,6 +81,7 @@ KERNEL_SOURCES = {
     "grouped_gemm_kernel": ["gemm.hip", "gemm_common.h", "layout.h", "formats.h"],
     "mx_gemm_kernel": ["gemm_mx.hip", "gemm_common.h", "layout.h", "formats.h"],
     "fp8_wide_gemm_kernel": ["gemm_fp8_wide.hip", "gemm_common.h", "layout.h", "formats.h"],
+    "bf16_wide_gemm_kernel": ["gemm_bf16_wide.hip", "gemm_common.h", "layout.h", "formats.h"],
 }
 
 

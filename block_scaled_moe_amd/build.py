@@ -16,7 +16,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["quant.hip", "route.hip", "permute.hip", "gemm.hip", "gemm_tile.hip", "gemm_stream.hip", "gemm_mx.hip",
-           "gemm_fp8_wide.hip", "combine.hip", "moe_api.hip"]
+           "gemm_fp8_wide.hip", "gemm_bf16_wide.hip", "combine.hip", "moe_api.hip"]
 FLAGS = ["-O3", "--offload-arch=gfx950", "-fPIC", "-std=c++17", "-ffp-contract=off",
          "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -167,6 +167,12 @@ hipError_t launch_mx_gemm(const GemmArgs &a, int mode, bool gate_up, bool stream
 // (fp8_wide_gemm_bm).
 int32_t fp8_wide_gemm_bm();
 hipError_t launch_fp8_wide_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s);
+// The prefill bf16-expert GEMMs on 256 x 256 workgroup tiles (gemm_bf16_wide.hip): the
+// arithmetic and results of launch_tile_gemm's kFmtBF, 256-row M-tiles (bf16_wide_gemm_bm),
+// K % 64 == 0 and 256-row weight blocks (bf16_wide_gemm_supported).
+int32_t bf16_wide_gemm_bm();
+bool bf16_wide_gemm_supported(int32_t K, int32_t N, bool gate_up);
+hipError_t launch_bf16_wide_gemm(const GemmArgs &a, bool gate_up, int32_t max_tiles, hipStream_t s);
 
 // ---- combine (combine.hip)
 hipError_t launch_combine(int32_t T, int32_t D, int32_t k, const int32_t *slot_pos, const float *w,

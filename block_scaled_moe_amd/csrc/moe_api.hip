@@ -37,11 +37,17 @@ constexpr int32_t kPrefillRowsPerExpert = 48;
 #ifndef MOE_FP8_WIDE
 #define MOE_FP8_WIDE 1
 #endif
+// bf16 experts outside decode on the 256 x 256 tiles of gemm_bf16_wide.hip (1) or on the
+// 64-row tiles of gemm_tile.hip (0)
+#ifndef MOE_BF16_WIDE
+#define MOE_BF16_WIDE 1
+#endif
 
 struct Plan {
     GemmShape shape;
     bool scaled;  // MXFP4 / MXFP8 / FP8 on the scaled MFMA with the codes as stored (gemm_mx.hip)
     bool wide;    // FP8 outside decode: the 256 x 256 tiles (gemm_fp8_wide.hip)
+    bool bfwide;  // bf16 experts outside decode: the 256 x 256 tiles (gemm_bf16_wide.hip)
     bool tiled;   // prefill on the MFMA tile kernels (64- or 128-row M-tiles), or scaled
     int32_t n_loc, chunk_tokens, n_chunks, bm, max_tiles;
     size_t ctrl, chunk_counts, counts, offsets, tile_expert, tile_row0, sorted_slot, slot_pos;
@@ -76,7 +82,9 @@ Plan make_plan(const moe_forward_args *a) {
     p.tiled = p.scaled || (p.shape == GemmShape::Prefill && tile_gemm_supported(gemm_fm(a->fmt), a->D, 2 * a->F, true) &&
                            tile_gemm_supported(gemm_fm(a->fmt), a->F, a->D, false));
     p.wide = f8 && p.shape == GemmShape::Prefill && MOE_FP8_WIDE;
-    p.bm = p.wide ? fp8_wide_gemm_bm() : p.scaled ? mx_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
+    p.bfwide = a->fmt == MOE_FMT_BF16 && p.shape == GemmShape::Prefill && MOE_BF16_WIDE &&
+               bf16_wide_gemm_supported(a->D, 2 * a->F, true) && bf16_wide_gemm_supported(a->F, a->D, false);
+    p.bm = p.wide ? fp8_wide_gemm_bm() : p.bfwide ? bf16_wide_gemm_bm() : p.scaled ? mx_gemm_bm() : (p.tiled ? tile_gemm_bm(gemm_fm(a->fmt)) : gemm_bm(p.shape));
     int32_t ct = (int32_t)(T / 256);
     p.chunk_tokens = ct < 8 ? 8 : (ct > 64 ? 64 : ct);
     p.n_chunks = (int32_t)((T + p.chunk_tokens - 1) / p.chunk_tokens);
@@ -112,10 +120,11 @@ Plan make_plan(const moe_forward_args *a) {
 }
 
 // The kernel family each GEMM of a plan runs (what run_gemm launches).
-enum class Kernel { Wide, Scaled, Tile, Stream, Grouped };
+enum class Kernel { Wide, BfWide, Scaled, Tile, Stream, Grouped };
 
 Kernel gemm_kernel(const Plan &P, int32_t K, int32_t N, bool gate_up) {
     if (P.wide) return Kernel::Wide;
+    if (P.bfwide) return Kernel::BfWide;
     if (P.scaled) return Kernel::Scaled;
     if (P.tiled) return Kernel::Tile;
     if (P.shape == GemmShape::Decode && stream_gemm_supported(K, N, gate_up)) return Kernel::Stream;
@@ -125,6 +134,7 @@ Kernel gemm_kernel(const Plan &P, int32_t K, int32_t N, bool gate_up) {
 const char *kernel_name(Kernel k) {
     switch (k) {
         case Kernel::Wide: return "fp8_wide_gemm_kernel";
+        case Kernel::BfWide: return "bf16_wide_gemm_kernel";
         case Kernel::Scaled: return "mx_gemm_kernel";
         case Kernel::Tile: return "tile_gemm_kernel";
         case Kernel::Stream: return "stream_gemm_kernel";
@@ -136,6 +146,7 @@ hipError_t run_gemm(const GemmArgs &g, int32_t fmt, bool gate_up, const Plan &P,
     const int fm = gemm_fm(fmt);
     switch (gemm_kernel(P, g.K, g.N, gate_up)) {
         case Kernel::Wide: return launch_fp8_wide_gemm(g, gate_up, P.max_tiles, s);
+        case Kernel::BfWide: return launch_bf16_wide_gemm(g, gate_up, P.max_tiles, s);
         case Kernel::Scaled:
             return launch_mx_gemm(g, fmt == MOE_FMT_MXFP8 ? kMxFP8 : (fmt == MOE_FMT_FP8 ? kMxFP8Rows : kMxFP4), gate_up,
                                   P.shape == GemmShape::Decode, P.max_tiles, s);

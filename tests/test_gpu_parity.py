@@ -235,6 +235,10 @@ LAYER_CASES = [
     dict(name="prefill-bf16-k1024", wl=synth.custom("bf16", T=1024, D=1024, F=512, E=32, seed=83)),
     dict(name="stream-bf16-k2048", wl=synth.custom("bf16", T=48, D=2048, F=1536, E=16, seed=84)),
     dict(name="ep-share-bf16", wl=synth.custom("bf16", T=400, D=512, F=384, E=24, e_begin=6, e_end=15, seed=85)),
+    # the 256 x 256 bf16 tiles: hot experts over several 256-row tiles with short tails, and
+    # widths that are not powers of two (5 gate_up N-blocks, 3 down N-blocks)
+    dict(name="prefill-bf16-skew-tiles", wl=synth.custom("bf16", T=1100, D=512, F=256, E=24, skew=True, seed=88)),
+    dict(name="prefill-bf16-d768-f640", wl=synth.custom("bf16", T=700, D=768, F=640, E=12, seed=89)),
     # MXFP8 with exact sums (MOE_FLAG_EXACT_SUMS): the bf16 expansion on the grouped,
     # tile and streaming kernels instead of the scaled FP8 MFMA
     dict(name="decode-mxfp8-exact", wl=synth.custom("mxfp8", T=40, D=256, F=256, E=16, seed=22), flags=1),
