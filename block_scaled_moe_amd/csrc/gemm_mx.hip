@@ -56,9 +56,16 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 
 #ifndef MOE_MX_GROUP
-#define MOE_MX_GROUP 4  // M-tiles per expert-major work group (gemm_common.h)
+#define MOE_MX_GROUP 4  // M-tiles per expert-major work group of the down GEMM (gemm_common.h)
 #endif
 constexpr int kBM = 128, kMS = kBM / 32, kThreads = 256, kGroup = MOE_MX_GROUP;
+// gate_up takes each expert's M-tiles as one group (a group size above any expert's tile
+// count below 2^19 rows; a larger expert still splits into groups, each correct): every
+// N-block's weight panel then passes the XCD's L2 once for all of the expert's tiles.
+// Measured against groups of 4 (same box): skewed-mxfp8 gate_up 3.35 -> 3.25 ms,
+// prefill-mxfp4-ep4 0.294 -> 0.290 ms; groups of 16, 32 and 64 fell in between. The
+// down GEMM keeps groups of 4: groups of 2 and 8 were slower there (1.85 -> 1.88, 1.89 ms).
+constexpr int kGroupGateUp = 4096;
 constexpr int kARow = 144;                     // LDS bytes per A row: 128 of codes + 16 (bank spread)
 constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [kBM rows][8]
 constexpr int kABuf = kACodes + kBM * 8;
@@ -122,8 +129,8 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
     const int b = blockIdx.x;
     if ((b >> 3) >= per_xcd) return;
     int tile, nb;
-    if (!expert_major_item<kGroup>((b & 7) * per_xcd + (b >> 3), NB, kBM, n_tiles, p.tile_expert, p.tile_row0, p.offsets,
-                           tile, nb))
+    if (!expert_major_item<(GATE_UP ? kGroupGateUp : kGroup)>((b & 7) * per_xcd + (b >> 3), NB, kBM, n_tiles,
+                                                              p.tile_expert, p.tile_row0, p.offsets, tile, nb))
         return;
 
     const int el = p.tile_expert[tile];
