@@ -31,6 +31,12 @@
 //    groups of 128 code bytes per row (four FP4 chunks, two FP8 chunks), loaded as whole
 //    128-byte pieces of the gathered token rows; each lane loads its weight operands
 //    straight from global memory into a register ring; one barrier per group;
+//  - the E8M0 scales of the tile's activation rows (K / 32 bytes per row) are staged in LDS
+//    once per tile, each load instruction reading consecutive bytes of one or two rows;
+//    loaded with each group's codes instead, 2 bytes per row and group, every instruction
+//    touched 32 gathered rows' lines, and those loads took about 10% of the MXFP8 and MXFP4
+//    prefill gate_up (a timing-only copy without them: skewed-mxfp8 3.30 -> 2.96 ms,
+//    prefill-mxfp4-ep4 0.295 -> 0.265 ms). K <= 8192 (the LDS region's size);
 //  - work items are ordered expert-major and dealt to the 8 XCDs in contiguous ranges, as
 //    in the tile kernels;
 //  - gate_up epilogue: SwiGLU in fp32, then each wave's rows x 32 tile goes through LDS and
@@ -67,8 +73,9 @@ constexpr int kBM = 128, kMS = kBM / 32, kThreads = 256, kGroup = MOE_MX_GROUP;
 // down GEMM keeps groups of 4: groups of 2 and 8 were slower there (1.85 -> 1.88, 1.89 ms).
 constexpr int kGroupGateUp = 4096;
 constexpr int kARow = 144;                     // LDS bytes per A row: 128 of codes + 16 (bank spread)
-constexpr int kACodes = kBM * kARow;           // scale bytes follow the codes: [kBM rows][8]
-constexpr int kABuf = kACodes + kBM * 8;
+constexpr int kACodes = kBM * kARow;           // one A buffer: [kBM rows][kARow]
+constexpr int kMaxK = 8192;                    // longest K of the staged row scales
+constexpr int kAScales = kBM * (kMaxK / 32 + 8);  // [kBM rows][K / 32 + 8] after the two A buffers
 constexpr int kEpiStride = 33;  // floats per row of a wave's SwiGLU tile (bank spread)
 
 #ifndef MOE_MX4_RING
@@ -117,8 +124,10 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
     using X = Mx<FP8>;
     constexpr int kGrp = X::kGrp, kRing = X::kRing, kCodeBlock = X::kCodeBlock, kScaleBlock = X::kScaleBlock;
     constexpr int kNS = X::NS, kBN = X::kBN;
-    constexpr int kLds = (GATE_UP && !ROWS && 4 * kBM * kEpiStride * 4 > 2 * kABuf) ? 4 * kBM * kEpiStride * 4 : 2 * kABuf;
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];  // A tiles; then the SwiGLU tiles
+    constexpr int kLoop = 2 * kACodes + (ROWS ? 0 : kAScales);  // A tiles and row scales
+    constexpr int kEpi = GATE_UP && !ROWS ? 4 * kBM * kEpiStride * 4 : 0;  // SwiGLU tiles
+    constexpr int kLds = kEpi > kLoop ? kEpi : kLoop;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLds];  // A tiles and scales; then the SwiGLU tiles
 
     const int K = p.K, N = p.N, F = N / 2;
     const int NB = GATE_UP ? F / (kBN / 2) : N / kBN;
@@ -175,52 +184,6 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
     auto run = [&](auto msa_c) __attribute__((always_inline)) {
         constexpr int MSA = decltype(msa_c)::value;
         constexpr int AQ = MSA;                   // 16-byte A pieces per thread per group (32 rows each)
-        constexpr int SROWS = kThreads / kGrp;    // rows whose scales one pass of the threads loads
-        constexpr int SQ = (32 * MSA + SROWS - 1) / SROWS;  // A scale loads per thread per group
-        // ---- A tile (activations) through LDS, one group (128 code bytes and 2 kGrp scale
-        // bytes per row) at a time, double-buffered. Thread t loads 16-byte pieces i = t +
-        // 256 q (row i / 8, piece i % 8: a wave covers 8 whole 128-byte pieces of rows, so
-        // the gathered token rows are read line by line) and the two scale bytes of rows
-        // t / kGrp + SROWS q, chunk t % kGrp. Rows past the tile's end read the tile's first
-        // row (in bounds; never stored); pieces and chunks past the end of K reread the
-        // group's first (unused).
-        const int piece = threadIdx.x & 7, s_chunk = threadIdx.x % kGrp;
-        const uint8_t *ap[AQ];
-#pragma unroll
-        for (int q = 0; q < AQ; ++q) ap[q] = p.a_codes + a_row(32 * q + (threadIdx.x >> 3)) * row_bytes;
-        const uint8_t *sp[SQ];
-#pragma unroll
-        for (int q = 0; q < SQ; ++q)
-            sp[q] = ROWS ? nullptr : p.a_scales + a_row(SROWS * q + threadIdx.x / kGrp) * (K / 32);
-        u32x4 a_pf[AQ];
-        uint32_t s_pf[SQ];
-        auto a_load = [&](int g) {
-            g = min(g, n_groups - 1);
-            const int off = 128 * g + 16 * piece;
-            const int off_ok = off < row_bytes ? off : 128 * g;
-#pragma unroll
-            for (int q = 0; q < AQ; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
-            if constexpr (!ROWS) {
-#pragma unroll
-                for (int q = 0; q < SQ; ++q)
-                    s_pf[q] = *reinterpret_cast<const uint16_t *>(sp[q] + 2 * min(kGrp * g + s_chunk, n_chunks - 1));
-            }
-        };
-        auto a_store = [&](int buf) {
-            uint8_t *ab = lds + buf * kABuf;
-#pragma unroll
-            for (int q = 0; q < AQ; ++q)
-                *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
-            if constexpr (!ROWS) {
-#pragma unroll
-                for (int q = 0; q < SQ; ++q) {
-                    const int r = SROWS * q + threadIdx.x / kGrp;
-                    if (SROWS * (q + 1) <= kBM || r < kBM)
-                        *reinterpret_cast<uint16_t *>(ab + kACodes + r * 8 + 2 * s_chunk) = (uint16_t)s_pf[q];
-                }
-            }
-        };
-
         // ---- B operand ring: chunk c + kRing - 1 is loaded into slot (c - 1) % kRing while
         // chunk c is multiplied; loads past the end repeat the last chunk (in bounds, unused)
         u32x4 breg[kRing][kNS][FP8 ? 2 : 1];
@@ -239,25 +202,102 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                 bsc[slot][ns] = ROWS ? 127 : bs[ns][(int64_t)kScaleBlock * c];
             }
         };
+        // ---- A tile (activations) through LDS, one group (128 code bytes per row) at a
+        // time, double-buffered. Thread t loads 16-byte pieces i = t + 256 q (row i / 8,
+        // piece i % 8: a wave covers 8 whole 128-byte pieces of rows, so the gathered token
+        // rows are read line by line). Rows past the tile's end read the tile's first row
+        // (in bounds; never stored); pieces past the end of K reread the group's first
+        // (unused).
+        // The tile's activation row scales go to LDS once: wave w takes rows w + 4 j, lane l
+        // dword l of the row's K / 32 bytes (K <= kMaxK: at most 64 dwords), into LDS rows
+        // of srow bytes, stored after the first A group's loads are issued and read per
+        // group by a_scales; lane j looks up row w + 4 j and each row's loads take that
+        // with readlane.
+        // The row lookups (sorted slots, in bounds for both GEMMs) are loaded without a
+        // branch and the first weight chunks after them, so one wait covers every lookup
+        // while the weights are in flight (a lookup per row under a branch made the
+        // compiler wait for each in turn before anything else was issued).
+        const int piece = threadIdx.x & 7;
+        constexpr int SQ = ROWS ? 1 : 8 * MSA;    // rows per wave
+        const int sdw = K / 128;                  // scale dwords per row (K % 128 == 0)
+        const int srow = K / 32 + 8;              // LDS bytes per row: 8-byte aligned, rows spread over banks
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        int pos[AQ + 1], slot_of[AQ + 1];
+#pragma unroll
+        for (int q = 0; q <= AQ; ++q) {
+            const int r = q < AQ ? 32 * q + (threadIdx.x >> 3) : wave_u + 4 * min(lane, SQ - 1);
+            pos[q] = p0 + (r < rows ? r : 0);
+            slot_of[q] = p.sorted_slot[pos[q]];
+        }
+#pragma unroll
+        for (int r = 0; r < kRing - 1; ++r) b_load(r, min(r, n_chunks - 1));
+        // an (empty) use of every lookup here: the compiler would otherwise move a lookup
+        // into the branch on gather_by_token, behind the weight loads, and wait for all
+#pragma unroll
+        for (int q = 0; q <= AQ; ++q) asm volatile("" ::"v"(slot_of[q]));
+        const uint8_t *ap[AQ];
+#pragma unroll
+        for (int q = 0; q < AQ; ++q)
+            ap[q] = p.a_codes + (int64_t)(p.gather_by_token ? slot_of[q] / p.top_k : pos[q]) * row_bytes;
+        uint32_t s_pre[SQ];
+        if constexpr (!ROWS) {
+            const int tok_l = p.gather_by_token ? slot_of[AQ] / p.top_k : pos[AQ];
+#pragma unroll
+            for (int j = 0; j < SQ; ++j) {
+                const uint8_t *src = p.a_scales + (int64_t)__builtin_amdgcn_readlane(tok_l, j) * (K / 32);
+                if (lane < sdw) s_pre[j] = reinterpret_cast<const uint32_t *>(src)[lane];
+            }
+        }
+        auto s_store = [&]() {
+            if constexpr (!ROWS) {
+#pragma unroll
+                for (int j = 0; j < SQ; ++j)
+                    if (lane < sdw)
+                        reinterpret_cast<uint32_t *>(lds + 2 * kACodes + (wave_u + 4 * j) * srow)[lane] = s_pre[j];
+            }
+        };
+        u32x4 a_pf[AQ];
+        auto a_load = [&](int g) {
+            g = min(g, n_groups - 1);
+            const int off = 128 * g + 16 * piece;
+            const int off_ok = off < row_bytes ? off : 128 * g;
+#pragma unroll
+            for (int q = 0; q < AQ; ++q) a_pf[q] = *reinterpret_cast<const u32x4 *>(ap[q] + off_ok);
+        };
+        auto a_store = [&](int buf) {
+            uint8_t *ab = lds + buf * kACodes;
+#pragma unroll
+            for (int q = 0; q < AQ; ++q)
+                *reinterpret_cast<u32x4 *>(ab + (32 * q + (threadIdx.x >> 3)) * kARow + 16 * piece) = a_pf[q];
+        };
+
         float16_t acc[MSA][kNS];
 #pragma unroll
         for (int i = 0; i < MSA; ++i)
 #pragma unroll
             for (int j = 0; j < kNS; ++j) acc[i][j] = (float16_t){};
+        // group g's scale bytes of this lane's rows: byte 2 j + g2 of the group's 2 kGrp
+        // (chunk j, block g2), taken by mma as (a_sc[ms][j / 2] >> 16 (j % 2)) & 0xff
         uint32_t a_sc[MSA][2];
-        auto a_scales = [&](int buf) {
+        auto a_scales = [&](int g) {
             if constexpr (ROWS) return;
-            const uint8_t *ab = lds + buf * kABuf + kACodes;
+            const uint8_t *sb = lds + 2 * kACodes + 2 * kGrp * g;
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms) {
-                const uint2 v = *reinterpret_cast<const uint2 *>(ab + (32 * ms + l32) * 8);
-                a_sc[ms][0] = v.x >> (8 * g2);
-                a_sc[ms][1] = v.y >> (8 * g2);
+                const uint8_t *sr = sb + (32 * ms + l32) * srow;
+                if constexpr (kGrp == 4) {
+                    const uint2 v = *reinterpret_cast<const uint2 *>(sr);
+                    a_sc[ms][0] = v.x >> (8 * g2);
+                    a_sc[ms][1] = v.y >> (8 * g2);
+                } else {
+                    a_sc[ms][0] = *reinterpret_cast<const uint32_t *>(sr) >> (8 * g2);
+                    a_sc[ms][1] = 0;
+                }
             }
         };
         // chunk j of the group in LDS buffer buf times the B operands in ring slot `slot`
         auto mma = [&](int buf, int j, int slot) {
-            const uint8_t *ab = lds + buf * kABuf;
+            const uint8_t *ab = lds + buf * kACodes;
             v8i af[MSA];
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms) {
@@ -293,10 +333,9 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
         };
 
         a_load(0);
+        s_store();
         a_store(0);
         a_load(1);
-#pragma unroll
-        for (int r = 0; r < kRing - 1; ++r) b_load(r, min(r, n_chunks - 1));
         __syncthreads();
         // whole ring turns without a branch inside (a conditional use would let the
         // compiler sink the prefetches into it), then the last n_chunks % kRing chunks,
@@ -306,7 +345,7 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
 #pragma unroll
             for (int gi = 0; gi < kRing / kGrp; ++gi) {
                 const int g = c0 / kGrp + gi;
-                a_scales(g & 1);
+                a_scales(g);
 #pragma unroll
                 for (int j = 0; j < kGrp; ++j) {
                     // keep each chunk's prefetch in place: left alone, the scheduler gathers
@@ -325,7 +364,7 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
             const int c = n_full + t;
             if (c >= n_chunks) break;
             const int g = c / kGrp;
-            if (t % kGrp == 0) a_scales(g & 1);
+            if (t % kGrp == 0) a_scales(g);
             mma(g & 1, t % kGrp, t);
             if (t % kGrp == kGrp - 1 && c + 1 < n_chunks) next_group(g);
         }
@@ -449,9 +488,10 @@ void launch_t(const GemmArgs &a, bool stream_once, dim3 grid, hipStream_t s) {
 
 int32_t mx_gemm_bm() { return kBM; }
 
-bool mx_gemm_supported(bool fp8, int32_t K, int32_t N, bool gate_up) {
-    const int bn = fp8 ? Mx<true>::kBN : Mx<false>::kBN;
-    if (K <= 0 || N <= 0 || K % 64) return false;
+bool mx_gemm_supported(int mode, int32_t K, int32_t N, bool gate_up) {
+    const int bn = mode != kMxFP4 ? Mx<true>::kBN : Mx<false>::kBN;
+    if (K <= 0 || N <= 0 || K % 128) return false;
+    if (mode != kMxFP8Rows && K > kMaxK) return false;  // the staged E8M0 row scales
     return gate_up ? (N % 2 == 0 && (N / 2) % (bn / 2) == 0) : N % bn == 0;
 }
 

@@ -151,12 +151,12 @@ hipError_t launch_stream_gemm(const GemmArgs &a, int fm, bool gate_up, int32_t m
 
 // MXFP4, MXFP8 and FP8 GEMMs on the gfx950 scaled MFMA with the codes (and E8M0 scales)
 // as stored (gemm_mx.hip): 128-row M-tiles (mx_gemm_bm), 128 NS weight rows per workgroup
-// (mx_gemm_supported checks K % 64 and the N-block fit); A operand: a_codes / a_scales
-// (FP8: a_codes / a_rscale). gate_up writes o_codes / o_scales (and o_tap); FP8 writes the
-// SwiGLU output to out_f32 for the row quantiser, its sums times fl32(row scale * channel
-// scale).
+// (mx_gemm_supported checks K % 128, K <= 8192 for the E8M0 formats and the N-block fit);
+// A operand: a_codes / a_scales (FP8: a_codes / a_rscale). gate_up writes o_codes /
+// o_scales (and o_tap); FP8 writes the SwiGLU output to out_f32 for the row quantiser, its
+// sums times fl32(row scale * channel scale).
 constexpr int kMxFP4 = 0, kMxFP8 = 1, kMxFP8Rows = 2;
-bool mx_gemm_supported(bool fp8, int32_t K, int32_t N, bool gate_up);
+bool mx_gemm_supported(int mode, int32_t K, int32_t N, bool gate_up);
 int32_t mx_gemm_bm();
 // mode: kMx*; stream_once: decode batches, where each weight panel is read by one M-tile
 // (non-temporal weight loads)

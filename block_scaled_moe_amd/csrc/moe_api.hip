@@ -74,8 +74,8 @@ Plan make_plan(const moe_forward_args *a) {
     // MXFP4 and FP8 always run the scaled MFMA kernels (validate_shape checks the fit);
     // MXFP8 the scaled-FP8 ones unless the caller asks for exact sums or the shape does not
     // fit them
-    const bool fp8 = byte_codes;
-    const bool mx_fit = mx_gemm_supported(fp8, a->D, 2 * a->F, true) && mx_gemm_supported(fp8, a->F, a->D, false);
+    const int mx_mode = mx4 ? kMxFP4 : (f8 ? kMxFP8Rows : kMxFP8);
+    const bool mx_fit = mx_gemm_supported(mx_mode, a->D, 2 * a->F, true) && mx_gemm_supported(mx_mode, a->F, a->D, false);
     p.scaled = mx4 || f8 ||
                (a->fmt == MOE_FMT_MXFP8 && !(a->flags & MOE_FLAG_EXACT_SUMS) && mx_fit &&
                 (p.shape == GemmShape::Prefill || MOE_MX8_DECODE_NATIVE));
@@ -280,12 +280,12 @@ int32_t validate_shape(const moe_forward_args *a) {
     if (a->D % 128 || a->F % 128) return MOE_ERR_UNSUPPORTED;
     if (a->flags & ~(uint32_t)MOE_FLAG_EXACT_SUMS) return MOE_ERR_INVALID_ARG;
     if (a->fmt == MOE_FMT_MXFP4 &&
-        !(mx_gemm_supported(false, a->D, 2 * a->F, true) && mx_gemm_supported(false, a->F, a->D, false)))
+        !(mx_gemm_supported(kMxFP4, a->D, 2 * a->F, true) && mx_gemm_supported(kMxFP4, a->F, a->D, false)))
         return MOE_ERR_UNSUPPORTED;
     // FP8 runs on the scaled FP8 MFMA only (no exact-sum route)
     if (a->fmt == MOE_FMT_FP8 &&
         ((a->flags & MOE_FLAG_EXACT_SUMS) ||
-         !(mx_gemm_supported(true, a->D, 2 * a->F, true) && mx_gemm_supported(true, a->F, a->D, false))))
+         !(mx_gemm_supported(kMxFP8Rows, a->D, 2 * a->F, true) && mx_gemm_supported(kMxFP8Rows, a->F, a->D, false))))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }

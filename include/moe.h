@@ -276,6 +276,8 @@ int32_t moe_forward_plan(const moe_forward_args *a, moe_plan_info *info);
  *  6. out[t] = sum over the token's local slots, j ascending, of topk_w[t][j] * y.
  * Requires D and F multiples of 128 (else MOE_ERR_UNSUPPORTED), and for MXFP4 and FP8
  * also D a multiple of 256 (their GEMMs run on the scaled MFMA in 256-row weight tiles),
+ * for MXFP4 also D, F <= 8192 (its kernel holds a tile's E8M0 activation scales for the
+ * whole K in LDS; MXFP8 beyond that runs the exact route),
  * 1 <= top_k <= 8, 0 <= e_begin < e_end <= E. gate_up/down must match fmt (NVFP4 for
  * W4A16) and shapes.
  * T = 0 is a no-op.

@@ -115,6 +115,27 @@ def test_mxfp4_needs_256_wide_d_model():
     assert _validate(m4) == EUNSUP
 
 
+def test_scaled_mfma_row_scale_limit():
+    """The MX kernel stages each activation row's E8M0 scales for the whole K in LDS, so
+    MXFP4 takes K <= 8192 (D and F); MXFP8 beyond it runs the exact route; FP8 (one scale
+    per row) has no such limit."""
+    def m4(D, F):
+        a = _args(fmt=3, D=D, F=F)
+        a.gate_up = moe.MoePacked(3, 384, 2 * F, D, A16, A16, 0)
+        a.down = moe.MoePacked(3, 384, D, F, A16, A16, 0)
+        return a
+    assert _validate(m4(8192, 2560)) == OK
+    assert _validate(m4(8448, 2560)) == EUNSUP
+    assert _validate(m4(4096, 8320)) == EUNSUP
+    a = _mx8(T=16384, D=8448)
+    a.gate_up = moe.MoePacked(2, 384, 5120, 8448, A16, A16, 0)
+    a.down = moe.MoePacked(2, 384, 8448, 2560, A16, A16, 0)
+    rc, info = _plan(a)
+    assert rc == OK and info.gate_up_kernel == b"tile_gemm_kernel"
+    f = _fp8(D=8448)
+    assert _validate(f) == OK and _plan(f)[1].gate_up_kernel == b"mx_gemm_kernel"
+
+
 @pytest.mark.parametrize("over,status", [
     (dict(fmt=7), EINVAL), (dict(fmt=0), EINVAL), (dict(T=-1), EINVAL), (dict(top_k=0), EINVAL), (dict(top_k=9), EINVAL),
     (dict(e_begin=10, e_end=10), EINVAL), (dict(e_end=385), EINVAL), (dict(e_begin=-1), EINVAL),
