@@ -153,9 +153,22 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
     const uint8_t *wc_e = p.w_codes + (int64_t)e * N * row_bytes;
     const uint8_t *ws_e = ROWS ? nullptr : p.w_scales + (int64_t)e * N * (K / 32);
 
+    // Weight scales: a chunk's scale block of a row group is 64 bytes (byte o = 2 row + g
+    // for MXFP8, 32 g + row for MXFP4) and a row group's blocks are consecutive over the
+    // chunks. SDW (MXFP8 outside decode): the wave's kNS groups of one ring turn (kRing
+    // chunks) are kNS runs of 64 kRing bytes, loaded as SW dwords per lane (dword D = 64 h
+    // + lane is dword D % 16 of chunk (D / 16) % kRing of subtile D / (16 kRing)), and each
+    // chunk's MFMAs take the lane's byte from the lane holding it (ds_bpermute, then a
+    // shift: the instruction reads the low byte). Otherwise each lane loads its byte per
+    // subtile and chunk. Measured (bench hipEvents, one box): skewed-mxfp8 gate_up 2.99 ->
+    // 2.90 ms and down 1.83 -> 1.78 ms with the dwords; prefill-mxfp4-ep4 unchanged, and
+    // decode-mxfp8 1.196 -> 1.205 ms (at one 32-row subtile per tile the exchange sits on
+    // each chunk's short path), so those keep the byte loads.
+    constexpr bool SDW = FP8 && !ROWS && !NT;
     // ---- this lane's B operand rows (weights): the first of its (one or two) 16-byte
-    // pieces of a chunk and its scale byte (MXFP4: half g2 at 512 g2, scale at 32 g2 +
-    // row; MXFP8: quarters g2 and 2 + g2 at 512 g2 and 512 g2 + 1024, scale at 2 row + g2)
+    // pieces of a chunk (MXFP4: half g2 at 512 g2; MXFP8: quarters g2 and 2 + g2 at 512 g2
+    // and 512 g2 + 1024), and its scale byte (SDW: the scale blocks of the wave's row
+    // groups, uniform)
     const uint8_t *bc[kNS];
     const uint8_t *bs[kNS];
 #pragma unroll
@@ -169,8 +182,25 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
         }
         const int64_t blk0 = (int64_t)(row >> 5) * kb;
         bc[ns] = wc_e + blk0 * kCodeBlock + g2 * 512 + (row & 31) * 16;
-        bs[ns] = ROWS ? nullptr : ws_e + blk0 * kScaleBlock + (FP8 ? 2 * (row & 31) + g2 : g2 * 32 + (row & 31));
+        bs[ns] = ROWS ? nullptr
+                      : ws_e + blk0 * kScaleBlock + (SDW ? 0 : (FP8 ? 2 * (row & 31) + g2 : g2 * 32 + (row & 31)));
     }
+    constexpr int SW = SDW ? kRing * kNS / 4 : 1;  // scale dwords per lane per ring turn
+    static_assert(!SDW || (16 * kRing * kNS) % 64 == 0, "whole dwords per lane");
+    const uint8_t *s_src[SW];
+    int s_cj[SW];
+#pragma unroll
+    for (int h = 0; h < SW; ++h) {
+        const int D = 64 * h + lane, ns = D / (16 * kRing);
+        const uint8_t *base = bs[0];
+#pragma unroll
+        for (int n = 1; n < kNS; ++n)
+            if (ns == n) base = bs[n];
+        s_src[h] = SDW ? base + 4 * (D % 16) : nullptr;
+        s_cj[h] = (D / 16) % kRing;
+    }
+    const int s_o = FP8 ? 2 * l32 + g2 : 32 * g2 + l32;  // this lane's byte in a scale block
+    const int s_perm = 4 * (s_o / 4), s_shift = 8 * (s_o % 4);
     const int n_chunks = K / 64;
     const int n_groups = (n_chunks + kGrp - 1) / kGrp;
     auto a_row = [&](int r) -> int64_t {
@@ -199,8 +229,25 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                     else
                         breg[slot][ns][h] = *src;
                 }
-                bsc[slot][ns] = ROWS ? 127 : bs[ns][(int64_t)kScaleBlock * c];
+                if constexpr (!SDW) bsc[slot][ns] = ROWS ? 127 : bs[ns][(int64_t)kScaleBlock * c];
             }
+        };
+        // the weight scales of the ring turn starting at chunk c0 (chunks past the end
+        // reread the last, in bounds and unused); sd_cur holds the current turn's
+        uint32_t sd_cur[SW], sd_next[SW];
+        auto s_load = [&](uint32_t(&dst)[SW], int c0) {
+            if constexpr (SDW) {
+#pragma unroll
+                for (int h = 0; h < SW; ++h)
+                    dst[h] = *reinterpret_cast<const uint32_t *>(s_src[h] +
+                                                               (int64_t)kScaleBlock * min(c0 + s_cj[h], n_chunks - 1));
+            }
+        };
+        // scale operand of subtile ns for chunk `slot` of the current turn
+        auto b_scale = [&](int slot, int ns) -> int {
+            if constexpr (!SDW) return bsc[slot][ns];
+            const int q = 16 * (slot + kRing * ns);
+            return __builtin_amdgcn_ds_bpermute(4 * (q % 64) + s_perm, (int)sd_cur[q / 64]) >> s_shift;
         };
         // ---- A tile (activations) through LDS, one group (128 code bytes per row) at a
         // time, double-buffered. Thread t loads 16-byte pieces i = t + 256 q (row i / 8,
@@ -231,6 +278,7 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
         }
 #pragma unroll
         for (int r = 0; r < kRing - 1; ++r) b_load(r, min(r, n_chunks - 1));
+        s_load(sd_cur, 0);
         // an (empty) use of every lookup here: the compiler would otherwise move a lookup
         // into the branch on gather_by_token, behind the weight loads, and wait for all
 #pragma unroll
@@ -308,6 +356,9 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                 else
                     af[ms] = operand(lo, (u32x4){});
             }
+            int sb[kNS];
+#pragma unroll
+            for (int ns = 0; ns < kNS; ++ns) sb[ns] = b_scale(slot, ns);
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms) {
                 // scale byte of chunk j, block g2: byte 2 j + g2 of the row's scales
@@ -320,7 +371,7 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                     else
                         bf = operand(breg[slot][ns][0], (u32x4){});
                     acc[ms][ns] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[ms], bf, acc[ms][ns], X::kFmt, X::kFmt, 0, sa, 0, bsc[slot][ns]);
+                        af[ms], bf, acc[ms][ns], X::kFmt, X::kFmt, 0, sa, 0, sb[ns]);
                 }
             }
         };
@@ -353,10 +404,15 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                     __builtin_amdgcn_sched_barrier(0);
                     const int slot = gi * kGrp + j;
                     b_load((slot + kRing - 1) % kRing, min(c0 + slot + kRing - 1, n_chunks - 1));
+                    if (slot == 0) s_load(sd_next, c0 + kRing);
                     mma(g & 1, j, slot);
                 }
                 __builtin_amdgcn_sched_barrier(0);
                 next_group(g);
+            }
+            if constexpr (SDW) {
+#pragma unroll
+                for (int h = 0; h < SW; ++h) sd_cur[h] = sd_next[h];
             }
         }
 #pragma unroll
