@@ -213,6 +213,12 @@ LAYER_CASES = [
     dict(name="ep-share-mxfp4", wl=synth.custom("mxfp4", T=400, D=512, F=384, E=24, e_begin=6, e_end=15, seed=54)),
     dict(name="skew-mxfp4", wl=synth.custom("mxfp4", T=600, D=256, F=128, E=16, skew=True, seed=55)),
     dict(name="mxfp4-full-dims", wl=synth.custom("mxfp4", T=64, D=4096, F=2560, E=16, seed=56)),
+    # the longest K whose activation row scales the MX kernel stages in LDS (8192: 64 dwords
+    # per row) and a down K of 10 chunks (5 dwords per row; the last 4-chunk group half full)
+    dict(name="prefill-mxfp4-k8192", wl=synth.custom("mxfp4", T=160, D=8192, F=640, E=8, seed=57)),
+    # the same limit for MXFP8 at prefill (weight scales exchanged per ring turn), and a
+    # down K of 3 dwords per row
+    dict(name="prefill-mxfp8-k8192", wl=synth.custom("mxfp8", T=160, D=8192, F=384, E=8, seed=58)),
     # NVFP4 weights with bf16 activations (W4A16) on all three kernel families
     dict(name="decode-w4a16", wl=synth.custom("w4a16", T=40, D=256, F=256, E=16, seed=61)),
     dict(name="prefill-w4a16", wl=synth.custom("w4a16", T=300, D=256, F=256, E=16, seed=62)),
