@@ -52,6 +52,18 @@ static_assert(kStage % 16 == 0 && 2 * kStage <= 160 * 1024, "stage layout");
 // the loads a stage needs are complete, their registers waited for before the stores.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// floats per row of a wave's 32 x 32 output staging tile (16-byte rows; eight waves' tiles
+// take 36 KiB of a free stage)
+constexpr int kYStride = 36;
+__device__ __forceinline__ void store_f4(float *p, float4 v, bool nt) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v x = {v.x, v.y, v.z, v.w};
+    if (nt)
+        __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(p));
+    else
+        *reinterpret_cast<f4v *>(p) = x;
+}
+
 template <bool GATE_UP>
 __global__ void __launch_bounds__(kThreads, 1) bf16_wide_gemm_kernel(const GemmArgs p) {
     __shared__ __attribute__((aligned(16))) uint8_t st0[kStage];
@@ -179,32 +191,60 @@ __global__ void __launch_bounds__(kThreads, 1) bf16_wide_gemm_kernel(const GemmA
 
         // ---- epilogue: accumulator v of subtile i = row 32 (2 i + wm) + 8(v/4) + 4 g2 + v%4
         if constexpr (MSA > 0) {
+            // the outputs leave 32 x 32 at a time through this wave's tile in stage 0 (every
+            // wave passed the loop's last barrier), each lane storing 16-byte row pieces (rows
+            // past the tile's end are not stored)
+            float *yt = reinterpret_cast<float *>(st0) + wave * 32 * kYStride;
+            auto stage = [&](const float (&val)[16]) __attribute__((always_inline)) {
+                __builtin_amdgcn_wave_barrier();  // the previous tile's reads of yt come first
+#pragma unroll
+                for (int v = 0; v < 16; ++v) yt[(8 * (v / 4) + 4 * g2 + (v % 4)) * kYStride + l32] = val[v];
+                __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+            };
             if (GATE_UP) {
-                // the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input
-                const int f = nb * (kBN / 2) + wn * 32 + l32;
+                // the SwiGLU output rounded to bf16 (nearest even) is the down GEMM's input;
+                // lane (r = lane / 4 + 16 j, eighth lane % 4) stores 8 values
+                const int f0 = nb * (kBN / 2) + wn * 32;
 #pragma unroll
-                for (int i = 0; i < MSA; ++i)
+                for (int i = 0; i < MSA; ++i) {
+                    float val[16];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int m = 32 * (2 * i + wm) + 8 * (v / 4) + 4 * g2 + (v % 4);
+                    for (int v = 0; v < 16; ++v) val[v] = swiglu(acc[i][0][v], acc[i][1][v]);
+                    stage(val);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int r = (lane >> 2) + 16 * j, e8 = lane & 3, m = 32 * (2 * i + wm) + r;
+                        const float4 x0 = *reinterpret_cast<const float4 *>(yt + r * kYStride + 8 * e8);
+                        const float4 x1 = *reinterpret_cast<const float4 *>(yt + r * kYStride + 8 * e8 + 4);
                         if (m < rows) {
-                            const int64_t o = (int64_t)(p0 + m) * F + f;
-                            const float hv = swiglu(acc[i][0][v], acc[i][1][v]);
-                            static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
-                            if (p.o_tap) p.o_tap[o] = hv;
+                            const int64_t o = (int64_t)(p0 + m) * F + f0 + 8 * e8;
+                            const __bf16 b[8] = {(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                                                 (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+                            *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.o_vals) + o) = __builtin_bit_cast(u32x4, b);
+                            if (p.o_tap) {
+                                store_f4(p.o_tap + o, x0, false);
+                                store_f4(p.o_tap + o + 4, x1, false);
+                            }
                         }
                     }
+                }
             } else {
 #pragma unroll
                 for (int ns = 0; ns < kNS; ++ns) {
-                    const int n = nb * kBN + wn * 64 + 32 * ns + l32;
+                    const int n0 = nb * kBN + wn * 64 + 32 * ns;
 #pragma unroll
-                    for (int i = 0; i < MSA; ++i)
+                    for (int i = 0; i < MSA; ++i) {
+                        float val[16];
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int m = 32 * (2 * i + wm) + 8 * (v / 4) + 4 * g2 + (v % 4);
-                            if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, acc[i][ns][v]);
+                        for (int v = 0; v < 16; ++v) val[v] = acc[i][ns][v];
+                        stage(val);
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) {
+                            const int r = (lane >> 3) + 8 * j, q = lane & 7, m = 32 * (2 * i + wm) + r;
+                            const float4 x = *reinterpret_cast<const float4 *>(yt + r * kYStride + 4 * q);
+                            if (m < rows) store_f4(p.out_f32 + (int64_t)(p0 + m) * N + n0 + 4 * q, x, true);
                         }
+                    }
                 }
             }
         }

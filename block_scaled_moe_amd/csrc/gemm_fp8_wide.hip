@@ -54,6 +54,18 @@ static_assert(kStage % 16 == 0 && 4 * kStage <= 160 * 1024, "stage layout");
 // waited for before the LDS stores.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// floats per row of a wave's 32 x 32 output staging tile (16-byte rows; eight waves' tiles
+// take 36 KiB of a free stage)
+constexpr int kYStride = 36;
+__device__ __forceinline__ void store_f4(float *p, float4 v, bool nt) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v x = {v.x, v.y, v.z, v.w};
+    if (nt)
+        __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(p));
+    else
+        *reinterpret_cast<f4v *>(p) = x;
+}
+
 __device__ __forceinline__ v8i operand(u32x4 lo, u32x4 hi) {
     return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
@@ -188,33 +200,48 @@ __global__ void __launch_bounds__(kThreads, 1) fp8_wide_gemm_kernel(const GemmAr
         if (t < 32 * n_sub) rs[t] = p.a_rscale[a_row(t)];
         __syncthreads();
         if constexpr (MSA > 0) {
+            // the outputs leave 32 x 32 at a time through this wave's tile in stage 1, each
+            // lane storing 16-byte row pieces (rows past the tile's end are not stored)
+            float *yt = reinterpret_cast<float *>(st1) + wave * 32 * kYStride;
+            auto put = [&](int i, const float (&val)[16], float *out, int64_t ld, bool nt) __attribute__((always_inline)) {
+                __builtin_amdgcn_wave_barrier();  // the previous tile's reads of yt come first
+#pragma unroll
+                for (int v = 0; v < 16; ++v) yt[(8 * (v / 4) + 4 * g2 + (v % 4)) * kYStride + l32] = val[v];
+                __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = (lane >> 3) + 8 * j, q = lane & 7, m = 32 * (2 * i + wm) + r;
+                    const float4 x = *reinterpret_cast<const float4 *>(yt + r * kYStride + 4 * q);
+                    if (m < rows) store_f4(out + (int64_t)(p0 + m) * ld + 4 * q, x, nt);
+                }
+            };
             const float *ch = p.w_tscale + (int64_t)e * N;
             if (GATE_UP) {
-                const int col = nb * (kBN / 2) + wn * 32 + l32;
-                const float cg = ch[col], cu = ch[F + col];
+                const int col0 = nb * (kBN / 2) + wn * 32;
+                const float cg = ch[col0 + l32], cu = ch[F + col0 + l32];
 #pragma unroll
-                for (int i = 0; i < MSA; ++i)
+                for (int i = 0; i < MSA; ++i) {
+                    float val[16];
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int m = 32 * (2 * i + wm) + 8 * (v / 4) + 4 * g2 + (v % 4);
-                        if (m < rows) {
-                            const float sr = rs[m];
-                            const float g = acc[i][0][v] * (sr * cg), u = acc[i][1][v] * (sr * cu);
-                            p.out_f32[(int64_t)(p0 + m) * F + col] = swiglu(g, u);
-                        }
+                        const float sr = rs[32 * (2 * i + wm) + 8 * (v / 4) + 4 * g2 + (v % 4)];
+                        val[v] = swiglu(acc[i][0][v] * (sr * cg), acc[i][1][v] * (sr * cu));
                     }
+                    put(i, val, p.out_f32 + col0, F, false);
+                }
             } else {
 #pragma unroll
                 for (int ns = 0; ns < kNS; ++ns) {
-                    const int n = nb * kBN + wn * 64 + 32 * ns + l32;
-                    const float cn = ch[n];
+                    const int n0 = nb * kBN + wn * 64 + 32 * ns;
+                    const float cn = ch[n0 + l32];
 #pragma unroll
-                    for (int i = 0; i < MSA; ++i)
+                    for (int i = 0; i < MSA; ++i) {
+                        float val[16];
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int m = 32 * (2 * i + wm) + 8 * (v / 4) + 4 * g2 + (v % 4);
-                            if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, acc[i][ns][v] * (rs[m] * cn));
-                        }
+                        for (int v = 0; v < 16; ++v)
+                            val[v] = acc[i][ns][v] * (rs[32 * (2 * i + wm) + 8 * (v / 4) + 4 * g2 + (v % 4)] * cn);
+                        put(i, val, p.out_f32 + n0, N, true);  // y: store_y's non-temporal stores
+                    }
                 }
             }
         }

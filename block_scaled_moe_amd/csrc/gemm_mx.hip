@@ -77,6 +77,8 @@ constexpr int kACodes = kBM * kARow;           // one A buffer: [kBM rows][kARow
 constexpr int kMaxK = 8192;                    // longest K of the staged row scales
 constexpr int kAScales = kBM * (kMaxK / 32 + 8);  // [kBM rows][K / 32 + 8] after the two A buffers
 constexpr int kEpiStride = 33;  // floats per row of a wave's SwiGLU tile (bank spread)
+constexpr int kYStride = 40;    // floats per row of a wave's 32 x 32 y tile (16-byte rows; lanes 32-63
+                                // write 4 rows down, 32 banks away)
 
 #ifndef MOE_MX4_RING
 #define MOE_MX4_RING 4
@@ -111,6 +113,12 @@ struct Mx {
     static_assert(kRing % kGrp == 0, "the B ring turns over whole A groups");
     static_assert(NS % 2 == 0, "gate_up pairs subtiles");
 };
+
+// four consecutive y values of a row, stored non-temporally like store_y (16-byte aligned)
+__device__ __forceinline__ void store_y4(float *p, float4 v) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store((f4v){v.x, v.y, v.z, v.w}, reinterpret_cast<f4v *>(p));
+}
 
 __device__ __forceinline__ v8i operand(u32x4 lo, u32x4 hi) {
     return (v8i){(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
@@ -426,6 +434,23 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
         }
 
         // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
+        // A down tile's y goes out 32 x 32 at a time through this wave's LDS tile (after the
+        // A buffers are done with): each lane stores 16-byte row pieces, a quarter of the
+        // store instructions of one 4-byte store per accumulator (which measured 11% of the
+        // skewed-mxfp8 down GEMM and 21% of the prefill-mxfp4-ep4 one in a timing-only copy
+        // without y stores). Rows past the tile's end are not stored.
+        auto store_y_tile = [&](float *yt, int ms, const float (&val)[16], float *out_col0) __attribute__((always_inline)) {
+            __builtin_amdgcn_wave_barrier();  // the previous tile's reads of yt come first
+#pragma unroll
+            for (int v = 0; v < 16; ++v) yt[(8 * (v / 4) + 4 * g2 + (v % 4)) * kYStride + l32] = val[v];
+            __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = (lane >> 3) + 8 * j, q = lane & 7, m = 32 * ms + r;
+                const float4 x = *reinterpret_cast<const float4 *>(yt + r * kYStride + 4 * q);
+                if (m < rows) store_y4(out_col0 + (int64_t)(p0 + m) * N + 4 * q, x);
+            }
+        };
         if constexpr (ROWS) {
             // the tile's row scales through LDS (the A tiles are done with)
             __syncthreads();
@@ -451,17 +476,18 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                         }
                 }
             } else {
+                float *yt = reinterpret_cast<float *>(lds) + kBM + wave * 32 * kYStride;  // after the row scales
 #pragma unroll
                 for (int ns = 0; ns < kNS; ++ns) {
-                    const int n = nb * kBN + wave * 32 * kNS + 32 * ns + l32;
-                    const float cn = ch[n];
+                    const int n0 = nb * kBN + wave * 32 * kNS + 32 * ns;
+                    const float cn = ch[n0 + l32];
 #pragma unroll
-                    for (int ms = 0; ms < MSA; ++ms)
+                    for (int ms = 0; ms < MSA; ++ms) {
+                        float val[16];
 #pragma unroll
-                        for (int v = 0; v < 16; ++v) {
-                            const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                            if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, acc[ms][ns][v] * (rs[m] * cn));
-                        }
+                        for (int v = 0; v < 16; ++v) val[v] = acc[ms][ns][v] * (rs[32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4)] * cn);
+                        store_y_tile(yt, ms, val, p.out_f32 + n0);
+                    }
                 }
             }
         } else if (GATE_UP) {
@@ -511,16 +537,16 @@ __global__ void __launch_bounds__(kThreads, (Mx<FP8>::kWaves)) mx_gemm_kernel(co
                 }
             }
         } else {
+            __syncthreads();  // the y tiles reuse the A tiles' LDS
+            float *yt = reinterpret_cast<float *>(lds) + wave * 32 * kYStride;
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
                 for (int ns = 0; ns < kNS; ++ns) {
-                    const int n = nb * kBN + wave * 32 * kNS + 32 * ns + l32;
+                    float val[16];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                        if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, acc[ms][ns][v]);
-                    }
+                    for (int v = 0; v < 16; ++v) val[v] = acc[ms][ns][v];
+                    store_y_tile(yt, ms, val, p.out_f32 + nb * kBN + wave * 32 * kNS + 32 * ns);
                 }
         }
     };

@@ -103,6 +103,18 @@ constexpr int tile_ns() {
 // lanes reading rows at the same column fall on different banks
 template <int NS>
 constexpr int kEpiStride() { return 16 * NS + 1; }
+// floats per row of a wave's 32 x 32 output staging tile (16-byte rows; four waves' tiles
+// fit the smallest activation double buffer)
+constexpr int kYStride = 36;
+
+__device__ __forceinline__ void store_f4(float *p, float4 v, bool nt) {
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    const f4v x = {v.x, v.y, v.z, v.w};
+    if (nt)
+        __builtin_nontemporal_store(x, reinterpret_cast<f4v *>(p));
+    else
+        *reinterpret_cast<f4v *>(p) = x;
+}
 
 // LDS of one workgroup: the double-buffered activation tile, or for the MXFP8 gate_up
 // epilogue the four waves' SwiGLU tiles if larger
@@ -306,41 +318,75 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
         }
 
         // ---- epilogue: accumulator v of lane l = row 32 ms + 8(v/4) + 4 g2 + v%4, column l32
+        // Outputs leave 32 x 32 at a time through this wave's LDS tile (the A stages are
+        // free: every wave passed the loop's last barrier), each lane storing 16-byte row
+        // pieces instead of one 2- or 4-byte store per accumulator element (the store
+        // instructions were a measurable share of the prefill epilogues). Rows past the
+        // tile's end are not stored.
+        float *yt = reinterpret_cast<float *>(smem) + wave * 32 * kYStride;
+        auto stage = [&](const float (&val)[16]) __attribute__((always_inline)) {
+            __builtin_amdgcn_wave_barrier();  // the previous tile's reads of yt come first
+#pragma unroll
+            for (int v = 0; v < 16; ++v) yt[(8 * (v / 4) + 4 * g2 + (v % 4)) * kYStride + l32] = val[v];
+            __builtin_amdgcn_wave_barrier();  // LDS accesses of one wave complete in issue order
+        };
+        // fp32 rows: lane (r = lane / 8 + 8 j, piece lane % 8) of the staged tile
+        auto put_f32 = [&](int ms, float *out, int64_t ld, int col0, bool nt) __attribute__((always_inline)) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = (lane >> 3) + 8 * j, q = lane & 7, m = 32 * ms + r;
+                const float4 x = *reinterpret_cast<const float4 *>(yt + r * kYStride + 4 * q);
+                if (m < rows) store_f4(out + (int64_t)(p0 + m) * ld + col0 + 4 * q, x, nt);
+            }
+        };
         if (GATE_UP && O16) {
             // W4A16 and bf16 experts: the SwiGLU output rounded to bf16 (nearest even) is
-            // the down GEMM's input
+            // the down GEMM's input; lane (r = lane / 4 + 16 j, eighth lane % 4) stores 8
+            // values
 #pragma unroll
             for (int q = 0; q < NS / 2; ++q) {
-                const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+                const int f0 = nb * (BN / 2) + wave * 16 * NS + 32 * q;
 #pragma unroll
-                for (int ms = 0; ms < MSA; ++ms)
+                for (int ms = 0; ms < MSA; ++ms) {
+                    float val[16];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
+                    for (int v = 0; v < 16; ++v) val[v] = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
+                    stage(val);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int r = (lane >> 2) + 16 * j, e8 = lane & 3, m = 32 * ms + r;
+                        const float4 x0 = *reinterpret_cast<const float4 *>(yt + r * kYStride + 8 * e8);
+                        const float4 x1 = *reinterpret_cast<const float4 *>(yt + r * kYStride + 8 * e8 + 4);
                         if (m < rows) {
-                            const int64_t o = (int64_t)(p0 + m) * F + f;
-                            const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
-                            static_cast<__bf16 *>(p.o_vals)[o] = (__bf16)hv;
-                            if (p.o_tap) p.o_tap[o] = hv;
+                            const int64_t o = (int64_t)(p0 + m) * F + f0 + 8 * e8;
+                            const __bf16 b[8] = {(__bf16)x0.x, (__bf16)x0.y, (__bf16)x0.z, (__bf16)x0.w,
+                                                 (__bf16)x1.x, (__bf16)x1.y, (__bf16)x1.z, (__bf16)x1.w};
+                            *reinterpret_cast<u32x4 *>(static_cast<__bf16 *>(p.o_vals) + o) = __builtin_bit_cast(u32x4, b);
+                            if (p.o_tap) {
+                                store_f4(p.o_tap + o, x0, false);
+                                store_f4(p.o_tap + o + 4, x1, false);
+                            }
                         }
                     }
+                }
             }
         } else if (GATE_UP && NV) {
             uint32_t amax = 0;
 #pragma unroll
             for (int q = 0; q < NS / 2; ++q) {
-                const int f = nb * (BN / 2) + wave * 16 * NS + 32 * q + l32;
+                const int f0 = nb * (BN / 2) + wave * 16 * NS + 32 * q;
 #pragma unroll
                 for (int ms = 0; ms < MSA; ++ms) {
+                    float val[16];
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
                         const float hv = swiglu(acc[ms][q][v] * scl, acc[ms][q + NS / 2][v] * scl);
-                        if (m < rows) {
-                            p.out_f32[(int64_t)(p0 + m) * F + f] = hv;
-                            amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
-                        }
+                        val[v] = hv;
+                        if (m < rows) amax = max(amax, __float_as_uint(hv) & 0x7fffffffu);
                     }
+                    stage(val);
+                    put_f32(ms, p.out_f32, F, f0, false);
                 }
             }
             for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
@@ -385,16 +431,16 @@ __global__ void __launch_bounds__(kThreads, (tile_waves_per_simd<NS, BM>())) til
                 }
             }
         } else {
+            // y, stored non-temporally (store_y: written once, read once by the combine)
 #pragma unroll
             for (int ms = 0; ms < MSA; ++ms)
 #pragma unroll
                 for (int ns = 0; ns < NS; ++ns) {
-                    const int n = nb * BN + wave * 32 * NS + 32 * ns + l32;
+                    float val[16];
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int m = 32 * ms + 8 * (v / 4) + 4 * g2 + (v % 4);
-                        if (m < rows) store_y(p.out_f32 + (int64_t)(p0 + m) * N + n, NV ? acc[ms][ns][v] * scl : acc[ms][ns][v]);
-                    }
+                    for (int v = 0; v < 16; ++v) val[v] = NV ? acc[ms][ns][v] * scl : acc[ms][ns][v];
+                    stage(val);
+                    put_f32(ms, p.out_f32, N, nb * BN + wave * 32 * NS + 32 * ns, true);
                 }
         }
     };
