@@ -219,6 +219,11 @@ LAYER_CASES = [
     # the same limit for MXFP8 at prefill (weight scales exchanged per ring turn), and a
     # down K of 3 dwords per row
     dict(name="prefill-mxfp8-k8192", wl=synth.custom("mxfp8", T=160, D=8192, F=384, E=8, seed=58)),
+    # three 256-wide weight tiles and a down K of six chunks (MX: the last 4-chunk group of
+    # MXFP4 half full, three MXFP8 ring turns), prefill-shaped on every scaled route
+    dict(name="prefill-mxfp8-d768-f384", wl=synth.custom("mxfp8", T=500, D=768, F=384, E=10, seed=81)),
+    dict(name="prefill-mxfp4-d768-f384", wl=synth.custom("mxfp4", T=500, D=768, F=384, E=10, seed=82)),
+    dict(name="prefill-fp8-d768-f384", wl=synth.custom("fp8", T=500, D=768, F=384, E=10, seed=83)),
     # NVFP4 weights with bf16 activations (W4A16) on all three kernel families
     dict(name="decode-w4a16", wl=synth.custom("w4a16", T=40, D=256, F=256, E=16, seed=61)),
     dict(name="prefill-w4a16", wl=synth.custom("w4a16", T=300, D=256, F=256, E=16, seed=62)),
