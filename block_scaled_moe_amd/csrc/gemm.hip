@@ -183,11 +183,13 @@ __global__ void __launch_bounds__(WM * WN * 64) grouped_gemm_kernel(const GemmAr
                 for (int ns = 0; ns < C::NS; ++ns) {
                     const uint8_t *srow = smem + C::S_OFF + MOE_BROW(ns) * C::SB;
                     if (NV) {
+                        // the two E4M3 scale bytes, exactly, by the hardware convert (unit scale)
                         const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
-                        sh[ns][0] = e4m3_to_f16(two & 0xff);
-                        sh[ns][1] = e4m3_to_f16(two >> 8);
-                        sf[ns][0] = (float)sh[ns][0];
-                        sf[ns][1] = (float)sh[ns][1];
+                        const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two, 1.0f, false);
+                        sh[ns][0] = h2[0];
+                        sh[ns][1] = h2[1];
+                        sf[ns][0] = (float)h2[0];
+                        sf[ns][1] = (float)h2[1];
                     } else {
                         sm[ns] = __uint_as_float((uint32_t)srow[4 * jj + g] << 23);
                     }

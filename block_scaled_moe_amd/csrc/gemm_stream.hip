@@ -34,6 +34,8 @@ namespace {
 
 using namespace gemm_detail;
 
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
 constexpr int kSub = 4;    // 16-row weight subtiles per workgroup
 constexpr int kRows = 64;  // weight rows per workgroup
 
@@ -219,11 +221,17 @@ __global__ void __launch_bounds__(256, (stream_occupancy<FM>())) stream_gemm_ker
             if (BW) {
                 sm[s][0] = sm[s][1] = 1.0f;
             } else if (NV) {
+                // the two E4M3 scale bytes, exactly, by the hardware convert (unit scale)
                 const uint32_t two = *reinterpret_cast<const uint16_t *>(srow + 8 * jj + 2 * g);
-                sh[s][0] = e4m3_to_f16(two & 0xff);
-                sh[s][1] = e4m3_to_f16(two >> 8);
-                sf[s][0] = (float)sh[s][0];
-                sf[s][1] = (float)sh[s][1];
+                if constexpr (A16) {
+                    const float2_t f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(two, 1.0f, false);
+                    sf[s][0] = f2[0];
+                    sf[s][1] = f2[1];
+                } else {
+                    const half2_t h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(two, 1.0f, false);
+                    sh[s][0] = h2[0];
+                    sh[s][1] = h2[1];
+                }
             } else {
                 // steps 2h, 2h + 1 lie in 32-block 2h + g/2 of the group
                 sm[s][0] = __uint_as_float((uint32_t)srow[4 * jj + (g >> 1)] << 23);
