@@ -278,6 +278,16 @@ LAYER_CASES = [
     dict(name="fp8-full-dims", wl=synth.custom("fp8", T=64, D=4096, F=2560, E=16, seed=85)),
     dict(name="prefill-fp8-d768-f640", wl=synth.custom("fp8", T=700, D=768, F=640, E=12, seed=86)),
     dict(name="fp8-edge-rows", wl=synth.custom("fp8", T=96, D=512, F=256, E=16, seed=87), edge_rows=True),
+    # NVFP4 weights whose block scales are E4M3 subnormals, on the streaming (NVFP4 and
+    # W4A16), prefill tile and grouped kernels
+    dict(name="stream-nvfp4-subnormal-scales", wl=synth.custom("nvfp4", T=40, D=1024, F=512, E=16, seed=91),
+         subnormal_w=True),
+    dict(name="prefill-nvfp4-subnormal-scales", wl=synth.custom("nvfp4", T=600, D=1024, F=512, E=16, seed=92),
+         subnormal_w=True),
+    dict(name="stream-w4a16-subnormal-scales", wl=synth.custom("w4a16", T=40, D=1024, F=512, E=16, seed=93),
+         subnormal_w=True),
+    dict(name="grouped-nvfp4-subnormal-scales", wl=synth.custom("nvfp4", T=24, D=512, F=384, E=12, seed=94),
+         subnormal_w=True),
 ]
 
 
@@ -292,6 +302,21 @@ def _edge_rows(h: np.ndarray) -> np.ndarray:
     return h
 
 
+def _subnormal_weight_scales(h: np.ndarray, gu: np.ndarray, dn: np.ndarray):
+    """Masters whose NVFP4 block scales are E4M3 subnormals. In every expert one 16-block
+    of 4096s sets the tensor scale, which puts every other block's scale below 2^-6. That
+    block only ever meets zeros: it sits in hidden features 0..15, which are zeroed, and
+    in the down columns of intermediate features 0..15, whose gate rows are zero (SwiGLU
+    of a zero gate is zero). So every output element comes from subnormally scaled
+    blocks."""
+    h, gu, dn = h.copy(), gu.copy(), dn.copy()
+    h[:, :16] = 0
+    gu[:, :16, :] = 0
+    gu[:, 16, :16] = 0x4580  # bf16 4096
+    dn[:, 0, :16] = 0x4580
+    return h, gu, dn
+
+
 @pytest.mark.parametrize("c", LAYER_CASES, ids=lambda c: c["name"])
 def test_forward_parity(c):
     wl = c["wl"]
@@ -300,6 +325,8 @@ def test_forward_parity(c):
     h, wr, bias, gu_m, dn_m = case_inputs(wl)
     if c.get("edge_rows"):
         h = _edge_rows(h)
+    if c.get("subnormal_w"):
+        h, gu_m, dn_m = _subnormal_weight_scales(h, gu_m, dn_m)
     report("forward", case=c["name"], fmt=fmt, T=T, D=D, F=F, E=E, local=(eb, ee))
 
     # GPU: quantise, route, forward with every tap
