@@ -81,21 +81,31 @@ __global__ void __launch_bounds__(256) router_prep_kernel(int32_t D, int32_t E, 
 #define MOE_CHAIN_RING 4  // weight blocks (32 k each) in the exact chain's register ring
 #endif
 static_assert(MOE_CHAIN_RING % 2 == 0, "h buffers alternate with the ring slots");
+constexpr int kChainKB = 32;  // k per block of the exact chain
+// blocks of padding past the end of the expert-fastest weight copy and of the chain's LDS
+// h row: the chain runs whole ring turns (up to R - 1 blocks past the last) and loads R - 1
+// blocks ahead of the block it computes
+constexpr int kChainPadBlocks = 2 * MOE_CHAIN_RING;
 
 // ---- exact logits: a workgroup = one wave = one token x 64 experts, one chain per lane,
 // k ascending (grid T x Ep/64, so a decode batch spreads its Ep/64 chains per token over
 // the whole chip instead of one CU per token). The token's h row is staged in LDS as
 // fp32 (all lanes read the same address, a broadcast); the weights stream from the
 // L2-resident bf16 copy through a four-block register ring (blocks of 32 k, loaded three
-// blocks ahead). Logits go to lg_ws [T][Ep] (for the selection kernel) and/or to the
-// caller's logits [T][E]; the workgroups of expert group 0 also fold max |h|.
+// blocks ahead). A wave issues about one instruction per four cycles whatever its kind,
+// so the loop keeps to the FMA, the widening of each weight and few others: each lane's
+// weight pointer advances by a constant stride per block, and the ring's loads ahead of
+// the last block read padding blocks of the weight copy and of the LDS row (values never
+// used) instead of clamping their block index. Logits go to lg_ws [T][Ep] (for the
+// selection kernel) and/or to the caller's logits [T][E]; the workgroups of expert group
+// 0 also fold max |h|.
 __global__ void __launch_bounds__(64) router_chain_kernel(int32_t D, int32_t E, int32_t Ep,
                                                           const uint16_t *__restrict__ h,
                                                           const uint16_t *__restrict__ wk8,
                                                           const float *__restrict__ bias, float *__restrict__ lg_ws,
                                                           float *__restrict__ logits,
                                                           uint32_t *__restrict__ amax_bits) {
-    extern __shared__ __attribute__((aligned(16))) float hrow[];  // [D]
+    extern __shared__ __attribute__((aligned(16))) float hrow[];  // [D + padding blocks]
     const int lane = threadIdx.x;
     const int t = blockIdx.x, e = blockIdx.y * 64 + lane;  // e < Ep
     const uint16_t *hp = h + (int64_t)t * D;
@@ -112,25 +122,27 @@ __global__ void __launch_bounds__(64) router_chain_kernel(int32_t D, int32_t E, 
         if (lane == 0 && amax) atomic_max_grow(amax_bits, amax << 16);
     }
     __syncthreads();
-    const uint16_t *wp = wk8 + (int64_t)e * 8;
-    const int64_t wstep = (int64_t)Ep * 8;  // one k-octet
-    float acc = 0.0f;
-    constexpr int KB = 32, R = MOE_CHAIN_RING;
+    constexpr int KB = kChainKB, R = MOE_CHAIN_RING, NQ = KB / 8;
     const int nb = D / KB;  // D % 64 == 0: even
-    u32x4 wq[R][KB / 8];    // weight ring, R blocks
-    float4 hq[2][KB / 4];   // h of the current and the next block (read from LDS one block ahead)
-    auto load = [&](int slot, int blk) {
+    // this lane's expert in k-octet 0 (u32x4 units: one k-octet holds Ep pieces); octet q of
+    // a block is q * Ep further, and the pointer advances one block per load
+    const u32x4 *wsrc = reinterpret_cast<const u32x4 *>(wk8) + e;
+    const int64_t oct = Ep, blk = (int64_t)NQ * Ep;
+    float acc = 0.0f;
+    u32x4 wq[R][NQ];       // weight ring, R blocks
+    float4 hq[2][KB / 4];  // h of the current and the next block (read from LDS one block ahead)
+    auto load = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < KB / 8; ++q)
-            wq[slot][q] = *reinterpret_cast<const u32x4 *>(wp + (int64_t)(blk * (KB / 8) + q) * wstep);
+        for (int q = 0; q < NQ; ++q) wq[slot][q] = wsrc[q * oct];
+        wsrc += blk;
     };
-    auto hload = [&](int buf, int blk) {
+    auto hload = [&](int buf, int b) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < KB / 4; ++q) hq[buf][q] = *reinterpret_cast<const float4 *>(hrow + blk * KB + 4 * q);
+        for (int q = 0; q < KB / 4; ++q) hq[buf][q] = *reinterpret_cast<const float4 *>(hrow + b * KB + 4 * q);
     };
-    auto compute = [&](int slot, int buf) {
+    auto compute = [&](int slot, int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int q = 0; q < KB / 8; ++q) {
+        for (int q = 0; q < NQ; ++q) {
             const float4 x0 = hq[buf][2 * q], x1 = hq[buf][2 * q + 1];
             const u32x4 y = wq[slot][q];
             acc = __builtin_fmaf(x0.x, bf_lo(y.x), acc);
@@ -143,29 +155,21 @@ __global__ void __launch_bounds__(64) router_chain_kernel(int32_t D, int32_t E, 
             acc = __builtin_fmaf(x1.w, bf_hi(y.w), acc);
         }
     };
-    // block b sits in weight slot b % R and h buffer b % 2. Whole ring turns run without a
-    // branch inside (a conditional use would let the compiler sink the prefetches into it),
-    // each step's prefetches pinned in place; then the last nb % R blocks, already loaded.
+    // block b sits in weight slot b % R and h buffer b % 2. Whole ring turns, each step's
+    // prefetches pinned in place (a conditional use would let the compiler sink them into
+    // it); only the compute of blocks past the last, on the final turn, is skipped.
 #pragma unroll
-    for (int r = 0; r < R - 1; ++r) load(r, min(r, nb - 1));
+    for (int r = 0; r < R - 1; ++r) load(r);
     hload(0, 0);
-    const int n_full = nb - nb % R;
-    for (int b0 = 0; b0 < n_full; b0 += R) {
+    for (int b0 = 0; b0 < nb; b0 += R) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             __builtin_amdgcn_sched_barrier(0);
-            load((r + R - 1) % R, min(b0 + r + R - 1, nb - 1));  // past the end: reload (unused)
-            hload((r + 1) & 1, min(b0 + r + 1, nb - 1));
+            load((r + R - 1) % R);  // block b0 + r + R - 1 (past the end: padding)
+            hload((r + 1) & 1, b0 + r + 1);
             __builtin_amdgcn_sched_barrier(0);  // the next block's h reads go out first
-            compute(r, r & 1);
+            if (b0 + r < nb) compute(r, r & 1);
         }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int r = 0; r < R - 1; ++r) {
-        if (n_full + r >= nb) break;
-        hload((r + 1) & 1, min(n_full + r + 1, nb - 1));
-        compute(r, r & 1);
     }
     const float lg = e < E ? (bias ? acc + bias[e] : acc) : 0.0f;
     if (lg_ws) lg_ws[(int64_t)t * Ep + e] = lg;
@@ -751,7 +755,7 @@ RoutePlan route_plan(int32_t T, int32_t D, int32_t E) {
         off += align256(n);
         return o;
     };
-    p.off_wk8 = take((size_t)D * p.Ep * 2);
+    p.off_wk8 = take((size_t)(D + kChainPadBlocks * kChainKB) * p.Ep * 2);  // + the chain's padding blocks
     if (!p.screen) p.off_exact = take((size_t)T * p.Ep * 4);  // exact logits for the selection
     if (p.screen) {
         p.off_logits = take((size_t)T * p.Ep * 4);  // the MFMA approximations
@@ -778,7 +782,8 @@ hipError_t launch_route(const RoutePlan &p, int32_t T, int32_t D, int32_t E, int
     auto exact = [&](float *out, int32_t *ix, float *wt, uint32_t *amax) {
         float *lg_ws = ix ? reinterpret_cast<float *>(ws + p.off_exact) : nullptr;
         hipLaunchKernelGGL(router_chain_kernel, dim3((unsigned)T, (unsigned)(p.Ep / 64)), dim3(64),
-                           (size_t)D * 4, s, D, E, p.Ep, h, wk8, bias, lg_ws, out, amax);
+                           (size_t)(D + kChainPadBlocks * kChainKB) * 4, s, D, E, p.Ep, h, wk8, bias, lg_ws, out,
+                           amax);
         hipError_t e2 = hipGetLastError();
         if (e2 != hipSuccess || !ix) return e2;
         const dim3 grid((unsigned)((T + 3) / 4)), block(256);
